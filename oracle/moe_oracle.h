@@ -1,0 +1,97 @@
+/*
+ * CPU oracle for the DeepSeekMoE layer forward pass and its bias update.
+ *
+ * TEST INFRASTRUCTURE. Only the tests, the smoke check and the benchmark's
+ * CPU-baseline leg may load this library. It shares no code, header, table or
+ * constant generator with the HIP path.
+ *
+ * Sources ("pages"):
+ *  [V3] "DeepSeek-V3 テクニカルレポート 論文解説" (xyznot.com explainer of the
+ *       DeepSeek-V3 technical report): key ideas (1 shared + 256 routed experts,
+ *       8 active; FP8 E4M3 with 1x128 activation tiles, 128x128 weight blocks,
+ *       FP32 accumulation every N_c = 128); method section 2 "DeepSeekMoE with
+ *       auxiliary-loss-free balancing" (the equation for h'_t, the sigmoid
+ *       affinity, the equation for g'_{i,t}, the end-of-step +-gamma bias rule).
+ *  [ARCH] "DeepSeek モデルアーキテクチャ徹底解説" (deepseekmodel.com): the block
+ *       quantisation pseudo-code (scale = amax / 448, the E4M3 maximum) and the
+ *       DeepSeekMoE forward listing (gate without bias, per-expert masks).
+ *
+ * Arithmetic: every sum is in double, in the order stated at each function.
+ * The only rounding points are the ones named (H at the FFN's rounding point,
+ * and the FP8 codes). The oracle is parallel over tokens or rows, never inside
+ * a sum, so its results do not depend on the thread count.
+ */
+#ifndef MOE_ORACLE_H
+#define MOE_ORACLE_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+enum { ORC_F32 = 0, ORC_BF16 = 1, ORC_FP8 = 2 };
+
+/* ---- scalar conversions --------------------------------------------------- */
+double orc_bf16_value(uint16_t bits);          /* exact widening                     */
+uint16_t orc_bf16_from_double(double x);       /* round to nearest even              */
+double orc_e4m3_value(uint8_t code);           /* OCP E4M3FN decode (NaN for 0x7F/0xFF) */
+uint8_t orc_e4m3_from_float(float x);          /* round to nearest even, saturating at +-448 */
+
+/* array forms of the two roundings */
+void orc_bf16_from_double_array(const double* x, int64_t n, uint16_t* out);
+void orc_e4m3_from_float_array(const float* x, int64_t n, uint8_t* out);
+
+/* ---- FP8 tile quantisation ([V3] key ideas; [ARCH] quantisation pseudo-code)
+ * x: [rows, cols] row-major of dtype xdt (ORC_F32 or ORC_BF16); tiles of tr x tc
+ * (rows % tr == 0, cols % tc == 0). Per tile: amax = max |x| (fp32), s = fl32(amax/448),
+ * q = E4M3_RNE(fl32(x / s)); s == 0 gives q = 0. s: [rows/tr, cols/tc]. */
+void orc_quantize_tiles(const void* x, int xdt, int64_t rows, int64_t cols, int tr, int tc,
+                        uint8_t* q, float* s);
+
+/* ---- routing ([V3] method section 2: sigmoid affinity, g', normalisation)
+ * u: [n, d] rows (act dtype), e: [n_r, d] (act dtype), b: [n_r] fp32.
+ * Out: idx [n, K] ascending expert ids; gate [n, K] (double) aligned with idx;
+ * gap [n] = v_(K) - v_(K+1) (+inf when K == n_r); v [n, n_r] biased scores (optional). */
+void orc_route(int64_t n, int d, int n_r, int K, int act, const void* u, const void* e,
+               const float* b, int32_t* idx, double* gate, double* gap, double* v);
+
+/* ---- dispatch: counts, exclusive offsets [n_r+1], rows sorted by (expert, token) */
+void orc_dispatch(int64_t T, int n_r, int K, const int32_t* idx, int32_t* count,
+                  int32_t* offset, int32_t* sorted_token, int32_t* pair_row);
+
+/* ---- end-of-step bias update ([V3] method section 2): overloaded -gamma, underloaded +gamma */
+void orc_bias_update(int64_t T, int n_r, int K, const int32_t* count, float gamma, float* b);
+
+/* ---- one expert's SwiGLU FFN on n rows
+ * ffn = ORC_F32: x, w fp32; H rounded to fp32.
+ * ffn = ORC_BF16: x, w bf16; H rounded to bf16.
+ * ffn = ORC_FP8: x bf16 (quantised here per 1x128), w1/w3/w2 E4M3 codes with block
+ *   scales s1/s3 [d_ff/128, d/128] and s2 [d/128, d_ff/128]; H rounded to fp32 then
+ *   quantised per 1x128.
+ * w1, w3: [d_ff, d]; w2: [d, d_ff]. Out: y [n, d] in double; h [n, d_ff] the H values
+ * at the rounding point (optional). */
+void orc_expert_rows(int d, int d_ff, int ffn, const void* x, int64_t n, const void* w1,
+                     const void* w3, const void* w2, const float* s1, const float* s3,
+                     const float* s2, double* h, double* y);
+
+/* ---- the layer for n tokens ([V3] method section 2, equation for h'_t)
+ * u: [n, d] rows of the tokens (act dtype). Routed expert i's weights are wr1[i],
+ * wr3[i], wr2[i] (and scales sr1[i], sr3[i], sr2[i] for FP8); an expert no token of
+ * the list selects may be NULL. Shared experts likewise (ws*, ss*), n_s of them.
+ * Out: out [n, d] = u + sum_shared + sum_routed(g * y), in double; optional
+ * idx/gate/gap as in orc_route; optional shared_sum/routed_sum [n, d].
+ * Returns 0, or -1 if a routed expert that is needed has a NULL weight pointer. */
+int orc_layer(int64_t n, int d, int n_r, int K, int n_s, int d_ff, int act, int ffn,
+              const void* u, const void* e, const float* b,
+              const void* const* wr1, const void* const* wr3, const void* const* wr2,
+              const float* const* sr1, const float* const* sr3, const float* const* sr2,
+              const void* const* ws1, const void* const* ws3, const void* const* ws2,
+              const float* const* ss1, const float* const* ss3, const float* const* ss2,
+              double* out, int32_t* idx, double* gate, double* gap,
+              double* shared_sum, double* routed_sum);
+
+#ifdef __cplusplus
+}
+#endif
+#endif

@@ -1,0 +1,90 @@
+"""Second formulations used to pin the oracle (tests only).
+
+These are written independently of ``oracle/moe_oracle.c``: NumPy float64 with
+BLAS matrix products (a different summation order), bit-level roundings, full
+sorts instead of arg-max passes, and the per-expert masked loop of the
+"DeepSeek モデルアーキテクチャ徹底解説" forward listing instead of per-token
+evaluation. They agree with the oracle to rounding order, not bit for bit.
+"""
+import numpy as np
+
+
+def widen(a, dt):
+    """bf16 bits (uint16) or float32 -> float64."""
+    if dt == "f32":
+        return np.asarray(a, np.float32).astype(np.float64)
+    return (np.asarray(a, np.uint16).astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+
+
+def round_bf16_bits(x):
+    """float64 -> bf16 value (as float64), round to nearest even, by integer ops on the
+    float64 bit pattern: keep sign, exponent and 7 fraction bits (valid for normal bf16)."""
+    x = np.asarray(x, np.float64)
+    b = x.view(np.uint64).copy()
+    low = np.uint64(45)  # 52 - 7 fraction bits dropped
+    keep_lsb = (b >> low) & np.uint64(1)
+    b = b + (np.uint64((1 << 44) - 1) + keep_lsb)
+    b = b & ~np.uint64((1 << 45) - 1)
+    return b.view(np.float64)
+
+
+def round_f32(x):
+    return np.asarray(x, np.float64).astype(np.float32).astype(np.float64)
+
+
+def sigmoid(z):
+    return 1.0 / (1.0 + np.exp(-z))
+
+
+def topk_by_sort(v, K):
+    """Top-K of each row by a full stable sort on (-v, index); ids ascending."""
+    n, E = v.shape
+    out = np.empty((n, K), np.int64)
+    for t in range(n):
+        order = np.lexsort((np.arange(E), -v[t]))
+        out[t] = np.sort(order[:K])
+    return out
+
+
+def swiglu_ffn(x, w1, w3, w2, hround):
+    """x [n,d] float64; w1,w3 [I,d]; w2 [d,I] -> y [n,d]; H rounded by `hround`."""
+    a = x @ w1.T
+    g = x @ w3.T
+    h = hround(a * sigmoid(a) * g)
+    return h @ w2.T
+
+
+def dense_layer(u, e, b, routed, shared, K, hround):
+    """All-experts dense evaluation: every routed expert on every token, with a gate
+    matrix that is zero outside each token's top-K. Inputs are float64."""
+    v = sigmoid(u @ e.T) + b[None, :]
+    s = sigmoid(u @ e.T)
+    sel = topk_by_sort(v, K)
+    G = np.zeros_like(s)
+    for t in range(u.shape[0]):
+        G[t, sel[t]] = s[t, sel[t]]
+        G[t] /= G[t, sel[t]].sum()
+    out = u.copy()
+    for (w1, w3, w2) in shared:
+        out = out + swiglu_ffn(u, w1, w3, w2, hround)
+    for i in range(e.shape[0]):
+        out = out + G[:, i:i + 1] * swiglu_ffn(u, *routed[i], hround)
+    return out, sel, G
+
+
+def masked_loop_layer(u, sel, gates, routed, shared, hround):
+    """The per-expert masked loop: for each expert, the tokens that chose it, their FFN
+    rows, and a gate-weighted accumulation; plus the shared experts and the residual."""
+    routed_out = np.zeros_like(u)
+    for i in sorted(routed):
+        mask = (sel == i)
+        tok = np.nonzero(mask.any(axis=1))[0]
+        if tok.size == 0:
+            continue
+        y = swiglu_ffn(u[tok], *routed[i], hround)
+        w = gates[mask]
+        routed_out[tok] += y * w[:, None]
+    shared_out = np.zeros_like(u)
+    for (w1, w3, w2) in shared:
+        shared_out += swiglu_ffn(u, w1, w3, w2, hround)
+    return u + shared_out + routed_out

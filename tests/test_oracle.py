@@ -1,0 +1,510 @@
+"""Pins of the CPU oracle against things other than itself (CPU only).
+
+Each test names what fixes the expected value: a closed form, an invariant, a
+brute-force search, a special case that reduces to a textbook routine, or a
+second formulation (dense all-experts, per-expert masks). Layer equations are
+from the DeepSeek-V3 explainer ("DeepSeek-V3 テクニカルレポート 論文解説",
+method section 2); FP8 constants from its key ideas and from the quantisation
+pseudo-code of "DeepSeek モデルアーキテクチャ徹底解説".
+"""
+import json
+import math
+import os
+import subprocess
+import sys
+from concurrent.futures import ThreadPoolExecutor
+
+import numpy as np
+import pytest
+
+import oracle
+from mixture_experts_layer_26_amd import inputs as I
+from tests import npref
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def _weights(w, shared, idx):
+    return I.make_expert(w, shared, idx)
+
+
+def _widen_tuple(w, tup):
+    dt = I.weight_dtype(w)
+    return tuple(npref.widen(a, dt) for a in tup)
+
+
+def _hround(w):
+    return npref.round_f32 if w.ffn == "f32" else npref.round_bf16_bits
+
+
+# ------------------------------------------------------------------ constants
+
+def test_page_constants_golden():
+    """The hyper-parameters the pages print (golden fixture with citations)."""
+    with open(os.path.join(GOLDEN, "page_constants.json")) as f:
+        g = json.load(f)
+    assert oracle.e4m3_value(0x7E) == g["e4m3_max"]["value"]
+    v3 = I.WORKLOADS["v3_prefill_bf16"]
+    assert (v3.n_routed, v3.top_k, v3.n_shared) == (g["n_routed"]["value"], g["top_k"]["value"],
+                                                     g["n_shared"]["value"])
+    assert v3.gamma == g["gamma"]["value"]
+    assert g["activation_tile"]["value"] == [1, 128] and g["weight_block"]["value"] == [128, 128]
+    assert g["n_c"]["value"] == 128
+
+
+# ------------------------------------------------------------------ generator
+
+def test_philox_known_answers():
+    """Philox4x32-10 known-answer vectors of the Random123 distribution."""
+    kat = [
+        ([0, 0, 0, 0], [0, 0], [0x6627E8D5, 0xE169C58D, 0xBC57AC4C, 0x9B00DBD8]),
+        ([0xFFFFFFFF] * 4, [0xFFFFFFFF] * 2, [0x408F276D, 0x41C83B0E, 0xA20BC7C6, 0x6D5451FD]),
+        ([0x243F6A88, 0x85A308D3, 0x13198A2E, 0x03707344], [0xA4093822, 0x299F31D0],
+         [0xD16CFE09, 0x94FDCCEB, 0x5001E420, 0x24126EA1]),
+    ]
+    for ctr, key, want in kat:
+        assert list(I.philox4x32_10(ctr, key)) == want
+
+
+def test_generator_moments_and_slices():
+    z = I.normal(11, 4, 0, 1 << 20, 1.0, "f32").astype(np.float64)
+    assert abs(z.mean()) < 5.0 / math.sqrt(z.size)
+    assert abs(z.var() - 1.0) < 0.01
+    # a slice regenerates to the same values (counter-based)
+    part = I.normal(11, 4, 12345, 1000, 1.0, "f32")
+    assert np.array_equal(part, I.normal(11, 4, 0, 13345, 1.0, "f32")[12345:])
+    u = I.uniform(11, 3, 0, 1 << 16, -0.01, 0.01)
+    assert u.min() > -0.01 and u.max() < 0.01
+
+
+# ------------------------------------------------------------ scalar roundings
+
+def test_bf16_rounding_brute_force():
+    """bf16 rounding is the nearer of the two bf16 neighbours, ties to even (checked on
+    random doubles and on exact midpoints)."""
+    rng = np.random.default_rng(1)
+    x = rng.standard_normal(200000) * np.exp2(rng.integers(-20, 20, 200000))
+    got = npref.widen(oracle.bf16_from_double(x), "bf16")
+    # neighbours: truncate the float32 of x towards zero, and one bf16 step further out
+    f = x.astype(np.float32)
+    lo = npref.widen((f.view(np.uint32) >> 16).astype(np.uint16), "bf16")
+    hi = npref.widen(((f.view(np.uint32) >> 16) + 1).astype(np.uint16), "bf16")
+    assert np.all((got == lo) | (got == hi))
+    dlo, dhi = np.abs(x - lo), np.abs(hi - x)
+    assert np.all(np.abs(x - got) <= np.minimum(dlo, dhi))
+    # exact midpoints go to the even pattern
+    base = rng.integers(0x3000, 0x4F00, 5000).astype(np.uint16)
+    mid = (npref.widen(base, "bf16") + npref.widen(base + 1, "bf16")) / 2.0
+    got_mid = oracle.bf16_from_double(mid)
+    assert np.all(got_mid % 2 == 0)
+    assert np.all((got_mid == base) | (got_mid == base + 1))
+    # and the bit-level reference agrees everywhere
+    assert np.array_equal(npref.round_bf16_bits(x), got)
+
+
+def test_e4m3_decode_facts():
+    """OCP E4M3FN facts: 0x7E = 448 (the pages' maximum), 0x08 = 2^-6 (smallest normal),
+    0x01 = 2^-9 (smallest subnormal), 0x38 = 1, 0x7F is NaN, sign symmetry, and the
+    finite codes 0..0x7E increase strictly."""
+    t = oracle.e4m3_table()
+    assert t[0x7E] == 448.0 and t[0x08] == 2.0 ** -6 and t[0x01] == 2.0 ** -9
+    assert t[0x38] == 1.0 and t[0x40] == 2.0 and t[0x00] == 0.0
+    assert math.isnan(t[0x7F]) and math.isnan(t[0xFF])
+    assert np.all(np.diff(t[:0x7F]) > 0)
+    assert np.array_equal(t[0x80:0xFF], -t[0x00:0x7F])
+    # 126 distinct positive finite values on the grid: multiples of 2^-9 below 2^-6 ...
+    assert np.array_equal(t[1:8] * 2 ** 9, np.arange(1, 8))
+    # ... and 8 mantissa steps per binade above
+    for ex in range(-6, 9):
+        row = t[(ex + 7) * 8:(ex + 8) * 8]
+        n = 7 if ex == 8 else 8          # the top binade's last pattern is NaN
+        assert np.array_equal(row[:n], ((1 + np.arange(8) / 8.0) * 2.0 ** ex)[:n])
+
+
+def _brute_e4m3(x, grid_vals, grid_codes):
+    """Nearest finite E4M3 by search over the sorted positive grid; ties to the even
+    code; beyond 448 saturate. x >= 0 float64."""
+    j = np.searchsorted(grid_vals, x, side="left")
+    j = np.clip(j, 1, len(grid_vals) - 1)
+    lo, hi = grid_vals[j - 1], grid_vals[j]
+    clo, chi = grid_codes[j - 1], grid_codes[j]
+    dlo, dhi = x - lo, hi - x
+    pick_hi = (dhi < dlo) | ((dhi == dlo) & (chi % 2 == 0))
+    code = np.where(pick_hi, chi, clo)
+    code = np.where(x >= grid_vals[-1], 0x7E, code)
+    code = np.where(x <= 0, 0, code)
+    return code.astype(np.uint8)
+
+
+@pytest.mark.slow
+def test_e4m3_encode_exhaustive():
+    """Every non-negative float32 up to 464 (and past it) against the brute-force search."""
+    t = oracle.e4m3_table()
+    grid_codes = np.arange(0, 0x7F)
+    grid_vals = t[:0x7F]
+    top = np.float32(464.0).view(np.uint32) + 4096
+    chunk = 1 << 23
+
+    def run(start):
+        bits = np.arange(start, min(start + chunk, top), dtype=np.uint32)
+        x = bits.view(np.float32)
+        got = oracle.e4m3_from_float(x)
+        want = _brute_e4m3(x.astype(np.float64), grid_vals, grid_codes)
+        bad = np.nonzero(got != want)[0]
+        return None if bad.size == 0 else (int(bits[bad[0]]), int(got[bad[0]]), int(want[bad[0]]))
+
+    with ThreadPoolExecutor(8) as ex:
+        res = list(ex.map(run, range(0, int(top), chunk)))
+    assert all(r is None for r in res), [r for r in res if r is not None][:3]
+    # negatives mirror the positives
+    x = np.random.default_rng(2).uniform(-500, 0, 100000).astype(np.float32)
+    assert np.array_equal(oracle.e4m3_from_float(x), oracle.e4m3_from_float(-x) | 0x80)
+
+
+def test_quantize_properties():
+    """scale = amax/448: each tile's largest magnitude lands on code 0x7E, decoded values
+    stay within half an E4M3 step of x / scale, and an all-zero tile has scale 0, codes 0."""
+    rng = np.random.default_rng(3)
+    x = rng.standard_normal((256, 384)).astype(np.float32)
+    x[128:256, 0:128] = 0.0
+    q, s = oracle.quantize(x, "f32", 128, 128)
+    t = oracle.e4m3_table()
+    for br in range(2):
+        for bc in range(3):
+            blk = x[br * 128:(br + 1) * 128, bc * 128:(bc + 1) * 128]
+            qb = q[br * 128:(br + 1) * 128, bc * 128:(bc + 1) * 128]
+            if not blk.any():
+                assert s[br, bc] == 0 and not qb.any()
+                continue
+            amax = np.abs(blk).max()
+            assert abs(s[br, bc] * 448.0 / amax - 1) < 1e-6
+            r, c = np.unravel_index(np.abs(blk).argmax(), blk.shape)
+            assert qb[r, c] & 0x7F == 0x7E
+            dec = t[qb]
+            ratio = blk.astype(np.float64) / s[br, bc]
+            step = np.where(np.abs(ratio) < 2 ** -6, 2.0 ** -9,
+                            2.0 ** (np.floor(np.log2(np.maximum(np.abs(ratio), 2 ** -6))) - 3))
+            assert np.all(np.abs(dec - ratio) <= step / 2 + 1e-12)
+    # 1x128 activation tiles: one scale per row per 128 columns
+    q1, s1 = oracle.quantize(x[:4], "f32", 1, 128)
+    assert s1.shape == (4, 3)
+    assert np.allclose(s1 * 448, np.abs(x[:4]).reshape(4, 3, 128).max(axis=2), rtol=1e-6)
+
+
+# ------------------------------------------------------------------ routing
+
+def _route_inputs(w, T=None):
+    if T is not None:
+        w = w.with_tokens(T)
+    return w, I.make_u(w), I.make_e(w), I.make_b(w)
+
+
+@pytest.mark.parametrize("name,T", [("tiny_f32", None), ("mid_bf16", 512), ("v3_prefill_bf16", 64),
+                                    ("v3_decode_skewed", None)])
+def test_route_against_full_sort(name, T):
+    """Top-K of the oracle equals a full sort of (-v, i); v and the gates match a BLAS
+    evaluation of sigmoid(u e^T) + b; gates sum to 1; ids are K distinct ascending."""
+    w, u, e, b = _route_inputs(I.WORKLOADS[name], T)
+    idx, gate, gap, v = oracle.route(u, e, b, w.top_k, w.act, want_v=True)
+    assert np.array_equal(idx, npref.topk_by_sort(v, w.top_k))
+    ud, ed = npref.widen(u, w.act), npref.widen(e, w.act)
+    s_ref = npref.sigmoid(ud @ ed.T)
+    v_ref = s_ref + b.astype(np.float64)[None, :]
+    assert np.max(np.abs(v - v_ref)) < 1e-12
+    sel_ref = npref.topk_by_sort(v_ref, w.top_k)
+    robust = gap > 1e-9
+    assert np.array_equal(idx[robust], sel_ref[robust])
+    g_ref = np.take_along_axis(s_ref, idx, 1)
+    g_ref /= g_ref.sum(1, keepdims=True)
+    assert np.max(np.abs(gate - g_ref)) < 1e-13
+    assert np.max(np.abs(gate.sum(1) - 1)) < 1e-13
+    assert np.all(np.diff(idx, axis=1) > 0)
+    # the gap is v_(K) - v_(K+1) of the sorted scores
+    vs = -np.sort(-v, axis=1)
+    assert np.allclose(gap, vs[:, w.top_k - 1] - vs[:, w.top_k], rtol=0, atol=0)
+
+
+def test_route_zero_centroids_and_ties():
+    """e = 0, b = 0: every score is 1/2, so experts 0..K-1 win by the lower-index rule with
+    gates exactly 1/K. A constructed tie (e_j := e_i, b_j := b_i, i < j) keeps i."""
+    w = I.WORKLOADS["mid_bf16"].with_tokens(32)
+    u = I.make_u(w)
+    e = np.zeros((w.n_routed, w.d), np.uint16)
+    b = np.zeros(w.n_routed, np.float32)
+    idx, gate, gap, _ = oracle.route(u, e, b, w.top_k, w.act)
+    assert np.all(idx == np.arange(w.top_k)[None, :])
+    assert np.all(gate == 1.0 / w.top_k)
+    assert np.all(gap == 0.0)
+    # tie: copy expert 3's centroid and bias onto expert 40 and make them dominant
+    e = I.make_e(w)
+    b = I.make_b(w)
+    e[40] = e[3]
+    b[3] = b[40] = 1.0
+    idx, _, _, v = oracle.route(u, e, b, w.top_k, w.act, want_v=True)
+    assert np.all(v[:, 3] == v[:, 40])
+    assert np.all(np.any(idx == 3, axis=1))
+    # with only one slot, the tie goes to 3
+    idx1, g1, _, _ = oracle.route(u, e, b, 1, w.act)
+    assert np.all(idx1[:, 0] == 3) and np.all(g1 == 1.0)
+
+
+def test_route_all_experts():
+    """K = N_r selects every expert, with g = s / sum(s) over all of them."""
+    w = I.WORKLOADS["tiny_f32"]
+    u, e, b = I.make_u(w), I.make_e(w), I.make_b(w)
+    idx, gate, gap, _ = oracle.route(u, e, b, w.n_routed, w.act)
+    assert np.all(idx == np.arange(w.n_routed)[None, :]) and np.all(np.isinf(gap))
+    s = npref.sigmoid(npref.widen(u, "f32") @ npref.widen(e, "f32").T)
+    assert np.max(np.abs(gate - s / s.sum(1, keepdims=True))) < 1e-14
+
+
+# ------------------------------------------------------------ dispatch, bias
+
+def _check_dispatch(idx, n_r, count, offset, sorted_token, pair_row):
+    T, K = idx.shape
+    assert count.sum() == T * K
+    assert np.array_equal(count, np.bincount(idx.ravel(), minlength=n_r))
+    assert offset[0] == 0 and np.array_equal(np.diff(offset), count)
+    for i in range(n_r):
+        seg = sorted_token[offset[i]:offset[i + 1]]
+        assert np.all(np.diff(seg) > 0)
+        assert np.array_equal(seg, np.nonzero((idx == i).any(1))[0])
+    tt = np.repeat(np.arange(T), K).reshape(T, K)
+    assert np.array_equal(sorted_token[pair_row], tt)
+    seg_of_row = np.searchsorted(offset, pair_row, side="right") - 1
+    assert np.array_equal(seg_of_row, idx)
+
+
+@pytest.mark.parametrize("name,T", [("tiny_f32", None), ("mid_bf16", 1024), ("v3_decode_skewed", None)])
+def test_dispatch_invariants(name, T):
+    w, u, e, b = _route_inputs(I.WORKLOADS[name], T)
+    idx, _, _, _ = oracle.route(u, e, b, w.top_k, w.act)
+    _check_dispatch(idx, w.n_routed, *oracle.dispatch(idx, w.n_routed))
+
+
+def test_dispatch_edge_cases():
+    """All tokens on one expert set; a single token; K = N_r."""
+    T, n_r, K = 300, 16, 3
+    idx = np.tile(np.array([2, 7, 9], np.int32), (T, 1))
+    res = oracle.dispatch(idx, n_r)
+    _check_dispatch(idx, n_r, *res)
+    assert res[0][2] == T and res[0][0] == 0
+    idx = np.array([[0, 5]], np.int32)
+    _check_dispatch(idx, 8, *oracle.dispatch(idx, 8))
+    idx = np.tile(np.arange(n_r, dtype=np.int32), (5, 1))
+    _check_dispatch(idx, n_r, *oracle.dispatch(idx, n_r))
+
+
+def test_bias_update_closed_form():
+    """Over the mean load T*K/N_r: b - gamma; under: b + gamma; at the mean: unchanged.
+    Each new value is the fp32 rounding of b -+ 0.001f."""
+    rng = np.random.default_rng(5)
+    T, n_r, K = 4096, 64, 6
+    mean = T * K // n_r
+    count = rng.integers(mean - 40, mean + 40, n_r).astype(np.int32)
+    count[:5] = mean
+    b = rng.uniform(-0.01, 0.01, n_r).astype(np.float32)
+    nb = oracle.bias_update(count, T, K, 0.001, b)
+    g = np.float32(0.001)
+    assert np.sum(nb < b) == np.sum(count > mean) and np.sum(nb > b) == np.sum(count < mean)
+    for i in range(n_r):
+        want = b[i] if count[i] == mean else (b[i] - g if count[i] > mean else b[i] + g)
+        assert nb[i] == np.float32(want)
+        half_ulp = 0.5 * abs(float(np.spacing(np.float32(nb[i]))))
+        if count[i] != mean:
+            step = float(nb[i]) - float(b[i])
+            assert abs(abs(step) - float(g)) <= half_ulp
+    # from b = 0 the new bias is exactly -0.001f, 0 or +0.001f
+    nb0 = oracle.bias_update(count, T, K, 0.001, np.zeros(n_r, np.float32))
+    assert set(np.unique(nb0)) <= {np.float32(-0.001), np.float32(0), np.float32(0.001)}
+
+
+# -------------------------------------------------------------- expert FFN
+
+def test_swiglu_closed_form():
+    """One-hot input row: a_j = W1[j,0], beta_j = W3[j,0], h_j = a_j*sigmoid(a_j)*beta_j,
+    y = W2 h; with W2 the identity, y = h. SiLU(0) = 0."""
+    d = d_ff = 128
+    x = np.zeros((1, d), np.float32)
+    x[0, 0] = 1.0
+    rng = np.random.default_rng(7)
+    w1 = np.zeros((d_ff, d), np.float32)
+    w3 = np.zeros((d_ff, d), np.float32)
+    w1[:, 0] = rng.uniform(-4, 4, d_ff).astype(np.float32)
+    w3[:, 0] = rng.uniform(-2, 2, d_ff).astype(np.float32)
+    w1[0, 0] = 0.0
+    w2 = np.eye(d, dtype=np.float32)
+    h, y = oracle.expert_rows(x, w1, w3, w2, "f32")
+    a, g = w1[:, 0].astype(np.float64), w3[:, 0].astype(np.float64)
+    want = np.array([float(np.float32(ai / (1 + math.exp(-ai)) * gi)) for ai, gi in zip(a, g)])
+    assert np.array_equal(h[0], want) and np.array_equal(y[0], want)
+    assert h[0, 0] == 0.0
+
+
+@pytest.mark.parametrize("name", ["tiny_f32", "mid_bf16"])
+def test_expert_rows_vs_blas(name):
+    w = I.WORKLOADS[name].with_tokens(16)
+    u = I.make_u(w)
+    w1, w3, w2 = _weights(w, False, 5)
+    h, y = oracle.expert_rows(u, w1, w3, w2, w.ffn)
+    ref = npref.swiglu_ffn(npref.widen(u, w.act), *_widen_tuple(w, (w1, w3, w2)), _hround(w))
+    assert np.max(np.abs(y - ref)) <= 1e-12 * np.max(np.abs(ref))
+
+
+# ------------------------------------------------------------------ FP8 path
+
+def _grid_block(rng, shape, k):
+    """Random normal E4M3 values with exponents -3..8 times 2^k, with one entry at
+    +-448 * 2^k so that amax / 448 = 2^k exactly (a lossless tile)."""
+    t = oracle.e4m3_table()
+    codes = rng.integers(0x20, 0x7F, shape)
+    vals = t[codes] * np.where(rng.random(shape) < 0.5, -1.0, 1.0)
+    vals.flat[rng.integers(0, vals.size)] = 448.0 * (1 if rng.random() < 0.5 else -1)
+    return vals * 2.0 ** k
+
+
+def test_fp8_lossless_equals_exact_path():
+    """Operands on the E4M3 grid with power-of-two block scales quantise losslessly; with
+    exponents bounded every sum is exact in double, so the FP8 first stage (per-block
+    scale products) must equal the fp32 path bit for bit."""
+    rng = np.random.default_rng(11)
+    d, d_ff, n = 512, 256, 3
+    x = np.array([np.concatenate([_grid_block(rng, (128,), rng.integers(-2, 3))
+                                  for _ in range(d // 128)]) for _ in range(n)])   # 1x128 tiles
+    w1 = np.block([[_grid_block(rng, (128, 128), rng.integers(-2, 3)) for _ in range(d // 128)]
+                   for _ in range(d_ff // 128)]) / 64.0
+    w3 = np.block([[_grid_block(rng, (128, 128), rng.integers(-2, 3)) for _ in range(d // 128)]
+                   for _ in range(d_ff // 128)]) / 64.0
+    w2 = np.zeros((d, d_ff))
+    xb = oracle.bf16_from_double(x)           # exact: grid values fit in bf16
+    assert np.array_equal(npref.widen(xb, "bf16"), x)
+    q1, s1 = oracle.quantize(w1.astype(np.float32), "f32", 128, 128)
+    q3, s3 = oracle.quantize(w3.astype(np.float32), "f32", 128, 128)
+    q2, s2 = oracle.quantize(w2.astype(np.float32), "f32", 128, 128)
+    t = oracle.e4m3_table()
+    assert np.array_equal(t[q1] * np.kron(s1, np.ones((128, 128))), w1)    # lossless
+    h8, _ = oracle.expert_rows(xb, q1, q3, q2, "fp8", s1, s3, s2)
+    h32, _ = oracle.expert_rows(x.astype(np.float32), w1.astype(np.float32), w3.astype(np.float32),
+                                w2.astype(np.float32), "f32")
+    assert np.array_equal(h8, h32)
+
+
+def test_fp8_second_stage_lossless():
+    """One-hot x with large a_j makes SiLU(a) = a exactly in double, so H lies on a scaled
+    E4M3 grid with power-of-two 1x128 scales; then y of the FP8 path equals W2 H of the
+    exact path up to summation order, which pins the H and W2 scale indexing."""
+    rng = np.random.default_rng(12)
+    d, d_ff = 256, 384
+    x = np.zeros((1, d))
+    x[0, 0] = 56.0                            # amax/448 = 1/8 exactly
+    w1 = np.zeros((d_ff, d))
+    w3 = np.zeros((d_ff, d))
+    w1[:, 0] = 1.75                           # a_j = 98 -> sigmoid(a_j) == 1.0 in double
+    for jb in range(d_ff // 128):             # block amax 1.75 -> scale 2^-8
+        col = _grid_block(rng, (128,), 0) / 256.0
+        col[np.argmax(np.abs(col))] = 1.75
+        w3[jb * 128:(jb + 1) * 128, 0] = col
+    w2 = np.block([[_grid_block(rng, (128, 128), rng.integers(-3, 3)) for _ in range(d_ff // 128)]
+                   for _ in range(d // 128)])
+    xb = oracle.bf16_from_double(x)
+    qs = [oracle.quantize(a.astype(np.float32), "f32", 128, 128) for a in (w1, w3, w2)]
+    h8, y8 = oracle.expert_rows(xb, qs[0][0], qs[1][0], qs[2][0], "fp8", qs[0][1], qs[1][1], qs[2][1])
+    h_exact = 98.0 * (56.0 * w3[:, 0])
+    assert np.array_equal(h8[0], h_exact)
+    y_ref = w2 @ h_exact
+    assert np.max(np.abs(y8[0] - y_ref)) <= 1e-13 * np.max(np.abs(y_ref))
+
+
+# ------------------------------------------------------------ the whole layer
+
+def _layer_case(name, T):
+    w = I.WORKLOADS[name]
+    w = w if T is None else w.with_tokens(T)
+    u, e, b = I.make_u(w), I.make_e(w), I.make_b(w)
+    routed = {i: _weights(w, False, i) for i in range(w.n_routed)}
+    shared = [_weights(w, True, j) for j in range(w.n_shared)]
+    res = oracle.layer(u, e, b, routed, shared, top_k=w.top_k, d_ff=w.d_ff, act=w.act, ffn=w.ffn,
+                       want_components=True)
+    return w, u, e, b, routed, shared, res
+
+
+@pytest.mark.parametrize("name,T", [("tiny_f32", None), ("mid_bf16", 24)])
+def test_layer_dense_all_experts(name, T):
+    """Second formulation: every routed expert on every token, with a gate matrix that is
+    zero outside the top-K, plus the shared experts and the residual (BLAS, float64)."""
+    w, u, e, b, routed, shared, res = _layer_case(name, T)
+    dt = I.weight_dtype(w)
+    ref, sel, G = npref.dense_layer(npref.widen(u, w.act), npref.widen(e, w.act), b.astype(np.float64),
+                                    {i: _widen_tuple(w, t) for i, t in routed.items()},
+                                    [_widen_tuple(w, t) for t in shared], w.top_k, _hround(w))
+    assert np.array_equal(res["idx"], sel)
+    scale = np.max(np.abs(ref))
+    assert np.max(np.abs(res["out"] - ref)) <= 1e-12 * scale
+    # the masked per-expert loop gives the same output
+    ref2 = npref.masked_loop_layer(npref.widen(u, w.act), res["idx"], res["gate"],
+                                   {i: _widen_tuple(w, t) for i, t in routed.items()},
+                                   [_widen_tuple(w, t) for t in shared], _hround(w))
+    assert np.max(np.abs(res["out"] - ref2)) <= 1e-12 * scale
+    # components add up to the output
+    recon = npref.widen(u, w.act) + res["shared_sum"] + res["routed_sum"]
+    assert np.max(np.abs(recon - res["out"])) <= 1e-13 * scale
+
+
+def test_layer_single_expert_reduces_to_dense_ffn():
+    """N_r = K = 1: the gate is exactly 1 and the layer is u + shared FFN + one SwiGLU FFN."""
+    base = I.WORKLOADS["tiny_f32"]
+    w = I.Workload("one", T=20, d=256, n_routed=1, top_k=1, n_shared=1, d_ff=128, act="f32",
+                   ffn="f32", seed=99, bias_range=0.0)
+    u, e, b = I.make_u(w), I.make_e(w), I.make_b(w)
+    r0, s0 = _weights(w, False, 0), _weights(w, True, 0)
+    res = oracle.layer(u, e, b, {0: r0}, [s0], top_k=1, d_ff=128, act="f32", ffn="f32")
+    assert np.all(res["gate"] == 1.0) and np.all(res["idx"] == 0)
+    ud = npref.widen(u, "f32")
+    ref = ud + npref.swiglu_ffn(ud, *_widen_tuple(w, s0), npref.round_f32) + \
+        npref.swiglu_ffn(ud, *_widen_tuple(w, r0), npref.round_f32)
+    assert np.max(np.abs(res["out"] - ref)) <= 1e-12 * np.max(np.abs(ref))
+    del base
+
+
+def test_layer_fp8_vs_bf16_close():
+    """The FP8 path on the bf16 tensors stays near the bf16 path (quantisation error only)."""
+    w = I.WORKLOADS["mid_bf16"].with_tokens(4)
+    u, e, b = I.make_u(w), I.make_e(w), I.make_b(w)
+    idx, _, _, _ = oracle.route(u, e, b, w.top_k, w.act)
+    need = sorted(set(idx.ravel().tolist()))
+    routed = {i: _weights(w, False, i) for i in need}
+    shared = [_weights(w, True, j) for j in range(w.n_shared)]
+    ref = oracle.layer(u, e, b, routed, shared, top_k=w.top_k, d_ff=w.d_ff, act="bf16", ffn="bf16",
+                       want_components=True)
+
+    def q(tup):
+        out = [oracle.quantize(a, "bf16", 128, 128) for a in tup]
+        return (out[0][0], out[1][0], out[2][0], out[0][1], out[1][1], out[2][1])
+
+    res = oracle.layer(u, e, b, {i: q(t) for i, t in routed.items()}, [q(t) for t in shared],
+                       top_k=w.top_k, d_ff=w.d_ff, act="bf16", ffn="fp8", want_components=True)
+    assert np.array_equal(res["idx"], ref["idx"])
+    fr = lambda a, r: np.linalg.norm(a - r) / np.linalg.norm(r)
+    # E4M3 keeps 3 fraction bits: a few percent per GEMM stage
+    assert fr(res["routed_sum"], ref["routed_sum"]) < 0.12
+    assert fr(res["shared_sum"], ref["shared_sum"]) < 0.12
+    assert fr(res["out"], ref["out"]) < 0.06
+
+
+def test_layer_thread_count_invariant():
+    """Two oracle runs with 1 and 4 OpenMP threads give bit-identical results."""
+    code = (
+        "import sys, numpy as np; sys.path.insert(0, %r);"
+        "import oracle; from mixture_experts_layer_26_amd import inputs as I;"
+        "w = I.WORKLOADS['mid_bf16'].with_tokens(8);"
+        "u, e, b = I.make_u(w), I.make_e(w), I.make_b(w);"
+        "r = {i: I.make_expert(w, False, i) for i in range(w.n_routed)};"
+        "s = [I.make_expert(w, True, j) for j in range(w.n_shared)];"
+        "res = oracle.layer(u, e, b, r, s, top_k=w.top_k, d_ff=w.d_ff, act=w.act, ffn=w.ffn);"
+        "sys.stdout.write(res['out'].tobytes().hex()[:4096] + str(hash(res['out'].tobytes())))"
+    ) % os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+    outs = []
+    for nt in ("1", "4"):
+        env = dict(os.environ, OMP_NUM_THREADS=nt, PYTHONHASHSEED="0")
+        outs.append(subprocess.check_output([sys.executable, "-c", code], env=env))
+    assert outs[0] == outs[1]
