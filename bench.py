@@ -1,0 +1,176 @@
+#!/usr/bin/env python3
+"""Benchmark of the DeepSeekMoE layer forward pass on one MI355X.
+
+A step is one pass of the whole layer over one batch of synthetic tokens:
+moe_route -> moe_dispatch -> moe_grouped_ffn -> moe_combine -> moe_bias_update, all
+on one HIP stream through the C ABI, with inputs and weights resident in HBM before
+the timed region. The bias carries over from step to step, as the end-of-step rule
+intends. The default workload is the DeepSeek-V3-shaped prefill layer in bf16
+(T=8192, d=7168, 256 routed experts, top-8, 1 shared, d_ff=2048).
+
+Prints one JSON line: whole-layer tokens/s, plus a roofline entry for the grouped
+FFN (the two expert GEMM launches, >99% of the FLOPs) timed with HIP events on the
+launch stream, and the CPU oracle timed on a bounded sample of the same workload.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAKS = {  # MI355X published dense peaks
+    "bf16": 2500.0, "fp8": 5000.0, "f32": 157.3,  # TFLOP/s
+    "hbm": 8000.0,  # GB/s
+}
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def parse():
+    p = argparse.ArgumentParser()
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=20)
+    p.add_argument("--warmup", type=int, default=3)
+    p.add_argument("--workload", default="v3_prefill_bf16")
+    p.add_argument("--cpu-baseline", dest="cpu", action="store_true", default=True)
+    p.add_argument("--no-cpu-baseline", dest="cpu", action="store_false")
+    p.add_argument("--cpu-tokens", type=int, default=0, help="oracle sample size (0 = auto)")
+    return p.parse_args()
+
+
+def setup(wname: str):
+    import torch
+
+    from mixture_experts_layer_26_amd import inputs as I
+    from mixture_experts_layer_26_amd.inputs import device as D
+    from mixture_experts_layer_26_amd.layer import MoeLayer, quantize_experts
+
+    w = I.WORKLOADS[wname]
+    t0 = time.time()
+    dev = D.upload(w, "cuda")
+    L = MoeLayer(w.T, w.d, w.n_routed, w.top_k, w.n_shared, w.d_ff, w.act, w.ffn)
+    if w.ffn == "fp8":
+        routed = quantize_experts(dev["routed"])
+        shared = quantize_experts(dev["shared"]) if dev["shared"] is not None else None
+        dev["routed"], dev["shared"] = None, None
+        torch.cuda.synchronize()
+        torch.cuda.empty_cache()
+        L.set_experts(routed, shared)
+        dev["fp8"] = (routed, shared)
+    else:
+        L.set_experts(dev["routed"], dev["shared"])
+    torch.cuda.synchronize()
+    log(f"[bench] {wname}: inputs generated and resident in {time.time() - t0:.1f} s")
+    return w, dev, L
+
+
+def time_steps(w, dev, L, steps: int, warmup: int):
+    import torch
+
+    stream = torch.cuda.current_stream()
+    bias = dev["b"].clone()
+    for _ in range(warmup):
+        L.step(dev["u"], dev["e"], bias, w.gamma, stream)
+    torch.cuda.synchronize()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+    t0 = time.perf_counter()
+    for i in range(steps):
+        L.route(dev["u"], dev["e"], bias, stream)
+        L.dispatch(stream)
+        ev[i][0].record(stream)
+        L.grouped_ffn(dev["u"], stream)
+        ev[i][1].record(stream)
+        L.combine(dev["u"], stream)
+        L.bias_update(bias, w.gamma, stream)
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    ffn_ms = [a.elapsed_time(b) for a, b in ev]
+    return elapsed, ffn_ms
+
+
+def cpu_baseline(w, n_tokens: int):
+    """The oracle, untuned, on the first n tokens of the same batch (whole layer per token)."""
+    import numpy as np
+
+    import oracle
+    from mixture_experts_layer_26_amd import inputs as I
+
+    u = I.make_u(w, slice(0, n_tokens))
+    e, b = I.make_e(w), I.make_b(w)
+    idx, _, _, _ = oracle.route(u, e, b, w.top_k, w.act)
+    need = sorted(set(idx.ravel().tolist()))
+    routed = {i: I.make_expert(w, False, i) for i in need}
+    shared = [I.make_expert(w, True, j) for j in range(w.n_shared)]
+    if w.ffn == "fp8":
+        def q(t):
+            o = [oracle.quantize(a, "bf16", 128, 128) for a in t]
+            return (o[0][0], o[1][0], o[2][0], o[0][1], o[1][1], o[2][1])
+        routed = {i: q(t) for i, t in routed.items()}
+        shared = [q(t) for t in shared]
+    t0 = time.perf_counter()
+    oracle.layer(u, e, b, routed, shared, top_k=w.top_k, d_ff=w.d_ff, act=w.act, ffn=w.ffn)
+    dt = time.perf_counter() - t0
+    cores = len(os.sched_getaffinity(0))
+    threads = int(os.environ.get("OMP_NUM_THREADS", cores))
+    del np
+    return {"value": n_tokens / dt, "unit": "tokens/s", "cores": min(cores, threads), "kind": "oracle",
+            "sample": f"whole layer (route, {w.top_k}+{w.n_shared} SwiGLU experts, combine) for the first "
+                      f"{n_tokens} tokens of the {w.name} batch, double precision, {dt:.1f} s"}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(json.dumps({"error": "this build runs on one GPU only; --gpus must be 1"}))
+        sys.exit(2)
+    import torch
+
+    assert torch.cuda.is_available(), "bench needs a GPU"
+    from mixture_experts_layer_26_amd import inputs as I  # noqa: F401
+
+    w, dev, L = setup(args.workload)
+    elapsed, ffn_ms = time_steps(w, dev, L, args.steps, args.warmup)
+    ms_step = 1e3 * elapsed / args.steps
+    tok_s = w.T * args.steps / elapsed
+    tflops = w.flops() * args.steps / elapsed / 1e12
+    ffn_avg = sum(ffn_ms) / len(ffn_ms)
+    ffn_tf = w.ffn_flops() / (ffn_avg * 1e-3) / 1e12
+    dt = "fp8" if w.ffn == "fp8" else w.act
+    peak = PEAKS[dt]
+    res = {
+        "metric": "MoE layer tokens/s + TFLOP/s (% MFMA peak), V3 shape bf16/fp8, 1 MI355X",
+        "value": round(tok_s, 1),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": dt,
+        "data": "synthetic (seeded Philox/Box-Muller inputs, random-init expert weights)",
+        "config": {"workload": w.name, "T": w.T, "d": w.d, "n_routed": w.n_routed, "top_k": w.top_k,
+                   "n_shared": w.n_shared, "d_ff": w.d_ff, "act": w.act, "ffn": w.ffn},
+        "layer_tflops": round(tflops, 2),
+        "layer_frac_of_peak": round(tflops / peak, 4),
+        "roofline": {"kernel": "grouped FFN (gate/up GEMM + SwiGLU, down GEMM)", "bound": "mfma",
+                     "achieved": round(ffn_tf, 2), "peak": peak, "unit": "TFLOP/s",
+                     "frac": round(ffn_tf / peak, 4), "traffic": None,
+                     "ms_per_launch": round(ffn_avg, 4)},
+    }
+    if args.cpu:
+        n = args.cpu_tokens or (64 if w.d <= 2048 else 16)
+        res["cpu_baseline"] = cpu_baseline(w, min(n, w.T))
+    print(json.dumps(res), flush=True)
+
+
+if __name__ == "__main__":
+    main()

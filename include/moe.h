@@ -1,0 +1,164 @@
+/*
+ * moe.h - C ABI of the DeepSeekMoE layer forward pass on AMD MI355X (gfx950).
+ *
+ * The layer (DeepSeek-V3 explainer, "DeepSeek-V3 テクニカルレポート 論文解説",
+ * xyznot.com, method section 2 "DeepSeekMoE with auxiliary-loss-free balancing"):
+ *
+ *   h'_t = u_t + sum_{j<N_s} FFN^(s)_j(u_t) + sum_{i<N_r} g_{i,t} FFN^(r)_i(u_t)
+ *   s_{i,t} = Sigmoid(u_t . e_i)
+ *   g'_{i,t} = s_{i,t} if s_{i,t} + b_i is among the K largest of {s_{j,t} + b_j}, else 0
+ *   g_{i,t}  = g'_{i,t} normalised over the selected experts
+ *   end of step: b_i -= gamma if expert i is overloaded, += gamma if underloaded
+ *
+ * FFN_i is the gated SiLU form W2 (SiLU(W1 x) * (W3 x)) with no bias terms. The
+ * optional FP8 path follows the same page's key ideas (E4M3 everywhere, 1x128
+ * activation tiles, 128x128 weight blocks, FP32 accumulation every 128 products)
+ * and the quantisation pseudo-code of "DeepSeek モデルアーキテクチャ徹底解説"
+ * (deepseekmodel.com): scale = amax / 448.
+ *
+ * Conventions for every call:
+ *  - All array pointers are DEVICE pointers, allocated and owned by the caller.
+ *    The library allocates no device memory and keeps no per-call state.
+ *  - `stream` is a hipStream_t passed as void* (NULL = the null stream). Every call
+ *    only enqueues work and returns; calls on one stream run in order. There is no
+ *    device-to-host copy or synchronisation inside any call.
+ *  - Arguments are validated on the host before anything is enqueued; a bad
+ *    argument returns MOE_ERR_INVALID_ARG (or MOE_ERR_UNSUPPORTED / MOE_ERR_WORKSPACE)
+ *    and touches no memory. Kernels trust the index arrays produced by earlier calls.
+ *  - Results are deterministic: the same inputs give bit-identical outputs, counts,
+ *    permutations and biases on every run (no atomics on any result).
+ *  - Row-major layouts throughout; "[A, B]" means A rows of B contiguous elements.
+ */
+#ifndef MOE_H
+#define MOE_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define MOE_ABI_VERSION 1
+
+typedef enum {
+  MOE_OK = 0,
+  MOE_ERR_INVALID_ARG = 1, /* null pointer, bad shape or bad dtype combination   */
+  MOE_ERR_UNSUPPORTED = 2, /* valid request outside what the kernels implement    */
+  MOE_ERR_WORKSPACE = 3,   /* workspace pointer null or smaller than required     */
+  MOE_ERR_HIP = 4          /* a HIP runtime call or kernel launch failed          */
+} moe_status;
+
+typedef enum { MOE_F32 = 0, MOE_BF16 = 1, MOE_FP8_E4M3 = 2 } moe_dtype;
+
+/* Layer shape.
+ *   T        tokens in the batch (>= 1)
+ *   d        hidden size (multiple of 8; multiple of 128 when ffn == MOE_FP8_E4M3)
+ *   n_routed routed experts N_r (1..256)
+ *   top_k    experts per token K (1..min(N_r, 16))
+ *   n_shared shared experts N_s (0..8)
+ *   d_ff     SwiGLU intermediate size per expert (multiple of 64; of 128 for FP8)
+ *   act      dtype of u, the centroids and the output: MOE_F32 or MOE_BF16
+ *   ffn      dtype of the expert GEMM operands: MOE_F32 (with act F32), MOE_BF16 or
+ *            MOE_FP8_E4M3 (both with act BF16) */
+typedef struct {
+  int64_t T;
+  int32_t d, n_routed, top_k, n_shared, d_ff;
+  int32_t act, ffn; /* moe_dtype */
+} moe_shape;
+
+/* Expert weights of one kind (routed: E = n_routed; shared: E = n_shared).
+ *   w1, w3: [E, d_ff, d]  gate and up projections (row j of expert i = output j)
+ *   w2:     [E, d, d_ff]  down projection
+ * Element type: fp32 (ffn F32), bf16 (ffn BF16) or E4M3 codes, one byte each (FP8).
+ * For FP8 the 128x128 block scales (fp32) are
+ *   s1, s3: [E, d_ff/128, d/128]    s2: [E, d/128, d_ff/128]
+ * and NULL otherwise. Weights are quantised once with moe_quantize_fp8(.., 128, 128). */
+typedef struct {
+  const void *w1, *w3, *w2;
+  const float *s1, *s3, *s2;
+} moe_expert_set;
+
+/* ---------------------------------------------------------------------------
+ * moe_route: router of method section 2 (sigmoid affinity, biased top-K, gates).
+ *   u         [T, d]      act dtype
+ *   centroids [N_r, d]    act dtype (the e_i; a bias-free linear gate)
+ *   bias      [N_r]       fp32, the b_i (read only here)
+ *   topk_idx  [T, K]      int32 out: selected expert ids, ascending within a token
+ *   topk_gate [T, K]      fp32 out: g_{i,t} aligned with topk_idx; sums to 1 per token
+ * Logits accumulate in fp32; ties in s + b go to the lower expert index. */
+moe_status moe_route(const moe_shape* shape, const void* u, const void* centroids,
+                     const float* bias, int32_t* topk_idx, float* topk_gate, void* stream);
+
+/* ---------------------------------------------------------------------------
+ * moe_dispatch: the per-expert grouping behind the sums of h'_t (the explainer's
+ * equation; the per-expert token masks of the deepseekmodel.com forward listing):
+ * a stable counting sort of the T*K (token, slot) pairs by expert.
+ *   topk_idx      [T, K]     int32 in (from moe_route)
+ *   expert_count  [N_r]      int32 out: pairs per expert (the expert's load)
+ *   expert_offset [N_r + 1]  int32 out: exclusive prefix sum of expert_count
+ *   sorted_token  [T*K]      int32 out: source token of each sorted row; rows of
+ *                            expert i are [offset[i], offset[i+1]), tokens ascending
+ *   pair_row      [T, K]     int32 out: sorted row of pair (t, k)
+ *   ws            workspace of moe_workspace_bytes(shape, MOE_CALL_DISPATCH) bytes */
+moe_status moe_dispatch(const moe_shape* shape, const int32_t* topk_idx, int32_t* expert_count,
+                        int32_t* expert_offset, int32_t* sorted_token, int32_t* pair_row,
+                        void* ws, size_t ws_bytes, void* stream);
+
+/* ---------------------------------------------------------------------------
+ * moe_grouped_ffn: every routed expert's SwiGLU FFN on its sorted rows, and every
+ * shared expert's on all tokens (the FFN terms of h'_t).
+ *   u             [T, d]       act dtype
+ *   expert_offset [N_r + 1]    from moe_dispatch (read on the device only)
+ *   sorted_token  [T*K]        from moe_dispatch
+ *   routed        N_r experts; shared: N_s experts (may be NULL when N_s == 0)
+ *   y_routed      [T*K, d]     out, act dtype: FFN_i(u_t) for sorted row r of (t, i)
+ *   y_shared      [T, d]       out, fp32: sum over the shared experts (zeros if N_s = 0)
+ *   ws            workspace of moe_workspace_bytes(shape, MOE_CALL_GROUPED_FFN) bytes;
+ *                 holds H (and, for FP8, the 1x128-quantised u and H with their scales)
+ * H is rounded to the GEMM operand type (fp32, bf16; FP8: fp32 then 1x128 E4M3). */
+moe_status moe_grouped_ffn(const moe_shape* shape, const void* u, const int32_t* expert_offset,
+                           const int32_t* sorted_token, const moe_expert_set* routed,
+                           const moe_expert_set* shared, void* y_routed, float* y_shared,
+                           void* ws, size_t ws_bytes, void* stream);
+
+/* ---------------------------------------------------------------------------
+ * moe_combine: h'_t = u_t + shared sum + sum_k g_{k,t} * y_routed[pair_row[t,k]], in
+ * fp32 in that order (experts ascending), rounded once to the act dtype.
+ *   out [T, d] act dtype (may not alias u) */
+moe_status moe_combine(const moe_shape* shape, const void* u, const void* y_routed,
+                       const float* y_shared, const int32_t* pair_row, const float* topk_gate,
+                       void* out, void* stream);
+
+/* ---------------------------------------------------------------------------
+ * moe_bias_update: end-of-step rule of method section 2. With the mean load
+ * T*K/N_r: count_i > mean -> b_i = fl32(b_i - gamma); count_i < mean -> fl32(b_i + gamma);
+ * count_i == mean -> unchanged (the comparison is exact, in integers).
+ *   bias [N_r] fp32, updated in place. Feeds the next step's moe_route. */
+moe_status moe_bias_update(const moe_shape* shape, const int32_t* expert_count, float gamma,
+                           float* bias, void* stream);
+
+/* ---------------------------------------------------------------------------
+ * moe_quantize_fp8: E4M3 tile quantisation (deepseekmodel.com pseudo-code; tile
+ * shapes from the explainer's key ideas). Per tile_r x tile_c tile:
+ *   amax = max|x| (fp32), s = fl32(amax / 448), q = E4M3_RNE(fl32(x / s)) saturating
+ *   at +-448 (OCP E4M3FN codes); s == 0 gives q = 0.
+ *   x [rows, cols] of dtype xt (MOE_F32 or MOE_BF16); rows % tile_r == 0,
+ *   cols % tile_c == 0; (tile_r, tile_c) = (1, 128) or (128, 128).
+ *   q [rows, cols] uint8 out; scale [rows/tile_r, cols/tile_c] fp32 out. */
+moe_status moe_quantize_fp8(const void* x, int32_t xt, int64_t rows, int64_t cols, int32_t tile_r,
+                            int32_t tile_c, uint8_t* q, float* scale, void* stream);
+
+/* workspace sizing: call = MOE_CALL_DISPATCH or MOE_CALL_GROUPED_FFN; 0 for others
+ * and for invalid shapes */
+enum { MOE_CALL_ROUTE = 0, MOE_CALL_DISPATCH = 1, MOE_CALL_GROUPED_FFN = 2,
+       MOE_CALL_COMBINE = 3, MOE_CALL_BIAS_UPDATE = 4 };
+size_t moe_workspace_bytes(const moe_shape* shape, int32_t call);
+
+const char* moe_status_string(moe_status status);
+int32_t moe_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* MOE_H */

@@ -1,0 +1,258 @@
+// C ABI of the MoE layer (include/moe.h): host-side validation, workspace sizing and
+// kernel launches. Validation runs before any HIP call, so a rejected call touches
+// neither the device nor the caller's memory.
+#include "../../include/moe.h"
+
+#include <hip/hip_runtime.h>
+
+#include <mutex>
+
+#include "launch.h"
+
+namespace {
+
+constexpr size_t kAlign = 256;
+
+size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
+
+bool valid_shape(const moe_shape* s) {
+  if (!s) return false;
+  if (s->T < 1 || s->T > (1LL << 26)) return false;
+  if (s->n_routed < 1 || s->n_routed > 256) return false;
+  if (s->top_k < 1 || s->top_k > 16 || s->top_k > s->n_routed) return false;
+  if (s->n_shared < 0 || s->n_shared > 8) return false;
+  if (s->d < 64 || s->d % 64 != 0 || s->d_ff < 64 || s->d_ff % 64 != 0) return false;
+  if (s->T * s->top_k >= (1LL << 31)) return false;
+  const bool f32 = s->act == MOE_F32 && s->ffn == MOE_F32;
+  const bool bf16 = s->act == MOE_BF16 && s->ffn == MOE_BF16;
+  const bool fp8 = s->act == MOE_BF16 && s->ffn == MOE_FP8_E4M3;
+  return f32 || bf16 || fp8;
+}
+
+// shapes the MFMA kernels tile exactly: output columns of the gated phase in 128s, of
+// the down phase in 256s
+bool tiled_shape(const moe_shape* s) {
+  if (s->ffn == MOE_F32) return true;
+  return s->d % 256 == 0 && s->d_ff % 128 == 0;
+}
+
+size_t act_bytes(int dt) { return dt == MOE_F32 ? 4 : 2; }
+
+hipStream_t as_stream(void* p) { return static_cast<hipStream_t>(p); }
+
+moe_status from_hip(hipError_t e) { return e == hipSuccess ? MOE_OK : MOE_ERR_HIP; }
+
+int grid_for_device() {
+  // one persistent workgroup per CU; cached per device
+  static std::mutex mu;
+  static int cus[64] = {0};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+  std::lock_guard<std::mutex> lock(mu);
+  if (cus[dev] == 0) {
+    int n = 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n < 8)
+      n = 256;
+    cus[dev] = n / 8 * 8;
+  }
+  return cus[dev];
+}
+
+struct FfnWorkspace {
+  size_t h_routed, h_shared, q_u, s_u, s_h_routed, s_h_shared, total;
+};
+
+FfnWorkspace ffn_workspace(const moe_shape* s) {
+  FfnWorkspace w{};
+  const int64_t P = s->T * s->top_k;
+  const int64_t Hs = s->T * static_cast<int64_t>(s->n_shared) * s->d_ff;
+  size_t off = 0;
+  if (s->ffn == MOE_FP8_E4M3) {
+    w.q_u = off;
+    off = align_up(off + static_cast<size_t>(s->T) * s->d);
+    w.s_u = off;
+    off = align_up(off + static_cast<size_t>(s->T) * (s->d / 128) * 4);
+    w.h_routed = off;
+    off = align_up(off + static_cast<size_t>(P) * s->d_ff);
+    w.s_h_routed = off;
+    off = align_up(off + static_cast<size_t>(P) * (s->d_ff / 128) * 4);
+    w.h_shared = off;
+    off = align_up(off + static_cast<size_t>(Hs));
+    w.s_h_shared = off;
+    off = align_up(off + static_cast<size_t>(Hs / 128) * 4);
+  } else {
+    const size_t e = act_bytes(s->ffn);
+    w.h_routed = off;
+    off = align_up(off + static_cast<size_t>(P) * s->d_ff * e);
+    w.h_shared = off;
+    off = align_up(off + static_cast<size_t>(Hs) * e);
+  }
+  w.total = off;
+  return w;
+}
+
+}  // namespace
+
+extern "C" {
+
+int32_t moe_abi_version(void) { return MOE_ABI_VERSION; }
+
+const char* moe_status_string(moe_status st) {
+  switch (st) {
+    case MOE_OK: return "ok";
+    case MOE_ERR_INVALID_ARG: return "invalid argument";
+    case MOE_ERR_UNSUPPORTED: return "unsupported shape or dtype";
+    case MOE_ERR_WORKSPACE: return "workspace missing or too small";
+    case MOE_ERR_HIP: return "HIP runtime error";
+  }
+  return "unknown status";
+}
+
+size_t moe_workspace_bytes(const moe_shape* s, int32_t call) {
+  if (!valid_shape(s)) return 0;
+  if (call == MOE_CALL_DISPATCH)
+    return align_up(static_cast<size_t>(moe::dispatch_blocks(s->T)) * s->n_routed * sizeof(int32_t));
+  if (call == MOE_CALL_GROUPED_FFN) return ffn_workspace(s).total;
+  return 0;
+}
+
+moe_status moe_route(const moe_shape* s, const void* u, const void* centroids, const float* bias,
+                     int32_t* topk_idx, float* topk_gate, void* stream) {
+  if (!valid_shape(s) || !u || !centroids || !bias || !topk_idx || !topk_gate)
+    return MOE_ERR_INVALID_ARG;
+  return from_hip(moe::launch_route(s->act == MOE_BF16 ? 1 : 0, u, centroids, bias, s->T, s->d,
+                                    s->n_routed, s->top_k, topk_idx, topk_gate, as_stream(stream)));
+}
+
+moe_status moe_dispatch(const moe_shape* s, const int32_t* topk_idx, int32_t* expert_count,
+                        int32_t* expert_offset, int32_t* sorted_token, int32_t* pair_row, void* ws,
+                        size_t ws_bytes, void* stream) {
+  if (!valid_shape(s) || !topk_idx || !expert_count || !expert_offset || !sorted_token || !pair_row)
+    return MOE_ERR_INVALID_ARG;
+  if (!ws || ws_bytes < moe_workspace_bytes(s, MOE_CALL_DISPATCH)) return MOE_ERR_WORKSPACE;
+  return from_hip(moe::launch_dispatch(topk_idx, s->T, s->top_k, s->n_routed,
+                                       static_cast<int32_t*>(ws), expert_count, expert_offset,
+                                       sorted_token, pair_row, as_stream(stream)));
+}
+
+moe_status moe_grouped_ffn(const moe_shape* s, const void* u, const int32_t* expert_offset,
+                           const int32_t* sorted_token, const moe_expert_set* routed,
+                           const moe_expert_set* shared, void* y_routed, float* y_shared, void* ws,
+                           size_t ws_bytes, void* stream) {
+  if (!valid_shape(s) || !u || !expert_offset || !sorted_token || !routed || !y_routed)
+    return MOE_ERR_INVALID_ARG;
+  if (!routed->w1 || !routed->w3 || !routed->w2) return MOE_ERR_INVALID_ARG;
+  if (s->n_shared > 0 && (!shared || !shared->w1 || !shared->w3 || !shared->w2 || !y_shared))
+    return MOE_ERR_INVALID_ARG;
+  const bool fp8 = s->ffn == MOE_FP8_E4M3;
+  if (fp8 && (!routed->s1 || !routed->s3 || !routed->s2 ||
+              (s->n_shared > 0 && (!shared->s1 || !shared->s3 || !shared->s2))))
+    return MOE_ERR_INVALID_ARG;
+  if (!tiled_shape(s)) return MOE_ERR_UNSUPPORTED;
+  const FfnWorkspace w = ffn_workspace(s);
+  if (!ws || ws_bytes < w.total) return MOE_ERR_WORKSPACE;
+  hipStream_t st = as_stream(stream);
+  unsigned char* wsb = static_cast<unsigned char*>(ws);
+  const int64_t P = s->T * s->top_k;
+
+  if (s->ffn == MOE_F32) {
+    const moe_expert_set empty{};
+    const moe_expert_set* sh = s->n_shared > 0 ? shared : &empty;
+    return from_hip(moe::launch_ffn_f32(
+        static_cast<const float*>(u), expert_offset, sorted_token,
+        static_cast<const float*>(routed->w1), static_cast<const float*>(routed->w3),
+        static_cast<const float*>(routed->w2), static_cast<const float*>(sh->w1),
+        static_cast<const float*>(sh->w3), static_cast<const float*>(sh->w2), s->T, s->d, s->d_ff,
+        s->n_routed, s->top_k, s->n_shared, reinterpret_cast<float*>(wsb + w.h_routed),
+        static_cast<float*>(y_routed), y_shared, st));
+  }
+  if (fp8) return MOE_ERR_UNSUPPORTED;
+
+  const int grid = grid_for_device();
+  uint16_t* h_r = reinterpret_cast<uint16_t*>(wsb + w.h_routed);
+  uint16_t* h_s = reinterpret_cast<uint16_t*>(wsb + w.h_shared);
+  const uint16_t* ub = static_cast<const uint16_t*>(u);
+
+  moe::GemmArgs g1{};
+  g1.a_routed = ub;
+  g1.a_shared = ub;
+  g1.lda_routed = g1.lda_shared = s->d;
+  g1.gather = sorted_token;
+  g1.b1_routed = static_cast<const uint16_t*>(routed->w1);
+  g1.b3_routed = static_cast<const uint16_t*>(routed->w3);
+  g1.b1_shared = s->n_shared > 0 ? static_cast<const uint16_t*>(shared->w1) : nullptr;
+  g1.b3_shared = s->n_shared > 0 ? static_cast<const uint16_t*>(shared->w3) : nullptr;
+  g1.b_expert_stride = static_cast<int64_t>(s->d_ff) * s->d;
+  g1.ldb = s->d;
+  g1.out_routed = h_r;
+  g1.out_shared = h_s;
+  g1.ldo_routed = s->d_ff;
+  g1.ldo_shared = static_cast<int64_t>(s->n_shared) * s->d_ff;
+  g1.offset = expert_offset;
+  g1.n_r = s->n_routed;
+  g1.n_shared_groups = s->n_shared;
+  g1.T = s->T;
+  g1.N = s->d_ff;
+  g1.K = s->d;
+  g1.k_segments = 1;
+  hipError_t err = moe::launch_grouped_gemm_bf16(g1, true, grid, st);
+  if (err != hipSuccess) return MOE_ERR_HIP;
+
+  moe::GemmArgs g2{};
+  g2.a_routed = h_r;
+  g2.a_shared = h_s;
+  g2.lda_routed = s->d_ff;
+  g2.lda_shared = static_cast<int64_t>(s->n_shared) * s->d_ff;
+  g2.gather = nullptr;
+  g2.b1_routed = static_cast<const uint16_t*>(routed->w2);
+  g2.b1_shared = s->n_shared > 0 ? static_cast<const uint16_t*>(shared->w2) : nullptr;
+  g2.b_expert_stride = static_cast<int64_t>(s->d) * s->d_ff;
+  g2.ldb = s->d_ff;
+  g2.out_routed = y_routed;
+  g2.out_shared = y_shared;
+  g2.ldo_routed = s->d;
+  g2.ldo_shared = s->d;
+  g2.offset = expert_offset;
+  g2.n_r = s->n_routed;
+  g2.n_shared_groups = s->n_shared > 0 ? 1 : 0;
+  g2.T = s->T;
+  g2.N = s->d;
+  g2.K = s->d_ff;
+  g2.k_segments = s->n_shared;
+  (void)P;
+  return from_hip(moe::launch_grouped_gemm_bf16(g2, false, grid, st));
+}
+
+moe_status moe_combine(const moe_shape* s, const void* u, const void* y_routed,
+                       const float* y_shared, const int32_t* pair_row, const float* topk_gate,
+                       void* out, void* stream) {
+  if (!valid_shape(s) || !u || !y_routed || !pair_row || !topk_gate || !out)
+    return MOE_ERR_INVALID_ARG;
+  if (s->n_shared > 0 && !y_shared) return MOE_ERR_INVALID_ARG;
+  if (out == u) return MOE_ERR_INVALID_ARG;
+  return from_hip(moe::launch_combine(s->act == MOE_BF16 ? 1 : 0, u, y_routed,
+                                      s->n_shared > 0 ? y_shared : nullptr, pair_row, topk_gate,
+                                      out, s->T, s->d, s->top_k, as_stream(stream)));
+}
+
+moe_status moe_bias_update(const moe_shape* s, const int32_t* expert_count, float gamma,
+                           float* bias, void* stream) {
+  if (!valid_shape(s) || !expert_count || !bias) return MOE_ERR_INVALID_ARG;
+  if (!(gamma >= 0.0f) || gamma > 1.0f) return MOE_ERR_INVALID_ARG;
+  return from_hip(moe::launch_bias_update(expert_count, s->T, s->n_routed, s->top_k, gamma, bias,
+                                          as_stream(stream)));
+}
+
+moe_status moe_quantize_fp8(const void* x, int32_t xt, int64_t rows, int64_t cols, int32_t tile_r,
+                            int32_t tile_c, uint8_t* q, float* scale, void* stream) {
+  if (!x || !q || !scale) return MOE_ERR_INVALID_ARG;
+  if (xt != MOE_F32 && xt != MOE_BF16) return MOE_ERR_INVALID_ARG;
+  if (!((tile_r == 1 && tile_c == 128) || (tile_r == 128 && tile_c == 128)))
+    return MOE_ERR_UNSUPPORTED;
+  if (rows < 1 || cols < 1 || rows % tile_r != 0 || cols % tile_c != 0) return MOE_ERR_INVALID_ARG;
+  if (rows * cols >= (1LL << 40)) return MOE_ERR_INVALID_ARG;
+  return from_hip(moe::launch_quantize_fp8(x, xt, rows, cols, tile_r, tile_c, q, scale,
+                                           as_stream(stream)));
+}
+
+}  // extern "C"

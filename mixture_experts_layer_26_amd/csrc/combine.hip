@@ -1,0 +1,112 @@
+// Combine and bias update.
+//
+// combine: h'_t = u_t + (shared sum)_t + sum_k g_{k,t} * y_routed[pair_row[t,k]], the
+// DeepSeek-V3 explainer's equation for h'_t (method section 2), as a gather over the
+// token's K sorted rows (no atomics), added in fp32 in the order residual, shared,
+// routed experts ascending, and rounded once to the output dtype.
+//
+// bias update: the same section's end-of-step rule, b_i -= gamma when expert i's load
+// is above the mean T*K/N_r, += gamma when below, compared exactly in integers.
+#include "device.h"
+#include "launch.h"
+
+namespace moe {
+
+namespace {
+
+constexpr int kThreads = 256;
+
+template <int ACT>  // 0: fp32 in/out (4 per vector), 1: bf16 (8 per vector)
+__global__ __launch_bounds__(kThreads) void combine_kernel(
+    const void* __restrict__ u, const void* __restrict__ y_routed, const float* __restrict__ y_shared,
+    const int32_t* __restrict__ pair_row, const float* __restrict__ gate, void* __restrict__ out,
+    int64_t T, int d, int K) {
+  constexpr int V = ACT == 1 ? 8 : 4;
+  __shared__ int32_t rows[16];
+  __shared__ float gs[16];
+  const int64_t t = blockIdx.x;
+  if (threadIdx.x < K) {
+    rows[threadIdx.x] = pair_row[t * K + threadIdx.x];
+    gs[threadIdx.x] = gate[t * K + threadIdx.x];
+  }
+  __syncthreads();
+  for (int c0 = threadIdx.x * V; c0 < d; c0 += kThreads * V) {
+    float acc[V];
+    if (ACT == 1) {
+      const uint4 uv = ld16(static_cast<const uint16_t*>(u) + t * d + c0);
+      const uint16_t* up = reinterpret_cast<const uint16_t*>(&uv);
+#pragma unroll
+      for (int q = 0; q < V; ++q) acc[q] = bf16_to_f32(up[q]);
+    } else {
+      const float4 uv = *reinterpret_cast<const float4*>(static_cast<const float*>(u) + t * d + c0);
+      acc[0] = uv.x; acc[1] = uv.y; acc[2] = uv.z; acc[3] = uv.w;
+    }
+    if (y_shared) {
+#pragma unroll
+      for (int q = 0; q < V; q += 4) {
+        const float4 s = *reinterpret_cast<const float4*>(y_shared + t * d + c0 + q);
+        acc[q] += s.x; acc[q + 1] += s.y; acc[q + 2] += s.z; acc[q + 3] += s.w;
+      }
+    }
+    for (int k = 0; k < K; ++k) {
+      const int64_t r = rows[k];
+      const float g = gs[k];
+      if (ACT == 1) {
+        const uint4 yv = ld16(static_cast<const uint16_t*>(y_routed) + r * d + c0);
+        const uint16_t* yp = reinterpret_cast<const uint16_t*>(&yv);
+#pragma unroll
+        for (int q = 0; q < V; ++q) acc[q] = fmaf(g, bf16_to_f32(yp[q]), acc[q]);
+      } else {
+        const float4 yv = *reinterpret_cast<const float4*>(static_cast<const float*>(y_routed) + r * d + c0);
+        acc[0] = fmaf(g, yv.x, acc[0]); acc[1] = fmaf(g, yv.y, acc[1]);
+        acc[2] = fmaf(g, yv.z, acc[2]); acc[3] = fmaf(g, yv.w, acc[3]);
+      }
+    }
+    if (ACT == 1) {
+      uint4 o;
+      o.x = pack_bf16x2(acc[0], acc[1]);
+      o.y = pack_bf16x2(acc[2], acc[3]);
+      o.z = pack_bf16x2(acc[4], acc[5]);
+      o.w = pack_bf16x2(acc[6], acc[7]);
+      st16(static_cast<uint16_t*>(out) + t * d + c0, o);
+    } else {
+      *reinterpret_cast<float4*>(static_cast<float*>(out) + t * d + c0) =
+          make_float4(acc[0], acc[1], acc[2], acc[3]);
+    }
+  }
+}
+
+__global__ void bias_update_kernel(const int32_t* __restrict__ count, int64_t total, int n_r,
+                                   float gamma, float* __restrict__ bias) {
+  const int i = blockIdx.x * blockDim.x + threadIdx.x;
+  if (i >= n_r) return;
+  const int64_t load = static_cast<int64_t>(count[i]) * n_r;
+  if (load > total)
+    bias[i] = bias[i] - gamma;
+  else if (load < total)
+    bias[i] = bias[i] + gamma;
+}
+
+}  // namespace
+
+hipError_t launch_combine(int act, const void* u, const void* y_routed, const float* y_shared,
+                          const int32_t* pair_row, const float* gate, void* out, int64_t T, int d,
+                          int K, hipStream_t stream) {
+  const dim3 grid(static_cast<unsigned>(T));
+  if (act == 1)
+    hipLaunchKernelGGL(combine_kernel<1>, grid, dim3(kThreads), 0, stream, u, y_routed, y_shared,
+                       pair_row, gate, out, T, d, K);
+  else
+    hipLaunchKernelGGL(combine_kernel<0>, grid, dim3(kThreads), 0, stream, u, y_routed, y_shared,
+                       pair_row, gate, out, T, d, K);
+  return hipGetLastError();
+}
+
+hipError_t launch_bias_update(const int32_t* count, int64_t T, int n_r, int K, float gamma,
+                              float* bias, hipStream_t stream) {
+  hipLaunchKernelGGL(bias_update_kernel, dim3((n_r + 255) / 256), dim3(256), 0, stream, count,
+                     T * K, n_r, gamma, bias);
+  return hipGetLastError();
+}
+
+}  // namespace moe

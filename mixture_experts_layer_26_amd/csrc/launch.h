@@ -1,0 +1,64 @@
+// Internal launchers of the gfx950 kernels (host side). Not part of the C ABI.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace moe {
+
+// Arguments of one grouped GEMM launch (phase 1 = gated gate/up, phase 2 = down).
+// Group g < n_r is routed expert g with rows [offset[g], offset[g+1]); groups n_r.. are
+// shared (phase 1: one per shared expert, rows = all T tokens; phase 2: one group whose
+// K runs over all shared experts' H columns, k_segments = n_shared).
+struct GemmArgs {
+  const uint16_t* a_routed;  // phase 1: u [T, d]; phase 2: H routed [P, d_ff]
+  const uint16_t* a_shared;  // phase 1: u; phase 2: H shared [T, n_s * d_ff]
+  int64_t lda_routed, lda_shared;
+  const int32_t* gather;     // phase 1: sorted_token; phase 2: nullptr
+  const uint16_t* b1_routed; // phase 1: W1 [n_r, d_ff, d]; phase 2: W2 [n_r, d, d_ff]
+  const uint16_t* b3_routed; // phase 1: W3; phase 2: unused
+  const uint16_t* b1_shared;
+  const uint16_t* b3_shared;
+  int64_t b_expert_stride;   // elements per expert in the weight arrays
+  int64_t ldb;               // row length of B (the K extent of one expert)
+  void* out_routed;          // phase 1: H routed (bf16); phase 2: y_routed (bf16)
+  void* out_shared;          // phase 1: H shared (bf16); phase 2: y_shared (fp32)
+  int64_t ldo_routed, ldo_shared;
+  const int32_t* offset;     // expert_offset [n_r + 1]
+  int n_r;
+  int n_shared_groups;       // phase 1: n_s; phase 2: 1 if n_s > 0 else 0
+  int64_t T;
+  int N;                     // output columns per group
+  int K;                     // K of one expert
+  int k_segments;            // phase 2 shared: n_s
+};
+
+hipError_t launch_route(int act, const void* u, const void* e, const float* bias, int64_t T, int d,
+                        int n_r, int K, int32_t* idx, float* gate, hipStream_t stream);
+
+int dispatch_blocks(int64_t T);
+hipError_t launch_dispatch(const int32_t* idx, int64_t T, int K, int n_r, int32_t* hist,
+                           int32_t* count, int32_t* offset, int32_t* sorted_token,
+                           int32_t* pair_row, hipStream_t stream);
+
+size_t ffn_bf16_lds_bytes();
+hipError_t launch_grouped_gemm_bf16(const GemmArgs& args, bool gated, int grid, hipStream_t stream);
+
+hipError_t launch_ffn_f32(const float* u, const int32_t* offset, const int32_t* sorted_token,
+                          const float* w1r, const float* w3r, const float* w2r, const float* w1s,
+                          const float* w3s, const float* w2s, int64_t T, int d, int d_ff, int n_r,
+                          int K, int n_s, float* h, float* y_routed, float* y_shared,
+                          hipStream_t stream);
+
+hipError_t launch_combine(int act, const void* u, const void* y_routed, const float* y_shared,
+                          const int32_t* pair_row, const float* gate, void* out, int64_t T, int d,
+                          int K, hipStream_t stream);
+
+hipError_t launch_bias_update(const int32_t* count, int64_t T, int n_r, int K, float gamma,
+                              float* bias, hipStream_t stream);
+
+hipError_t launch_quantize_fp8(const void* x, int xt, int64_t rows, int64_t cols, int tile_r,
+                               int tile_c, uint8_t* q, float* scale, hipStream_t stream);
+
+}  // namespace moe

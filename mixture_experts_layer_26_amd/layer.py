@@ -1,0 +1,91 @@
+"""Device buffers for one layer shape and the five-call step of the C ABI.
+
+A step is: moe_route -> moe_dispatch -> moe_grouped_ffn -> moe_combine ->
+moe_bias_update, all enqueued on one stream with no host synchronisation. The
+bias is the caller's persistent state; the update feeds the next step's routing
+(DeepSeek-V3 explainer, method section 2: the bias moves at the end of each step).
+"""
+from __future__ import annotations
+
+import torch
+
+from . import abi
+
+_TORCH_ACT = {"f32": torch.float32, "bf16": torch.bfloat16}
+
+
+class MoeLayer:
+    def __init__(self, T: int, d: int, n_routed: int, top_k: int, n_shared: int, d_ff: int,
+                 act: str = "bf16", ffn: str = "bf16", device: str = "cuda"):
+        self.T, self.d, self.n_routed, self.top_k = T, d, n_routed, top_k
+        self.n_shared, self.d_ff, self.act, self.ffn = n_shared, d_ff, act, ffn
+        self.device = torch.device(device)
+        self.shape = abi.make_shape(T, d, n_routed, top_k, n_shared, d_ff, act, ffn)
+        adt = _TORCH_ACT[act]
+        dev = self.device
+        i32 = torch.int32
+        self.topk_idx = torch.empty((T, top_k), dtype=i32, device=dev)
+        self.topk_gate = torch.empty((T, top_k), dtype=torch.float32, device=dev)
+        self.expert_count = torch.empty(n_routed, dtype=i32, device=dev)
+        self.expert_offset = torch.empty(n_routed + 1, dtype=i32, device=dev)
+        self.sorted_token = torch.empty(T * top_k, dtype=i32, device=dev)
+        self.pair_row = torch.empty((T, top_k), dtype=i32, device=dev)
+        self.y_routed = torch.empty((T * top_k, d), dtype=adt, device=dev)
+        self.y_shared = torch.empty((T, d), dtype=torch.float32, device=dev) if n_shared > 0 else None
+        self.out = torch.empty((T, d), dtype=adt, device=dev)
+        self.ws_dispatch_bytes = abi.moe_workspace_bytes(self.shape, abi.MOE_CALL_DISPATCH)
+        self.ws_ffn_bytes = abi.moe_workspace_bytes(self.shape, abi.MOE_CALL_GROUPED_FFN)
+        self.ws_dispatch = torch.empty(max(1, self.ws_dispatch_bytes), dtype=torch.uint8, device=dev)
+        self.ws_ffn = torch.empty(max(1, self.ws_ffn_bytes), dtype=torch.uint8, device=dev)
+        self.routed = None
+        self.shared = None
+        self._keep = []
+
+    def set_experts(self, routed: tuple, shared: tuple | None):
+        """routed/shared: (w1, w3, w2) device tensors, or (w1, w3, w2, s1, s3, s2) for FP8."""
+        self._keep = [routed, shared]
+        self.routed = abi.make_expert_set(*routed)
+        self.shared = abi.make_expert_set(*shared) if shared is not None else None
+
+    # -- the five calls ----------------------------------------------------------
+    def route(self, u, centroids, bias, stream=None):
+        abi.moe_route(self.shape, u, centroids, bias, self.topk_idx, self.topk_gate, stream)
+
+    def dispatch(self, stream=None):
+        abi.moe_dispatch(self.shape, self.topk_idx, self.expert_count, self.expert_offset,
+                         self.sorted_token, self.pair_row, self.ws_dispatch, self.ws_dispatch_bytes, stream)
+
+    def grouped_ffn(self, u, stream=None):
+        abi.moe_grouped_ffn(self.shape, u, self.expert_offset, self.sorted_token, self.routed, self.shared,
+                            self.y_routed, self.y_shared, self.ws_ffn, self.ws_ffn_bytes, stream)
+
+    def combine(self, u, stream=None):
+        abi.moe_combine(self.shape, u, self.y_routed, self.y_shared, self.pair_row, self.topk_gate, self.out,
+                        stream)
+
+    def bias_update(self, bias, gamma: float, stream=None):
+        abi.moe_bias_update(self.shape, self.expert_count, gamma, bias, stream)
+
+    def step(self, u, centroids, bias, gamma: float = 0.001, stream=None):
+        """One pass of the whole layer; returns the output buffer (overwritten next step)."""
+        self.route(u, centroids, bias, stream)
+        self.dispatch(stream)
+        self.grouped_ffn(u, stream)
+        self.combine(u, stream)
+        self.bias_update(bias, gamma, stream)
+        return self.out
+
+
+def quantize_experts(ws: tuple, stream=None) -> tuple:
+    """E4M3 codes and 128x128 block scales of stacked expert weights (w1, w3, w2) ->
+    (q1, q3, q2, s1, s3, s2), made by moe_quantize_fp8 on the device."""
+    outs_q, outs_s = [], []
+    for w in ws:
+        E, R, C = w.shape
+        q = torch.empty((E, R, C), dtype=torch.uint8, device=w.device)
+        s = torch.empty((E, R // 128, C // 128), dtype=torch.float32, device=w.device)
+        xt = abi.MOE_BF16 if w.dtype == torch.bfloat16 else abi.MOE_F32
+        abi.moe_quantize_fp8(w, xt, E * R, C, 128, 128, q, s, stream)
+        outs_q.append(q)
+        outs_s.append(s)
+    return tuple(outs_q) + tuple(outs_s)

@@ -61,6 +61,8 @@ def _load():
     lib.orc_layer.argtypes = [i64, i32, i32, i32, i32, i32, i32, i32, vp, vp, vp] + [vp] * 12 + \
         [vp] * 6
     lib.orc_layer.restype = i32
+    lib.orc_combine.argtypes = [i64, i32, i32, i32, vp, vp, vp, vp, vp, vp]
+    lib.orc_combine.restype = None
     for f in (lib.orc_bf16_from_double_array, lib.orc_e4m3_from_float_array,
               lib.orc_quantize_tiles, lib.orc_route, lib.orc_dispatch, lib.orc_bias_update,
               lib.orc_expert_rows):
@@ -225,3 +227,18 @@ def layer(u, e, b, routed: dict, shared: list, *, top_k: int, d_ff: int, act: st
         res["shared_sum"] = ssum
         res["routed_sum"] = rsum
     return res
+
+
+def combine(u, y_shared, y_routed, pair_row, gate, act: str):
+    """out = u + y_shared + sum_k gate * y_routed[pair_row], in double."""
+    dt = _DT[act]
+    u = _act_arr(u, dt)
+    y = _act_arr(y_routed, dt)
+    ysh = None if y_shared is None else _c(y_shared, np.float32)
+    pr = _c(pair_row, np.int32)
+    g = _c(gate, np.float32)
+    n, d = u.shape
+    K = pr.shape[1]
+    out = np.empty((n, d), np.float64)
+    _load().orc_combine(n, d, K, dt, _p(u), _p(ysh), _p(y), _p(pr), _p(g), _p(out))
+    return out

@@ -448,3 +448,19 @@ void orc_e4m3_from_float_array(const float* x, int64_t n, uint8_t* out) {
 #pragma omp parallel for schedule(static)
   for (int64_t i = 0; i < n; ++i) out[i] = orc_e4m3_from_float(x[i]);
 }
+
+/* [V3] method section 2, equation for h'_t, as a combine of precomputed expert
+ * outputs: out_t = u_t + ysh_t + sum_k g_{t,k} y[pair_row[t,k]], in double, in that
+ * order (k ascending = experts ascending). ysh may be NULL (no shared experts). */
+void orc_combine(int64_t n, int d, int K, int act, const void* u, const float* ysh,
+                 const void* y, const int32_t* pair_row, const float* gate, double* out) {
+#pragma omp parallel for schedule(static)
+  for (int64_t t = 0; t < n; ++t)
+    for (int c = 0; c < d; ++c) {
+      double o = load_val(u, act, t * d + c);
+      if (ysh) o += (double)ysh[t * d + c];
+      for (int k = 0; k < K; ++k)
+        o += (double)gate[t * K + k] * load_val(y, act, (int64_t)pair_row[t * K + k] * d + c);
+      out[t * d + c] = o;
+    }
+}

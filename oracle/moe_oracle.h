@@ -91,6 +91,12 @@ int orc_layer(int64_t n, int d, int n_r, int K, int n_s, int d_ff, int act, int 
               double* out, int32_t* idx, double* gate, double* gap,
               double* shared_sum, double* routed_sum);
 
+/* ---- combine of precomputed expert outputs ([V3] method section 2, equation for h'_t)
+ * u [n, d] and y [rows, d] in act dtype; ysh [n, d] fp32 (sum over shared experts, may be
+ * NULL); pair_row [n, K]; gate [n, K] fp32. out [n, d] double. */
+void orc_combine(int64_t n, int d, int K, int act, const void* u, const float* ysh,
+                 const void* y, const int32_t* pair_row, const float* gate, double* out);
+
 #ifdef __cplusplus
 }
 #endif

@@ -508,3 +508,32 @@ def test_layer_thread_count_invariant():
         env = dict(os.environ, OMP_NUM_THREADS=nt, PYTHONHASHSEED="0")
         outs.append(subprocess.check_output([sys.executable, "-c", code], env=env))
     assert outs[0] == outs[1]
+
+
+def test_combine_matches_layer_components():
+    """The standalone combine, fed the layer's own expert outputs, reproduces the layer
+    output (the shared sum is pre-added, so agreement is to rounding order)."""
+    w = I.WORKLOADS["mid_bf16"].with_tokens(6)
+    u, e, b = I.make_u(w), I.make_e(w), I.make_b(w)
+    idx, gate, _, _ = oracle.route(u, e, b, w.top_k, w.act)
+    count, offset, sorted_token, pair_row = oracle.dispatch(idx, w.n_routed)
+    routed = {i: _weights(w, False, i) for i in sorted(set(idx.ravel().tolist()))}
+    shared = [_weights(w, True, j) for j in range(w.n_shared)]
+    res = oracle.layer(u, e, b, routed, shared, top_k=w.top_k, d_ff=w.d_ff, act=w.act, ffn=w.ffn,
+                       want_components=True)
+    # y rows in sorted order, kept exactly (fp32 here so that nothing is rounded away)
+    y = np.zeros((w.pairs, w.d), np.float64)
+    for i, (w1, w3, w2) in routed.items():
+        rows = np.arange(offset[i], offset[i + 1])
+        _, yi = oracle.expert_rows(u[sorted_token[rows]], w1, w3, w2, w.ffn)
+        y[rows] = yi
+    g32 = gate.astype(np.float32)
+    out = oracle.combine(npref.widen(u, w.act).astype(np.float32), res["shared_sum"].astype(np.float32),
+                         y.astype(np.float32), pair_row, g32, "f32")
+    scale = np.max(np.abs(res["out"]))
+    assert np.max(np.abs(out - res["out"])) < 2e-6 * scale
+    # exact check of the order of the sum on values that are exact in fp32
+    ref = npref.widen(u, w.act) + res["shared_sum"].astype(np.float32).astype(np.float64)
+    for k in range(w.top_k):
+        ref = ref + g32[:, k:k + 1].astype(np.float64) * y.astype(np.float32).astype(np.float64)[pair_row[:, k]]
+    assert np.max(np.abs(out - ref)) <= 1e-12 * scale
