@@ -38,6 +38,14 @@ __device__ __forceinline__ float silu(float x) { return x * fast_sigmoid(x); }
 __device__ __forceinline__ uint4 ld16(const void* p) { return *reinterpret_cast<const uint4*>(p); }
 __device__ __forceinline__ void st16(void* p, uint4 v) { *reinterpret_cast<uint4*>(p) = v; }
 
+// Workgroup barrier that orders LDS only: waits for this wave's LDS operations, then
+// s_barrier. Unlike __syncthreads() it does not wait for outstanding global loads, so
+// loads issued for a later K-step stay in flight across it. The memory clobber keeps
+// the compiler from moving memory accesses across the barrier.
+__device__ __forceinline__ void lds_barrier() {
+  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
+
 // XCD-aware ordering: workgroups are dispatched round-robin over the 8 XCDs, so
 // workgroup b runs on XCD b % 8. Returns the index b would have if the grid were
 // split into 8 contiguous chunks, one per XCD (grid must be a multiple of 8).
