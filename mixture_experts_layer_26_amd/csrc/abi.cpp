@@ -59,7 +59,7 @@ int grid_for_device() {
 }
 
 struct FfnWorkspace {
-  size_t h_routed, h_shared, q_u, s_u, s_h_routed, s_h_shared, total;
+  size_t counters, h_routed, h_shared, q_u, s_u, s_h_routed, s_h_shared, total;
 };
 
 FfnWorkspace ffn_workspace(const moe_shape* s) {
@@ -67,6 +67,8 @@ FfnWorkspace ffn_workspace(const moe_shape* s) {
   const int64_t P = s->T * s->top_k;
   const int64_t Hs = s->T * static_cast<int64_t>(s->n_shared) * s->d_ff;
   size_t off = 0;
+  w.counters = off;  // 2 x 8 int32 tile-claim counters (one set per GEMM launch)
+  off = align_up(off + 16 * sizeof(int32_t));
   if (s->ffn == MOE_FP8_E4M3) {
     w.q_u = off;
     off = align_up(off + static_cast<size_t>(s->T) * s->d);
@@ -169,6 +171,8 @@ moe_status moe_grouped_ffn(const moe_shape* s, const void* u, const int32_t* exp
   if (fp8) return MOE_ERR_UNSUPPORTED;
 
   const int grid = grid_for_device();
+  int32_t* counters = reinterpret_cast<int32_t*>(wsb + w.counters);
+  if (moe::launch_zero_i32(counters, 16, st) != hipSuccess) return MOE_ERR_HIP;
   uint16_t* h_r = reinterpret_cast<uint16_t*>(wsb + w.h_routed);
   uint16_t* h_s = reinterpret_cast<uint16_t*>(wsb + w.h_shared);
   const uint16_t* ub = static_cast<const uint16_t*>(u);
@@ -195,6 +199,7 @@ moe_status moe_grouped_ffn(const moe_shape* s, const void* u, const int32_t* exp
   g1.N = s->d_ff;
   g1.K = s->d;
   g1.k_segments = 1;
+  g1.tile_counter = counters;
   hipError_t err = moe::launch_grouped_gemm_bf16(g1, true, grid, st);
   if (err != hipSuccess) return MOE_ERR_HIP;
 
@@ -219,6 +224,7 @@ moe_status moe_grouped_ffn(const moe_shape* s, const void* u, const int32_t* exp
   g2.N = s->d;
   g2.K = s->d_ff;
   g2.k_segments = s->n_shared;
+  g2.tile_counter = counters + 8;
   (void)P;
   return from_hip(moe::launch_grouped_gemm_bf16(g2, false, grid, st));
 }

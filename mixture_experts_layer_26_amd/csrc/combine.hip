@@ -76,6 +76,10 @@ __global__ __launch_bounds__(kThreads) void combine_kernel(
   }
 }
 
+__global__ void zero_i32_kernel(int* __restrict__ p, int n) {
+  for (int i = threadIdx.x; i < n; i += blockDim.x) p[i] = 0;
+}
+
 __global__ void bias_update_kernel(const int32_t* __restrict__ count, int64_t total, int n_r,
                                    float gamma, float* __restrict__ bias) {
   const int i = blockIdx.x * blockDim.x + threadIdx.x;
@@ -99,6 +103,11 @@ hipError_t launch_combine(int act, const void* u, const void* y_routed, const fl
   else
     hipLaunchKernelGGL(combine_kernel<0>, grid, dim3(kThreads), 0, stream, u, y_routed, y_shared,
                        pair_row, gate, out, T, d, K);
+  return hipGetLastError();
+}
+
+hipError_t launch_zero_i32(int* p, int n, hipStream_t stream) {
+  hipLaunchKernelGGL(zero_i32_kernel, dim3(1), dim3(64), 0, stream, p, n);
   return hipGetLastError();
 }
 

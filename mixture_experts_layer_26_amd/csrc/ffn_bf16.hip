@@ -381,15 +381,29 @@ __global__ __launch_bounds__(kThreads) void grouped_gemm_bf16(GemmArgs args) {
   const int wm = wave / WN, wn = wave % WN;
   const int cc = tid % 8, cr = tid / 8;
 
-  // XCD-contiguous walk over the tile list
-  const int per_xcd_slots = gridDim.x / 8;
-  const int xcd = blockIdx.x % 8, slot = blockIdx.x / 8;
+  // Tile claiming: the tile list is cut into 8 contiguous chunks, one per XCD. A
+  // workgroup claims tiles of its own XCD's chunk from that chunk's counter, so the
+  // tiles in flight on an XCD are always neighbours in the list (the same expert's
+  // column tiles and row tiles), whose gathered rows and weights its L2 then serves to
+  // several CUs. When the chunk runs out it helps the other XCDs' chunks. The
+  // counters only decide which CU computes a tile, never what a tile computes.
+  __shared__ int claim;
+  uint32_t xcc;
+  asm volatile("s_getreg_b32 %0, hwreg(HW_REG_XCC_ID)" : "=s"(xcc));
+  xcc &= 7;
   const int chunk = (total + 7) / 8;
-  const int L_begin = xcd * chunk;
-  int L_end = L_begin + chunk;
-  if (L_end > total) L_end = total;
-
-  for (int L = L_begin + slot; L < L_end; L += per_xcd_slots) {
+  int o = 0;
+  while (o < 8) {
+    const int x = (static_cast<int>(xcc) + o) & 7;
+    if (tid == 0) claim = atomicAdd(args.tile_counter + x, 1);
+    __syncthreads();
+    const int local = claim;
+    __syncthreads();
+    const int L = x * chunk + local;
+    if (local >= chunk || L >= total) {
+      ++o;
+      continue;
+    }
     const Tile t = tile_at(tm, L, ng, ntn, args.offset, n_r, args.T, bn_out);
     const bool routed = t.group < n_r;
     const int sg = t.group - n_r;  // shared group index

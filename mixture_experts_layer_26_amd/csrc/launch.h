@@ -32,7 +32,10 @@ struct GemmArgs {
   int N;                     // output columns per group
   int K;                     // K of one expert
   int k_segments;            // phase 2 shared: n_s
+  int* tile_counter;         // 8 zeroed ints: per-XCD tile claim counters
 };
+
+hipError_t launch_zero_i32(int* p, int n, hipStream_t stream);
 
 hipError_t launch_route(int act, const void* u, const void* e, const float* bias, int64_t T, int d,
                         int n_r, int K, int32_t* idx, float* gate, hipStream_t stream);
