@@ -12,7 +12,7 @@ OBJ = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libmoe.so")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
-SOURCES = ["abi.cpp", "route.hip", "dispatch.hip", "ffn_bf16.hip", "ffn_f32.hip", "combine.hip",
+SOURCES = ["abi.cpp", "route.hip", "dispatch.hip", "ffn_bf16.hip", "ffn_fp8.hip", "ffn_f32.hip", "combine.hip",
            "quant.hip"]
 
 # Packed fp32 VALU ops are disabled for all device code.

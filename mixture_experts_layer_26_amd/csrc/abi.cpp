@@ -93,6 +93,93 @@ FfnWorkspace ffn_workspace(const moe_shape* s) {
   return w;
 }
 
+
+// The FP8 expert FFN: u quantised per 1x128 tile into the workspace, then the two
+// FP8 grouped GEMMs (phase 1 also quantises H per 1x128).
+moe_status grouped_ffn_fp8(const moe_shape* s, const void* u, const int32_t* expert_offset,
+                           const int32_t* sorted_token, const moe_expert_set* routed,
+                           const moe_expert_set* shared, void* y_routed, float* y_shared,
+                           unsigned char* wsb, const FfnWorkspace& w, int32_t* counters, int grid,
+                           hipStream_t st) {
+  uint8_t* q_u = wsb + w.q_u;
+  float* s_u = reinterpret_cast<float*>(wsb + w.s_u);
+  uint8_t* h_r = wsb + w.h_routed;
+  uint8_t* h_s = wsb + w.h_shared;
+  float* sh_r = reinterpret_cast<float*>(wsb + w.s_h_routed);
+  float* sh_s = reinterpret_cast<float*>(wsb + w.s_h_shared);
+  const int d = s->d, I = s->d_ff, ns = s->n_shared;
+  if (moe::launch_quantize_fp8(u, MOE_BF16, s->T, d, 1, 128, q_u, s_u, st) != hipSuccess) return MOE_ERR_HIP;
+  auto b = [](const void* p) { return static_cast<const uint16_t*>(p); };
+
+  moe::Fp8Args f1{};
+  f1.g.a_routed = f1.g.a_shared = reinterpret_cast<const uint16_t*>(q_u);
+  f1.g.lda_routed = f1.g.lda_shared = d;
+  f1.g.gather = sorted_token;
+  f1.g.b1_routed = b(routed->w1);
+  f1.g.b3_routed = b(routed->w3);
+  f1.g.b1_shared = ns > 0 ? b(shared->w1) : nullptr;
+  f1.g.b3_shared = ns > 0 ? b(shared->w3) : nullptr;
+  f1.g.b_expert_stride = static_cast<int64_t>(I) * d;
+  f1.g.ldb = d;
+  f1.g.out_routed = h_r;
+  f1.g.out_shared = h_s;
+  f1.g.ldo_routed = I;
+  f1.g.ldo_shared = static_cast<int64_t>(ns) * I;
+  f1.g.offset = expert_offset;
+  f1.g.n_r = s->n_routed;
+  f1.g.n_shared_groups = ns;
+  f1.g.T = s->T;
+  f1.g.N = I;
+  f1.g.K = d;
+  f1.g.k_segments = 1;
+  f1.g.tile_counter = counters;
+  f1.sa_routed = f1.sa_shared = s_u;
+  f1.ldsa_routed = f1.ldsa_shared = d / 128;
+  f1.sb1_routed = routed->s1;
+  f1.sb3_routed = routed->s3;
+  f1.sb1_shared = ns > 0 ? shared->s1 : nullptr;
+  f1.sb3_shared = ns > 0 ? shared->s3 : nullptr;
+  f1.sb_expert_stride = static_cast<int64_t>(I / 128) * (d / 128);
+  f1.kblocks = d / 128;
+  f1.os_routed = sh_r;
+  f1.os_shared = sh_s;
+  f1.ldos_routed = I / 128;
+  f1.ldos_shared = static_cast<int64_t>(ns) * (I / 128);
+  if (moe::launch_grouped_gemm_fp8(f1, true, grid, st) != hipSuccess) return MOE_ERR_HIP;
+
+  moe::Fp8Args f2{};
+  f2.g.a_routed = reinterpret_cast<const uint16_t*>(h_r);
+  f2.g.a_shared = reinterpret_cast<const uint16_t*>(h_s);
+  f2.g.lda_routed = I;
+  f2.g.lda_shared = static_cast<int64_t>(ns) * I;
+  f2.g.gather = nullptr;
+  f2.g.b1_routed = b(routed->w2);
+  f2.g.b1_shared = ns > 0 ? b(shared->w2) : nullptr;
+  f2.g.b_expert_stride = static_cast<int64_t>(d) * I;
+  f2.g.ldb = I;
+  f2.g.out_routed = y_routed;
+  f2.g.out_shared = y_shared;
+  f2.g.ldo_routed = d;
+  f2.g.ldo_shared = d;
+  f2.g.offset = expert_offset;
+  f2.g.n_r = s->n_routed;
+  f2.g.n_shared_groups = ns > 0 ? 1 : 0;
+  f2.g.T = s->T;
+  f2.g.N = d;
+  f2.g.K = I;
+  f2.g.k_segments = ns;
+  f2.g.tile_counter = counters + 8;
+  f2.sa_routed = sh_r;
+  f2.ldsa_routed = I / 128;
+  f2.sa_shared = sh_s;
+  f2.ldsa_shared = static_cast<int64_t>(ns) * (I / 128);
+  f2.sb1_routed = routed->s2;
+  f2.sb1_shared = ns > 0 ? shared->s2 : nullptr;
+  f2.sb_expert_stride = static_cast<int64_t>(d / 128) * (I / 128);
+  f2.kblocks = I / 128;
+  return from_hip(moe::launch_grouped_gemm_fp8(f2, false, grid, st));
+}
+
 }  // namespace
 
 extern "C" {
@@ -168,11 +255,11 @@ moe_status moe_grouped_ffn(const moe_shape* s, const void* u, const int32_t* exp
         s->n_routed, s->top_k, s->n_shared, reinterpret_cast<float*>(wsb + w.h_routed),
         static_cast<float*>(y_routed), y_shared, st));
   }
-  if (fp8) return MOE_ERR_UNSUPPORTED;
-
   const int grid = grid_for_device();
   int32_t* counters = reinterpret_cast<int32_t*>(wsb + w.counters);
   if (moe::launch_zero_i32(counters, 16, st) != hipSuccess) return MOE_ERR_HIP;
+  if (fp8) return grouped_ffn_fp8(s, u, expert_offset, sorted_token, routed, shared, y_routed, y_shared,
+                                  wsb, w, counters, grid, st);
   uint16_t* h_r = reinterpret_cast<uint16_t*>(wsb + w.h_routed);
   uint16_t* h_s = reinterpret_cast<uint16_t*>(wsb + w.h_shared);
   const uint16_t* ub = static_cast<const uint16_t*>(u);

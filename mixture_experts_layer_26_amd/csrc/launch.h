@@ -12,7 +12,7 @@ namespace moe {
 // shared (phase 1: one per shared expert, rows = all T tokens; phase 2: one group whose
 // K runs over all shared experts' H columns, k_segments = n_shared).
 struct GemmArgs {
-  const uint16_t* a_routed;  // phase 1: u [T, d]; phase 2: H routed [P, d_ff]
+  const uint16_t* a_routed;  // phase 1: u [T, d]; phase 2: H routed [P, d_ff] (FP8: byte codes)
   const uint16_t* a_shared;  // phase 1: u; phase 2: H shared [T, n_s * d_ff]
   int64_t lda_routed, lda_shared;
   const int32_t* gather;     // phase 1: sorted_token; phase 2: nullptr
@@ -36,6 +36,28 @@ struct GemmArgs {
 };
 
 hipError_t launch_zero_i32(int* p, int n, hipStream_t stream);
+
+// FP8 grouped GEMM: the codes travel in the GemmArgs pointers (as bytes), the fp32
+// scales here. A-row scales: one per row per 128-wide K block; B scales: one per
+// 128 x 128 block of a weight matrix [E, N/128, K/128].
+struct Fp8Args {
+  GemmArgs g;
+  const float* sa_routed;   // [rows, K/128] (routed A rows, same row index as A)
+  const float* sa_shared;
+  int64_t ldsa_routed, ldsa_shared;
+  const float* sb1_routed;  // phase 1: s1; phase 2: s2
+  const float* sb3_routed;  // phase 1: s3
+  const float* sb1_shared;
+  const float* sb3_shared;
+  int64_t sb_expert_stride; // scales per expert: (N/128) * (K/128)
+  int kblocks;              // K/128 of one expert (scale row length)
+  float* os_routed;         // phase 1: H scales [P, d_ff/128]
+  float* os_shared;         // phase 1: H scales [T, n_s * d_ff/128]
+  int64_t ldos_routed, ldos_shared;
+};
+
+size_t ffn_fp8_lds_bytes();
+hipError_t launch_grouped_gemm_fp8(const Fp8Args& args, bool gated, int grid, hipStream_t stream);
 
 hipError_t launch_route(int act, const void* u, const void* e, const float* bias, int64_t T, int d,
                         int n_r, int K, int32_t* idx, float* gate, hipStream_t stream);

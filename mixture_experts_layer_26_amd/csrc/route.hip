@@ -4,8 +4,8 @@
 // equation for g'_{i,t}; gates normalise g'.
 //
 // One workgroup of 4 waves owns 32 tokens and every expert. Logits come from bf16
-// MFMA 32x32x16 (fp32 accumulate) straight from global memory: each wave takes
-// 32-expert blocks; the 32 x N_r sigmoid scores are parked in LDS, then each wave
+// MFMA 32x32x16 (fp32 accumulate) straight from global memory: each wave takes two
+// 32-expert blocks in one K loop; the 32 x N_r sigmoid scores are parked in LDS, then each wave
 // selects the top-K of 8 tokens with 64-bit (score, ~index) keys reduced across the
 // wave. For fp32 activations the logits are plain fp32 FMA dot products.
 #include "device.h"
@@ -37,58 +37,75 @@ __device__ __forceinline__ uint64_t wave_max_u64(uint64_t x) {
 
 __device__ __forceinline__ float sigmoid_precise(float z) { return 1.0f / (1.0f + expf(-z)); }
 
-// logits of 32 tokens x n_r experts, bf16 inputs, into sc[32][n_r] as sigmoid scores
-__device__ void logits_bf16(const uint16_t* __restrict__ u, const uint16_t* __restrict__ e,
-                            int64_t T, int d, int n_r, int64_t t0, float* sc) {
+// logits of 32 tokens x n_r experts, bf16 inputs, into sc[32][n_r] as sigmoid scores.
+// Wave w owns expert blocks w and w + 4 (32 experts each) and runs both in one K loop,
+// so each u fragment is loaded once per wave. K advances in chunks of KC*16 with the
+// next chunk's loads in flight while the current chunk's MFMAs run.
+template <int KC>
+__device__ void logits_bf16_kc(const uint16_t* __restrict__ u, const uint16_t* __restrict__ e,
+                               int64_t T, int d, int n_r, int64_t t0, float* sc) {
   const int lane = threadIdx.x % kWave, wave = threadIdx.x / kWave;
   const int r = lane % 32, kh = (lane / 32) * 8;
   int64_t trow = t0 + r;
   if (trow >= T) trow = T - 1;
   const uint16_t* ap = u + trow * d + kh;
   const int nblk = (n_r + 31) / 32;
-  for (int eb = wave; eb < nblk; eb += 4) {
-    int erow = eb * 32 + r;
-    if (erow >= n_r) erow = n_r - 1;
-    const uint16_t* bp = e + static_cast<int64_t>(erow) * d + kh;
-    f32x16 acc = {};
-    uint4 a[4], b[4];
+  const bool two = wave + 4 < nblk;
+  if (wave >= nblk) return;
+  int e0 = wave * 32 + r, e1 = (wave + 4) * 32 + r;
+  if (e0 >= n_r) e0 = n_r - 1;
+  if (e1 >= n_r) e1 = n_r - 1;
+  const uint16_t* bp0 = e + static_cast<int64_t>(e0) * d + kh;
+  const uint16_t* bp1 = e + static_cast<int64_t>(two ? e1 : e0) * d + kh;
+  f32x16 acc0 = {}, acc1 = {};
+  uint4 a[KC], b0[KC], b1[KC];
+  auto load = [&](int k0) {
 #pragma unroll
-    for (int s = 0; s < 4; ++s) {
-      a[s] = ld16(ap + s * 16);
-      b[s] = ld16(bp + s * 16);
+    for (int s = 0; s < KC; ++s) {
+      a[s] = ld16(ap + k0 + s * 16);
+      b0[s] = ld16(bp0 + k0 + s * 16);
+      b1[s] = ld16(bp1 + k0 + s * 16);
     }
-    for (int k0 = 0; k0 < d; k0 += 64) {
-      uint4 an[4], bn[4];
-      const bool more = k0 + 64 < d;
-      if (more) {
+  };
+  load(0);
+  for (int k0 = 0; k0 < d; k0 += KC * 16) {
+    uint4 ca[KC], cb0[KC], cb1[KC];
 #pragma unroll
-        for (int s = 0; s < 4; ++s) {
-          an[s] = ld16(ap + k0 + 64 + s * 16);
-          bn[s] = ld16(bp + k0 + 64 + s * 16);
-        }
-      }
-#pragma unroll
-      for (int s = 0; s < 4; ++s)
-        acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a[s]),
-                                                      __builtin_bit_cast(bf16x8, b[s]), acc, 0, 0, 0);
-      if (more) {
-#pragma unroll
-        for (int s = 0; s < 4; ++s) {
-          a[s] = an[s];
-          b[s] = bn[s];
-        }
-      }
+    for (int s = 0; s < KC; ++s) {
+      ca[s] = a[s];
+      cb0[s] = b0[s];
+      cb1[s] = b1[s];
     }
-    // C layout of 32x32 MFMA: lane holds column (expert) lane%32, rows 8*(v/4)+4*(lane/32)+v%4
-    const int j = eb * 32 + (lane % 32);
+    if (k0 + KC * 16 < d) load(k0 + KC * 16);
+#pragma unroll
+    for (int s = 0; s < KC; ++s) {
+      acc0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, ca[s]),
+                                                     __builtin_bit_cast(bf16x8, cb0[s]), acc0, 0, 0, 0);
+      acc1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, ca[s]),
+                                                     __builtin_bit_cast(bf16x8, cb1[s]), acc1, 0, 0, 0);
+    }
+  }
+  // C layout of 32x32 MFMA: lane holds column (expert) lane%32, rows 8*(v/4)+4*(lane/32)+v%4
+#pragma unroll
+  for (int blk = 0; blk < 2; ++blk) {
+    if (blk == 1 && !two) break;
+    const int j = (wave + 4 * blk) * 32 + (lane % 32);
     if (j < n_r) {
 #pragma unroll
       for (int v = 0; v < 16; ++v) {
         const int i = 8 * (v / 4) + 4 * (lane / 32) + (v % 4);
-        sc[i * n_r + j] = sigmoid_precise(acc[v]);
+        sc[i * n_r + j] = sigmoid_precise(blk == 0 ? acc0[v] : acc1[v]);
       }
     }
   }
+}
+
+__device__ void logits_bf16(const uint16_t* __restrict__ u, const uint16_t* __restrict__ e,
+                            int64_t T, int d, int n_r, int64_t t0, float* sc) {
+  if (d % 128 == 0)
+    logits_bf16_kc<8>(u, e, T, d, n_r, t0, sc);
+  else
+    logits_bf16_kc<4>(u, e, T, d, n_r, t0, sc);
 }
 
 __device__ void logits_f32(const float* __restrict__ u, const float* __restrict__ e, int64_t T,

@@ -1,0 +1,158 @@
+"""GPU parity of the FP8 E4M3 path against the CPU oracle (needs an MI355X).
+
+Quantisation of inputs (weights in 128x128 blocks, activations in 1x128 tiles) is
+deterministic, so the GPU's codes and scales must equal the oracle's bit for bit.
+The FP8 layer output is compared with the oracle applying the identical
+quantisation, within the layer tolerance.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from mixture_experts_layer_26_amd import abi
+from mixture_experts_layer_26_amd import inputs as I
+from mixture_experts_layer_26_amd.layer import MoeLayer, quantize_experts
+from tests.gpu_util import (FROB_TOL, MAXABS_TOL, check_routing, log, rel_errors, sample_tokens, to_dev,
+                            to_np, workload_on_device)
+
+pytestmark = pytest.mark.gpu
+
+
+def _gpu_quantize(x: np.ndarray, xt: str, tr: int, tc: int):
+    rows, cols = x.shape
+    xd = to_dev(x, bf16=(xt == "bf16"))
+    q = torch.empty((rows, cols), dtype=torch.uint8, device="cuda")
+    s = torch.empty((rows // tr, cols // tc), dtype=torch.float32, device="cuda")
+    abi.moe_quantize_fp8(xd, abi.MOE_BF16 if xt == "bf16" else abi.MOE_F32, rows, cols, tr, tc, q, s)
+    torch.cuda.synchronize()
+    return to_np(q), to_np(s)
+
+
+@pytest.mark.parametrize("tiles", [(128, 128), (1, 128)])
+@pytest.mark.parametrize("xt", ["bf16", "f32"])
+def test_quantize_parity(tiles, xt):
+    tr, tc = tiles
+    rng = np.random.default_rng(5)
+    x = (rng.standard_normal((384, 640)) * np.exp2(rng.integers(-12, 6, (384, 1)))).astype(np.float32)
+    x[0:128, 0:128] = 0.0                                  # an all-zero tile
+    x[200, 300] = 3.0e-40                                   # a subnormal input
+    x[130:140, 256:384] = np.float32(448.0) * 2.0 ** -20   # flat tile
+    if xt == "bf16":
+        x = oracle.bf16_from_double(x.astype(np.float64))
+    q, s = _gpu_quantize(x, xt, tr, tc)
+    qr, sr = oracle.quantize(x, xt, tr, tc)
+    assert np.array_equal(s.view(np.uint32), sr.view(np.uint32))
+    assert np.array_equal(q, qr)
+
+
+@pytest.mark.slow
+def test_e4m3_conversion_exhaustive():
+    """Every non-negative float32 up to 448 (and its negative) through the GPU
+    quantiser with a unit scale: rows of 127 values plus one 448, so amax / 448 = 1
+    and the codes are the plain E4M3 rounding, compared with the oracle's encoder."""
+    top = int(np.float32(448.0).view(np.uint32))
+    per_row = 127
+    chunk_rows = 1 << 19
+    start = 0
+    checked = 0
+    while start <= top:
+        n = min(chunk_rows * per_row, top + 1 - start)
+        bits = np.arange(start, start + n, dtype=np.uint64).astype(np.uint32)
+        rows = (n + per_row - 1) // per_row
+        vals = np.zeros(rows * per_row, np.float32)
+        vals[:n] = bits.view(np.float32)
+        for sign in (1.0, -1.0):
+            x = np.empty((rows, 128), np.float32)
+            x[:, 0] = 448.0
+            x[:, 1:] = sign * vals.reshape(rows, per_row)
+            q, s = _gpu_quantize(x, "f32", 1, 128)
+            assert np.all(s == 1.0)
+            want = oracle.e4m3_from_float(x[:, 1:].ravel()[:n])
+            got = q[:, 1:].ravel()[:n]
+            bad = np.nonzero(got != want)[0]
+            assert bad.size == 0, (sign, hex(int(bits[bad[0]])), got[bad[0]], want[bad[0]])
+        checked += n
+        start += n
+    log(f"[e4m3] {checked} magnitudes, both signs: GPU conversion equals the oracle")
+
+
+def _fp8_setup(base: str, T=None):
+    """Device FP8 weights made by the library from the bf16 tensors of workload `base`
+    (the FP8 workloads share their tensors with a bf16 one)."""
+    _, dev = workload_on_device(base, T)
+    key = "_fp8_"
+    if key not in dev:
+        routed = quantize_experts(dev["routed"])
+        shared = quantize_experts(dev["shared"]) if dev["shared"] is not None else None
+        torch.cuda.synchronize()
+        dev[key] = (routed, shared)
+    return dev, dev[key]
+
+
+def _q_host(tup):
+    out = [oracle.quantize(a, "bf16", 128, 128) for a in tup]
+    return (out[0][0], out[1][0], out[2][0], out[0][1], out[1][1], out[2][1])
+
+
+def test_fp8_weight_codes_match_oracle():
+    w = I.WORKLOADS["v3_prefill_fp8"]
+    dev, (routed, shared) = _fp8_setup("v3_prefill_bf16")
+    for i in (0, 77, 255):
+        want = _q_host(I.make_expert(w, False, i))
+        for j in range(6):
+            assert np.array_equal(to_np(routed[j][i]), want[j]), (i, j)
+    want = _q_host(I.make_expert(w, True, 0))
+    for j in range(6):
+        assert np.array_equal(to_np(shared[j][0]), want[j])
+
+
+def _layer(w):
+    return MoeLayer(w.T, w.d, w.n_routed, w.top_k, w.n_shared, w.d_ff, w.act, w.ffn)
+
+
+@pytest.mark.parametrize("base,T", [("mid_bf16", 512), ("v3_prefill_bf16", None)])
+def test_fp8_layer_end_to_end(base, T):
+    """The V3 prefill workload in FP8, and the mid shape in FP8 (d = 2048, d_ff = 1408,
+    two shared experts, ragged 11-block d_ff), on the tensors of the bf16 workloads."""
+    wb = I.WORKLOADS[base]
+    w = I.Workload(wb.name.replace("bf16", "fp8"), T=wb.T, d=wb.d, n_routed=wb.n_routed, top_k=wb.top_k,
+                   n_shared=wb.n_shared, d_ff=wb.d_ff, act="bf16", ffn="fp8", seed=wb.seed,
+                   bias_range=wb.bias_range)
+    if T is not None:
+        w = w.with_tokens(T)
+    dev, (routed, shared) = _fp8_setup(base, T)
+    L = _layer(w)
+    L.set_experts(routed, shared)
+    bias = dev["b"].clone()
+    L.step(dev["u"], dev["e"], bias, w.gamma)
+    torch.cuda.synchronize()
+    u = I.make_u(w)
+    e, b = I.make_e(w), I.make_b(w)
+    idx, gate, gap, v = oracle.route(u, e, b, w.top_k, w.act, want_v=True)
+    diff, n_exempt = check_routing(to_np(L.topk_idx), to_np(L.topk_gate), idx, gate, gap, v, w.top_k)
+    tok = np.setdiff1d(sample_tokens(w.T, 12 if w.d > 4096 else 48), diff)
+    idx_s, _, _, _ = oracle.route(u[tok], e, b, w.top_k, w.act)
+    need = sorted(set(idx_s.ravel().tolist()))
+    r_host = {i: _q_host(I.make_expert(w, False, i)) for i in need}
+    s_host = [_q_host(I.make_expert(w, True, j)) for j in range(w.n_shared)]
+    res = oracle.layer(u[tok], e, b, r_host, s_host, top_k=w.top_k, d_ff=w.d_ff, act="bf16", ffn="fp8",
+                       want_components=True)
+    out = I.bf16_bits_to_f32(to_np(L.out[torch.from_numpy(tok).cuda()]))
+    frob, mx = rel_errors(out, res["out"])
+    ysh = to_np(L.y_shared[torch.from_numpy(tok).cuda()])
+    f2, m2 = rel_errors(ysh, res["shared_sum"])
+    log(f"[fp8 e2e] {w.name}: tokens {tok.size} exempt {n_exempt} out frob {frob:.2e} maxabs {mx:.2e}; "
+        f"shared frob {f2:.2e}")
+    assert frob <= FROB_TOL and mx <= MAXABS_TOL
+    assert f2 <= FROB_TOL and m2 <= MAXABS_TOL
+    # routed rows of the sampled tokens, one by one, against the oracle's FP8 FFN
+    pr = to_np(L.pair_row)[tok]
+    y_gpu = I.bf16_bits_to_f32(to_np(L.y_routed[torch.from_numpy(pr.ravel()).cuda()]))
+    y_ref = np.empty_like(y_gpu, dtype=np.float64)
+    sel = to_np(L.topk_idx)[tok]
+    for j, (t, row) in enumerate(zip(np.repeat(tok, w.top_k), sel.ravel())):
+        y_ref[j] = oracle.expert_rows(u[t:t + 1], *r_host[int(row)][:3], "fp8", *r_host[int(row)][3:])[1][0]
+    f3, m3 = rel_errors(y_gpu, y_ref)
+    log(f"[fp8 ffn] {w.name}: routed rows {y_gpu.shape[0]} frob {f3:.2e} maxabs {m3:.2e}")
+    assert f3 <= FROB_TOL and m3 <= MAXABS_TOL
