@@ -42,7 +42,34 @@ def parse():
     p.add_argument("--cpu-baseline", dest="cpu", action="store_true", default=True)
     p.add_argument("--no-cpu-baseline", dest="cpu", action="store_false")
     p.add_argument("--cpu-tokens", type=int, default=0, help="oracle sample size (0 = auto)")
+    p.add_argument("--calibrate-copy", action="store_true",
+                   help="also run one plain 1 GiB device copy (the reference for FETCH_SIZE/WRITE_SIZE)")
     return p.parse_args()
+
+
+def kernel_source_hash() -> str:
+    """Hash of the grouped-FFN kernel sources; a stored traffic measurement is used only
+    while the kernels it was taken on are unchanged."""
+    import hashlib
+    h = hashlib.sha256()
+    csrc = os.path.join(ROOT, "mixture_experts_layer_26_amd", "csrc")
+    for f in ("gemm_common.h", "ffn_bf16.hip", "ffn_fp8.hip", "device.h"):
+        with open(os.path.join(csrc, f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def stored_traffic(workload: str):
+    """HBM bytes per grouped-FFN call from the committed counter runs (profiles/), or
+    None when absent or taken on other kernel sources."""
+    path = os.path.join(ROOT, "profiles", f"traffic_{workload}.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        t = json.load(f)
+    if t.get("kernel_source_hash") != kernel_source_hash():
+        return None
+    return t
 
 
 def setup(wname: str):
@@ -95,6 +122,49 @@ def time_steps(w, dev, L, steps: int, warmup: int):
     return elapsed, ffn_ms
 
 
+def call_breakdown(w, dev, L, steps: int = 3):
+    """Average milliseconds of each ABI call (HIP events on the launch stream)."""
+    import torch
+
+    stream = torch.cuda.current_stream()
+    bias = dev["b"].clone()
+    names = ["route", "dispatch", "grouped_ffn", "combine", "bias_update"]
+    acc = dict.fromkeys(names, 0.0)
+    for _ in range(steps):
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(len(names) + 1)]
+        ev[0].record(stream)
+        L.route(dev["u"], dev["e"], bias, stream)
+        ev[1].record(stream)
+        L.dispatch(stream)
+        ev[2].record(stream)
+        L.grouped_ffn(dev["u"], stream)
+        ev[3].record(stream)
+        L.combine(dev["u"], stream)
+        ev[4].record(stream)
+        L.bias_update(bias, w.gamma, stream)
+        ev[5].record(stream)
+        torch.cuda.synchronize()
+        for i, n in enumerate(names):
+            acc[n] += ev[i].elapsed_time(ev[i + 1])
+    return {n: round(v / steps, 4) for n, v in acc.items()}
+
+
+def ffn_algorithmic_bytes(w, L) -> float:
+    """Bytes the grouped FFN must move at least once: the weights of every expert that
+    received a row (plus the shared experts) and scales for FP8, the activations read
+    (u) and the outputs written (y_routed, y_shared). H is an intermediate and is not
+    counted."""
+    counts = L.expert_count.cpu().numpy()
+    active = int((counts > 0).sum())
+    wbytes = 1 if w.ffn == "fp8" else (4 if w.ffn == "f32" else 2)
+    per_expert = 3 * w.d * w.d_ff * wbytes
+    if w.ffn == "fp8":
+        per_expert += 3 * (w.d // 128) * (w.d_ff // 128) * 4
+    abytes = 4 if w.act == "f32" else 2
+    io = w.T * w.d * abytes + w.pairs * w.d * abytes + (w.T * w.d * 4 if w.n_shared else 0)
+    return (active + w.n_shared) * per_expert + io, active
+
+
 def cpu_baseline(w, n_tokens: int):
     """The oracle, untuned, on the first n tokens of the same batch (whole layer per token)."""
     import numpy as np
@@ -136,14 +206,37 @@ def main():
     from mixture_experts_layer_26_amd import inputs as I  # noqa: F401
 
     w, dev, L = setup(args.workload)
+    if args.calibrate_copy:
+        src = torch.empty(1 << 30, dtype=torch.uint8, device="cuda")
+        dst = torch.empty_like(src)
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
     elapsed, ffn_ms = time_steps(w, dev, L, args.steps, args.warmup)
+    calls = call_breakdown(w, dev, L)
     ms_step = 1e3 * elapsed / args.steps
     tok_s = w.T * args.steps / elapsed
     tflops = w.flops() * args.steps / elapsed / 1e12
     ffn_avg = sum(ffn_ms) / len(ffn_ms)
     ffn_tf = w.ffn_flops() / (ffn_avg * 1e-3) / 1e12
     dt = "fp8" if w.ffn == "fp8" else w.act
-    peak = PEAKS[dt]
+    abytes, active = ffn_algorithmic_bytes(w, L)
+    traffic = stored_traffic(w.name)
+    decode = w.T * w.top_k < 32 * w.n_routed  # under one MFMA block of rows per expert: weight streaming
+    if decode:
+        gbs = abytes / (ffn_avg * 1e-3) / 1e9
+        roof = {"bound": "hbm", "achieved": round(gbs, 1), "peak": PEAKS["hbm"], "unit": "GB/s",
+                "frac": round(gbs / PEAKS["hbm"], 4)}
+    else:
+        roof = {"bound": "mfma", "achieved": round(ffn_tf, 2), "peak": PEAKS[dt], "unit": "TFLOP/s",
+                "frac": round(ffn_tf / PEAKS[dt], 4)}
+    roof.update({"traffic": traffic["hbm_bytes_per_call"] if traffic else None,
+                 "kernel": "grouped FFN (gate/up GEMM + SwiGLU, down GEMM)",
+                 "ms_per_launch": round(ffn_avg, 4),
+                 "algorithmic_bytes": abytes, "algorithmic_flops": w.ffn_flops(),
+                 "ffn_tflops": round(ffn_tf, 2),
+                 "ffn_hbm_gbs": round(abytes / (ffn_avg * 1e-3) / 1e9, 1),
+                 "active_experts": active})
     res = {
         "metric": "MoE layer tokens/s + TFLOP/s (% MFMA peak), V3 shape bf16/fp8, 1 MI355X",
         "value": round(tok_s, 1),
@@ -160,14 +253,12 @@ def main():
         "config": {"workload": w.name, "T": w.T, "d": w.d, "n_routed": w.n_routed, "top_k": w.top_k,
                    "n_shared": w.n_shared, "d_ff": w.d_ff, "act": w.act, "ffn": w.ffn},
         "layer_tflops": round(tflops, 2),
-        "layer_frac_of_peak": round(tflops / peak, 4),
-        "roofline": {"kernel": "grouped FFN (gate/up GEMM + SwiGLU, down GEMM)", "bound": "mfma",
-                     "achieved": round(ffn_tf, 2), "peak": peak, "unit": "TFLOP/s",
-                     "frac": round(ffn_tf / peak, 4), "traffic": None,
-                     "ms_per_launch": round(ffn_avg, 4)},
+        "layer_frac_of_peak": round(tflops / PEAKS[dt], 4),
+        "call_ms": calls,
+        "roofline": roof,
     }
     if args.cpu:
-        n = args.cpu_tokens or (64 if w.d <= 2048 else 16)
+        n = args.cpu_tokens or (512 if w.d <= 2048 else 192)
         res["cpu_baseline"] = cpu_baseline(w, min(n, w.T))
     print(json.dumps(res), flush=True)
 
