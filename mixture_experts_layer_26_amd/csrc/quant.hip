@@ -11,10 +11,6 @@ namespace moe {
 
 namespace {
 
-__device__ __forceinline__ float load_elem(const void* x, int xt, int64_t i) {
-  return xt == 1 ? bf16_to_f32(static_cast<const uint16_t*>(x)[i]) : static_cast<const float*>(x)[i];
-}
-
 __device__ __forceinline__ uint32_t e4m3_pair(float a, float b) {
   a = fminf(fmaxf(a, -448.0f), 448.0f);
   b = fminf(fmaxf(b, -448.0f), 448.0f);
@@ -27,50 +23,102 @@ __device__ __forceinline__ float wave_max(float v) {
   return v;
 }
 
-// 1 x 128 tiles: one wave per tile, two elements per lane
-__global__ __launch_bounds__(256) void quant_row_tiles(const void* __restrict__ x, int xt,
-                                                       int64_t rows, int64_t cols,
-                                                       uint8_t* __restrict__ q,
-                                                       float* __restrict__ scale) {
-  const int lane = threadIdx.x % kWave;
-  const int64_t tile = blockIdx.x * 4LL + threadIdx.x / kWave;
-  const int64_t tiles_per_row = cols / 128;
-  if (tile >= rows * tiles_per_row) return;
-  const int64_t r = tile / tiles_per_row, cb = tile % tiles_per_row;
-  const int64_t base = r * cols + cb * 128 + 2 * lane;
-  const float a = load_elem(x, xt, base), b = load_elem(x, xt, base + 1);
-  const float amax = wave_max(fmaxf(fabsf(a), fabsf(b)));
-  const float s = amax / 448.0f;
-  uint32_t pair = 0;
-  if (s != 0.0f) pair = e4m3_pair(a / s, b / s);
-  *reinterpret_cast<uint16_t*>(q + base) = static_cast<uint16_t>(pair);
-  if (lane == 0) scale[tile] = s;
+// 16 bytes of x at element index i as floats: 8 bf16 or 4 fp32 values
+template <int XT>
+__device__ __forceinline__ void load_chunk(const void* x, int64_t i, float* v) {
+  const uint4 raw = XT == 1 ? ld16(static_cast<const uint16_t*>(x) + i) : ld16(static_cast<const float*>(x) + i);
+  if (XT == 1) {
+    const uint32_t w[4] = {raw.x, raw.y, raw.z, raw.w};
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      v[2 * k] = __uint_as_float(w[k] << 16);
+      v[2 * k + 1] = __uint_as_float(w[k] & 0xFFFF0000u);
+    }
+  } else {
+    v[0] = __uint_as_float(raw.x); v[1] = __uint_as_float(raw.y);
+    v[2] = __uint_as_float(raw.z); v[3] = __uint_as_float(raw.w);
+  }
 }
 
-// 128 x 128 tiles: one workgroup of 256 threads per tile
-__global__ __launch_bounds__(256) void quant_block_tiles(const void* __restrict__ x, int xt,
-                                                         int64_t rows, int64_t cols,
-                                                         uint8_t* __restrict__ q,
-                                                         float* __restrict__ scale) {
+// E4M3 codes of n = 8 (bf16) or 4 (fp32) values, packed little-endian
+template <int N>
+__device__ __forceinline__ uint64_t codes(const float* v, float s) {
+  uint64_t out = 0;
+#pragma unroll
+  for (int k = 0; k < N; k += 2) {
+    const uint32_t pair = s == 0.0f ? 0u : e4m3_pair(v[k] / s, v[k + 1] / s);
+    out |= static_cast<uint64_t>(pair) << (8 * k);
+  }
+  return out;
+}
+
+// 1 x 128 tiles: a group of G lanes (16 for bf16, 32 for fp32) covers one tile with one
+// 16-byte load each; the tile's amax is reduced across the group.
+template <int XT>
+__global__ __launch_bounds__(256) void quant_row_tiles(const void* __restrict__ x, int64_t rows, int64_t cols,
+                                                       uint8_t* __restrict__ q, float* __restrict__ scale) {
+  constexpr int E = XT == 1 ? 8 : 4;  // elements per lane
+  constexpr int G = 128 / E;          // lanes per tile
+  const int64_t tiles = rows * (cols / 128);
+  const int64_t tile = (blockIdx.x * 256LL + threadIdx.x) / G;
+  const int gl = threadIdx.x % G;
+  const bool live = tile < tiles;
+  const int64_t r = live ? tile / (cols / 128) : 0, cb = live ? tile % (cols / 128) : 0;
+  const int64_t base = r * cols + cb * 128 + gl * E;
+  float v[E];
+  if (live) load_chunk<XT>(x, base, v);
+  float m = 0.0f;
+#pragma unroll
+  for (int k = 0; k < E; ++k) m = fmaxf(m, live ? fabsf(v[k]) : 0.0f);
+#pragma unroll
+  for (int off = 1; off < G; off <<= 1) m = fmaxf(m, __shfl_xor(m, off, kWave));
+  if (!live) return;
+  const float s = m / 448.0f;
+  const uint64_t c = codes<E>(v, s);
+  if (E == 8)
+    *reinterpret_cast<uint64_t*>(q + base) = c;
+  else
+    *reinterpret_cast<uint32_t*>(q + base) = static_cast<uint32_t>(c);
+  if (gl == 0) scale[tile] = s;
+}
+
+// 128 x 128 tiles: one workgroup of 256 threads per tile; each thread holds 64 values
+// (16-byte chunks of 8 rows), the amax is reduced across the workgroup.
+template <int XT>
+__global__ __launch_bounds__(256) void quant_block_tiles(const void* __restrict__ x, int64_t rows, int64_t cols,
+                                                         uint8_t* __restrict__ q, float* __restrict__ scale) {
+  constexpr int E = XT == 1 ? 8 : 4;  // elements per chunk
+  constexpr int CPR = 128 / E;        // chunks per tile row
+  constexpr int RPP = 256 / CPR;      // rows covered per pass
+  constexpr int NP = 128 / RPP;       // passes
   __shared__ float wmax[4];
   const int64_t nbc = cols / 128;
   const int64_t br = blockIdx.x / nbc, bc = blockIdx.x % nbc;
   const int tid = threadIdx.x;
-  // thread covers row (tid / 2) and columns 64 * (tid % 2) .. +64
-  const int64_t r = br * 128 + tid / 2;
-  const int64_t c0 = bc * 128 + 64 * (tid % 2);
+  const int cc = tid % CPR, rr = tid / CPR;
+  float v[NP][E];
   float m = 0.0f;
-  for (int j = 0; j < 64; ++j) m = fmaxf(m, fabsf(load_elem(x, xt, r * cols + c0 + j)));
+#pragma unroll
+  for (int p = 0; p < NP; ++p) {
+    const int64_t row = br * 128 + rr + RPP * p;
+    load_chunk<XT>(x, row * cols + bc * 128 + cc * E, v[p]);
+#pragma unroll
+    for (int k = 0; k < E; ++k) m = fmaxf(m, fabsf(v[p][k]));
+  }
   m = wave_max(m);
   if (tid % kWave == 0) wmax[tid / kWave] = m;
   __syncthreads();
   const float amax = fmaxf(fmaxf(wmax[0], wmax[1]), fmaxf(wmax[2], wmax[3]));
   const float s = amax / 448.0f;
-  for (int j = 0; j < 64; j += 2) {
-    uint32_t pair = 0;
-    if (s != 0.0f)
-      pair = e4m3_pair(load_elem(x, xt, r * cols + c0 + j) / s, load_elem(x, xt, r * cols + c0 + j + 1) / s);
-    *reinterpret_cast<uint16_t*>(q + r * cols + c0 + j) = static_cast<uint16_t>(pair);
+#pragma unroll
+  for (int p = 0; p < NP; ++p) {
+    const int64_t row = br * 128 + rr + RPP * p;
+    const uint64_t c = codes<E>(v[p], s);
+    uint8_t* dst = q + row * cols + bc * 128 + cc * E;
+    if (E == 8)
+      *reinterpret_cast<uint64_t*>(dst) = c;
+    else
+      *reinterpret_cast<uint32_t*>(dst) = static_cast<uint32_t>(c);
   }
   if (tid == 0) scale[blockIdx.x] = s;
 }
@@ -81,13 +129,18 @@ hipError_t launch_quantize_fp8(const void* x, int xt, int64_t rows, int64_t cols
                                int tile_c, uint8_t* q, float* scale, hipStream_t stream) {
   (void)tile_c;
   if (tile_r == 1) {
-    const int64_t tiles = rows * (cols / 128);
-    hipLaunchKernelGGL(quant_row_tiles, dim3(static_cast<unsigned>((tiles + 3) / 4)), dim3(256), 0,
-                       stream, x, xt, rows, cols, q, scale);
+    const int64_t lanes = rows * (cols / 128) * (xt == 1 ? 16 : 32);
+    const dim3 grid(static_cast<unsigned>((lanes + 255) / 256));
+    if (xt == 1)
+      hipLaunchKernelGGL(quant_row_tiles<1>, grid, dim3(256), 0, stream, x, rows, cols, q, scale);
+    else
+      hipLaunchKernelGGL(quant_row_tiles<0>, grid, dim3(256), 0, stream, x, rows, cols, q, scale);
   } else {
-    const int64_t tiles = (rows / 128) * (cols / 128);
-    hipLaunchKernelGGL(quant_block_tiles, dim3(static_cast<unsigned>(tiles)), dim3(256), 0, stream,
-                       x, xt, rows, cols, q, scale);
+    const dim3 grid(static_cast<unsigned>((rows / 128) * (cols / 128)));
+    if (xt == 1)
+      hipLaunchKernelGGL(quant_block_tiles<1>, grid, dim3(256), 0, stream, x, rows, cols, q, scale);
+    else
+      hipLaunchKernelGGL(quant_block_tiles<0>, grid, dim3(256), 0, stream, x, rows, cols, q, scale);
   }
   return hipGetLastError();
 }
