@@ -58,8 +58,34 @@ int grid_for_device() {
   return cus[dev];
 }
 
+// Upper bound on the tiles of a grouped GEMM launch (phase 1: gate/up, 128 output
+// columns per tile; phase 2: down, 256): an expert of r rows has ceil(r / 256) row
+// blocks, at most r / 256 + 1, and each shared group ceil(T / 256).
+int64_t ffn_max_tiles(const moe_shape* s, int phase) {
+  const int64_t bm = moe::kTileRows;
+  const int64_t P = s->T * s->top_k;
+  const int64_t routed_blocks = P / bm + s->n_routed + 1;
+  const int64_t tb = (s->T + bm - 1) / bm;
+  if (phase == 1) return (routed_blocks + s->n_shared * tb) * (s->d_ff / 128);
+  return (routed_blocks + (s->n_shared > 0 ? tb : 0)) * (s->d / 256);
+}
+
+// Persistent grid of the grouped GEMMs: one workgroup per CU, at least 64 (8 per gang),
+// which the scheduling state in the workspace is sized for.
+constexpr int kMinGemmGrid = 64;
+int gemm_grid() {
+  const int g = grid_for_device();
+  return g < kMinGemmGrid ? kMinGemmGrid : g;
+}
+
+struct SchedState {  // the two launches' regions of the scheduling state
+  int32_t* s1;
+  int32_t* s2;
+  int stride1, stride2;
+};
+
 struct FfnWorkspace {
-  size_t counters, h_routed, h_shared, q_u, s_u, s_h_routed, s_h_shared, total;
+  size_t sched, h_routed, h_shared, q_u, s_u, s_h_routed, s_h_shared, total;
 };
 
 FfnWorkspace ffn_workspace(const moe_shape* s) {
@@ -67,8 +93,9 @@ FfnWorkspace ffn_workspace(const moe_shape* s) {
   const int64_t P = s->T * s->top_k;
   const int64_t Hs = s->T * static_cast<int64_t>(s->n_shared) * s->d_ff;
   size_t off = 0;
-  w.counters = off;  // 2 x 8 int32 tile-claim counters (one set per GEMM launch)
-  off = align_up(off + 16 * sizeof(int32_t));
+  w.sched = off;  // gang-scheduling state of the two GEMM launches, sized for the smallest grid
+  off = align_up(off + (moe::sched_ints(ffn_max_tiles(s, 1), kMinGemmGrid) +
+                        moe::sched_ints(ffn_max_tiles(s, 2), kMinGemmGrid)) * sizeof(int32_t));
   if (s->ffn == MOE_FP8_E4M3) {
     w.q_u = off;
     off = align_up(off + static_cast<size_t>(s->T) * s->d);
@@ -99,7 +126,7 @@ FfnWorkspace ffn_workspace(const moe_shape* s) {
 moe_status grouped_ffn_fp8(const moe_shape* s, const void* u, const int32_t* expert_offset,
                            const int32_t* sorted_token, const moe_expert_set* routed,
                            const moe_expert_set* shared, void* y_routed, float* y_shared,
-                           unsigned char* wsb, const FfnWorkspace& w, int32_t* counters, int grid,
+                           unsigned char* wsb, const FfnWorkspace& w, const SchedState& sc, int grid,
                            hipStream_t st) {
   uint8_t* q_u = wsb + w.q_u;
   float* s_u = reinterpret_cast<float*>(wsb + w.s_u);
@@ -132,7 +159,8 @@ moe_status grouped_ffn_fp8(const moe_shape* s, const void* u, const int32_t* exp
   f1.g.N = I;
   f1.g.K = d;
   f1.g.k_segments = 1;
-  f1.g.tile_counter = counters;
+  f1.g.sched = sc.s1;
+  f1.g.slot_stride = sc.stride1;
   f1.sa_routed = f1.sa_shared = s_u;
   f1.ldsa_routed = f1.ldsa_shared = d / 128;
   f1.sb1_routed = routed->s1;
@@ -168,7 +196,8 @@ moe_status grouped_ffn_fp8(const moe_shape* s, const void* u, const int32_t* exp
   f2.g.N = d;
   f2.g.K = I;
   f2.g.k_segments = ns;
-  f2.g.tile_counter = counters + 8;
+  f2.g.sched = sc.s2;
+  f2.g.slot_stride = sc.stride2;
   f2.sa_routed = sh_r;
   f2.ldsa_routed = I / 128;
   f2.sa_shared = sh_s;
@@ -255,11 +284,18 @@ moe_status moe_grouped_ffn(const moe_shape* s, const void* u, const int32_t* exp
         s->n_routed, s->top_k, s->n_shared, reinterpret_cast<float*>(wsb + w.h_routed),
         static_cast<float*>(y_routed), y_shared, st));
   }
-  const int grid = grid_for_device();
-  int32_t* counters = reinterpret_cast<int32_t*>(wsb + w.counters);
-  if (moe::launch_zero_i32(counters, 16, st) != hipSuccess) return MOE_ERR_HIP;
+  const int grid = gemm_grid();
+  const int64_t t1 = ffn_max_tiles(s, 1), t2 = ffn_max_tiles(s, 2);
+  if (t1 > INT32_MAX / 2 || t2 > INT32_MAX / 2) return MOE_ERR_UNSUPPORTED;
+  SchedState sc;
+  sc.s1 = reinterpret_cast<int32_t*>(wsb + w.sched);
+  sc.s2 = sc.s1 + moe::sched_ints(t1, grid);
+  sc.stride1 = static_cast<int>(moe::sched_slot_stride(t1, grid));
+  sc.stride2 = static_cast<int>(moe::sched_slot_stride(t2, grid));
+  const int64_t n_sched = moe::sched_ints(t1, grid) + moe::sched_ints(t2, grid);
+  if (moe::launch_zero_i32(sc.s1, static_cast<int>(n_sched), st) != hipSuccess) return MOE_ERR_HIP;
   if (fp8) return grouped_ffn_fp8(s, u, expert_offset, sorted_token, routed, shared, y_routed, y_shared,
-                                  wsb, w, counters, grid, st);
+                                  wsb, w, sc, grid, st);
   uint16_t* h_r = reinterpret_cast<uint16_t*>(wsb + w.h_routed);
   uint16_t* h_s = reinterpret_cast<uint16_t*>(wsb + w.h_shared);
   const uint16_t* ub = static_cast<const uint16_t*>(u);
@@ -286,7 +322,8 @@ moe_status moe_grouped_ffn(const moe_shape* s, const void* u, const int32_t* exp
   g1.N = s->d_ff;
   g1.K = s->d;
   g1.k_segments = 1;
-  g1.tile_counter = counters;
+  g1.sched = sc.s1;
+  g1.slot_stride = sc.stride1;
   hipError_t err = moe::launch_grouped_gemm_bf16(g1, true, grid, st);
   if (err != hipSuccess) return MOE_ERR_HIP;
 
@@ -311,7 +348,8 @@ moe_status moe_grouped_ffn(const moe_shape* s, const void* u, const int32_t* exp
   g2.N = s->d;
   g2.K = s->d_ff;
   g2.k_segments = s->n_shared;
-  g2.tile_counter = counters + 8;
+  g2.sched = sc.s2;
+  g2.slot_stride = sc.stride2;
   (void)P;
   return from_hip(moe::launch_grouped_gemm_bf16(g2, false, grid, st));
 }

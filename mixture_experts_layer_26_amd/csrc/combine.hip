@@ -77,7 +77,7 @@ __global__ __launch_bounds__(kThreads) void combine_kernel(
 }
 
 __global__ void zero_i32_kernel(int* __restrict__ p, int n) {
-  for (int i = threadIdx.x; i < n; i += blockDim.x) p[i] = 0;
+  for (int i = blockIdx.x * blockDim.x + threadIdx.x; i < n; i += gridDim.x * blockDim.x) p[i] = 0;
 }
 
 __global__ void bias_update_kernel(const int32_t* __restrict__ count, int64_t total, int n_r,
@@ -107,7 +107,8 @@ hipError_t launch_combine(int act, const void* u, const void* y_routed, const fl
 }
 
 hipError_t launch_zero_i32(int* p, int n, hipStream_t stream) {
-  hipLaunchKernelGGL(zero_i32_kernel, dim3(1), dim3(64), 0, stream, p, n);
+  const int blocks = n <= 0 ? 1 : (n + 255) / 256 < 256 ? (n + 255) / 256 : 256;
+  hipLaunchKernelGGL(zero_i32_kernel, dim3(blocks), dim3(256), 0, stream, p, n);
   return hipGetLastError();
 }
 

@@ -120,27 +120,31 @@ __device__ __forceinline__ void mainloop(const TileCtx& c, unsigned char* smem, 
     sw[0] = sw[1] = s0;
     sw[2] = sw[3] = s1;
   };
+  // In its memory half a group stores the registers loaded one K-step earlier, loads
+  // the weight scales of its next compute half, then the tiles of the step after next
+  // (in that order: the scales are waited for first, and loads complete in order).
+  float sw[4];
   gload(0);
   lstore(0);
-  if (g == 1) gload(1);
+  if (g == 0) wscales(0, sw);
+  gload(1);
   __syncthreads();
   for (int kt = 0; kt < c.nk; ++kt) {
     const int cur = kt & 1;
-    float sw[4];
     if (g == 0) {
-      gload(kt + 1);
-      wscales(kt, sw);
       compute_step<NM>(la(cur), lb(cur), lsa(cur), arow0, brow, sw, lane, acc);
     } else {
       lstore(cur ^ 1);
+      wscales(kt, sw);
+      gload(kt + 2);
     }
     lds_barrier();
     if (g == 1) {
-      gload(kt + 2);
-      wscales(kt, sw);
       compute_step<NM>(la(cur), lb(cur), lsa(cur), arow0, brow, sw, lane, acc);
     } else {
       lstore(cur ^ 1);
+      wscales(kt + 1 < last ? kt + 1 : last, sw);
+      gload(kt + 2);
     }
     lds_barrier();
   }
@@ -158,9 +162,10 @@ __global__ __launch_bounds__(kThreads) void grouped_gemm_fp8(Fp8Args fa) {
   extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
 
   const int n_r = args.n_r;
-  const int ng = n_r + args.n_shared_groups;
   const int bn_out = GATED ? BNB / 2 : BNB;
-  build_tile_map(tm, args.offset, n_r, args.n_shared_groups, args.T, args.N / bn_out);
+  const int ntn = args.N / bn_out;
+  build_tile_map(tm, args.offset, n_r, args.n_shared_groups, args.T, ntn);
+  auto rows_of = [&](int grp) -> int64_t { return grp < n_r ? args.offset[grp + 1] - args.offset[grp] : args.T; };
 
   const int tid = threadIdx.x, lane = tid % kWave, wave = tid / kWave;
   const int g = wave / 4, wn = wave % 4;
@@ -168,8 +173,8 @@ __global__ __launch_bounds__(kThreads) void grouped_gemm_fp8(Fp8Args fa) {
   const uint8_t* a_routed = reinterpret_cast<const uint8_t*>(args.a_routed);
   const uint8_t* a_shared = reinterpret_cast<const uint8_t*>(args.a_shared);
 
-  for_each_tile(tm.total, args.tile_counter, [&](int L) {
-    const Tile t = tile_at(tm, L, ng, args.offset, n_r, args.T, bn_out);
+  for_each_tile(tm.total, args.sched, args.slot_stride, [&](int L) {
+    const Tile t = tile_at(tm, L, n_r, bn_out, ntn, rows_of);
     const bool routed = t.group < n_r;
     const int sg = t.group - n_r;
     const int64_t row_base = routed ? args.offset[t.group] : 0;

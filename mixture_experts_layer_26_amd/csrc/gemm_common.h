@@ -2,18 +2,21 @@
 //
 // A launch covers a list of groups: routed expert g < n_r owns the sorted rows
 // [offset[g], offset[g+1]); groups n_r.. are the shared experts (all T tokens). Each
-// group is cut into tiles of BM rows x one output-column block; the tile list is built
-// on the device from expert_offset, so no host synchronisation is needed, and tiles
-// are claimed per XCD (see for_each_tile).
+// group is cut into row blocks of at most BM rows -- a group of r rows into ceil(r/BM)
+// blocks of equal size, so the two blocks of an expert with 257..512 rows take the same
+// time -- and each block into output-column tiles. The tile list is built on the device
+// from expert_offset, so no host synchronisation is needed, and it is walked by gangs of
+// workgroups that run neighbouring tiles at the same time (see for_each_tile).
 #pragma once
 
 #include "device.h"
+#include "launch.h"
 
 namespace moe {
 namespace gemm {
 
 constexpr int kThreads = 512;  // 8 waves: two groups of 4, one wave of each group per SIMD
-constexpr int BM = 256;        // rows per tile
+constexpr int BM = kTileRows;  // rows per tile (at most)
 constexpr int BNB = 256;       // B rows (weight rows) per tile
 constexpr int kRowBytes = 128; // bytes per tile row per K-step (64 bf16 or 128 fp8)
 constexpr int kStageBytes = BM * kRowBytes;  // one operand's LDS stage (32 KB)
@@ -26,11 +29,18 @@ struct Tile {
   int rows;   // valid rows in this tile
 };
 
-// Tile list: routed groups first (expert-major, then output-column tile, then row
-// tile), then the shared groups. Built per workgroup in LDS.
+// Tile list, by position: first the routed experts with an even number of row blocks,
+// then those with an odd number, then the shared groups, so that with 16 column tiles
+// per block and 32-tile gang items an expert of two blocks fills exactly one item.
+// Routed groups list their tiles column-major (the row blocks of one column tile are
+// neighbours: they read the same weights); shared groups row-major (the column tiles of
+// one row block are neighbours: they read the same rows). Built per workgroup in LDS.
 struct TileMap {
-  int cum[kMaxGroups + 1];  // first tile index of each group
-  int mt[kMaxGroups];       // row tiles per group
+  int cum[kMaxGroups + 1];  // first tile index of the group at each position
+  int grp[kMaxGroups];      // group at each position
+  int mt[kMaxGroups];       // row blocks of each group
+  int rpb[kMaxGroups];      // rows per block of each group
+  int ng;                   // positions (groups with rows)
   int total;
 };
 
@@ -39,66 +49,103 @@ __device__ inline void build_tile_map(TileMap& tm, const int32_t* offset, int n_
   const int ng = n_r + n_groups_shared;
   for (int g = threadIdx.x; g < ng; g += kThreads) {
     const int64_t rows = g < n_r ? (offset[g + 1] - offset[g]) : T;
-    tm.mt[g] = static_cast<int>((rows + BM - 1) / BM);
+    const int64_t mt0 = (rows + BM - 1) / BM;
+    const int64_t rpb = mt0 > 0 ? (rows + mt0 - 1) / mt0 : 0;  // <= BM
+    tm.rpb[g] = static_cast<int>(rpb);
+    tm.mt[g] = rpb > 0 ? static_cast<int>((rows + rpb - 1) / rpb) : 0;  // no empty last block
   }
   __syncthreads();
   if (threadIdx.x == 0) {
-    int acc = 0;
-    for (int g = 0; g < ng; ++g) {
-      tm.cum[g] = acc;
-      acc += tm.mt[g] * ntn;
+    int acc = 0, pos = 0;
+    for (int pass = 0; pass < 3; ++pass) {
+      const int lo = pass < 2 ? 0 : n_r, hi = pass < 2 ? n_r : ng;
+      for (int g = lo; g < hi; ++g) {
+        const int mt = tm.mt[g];
+        if (mt == 0 || (pass < 2 && (mt & 1) != pass)) continue;
+        tm.grp[pos] = g;
+        tm.cum[pos] = acc;
+        acc += mt * ntn;
+        ++pos;
+      }
     }
-    tm.cum[ng] = acc;
+    tm.cum[pos] = acc;
+    tm.ng = pos;
     tm.total = acc;
   }
   __syncthreads();
 }
 
-__device__ __forceinline__ Tile tile_at(const TileMap& tm, int L, int ng, const int32_t* offset, int n_r,
-                                        int64_t T, int bn_out) {
-  int lo = 0, hi = ng - 1;  // last group with cum[g] <= L
+// Tile L of the list. rows_of(g) gives the rows of group g.
+template <class RowsOf>
+__device__ __forceinline__ Tile tile_at(const TileMap& tm, int L, int n_r, int bn_out, int ntn,
+                                        RowsOf&& rows_of) {
+  int lo = 0, hi = tm.ng - 1;  // last position with cum[pos] <= L
   while (lo < hi) {
     const int mid = (lo + hi + 1) / 2;
     if (tm.cum[mid] <= L) lo = mid; else hi = mid - 1;
   }
   Tile t;
-  t.group = lo;
+  t.group = tm.grp[lo];
   const int local = L - tm.cum[lo];
-  const int mt = tm.mt[lo];
-  t.n0 = (local / mt) * bn_out;
-  t.m0 = (local % mt) * BM;
-  const int64_t rows = lo < n_r ? (offset[lo + 1] - offset[lo]) : T;
-  const int64_t left = rows - t.m0;
-  t.rows = static_cast<int>(left < BM ? left : BM);
+  int m, n;
+  if (t.group < n_r) {
+    const int mt = tm.mt[t.group];
+    n = local / mt;
+    m = local - n * mt;
+  } else {
+    m = local / ntn;
+    n = local - m * ntn;
+  }
+  const int rpb = tm.rpb[t.group];
+  t.n0 = n * bn_out;
+  t.m0 = m * rpb;
+  const int64_t left = rows_of(t.group) - t.m0;
+  t.rows = static_cast<int>(left < rpb ? left : rpb);
   return t;
 }
 
-// Tile claiming. The tile list is cut into 8 contiguous chunks, one per XCD. A
-// workgroup claims tiles of its own XCD's chunk (XCD id read from HW_REG_XCC_ID) from
-// that chunk's counter, so the tiles in flight on an XCD are neighbours in the list (one
-// expert's column and row tiles), whose gathered rows and weights its L2 then serves
-// to several CUs. When its chunk runs out it helps the other chunks. The counters only
-// decide which CU computes a tile, never what a tile computes. counter: 8 zeroed ints.
+// Tile claiming by gangs. Workgroup b is member b / 8 of gang b % 8; workgroups are
+// dispatched round-robin over the 8 XCDs, so a gang's members share one XCD and its L2.
+// A gang takes items of G = gridDim.x / 8 consecutive tiles and member i computes tile i
+// of the item, so the column tiles of a row block (same rows) and the row blocks of a
+// column tile (same weights) run side by side and their common operand comes from HBM
+// once. Items are handed out dynamically from one counter. The k-th item of a gang is
+// published in slot k of the gang's row of slots: the first member to reach step k
+// claims it (slot 0 -> -1 -> item + 1), the others read the slot. A member only waits
+// for one that has passed the compare-and-swap and is two atomics from publishing, so
+// every wait ends. The claims decide which workgroup computes a tile, never what it
+// computes.
+// sched: [0] the item counter, then kGangs rows of slot_stride slots, all zeroed before
+// the launch; slot_stride > ceil(total / G).
 template <class F>
-__device__ __forceinline__ void for_each_tile(int total, int* counter, F&& body) {
+__device__ __forceinline__ void for_each_tile(int total, int* sched, int slot_stride, F&& body) {
   __shared__ int claim;
-  uint32_t xcc;
-  asm volatile("s_getreg_b32 %0, hwreg(HW_REG_XCC_ID)" : "=s"(xcc));
-  xcc &= 7;
-  const int chunk = (total + 7) / 8;
-  int o = 0;
-  while (o < 8) {
-    const int x = (static_cast<int>(xcc) + o) & 7;
-    if (threadIdx.x == 0) claim = atomicAdd(counter + x, 1);
-    __syncthreads();
-    const int local = claim;
-    __syncthreads();
-    const int L = x * chunk + local;
-    if (local >= chunk || L >= total) {
-      ++o;
-      continue;
+  const int G = static_cast<int>(gridDim.x) / kGangs;
+  const int gang = static_cast<int>(blockIdx.x) % kGangs, rank = static_cast<int>(blockIdx.x) / kGangs;
+  if (rank >= G) return;  // a grid that is not a multiple of 8 leaves its last workgroups idle
+  const int n_items = (total + G - 1) / G;
+  int* slot = sched + 1 + static_cast<int64_t>(gang) * slot_stride;
+  for (int k = 0; k < slot_stride; ++k) {
+    if (threadIdx.x == 0) {
+      int v = 0;
+      if (__hip_atomic_compare_exchange_strong(slot + k, &v, -1, __ATOMIC_RELAXED, __ATOMIC_RELAXED,
+                                               __HIP_MEMORY_SCOPE_AGENT)) {
+        v = atomicAdd(sched, 1) + 1;
+        __hip_atomic_store(slot + k, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      } else {
+        while (v == -1) {
+          __builtin_amdgcn_s_sleep(2);
+          v = __hip_atomic_load(slot + k, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        }
+      }
+      claim = v - 1;
     }
-    body(L);
+    __syncthreads();
+    const int item = claim;
+    __syncthreads();
+    if (item >= n_items) break;
+    const int L = item * G + rank;
+    if (L < total) body(L);
   }
 }
 

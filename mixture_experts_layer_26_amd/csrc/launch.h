@@ -32,8 +32,20 @@ struct GemmArgs {
   int N;                     // output columns per group
   int K;                     // K of one expert
   int k_segments;            // phase 2 shared: n_s
-  int* tile_counter;         // 8 zeroed ints: per-XCD tile claim counters
+  int* sched;                // zeroed gang-scheduling state: 1 + kGangs * slot_stride ints
+  int slot_stride;           // slots per gang (> tiles / (grid / kGangs))
 };
+
+// Tile scheduling of the grouped GEMMs: workgroup b belongs to gang b % kGangs (one
+// gang per XCD). Ints of scheduling state one launch of at most max_tiles tiles needs on
+// a grid of `grid` workgroups, and the slot stride that goes with it.
+constexpr int kGangs = 8;
+constexpr int kTileRows = 256;  // rows per tile at most
+inline int64_t sched_slot_stride(int64_t max_tiles, int grid) {
+  const int64_t G = grid / kGangs > 0 ? grid / kGangs : 1;
+  return (max_tiles + G - 1) / G + 2;
+}
+inline int64_t sched_ints(int64_t max_tiles, int grid) { return 1 + kGangs * sched_slot_stride(max_tiles, grid); }
 
 hipError_t launch_zero_i32(int* p, int n, hipStream_t stream);
 
