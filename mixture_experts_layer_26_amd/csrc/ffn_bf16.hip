@@ -59,6 +59,7 @@ __device__ __forceinline__ void dma16(const void* gptr, const unsigned char* lds
 }
 
 struct TileCtx {
+  bool load_a;           // this wave's 32 A rows hold at least one of the tile's rows
   const uint16_t* a[4];  // this lane's four A rows (chunk included)
   const uint16_t* b[4];  // this lane's four B rows (chunk included)
   int64_t seg_stride;    // phase 2 shared: W2 stride per K segment, else 0
@@ -69,14 +70,18 @@ struct TileCtx {
 
 // Direct loads of K-step kt into stage ST: wave w fills A rows and B rows 32w..32w+31,
 // four 8-row instructions each; lane i writes row 8j + i/8 of its instruction's block,
-// 16-byte slot i%8, whose global chunk was chosen when the pointers were made.
+// 16-byte slot i%8, whose global chunk was chosen when the pointers were made. A wave
+// whose A rows all lie past the tile's rows loads no A (those LDS rows feed only
+// outputs that are not stored).
 template <int ST>
 __device__ __forceinline__ void dma_step(const TileCtx& c, int kt, int wave) {
   unsigned char* st = stage<ST>();
   const int64_t aoff = static_cast<int64_t>(kt) * BK;
   const int64_t boff = b_offset(kt, c.kseg_steps, c.kseg_inv, c.seg_stride, BK);
+  if (c.load_a) {
 #pragma unroll
-  for (int j = 0; j < 4; ++j) dma16(c.a[j] + aoff, st + (32 * wave + 8 * j) * kRow);
+    for (int j = 0; j < 4; ++j) dma16(c.a[j] + aoff, st + (32 * wave + 8 * j) * kRow);
+  }
 #pragma unroll
   for (int j = 0; j < 4; ++j) dma16(c.b[j] + boff, st + kOperand + (32 * wave + 8 * j) * kRow);
 }
@@ -126,10 +131,12 @@ template <int NEWER>
 __device__ __forceinline__ void step_barrier() {
   if constexpr (NEWER == 8)
     asm volatile("s_waitcnt vmcnt(8)\n\ts_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+  else if constexpr (NEWER == 4)
+    asm volatile("s_waitcnt vmcnt(4)\n\ts_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
   else
     asm volatile("s_waitcnt vmcnt(0)\n\ts_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
 }
-static_assert(kDmaPerStep == 8, "step_barrier's wait counts assume 8 loads per step");
+static_assert(kDmaPerStep == 8, "step_barrier's wait counts assume 8 loads per step (4 without A)");
 
 // One K-step s from stage ST = s % 2, four 16-wide sub-steps. Fragment sets f0 and f1
 // alternate: each sub-step's MFMAs run while the sub-step after next is read. On entry
@@ -177,7 +184,11 @@ __device__ __forceinline__ void mainloop(const TileCtx& c, f32x16 (&acc)[4][2], 
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
   dma_step<0>(c, 0, wave);
   dma_step<1>(c, 1, wave);
-  step_barrier<kDmaPerStep>();  // step 0 landed; step 1 in flight
+  // step 0 landed; step 1 (8 loads, or 4 without A) in flight
+  if (c.load_a)
+    step_barrier<kDmaPerStep>();
+  else
+    step_barrier<kDmaPerStep / 2>();
   Frags<NMB> f0, f1;
   read_frags<0, NMB>(f0, 0, arow0, brow, lane);
   read_frags<0, NMB>(f1, 1, arow0, brow, lane);
@@ -213,6 +224,7 @@ __global__ __launch_bounds__(kThreads) void grouped_gemm_bf16(GemmArgs args) {
     // this lane's load rows: 32*wave + 8j + lane/8 of the tile, slot lane%8, holding
     // global chunk slot ^ ((row/2)%8) (the swizzle of swz)
     const int64_t eoff = static_cast<int64_t>(routed ? t.group : sg) * args.b_expert_stride;
+    c.load_a = __builtin_amdgcn_readfirstlane(32 * wave < t.rows ? 1 : 0) != 0;
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       const int r = 32 * wave + 8 * j + lane / 8;
