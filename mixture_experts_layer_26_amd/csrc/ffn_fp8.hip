@@ -26,15 +26,51 @@ namespace {
 
 using namespace gemm;
 
-constexpr int BK = 128;  // fp8 elements (bytes) per K-step = one scale block
-constexpr int kScaleBytes = BM * 4;  // one stage of A-row scales
+constexpr int BK = 128;                 // fp8 elements (bytes) per K-step = one scale block
+constexpr int kOperand = BM * BK;       // 32 KB: one operand of one stage
+constexpr int kScaleBytes = BM * 4;     // A-row scales of one stage
+constexpr int kStageSize = 2 * kOperand + kScaleBytes;
+
+// The two stages (A rows, B rows, A-row scales), one LDS array so that every load
+// destination is a wave base plus a constant.
+__shared__ __attribute__((aligned(16))) unsigned char stages[2 * kStageSize];
+
+template <int ST>
+__device__ __forceinline__ unsigned char* stage() {
+  return stages + ST * kStageSize;
+}
+
+typedef __attribute__((address_space(3))) unsigned char* lds_ptr;
+
+// One global_load_lds_dwordx4: lane i copies the 16 bytes at gptr (its own address) to
+// LDS byte base + OFF + 16 i. M0 holds the LDS address (one wait state after writing
+// it). The instruction is written out rather than taken from the builtin so that the
+// compiler adds no wait of its own before the LDS reads; the waits are the explicit
+// ones in step_barrier. Nothing else in these kernels uses M0.
+template <int OFF>
+__device__ __forceinline__ void dma16(const void* gptr, uint32_t base) {
+  asm volatile("s_add_u32 m0, %1, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(gptr), "s"(base), "n"(OFF)
+               : "memory");
+}
+
+// The same with 4 bytes per lane (lane i writes LDS byte base + OFF + 4 i).
+template <int OFF>
+__device__ __forceinline__ void dma4(const void* gptr, uint32_t base) {
+  asm volatile("s_add_u32 m0, %1, %2\n\ts_nop 0\n\tglobal_load_lds_dword %0, off" ::"v"(gptr), "s"(base), "n"(OFF)
+               : "memory");
+}
 
 struct TileCtx {
-  const uint8_t* arow[4];   // this thread's 4 A rows (its 16-byte chunk)
-  const uint8_t* b;         // this thread's first B row (chunk); rows +32*i
-  const float* sa_row;      // A-row scales of row gr (threads with gt < 128: row 128g + gt)
+  uint32_t lds_wave;        // LDS address of this wave's rows (32 wave) in stage 0
+  uint32_t lds_scale;       // waves 0..3: LDS address of row scales 64 wave.. in stage 0
+  bool load_a;              // this wave's 32 A rows hold at least one of the tile's rows
+  bool load_scale;          // waves 0..3 load the A-row scales (one row per lane)
+  const uint8_t* a[4];      // this lane's four A rows (chunk included)
+  const uint8_t* b;         // this lane's first B row (chunk included); row j: + 8 j ldb,
+  int64_t ldb8;             //   and + odd_chunk for odd j (8 rows on, the swizzle term
+  int odd_chunk;            //   (row/2)%8 differs by 4: the chunk index flips bit 2)
+  const float* sa_row;      // threads 0..255: A-row scales of tile row tid (K-block 0)
   const float* sb[2];       // this wave's two B-scale rows (gate/up, or the wave's block)
-  int64_t ldb;
   int64_t seg_stride;       // phase 2 shared: W2 stride per K segment, else 0
   int64_t sb_seg_stride;    // same for the W2 scales
   int kseg_steps;
@@ -42,6 +78,28 @@ struct TileCtx {
   int nk;
 };
 
+// Direct loads of K-step kt into stage ST: wave w fills A rows and B rows 32w..32w+31,
+// four 8-row instructions each; lane i writes row 8j + i/8, 16-byte slot i%8, whose
+// global chunk was chosen when the pointers were made. A wave whose A rows all lie past
+// the tile's rows loads no A.
+template <int ST>
+__device__ __forceinline__ void dma_step(const TileCtx& c, int kt) {
+  const int64_t aoff = static_cast<int64_t>(kt) * BK;
+  const int64_t boff = b_offset(kt, c.kseg_steps, c.kseg_inv, c.seg_stride, BK);
+  if (c.load_a) {
+    dma16<ST * kStageSize + 0 * 8 * BK>(c.a[0] + aoff, c.lds_wave);
+    dma16<ST * kStageSize + 1 * 8 * BK>(c.a[1] + aoff, c.lds_wave);
+    dma16<ST * kStageSize + 2 * 8 * BK>(c.a[2] + aoff, c.lds_wave);
+    dma16<ST * kStageSize + 3 * 8 * BK>(c.a[3] + aoff, c.lds_wave);
+  }
+  dma16<ST * kStageSize + kOperand + 0 * 8 * BK>(c.b + (boff + 0 * c.ldb8), c.lds_wave);
+  dma16<ST * kStageSize + kOperand + 1 * 8 * BK>(c.b + (boff + 1 * c.ldb8 + c.odd_chunk), c.lds_wave);
+  dma16<ST * kStageSize + kOperand + 2 * 8 * BK>(c.b + (boff + 2 * c.ldb8), c.lds_wave);
+  dma16<ST * kStageSize + kOperand + 3 * 8 * BK>(c.b + (boff + 3 * c.ldb8 + c.odd_chunk), c.lds_wave);
+  if (c.load_scale) dma4<ST * kStageSize>(c.sa_row + kt, c.lds_scale);
+}
+
+// A 16 x 128 fp8 fragment (rows row.., this lane's 32 bytes of K) from a swizzled stage.
 __device__ __forceinline__ i32x8 rd_frag(const unsigned char* base, int row, int q) {
   const uint4 lo = *reinterpret_cast<const uint4*>(base + swz(row, 2 * q));
   const uint4 hi = *reinterpret_cast<const uint4*>(base + swz(row, 2 * q + 1));
@@ -51,39 +109,92 @@ __device__ __forceinline__ i32x8 rd_frag(const unsigned char* base, int row, int
   return f;
 }
 
-// One K-step (one scale block) for a wave holding NM live 32-row blocks (2*NM 16-row
-// MFMA blocks). sw[nb]: the weight scale of output block nb.
-template <int NM>
-__device__ __forceinline__ void compute_step(const unsigned char* la, const unsigned char* lb, const float* lsa,
-                                             int arow0, const int (&brow)[4], const float (&sw)[4], int lane,
+// Scheduling fence: the compiler moves no instruction across it.
+__device__ __forceinline__ void fence() { __builtin_amdgcn_sched_barrier(0); }
+
+// One K-step (one scale block) from stage ST for a wave holding NM live 32-row blocks
+// (2*NM 16-row MFMA blocks). sw[p]: the weight scale of output blocks 2p, 2p+1. The
+// MFMAs of a block start from a zero that an empty asm statement produces after the
+// previous block's accumulators are final, so the compiler cannot hoist all MFMAs of
+// the step ahead of their scaling (which would hold 32 MFMA results at once).
+template <int ST, int NM>
+__device__ __forceinline__ void compute_step(int arow0, const int (&brow)[4], const float (&sw)[2], int lane,
                                              f32x4 (&acc)[8][4]) {
+  if constexpr (NM == 0) return;
+  const unsigned char* la = stage<ST>();
+  const unsigned char* lb = la + kOperand;
+  const float* lsa = reinterpret_cast<const float*>(la + 2 * kOperand);
   const int q = lane / 16;
   i32x8 bfr[4];
 #pragma unroll
   for (int nb = 0; nb < 4; ++nb) bfr[nb] = rd_frag(lb, brow[nb], q);
 #pragma unroll
   for (int mb = 0; mb < 2 * NM; ++mb) {
+    f32x4 zero = {};
+    if (mb > 0)
+      asm volatile("" : "+v"(zero) : "v"(acc[mb - 1][0]), "v"(acc[mb - 1][1]), "v"(acc[mb - 1][2]), "v"(acc[mb - 1][3]));
     const i32x8 af = rd_frag(la, arow0 + 16 * mb, q);
     // scales of this lane's 4 rows (16*mb + 4*q + v), contiguous in LDS
     const f32x4 sa = *reinterpret_cast<const f32x4*>(lsa + (arow0 - lane % 16) + 16 * mb + 4 * q);
+    f32x4 prod[2];  // row scale x weight scale, per pair of output blocks
+#pragma unroll
+    for (int p = 0; p < 2; ++p)
+#pragma unroll
+      for (int v = 0; v < 4; ++v) prod[p][v] = sa[v] * sw[p];
 #pragma unroll
     for (int nb = 0; nb < 4; ++nb) {
-      const f32x4 blk = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(af, bfr[nb], f32x4{}, 0, 0, 0, 127, 0, 127);
+      const f32x4 blk = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(af, bfr[nb], zero, 0, 0, 0, 127, 0, 127);
 #pragma unroll
-      for (int v = 0; v < 4; ++v) acc[mb][nb][v] = fmaf(blk[v], sa[v] * sw[nb], acc[mb][nb][v]);
+      for (int v = 0; v < 4; ++v) acc[mb][nb][v] = fmaf(blk[v], prod[nb / 2][v], acc[mb][nb][v]);
     }
   }
 }
 
+// Workgroup barrier at the end of a K-step: this wave's loads of the next step have
+// landed (vmcnt(0)), its row scale of the next step is written to LDS, and its LDS
+// operations are done; after the barrier every wave's part of the next step is in LDS
+// and no wave reads the current stage any more.
+__device__ __forceinline__ void step_barrier() {
+  asm volatile("s_waitcnt vmcnt(0)\n\ts_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
+
+// Weight scales of K-step kt for this wave's two pairs of output blocks.
+__device__ __forceinline__ void wscales(const TileCtx& c, int kt, float (&sw)[2]) {
+  const int64_t o = b_offset(kt, c.kseg_steps, c.kseg_inv, c.sb_seg_stride, 1);
+  sw[0] = c.sb[0][o];
+  sw[1] = c.sb[1][o];
+}
+
+// One K-step s from stage ST = s % 2. When MORE, step s+1 (tiles and row scales by
+// DMA, the weight scales into sw for the next step) is loaded into the other stage
+// while this one is computed.
+template <int ST, int NM, bool MORE>
+__device__ __forceinline__ void k_step(const TileCtx& c, int s, int arow0, const int (&brow)[4], int lane,
+                                       float (&sw)[2], f32x4 (&acc)[8][4]) {
+  float swn[2];
+  if constexpr (MORE) {
+    dma_step<(ST + 1) % 2>(c, s + 1);
+    wscales(c, s + 1, swn);
+  }
+  fence();
+  compute_step<ST, NM>(arow0, brow, sw, lane, acc);
+  fence();
+  if constexpr (MORE) {
+    sw[0] = swn[0];
+    sw[1] = swn[1];
+  }
+  step_barrier();
+}
+
+// The K loop of one tile: stage s % 2 is computed while step s+1 is loaded into the
+// other stage. With an odd number of steps the first runs from stage 1, so the rest
+// pair up (stage 0, stage 1). On exit no load is in flight and every wave is past the
+// last read of the stages.
 template <bool GATED, int NM>
-__device__ __forceinline__ void mainloop(const TileCtx& c, unsigned char* smem, f32x4 (&acc)[8][4]) {
-  const int tid = threadIdx.x, lane = tid % kWave, wave = tid / kWave;
-  const int g = __builtin_amdgcn_readfirstlane(wave / 4), wn = wave % 4;
-  const int gt = tid % 256, cc = gt % 8, cr = gt / 8;
-  const int last = c.nk - 1;
-  auto la = [&](int st) { return smem + st * kStageBytes; };
-  auto lb = [&](int st) { return smem + 2 * kStageBytes + st * kStageBytes; };
-  auto lsa = [&](int st) { return reinterpret_cast<float*>(smem + 4 * kStageBytes + st * kScaleBytes); };
+__device__ __forceinline__ void mainloop(const TileCtx& c, f32x4 (&acc)[8][4]) {
+  const int tid = threadIdx.x, lane = tid % kWave;
+  const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);
+  const int g = wave / 4, wn = wave % 4;
   const int arow0 = 128 * g + lane % 16;
   int brow[4];
 #pragma unroll
@@ -93,61 +204,24 @@ __device__ __forceinline__ void mainloop(const TileCtx& c, unsigned char* smem, 
     else
       brow[nb] = 64 * wn + 16 * nb + lane % 16;
   }
-  uint4 ra[4], rb[4];
-  float rs = 0.0f;
-  auto gload = [&](int kt) {
-    kt = kt < last ? kt : last;
-    const int64_t aoff = static_cast<int64_t>(kt) * BK;
-    const int64_t boff = b_offset(kt, c.kseg_steps, c.kseg_inv, c.seg_stride, BK);
-#pragma unroll
-    for (int i = 0; i < 4; ++i) ra[i] = ld16(c.arow[i] + aoff);
-#pragma unroll
-    for (int i = 0; i < 4; ++i) rb[i] = ld16(c.b + static_cast<int64_t>(32 * i) * c.ldb + boff);
-    if (gt < 128) rs = c.sa_row[kt];
-  };
-  auto lstore = [&](int st) {
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int r = 128 * g + cr + 32 * i;
-      *reinterpret_cast<uint4*>(la(st) + swz(r, cc)) = ra[i];
-      *reinterpret_cast<uint4*>(lb(st) + swz(r, cc)) = rb[i];
-    }
-    if (gt < 128) lsa(st)[128 * g + gt] = rs;
-  };
-  auto wscales = [&](int kt, float (&sw)[4]) {
-    const int64_t o = b_offset(kt, c.kseg_steps, c.kseg_inv, c.sb_seg_stride, 1);
-    const float s0 = c.sb[0][o], s1 = c.sb[1][o];
-    sw[0] = sw[1] = s0;
-    sw[2] = sw[3] = s1;
-  };
-  // In its memory half a group stores the registers loaded one K-step earlier, loads
-  // the weight scales of its next compute half, then the tiles of the step after next
-  // (in that order: the scales are waited for first, and loads complete in order).
-  float sw[4];
-  gload(0);
-  lstore(0);
-  if (g == 0) wscales(0, sw);
-  gload(1);
-  __syncthreads();
-  for (int kt = 0; kt < c.nk; ++kt) {
-    const int cur = kt & 1;
-    if (g == 0) {
-      compute_step<NM>(la(cur), lb(cur), lsa(cur), arow0, brow, sw, lane, acc);
-    } else {
-      lstore(cur ^ 1);
-      wscales(kt, sw);
-      gload(kt + 2);
-    }
-    lds_barrier();
-    if (g == 1) {
-      compute_step<NM>(la(cur), lb(cur), lsa(cur), arow0, brow, sw, lane, acc);
-    } else {
-      lstore(cur ^ 1);
-      wscales(kt + 1 < last ? kt + 1 : last, sw);
-      gload(kt + 2);
-    }
-    lds_barrier();
+  float sw[2];
+  wscales(c, 0, sw);
+  int s = 0;
+  if (c.nk & 1) {  // odd: step 0 from stage 1, the rest in pairs as below
+    dma_step<1>(c, 0);
+    step_barrier();
+    k_step<1, NM, true>(c, 0, arow0, brow, lane, sw, acc);
+    s = 1;
+  } else {
+    dma_step<0>(c, 0);
+    step_barrier();
   }
+  for (; s + 2 < c.nk; s += 2) {
+    k_step<0, NM, true>(c, s, arow0, brow, lane, sw, acc);
+    k_step<1, NM, true>(c, s + 1, arow0, brow, lane, sw, acc);
+  }
+  k_step<0, NM, true>(c, s, arow0, brow, lane, sw, acc);
+  k_step<1, NM, false>(c, s + 1, arow0, brow, lane, sw, acc);
 }
 
 __device__ __forceinline__ uint32_t e4m3(float x) {
@@ -159,7 +233,6 @@ template <bool GATED>
 __global__ __launch_bounds__(kThreads) void grouped_gemm_fp8(Fp8Args fa) {
   const GemmArgs& args = fa.g;
   __shared__ TileMap tm;
-  extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
 
   const int n_r = args.n_r;
   const int bn_out = GATED ? BNB / 2 : BNB;
@@ -169,7 +242,6 @@ __global__ __launch_bounds__(kThreads) void grouped_gemm_fp8(Fp8Args fa) {
 
   const int tid = threadIdx.x, lane = tid % kWave, wave = tid / kWave;
   const int g = wave / 4, wn = wave % 4;
-  const int gt = tid % 256, cc = gt % 8, gr = gt / 8;
   const uint8_t* a_routed = reinterpret_cast<const uint8_t*>(args.a_routed);
   const uint8_t* a_shared = reinterpret_cast<const uint8_t*>(args.a_shared);
 
@@ -186,32 +258,49 @@ __global__ __launch_bounds__(kThreads) void grouped_gemm_fp8(Fp8Args fa) {
       if (routed) return args.gather ? args.gather[row_base + m] : (row_base + m);
       return m;
     };
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int64_t src = src_row(128 * g + gr + 32 * i);
-      c.arow[i] = (routed ? a_routed + src * args.lda_routed : a_shared + src * args.lda_shared) + cc * 16;
-    }
-    {
-      const int64_t src = src_row(128 * g + (gt & 127));
-      c.sa_row = routed ? fa.sa_routed + src * fa.ldsa_routed : fa.sa_shared + src * fa.ldsa_shared;
-    }
     const int64_t eidx = routed ? t.group : sg;
     const int64_t eoff = eidx * args.b_expert_stride;
     const uint8_t* b1r = reinterpret_cast<const uint8_t*>(args.b1_routed);
     const uint8_t* b3r = reinterpret_cast<const uint8_t*>(args.b3_routed);
     const uint8_t* b1s = reinterpret_cast<const uint8_t*>(args.b1_shared);
     const uint8_t* b3s = reinterpret_cast<const uint8_t*>(args.b3_shared);
-    const uint8_t* base;
-    int64_t nrow;
-    if (GATED) {
-      base = (g == 0 ? (routed ? b1r : b1s) : (routed ? b3r : b3s)) + eoff;
-      nrow = t.n0 + gr;
-    } else {
-      base = routed ? b1r + eoff : b1s;
-      nrow = t.n0 + 128 * g + gr;
+    c.load_a = __builtin_amdgcn_readfirstlane(32 * wave < t.rows ? 1 : 0) != 0;
+    {
+      const uint32_t lds0 = static_cast<uint32_t>(reinterpret_cast<uintptr_t>((lds_ptr)(stages)));
+      const int wv = __builtin_amdgcn_readfirstlane(wave);
+      c.lds_wave = lds0 + static_cast<uint32_t>(32 * wv * BK);
+      c.lds_scale = lds0 + static_cast<uint32_t>(2 * kOperand + 4 * kWave * wv);
+      c.load_scale = wv < BM / kWave;
     }
-    c.b = base + nrow * args.ldb + cc * 16;
-    c.ldb = args.ldb;
+    // this lane's load rows: 32*wave + 8j + lane/8 of the tile, slot lane%8, holding
+    // global chunk slot ^ ((row/2)%8) (the swizzle of swz)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int r = 32 * wave + 8 * j + lane / 8;
+      const int chunk = (lane % 8) ^ ((r >> 1) & 7);
+      const int64_t src = src_row(r);
+      c.a[j] = (routed ? a_routed + src * args.lda_routed : a_shared + src * args.lda_shared) + chunk * 16;
+    }
+    {
+      const int r = 32 * wave + lane / 8;
+      const int chunk = (lane % 8) ^ ((r >> 1) & 7);
+      const uint8_t* base;
+      int64_t nrow;
+      if (GATED) {  // tile rows 0..127 gate, 128..255 up (a wave's 32 rows lie in one)
+        base = (r < 128 ? (routed ? b1r : b1s) : (routed ? b3r : b3s)) + eoff;
+        nrow = t.n0 + (r & 127);
+      } else {
+        base = routed ? b1r + eoff : b1s;
+        nrow = t.n0 + r;
+      }
+      c.b = base + nrow * args.ldb + chunk * 16;
+      c.ldb8 = 8 * args.ldb;
+      c.odd_chunk = ((chunk ^ 4) - chunk) * 16;
+    }
+    {
+      const int64_t src = src_row(tid & (BM - 1));
+      c.sa_row = routed ? fa.sa_routed + src * fa.ldsa_routed : fa.sa_shared + src * fa.ldsa_shared;
+    }
     // weight-scale rows: [expert][N/128][K/128]
     const int64_t sbe = (routed || GATED) ? eidx * fa.sb_expert_stride : 0;
     if (GATED) {
@@ -237,12 +326,12 @@ __global__ __launch_bounds__(kThreads) void grouped_gemm_fp8(Fp8Args fa) {
     int vblk = (t.rows - 128 * g + 31) / 32;
     vblk = vblk < 0 ? 0 : (vblk > 4 ? 4 : vblk);
     vblk = __builtin_amdgcn_readfirstlane(vblk);
-    switch (vblk) {
-      case 4: mainloop<GATED, 4>(c, smem, acc); break;
-      case 3: mainloop<GATED, 3>(c, smem, acc); break;
-      case 2: mainloop<GATED, 2>(c, smem, acc); break;
-      case 1: mainloop<GATED, 1>(c, smem, acc); break;
-      default: mainloop<GATED, 0>(c, smem, acc); break;
+    switch (vblk) {  // every wave runs the same loads and barriers; only the MFMA count differs
+      case 4: mainloop<GATED, 4>(c, acc); break;
+      case 3: mainloop<GATED, 3>(c, acc); break;
+      case 2: mainloop<GATED, 2>(c, acc); break;
+      case 1: mainloop<GATED, 1>(c, acc); break;
+      default: mainloop<GATED, 0>(c, acc); break;
     }
 
     // epilogue: C layout of the 16x16 MFMA -- lane holds column lane%16 and rows
@@ -251,7 +340,7 @@ __global__ __launch_bounds__(kThreads) void grouped_gemm_fp8(Fp8Args fa) {
     if (GATED) {
       // H = SiLU(gate) * up, then per-row 1x128 quantisation over the tile's 128 gate
       // columns (spread over the 4 waves of the group): amax per row via LDS
-      float* amaxbuf = reinterpret_cast<float*>(smem);  // [4 waves][256 rows]
+      float* amaxbuf = reinterpret_cast<float*>(stage<0>());  // [4 waves][256 rows]
       float h[8][2][4];
 #pragma unroll
       for (int mb = 0; mb < 8; ++mb)
@@ -322,18 +411,14 @@ __global__ __launch_bounds__(kThreads) void grouped_gemm_fp8(Fp8Args fa) {
 
 }  // namespace
 
-size_t ffn_fp8_lds_bytes() { return 4 * kStageBytes + 2 * kScaleBytes; }
+size_t ffn_fp8_lds_bytes() { return 2 * kStageSize; }
 
 hipError_t launch_grouped_gemm_fp8(const Fp8Args& args, bool gated, int grid, hipStream_t stream) {
-  const size_t lds = ffn_fp8_lds_bytes();
-  const void* fn = gated ? reinterpret_cast<const void*>(grouped_gemm_fp8<true>)
-                         : reinterpret_cast<const void*>(grouped_gemm_fp8<false>);
-  hipError_t err = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(lds));
-  if (err != hipSuccess) return err;
+  if (args.g.K % BK != 0) return hipErrorInvalidValue;
   if (gated)
-    hipLaunchKernelGGL(grouped_gemm_fp8<true>, dim3(grid), dim3(kThreads), lds, stream, args);
+    hipLaunchKernelGGL(grouped_gemm_fp8<true>, dim3(grid), dim3(kThreads), 0, stream, args);
   else
-    hipLaunchKernelGGL(grouped_gemm_fp8<false>, dim3(grid), dim3(kThreads), lds, stream, args);
+    hipLaunchKernelGGL(grouped_gemm_fp8<false>, dim3(grid), dim3(kThreads), 0, stream, args);
   return hipGetLastError();
 }
 
