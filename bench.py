@@ -258,7 +258,7 @@ def main():
         "roofline": roof,
     }
     if args.cpu:
-        n = args.cpu_tokens or (512 if w.d <= 2048 else 192)
+        n = args.cpu_tokens or (1024 if w.d <= 2048 else 384)
         res["cpu_baseline"] = cpu_baseline(w, min(n, w.T))
     print(json.dumps(res), flush=True)
 
