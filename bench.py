@@ -42,6 +42,8 @@ def parse():
     p.add_argument("--cpu-baseline", dest="cpu", action="store_true", default=True)
     p.add_argument("--no-cpu-baseline", dest="cpu", action="store_false")
     p.add_argument("--cpu-tokens", type=int, default=0, help="oracle sample size (0 = auto)")
+    p.add_argument("--layout", choices=["tiled", "rows"], default="tiled",
+                   help="expert weight layout: tiled (packed once at setup by moe_pack_weights) or row-major")
     p.add_argument("--calibrate-copy", action="store_true",
                    help="also run one plain 1 GiB device copy (the reference for FETCH_SIZE/WRITE_SIZE)")
     return p.parse_args()
@@ -53,49 +55,55 @@ def kernel_source_hash() -> str:
     import hashlib
     h = hashlib.sha256()
     csrc = os.path.join(ROOT, "mixture_experts_layer_26_amd", "csrc")
-    for f in ("gemm_common.h", "ffn_bf16.hip", "ffn_fp8.hip", "device.h"):
+    for f in ("gemm_common.h", "ffn_bf16.hip", "ffn_fp8.hip", "device.h", "pack.hip"):
         with open(os.path.join(csrc, f), "rb") as fh:
             h.update(fh.read())
     return h.hexdigest()[:16]
 
 
-def stored_traffic(workload: str):
+def stored_traffic(workload: str, layout: str):
     """HBM bytes per grouped-FFN call from the committed counter runs (profiles/), or
-    None when absent or taken on other kernel sources."""
+    None when absent or taken on other kernel sources or another weight layout."""
     path = os.path.join(ROOT, "profiles", f"traffic_{workload}.json")
     if not os.path.exists(path):
         return None
     with open(path) as f:
         t = json.load(f)
-    if t.get("kernel_source_hash") != kernel_source_hash():
+    if t.get("kernel_source_hash") != kernel_source_hash() or t.get("weights", "rows") != layout:
         return None
     return t
 
 
-def setup(wname: str):
+def setup(wname: str, layout: str):
     import torch
 
+    from mixture_experts_layer_26_amd import abi
     from mixture_experts_layer_26_amd import inputs as I
     from mixture_experts_layer_26_amd.inputs import device as D
-    from mixture_experts_layer_26_amd.layer import MoeLayer, quantize_experts
+    from mixture_experts_layer_26_amd.layer import MoeLayer, pack_experts, quantize_experts
 
     w = I.WORKLOADS[wname]
     t0 = time.time()
     dev = D.upload(w, "cuda")
     L = MoeLayer(w.T, w.d, w.n_routed, w.top_k, w.n_shared, w.d_ff, w.act, w.ffn)
-    if w.ffn == "fp8":
-        routed = quantize_experts(dev["routed"])
-        shared = quantize_experts(dev["shared"]) if dev["shared"] is not None else None
-        dev["routed"], dev["shared"] = None, None
-        torch.cuda.synchronize()
-        torch.cuda.empty_cache()
-        L.set_experts(routed, shared)
-        dev["fp8"] = (routed, shared)
-    else:
-        L.set_experts(dev["routed"], dev["shared"])
+    routed, shared = dev["routed"], dev["shared"]
+    if w.ffn == "fp8":  # one-time preparation of the weights, outside the timed region
+        routed = quantize_experts(routed)
+        shared = quantize_experts(shared) if shared is not None else None
+    lay = abi.MOE_LAYOUT_ROWS
+    if layout == "tiled" and w.ffn != "f32":
+        routed = pack_experts(L.shape, routed)
+        shared = pack_experts(L.shape, shared) if shared is not None else None
+        lay = abi.MOE_LAYOUT_TILED
+    dev["routed"], dev["shared"] = None, None
     torch.cuda.synchronize()
-    log(f"[bench] {wname}: inputs generated and resident in {time.time() - t0:.1f} s")
-    return w, dev, L
+    torch.cuda.empty_cache()
+    L.set_experts(routed, shared, lay)
+    dev["weights"] = (routed, shared)
+    torch.cuda.synchronize()
+    log(f"[bench] {wname}: inputs generated and resident in {time.time() - t0:.1f} s "
+        f"({'tiled' if lay == abi.MOE_LAYOUT_TILED else 'row-major'} weights)")
+    return w, dev, L, ("tiled" if lay == abi.MOE_LAYOUT_TILED else "rows")
 
 
 def time_steps(w, dev, L, steps: int, warmup: int):
@@ -205,7 +213,7 @@ def main():
     assert torch.cuda.is_available(), "bench needs a GPU"
     from mixture_experts_layer_26_amd import inputs as I  # noqa: F401
 
-    w, dev, L = setup(args.workload)
+    w, dev, L, layout = setup(args.workload, args.layout)
     if args.calibrate_copy:
         src = torch.empty(1 << 30, dtype=torch.uint8, device="cuda")
         dst = torch.empty_like(src)
@@ -221,7 +229,7 @@ def main():
     ffn_tf = w.ffn_flops() / (ffn_avg * 1e-3) / 1e12
     dt = "fp8" if w.ffn == "fp8" else w.act
     abytes, active = ffn_algorithmic_bytes(w, L)
-    traffic = stored_traffic(w.name)
+    traffic = stored_traffic(w.name, layout)
     decode = w.T * w.top_k < 32 * w.n_routed  # under one MFMA block of rows per expert: weight streaming
     if decode:
         gbs = abytes / (ffn_avg * 1e-3) / 1e9
@@ -251,7 +259,7 @@ def main():
         "dtype": dt,
         "data": "synthetic (seeded Philox/Box-Muller inputs, random-init expert weights)",
         "config": {"workload": w.name, "T": w.T, "d": w.d, "n_routed": w.n_routed, "top_k": w.top_k,
-                   "n_shared": w.n_shared, "d_ff": w.d_ff, "act": w.act, "ffn": w.ffn},
+                   "n_shared": w.n_shared, "d_ff": w.d_ff, "act": w.act, "ffn": w.ffn, "weights": layout},
         "layer_tflops": round(tflops, 2),
         "layer_frac_of_peak": round(tflops / PEAKS[dt], 4),
         "call_ms": calls,

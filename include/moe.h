@@ -39,7 +39,7 @@
 extern "C" {
 #endif
 
-#define MOE_ABI_VERSION 1
+#define MOE_ABI_VERSION 2
 
 typedef enum {
   MOE_OK = 0,
@@ -67,16 +67,24 @@ typedef struct {
   int32_t act, ffn; /* moe_dtype */
 } moe_shape;
 
+/* Weight layouts. ROWS: [E, N, K] row-major as listed below. TILED: the same values
+ * reordered by moe_pack_weights so that each GEMM tile's K-step is contiguous in HBM
+ * (bf16 and FP8 only). */
+typedef enum { MOE_LAYOUT_ROWS = 0, MOE_LAYOUT_TILED = 1 } moe_weight_layout;
+
 /* Expert weights of one kind (routed: E = n_routed; shared: E = n_shared).
  *   w1, w3: [E, d_ff, d]  gate and up projections (row j of expert i = output j)
  *   w2:     [E, d, d_ff]  down projection
  * Element type: fp32 (ffn F32), bf16 (ffn BF16) or E4M3 codes, one byte each (FP8).
  * For FP8 the 128x128 block scales (fp32) are
  *   s1, s3: [E, d_ff/128, d/128]    s2: [E, d/128, d_ff/128]
- * and NULL otherwise. Weights are quantised once with moe_quantize_fp8(.., 128, 128). */
+ * and NULL otherwise (scales are never tiled). Weights are quantised once with
+ * moe_quantize_fp8(.., 128, 128), on the row-major layout.
+ * layout: moe_weight_layout of w1, w3 and w2. */
 typedef struct {
   const void *w1, *w3, *w2;
   const float *s1, *s3, *s2;
+  int32_t layout;
 } moe_expert_set;
 
 /* ---------------------------------------------------------------------------
@@ -116,7 +124,10 @@ moe_status moe_dispatch(const moe_shape* shape, const int32_t* topk_idx, int32_t
  *   y_shared      [T, d]       out, fp32: sum over the shared experts (zeros if N_s = 0)
  *   ws            workspace of moe_workspace_bytes(shape, MOE_CALL_GROUPED_FFN) bytes;
  *                 holds H (and, for FP8, the 1x128-quantised u and H with their scales)
- * H is rounded to the GEMM operand type (fp32, bf16; FP8: fp32 then 1x128 E4M3). */
+ *                 and the GEMMs' tile-scheduling state
+ * H is rounded to the GEMM operand type (fp32, bf16; FP8: fp32 then 1x128 E4M3).
+ * routed and shared must have the same layout; TILED needs ffn BF16 or FP8 (else
+ * MOE_ERR_UNSUPPORTED). Both layouts give bit-identical results. */
 moe_status moe_grouped_ffn(const moe_shape* shape, const void* u, const int32_t* expert_offset,
                            const int32_t* sorted_token, const moe_expert_set* routed,
                            const moe_expert_set* shared, void* y_routed, float* y_shared,
@@ -148,6 +159,22 @@ moe_status moe_bias_update(const moe_shape* shape, const int32_t* expert_count, 
  *   q [rows, cols] uint8 out; scale [rows/tile_r, cols/tile_c] fp32 out. */
 moe_status moe_quantize_fp8(const void* x, int32_t xt, int64_t rows, int64_t cols, int32_t tile_r,
                             int32_t tile_c, uint8_t* q, float* scale, void* stream);
+
+/* ---------------------------------------------------------------------------
+ * moe_pack_weights: reorders one weight array of an expert set from the ROWS layout
+ * into the TILED layout read by moe_grouped_ffn. Not a step of the layer: a one-time
+ * preparation, like the FP8 quantisation of the weights. With KS = 128 bytes of K
+ * (64 bf16 or 128 FP8 codes) and R = 128 for W1/W3 (N = d_ff, K = d) or 256 for W2
+ * (N = d, K = d_ff), [E, N, K] becomes [E][N/R][K/KS][R][KS].
+ *   matrix      MOE_W1, MOE_W3 or MOE_W2
+ *   n_experts   E (>= 1)
+ *   src, dst    device arrays of E*N*K elements of the ffn dtype (bf16 or E4M3 codes);
+ *               they must not overlap
+ * Needs a shape the MFMA kernels tile (d % 256 == 0, d_ff % 128 == 0); ffn F32 gives
+ * MOE_ERR_UNSUPPORTED. */
+enum { MOE_W1 = 0, MOE_W3 = 1, MOE_W2 = 2 };
+moe_status moe_pack_weights(const moe_shape* shape, int32_t matrix, int64_t n_experts, const void* src,
+                            void* dst, void* stream);
 
 /* workspace sizing: call = MOE_CALL_DISPATCH or MOE_CALL_GROUPED_FFN; 0 for others
  * and for invalid shapes */

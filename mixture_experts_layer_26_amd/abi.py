@@ -16,6 +16,9 @@ LIB_PATH = os.path.join(HERE, "libmoe.so")
 MOE_OK, MOE_ERR_INVALID_ARG, MOE_ERR_UNSUPPORTED, MOE_ERR_WORKSPACE, MOE_ERR_HIP = range(5)
 MOE_F32, MOE_BF16, MOE_FP8_E4M3 = 0, 1, 2
 MOE_CALL_ROUTE, MOE_CALL_DISPATCH, MOE_CALL_GROUPED_FFN, MOE_CALL_COMBINE, MOE_CALL_BIAS_UPDATE = range(5)
+MOE_LAYOUT_ROWS, MOE_LAYOUT_TILED = 0, 1
+MOE_W1, MOE_W3, MOE_W2 = 0, 1, 2
+ABI_VERSION = 2
 DTYPES = {"f32": MOE_F32, "bf16": MOE_BF16, "fp8": MOE_FP8_E4M3}
 
 
@@ -33,7 +36,8 @@ class moe_shape(ctypes.Structure):
 
 class moe_expert_set(ctypes.Structure):
     _fields_ = [("w1", ctypes.c_void_p), ("w3", ctypes.c_void_p), ("w2", ctypes.c_void_p),
-                ("s1", ctypes.c_void_p), ("s3", ctypes.c_void_p), ("s2", ctypes.c_void_p)]
+                ("s1", ctypes.c_void_p), ("s3", ctypes.c_void_p), ("s2", ctypes.c_void_p),
+                ("layout", ctypes.c_int32)]
 
 
 _lib = None
@@ -58,6 +62,7 @@ def load():
         "moe_combine": [sp, vp, vp, vp, vp, vp, vp, vp],
         "moe_bias_update": [sp, vp, f32, vp, vp],
         "moe_quantize_fp8": [vp, i32, i64, i64, i32, i32, vp, vp, vp],
+        "moe_pack_weights": [sp, i32, i64, vp, vp, vp],
     }
     for name, args in sig.items():
         fn = getattr(lib, name)
@@ -99,8 +104,8 @@ def make_shape(T, d, n_routed, top_k, n_shared, d_ff, act="bf16", ffn="bf16") ->
     return moe_shape(T, d, n_routed, top_k, n_shared, d_ff, DTYPES[act], DTYPES[ffn])
 
 
-def make_expert_set(w1, w3, w2, s1=None, s3=None, s2=None) -> moe_expert_set:
-    return moe_expert_set(_ptr(w1), _ptr(w3), _ptr(w2), _ptr(s1), _ptr(s3), _ptr(s2))
+def make_expert_set(w1, w3, w2, s1=None, s3=None, s2=None, layout: int = MOE_LAYOUT_ROWS) -> moe_expert_set:
+    return moe_expert_set(_ptr(w1), _ptr(w3), _ptr(w2), _ptr(s1), _ptr(s3), _ptr(s2), layout)
 
 
 def moe_workspace_bytes(shape: moe_shape, call: int) -> int:
@@ -136,6 +141,11 @@ def moe_combine(shape, u, y_routed, y_shared, pair_row, topk_gate, out, stream=N
 def moe_bias_update(shape, expert_count, gamma, bias, stream=None):
     _check("moe_bias_update", load().moe_bias_update(ctypes.byref(shape), _ptr(expert_count), gamma,
                                                      _ptr(bias), _stream(stream)))
+
+
+def moe_pack_weights(shape, matrix: int, n_experts: int, src, dst, stream=None):
+    _check("moe_pack_weights", load().moe_pack_weights(ctypes.byref(shape), matrix, n_experts, _ptr(src), _ptr(dst),
+                                                       _stream(stream)))
 
 
 def moe_quantize_fp8(x, xt: int, rows: int, cols: int, tile_r: int, tile_c: int, q, scale, stream=None):

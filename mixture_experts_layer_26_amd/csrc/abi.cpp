@@ -127,7 +127,7 @@ moe_status grouped_ffn_fp8(const moe_shape* s, const void* u, const int32_t* exp
                            const int32_t* sorted_token, const moe_expert_set* routed,
                            const moe_expert_set* shared, void* y_routed, float* y_shared,
                            unsigned char* wsb, const FfnWorkspace& w, const SchedState& sc, int grid,
-                           hipStream_t st) {
+                           int b_tiled, hipStream_t st) {
   uint8_t* q_u = wsb + w.q_u;
   float* s_u = reinterpret_cast<float*>(wsb + w.s_u);
   uint8_t* h_r = wsb + w.h_routed;
@@ -160,6 +160,7 @@ moe_status grouped_ffn_fp8(const moe_shape* s, const void* u, const int32_t* exp
   f1.g.K = d;
   f1.g.k_segments = 1;
   f1.g.sched = sc.s1;
+  f1.g.b_tiled = b_tiled;
   f1.g.slot_stride = sc.stride1;
   f1.sa_routed = f1.sa_shared = s_u;
   f1.ldsa_routed = f1.ldsa_shared = d / 128;
@@ -197,6 +198,7 @@ moe_status grouped_ffn_fp8(const moe_shape* s, const void* u, const int32_t* exp
   f2.g.K = I;
   f2.g.k_segments = ns;
   f2.g.sched = sc.s2;
+  f2.g.b_tiled = b_tiled;
   f2.g.slot_stride = sc.stride2;
   f2.sa_routed = sh_r;
   f2.ldsa_routed = I / 128;
@@ -266,6 +268,10 @@ moe_status moe_grouped_ffn(const moe_shape* s, const void* u, const int32_t* exp
   if (fp8 && (!routed->s1 || !routed->s3 || !routed->s2 ||
               (s->n_shared > 0 && (!shared->s1 || !shared->s3 || !shared->s2))))
     return MOE_ERR_INVALID_ARG;
+  if (routed->layout != MOE_LAYOUT_ROWS && routed->layout != MOE_LAYOUT_TILED) return MOE_ERR_INVALID_ARG;
+  if (s->n_shared > 0 && shared->layout != routed->layout) return MOE_ERR_INVALID_ARG;
+  const int b_tiled = routed->layout == MOE_LAYOUT_TILED ? 1 : 0;
+  if (b_tiled && s->ffn == MOE_F32) return MOE_ERR_UNSUPPORTED;
   if (!tiled_shape(s)) return MOE_ERR_UNSUPPORTED;
   const FfnWorkspace w = ffn_workspace(s);
   if (!ws || ws_bytes < w.total) return MOE_ERR_WORKSPACE;
@@ -295,7 +301,7 @@ moe_status moe_grouped_ffn(const moe_shape* s, const void* u, const int32_t* exp
   const int64_t n_sched = moe::sched_ints(t1, grid) + moe::sched_ints(t2, grid);
   if (moe::launch_zero_i32(sc.s1, static_cast<int>(n_sched), st) != hipSuccess) return MOE_ERR_HIP;
   if (fp8) return grouped_ffn_fp8(s, u, expert_offset, sorted_token, routed, shared, y_routed, y_shared,
-                                  wsb, w, sc, grid, st);
+                                  wsb, w, sc, grid, b_tiled, st);
   uint16_t* h_r = reinterpret_cast<uint16_t*>(wsb + w.h_routed);
   uint16_t* h_s = reinterpret_cast<uint16_t*>(wsb + w.h_shared);
   const uint16_t* ub = static_cast<const uint16_t*>(u);
@@ -323,6 +329,7 @@ moe_status moe_grouped_ffn(const moe_shape* s, const void* u, const int32_t* exp
   g1.K = s->d;
   g1.k_segments = 1;
   g1.sched = sc.s1;
+  g1.b_tiled = b_tiled;
   g1.slot_stride = sc.stride1;
   hipError_t err = moe::launch_grouped_gemm_bf16(g1, true, grid, st);
   if (err != hipSuccess) return MOE_ERR_HIP;
@@ -349,6 +356,7 @@ moe_status moe_grouped_ffn(const moe_shape* s, const void* u, const int32_t* exp
   g2.K = s->d_ff;
   g2.k_segments = s->n_shared;
   g2.sched = sc.s2;
+  g2.b_tiled = b_tiled;
   g2.slot_stride = sc.stride2;
   (void)P;
   return from_hip(moe::launch_grouped_gemm_bf16(g2, false, grid, st));
@@ -372,6 +380,24 @@ moe_status moe_bias_update(const moe_shape* s, const int32_t* expert_count, floa
   if (!(gamma >= 0.0f) || gamma > 1.0f) return MOE_ERR_INVALID_ARG;
   return from_hip(moe::launch_bias_update(expert_count, s->T, s->n_routed, s->top_k, gamma, bias,
                                           as_stream(stream)));
+}
+
+moe_status moe_pack_weights(const moe_shape* s, int32_t matrix, int64_t n_experts, const void* src, void* dst,
+                            void* stream) {
+  if (!valid_shape(s) || !src || !dst || n_experts < 1) return MOE_ERR_INVALID_ARG;
+  if (matrix != MOE_W1 && matrix != MOE_W3 && matrix != MOE_W2) return MOE_ERR_INVALID_ARG;
+  if (s->ffn == MOE_F32) return MOE_ERR_UNSUPPORTED;
+  if (!tiled_shape(s)) return MOE_ERR_UNSUPPORTED;
+  const int esz = s->ffn == MOE_FP8_E4M3 ? 1 : 2;
+  const int64_t N = matrix == MOE_W2 ? s->d : s->d_ff;
+  const int64_t K = matrix == MOE_W2 ? s->d_ff : s->d;
+  const int R = matrix == MOE_W2 ? 256 : 128;
+  const int64_t bytes = n_experts * N * K * esz;
+  if (n_experts > (1LL << 40) / (N * K)) return MOE_ERR_INVALID_ARG;
+  const char* a = static_cast<const char*>(src);
+  const char* b = static_cast<const char*>(dst);
+  if (a < b + bytes && b < a + bytes) return MOE_ERR_INVALID_ARG;  // overlap
+  return from_hip(moe::launch_pack_weights(src, dst, esz, n_experts, N, K, R, as_stream(stream)));
 }
 
 moe_status moe_quantize_fp8(const void* x, int32_t xt, int64_t rows, int64_t cols, int32_t tile_r,

@@ -63,6 +63,7 @@ struct TileCtx {
   const uint16_t* a[4];  // this lane's four A rows (chunk included)
   const uint16_t* b[4];  // this lane's four B rows (chunk included)
   int64_t seg_stride;    // phase 2 shared: W2 stride per K segment, else 0
+  int bstep;             // elements from one K-step of a B row to the next
   int kseg_steps;
   uint32_t kseg_inv;
   int nk;                // K-steps
@@ -77,7 +78,7 @@ template <int ST>
 __device__ __forceinline__ void dma_step(const TileCtx& c, int kt, int wave) {
   unsigned char* st = stage<ST>();
   const int64_t aoff = static_cast<int64_t>(kt) * BK;
-  const int64_t boff = b_offset(kt, c.kseg_steps, c.kseg_inv, c.seg_stride, BK);
+  const int64_t boff = b_offset(kt, c.kseg_steps, c.kseg_inv, c.seg_stride, c.bstep);
   if (c.load_a) {
 #pragma unroll
     for (int j = 0; j < 4; ++j) dma16(c.a[j] + aoff, st + (32 * wave + 8 * j) * kRow);
@@ -249,9 +250,15 @@ __global__ __launch_bounds__(kThreads) void grouped_gemm_bf16(GemmArgs args) {
         base = routed ? args.b1_routed + eoff : args.b1_shared;
         nrow = t.n0 + r;
       }
-      c.b[j] = base + nrow * args.ldb + chunk * 8;
+      if (args.b_tiled) {  // [E][N/R][K/64][R][64]: one K-step of the tile is R contiguous rows
+        constexpr int R = GATED ? 128 : 256;
+        c.b[j] = base + (t.n0 / R) * (args.ldb / BK) * (R * BK) + static_cast<int64_t>(nrow - t.n0) * BK + chunk * 8;
+      } else {
+        c.b[j] = base + nrow * args.ldb + chunk * 8;
+      }
     }
     c.seg_stride = (!routed && !GATED) ? args.b_expert_stride : 0;
+    c.bstep = args.b_tiled ? (GATED ? 128 : 256) * BK : BK;
     c.kseg_steps = args.K / BK;
     c.kseg_inv = static_cast<uint32_t>((0x100000000ull + c.kseg_steps - 1) / c.kseg_steps);
     c.nk = (routed ? args.K : args.K * (GATED ? 1 : args.k_segments)) / BK;

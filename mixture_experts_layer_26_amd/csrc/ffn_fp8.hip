@@ -72,6 +72,7 @@ struct TileCtx {
   const float* sa_row;      // threads 0..255: A-row scales of tile row tid (K-block 0)
   const float* sb[2];       // this wave's two B-scale rows (gate/up, or the wave's block)
   int64_t seg_stride;       // phase 2 shared: W2 stride per K segment, else 0
+  int bstep;                // bytes from one K-step of a B row to the next
   int64_t sb_seg_stride;    // same for the W2 scales
   int kseg_steps;
   uint32_t kseg_inv;
@@ -85,7 +86,7 @@ struct TileCtx {
 template <int ST>
 __device__ __forceinline__ void dma_step(const TileCtx& c, int kt) {
   const int64_t aoff = static_cast<int64_t>(kt) * BK;
-  const int64_t boff = b_offset(kt, c.kseg_steps, c.kseg_inv, c.seg_stride, BK);
+  const int64_t boff = b_offset(kt, c.kseg_steps, c.kseg_inv, c.seg_stride, c.bstep);
   if (c.load_a) {
     dma16<ST * kStageSize + 0 * 8 * BK>(c.a[0] + aoff, c.lds_wave);
     dma16<ST * kStageSize + 1 * 8 * BK>(c.a[1] + aoff, c.lds_wave);
@@ -293,8 +294,14 @@ __global__ __launch_bounds__(kThreads) void grouped_gemm_fp8(Fp8Args fa) {
         base = routed ? b1r + eoff : b1s;
         nrow = t.n0 + r;
       }
-      c.b = base + nrow * args.ldb + chunk * 16;
-      c.ldb8 = 8 * args.ldb;
+      if (args.b_tiled) {  // [E][N/R][K/128][R][128]: one K-step of the tile is R contiguous rows
+        constexpr int R = GATED ? 128 : 256;
+        c.b = base + (t.n0 / R) * (args.ldb / BK) * (R * BK) + static_cast<int64_t>(nrow - t.n0) * BK + chunk * 16;
+        c.ldb8 = 8 * BK;
+      } else {
+        c.b = base + nrow * args.ldb + chunk * 16;
+        c.ldb8 = 8 * args.ldb;
+      }
       c.odd_chunk = ((chunk ^ 4) - chunk) * 16;
     }
     {
@@ -312,6 +319,7 @@ __global__ __launch_bounds__(kThreads) void grouped_gemm_fp8(Fp8Args fa) {
       c.sb[0] = c.sb[1] = (routed ? fa.sb1_routed : fa.sb1_shared) + sbe + nblk * fa.kblocks;
     }
     c.seg_stride = (!routed && !GATED) ? args.b_expert_stride : 0;
+    c.bstep = args.b_tiled ? (GATED ? 128 : 256) * BK : BK;
     c.sb_seg_stride = (!routed && !GATED) ? fa.sb_expert_stride : 0;
     c.kseg_steps = args.K / BK;
     c.kseg_inv = static_cast<uint32_t>((0x100000000ull + c.kseg_steps - 1) / c.kseg_steps);

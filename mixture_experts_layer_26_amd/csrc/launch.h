@@ -22,6 +22,7 @@ struct GemmArgs {
   const uint16_t* b3_shared;
   int64_t b_expert_stride;   // elements per expert in the weight arrays
   int64_t ldb;               // row length of B (the K extent of one expert)
+  int b_tiled;               // weights in the tiled layout (see moe_pack_weights)
   void* out_routed;          // phase 1: H routed (bf16); phase 2: y_routed (bf16)
   void* out_shared;          // phase 1: H shared (bf16); phase 2: y_shared (fp32)
   int64_t ldo_routed, ldo_shared;
@@ -94,6 +95,11 @@ hipError_t launch_combine(int act, const void* u, const void* y_routed, const fl
 
 hipError_t launch_bias_update(const int32_t* count, int64_t T, int n_r, int K, float gamma,
                               float* bias, hipStream_t stream);
+
+// Tiled weight layout: [E, N, K] row-major -> [E][N/R][K/KS][R][KS], KS elements = 128
+// bytes (64 bf16, 128 fp8), R = 128 (gate/up) or 256 (down).
+hipError_t launch_pack_weights(const void* src, void* dst, int esz, int64_t E, int64_t N, int64_t K, int R,
+                               hipStream_t stream);
 
 hipError_t launch_quantize_fp8(const void* x, int xt, int64_t rows, int64_t cols, int tile_r,
                                int tile_c, uint8_t* q, float* scale, hipStream_t stream);

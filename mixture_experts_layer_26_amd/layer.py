@@ -41,11 +41,13 @@ class MoeLayer:
         self.shared = None
         self._keep = []
 
-    def set_experts(self, routed: tuple, shared: tuple | None):
-        """routed/shared: (w1, w3, w2) device tensors, or (w1, w3, w2, s1, s3, s2) for FP8."""
+    def set_experts(self, routed: tuple, shared: tuple | None, layout: int = abi.MOE_LAYOUT_ROWS):
+        """routed/shared: (w1, w3, w2) device tensors, or (w1, w3, w2, s1, s3, s2) for FP8, in
+        the given weight layout (ROWS, or TILED as made by pack_experts)."""
         self._keep = [routed, shared]
-        self.routed = abi.make_expert_set(*routed)
-        self.shared = abi.make_expert_set(*shared) if shared is not None else None
+        w = lambda t: tuple(t) + (None,) * (6 - len(t))
+        self.routed = abi.make_expert_set(*w(routed), layout=layout)
+        self.shared = abi.make_expert_set(*w(shared), layout=layout) if shared is not None else None
 
     # -- the five calls ----------------------------------------------------------
     def route(self, u, centroids, bias, stream=None):
@@ -89,3 +91,14 @@ def quantize_experts(ws: tuple, stream=None) -> tuple:
         outs_q.append(q)
         outs_s.append(s)
     return tuple(outs_q) + tuple(outs_s)
+
+
+def pack_experts(shape, ws: tuple, stream=None) -> tuple:
+    """The TILED layout of stacked expert weights (w1, w3, w2[, s1, s3, s2]) made by
+    moe_pack_weights; scales are passed through unchanged."""
+    out = []
+    for m, w in zip((abi.MOE_W1, abi.MOE_W3, abi.MOE_W2), ws[:3]):
+        t = torch.empty_like(w)
+        abi.moe_pack_weights(shape, m, w.shape[0], w, t, stream)
+        out.append(t)
+    return tuple(out) + tuple(ws[3:])

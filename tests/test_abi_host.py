@@ -23,7 +23,7 @@ def test_exports_every_declared_symbol():
     assert {"moe_route", "moe_dispatch", "moe_grouped_ffn", "moe_combine", "moe_bias_update"} <= set(names)
     for n in names:
         assert hasattr(lib, n), n
-    assert lib.moe_abi_version() == 1
+    assert lib.moe_abi_version() == abi.ABI_VERSION == 2
     assert lib.moe_status_string(0) == b"ok"
 
 
@@ -98,3 +98,31 @@ def test_quantize_args_rejected():
     assert q(FAKE, abi.MOE_F32, 128, 128, 64, 64, FAKE, FAKE, None) == abi.MOE_ERR_UNSUPPORTED
     assert q(FAKE, 7, 128, 128, 1, 128, FAKE, FAKE, None) == abi.MOE_ERR_INVALID_ARG
     assert q(None, abi.MOE_F32, 128, 128, 1, 128, FAKE, FAKE, None) == abi.MOE_ERR_INVALID_ARG
+
+
+def test_weight_layout_checks():
+    lib = abi.load()
+    sb = _shape(d=256, d_ff=128, act="bf16", ffn="bf16")
+    rows = abi.make_expert_set(FAKE, FAKE, FAKE)
+    tiled = abi.make_expert_set(FAKE, FAKE, FAKE, layout=abi.MOE_LAYOUT_TILED)
+    bad = abi.make_expert_set(FAKE, FAKE, FAKE, layout=7)
+    ffn = lambda s, r, sh: lib.moe_grouped_ffn(ctypes.byref(s), FAKE, FAKE, FAKE, ctypes.byref(r), ctypes.byref(sh),
+                                               FAKE, FAKE, FAKE, 1 << 30, None)
+    assert ffn(sb, bad, bad) == abi.MOE_ERR_INVALID_ARG
+    assert ffn(sb, tiled, rows) == abi.MOE_ERR_INVALID_ARG  # routed and shared must agree
+    s32 = _shape()  # fp32 expert GEMMs read only the row-major layout
+    assert ffn(s32, tiled, tiled) == abi.MOE_ERR_UNSUPPORTED
+
+
+def test_pack_weights_args_rejected():
+    lib = abi.load()
+    p = lambda s, m, e, a, b: lib.moe_pack_weights(ctypes.byref(s), m, e, a, b, None)
+    sb = _shape(d=256, d_ff=128, act="bf16", ffn="bf16")
+    other = FAKE + (1 << 30)
+    assert p(sb, 3, 1, FAKE, other) == abi.MOE_ERR_INVALID_ARG            # no such matrix
+    assert p(sb, abi.MOE_W1, 0, FAKE, other) == abi.MOE_ERR_INVALID_ARG   # no experts
+    assert p(sb, abi.MOE_W1, 1, None, other) == abi.MOE_ERR_INVALID_ARG
+    assert p(sb, abi.MOE_W2, 2, FAKE, FAKE + 1024) == abi.MOE_ERR_INVALID_ARG  # overlapping
+    assert p(_shape(), abi.MOE_W1, 1, FAKE, other) == abi.MOE_ERR_UNSUPPORTED  # fp32 is never tiled
+    assert p(_shape(d=320, d_ff=128, act="bf16", ffn="bf16"), abi.MOE_W1, 1, FAKE, other) == \
+        abi.MOE_ERR_UNSUPPORTED
