@@ -94,9 +94,13 @@ typedef struct {
  *   bias      [N_r]       fp32, the b_i (read only here)
  *   topk_idx  [T, K]      int32 out: selected expert ids, ascending within a token
  *   topk_gate [T, K]      fp32 out: g_{i,t} aligned with topk_idx; sums to 1 per token
- * Logits accumulate in fp32; ties in s + b go to the lower expert index. */
+ *   ws            workspace of moe_workspace_bytes(shape, MOE_CALL_ROUTE) bytes (the
+ *                 partial logits of the K chunks; 0 bytes, ws may be NULL, for fp32 act)
+ * Logits accumulate in fp32 (bf16: per K chunk, the chunks added in order); ties in
+ * s + b go to the lower expert index. */
 moe_status moe_route(const moe_shape* shape, const void* u, const void* centroids,
-                     const float* bias, int32_t* topk_idx, float* topk_gate, void* stream);
+                     const float* bias, int32_t* topk_idx, float* topk_gate, void* ws,
+                     size_t ws_bytes, void* stream);
 
 /* ---------------------------------------------------------------------------
  * moe_dispatch: the per-expert grouping behind the sums of h'_t (the explainer's
@@ -176,8 +180,8 @@ enum { MOE_W1 = 0, MOE_W3 = 1, MOE_W2 = 2 };
 moe_status moe_pack_weights(const moe_shape* shape, int32_t matrix, int64_t n_experts, const void* src,
                             void* dst, void* stream);
 
-/* workspace sizing: call = MOE_CALL_DISPATCH or MOE_CALL_GROUPED_FFN; 0 for others
- * and for invalid shapes */
+/* workspace sizing: call = MOE_CALL_ROUTE, MOE_CALL_DISPATCH or MOE_CALL_GROUPED_FFN;
+ * 0 for others and for invalid shapes */
 enum { MOE_CALL_ROUTE = 0, MOE_CALL_DISPATCH = 1, MOE_CALL_GROUPED_FFN = 2,
        MOE_CALL_COMBINE = 3, MOE_CALL_BIAS_UPDATE = 4 };
 size_t moe_workspace_bytes(const moe_shape* shape, int32_t call);

@@ -56,7 +56,7 @@ def load():
     sp = ctypes.POINTER(moe_shape)
     ep = ctypes.POINTER(moe_expert_set)
     sig = {
-        "moe_route": [sp, vp, vp, vp, vp, vp, vp],
+        "moe_route": [sp, vp, vp, vp, vp, vp, vp, sz, vp],
         "moe_dispatch": [sp, vp, vp, vp, vp, vp, vp, sz, vp],
         "moe_grouped_ffn": [sp, vp, vp, vp, ep, ep, vp, vp, vp, sz, vp],
         "moe_combine": [sp, vp, vp, vp, vp, vp, vp, vp],
@@ -112,9 +112,9 @@ def moe_workspace_bytes(shape: moe_shape, call: int) -> int:
     return load().moe_workspace_bytes(ctypes.byref(shape), call)
 
 
-def moe_route(shape, u, centroids, bias, topk_idx, topk_gate, stream=None):
+def moe_route(shape, u, centroids, bias, topk_idx, topk_gate, ws, ws_bytes: int, stream=None):
     _check("moe_route", load().moe_route(ctypes.byref(shape), _ptr(u), _ptr(centroids), _ptr(bias),
-                                         _ptr(topk_idx), _ptr(topk_gate), _stream(stream)))
+                                         _ptr(topk_idx), _ptr(topk_gate), _ptr(ws), ws_bytes, _stream(stream)))
 
 
 def moe_dispatch(shape, topk_idx, expert_count, expert_offset, sorted_token, pair_row, ws, ws_bytes,

@@ -233,15 +233,20 @@ size_t moe_workspace_bytes(const moe_shape* s, int32_t call) {
   if (call == MOE_CALL_DISPATCH)
     return align_up(static_cast<size_t>(moe::dispatch_blocks(s->T)) * s->n_routed * sizeof(int32_t));
   if (call == MOE_CALL_GROUPED_FFN) return ffn_workspace(s).total;
+  if (call == MOE_CALL_ROUTE)
+    return s->act == MOE_BF16 ? align_up(moe::route_workspace_bytes(s->T, s->d, s->n_routed)) : 0;
   return 0;
 }
 
 moe_status moe_route(const moe_shape* s, const void* u, const void* centroids, const float* bias,
-                     int32_t* topk_idx, float* topk_gate, void* stream) {
+                     int32_t* topk_idx, float* topk_gate, void* ws, size_t ws_bytes, void* stream) {
   if (!valid_shape(s) || !u || !centroids || !bias || !topk_idx || !topk_gate)
     return MOE_ERR_INVALID_ARG;
+  const size_t need = moe_workspace_bytes(s, MOE_CALL_ROUTE);
+  if (need > 0 && (!ws || ws_bytes < need)) return MOE_ERR_WORKSPACE;
   return from_hip(moe::launch_route(s->act == MOE_BF16 ? 1 : 0, u, centroids, bias, s->T, s->d,
-                                    s->n_routed, s->top_k, topk_idx, topk_gate, as_stream(stream)));
+                                    s->n_routed, s->top_k, topk_idx, topk_gate, static_cast<float*>(ws),
+                                    as_stream(stream)));
 }
 
 moe_status moe_dispatch(const moe_shape* s, const int32_t* topk_idx, int32_t* expert_count,

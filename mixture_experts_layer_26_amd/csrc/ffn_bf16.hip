@@ -9,16 +9,17 @@
 //
 // Kernel shape: a persistent grid of one 8-wave workgroup per CU walks the device-built
 // tile list in gangs (gemm_common.h). A tile is up to 256 rows x 256 weight rows (phase
-// 1: 128 gate + 128 up columns). K advances in steps of 32 through a ring of four LDS
-// stages filled by direct global-to-LDS loads (global_load_lds_dwordx4): no staging
-// registers and no LDS store instructions, and a stage is loaded four steps before it
-// is computed, which covers the HBM latency of the gathered rows and the weight stream.
-// One barrier per step, between its two 16-wide sub-steps, so each wave reads the next
-// step's fragments while the MFMAs of the current one run. Every wave computes a 128 x 64 block with v_mfma_f32_32x32x16_bf16 (8 MFMA
-// tiles): wave (g, wn) owns rows 128g.. of the tile and, in phase 1, gate rows 32wn..
-// and the matching up rows (so SiLU(gate) * up is formed in registers). The K loop is
-// specialised on the number of 32-row blocks of a wave that hold rows, so row blocks
-// past an expert's count cost no MFMA work.
+// 1: 128 gate + 128 up columns). K advances in steps of 64 (128-byte rows) through two
+// LDS stages filled by direct global-to-LDS loads (global_load_lds_dwordx4): no staging
+// registers and no LDS store instructions; a stage is loaded one step before it is
+// computed. One barrier per step, before its last 16-wide sub-step, so each wave reads
+// the next step's first fragments while the MFMAs of the current one run. Every wave
+// computes a 128 x 64 block with v_mfma_f32_32x32x16_bf16 (8 MFMA tiles): wave (g, wn)
+// owns rows 128g.. of the tile and, in phase 1, gate rows 32wn.. and the matching up
+// rows (so SiLU(gate) * up is formed in registers). The K loop is specialised on the
+// number of 32-row blocks of a wave that hold rows, so row blocks past an expert's
+// count cost no MFMA work. Weights are read row-major or in the tiled layout of
+// pack.hip.
 #include "gemm_common.h"
 #include "launch.h"
 

@@ -72,8 +72,16 @@ struct Fp8Args {
 size_t ffn_fp8_lds_bytes();
 hipError_t launch_grouped_gemm_fp8(const Fp8Args& args, bool gated, int grid, hipStream_t stream);
 
+// Router (bf16): the K range is split into chunks of whole 64-wide steps; the partial
+// logits of every chunk, [chunks][T][n_r] fp32, live in the caller's workspace.
+struct RouteChunks {
+  int chunks;
+  int steps_per_chunk;
+};
+RouteChunks route_chunks(int64_t T, int d);
+size_t route_workspace_bytes(int64_t T, int d, int n_r);
 hipError_t launch_route(int act, const void* u, const void* e, const float* bias, int64_t T, int d,
-                        int n_r, int K, int32_t* idx, float* gate, hipStream_t stream);
+                        int n_r, int K, int32_t* idx, float* gate, float* part, hipStream_t stream);
 
 int dispatch_blocks(int64_t T);
 hipError_t launch_dispatch(const int32_t* idx, int64_t T, int K, int n_r, int32_t* hist,

@@ -3,12 +3,14 @@
 // DeepSeek-V3 explainer (xyznot.com), method section 2: the sigmoid affinity and the
 // equation for g'_{i,t}; gates normalise g'.
 //
-// One workgroup of 8 waves owns 32 tokens and every expert. Logits come from bf16
-// MFMA 32x32x16 (fp32 accumulate) straight from global memory: each wave takes two
-// 32-expert blocks over half of K; the 32 x N_r sigmoid scores are parked in LDS, then
-// each wave selects the top-K of 4 tokens with 64-bit (score, ~index) keys reduced
-// across the wave. For fp32 activations the logits are plain fp32 FMA dot products.
-#include "device.h"
+// bf16 activations take two kernels. route_logits: a workgroup owns 128 tokens x 256
+// experts over one chunk of K (the grid splits K so that it fills the chip even for a
+// small batch), stages u and e through swizzled LDS in steps of 64 and accumulates with
+// bf16 MFMA 32x32x16 in fp32; it writes the chunk's partial logits. route_topk: one
+// wave per token adds the chunks' partials in chunk order, takes the sigmoid and
+// selects the top-K with 64-bit (score, ~index) keys reduced across the wave. fp32
+// activations take one kernel of plain fp32 dot products (route_kernel).
+#include "gemm_common.h"
 #include "launch.h"
 
 namespace moe {
@@ -37,91 +39,156 @@ __device__ __forceinline__ uint64_t wave_max_u64(uint64_t x) {
 
 __device__ __forceinline__ float sigmoid_precise(float z) { return 1.0f / (1.0f + expf(-z)); }
 
-// logits of 32 tokens x n_r experts, bf16 inputs, into sc[32][n_r] as sigmoid scores.
-// 8 waves: wave w owns expert blocks (w%4) and (w%4)+4 (32 experts each) over half of
-// the K range (w/4), running both blocks in one loop so each u fragment is loaded once.
-// K advances in chunks of KC*16 with the next chunk's loads in flight. The two K
-// halves meet in LDS and are added in a fixed order (first half + second half).
-template <int KC>
-__device__ void logits_bf16_kc(const uint16_t* __restrict__ u, const uint16_t* __restrict__ e,
-                               int64_t T, int d, int n_r, int64_t t0, float* sc, float* part) {
-  const int lane = threadIdx.x % kWave, wave = threadIdx.x / kWave;
-  const int bp = wave % 4, kh = wave / 4;
-  const int r = lane % 32, koff = (lane / 32) * 8;
-  int64_t trow = t0 + r;
-  if (trow >= T) trow = T - 1;
-  const int nblk = (n_r + 31) / 32;
-  const bool active = bp < nblk;
-  const bool two = bp + 4 < nblk;
-  const int khalf = d / 2;  // d % (2 * KC * 16) == 0 (host check)
-  const uint16_t* ap = u + trow * d + koff + kh * khalf;
-  int e0 = bp * 32 + r, e1 = (bp + 4) * 32 + r;
-  if (e0 >= n_r) e0 = n_r - 1;
-  if (e1 >= n_r) e1 = n_r - 1;
-  if (!two) e1 = e0;
-  const uint16_t* bp0 = e + static_cast<int64_t>(e0) * d + koff + kh * khalf;
-  const uint16_t* bp1 = e + static_cast<int64_t>(e1) * d + koff + kh * khalf;
-  f32x16 acc0 = {}, acc1 = {};
-  if (active) {
-    uint4 a[KC], b0[KC], b1[KC];
-    auto load = [&](int k0) {
+// Top-K of one token held by one wave: lane l holds the keys and scores of experts
+// l + 64 c (c = 0..3; key 0 = no expert). Lane k < K keeps the k-th pick (no per-lane
+// array is indexed at run time); picks are written in ascending expert order with
+// gates = score / (sum of the picked scores, added in ascending expert order).
+__device__ __forceinline__ void topk_select(uint64_t (&key)[4], const float (&sv)[4], int lane, int K,
+                                            int32_t* __restrict__ idx, float* __restrict__ gate) {
+  int mysel = 0x7FFFFFFF;
+  for (int k = 0; k < K; ++k) {
+    uint64_t best = key[0];
 #pragma unroll
-      for (int s = 0; s < KC; ++s) {
-        a[s] = ld16(ap + k0 + s * 16);
-        b0[s] = ld16(bp0 + k0 + s * 16);
-        b1[s] = ld16(bp1 + k0 + s * 16);
-      }
-    };
-    load(0);
-    for (int k0 = 0; k0 < khalf; k0 += KC * 16) {
-      uint4 ca[KC], cb0[KC], cb1[KC];
+    for (int c = 1; c < 4; ++c) best = key[c] > best ? key[c] : best;
+    best = wave_max_u64(best);
+    const int j = static_cast<int>(0xFFFFFFFFu - static_cast<uint32_t>(best));
+    if (lane == k) mysel = j;
 #pragma unroll
-      for (int s = 0; s < KC; ++s) {
-        ca[s] = a[s];
-        cb0[s] = b0[s];
-        cb1[s] = b1[s];
-      }
-      if (k0 + KC * 16 < khalf) load(k0 + KC * 16);
+    for (int c = 0; c < 4; ++c)
+      if (lane + 64 * c == j) key[c] = 0;
+  }
+  // position of each pick in ascending expert order
+  int rank = 0;
+  for (int k = 0; k < K; ++k) rank += __shfl(mysel, k, kWave) < mysel ? 1 : 0;
+  // the pick's score lives in lane mysel % 64, slot mysel / 64
+  const int src = (lane < K ? mysel : 0) & 63, slot = (lane < K ? mysel : 0) >> 6;
+  float v0 = __shfl(sv[0], src, kWave), v1 = __shfl(sv[1], src, kWave);
+  float v2 = __shfl(sv[2], src, kWave), v3 = __shfl(sv[3], src, kWave);
+  const float myv = lane < K ? (slot == 0 ? v0 : slot == 1 ? v1 : slot == 2 ? v2 : v3) : 0.0f;
+  float denom = 0.0f;
+  for (int p = 0; p < K; ++p) {
+    const uint64_t m = __ballot(lane < K && rank == p);
+    denom += __shfl(myv, __ffsll(static_cast<unsigned long long>(m)) - 1, kWave);
+  }
+  if (lane < K) {
+    idx[rank] = mysel;
+    gate[rank] = myv / denom;
+  }
+}
+
+// ---------------------------------------------------------------------------- bf16
+constexpr int kTB = 128;   // tokens per logits workgroup
+constexpr int kEB = 256;   // experts per logits workgroup (all of them, n_r <= 256)
+constexpr int kLK = 64;    // K per LDS stage (128-byte rows)
+
+// Partial logits of tokens t0.. (128) x experts 0..255 over K-steps [k0, k1) of 64:
+// part[chunk][t][j]. Waves: token block w % 4 (32 tokens), expert half w / 4 (4 blocks
+// of 32 experts). Rows past T or n_r repeat a valid row and are not stored.
+__global__ __launch_bounds__(kThreads) void route_logits(const uint16_t* __restrict__ u,
+                                                         const uint16_t* __restrict__ e, int64_t T, int d,
+                                                         int n_r, int steps_per_chunk,
+                                                         float* __restrict__ part) {
+  __shared__ __attribute__((aligned(16))) unsigned char su[2][kTB * 128];
+  __shared__ __attribute__((aligned(16))) unsigned char se[2][kEB * 128];
+  const int tid = threadIdx.x, lane = tid % kWave, wave = tid / kWave;
+  const int64_t t0 = static_cast<int64_t>(blockIdx.x) * kTB;
+  const int chunk = blockIdx.y;
+  const int nsteps = d / kLK;
+  const int k0 = chunk * steps_per_chunk;
+  const int k1 = k0 + steps_per_chunk < nsteps ? k0 + steps_per_chunk : nsteps;
+  // loads: u tile 128 rows x 8 chunks (2 per thread), e tile 256 rows x 8 (4 per thread)
+  const int cc = tid % 8, cr = tid / 8;  // 16-byte chunk, row 0..63
+  const uint16_t* ua[2];
+  const uint16_t* ea[4];
 #pragma unroll
-      for (int s = 0; s < KC; ++s) {
-        acc0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, ca[s]),
-                                                       __builtin_bit_cast(bf16x8, cb0[s]), acc0, 0, 0, 0);
-        acc1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, ca[s]),
-                                                       __builtin_bit_cast(bf16x8, cb1[s]), acc1, 0, 0, 0);
+  for (int i = 0; i < 2; ++i) {
+    int64_t t = t0 + cr + 64 * i;
+    if (t >= T) t = T - 1;
+    ua[i] = u + t * d + cc * 8;
+  }
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    int j = cr + 64 * i;
+    if (j >= n_r) j = n_r - 1;
+    ea[i] = e + static_cast<int64_t>(j) * d + cc * 8;
+  }
+  uint4 ru[2], re[4];
+  auto gload = [&](int kt) {
+    const int64_t off = static_cast<int64_t>(kt) * kLK;
+#pragma unroll
+    for (int i = 0; i < 2; ++i) ru[i] = ld16(ua[i] + off);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) re[i] = ld16(ea[i] + off);
+  };
+  auto lstore = [&](int st) {
+#pragma unroll
+    for (int i = 0; i < 2; ++i) *reinterpret_cast<uint4*>(su[st] + gemm::swz(cr + 64 * i, cc)) = ru[i];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) *reinterpret_cast<uint4*>(se[st] + gemm::swz(cr + 64 * i, cc)) = re[i];
+  };
+  const int tb = wave % 4, eh = wave / 4;
+  const int arow = 32 * tb + lane % 32;
+  f32x16 acc[4];
+#pragma unroll
+  for (int b = 0; b < 4; ++b) acc[b] = f32x16{};
+  if (k0 < k1) {
+    gload(k0);
+    lstore(0);
+    __syncthreads();
+    for (int kt = k0; kt < k1; ++kt) {
+      const int cur = (kt - k0) & 1;
+      if (kt + 1 < k1) gload(kt + 1);
+#pragma unroll
+      for (int sub = 0; sub < 4; ++sub) {
+        const int ch = 2 * sub + lane / 32;
+        const bf16x8 a = *reinterpret_cast<const bf16x8*>(su[cur] + gemm::swz(arow, ch));
+#pragma unroll
+        for (int b = 0; b < 4; ++b) {
+          const bf16x8 w = *reinterpret_cast<const bf16x8*>(se[cur] + gemm::swz(128 * eh + 32 * b + lane % 32, ch));
+          acc[b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, w, acc[b], 0, 0, 0);
+        }
       }
+      if (kt + 1 < k1) lstore(cur ^ 1);
+      __syncthreads();
     }
   }
   // C layout of 32x32 MFMA: lane holds column (expert) lane%32, rows 8*(v/4)+4*(lane/32)+v%4
-  auto store = [&](float* dst, bool sig) {
 #pragma unroll
-    for (int blk = 0; blk < 2; ++blk) {
-      if (!active || (blk == 1 && !two)) continue;
-      const int j = (bp + 4 * blk) * 32 + (lane % 32);
-      if (j >= n_r) continue;
+  for (int b = 0; b < 4; ++b) {
+    const int j = 128 * eh + 32 * b + lane % 32;
+    if (j >= n_r) continue;
 #pragma unroll
-      for (int v = 0; v < 16; ++v) {
-        const int i = 8 * (v / 4) + 4 * (lane / 32) + (v % 4);
-        const float z = blk == 0 ? acc0[v] : acc1[v];
-        if (sig)
-          dst[i * n_r + j] = sigmoid_precise(dst[i * n_r + j] + z);  // first half + second half
-        else
-          dst[i * n_r + j] = z;
-      }
+    for (int v = 0; v < 16; ++v) {
+      const int64_t t = t0 + 32 * tb + 8 * (v / 4) + 4 * (lane / 32) + (v % 4);
+      if (t < T) part[(static_cast<int64_t>(chunk) * T + t) * n_r + j] = acc[b][v];
     }
-  };
-  if (kh == 0) store(part, false);
-  __syncthreads();
-  if (kh == 1) store(part, true);
-  __syncthreads();
-  for (int p = threadIdx.x; p < kTok * n_r; p += kThreads) sc[p] = part[p];
+  }
 }
 
-__device__ void logits_bf16(const uint16_t* __restrict__ u, const uint16_t* __restrict__ e,
-                            int64_t T, int d, int n_r, int64_t t0, float* sc, float* part) {
-  if (d % 256 == 0)
-    logits_bf16_kc<8>(u, e, T, d, n_r, t0, sc, part);
-  else
-    logits_bf16_kc<2>(u, e, T, d, n_r, t0, sc, part);
+// Top-K of one token per wave from the partial logits of n_chunks chunks.
+__global__ __launch_bounds__(256) void route_topk(const float* __restrict__ part, int n_chunks,
+                                                  const float* __restrict__ bias, int64_t T, int n_r, int K,
+                                                  int32_t* __restrict__ topk_idx, float* __restrict__ topk_gate) {
+  const int lane = threadIdx.x % kWave;
+  const int64_t t = static_cast<int64_t>(blockIdx.x) * (256 / kWave) + threadIdx.x / kWave;
+  if (t >= T) return;
+  // this lane's candidates: experts lane, lane+64, lane+128, lane+192
+  float sv[4];
+  uint64_t key[4];
+#pragma unroll
+  for (int c = 0; c < 4; ++c) {
+    const int j = lane + 64 * c;
+    sv[c] = 0.0f;
+    key[c] = 0;  // below every real key
+    if (j < n_r) {
+      float z = 0.0f;
+      for (int q = 0; q < n_chunks; ++q) z += part[(static_cast<int64_t>(q) * T + t) * n_r + j];
+      sv[c] = sigmoid_precise(z);
+      const float v = sv[c] + bias[j];
+      key[c] = (static_cast<uint64_t>(orderable(v)) << 32) | (0xFFFFFFFFu - static_cast<uint32_t>(j));
+    }
+  }
+  topk_select(key, sv, lane, K, topk_idx + t * K, topk_gate + t * K);
 }
 
 __device__ void logits_f32(const float* __restrict__ u, const float* __restrict__ e, int64_t T,
@@ -138,84 +205,75 @@ __device__ void logits_f32(const float* __restrict__ u, const float* __restrict_
   }
 }
 
-template <int ACT>
-__global__ __launch_bounds__(kThreads) void route_kernel(const void* __restrict__ u,
-                                                         const void* __restrict__ e,
-                                                         const float* __restrict__ bias, int64_t T,
-                                                         int d, int n_r, int K,
-                                                         int32_t* __restrict__ topk_idx,
+// fp32 activations: one workgroup of 8 waves owns 32 tokens; logits are plain fp32
+// dot products parked in LDS as sigmoid scores, then one wave per token selects.
+__global__ __launch_bounds__(kThreads) void route_kernel(const float* __restrict__ u, const float* __restrict__ e,
+                                                         const float* __restrict__ bias, int64_t T, int d, int n_r,
+                                                         int K, int32_t* __restrict__ topk_idx,
                                                          float* __restrict__ topk_gate) {
   __shared__ float sc[kTok * kMaxExperts];
-  __shared__ float part[kTok * kMaxExperts];
   const int64_t t0 = static_cast<int64_t>(blockIdx.x) * kTok;
-  if (ACT == 1)
-    logits_bf16(static_cast<const uint16_t*>(u), static_cast<const uint16_t*>(e), T, d, n_r, t0, sc, part);
-  else
-    logits_f32(static_cast<const float*>(u), static_cast<const float*>(e), T, d, n_r, t0, sc);
+  logits_f32(u, e, T, d, n_r, t0, sc);
   __syncthreads();
-
   const int lane = threadIdx.x % kWave, wave = threadIdx.x / kWave;
-  // this lane's candidates: experts lane, lane+64, lane+128, lane+192
-  float bl[4];
-#pragma unroll
-  for (int c = 0; c < 4; ++c) {
-    const int j = lane + 64 * c;
-    bl[c] = j < n_r ? bias[j] : 0.0f;
-  }
   for (int i = wave; i < kTok; i += kThreads / kWave) {
     const int64_t t = t0 + i;
     if (t >= T) break;
     uint64_t key[4];
+    float sv[4];
 #pragma unroll
     for (int c = 0; c < 4; ++c) {
       const int j = lane + 64 * c;
       key[c] = 0;  // below every real key
+      sv[c] = 0.0f;
       if (j < n_r) {
-        const float v = sc[i * n_r + j] + bl[c];
+        sv[c] = sc[i * n_r + j];
+        const float v = sv[c] + bias[j];
         key[c] = (static_cast<uint64_t>(orderable(v)) << 32) | (0xFFFFFFFFu - static_cast<uint32_t>(j));
       }
     }
-    // lane k < K keeps the k-th pick; no per-lane arrays indexed at run time
-    int mysel = 0x7FFFFFFF;
-    for (int k = 0; k < K; ++k) {
-      uint64_t best = key[0];
-#pragma unroll
-      for (int c = 1; c < 4; ++c) best = key[c] > best ? key[c] : best;
-      best = wave_max_u64(best);
-      const int j = static_cast<int>(0xFFFFFFFFu - static_cast<uint32_t>(best));
-      if (lane == k) mysel = j;
-#pragma unroll
-      for (int c = 0; c < 4; ++c)
-        if (lane + 64 * c == j) key[c] = 0;
-    }
-    // position of each pick in ascending expert order
-    int rank = 0;
-    for (int k = 0; k < K; ++k) rank += __shfl(mysel, k, kWave) < mysel ? 1 : 0;
-    // gate denominator: the picked scores summed in ascending expert order
-    const float myv = lane < K ? sc[i * n_r + mysel] : 0.0f;
-    float denom = 0.0f;
-    for (int p = 0; p < K; ++p) {
-      const uint64_t m = __ballot(lane < K && rank == p);
-      denom += __shfl(myv, __ffsll(static_cast<unsigned long long>(m)) - 1, kWave);
-    }
-    if (lane < K) {
-      topk_idx[t * K + rank] = mysel;
-      topk_gate[t * K + rank] = myv / denom;
-    }
+    topk_select(key, sv, lane, K, topk_idx + t * K, topk_gate + t * K);
   }
 }
 
 }  // namespace
 
-hipError_t launch_route(int act, const void* u, const void* e, const float* bias, int64_t T, int d,
-                        int n_r, int K, int32_t* idx, float* gate, hipStream_t stream) {
+RouteChunks route_chunks(int64_t T, int d) {
+  // enough (token block, K chunk) workgroups to fill the chip: about 512, at most 32
+  // chunks, each a whole number of 64-wide K-steps
+  const int64_t blocks = (T + kTB - 1) / kTB;
+  const int nsteps = d / kLK;
+  int64_t want = (512 + blocks - 1) / blocks;
+  const int cap = nsteps < 32 ? nsteps : 32;
+  if (want > cap) want = cap;
+  if (want < 1) want = 1;
+  RouteChunks r;
+  r.steps_per_chunk = static_cast<int>((nsteps + want - 1) / want);
+  r.chunks = (nsteps + r.steps_per_chunk - 1) / r.steps_per_chunk;
+  return r;
+}
+
+size_t route_workspace_bytes(int64_t T, int d, int n_r) {
+  return static_cast<size_t>(route_chunks(T, d).chunks) * static_cast<size_t>(T) * n_r * sizeof(float);
+}
+
+hipError_t launch_route(int act, const void* u, const void* e, const float* bias, int64_t T, int d, int n_r,
+                        int K, int32_t* idx, float* gate, float* part, hipStream_t stream) {
+  if (act == 1) {
+    const RouteChunks rc = route_chunks(T, d);
+    const dim3 grid(static_cast<unsigned>((T + kTB - 1) / kTB), static_cast<unsigned>(rc.chunks));
+    hipLaunchKernelGGL(route_logits, grid, dim3(kThreads), 0, stream, static_cast<const uint16_t*>(u),
+                       static_cast<const uint16_t*>(e), T, d, n_r, rc.steps_per_chunk, part);
+    hipError_t err = hipGetLastError();
+    if (err != hipSuccess) return err;
+    const unsigned waves_per_block = 256 / kWave;
+    hipLaunchKernelGGL(route_topk, dim3(static_cast<unsigned>((T + waves_per_block - 1) / waves_per_block)),
+                       dim3(256), 0, stream, part, rc.chunks, bias, T, n_r, K, idx, gate);
+    return hipGetLastError();
+  }
   const dim3 grid(static_cast<unsigned>((T + kTok - 1) / kTok));
-  if (act == 1)
-    hipLaunchKernelGGL(route_kernel<1>, grid, dim3(kThreads), 0, stream, u, e, bias, T, d, n_r, K,
-                       idx, gate);
-  else
-    hipLaunchKernelGGL(route_kernel<0>, grid, dim3(kThreads), 0, stream, u, e, bias, T, d, n_r, K,
-                       idx, gate);
+  hipLaunchKernelGGL(route_kernel, grid, dim3(kThreads), 0, stream, static_cast<const float*>(u),
+                     static_cast<const float*>(e), bias, T, d, n_r, K, idx, gate);
   return hipGetLastError();
 }
 

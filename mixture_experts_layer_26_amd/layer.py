@@ -33,8 +33,10 @@ class MoeLayer:
         self.y_routed = torch.empty((T * top_k, d), dtype=adt, device=dev)
         self.y_shared = torch.empty((T, d), dtype=torch.float32, device=dev) if n_shared > 0 else None
         self.out = torch.empty((T, d), dtype=adt, device=dev)
+        self.ws_route_bytes = abi.moe_workspace_bytes(self.shape, abi.MOE_CALL_ROUTE)
         self.ws_dispatch_bytes = abi.moe_workspace_bytes(self.shape, abi.MOE_CALL_DISPATCH)
         self.ws_ffn_bytes = abi.moe_workspace_bytes(self.shape, abi.MOE_CALL_GROUPED_FFN)
+        self.ws_route = torch.empty(max(1, self.ws_route_bytes), dtype=torch.uint8, device=dev)
         self.ws_dispatch = torch.empty(max(1, self.ws_dispatch_bytes), dtype=torch.uint8, device=dev)
         self.ws_ffn = torch.empty(max(1, self.ws_ffn_bytes), dtype=torch.uint8, device=dev)
         self.routed = None
@@ -51,7 +53,8 @@ class MoeLayer:
 
     # -- the five calls ----------------------------------------------------------
     def route(self, u, centroids, bias, stream=None):
-        abi.moe_route(self.shape, u, centroids, bias, self.topk_idx, self.topk_gate, stream)
+        abi.moe_route(self.shape, u, centroids, bias, self.topk_idx, self.topk_gate, self.ws_route,
+                      self.ws_route_bytes, stream)
 
     def dispatch(self, stream=None):
         abi.moe_dispatch(self.shape, self.topk_idx, self.expert_count, self.expert_offset,

@@ -43,7 +43,7 @@ FAKE = 0x1000  # never dereferenced: every call below is rejected on the host
 def test_bad_shapes_rejected(kw):
     s = _shape(**kw)
     lib = abi.load()
-    st = lib.moe_route(ctypes.byref(s), FAKE, FAKE, FAKE, FAKE, FAKE, None)
+    st = lib.moe_route(ctypes.byref(s), FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 1 << 30, None)
     assert st == abi.MOE_ERR_INVALID_ARG
     assert abi.moe_workspace_bytes(s, abi.MOE_CALL_DISPATCH) == 0
 
@@ -51,8 +51,9 @@ def test_bad_shapes_rejected(kw):
 def test_null_pointers_rejected():
     s = _shape()
     lib = abi.load()
-    assert lib.moe_route(ctypes.byref(s), None, FAKE, FAKE, FAKE, FAKE, None) == abi.MOE_ERR_INVALID_ARG
-    assert lib.moe_route(None, FAKE, FAKE, FAKE, FAKE, FAKE, None) == abi.MOE_ERR_INVALID_ARG
+    assert lib.moe_route(ctypes.byref(s), None, FAKE, FAKE, FAKE, FAKE, FAKE, 1 << 30, None) == \
+        abi.MOE_ERR_INVALID_ARG
+    assert lib.moe_route(None, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 1 << 30, None) == abi.MOE_ERR_INVALID_ARG
     assert lib.moe_dispatch(ctypes.byref(s), FAKE, FAKE, FAKE, FAKE, None, FAKE, 1 << 20, None) == \
         abi.MOE_ERR_INVALID_ARG
     assert lib.moe_combine(ctypes.byref(s), FAKE, FAKE, None, FAKE, FAKE, FAKE, None) == \
@@ -88,6 +89,20 @@ def test_workspace_checks():
     sb = _shape(d=320, d_ff=128, act="bf16", ffn="bf16")
     assert lib.moe_grouped_ffn(ctypes.byref(sb), FAKE, FAKE, FAKE, ctypes.byref(es), ctypes.byref(es), FAKE,
                                FAKE, FAKE, 1 << 30, None) == abi.MOE_ERR_UNSUPPORTED
+
+
+def test_route_workspace():
+    lib = abi.load()
+    s32 = _shape()  # fp32 activations need no workspace
+    assert abi.moe_workspace_bytes(s32, abi.MOE_CALL_ROUTE) == 0
+    sb = _shape(T=8192, d=7168, n_routed=256, top_k=8, d_ff=2048, act="bf16", ffn="bf16")
+    need = abi.moe_workspace_bytes(sb, abi.MOE_CALL_ROUTE)
+    # partial logits of the K chunks: [chunks][T][N_r] fp32, 1 <= chunks <= 32
+    assert 8192 * 256 * 4 <= need <= 32 * 8192 * 256 * 4 + 4096
+    assert lib.moe_route(ctypes.byref(sb), FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, need - 1, None) == \
+        abi.MOE_ERR_WORKSPACE
+    assert lib.moe_route(ctypes.byref(sb), FAKE, FAKE, FAKE, FAKE, FAKE, None, need, None) == \
+        abi.MOE_ERR_WORKSPACE
 
 
 def test_quantize_args_rejected():
