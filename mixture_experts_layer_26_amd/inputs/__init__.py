@@ -27,6 +27,7 @@ _LIB_PATH = os.path.join(_HERE, "libmoe_inputs.so")
 
 # tensor ids: the third Philox counter word
 TID_U, TID_E, TID_B, TID_W1, TID_W3, TID_W2, TID_SW1, TID_SW3, TID_SW2 = range(1, 10)
+TID_U_BATCH = 0x100  # u of a later token batch: TID_U_BATCH + batch (batch >= 1)
 
 F32, BF16, FP8 = "f32", "bf16", "fp8"
 
@@ -156,10 +157,15 @@ def weight_dtype(w: Workload) -> str:
     return F32 if w.ffn == F32 else BF16
 
 
-def make_u(w: Workload, rows: slice = None) -> np.ndarray:
-    """u ~ N(0,1), [T, d] (act dtype); `rows` selects a token range."""
+def _tid_u(batch: int) -> int:
+    return TID_U if batch == 0 else TID_U_BATCH + batch
+
+
+def make_u(w: Workload, rows: slice = None, batch: int = 0) -> np.ndarray:
+    """u ~ N(0,1), [T, d] (act dtype); `rows` selects a token range; `batch` > 0 draws
+    the tokens of a later batch (an independent stream of the same distribution)."""
     r0, r1 = (0, w.T) if rows is None else (rows.start, rows.stop)
-    a = normal(w.seed, TID_U, r0 * w.d, (r1 - r0) * w.d, 1.0, w.act)
+    a = normal(w.seed, _tid_u(batch), r0 * w.d, (r1 - r0) * w.d, 1.0, w.act)
     return a.reshape(r1 - r0, w.d)
 
 

@@ -319,6 +319,36 @@ def test_bias_update_closed_form():
     assert set(np.unique(nb0)) <= {np.float32(-0.001), np.float32(0), np.float32(0.001)}
 
 
+def test_bias_loop_balances_skewed_routing():
+    """Closed loop over fresh batches: route with b, count, update b, next batch.
+    Every move has the sign of (mean - load) and size gamma, so |b_S - b_0| <= S*gamma;
+    and with hot experts (centroids scaled 3x) the loop pulls the max/mean load down,
+    the behaviour the aux-loss-free rule exists for."""
+    w = I.Workload("balance_cpu", T=512, d=64, n_routed=16, top_k=2, n_shared=0, d_ff=64, act="f32",
+                   ffn="f32", seed=77, bias_range=0.0, hot_experts=(0, 5), hot_scale=3.0, gamma=0.02)
+    e = I.make_e(w)
+    b0 = I.make_b(w)
+    b = b0.copy()
+    mean = w.T * w.top_k / w.n_routed
+    ratios = []
+    S = 60
+    for s in range(S):
+        idx, _, _, _ = oracle.route(I.make_u(w, batch=s + 1), e, b, w.top_k, w.act)
+        count = oracle.dispatch(idx, w.n_routed)[0]
+        assert count.sum() == w.T * w.top_k
+        nb = oracle.bias_update(count, w.T, w.top_k, w.gamma, b)
+        step = nb.astype(np.float64) - b.astype(np.float64)
+        assert np.all(np.sign(step) == np.sign(mean - count))
+        assert np.all(np.abs(np.abs(step[count != mean]) - w.gamma) <= 1e-6)
+        b = nb
+        ratios.append(count.max() / mean)
+    assert np.all(np.abs(b.astype(np.float64) - b0) <= S * w.gamma * (1 + 1e-5))
+    assert ratios[0] > 2.0                          # the skew is real
+    assert np.mean(ratios[-10:]) < 0.6 * ratios[0]  # and the loop removes most of it
+    # hot experts end with the lowest biases
+    assert set(np.argsort(b)[:2].tolist()) == {0, 5}
+
+
 # -------------------------------------------------------------- expert FFN
 
 def test_swiglu_closed_form():
