@@ -19,6 +19,8 @@ _LIB_PATH = os.path.join(_HERE, "libmoe_oracle.so")
 
 ORC_F32, ORC_BF16, ORC_FP8 = 0, 1, 2
 _DT = {"f32": ORC_F32, "bf16": ORC_BF16, "fp8": ORC_FP8}
+ORC_SIGMOID, ORC_SOFTMAX = 0, 1
+_SCORE = {"sigmoid": ORC_SIGMOID, "softmax": ORC_SOFTMAX}
 
 _lib = None
 
@@ -54,11 +56,11 @@ def _load():
     lib.orc_bf16_from_double_array.argtypes = [vp, i64, vp]
     lib.orc_e4m3_from_float_array.argtypes = [vp, i64, vp]
     lib.orc_quantize_tiles.argtypes = [vp, i32, i64, i64, i32, i32, vp, vp]
-    lib.orc_route.argtypes = [i64, i32, i32, i32, i32, vp, vp, vp, vp, vp, vp, vp]
+    lib.orc_route.argtypes = [i64, i32, i32, i32, i32, i32, vp, vp, vp, vp, vp, vp, vp]
     lib.orc_dispatch.argtypes = [i64, i32, i32, vp, vp, vp, vp, vp]
     lib.orc_bias_update.argtypes = [i64, i32, i32, vp, flt, vp]
     lib.orc_expert_rows.argtypes = [i32, i32, i32, vp, i64, vp, vp, vp, vp, vp, vp, vp, vp]
-    lib.orc_layer.argtypes = [i64, i32, i32, i32, i32, i32, i32, i32, vp, vp, vp] + [vp] * 12 + \
+    lib.orc_layer.argtypes = [i64, i32, i32, i32, i32, i32, i32, i32, i32, vp, vp, vp] + [vp] * 12 + \
         [vp] * 6
     lib.orc_layer.restype = i32
     lib.orc_combine.argtypes = [i64, i32, i32, i32, vp, vp, vp, vp, vp, vp]
@@ -125,19 +127,21 @@ def quantize(x, dtype: str, tr: int, tc: int):
     return q, s
 
 
-def route(u, e, b, top_k: int, act: str, want_v: bool = False):
-    """Routing of the rows of u: (idx [n,K] ascending, gate [n,K] double, gap [n], v or None)."""
+def route(u, e, b, top_k: int, act: str, want_v: bool = False, score: str = "sigmoid"):
+    """Routing of the rows of u: (idx [n,K] ascending, gate [n,K] double, gap [n], v or None).
+    score "sigmoid": biased top-K of Sigmoid(z); "softmax": top-K of z, b unused (may be None)."""
     dt = _DT[act]
     u = _act_arr(u, dt)
     e = _act_arr(e, dt)
-    b = _c(b, np.float32)
     n, d = u.shape
     n_r = e.shape[0]
+    b = _c(np.zeros(n_r, np.float32) if b is None else b, np.float32)
     idx = np.empty((n, top_k), np.int32)
     gate = np.empty((n, top_k), np.float64)
     gap = np.empty(n, np.float64)
     v = np.empty((n, n_r), np.float64) if want_v else None
-    _load().orc_route(n, d, n_r, top_k, dt, _p(u), _p(e), _p(b), _p(idx), _p(gate), _p(gap), _p(v))
+    _load().orc_route(n, d, n_r, top_k, dt, _SCORE[score], _p(u), _p(e), _p(b), _p(idx), _p(gate), _p(gap),
+                      _p(v))
     return idx, gate, gap, v
 
 
@@ -184,18 +188,19 @@ def _ptr_array(items):
 
 
 def layer(u, e, b, routed: dict, shared: list, *, top_k: int, d_ff: int, act: str, ffn: str,
-          want_components: bool = False):
+          want_components: bool = False, score: str = "sigmoid"):
     """The layer output for the tokens whose rows are u, in double.
 
     routed: {expert id: (w1, w3, w2) or (w1, w3, w2, s1, s3, s2)} for at least every
     expert those tokens select; shared: list of the same tuples for the N_s shared experts.
-    Returns a dict with out, idx, gate, gap (and shared_sum, routed_sum)."""
+    Routing as in route() with the given score. Returns a dict with out, idx, gate, gap
+    (and shared_sum, routed_sum)."""
     adt, fdt = _DT[act], _DT[ffn]
     u = _act_arr(u, adt)
     e = _act_arr(e, adt)
-    b = _c(b, np.float32)
     n, d = u.shape
     n_r = e.shape[0]
+    b = _c(np.zeros(n_r, np.float32) if b is None else b, np.float32)
     wdt = np.uint8 if fdt == ORC_FP8 else (np.float32 if fdt == ORC_F32 else np.uint16)
     keep = []
 
@@ -217,7 +222,7 @@ def layer(u, e, b, routed: dict, shared: list, *, top_k: int, d_ff: int, act: st
     gap = np.empty(n, np.float64)
     ssum = np.empty((n, d), np.float64) if want_components else None
     rsum = np.empty((n, d), np.float64) if want_components else None
-    st = _load().orc_layer(n, d, n_r, top_k, len(shared), d_ff, adt, fdt, _p(u), _p(e), _p(b),
+    st = _load().orc_layer(n, d, n_r, top_k, len(shared), d_ff, adt, fdt, _SCORE[score], _p(u), _p(e), _p(b),
                            *[ctypes.cast(a, ctypes.c_void_p) for a in arrs],
                            _p(out), _p(idx), _p(gate), _p(gap), _p(ssum), _p(rsum))
     if st != 0:

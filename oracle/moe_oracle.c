@@ -130,12 +130,17 @@ static void quantize_row(const void* x, int xdt, int64_t cols, uint8_t* q, float
 
 /* -------------------------------------------------------------------- routing */
 
-/* [V3] method section 2: s_{i,t} = Sigmoid(u_t . e_i); expert i is selected when
- * s_{i,t} + b_i is among the K largest biased scores, and then g'_{i,t} = s_{i,t};
- * g_{i,t} is g' normalised over the selected experts (the bias only steers the
- * choice, it is not part of the gate). Equal biased scores go to the lower index.
- * The K ids are returned in ascending order. */
-static void route_one(int d, int n_r, int K, int act, const void* u_row, const void* e,
+/* score == ORC_SIGMOID, [V3] method section 2: s_{i,t} = Sigmoid(u_t . e_i); expert i
+ * is selected when s_{i,t} + b_i is among the K largest biased scores, and then
+ * g'_{i,t} = s_{i,t}; g_{i,t} is g' normalised over the selected experts (the bias
+ * only steers the choice, it is not part of the gate).
+ * score == ORC_SOFTMAX, the [ARCH] DeepSeekMoE forward listing: the K largest logits
+ * z_{i,t} = u_t . e_i are selected (no bias; b is not read), and the gates are the
+ * softmax of the selected logits, exp(z_i - z_max) / sum over the selection of
+ * exp(z_j - z_max), the sum taken in ascending expert order.
+ * Either way equal keys go to the lower index, v holds the selection keys (s + b or
+ * z), and the K ids are returned in ascending order. */
+static void route_one(int d, int n_r, int K, int act, int score, const void* u_row, const void* e,
                       const float* b, double* ud, double* s, double* v, char* taken, int32_t* idx,
                       double* gate, double* gap) {
   for (int c = 0; c < d; ++c) ud[c] = load_val(u_row, act, c);
@@ -145,8 +150,13 @@ static void route_one(int d, int n_r, int K, int act, const void* u_row, const v
     for (int c = 0; c < d; ++c)
       for (int q = 0; q < ni; ++q) z[q] += ud[c] * load_val(e, act, (int64_t)(i0 + q) * d + c);
     for (int q = 0; q < ni; ++q) {
-      s[i0 + q] = sigmoid(z[q]);
-      v[i0 + q] = s[i0 + q] + (double)b[i0 + q];
+      if (score == ORC_SOFTMAX) {
+        s[i0 + q] = z[q];
+        v[i0 + q] = z[q];
+      } else {
+        s[i0 + q] = sigmoid(z[q]);
+        v[i0 + q] = s[i0 + q] + (double)b[i0 + q];
+      }
       taken[i0 + q] = 0;
     }
   }
@@ -167,16 +177,19 @@ static void route_one(int d, int n_r, int K, int act, const void* u_row, const v
     *gap = INFINITY;
   }
   int k = 0;
-  double denom = 0.0;
   for (int i = 0; i < n_r; ++i)
-    if (taken[i]) {
-      idx[k++] = i;
-      denom += s[i];
-    }
+    if (taken[i]) idx[k++] = i;
+  if (score == ORC_SOFTMAX) { /* g'_k = exp(z_k - max z), then normalised like s */
+    double zmax = -INFINITY;
+    for (k = 0; k < K; ++k) zmax = s[idx[k]] > zmax ? s[idx[k]] : zmax;
+    for (k = 0; k < K; ++k) s[idx[k]] = exp(s[idx[k]] - zmax);
+  }
+  double denom = 0.0;
+  for (k = 0; k < K; ++k) denom += s[idx[k]];
   for (k = 0; k < K; ++k) gate[k] = s[idx[k]] / denom;
 }
 
-void orc_route(int64_t n, int d, int n_r, int K, int act, const void* u, const void* e,
+void orc_route(int64_t n, int d, int n_r, int K, int act, int score, const void* u, const void* e,
                const float* b, int32_t* idx, double* gate, double* gap, double* v) {
   const size_t esz = (act == ORC_F32) ? 4 : 2;
 #pragma omp parallel
@@ -188,7 +201,7 @@ void orc_route(int64_t n, int d, int n_r, int K, int act, const void* u, const v
 #pragma omp for schedule(static)
     for (int64_t t = 0; t < n; ++t) {
       double g;
-      route_one(d, n_r, K, act, (const char*)u + (size_t)t * d * esz, e, b, ud, s, vv, taken,
+      route_one(d, n_r, K, act, score, (const char*)u + (size_t)t * d * esz, e, b, ud, s, vv, taken,
                 idx + t * K, gate + t * K, &g);
       if (gap) gap[t] = g;
       if (v) memcpy(v + t * n_r, vv, sizeof(double) * n_r);
@@ -366,7 +379,7 @@ void orc_expert_rows(int d, int d_ff, int ffn, const void* x, int64_t n, const v
  *   h'_t = u_t + sum_{j<N_s} FFN^(s)_j(u_t) + sum_{i selected} g_{i,t} FFN^(r)_i(u_t),
  * added in that order (residual, shared experts ascending, routed experts ascending),
  * in double. Shared experts carry no gate. */
-int orc_layer(int64_t n, int d, int n_r, int K, int n_s, int d_ff, int act, int ffn,
+int orc_layer(int64_t n, int d, int n_r, int K, int n_s, int d_ff, int act, int ffn, int score,
               const void* u, const void* e, const float* b,
               const void* const* wr1, const void* const* wr3, const void* const* wr2,
               const float* const* sr1, const float* const* sr3, const float* const* sr2,
@@ -378,7 +391,7 @@ int orc_layer(int64_t n, int d, int n_r, int K, int n_s, int d_ff, int act, int 
   int32_t* my_idx = (int32_t*)malloc(sizeof(int32_t) * n * K);
   double* my_gate = (double*)malloc(sizeof(double) * n * K);
   double* my_gap = (double*)malloc(sizeof(double) * n);
-  orc_route(n, d, n_r, K, act, u, e, b, my_idx, my_gate, my_gap, NULL);
+  orc_route(n, d, n_r, K, act, score, u, e, b, my_idx, my_gate, my_gap, NULL);
   int status = 0;
   for (int64_t p = 0; p < n * K; ++p)
     if (!wr1[my_idx[p]] || !wr3[my_idx[p]] || !wr2[my_idx[p]]) status = -1;

@@ -31,6 +31,7 @@ extern "C" {
 #endif
 
 enum { ORC_F32 = 0, ORC_BF16 = 1, ORC_FP8 = 2 };
+enum { ORC_SIGMOID = 0, ORC_SOFTMAX = 1 }; /* router scoring */
 
 /* ---- scalar conversions --------------------------------------------------- */
 double orc_bf16_value(uint16_t bits);          /* exact widening                     */
@@ -49,11 +50,15 @@ void orc_e4m3_from_float_array(const float* x, int64_t n, uint8_t* out);
 void orc_quantize_tiles(const void* x, int xdt, int64_t rows, int64_t cols, int tr, int tc,
                         uint8_t* q, float* s);
 
-/* ---- routing ([V3] method section 2: sigmoid affinity, g', normalisation)
- * u: [n, d] rows (act dtype), e: [n_r, d] (act dtype), b: [n_r] fp32.
+/* ---- routing
+ * score ORC_SIGMOID ([V3] method section 2: sigmoid affinity, biased top-K, g'
+ * normalised) or ORC_SOFTMAX ([ARCH] DeepSeekMoE forward listing: top-K of the logits,
+ * no bias, softmax over the selected logits).
+ * u: [n, d] rows (act dtype), e: [n_r, d] (act dtype), b: [n_r] fp32 (sigmoid only).
  * Out: idx [n, K] ascending expert ids; gate [n, K] (double) aligned with idx;
- * gap [n] = v_(K) - v_(K+1) (+inf when K == n_r); v [n, n_r] biased scores (optional). */
-void orc_route(int64_t n, int d, int n_r, int K, int act, const void* u, const void* e,
+ * gap [n] = v_(K) - v_(K+1) (+inf when K == n_r); v [n, n_r] selection keys, s + b or
+ * z (optional). */
+void orc_route(int64_t n, int d, int n_r, int K, int act, int score, const void* u, const void* e,
                const float* b, int32_t* idx, double* gate, double* gap, double* v);
 
 /* ---- dispatch: counts, exclusive offsets [n_r+1], rows sorted by (expert, token) */
@@ -79,10 +84,10 @@ void orc_expert_rows(int d, int d_ff, int ffn, const void* x, int64_t n, const v
  * u: [n, d] rows of the tokens (act dtype). Routed expert i's weights are wr1[i],
  * wr3[i], wr2[i] (and scales sr1[i], sr3[i], sr2[i] for FP8); an expert no token of
  * the list selects may be NULL. Shared experts likewise (ws*, ss*), n_s of them.
- * Out: out [n, d] = u + sum_shared + sum_routed(g * y), in double; optional
- * idx/gate/gap as in orc_route; optional shared_sum/routed_sum [n, d].
+ * Out: out [n, d] = u + sum_shared + sum_routed(g * y), in double; routing by
+ * orc_route with the given score; optional idx/gate/gap as in orc_route; optional shared_sum/routed_sum [n, d].
  * Returns 0, or -1 if a routed expert that is needed has a NULL weight pointer. */
-int orc_layer(int64_t n, int d, int n_r, int K, int n_s, int d_ff, int act, int ffn,
+int orc_layer(int64_t n, int d, int n_r, int K, int n_s, int d_ff, int act, int ffn, int score,
               const void* u, const void* e, const float* b,
               const void* const* wr1, const void* const* wr3, const void* const* wr2,
               const float* const* sr1, const float* const* sr3, const float* const* sr2,

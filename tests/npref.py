@@ -7,6 +7,7 @@ sorts instead of arg-max passes, and the per-expert masked loop of the
 evaluation. They agree with the oracle to rounding order, not bit for bit.
 """
 import numpy as np
+import scipy.special
 
 
 def widen(a, dt):
@@ -54,16 +55,23 @@ def swiglu_ffn(x, w1, w3, w2, hround):
     return h @ w2.T
 
 
-def dense_layer(u, e, b, routed, shared, K, hround):
+def dense_layer(u, e, b, routed, shared, K, hround, score="sigmoid"):
     """All-experts dense evaluation: every routed expert on every token, with a gate
-    matrix that is zero outside each token's top-K. Inputs are float64."""
-    v = sigmoid(u @ e.T) + b[None, :]
-    s = sigmoid(u @ e.T)
-    sel = topk_by_sort(v, K)
-    G = np.zeros_like(s)
-    for t in range(u.shape[0]):
-        G[t, sel[t]] = s[t, sel[t]]
-        G[t] /= G[t, sel[t]].sum()
+    matrix that is zero outside each token's top-K. Inputs are float64.
+    score "sigmoid": top-K of sigmoid(z) + b, gates sigmoid(z) normalised; "softmax": top-K
+    of z, gates scipy's softmax of the selected logits."""
+    z = u @ e.T
+    G = np.zeros_like(z)
+    if score == "softmax":
+        sel = topk_by_sort(z, K)
+        for t in range(u.shape[0]):
+            G[t, sel[t]] = scipy.special.softmax(z[t, sel[t]])
+    else:
+        s = sigmoid(z)
+        sel = topk_by_sort(s + b[None, :], K)
+        for t in range(u.shape[0]):
+            G[t, sel[t]] = s[t, sel[t]]
+            G[t] /= G[t, sel[t]].sum()
     out = u.copy()
     for (w1, w3, w2) in shared:
         out = out + swiglu_ffn(u, w1, w3, w2, hround)

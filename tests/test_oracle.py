@@ -16,6 +16,7 @@ from concurrent.futures import ThreadPoolExecutor
 
 import numpy as np
 import pytest
+import scipy.special
 
 import oracle
 from mixture_experts_layer_26_amd import inputs as I
@@ -258,6 +259,51 @@ def test_route_all_experts():
     assert np.max(np.abs(gate - s / s.sum(1, keepdims=True))) < 1e-14
 
 
+@pytest.mark.parametrize("name,T", [("tiny_f32", None), ("mid_bf16", 512), ("v3_decode_skewed", None)])
+def test_route_softmax_against_full_sort(name, T):
+    """Softmax scoring (the deepseekmodel.com forward listing): the K largest logits by a
+    full sort of (-z, i), whatever b holds; gates are scipy's softmax of the selected
+    logits; sigmoid being increasing, the sigmoid mode at b = 0 selects the same experts."""
+    w, u, e, b = _route_inputs(I.WORKLOADS[name], T)
+    idx, gate, gap, v = oracle.route(u, e, b, w.top_k, w.act, want_v=True, score="softmax")
+    z = npref.widen(u, w.act) @ npref.widen(e, w.act).T
+    assert np.max(np.abs(v - z)) < 1e-12
+    assert np.array_equal(idx, npref.topk_by_sort(v, w.top_k))
+    robust = gap > 1e-9
+    assert robust.mean() > 0.99
+    assert np.array_equal(idx[robust], npref.topk_by_sort(z, w.top_k)[robust])
+    g_ref = scipy.special.softmax(np.take_along_axis(z, idx, 1), axis=1)
+    assert np.max(np.abs(gate - g_ref)) < 1e-13
+    assert np.all(np.diff(idx, axis=1) > 0)
+    # the bias plays no part
+    idx0, gate0, gap0, _ = oracle.route(u, e, None, w.top_k, w.act, score="softmax")
+    assert np.array_equal(idx0, idx) and np.array_equal(gate0, gate) and np.array_equal(gap0, gap)
+    # the same experts as sigmoid scoring without bias
+    idx_s, _, gap_s, _ = oracle.route(u, e, np.zeros_like(b), w.top_k, w.act, score="sigmoid")
+    both = robust & (gap_s > 1e-12)
+    assert np.array_equal(idx_s[both], idx[both])
+
+
+def test_route_softmax_special_cases():
+    """K = N_r: the gates are the softmax over all experts (scipy). e = 0: every logit is 0,
+    experts 0..K-1 win by the lower-index rule with gates exactly 1/K. K = 1: gate 1."""
+    w = I.WORKLOADS["tiny_f32"]
+    u, e = I.make_u(w), I.make_e(w)
+    idx, gate, gap, _ = oracle.route(u, e, None, w.n_routed, w.act, score="softmax")
+    assert np.all(idx == np.arange(w.n_routed)[None, :]) and np.all(np.isinf(gap))
+    z = npref.widen(u, "f32") @ npref.widen(e, "f32").T
+    assert np.max(np.abs(gate - scipy.special.softmax(z, axis=1))) < 1e-14
+    w2 = I.WORKLOADS["mid_bf16"].with_tokens(16)
+    u2 = I.make_u(w2)
+    idx, gate, gap, _ = oracle.route(u2, np.zeros((w2.n_routed, w2.d), np.uint16), None, w2.top_k, w2.act,
+                                     score="softmax")
+    assert np.all(idx == np.arange(w2.top_k)[None, :]) and np.all(gate == 1.0 / w2.top_k)
+    assert np.all(gap == 0.0)
+    idx1, g1, _, _ = oracle.route(u2, I.make_e(w2), None, 1, w2.act, score="softmax")
+    z2 = npref.widen(u2, "bf16") @ npref.widen(I.make_e(w2), "bf16").T
+    assert np.array_equal(idx1[:, 0], np.argmax(z2, axis=1)) and np.all(g1 == 1.0)
+
+
 # ------------------------------------------------------------ dispatch, bias
 
 def _check_dispatch(idx, n_r, count, offset, sorted_token, pair_row):
@@ -447,26 +493,26 @@ def test_fp8_second_stage_lossless():
 
 # ------------------------------------------------------------ the whole layer
 
-def _layer_case(name, T):
+def _layer_case(name, T, score="sigmoid"):
     w = I.WORKLOADS[name]
     w = w if T is None else w.with_tokens(T)
     u, e, b = I.make_u(w), I.make_e(w), I.make_b(w)
     routed = {i: _weights(w, False, i) for i in range(w.n_routed)}
     shared = [_weights(w, True, j) for j in range(w.n_shared)]
     res = oracle.layer(u, e, b, routed, shared, top_k=w.top_k, d_ff=w.d_ff, act=w.act, ffn=w.ffn,
-                       want_components=True)
+                       want_components=True, score=score)
     return w, u, e, b, routed, shared, res
 
 
-@pytest.mark.parametrize("name,T", [("tiny_f32", None), ("mid_bf16", 24)])
-def test_layer_dense_all_experts(name, T):
+@pytest.mark.parametrize("name,T,score", [("tiny_f32", None, "sigmoid"), ("mid_bf16", 24, "sigmoid"),
+                                          ("tiny_f32", None, "softmax"), ("mid_bf16", 24, "softmax")])
+def test_layer_dense_all_experts(name, T, score):
     """Second formulation: every routed expert on every token, with a gate matrix that is
     zero outside the top-K, plus the shared experts and the residual (BLAS, float64)."""
-    w, u, e, b, routed, shared, res = _layer_case(name, T)
-    dt = I.weight_dtype(w)
+    w, u, e, b, routed, shared, res = _layer_case(name, T, score)
     ref, sel, G = npref.dense_layer(npref.widen(u, w.act), npref.widen(e, w.act), b.astype(np.float64),
                                     {i: _widen_tuple(w, t) for i, t in routed.items()},
-                                    [_widen_tuple(w, t) for t in shared], w.top_k, _hround(w))
+                                    [_widen_tuple(w, t) for t in shared], w.top_k, _hround(w), score)
     assert np.array_equal(res["idx"], sel)
     scale = np.max(np.abs(ref))
     assert np.max(np.abs(res["out"] - ref)) <= 1e-12 * scale
