@@ -39,7 +39,7 @@
 extern "C" {
 #endif
 
-#define MOE_ABI_VERSION 2
+#define MOE_ABI_VERSION 3
 
 typedef enum {
   MOE_OK = 0,
@@ -51,6 +51,13 @@ typedef enum {
 
 typedef enum { MOE_F32 = 0, MOE_BF16 = 1, MOE_FP8_E4M3 = 2 } moe_dtype;
 
+/* Router scoring.
+ *   SIGMOID  the explainer's method section 2: s = Sigmoid(z), top-K of s + b, gates s
+ *            normalised over the selection (the default, 0).
+ *   SOFTMAX  the deepseekmodel.com DeepSeekMoE forward listing: top-K of the logits z
+ *            themselves, no bias, gates = softmax of the K selected logits. */
+typedef enum { MOE_SCORE_SIGMOID = 0, MOE_SCORE_SOFTMAX = 1 } moe_score;
+
 /* Layer shape.
  *   T        tokens in the batch (>= 1)
  *   d        hidden size (multiple of 8; multiple of 128 when ffn == MOE_FP8_E4M3)
@@ -60,11 +67,13 @@ typedef enum { MOE_F32 = 0, MOE_BF16 = 1, MOE_FP8_E4M3 = 2 } moe_dtype;
  *   d_ff     SwiGLU intermediate size per expert (multiple of 64; of 128 for FP8)
  *   act      dtype of u, the centroids and the output: MOE_F32 or MOE_BF16
  *   ffn      dtype of the expert GEMM operands: MOE_F32 (with act F32), MOE_BF16 or
- *            MOE_FP8_E4M3 (both with act BF16) */
+ *            MOE_FP8_E4M3 (both with act BF16)
+ *   score    moe_score of the router (only moe_route reads it) */
 typedef struct {
   int64_t T;
   int32_t d, n_routed, top_k, n_shared, d_ff;
   int32_t act, ffn; /* moe_dtype */
+  int32_t score;    /* moe_score */
 } moe_shape;
 
 /* Weight layouts. ROWS: [E, N, K] row-major as listed below. TILED: the same values
@@ -88,16 +97,19 @@ typedef struct {
 } moe_expert_set;
 
 /* ---------------------------------------------------------------------------
- * moe_route: router of method section 2 (sigmoid affinity, biased top-K, gates).
+ * moe_route: router of method section 2 (sigmoid affinity, biased top-K, gates), or
+ * with shape->score == MOE_SCORE_SOFTMAX the forward listing's softmax router.
  *   u         [T, d]      act dtype
  *   centroids [N_r, d]    act dtype (the e_i; a bias-free linear gate)
- *   bias      [N_r]       fp32, the b_i (read only here)
+ *   bias      [N_r]       fp32, the b_i (read only here; may be NULL for SOFTMAX, which
+ *                         does not read it)
  *   topk_idx  [T, K]      int32 out: selected expert ids, ascending within a token
  *   topk_gate [T, K]      fp32 out: g_{i,t} aligned with topk_idx; sums to 1 per token
  *   ws            workspace of moe_workspace_bytes(shape, MOE_CALL_ROUTE) bytes (the
  *                 partial logits of the K chunks; 0 bytes, ws may be NULL, for fp32 act)
  * Logits accumulate in fp32 (bf16: per K chunk, the chunks added in order); ties in
- * s + b go to the lower expert index. */
+ * the selection key (s + b, or z) go to the lower expert index. SOFTMAX gates are
+ * expf(z_k - max z) over the selection divided by their sum in ascending expert order. */
 moe_status moe_route(const moe_shape* shape, const void* u, const void* centroids,
                      const float* bias, int32_t* topk_idx, float* topk_gate, void* ws,
                      size_t ws_bytes, void* stream);

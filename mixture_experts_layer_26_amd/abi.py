@@ -18,8 +18,10 @@ MOE_F32, MOE_BF16, MOE_FP8_E4M3 = 0, 1, 2
 MOE_CALL_ROUTE, MOE_CALL_DISPATCH, MOE_CALL_GROUPED_FFN, MOE_CALL_COMBINE, MOE_CALL_BIAS_UPDATE = range(5)
 MOE_LAYOUT_ROWS, MOE_LAYOUT_TILED = 0, 1
 MOE_W1, MOE_W3, MOE_W2 = 0, 1, 2
-ABI_VERSION = 2
+MOE_SCORE_SIGMOID, MOE_SCORE_SOFTMAX = 0, 1
+ABI_VERSION = 3
 DTYPES = {"f32": MOE_F32, "bf16": MOE_BF16, "fp8": MOE_FP8_E4M3}
+SCORES = {"sigmoid": MOE_SCORE_SIGMOID, "softmax": MOE_SCORE_SOFTMAX}
 
 
 class MoeError(RuntimeError):
@@ -31,7 +33,7 @@ class MoeError(RuntimeError):
 class moe_shape(ctypes.Structure):
     _fields_ = [("T", ctypes.c_int64), ("d", ctypes.c_int32), ("n_routed", ctypes.c_int32),
                 ("top_k", ctypes.c_int32), ("n_shared", ctypes.c_int32), ("d_ff", ctypes.c_int32),
-                ("act", ctypes.c_int32), ("ffn", ctypes.c_int32)]
+                ("act", ctypes.c_int32), ("ffn", ctypes.c_int32), ("score", ctypes.c_int32)]
 
 
 class moe_expert_set(ctypes.Structure):
@@ -100,8 +102,8 @@ def _check(call: str, st: int):
         raise MoeError(call, st, load().moe_status_string(st).decode())
 
 
-def make_shape(T, d, n_routed, top_k, n_shared, d_ff, act="bf16", ffn="bf16") -> moe_shape:
-    return moe_shape(T, d, n_routed, top_k, n_shared, d_ff, DTYPES[act], DTYPES[ffn])
+def make_shape(T, d, n_routed, top_k, n_shared, d_ff, act="bf16", ffn="bf16", score="sigmoid") -> moe_shape:
+    return moe_shape(T, d, n_routed, top_k, n_shared, d_ff, DTYPES[act], DTYPES[ffn], SCORES[score])
 
 
 def make_expert_set(w1, w3, w2, s1=None, s3=None, s2=None, layout: int = MOE_LAYOUT_ROWS) -> moe_expert_set:

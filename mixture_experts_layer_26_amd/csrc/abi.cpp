@@ -26,6 +26,7 @@ bool valid_shape(const moe_shape* s) {
   const bool f32 = s->act == MOE_F32 && s->ffn == MOE_F32;
   const bool bf16 = s->act == MOE_BF16 && s->ffn == MOE_BF16;
   const bool fp8 = s->act == MOE_BF16 && s->ffn == MOE_FP8_E4M3;
+  if (s->score != MOE_SCORE_SIGMOID && s->score != MOE_SCORE_SOFTMAX) return false;
   return f32 || bf16 || fp8;
 }
 
@@ -240,13 +241,14 @@ size_t moe_workspace_bytes(const moe_shape* s, int32_t call) {
 
 moe_status moe_route(const moe_shape* s, const void* u, const void* centroids, const float* bias,
                      int32_t* topk_idx, float* topk_gate, void* ws, size_t ws_bytes, void* stream) {
-  if (!valid_shape(s) || !u || !centroids || !bias || !topk_idx || !topk_gate)
-    return MOE_ERR_INVALID_ARG;
+  if (!valid_shape(s) || !u || !centroids || !topk_idx || !topk_gate) return MOE_ERR_INVALID_ARG;
+  const bool softmax = s->score == MOE_SCORE_SOFTMAX;
+  if (!bias && !softmax) return MOE_ERR_INVALID_ARG;
   const size_t need = moe_workspace_bytes(s, MOE_CALL_ROUTE);
   if (need > 0 && (!ws || ws_bytes < need)) return MOE_ERR_WORKSPACE;
-  return from_hip(moe::launch_route(s->act == MOE_BF16 ? 1 : 0, u, centroids, bias, s->T, s->d,
-                                    s->n_routed, s->top_k, topk_idx, topk_gate, static_cast<float*>(ws),
-                                    as_stream(stream)));
+  return from_hip(moe::launch_route(s->act == MOE_BF16 ? 1 : 0, softmax ? 1 : 0, u, centroids,
+                                    softmax ? nullptr : bias, s->T, s->d, s->n_routed, s->top_k, topk_idx,
+                                    topk_gate, static_cast<float*>(ws), as_stream(stream)));
 }
 
 moe_status moe_dispatch(const moe_shape* s, const int32_t* topk_idx, int32_t* expert_count,

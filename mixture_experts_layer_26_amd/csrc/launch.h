@@ -80,8 +80,9 @@ struct RouteChunks {
 };
 RouteChunks route_chunks(int64_t T, int d);
 size_t route_workspace_bytes(int64_t T, int d, int n_r);
-hipError_t launch_route(int act, const void* u, const void* e, const float* bias, int64_t T, int d,
-                        int n_r, int K, int32_t* idx, float* gate, float* part, hipStream_t stream);
+// score: 0 sigmoid with bias, 1 softmax over the top-K logits (bias unused, may be null)
+hipError_t launch_route(int act, int score, const void* u, const void* e, const float* bias, int64_t T,
+                        int d, int n_r, int K, int32_t* idx, float* gate, float* part, hipStream_t stream);
 
 int dispatch_blocks(int64_t T);
 hipError_t launch_dispatch(const int32_t* idx, int64_t T, int K, int n_r, int32_t* hist,

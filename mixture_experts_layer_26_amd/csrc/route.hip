@@ -2,6 +2,8 @@
 // gates = selected s normalised over the selection.
 // DeepSeek-V3 explainer (xyznot.com), method section 2: the sigmoid affinity and the
 // equation for g'_{i,t}; gates normalise g'.
+// Softmax scoring (the DeepSeekMoE forward listing of deepseekmodel.com): top-K of the
+// logits z themselves, no bias, gates = softmax of the selected logits.
 //
 // bf16 activations take two kernels. route_logits: a workgroup owns 128 tokens x 256
 // experts over one chunk of K (the grid splits K so that it fills the chip even for a
@@ -42,7 +44,10 @@ __device__ __forceinline__ float sigmoid_precise(float z) { return 1.0f / (1.0f 
 // Top-K of one token held by one wave: lane l holds the keys and scores of experts
 // l + 64 c (c = 0..3; key 0 = no expert). Lane k < K keeps the k-th pick (no per-lane
 // array is indexed at run time); picks are written in ascending expert order with
-// gates = score / (sum of the picked scores, added in ascending expert order).
+// gates = score / (sum of the picked scores, added in ascending expert order). With
+// SOFTMAX the scores are the logits and each picked one becomes expf(z - z_max) first;
+// the first pick has the largest key, so its logit is z_max.
+template <bool SOFTMAX>
 __device__ __forceinline__ void topk_select(uint64_t (&key)[4], const float (&sv)[4], int lane, int K,
                                             int32_t* __restrict__ idx, float* __restrict__ gate) {
   int mysel = 0x7FFFFFFF;
@@ -64,7 +69,11 @@ __device__ __forceinline__ void topk_select(uint64_t (&key)[4], const float (&sv
   const int src = (lane < K ? mysel : 0) & 63, slot = (lane < K ? mysel : 0) >> 6;
   float v0 = __shfl(sv[0], src, kWave), v1 = __shfl(sv[1], src, kWave);
   float v2 = __shfl(sv[2], src, kWave), v3 = __shfl(sv[3], src, kWave);
-  const float myv = lane < K ? (slot == 0 ? v0 : slot == 1 ? v1 : slot == 2 ? v2 : v3) : 0.0f;
+  float myv = lane < K ? (slot == 0 ? v0 : slot == 1 ? v1 : slot == 2 ? v2 : v3) : 0.0f;
+  if (SOFTMAX) {
+    const float zmax = __shfl(myv, 0, kWave);
+    myv = lane < K ? expf(myv - zmax) : 0.0f;
+  }
   float denom = 0.0f;
   for (int p = 0; p < K; ++p) {
     const uint64_t m = __ballot(lane < K && rank == p);
@@ -165,7 +174,22 @@ __global__ __launch_bounds__(kThreads) void route_logits(const uint16_t* __restr
   }
 }
 
+// Selection key and score of one expert from its logit z.
+template <int SCORE>
+__device__ __forceinline__ void score_key(float z, const float* __restrict__ bias, int j, float& sv, uint64_t& key) {
+  float v;
+  if (SCORE == 1) {
+    sv = z;
+    v = z;
+  } else {
+    sv = sigmoid_precise(z);
+    v = sv + bias[j];
+  }
+  key = (static_cast<uint64_t>(orderable(v)) << 32) | (0xFFFFFFFFu - static_cast<uint32_t>(j));
+}
+
 // Top-K of one token per wave from the partial logits of n_chunks chunks.
+template <int SCORE>
 __global__ __launch_bounds__(256) void route_topk(const float* __restrict__ part, int n_chunks,
                                                   const float* __restrict__ bias, int64_t T, int n_r, int K,
                                                   int32_t* __restrict__ topk_idx, float* __restrict__ topk_gate) {
@@ -183,16 +207,14 @@ __global__ __launch_bounds__(256) void route_topk(const float* __restrict__ part
     if (j < n_r) {
       float z = 0.0f;
       for (int q = 0; q < n_chunks; ++q) z += part[(static_cast<int64_t>(q) * T + t) * n_r + j];
-      sv[c] = sigmoid_precise(z);
-      const float v = sv[c] + bias[j];
-      key[c] = (static_cast<uint64_t>(orderable(v)) << 32) | (0xFFFFFFFFu - static_cast<uint32_t>(j));
+      score_key<SCORE>(z, bias, j, sv[c], key[c]);
     }
   }
-  topk_select(key, sv, lane, K, topk_idx + t * K, topk_gate + t * K);
+  topk_select<SCORE == 1>(key, sv, lane, K, topk_idx + t * K, topk_gate + t * K);
 }
 
 __device__ void logits_f32(const float* __restrict__ u, const float* __restrict__ e, int64_t T,
-                           int d, int n_r, int64_t t0, float* sc) {
+                           int d, int n_r, int64_t t0, float* zs) {
   for (int p = threadIdx.x; p < kTok * n_r; p += kThreads) {
     const int i = p / n_r, j = p % n_r;
     int64_t t = t0 + i;
@@ -201,19 +223,20 @@ __device__ void logits_f32(const float* __restrict__ u, const float* __restrict_
     const float* b = e + static_cast<int64_t>(j) * d;
     float z = 0.0f;
     for (int c = 0; c < d; ++c) z = fmaf(a[c], b[c], z);
-    sc[i * n_r + j] = sigmoid_precise(z);
+    zs[i * n_r + j] = z;
   }
 }
 
 // fp32 activations: one workgroup of 8 waves owns 32 tokens; logits are plain fp32
-// dot products parked in LDS as sigmoid scores, then one wave per token selects.
+// dot products parked in LDS, then one wave per token scores and selects.
+template <int SCORE>
 __global__ __launch_bounds__(kThreads) void route_kernel(const float* __restrict__ u, const float* __restrict__ e,
                                                          const float* __restrict__ bias, int64_t T, int d, int n_r,
                                                          int K, int32_t* __restrict__ topk_idx,
                                                          float* __restrict__ topk_gate) {
-  __shared__ float sc[kTok * kMaxExperts];
+  __shared__ float zs[kTok * kMaxExperts];
   const int64_t t0 = static_cast<int64_t>(blockIdx.x) * kTok;
-  logits_f32(u, e, T, d, n_r, t0, sc);
+  logits_f32(u, e, T, d, n_r, t0, zs);
   __syncthreads();
   const int lane = threadIdx.x % kWave, wave = threadIdx.x / kWave;
   for (int i = wave; i < kTok; i += kThreads / kWave) {
@@ -226,13 +249,9 @@ __global__ __launch_bounds__(kThreads) void route_kernel(const float* __restrict
       const int j = lane + 64 * c;
       key[c] = 0;  // below every real key
       sv[c] = 0.0f;
-      if (j < n_r) {
-        sv[c] = sc[i * n_r + j];
-        const float v = sv[c] + bias[j];
-        key[c] = (static_cast<uint64_t>(orderable(v)) << 32) | (0xFFFFFFFFu - static_cast<uint32_t>(j));
-      }
+      if (j < n_r) score_key<SCORE>(zs[i * n_r + j], bias, j, sv[c], key[c]);
     }
-    topk_select(key, sv, lane, K, topk_idx + t * K, topk_gate + t * K);
+    topk_select<SCORE == 1>(key, sv, lane, K, topk_idx + t * K, topk_gate + t * K);
   }
 }
 
@@ -257,8 +276,8 @@ size_t route_workspace_bytes(int64_t T, int d, int n_r) {
   return static_cast<size_t>(route_chunks(T, d).chunks) * static_cast<size_t>(T) * n_r * sizeof(float);
 }
 
-hipError_t launch_route(int act, const void* u, const void* e, const float* bias, int64_t T, int d, int n_r,
-                        int K, int32_t* idx, float* gate, float* part, hipStream_t stream) {
+hipError_t launch_route(int act, int score, const void* u, const void* e, const float* bias, int64_t T, int d,
+                        int n_r, int K, int32_t* idx, float* gate, float* part, hipStream_t stream) {
   if (act == 1) {
     const RouteChunks rc = route_chunks(T, d);
     const dim3 grid(static_cast<unsigned>((T + kTB - 1) / kTB), static_cast<unsigned>(rc.chunks));
@@ -267,13 +286,20 @@ hipError_t launch_route(int act, const void* u, const void* e, const float* bias
     hipError_t err = hipGetLastError();
     if (err != hipSuccess) return err;
     const unsigned waves_per_block = 256 / kWave;
-    hipLaunchKernelGGL(route_topk, dim3(static_cast<unsigned>((T + waves_per_block - 1) / waves_per_block)),
-                       dim3(256), 0, stream, part, rc.chunks, bias, T, n_r, K, idx, gate);
+    const dim3 tgrid(static_cast<unsigned>((T + waves_per_block - 1) / waves_per_block));
+    if (score == 1)
+      hipLaunchKernelGGL(route_topk<1>, tgrid, dim3(256), 0, stream, part, rc.chunks, bias, T, n_r, K, idx, gate);
+    else
+      hipLaunchKernelGGL(route_topk<0>, tgrid, dim3(256), 0, stream, part, rc.chunks, bias, T, n_r, K, idx, gate);
     return hipGetLastError();
   }
   const dim3 grid(static_cast<unsigned>((T + kTok - 1) / kTok));
-  hipLaunchKernelGGL(route_kernel, grid, dim3(kThreads), 0, stream, static_cast<const float*>(u),
-                     static_cast<const float*>(e), bias, T, d, n_r, K, idx, gate);
+  if (score == 1)
+    hipLaunchKernelGGL(route_kernel<1>, grid, dim3(kThreads), 0, stream, static_cast<const float*>(u),
+                       static_cast<const float*>(e), bias, T, d, n_r, K, idx, gate);
+  else
+    hipLaunchKernelGGL(route_kernel<0>, grid, dim3(kThreads), 0, stream, static_cast<const float*>(u),
+                       static_cast<const float*>(e), bias, T, d, n_r, K, idx, gate);
   return hipGetLastError();
 }
 

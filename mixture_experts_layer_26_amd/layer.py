@@ -16,11 +16,12 @@ _TORCH_ACT = {"f32": torch.float32, "bf16": torch.bfloat16}
 
 class MoeLayer:
     def __init__(self, T: int, d: int, n_routed: int, top_k: int, n_shared: int, d_ff: int,
-                 act: str = "bf16", ffn: str = "bf16", device: str = "cuda"):
+                 act: str = "bf16", ffn: str = "bf16", device: str = "cuda", score: str = "sigmoid"):
         self.T, self.d, self.n_routed, self.top_k = T, d, n_routed, top_k
         self.n_shared, self.d_ff, self.act, self.ffn = n_shared, d_ff, act, ffn
+        self.score = score
         self.device = torch.device(device)
-        self.shape = abi.make_shape(T, d, n_routed, top_k, n_shared, d_ff, act, ffn)
+        self.shape = abi.make_shape(T, d, n_routed, top_k, n_shared, d_ff, act, ffn, score)
         adt = _TORCH_ACT[act]
         dev = self.device
         i32 = torch.int32

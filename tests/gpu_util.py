@@ -61,8 +61,9 @@ def rel_errors(out: np.ndarray, ref: np.ndarray):
     return frob, maxabs
 
 
-def check_routing(idx_gpu, gate_gpu, idx_ref, gate_ref, gap_ref, v_ref, K):
-    """Bit-exact ids on non-exempt tokens; exempt tokens must be valid within the band.
+def check_routing(idx_gpu, gate_gpu, idx_ref, gate_ref, gap_ref, v_ref, K, gate_tol=1e-6):
+    """Bit-exact ids on non-exempt tokens; exempt tokens must be valid within the band;
+    gates within gate_tol of the oracle's where the selection agrees.
     Returns the indices of tokens whose selection differs from the oracle's."""
     exempt = gap_ref < TIE_BAND
     diff = np.any(idx_gpu != idx_ref, axis=1)
@@ -76,7 +77,7 @@ def check_routing(idx_gpu, gate_gpu, idx_ref, gate_ref, gap_ref, v_ref, K):
         rest = np.setdiff1d(np.arange(v_ref.shape[1]), sel)
         assert np.all(v_ref[t, rest] <= vK1 + TIE_BAND)
     same = ~diff
-    assert np.max(np.abs(gate_gpu[same] - gate_ref[same])) <= 1e-6
+    assert np.max(np.abs(gate_gpu[same] - gate_ref[same])) <= gate_tol
     assert np.max(np.abs(gate_gpu.sum(1) - 1.0)) <= K * 2.0 ** -23
     return np.nonzero(diff)[0], int(exempt.sum())
 

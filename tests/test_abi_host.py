@@ -23,7 +23,7 @@ def test_exports_every_declared_symbol():
     assert {"moe_route", "moe_dispatch", "moe_grouped_ffn", "moe_combine", "moe_bias_update"} <= set(names)
     for n in names:
         assert hasattr(lib, n), n
-    assert lib.moe_abi_version() == abi.ABI_VERSION == 2
+    assert lib.moe_abi_version() == abi.ABI_VERSION == 3
     assert lib.moe_status_string(0) == b"ok"
 
 
@@ -102,6 +102,26 @@ def test_route_workspace():
     assert lib.moe_route(ctypes.byref(sb), FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, need - 1, None) == \
         abi.MOE_ERR_WORKSPACE
     assert lib.moe_route(ctypes.byref(sb), FAKE, FAKE, FAKE, FAKE, FAKE, None, need, None) == \
+        abi.MOE_ERR_WORKSPACE
+
+
+def test_route_score_modes():
+    """score is SIGMOID or SOFTMAX; only SOFTMAX may go without a bias. Every call here is
+    stopped on the host (the workspace is one byte short)."""
+    lib = abi.load()
+    assert ctypes.sizeof(abi.moe_shape) == 40
+    bad = _shape()
+    bad.score = 2
+    assert lib.moe_route(ctypes.byref(bad), FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 1 << 30, None) == \
+        abi.MOE_ERR_INVALID_ARG
+    assert abi.moe_workspace_bytes(bad, abi.MOE_CALL_ROUTE) == 0
+    sig = _shape(T=256, d=256, act="bf16", ffn="bf16")
+    soft = _shape(T=256, d=256, act="bf16", ffn="bf16", score="softmax")
+    need = abi.moe_workspace_bytes(soft, abi.MOE_CALL_ROUTE)
+    assert need == abi.moe_workspace_bytes(sig, abi.MOE_CALL_ROUTE) > 0
+    assert lib.moe_route(ctypes.byref(sig), FAKE, FAKE, None, FAKE, FAKE, FAKE, need, None) == \
+        abi.MOE_ERR_INVALID_ARG
+    assert lib.moe_route(ctypes.byref(soft), FAKE, FAKE, None, FAKE, FAKE, FAKE, need - 1, None) == \
         abi.MOE_ERR_WORKSPACE
 
 
