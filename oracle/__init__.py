@@ -65,6 +65,9 @@ def _load():
     lib.orc_layer.restype = i32
     lib.orc_combine.argtypes = [i64, i32, i32, i32, vp, vp, vp, vp, vp, vp]
     lib.orc_combine.restype = None
+    lib.orc_layer_backward.argtypes = [i64, i32, i32, i32, i32, i32, i32, i32, i32, vp, vp, vp] + \
+        [vp] * 6 + [vp] * 3 + [vp] * 6 + [vp] * 4
+    lib.orc_layer_backward.restype = i32
     for f in (lib.orc_bf16_from_double_array, lib.orc_e4m3_from_float_array,
               lib.orc_quantize_tiles, lib.orc_route, lib.orc_dispatch, lib.orc_bias_update,
               lib.orc_expert_rows):
@@ -247,3 +250,55 @@ def combine(u, y_shared, y_routed, pair_row, gate, act: str):
     out = np.empty((n, d), np.float64)
     _load().orc_combine(n, d, K, dt, _p(u), _p(ysh), _p(y), _p(pr), _p(g), _p(out))
     return out
+
+
+def layer_backward(u, e, b, routed: dict, shared: list, dout, *, top_k: int, d_ff: int, act: str,
+                   ffn: str, score: str = "sigmoid", want_du: bool = True, want_de: bool = True,
+                   grad_routed=(), grad_shared: bool = False):
+    """Gradients of sum(dout * out) for the tokens whose rows are u, in double.
+
+    routed: {expert id: (w1, w3, w2)} for at least every expert whose rows are needed
+    (all selected experts when du or de is wanted, else those in grad_routed); shared: the
+    N_s shared experts' tuples. grad_routed: routed ids whose dW1, dW3, dW2 are formed;
+    grad_shared: form the shared experts' too. Returns a dict with du, de (or None),
+    dw_routed {i: (dw1, dw3, dw2)}, dw_shared [(dw1, dw3, dw2)], idx, gate, dgate, dz."""
+    adt, fdt = _DT[act], _DT[ffn]
+    u = _act_arr(u, adt)
+    e = _act_arr(e, adt)
+    dout = _act_arr(dout, adt)
+    n, d = u.shape
+    n_r = e.shape[0]
+    n_s = len(shared)
+    b = _c(np.zeros(n_r, np.float32) if b is None else b, np.float32)
+    wdt = np.float32 if fdt == ORC_F32 else np.uint16
+    keep = []
+
+    def prep(tup):
+        ws = [_c(a, wdt) for a in tup[:3]]
+        keep.extend(ws)
+        return ws
+
+    r = [prep(routed[i]) if i in routed else [None] * 3 for i in range(n_r)]
+    s = [prep(t) for t in shared]
+    warrs = [_ptr_array([x[j] for x in r]) for j in range(3)] + [_ptr_array([x[j] for x in s]) for j in range(3)]
+    dwr = {int(i): (np.empty((d_ff, d)), np.empty((d_ff, d)), np.empty((d, d_ff))) for i in grad_routed}
+    dws = [(np.empty((d_ff, d)), np.empty((d_ff, d)), np.empty((d, d_ff))) for _ in range(n_s)] \
+        if grad_shared else []
+    garrs = [_ptr_array([dwr[i][j] if i in dwr else None for i in range(n_r)]) for j in range(3)] + \
+            [_ptr_array([x[j] for x in dws]) if dws else None for j in range(3)]
+    du = np.empty((n, d)) if want_du else None
+    de = np.empty((n_r, d)) if want_de else None
+    idx = np.empty((n, top_k), np.int32)
+    gate = np.empty((n, top_k))
+    dgate = np.empty((n, top_k))
+    dz = np.empty((n, top_k))
+    full = want_du or want_de
+    st = _load().orc_layer_backward(
+        n, d, n_r, top_k, n_s, d_ff, adt, fdt, _SCORE[score], _p(u), _p(e), _p(b),
+        *[ctypes.cast(a, ctypes.c_void_p) for a in warrs], _p(dout), _p(du), _p(de),
+        *[None if a is None else ctypes.cast(a, ctypes.c_void_p) for a in garrs],
+        _p(idx), _p(gate), _p(dgate) if full else None, _p(dz) if full else None)
+    if st != 0:
+        raise ValueError(f"oracle layer_backward: status {st}")
+    return {"du": du, "de": de, "dw_routed": dwr, "dw_shared": dws, "idx": idx, "gate": gate,
+            "dgate": dgate if full else None, "dz": dz if full else None}

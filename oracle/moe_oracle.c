@@ -477,3 +477,249 @@ void orc_combine(int64_t n, int d, int K, int act, const void* u, const float* y
       out[t * d + c] = o;
     }
 }
+
+/* -------------------------------------------------------------------- backward */
+
+/* rounding to the GEMM operand type (ORC_F32 or ORC_BF16) */
+static double op_round(int dt, double x) {
+  return dt == ORC_F32 ? (double)(float)x : orc_bf16_value(orc_bf16_from_double(x));
+}
+
+/* Backward of one row through one SwiGLU expert, the chain rule on
+ *   a = W1 x,  v = W3 x,  h = SiLU(a) v,  y = W2 h,
+ * for the row's output gradient dy:
+ *   dh = W2^T dy,  da = dh v SiLU'(a),  dv = dh SiLU(a),  dx = W1^T da + W3^T dv,
+ * with SiLU(a) = a sigmoid(a) and SiLU'(a) = sigmoid(a) (1 + a (1 - sigmoid(a))).
+ * The row's weight-gradient terms are da x^T (W1), dv x^T (W3) and dy h^T (W2).
+ * Rounding points: h as in the forward; da and dv at the operand type, since the
+ * products that take them run in that type ([ARCH] quantisation section: gradients
+ * in BF16). xd and dyd are the row's x and dy in double, dy already rounded.
+ * Out: h, da, dv [d_ff]; y [d] (optional); dx [d] (optional). */
+static void ffn_row_backward(int d, int d_ff, int wdt, const double* xd, const double* dyd,
+                             const void* w1, const void* w3, const void* w2, double* h, double* da,
+                             double* dv, double* y, double* dx) {
+  for (int j = 0; j < d_ff; ++j) {
+    double a = 0.0, v = 0.0, dh = 0.0;
+    for (int c = 0; c < d; ++c) {
+      a += xd[c] * load_val(w1, wdt, (int64_t)j * d + c);
+      v += xd[c] * load_val(w3, wdt, (int64_t)j * d + c);
+      dh += dyd[c] * load_val(w2, wdt, (int64_t)c * d_ff + j);
+    }
+    const double sg = sigmoid(a);
+    h[j] = op_round(wdt, a * sg * v);
+    da[j] = op_round(wdt, dh * v * sg * (1.0 + a * (1.0 - sg)));
+    dv[j] = op_round(wdt, dh * a * sg);
+  }
+  if (y)
+    for (int c = 0; c < d; ++c) {
+      double acc = 0.0;
+      for (int j = 0; j < d_ff; ++j) acc += h[j] * load_val(w2, wdt, (int64_t)c * d_ff + j);
+      y[c] = acc;
+    }
+  if (dx)
+    for (int c = 0; c < d; ++c) {
+      double s1 = 0.0, s3 = 0.0;
+      for (int j = 0; j < d_ff; ++j) {
+        s1 += da[j] * load_val(w1, wdt, (int64_t)j * d + c);
+        s3 += dv[j] * load_val(w3, wdt, (int64_t)j * d + c);
+      }
+      dx[c] = s1 + s3;
+    }
+}
+
+/* Gradient of the router's gates with respect to the selected logits z_k.
+ * Sigmoid ([V3] method section 2): g_k = s_k / S, s_k = sigmoid(z_k), S = sum of the
+ * selected s; the bias only chooses the set, so it carries no gradient and the set is
+ * held fixed: dL/ds_k = (dg_k - sum_j g_j dg_j) / S, dz_k = dL/ds_k s_k (1 - s_k).
+ * Softmax ([ARCH] forward listing): dz_k = g_k (dg_k - sum_j g_j dg_j).
+ * sel[k]: s_k (sigmoid) or z_k (softmax) of the K picks; g: their gates. */
+static void router_backward(int K, int score, const double* sel, const double* g, const double* dg,
+                            double* dz) {
+  double gbar = 0.0;
+  for (int k = 0; k < K; ++k) gbar += g[k] * dg[k];
+  if (score == ORC_SOFTMAX) {
+    for (int k = 0; k < K; ++k) dz[k] = g[k] * (dg[k] - gbar);
+    return;
+  }
+  double S = 0.0;
+  for (int k = 0; k < K; ++k) S += sel[k];
+  for (int k = 0; k < K; ++k) dz[k] = (dg[k] - gbar) / S * sel[k] * (1.0 - sel[k]);
+}
+
+typedef struct {
+  double *h, *da, *dv, *dy;
+} row_grads;
+
+/* Backward of the layer for n tokens with output gradient dout [n, d] (act dtype),
+ * i.e. the gradients of L = sum dout . h' with the routing held fixed (selection is
+ * piecewise constant in u, e and b). Forward as orc_layer (bf16 or fp32 experts).
+ *   du [n, d]: dout (residual) + shared experts' dx + routed dx + sum_k dz_k e_{i_k}
+ *   de [n_r, d]: sum over the tokens that chose expert i of dz u_t
+ *   dwr1/dwr3 [d_ff, d], dwr2 [d, d_ff] per routed expert; dws* per shared expert:
+ *     sums over the expert's rows in token order of the row terms of ffn_row_backward.
+ * A routed row's dy is g_k dout_t rounded to the operand type; a shared row's is dout_t.
+ * dgate [n, K] = dout_t . y_{k,t}; dz [n, K] as router_backward. Every output pointer
+ * may be NULL (an entry of dwr* / dws* too: that expert's gradient is not formed);
+ * only the rows that the requested outputs need are evaluated.
+ * Returns 0; -1 for FP8 experts; -2 if a needed expert has no weights. */
+int orc_layer_backward(int64_t n, int d, int n_r, int K, int n_s, int d_ff, int act, int ffn,
+                       int score, const void* u, const void* e, const float* b,
+                       const void* const* wr1, const void* const* wr3, const void* const* wr2,
+                       const void* const* ws1, const void* const* ws3, const void* const* ws2,
+                       const void* dout, double* du, double* de, double* const* dwr1,
+                       double* const* dwr3, double* const* dwr2, double* const* dws1,
+                       double* const* dws3, double* const* dws2, int32_t* idx_out,
+                       double* gate_out, double* dgate_out, double* dz_out) {
+  if (ffn == ORC_FP8) return -1;
+  const size_t usz = (act == ORC_F32) ? 4 : 2;
+  const int full = du || de || dgate_out || dz_out;
+  int32_t* idx = (int32_t*)malloc(sizeof(int32_t) * n * K);
+  double* gate = (double*)malloc(sizeof(double) * n * K);
+  double* sel = (double*)malloc(sizeof(double) * n * K);
+  double* dg = (double*)calloc((size_t)(n * K), sizeof(double));
+  double* dz = (double*)calloc((size_t)(n * K), sizeof(double));
+  /* routing, as the forward */
+#pragma omp parallel
+  {
+    double* ud = (double*)malloc(sizeof(double) * d);
+    double* s = (double*)malloc(sizeof(double) * n_r);
+    double* vv = (double*)malloc(sizeof(double) * n_r);
+    char* taken = (char*)malloc(n_r);
+#pragma omp for schedule(static)
+    for (int64_t t = 0; t < n; ++t) {
+      double gap;
+      route_one(d, n_r, K, act, score, (const char*)u + (size_t)t * d * usz, e, b, ud, s, vv, taken,
+                idx + t * K, gate + t * K, &gap);
+      for (int k = 0; k < K; ++k) sel[t * K + k] = s[idx[t * K + k]];
+    }
+    free(ud); free(s); free(vv); free(taken);
+  }
+  int status = 0;
+  /* which rows are evaluated, and where the kept row terms go */
+  const int wants_r = dwr1 || dwr3 || dwr2;
+  int64_t* slot = (int64_t*)malloc(sizeof(int64_t) * n * K);
+  int64_t n_keep = 0;
+  for (int64_t p = 0; p < n * K; ++p) {
+    const int i = idx[p];
+    const int keep = wants_r && ((dwr1 && dwr1[i]) || (dwr3 && dwr3[i]) || (dwr2 && dwr2[i]));
+    slot[p] = keep ? n_keep++ : -1;
+    if ((full || keep) && (!wr1[i] || !wr3[i] || !wr2[i])) status = -2;
+  }
+  int shared_keep = 0;
+  for (int j = 0; j < n_s; ++j)
+    if ((dws1 && dws1[j]) || (dws3 && dws3[j]) || (dws2 && dws2[j])) shared_keep = 1;
+  if (status != 0) {
+    free(idx); free(gate); free(sel); free(dg); free(dz); free(slot);
+    return status;
+  }
+  const size_t rowlen = (size_t)3 * d_ff + d;
+  double* kept = (double*)malloc(sizeof(double) * rowlen * (size_t)(n_keep > 0 ? n_keep : 1));
+  double* kept_s = shared_keep ? (double*)malloc(sizeof(double) * rowlen * (size_t)n * n_s) : NULL;
+#pragma omp parallel
+  {
+    double* xd = (double*)malloc(sizeof(double) * d);
+    double* dyd = (double*)malloc(sizeof(double) * d);
+    double* y = (double*)malloc(sizeof(double) * d);
+    double* dx = (double*)malloc(sizeof(double) * d);
+    double* acc = (double*)malloc(sizeof(double) * d);
+    double* tmp = (double*)malloc(sizeof(double) * rowlen);
+#pragma omp for schedule(dynamic, 1)
+    for (int64_t t = 0; t < n; ++t) {
+      const void* xrow = (const char*)u + (size_t)t * d * usz;
+      int any = full || shared_keep;
+      for (int k = 0; k < K; ++k) any |= slot[t * K + k] >= 0;
+      if (!any) continue;
+      for (int c = 0; c < d; ++c) {
+        xd[c] = load_val(xrow, act, c);
+        acc[c] = load_val(dout, act, t * d + c); /* residual */
+      }
+      /* shared experts: dy = dout_t */
+      if (full || shared_keep)
+        for (int j = 0; j < n_s; ++j) {
+          double* r = kept_s ? kept_s + rowlen * (size_t)(t * n_s + j) : tmp;
+          for (int c = 0; c < d; ++c) r[3 * d_ff + c] = load_val(dout, act, t * d + c);
+          ffn_row_backward(d, d_ff, ffn, xd, r + 3 * d_ff, ws1[j], ws3[j], ws2[j], r, r + d_ff,
+                           r + 2 * d_ff, NULL, full ? dx : NULL);
+          if (full)
+            for (int c = 0; c < d; ++c) acc[c] += dx[c];
+        }
+      /* routed experts, ascending: dy = g dout_t at the operand type */
+      for (int k = 0; k < K; ++k) {
+        const int64_t p = t * K + k;
+        if (!full && slot[p] < 0) continue;
+        const int i = idx[p];
+        double* r = slot[p] >= 0 ? kept + rowlen * (size_t)slot[p] : tmp;
+        for (int c = 0; c < d; ++c) r[3 * d_ff + c] = op_round(ffn, gate[p] * load_val(dout, act, t * d + c));
+        ffn_row_backward(d, d_ff, ffn, xd, r + 3 * d_ff, wr1[i], wr3[i], wr2[i], r, r + d_ff,
+                         r + 2 * d_ff, full ? y : NULL, full ? dx : NULL);
+        if (full) {
+          double s = 0.0;
+          for (int c = 0; c < d; ++c) {
+            acc[c] += dx[c];
+            s += load_val(dout, act, t * d + c) * y[c];
+          }
+          dg[p] = s;
+        }
+      }
+      if (full) {
+        router_backward(K, score, sel + t * K, gate + t * K, dg + t * K, dz + t * K);
+        for (int k = 0; k < K; ++k) {
+          const int i = idx[t * K + k];
+          for (int c = 0; c < d; ++c) acc[c] += dz[t * K + k] * load_val(e, act, (int64_t)i * d + c);
+        }
+        if (du) memcpy(du + t * d, acc, sizeof(double) * d);
+      }
+    }
+    free(xd); free(dyd); free(y); free(dx); free(acc); free(tmp);
+  }
+  /* per-expert sums over rows in token order */
+#pragma omp parallel for schedule(dynamic, 1)
+  for (int i = 0; i < n_r + n_s; ++i) {
+    const int shared = i >= n_r;
+    const int j = shared ? i - n_r : i;
+    double* g1 = shared ? (dws1 ? dws1[j] : NULL) : (dwr1 ? dwr1[j] : NULL);
+    double* g3 = shared ? (dws3 ? dws3[j] : NULL) : (dwr3 ? dwr3[j] : NULL);
+    double* g2 = shared ? (dws2 ? dws2[j] : NULL) : (dwr2 ? dwr2[j] : NULL);
+    double* gde = (!shared && de) ? de + (int64_t)j * d : NULL;
+    if (!g1 && !g3 && !g2 && !gde) continue;
+    if (g1) memset(g1, 0, sizeof(double) * d_ff * d);
+    if (g3) memset(g3, 0, sizeof(double) * d_ff * d);
+    if (g2) memset(g2, 0, sizeof(double) * d * d_ff);
+    if (gde) memset(gde, 0, sizeof(double) * d);
+    double* xd = (double*)malloc(sizeof(double) * d);
+    for (int64_t t = 0; t < n; ++t) {
+      const double* r = NULL;
+      double dzt = 0.0;
+      if (shared) {
+        r = kept_s + rowlen * (size_t)(t * n_s + j);
+      } else {
+        int k = 0;
+        while (k < K && idx[t * K + k] != j) ++k;
+        if (k == K) continue;
+        const int64_t p = t * K + k;
+        dzt = dz[p];
+        if (slot[p] >= 0) r = kept + rowlen * (size_t)slot[p];
+      }
+      for (int c = 0; c < d; ++c) xd[c] = load_val(u, act, t * d + c);
+      if (gde)
+        for (int c = 0; c < d; ++c) gde[c] += dzt * xd[c];
+      if (!r) continue;
+      const double *h = r, *da = r + d_ff, *dv = r + 2 * d_ff, *dy = r + 3 * d_ff;
+      for (int jj = 0; jj < d_ff; ++jj)
+        for (int c = 0; c < d; ++c) {
+          if (g1) g1[(int64_t)jj * d + c] += da[jj] * xd[c];
+          if (g3) g3[(int64_t)jj * d + c] += dv[jj] * xd[c];
+        }
+      if (g2)
+        for (int c = 0; c < d; ++c)
+          for (int jj = 0; jj < d_ff; ++jj) g2[(int64_t)c * d_ff + jj] += dy[c] * h[jj];
+    }
+    free(xd);
+  }
+  if (idx_out) memcpy(idx_out, idx, sizeof(int32_t) * n * K);
+  if (gate_out) memcpy(gate_out, gate, sizeof(double) * n * K);
+  if (dgate_out) memcpy(dgate_out, dg, sizeof(double) * n * K);
+  if (dz_out) memcpy(dz_out, dz, sizeof(double) * n * K);
+  free(idx); free(gate); free(sel); free(dg); free(dz); free(slot); free(kept); free(kept_s);
+  return 0;
+}

@@ -96,6 +96,31 @@ int orc_layer(int64_t n, int d, int n_r, int K, int n_s, int d_ff, int act, int 
               double* out, int32_t* idx, double* gate, double* gap,
               double* shared_sum, double* routed_sum);
 
+/* ---- backward of the layer (gradients of L = sum dout . h', routing held fixed)
+ * Forward as orc_layer with bf16 or fp32 experts (FP8 returns -1). Row chain rule:
+ *   a = W1 x, v = W3 x, h = SiLU(a) v, y = W2 h; dh = W2^T dy, da = dh v SiLU'(a),
+ *   dv = dh SiLU(a), dx = W1^T da + W3^T dv; row terms of dW1, dW3, dW2: da x^T,
+ *   dv x^T, dy h^T. Rounded to the operand type: h, da, dv, and a routed row's dy =
+ *   g dout_t ([ARCH] quantisation section: gradients in BF16); shared rows take dy = dout_t.
+ * Router ([V3] method section 2: the bias only selects): with the selection fixed,
+ *   sigmoid: dz_k = (dg_k - sum_j g_j dg_j) / S * s_k (1 - s_k), S = sum of picked s;
+ *   softmax: dz_k = g_k (dg_k - sum_j g_j dg_j); dg_k = dout_t . y_k.
+ * Outputs (each may be NULL; so may entries of dwr* and dws*):
+ *   du [n, d] = dout_t + shared dx + routed dx (ascending) + sum_k dz_k e_{i_k}
+ *   de [n_r, d] = sum over tokens choosing i (ascending) of dz u_t
+ *   dwr1[i], dwr3[i] [d_ff, d], dwr2[i] [d, d_ff]; dws* for the shared experts,
+ *     each a sum over the expert's rows in token order
+ *   idx, gate, dgate, dz [n, K]
+ * Returns 0, -1 (FP8) or -2 (a needed expert has no weights). */
+int orc_layer_backward(int64_t n, int d, int n_r, int K, int n_s, int d_ff, int act, int ffn,
+                       int score, const void* u, const void* e, const float* b,
+                       const void* const* wr1, const void* const* wr3, const void* const* wr2,
+                       const void* const* ws1, const void* const* ws3, const void* const* ws2,
+                       const void* dout, double* du, double* de, double* const* dwr1,
+                       double* const* dwr3, double* const* dwr2, double* const* dws1,
+                       double* const* dws3, double* const* dws2, int32_t* idx_out,
+                       double* gate_out, double* dgate_out, double* dz_out);
+
 /* ---- combine of precomputed expert outputs ([V3] method section 2, equation for h'_t)
  * u [n, d] and y [rows, d] in act dtype; ysh [n, d] fp32 (sum over shared experts, may be
  * NULL); pair_row [n, K]; gate [n, K] fp32. out [n, d] double. */

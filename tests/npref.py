@@ -96,3 +96,17 @@ def masked_loop_layer(u, sel, gates, routed, shared, hround):
     for (w1, w3, w2) in shared:
         shared_out += swiglu_ffn(u, w1, w3, w2, hround)
     return u + shared_out + routed_out
+
+
+def swiglu_backward(x, w1, w3, w2, dy, hround):
+    """Matrix form of one expert's backward for rows x [n,d] with output gradient dy
+    [n,d] (float64): returns dx [n,d], dW1, dW3 [I,d], dW2 [d,I]; h, da, dv rounded by
+    `hround` (the operand type)."""
+    a = x @ w1.T
+    v = x @ w3.T
+    sg = sigmoid(a)
+    h = hround(a * sg * v)
+    dh = dy @ w2
+    da = hround(dh * v * sg * (1.0 + a * (1.0 - sg)))
+    dv = hround(dh * a * sg)
+    return da @ w1 + dv @ w3, da.T @ x, dv.T @ x, dy.T @ h
