@@ -192,10 +192,76 @@ enum { MOE_W1 = 0, MOE_W3 = 1, MOE_W2 = 2 };
 moe_status moe_pack_weights(const moe_shape* shape, int32_t matrix, int64_t n_experts, const void* src,
                             void* dst, void* stream);
 
-/* workspace sizing: call = MOE_CALL_ROUTE, MOE_CALL_DISPATCH or MOE_CALL_GROUPED_FFN;
- * 0 for others and for invalid shapes */
+/* ===========================================================================
+ * Backward (gradients of L = sum dout . h' with the routing held fixed; the selection is
+ * piecewise constant, and the bias only selects, so it has no gradient). Gradients are
+ * bf16 ("gradients in BF16", quantisation section of deepseekmodel.com): GEMM operands
+ * bf16, fp32 accumulation, each gradient rounded once. Needs act = ffn = MOE_BF16, the
+ * ROWS weight layout, d % 128 == 0 and d_ff % 128 == 0 (else MOE_ERR_UNSUPPORTED).
+ * The order of the three calls: moe_combine_backward, moe_grouped_ffn_backward,
+ * moe_route_backward. */
+
+/* Weight gradients of one expert kind, bf16, in the weight layouts:
+ *   dw1, dw3 [E, d_ff, d]; dw2 [E, d, d_ff] */
+typedef struct {
+  void *dw1, *dw3, *dw2;
+} moe_expert_grads;
+
+/* moe_combine_backward: adjoint of moe_combine.
+ *   dout      [T, d]   bf16: gradient of the layer output
+ *   y_routed  [T*K, d] bf16 from moe_grouped_ffn; pair_row, topk_gate [T, K] from the step
+ *   dy_routed [T*K, d] bf16 out: g_{k,t} dout_t at sorted row pair_row[t, k]
+ *   dgate     [T, K]   fp32 out: dout_t . y_routed[pair_row[t, k]] (fp32 sum) */
+moe_status moe_combine_backward(const moe_shape* shape, const void* dout, const void* y_routed,
+                                const int32_t* pair_row, const float* topk_gate, void* dy_routed,
+                                float* dgate, void* stream);
+
+/* moe_grouped_ffn_backward: backward of every expert's SwiGLU FFN on its rows. With
+ * a = X W1^T, v = X W3^T, h = SiLU(a) v, y = h W2^T per expert:
+ *   dh = dY W2, da = dh v SiLU'(a), dv = dh SiLU(a) (h, da, dv rounded to bf16),
+ *   dX = da W1 + dv W3, dW1 = da^T X, dW3 = dv^T X, dW2 = dY^T h.
+ *   u, expert_offset, sorted_token, routed, shared: as in moe_grouped_ffn
+ *   dout      [T, d] bf16: the shared experts' dY
+ *   dy_routed [T*K, d] bf16 from moe_combine_backward: the routed rows' dY
+ *   dx_routed [T*K, d] bf16 out, sorted rows
+ *   dx_shared [T, d] fp32 out: sum over the shared experts (NULL when N_s == 0)
+ *   d_routed  weight gradients of the N_r routed experts (out; zeros for experts with no
+ *             rows); d_shared: of the N_s shared experts (NULL when N_s == 0)
+ *   ws        moe_workspace_bytes(shape, MOE_CALL_GROUPED_FFN_BACKWARD) bytes (h, da, dv) */
+moe_status moe_grouped_ffn_backward(const moe_shape* shape, const void* u, const void* dout,
+                                    const int32_t* expert_offset, const int32_t* sorted_token,
+                                    const moe_expert_set* routed, const moe_expert_set* shared,
+                                    const void* dy_routed, void* dx_routed, float* dx_shared,
+                                    const moe_expert_grads* d_routed, const moe_expert_grads* d_shared,
+                                    void* ws, size_t ws_bytes, void* stream);
+
+/* moe_route_backward: the router's logit gradients, the input gradient and the centroid
+ * gradient (the explainer's method section 2 for sigmoid gates, the forward listing for
+ * softmax gates; shape->score picks).
+ *   sigmoid: s_k = Sigmoid(z_k) of the picks (z recomputed in fp32), S = sum s_k,
+ *            dz_k = (dg_k - sum_j g_j dg_j) / S * s_k (1 - s_k) with g_j = s_j / S;
+ *   softmax: dz_k = g_k (dg_k - sum_j g_j dg_j) with the forward's gates.
+ *   u, centroids, topk_idx, topk_gate, expert_offset, sorted_token, pair_row: the step's
+ *   dgate [T, K] from moe_combine_backward; dout [T, d] bf16
+ *   dx_routed, dx_shared from moe_grouped_ffn_backward (dx_shared NULL when N_s == 0)
+ *   du   [T, d] bf16 out: dout + dx_shared + sum_k dx_routed[pair_row] + sum_k dz_k e_{i_k},
+ *        added in fp32 in that order (experts ascending) and rounded once
+ *   dcentroids [N_r, d] bf16 out: sum over expert i's sorted rows of dz u_t
+ *   dz   [T, K] fp32 out
+ *   ws   moe_workspace_bytes(shape, MOE_CALL_ROUTE_BACKWARD) bytes */
+moe_status moe_route_backward(const moe_shape* shape, const void* u, const void* centroids,
+                              const int32_t* topk_idx, const float* topk_gate, const float* dgate,
+                              const int32_t* expert_offset, const int32_t* sorted_token,
+                              const int32_t* pair_row, const void* dout, const void* dx_routed,
+                              const float* dx_shared, void* du, void* dcentroids, float* dz, void* ws,
+                              size_t ws_bytes, void* stream);
+
+/* workspace sizing: call = MOE_CALL_ROUTE, MOE_CALL_DISPATCH, MOE_CALL_GROUPED_FFN,
+ * MOE_CALL_GROUPED_FFN_BACKWARD or MOE_CALL_ROUTE_BACKWARD; 0 for others and for invalid
+ * shapes */
 enum { MOE_CALL_ROUTE = 0, MOE_CALL_DISPATCH = 1, MOE_CALL_GROUPED_FFN = 2,
-       MOE_CALL_COMBINE = 3, MOE_CALL_BIAS_UPDATE = 4 };
+       MOE_CALL_COMBINE = 3, MOE_CALL_BIAS_UPDATE = 4, MOE_CALL_GROUPED_FFN_BACKWARD = 5,
+       MOE_CALL_ROUTE_BACKWARD = 6 };
 size_t moe_workspace_bytes(const moe_shape* shape, int32_t call);
 
 const char* moe_status_string(moe_status status);

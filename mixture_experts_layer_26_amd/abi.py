@@ -16,6 +16,7 @@ LIB_PATH = os.path.join(HERE, "libmoe.so")
 MOE_OK, MOE_ERR_INVALID_ARG, MOE_ERR_UNSUPPORTED, MOE_ERR_WORKSPACE, MOE_ERR_HIP = range(5)
 MOE_F32, MOE_BF16, MOE_FP8_E4M3 = 0, 1, 2
 MOE_CALL_ROUTE, MOE_CALL_DISPATCH, MOE_CALL_GROUPED_FFN, MOE_CALL_COMBINE, MOE_CALL_BIAS_UPDATE = range(5)
+MOE_CALL_GROUPED_FFN_BACKWARD, MOE_CALL_ROUTE_BACKWARD = 5, 6
 MOE_LAYOUT_ROWS, MOE_LAYOUT_TILED = 0, 1
 MOE_W1, MOE_W3, MOE_W2 = 0, 1, 2
 MOE_SCORE_SIGMOID, MOE_SCORE_SOFTMAX = 0, 1
@@ -42,6 +43,10 @@ class moe_expert_set(ctypes.Structure):
                 ("layout", ctypes.c_int32)]
 
 
+class moe_expert_grads(ctypes.Structure):
+    _fields_ = [("dw1", ctypes.c_void_p), ("dw3", ctypes.c_void_p), ("dw2", ctypes.c_void_p)]
+
+
 _lib = None
 
 
@@ -57,6 +62,7 @@ def load():
     vp, sz, i32, i64, f32 = ctypes.c_void_p, ctypes.c_size_t, ctypes.c_int32, ctypes.c_int64, ctypes.c_float
     sp = ctypes.POINTER(moe_shape)
     ep = ctypes.POINTER(moe_expert_set)
+    gp = ctypes.POINTER(moe_expert_grads)
     sig = {
         "moe_route": [sp, vp, vp, vp, vp, vp, vp, sz, vp],
         "moe_dispatch": [sp, vp, vp, vp, vp, vp, vp, sz, vp],
@@ -65,6 +71,9 @@ def load():
         "moe_bias_update": [sp, vp, f32, vp, vp],
         "moe_quantize_fp8": [vp, i32, i64, i64, i32, i32, vp, vp, vp],
         "moe_pack_weights": [sp, i32, i64, vp, vp, vp],
+        "moe_combine_backward": [sp, vp, vp, vp, vp, vp, vp, vp],
+        "moe_grouped_ffn_backward": [sp, vp, vp, vp, vp, ep, ep, vp, vp, vp, gp, gp, vp, sz, vp],
+        "moe_route_backward": [sp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp],
     }
     for name, args in sig.items():
         fn = getattr(lib, name)
@@ -143,6 +152,33 @@ def moe_combine(shape, u, y_routed, y_shared, pair_row, topk_gate, out, stream=N
 def moe_bias_update(shape, expert_count, gamma, bias, stream=None):
     _check("moe_bias_update", load().moe_bias_update(ctypes.byref(shape), _ptr(expert_count), gamma,
                                                      _ptr(bias), _stream(stream)))
+
+
+def make_expert_grads(dw1, dw3, dw2) -> moe_expert_grads:
+    return moe_expert_grads(_ptr(dw1), _ptr(dw3), _ptr(dw2))
+
+
+def moe_combine_backward(shape, dout, y_routed, pair_row, topk_gate, dy_routed, dgate, stream=None):
+    _check("moe_combine_backward", load().moe_combine_backward(
+        ctypes.byref(shape), _ptr(dout), _ptr(y_routed), _ptr(pair_row), _ptr(topk_gate), _ptr(dy_routed),
+        _ptr(dgate), _stream(stream)))
+
+
+def moe_grouped_ffn_backward(shape, u, dout, expert_offset, sorted_token, routed, shared, dy_routed, dx_routed,
+                             dx_shared, d_routed, d_shared, ws, ws_bytes: int, stream=None):
+    _check("moe_grouped_ffn_backward", load().moe_grouped_ffn_backward(
+        ctypes.byref(shape), _ptr(u), _ptr(dout), _ptr(expert_offset), _ptr(sorted_token), ctypes.byref(routed),
+        ctypes.byref(shared) if shared is not None else None, _ptr(dy_routed), _ptr(dx_routed), _ptr(dx_shared),
+        ctypes.byref(d_routed), ctypes.byref(d_shared) if d_shared is not None else None, _ptr(ws), ws_bytes,
+        _stream(stream)))
+
+
+def moe_route_backward(shape, u, centroids, topk_idx, topk_gate, dgate, expert_offset, sorted_token, pair_row,
+                       dout, dx_routed, dx_shared, du, dcentroids, dz, ws, ws_bytes: int, stream=None):
+    _check("moe_route_backward", load().moe_route_backward(
+        ctypes.byref(shape), _ptr(u), _ptr(centroids), _ptr(topk_idx), _ptr(topk_gate), _ptr(dgate),
+        _ptr(expert_offset), _ptr(sorted_token), _ptr(pair_row), _ptr(dout), _ptr(dx_routed), _ptr(dx_shared),
+        _ptr(du), _ptr(dcentroids), _ptr(dz), _ptr(ws), ws_bytes, _stream(stream)))
 
 
 def moe_pack_weights(shape, matrix: int, n_experts: int, src, dst, stream=None):

@@ -121,6 +121,36 @@ FfnWorkspace ffn_workspace(const moe_shape* s) {
   return w;
 }
 
+// Backward: shapes it runs (bf16, row-major weights, 128-multiples) and its workspaces.
+bool backward_shape(const moe_shape* s) {
+  return s->act == MOE_BF16 && s->ffn == MOE_BF16 && s->d % 128 == 0 && s->d_ff % 128 == 0 && s->top_k <= 16;
+}
+
+struct BwdWorkspace {
+  size_t h_r, da_r, dv_r, h_s, da_s, dv_s, total;
+};
+
+BwdWorkspace bwd_workspace(const moe_shape* s) {
+  BwdWorkspace w{};
+  const size_t pr = static_cast<size_t>(s->T) * s->top_k * s->d_ff * 2;
+  const size_t ps = static_cast<size_t>(s->T) * s->n_shared * s->d_ff * 2;
+  size_t off = 0;
+  w.h_r = off;
+  off = align_up(off + pr);
+  w.da_r = off;
+  off = align_up(off + pr);
+  w.dv_r = off;
+  off = align_up(off + pr);
+  w.h_s = off;
+  off = align_up(off + ps);
+  w.da_s = off;
+  off = align_up(off + ps);
+  w.dv_s = off;
+  off = align_up(off + ps);
+  w.total = off;
+  return w;
+}
+
 
 // The FP8 expert FFN: u quantised per 1x128 tile into the workspace, then the two
 // FP8 grouped GEMMs (phase 1 also quantises H per 1x128).
@@ -234,6 +264,9 @@ size_t moe_workspace_bytes(const moe_shape* s, int32_t call) {
   if (call == MOE_CALL_DISPATCH)
     return align_up(static_cast<size_t>(moe::dispatch_blocks(s->T)) * s->n_routed * sizeof(int32_t));
   if (call == MOE_CALL_GROUPED_FFN) return ffn_workspace(s).total;
+  if (call == MOE_CALL_GROUPED_FFN_BACKWARD) return backward_shape(s) ? bwd_workspace(s).total : 0;
+  if (call == MOE_CALL_ROUTE_BACKWARD)
+    return backward_shape(s) ? align_up(static_cast<size_t>(s->T) * s->top_k * sizeof(float)) : 0;
   if (call == MOE_CALL_ROUTE)
     return s->act == MOE_BF16 ? align_up(moe::route_workspace_bytes(s->T, s->d, s->n_routed)) : 0;
   return 0;
@@ -417,6 +450,92 @@ moe_status moe_quantize_fp8(const void* x, int32_t xt, int64_t rows, int64_t col
   if (rows * cols >= (1LL << 40)) return MOE_ERR_INVALID_ARG;
   return from_hip(moe::launch_quantize_fp8(x, xt, rows, cols, tile_r, tile_c, q, scale,
                                            as_stream(stream)));
+}
+
+moe_status moe_combine_backward(const moe_shape* s, const void* dout, const void* y_routed,
+                                const int32_t* pair_row, const float* topk_gate, void* dy_routed, float* dgate,
+                                void* stream) {
+  if (!valid_shape(s) || !dout || !y_routed || !pair_row || !topk_gate || !dy_routed || !dgate)
+    return MOE_ERR_INVALID_ARG;
+  if (!backward_shape(s)) return MOE_ERR_UNSUPPORTED;
+  return from_hip(moe::launch_combine_backward(dout, y_routed, pair_row, topk_gate, dy_routed, dgate, s->T, s->d,
+                                               s->top_k, as_stream(stream)));
+}
+
+moe_status moe_grouped_ffn_backward(const moe_shape* s, const void* u, const void* dout,
+                                    const int32_t* expert_offset, const int32_t* sorted_token,
+                                    const moe_expert_set* routed, const moe_expert_set* shared,
+                                    const void* dy_routed, void* dx_routed, float* dx_shared,
+                                    const moe_expert_grads* d_routed, const moe_expert_grads* d_shared, void* ws,
+                                    size_t ws_bytes, void* stream) {
+  if (!valid_shape(s) || !u || !dout || !expert_offset || !sorted_token || !routed || !dy_routed || !dx_routed ||
+      !d_routed)
+    return MOE_ERR_INVALID_ARG;
+  if (!routed->w1 || !routed->w3 || !routed->w2 || !d_routed->dw1 || !d_routed->dw3 || !d_routed->dw2)
+    return MOE_ERR_INVALID_ARG;
+  if (s->n_shared > 0) {
+    if (!shared || !shared->w1 || !shared->w3 || !shared->w2 || !dx_shared || !d_shared || !d_shared->dw1 ||
+        !d_shared->dw3 || !d_shared->dw2)
+      return MOE_ERR_INVALID_ARG;
+  }
+  if (!backward_shape(s)) return MOE_ERR_UNSUPPORTED;
+  if (routed->layout != MOE_LAYOUT_ROWS || (s->n_shared > 0 && shared->layout != MOE_LAYOUT_ROWS))
+    return MOE_ERR_UNSUPPORTED;
+  const BwdWorkspace w = bwd_workspace(s);
+  if (!ws || ws_bytes < w.total) return MOE_ERR_WORKSPACE;
+  unsigned char* wsb = static_cast<unsigned char*>(ws);
+  moe::BwdArgs a{};
+  a.u = static_cast<const uint16_t*>(u);
+  a.dout = static_cast<const uint16_t*>(dout);
+  a.dy_routed = static_cast<const uint16_t*>(dy_routed);
+  a.offset = expert_offset;
+  a.sorted_token = sorted_token;
+  a.w1r = static_cast<const uint16_t*>(routed->w1);
+  a.w3r = static_cast<const uint16_t*>(routed->w3);
+  a.w2r = static_cast<const uint16_t*>(routed->w2);
+  const bool has_s = s->n_shared > 0;
+  a.w1s = has_s ? static_cast<const uint16_t*>(shared->w1) : nullptr;
+  a.w3s = has_s ? static_cast<const uint16_t*>(shared->w3) : nullptr;
+  a.w2s = has_s ? static_cast<const uint16_t*>(shared->w2) : nullptr;
+  a.h_r = reinterpret_cast<uint16_t*>(wsb + w.h_r);
+  a.da_r = reinterpret_cast<uint16_t*>(wsb + w.da_r);
+  a.dv_r = reinterpret_cast<uint16_t*>(wsb + w.dv_r);
+  a.h_s = reinterpret_cast<uint16_t*>(wsb + w.h_s);
+  a.da_s = reinterpret_cast<uint16_t*>(wsb + w.da_s);
+  a.dv_s = reinterpret_cast<uint16_t*>(wsb + w.dv_s);
+  a.dx_r = static_cast<uint16_t*>(dx_routed);
+  a.dx_s = has_s ? dx_shared : nullptr;
+  a.dw1r = static_cast<uint16_t*>(d_routed->dw1);
+  a.dw3r = static_cast<uint16_t*>(d_routed->dw3);
+  a.dw2r = static_cast<uint16_t*>(d_routed->dw2);
+  a.dw1s = has_s ? static_cast<uint16_t*>(d_shared->dw1) : nullptr;
+  a.dw3s = has_s ? static_cast<uint16_t*>(d_shared->dw3) : nullptr;
+  a.dw2s = has_s ? static_cast<uint16_t*>(d_shared->dw2) : nullptr;
+  a.T = s->T;
+  a.K = s->top_k;
+  a.d = s->d;
+  a.F = s->d_ff;
+  a.n_r = s->n_routed;
+  a.n_s = s->n_shared;
+  return from_hip(moe::launch_ffn_backward(a, as_stream(stream)));
+}
+
+moe_status moe_route_backward(const moe_shape* s, const void* u, const void* centroids, const int32_t* topk_idx,
+                              const float* topk_gate, const float* dgate, const int32_t* expert_offset,
+                              const int32_t* sorted_token, const int32_t* pair_row, const void* dout,
+                              const void* dx_routed, const float* dx_shared, void* du, void* dcentroids, float* dz,
+                              void* ws, size_t ws_bytes, void* stream) {
+  if (!valid_shape(s) || !u || !centroids || !topk_idx || !topk_gate || !dgate || !expert_offset ||
+      !sorted_token || !pair_row || !dout || !dx_routed || !du || !dcentroids || !dz)
+    return MOE_ERR_INVALID_ARG;
+  if (s->n_shared > 0 && !dx_shared) return MOE_ERR_INVALID_ARG;
+  if (!backward_shape(s)) return MOE_ERR_UNSUPPORTED;
+  if (!ws || ws_bytes < moe_workspace_bytes(s, MOE_CALL_ROUTE_BACKWARD)) return MOE_ERR_WORKSPACE;
+  return from_hip(moe::launch_route_backward(s->score == MOE_SCORE_SOFTMAX ? 1 : 0, u, centroids, topk_idx,
+                                             topk_gate, dgate, expert_offset, sorted_token, pair_row, dout,
+                                             dx_routed, s->n_shared > 0 ? dx_shared : nullptr, du, dcentroids, dz,
+                                             static_cast<float*>(ws), s->T, s->d, s->n_routed, s->top_k,
+                                             as_stream(stream)));
 }
 
 }  // extern "C"

@@ -1,0 +1,407 @@
+// Backward of the grouped SwiGLU experts (bf16 operands, fp32 accumulation, bf16
+// gradients: the quantisation section of "DeepSeek モデルアーキテクチャ徹底解説" computes
+// the backward's gradients in BF16).
+//
+// For one expert with rows X (the tokens routed to it, in sorted-row order), output
+// gradient dY, a = X W1^T, v = X W3^T, h = SiLU(a) v and y = h W2^T:
+//   dh = dY W2,  da = dh v SiLU'(a),  dv = dh SiLU(a),  dX = da W1 + dv W3,
+//   dW1 = da^T X,  dW3 = dv^T X,  dW2 = dY^T h.
+// Four launches, each a grid of 128 x 128 output tiles on 4 waves (64 x 64 each, four
+// v_mfma_f32_32x32x16_bf16 tiles per product), K in steps of 32 through two LDS stages
+// filled from registers:
+//   kGateUp: rows x d_ff tiles, K = d: a, v and dh in three accumulators; the epilogue
+//            forms h (as the forward does), da and dv and stores them in bf16.
+//   kDx:     rows x d tiles, K = d_ff (the shared experts' K ranges one after another):
+//            dX = da W1 + dv W3 in one accumulator.
+//   kDw13:   d_ff x d tiles per expert, K = the expert's rows: dW1 and dW3.
+//   kDw2:    d x d_ff tiles per expert, K = the expert's rows: dW2.
+// Operands whose K is contiguous in memory (X, dY, da, dv in kGateUp/kDx, the rows of
+// W1/W3 in kGateUp) are staged as [rows][32 k] and read with ds_read_b128. Operands
+// whose K runs across rows (W2 in kGateUp, W1/W3 in kDx, everything in the weight
+// gradients) are staged as they lie, [32 k][128 columns], and read with
+// ds_read_b64_tr_b16, which hands each lane four consecutive k of one column: within
+// 16 lanes, lane i receives column i of the 4 x 16 block whose rows the lanes'
+// addresses name (lane j points at row j / 4, columns 4 (j % 4) .. + 3). Two such reads
+// give the 8 consecutive k of an MFMA operand fragment.
+#include "device.h"
+#include "launch.h"
+
+namespace moe {
+
+namespace {
+
+constexpr int kBT = 128;                 // tile rows and columns
+constexpr int kBK = 32;                  // K per step
+constexpr int kThr = 256;                // 4 waves
+constexpr int kTileBytes = kBT * kBK * 2;  // one staged operand: 8 KB
+
+enum { kGateUp = 0, kDx = 1, kDw13 = 2, kDw2 = 3 };
+
+// operands per mode: A operands (M side), B operands (N side); K-major flags
+template <int MODE> struct Cfg;
+template <> struct Cfg<kGateUp> {  // A: X, dY (K-contiguous); B: W1, W3 (K-contig.), W2 (K-major)
+  static constexpr int NA = 2, NB = 3, NACC = 3;
+  static constexpr bool a_km = false;
+  static constexpr bool b_km(int j) { return j == 2; }
+};
+template <> struct Cfg<kDx> {  // A: da, dv (K-contiguous); B: W1, W3 (K-major)
+  static constexpr int NA = 2, NB = 2, NACC = 1;
+  static constexpr bool a_km = false;
+  static constexpr bool b_km(int) { return true; }
+};
+template <> struct Cfg<kDw13> {  // A: da, dv; B: X (all K-major)
+  static constexpr int NA = 2, NB = 1, NACC = 2;
+  static constexpr bool a_km = true;
+  static constexpr bool b_km(int) { return true; }
+};
+template <> struct Cfg<kDw2> {  // A: dY; B: h (K-major)
+  static constexpr int NA = 1, NB = 1, NACC = 1;
+  static constexpr bool a_km = true;
+  static constexpr bool b_km(int) { return true; }
+};
+
+// LDS offsets. K-contiguous tile [128 rows][32 k]: 64-byte rows, 16-byte chunk c of row r
+// at chunk c ^ ((r >> 2) & 3), so the 32 rows of a fragment read cover all banks.
+__device__ __forceinline__ int kc_off(int r, int c) { return r * 64 + ((c ^ ((r >> 2) & 3)) << 4); }
+// K-major tile [32 k][128 columns]: 256-byte rows, 64-byte unit q of row k at q ^ (k & 3),
+// so the 4 rows of one transposed read fall in different banks.
+__device__ __forceinline__ int km_off(int k, int byte) { return k * 256 + ((((byte >> 6) ^ k) & 3) << 6) + (byte & 63); }
+
+typedef short v4s __attribute__((ext_vector_type(4)));
+
+// MFMA fragment (8 consecutive k of row/column `lane % 32` of a 32-block) of sub-step s.
+__device__ __forceinline__ bf16x8 frag_kc(const unsigned char* t, int r0, int s, int lane) {
+  return *reinterpret_cast<const bf16x8*>(t + kc_off(r0 + lane % 32, 2 * s + lane / 32));
+}
+__device__ __forceinline__ bf16x8 frag_km(const unsigned char* t, int c0, int s, int lane) {
+  const int g = lane / 16, j = lane % 16;
+  const int col = c0 + 16 * (g % 2) + 4 * (j % 4);
+  const int k = 16 * s + 8 * (g / 2) + j / 4;
+  typedef __attribute__((address_space(3))) v4s lds_v4s;  // the tile lives in LDS
+  unsigned char* p = const_cast<unsigned char*>(t);
+  const v4s lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4s*)(p + km_off(k, 2 * col)));
+  const v4s hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4s*)(p + km_off(k + 4, 2 * col)));
+  typedef short v8s __attribute__((ext_vector_type(8)));
+  const v8s both = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+  return __builtin_bit_cast(bf16x8, both);
+}
+
+__device__ __forceinline__ uint4 ld_or_zero(const uint16_t* p) {
+  return p ? ld16(p) : make_uint4(0, 0, 0, 0);
+}
+
+// Where a tile's rows, weights and outputs are.
+struct Ctx {
+  int g;          // group: routed expert (< n_r) or shared expert / shared group
+  bool shared;
+  int64_t row0;   // first row of the group in the routed row space (routed) or 0 (shared)
+  int rows;       // rows of the group (kDw*: the K extent) or valid rows of the tile (kGateUp/kDx)
+  int64_t m0;     // tile's first row within the group (kGateUp/kDx), else 0
+  int c0;         // tile's first output column (kGateUp: d_ff; kDx: d)
+  int mo, no;     // kDw*: tile's first output row / column
+  int nk;         // K-steps
+};
+
+// Row tiles of kGateUp / kDx: groups are the routed experts, then the shared groups
+// (kGateUp: each shared expert; kDx: one group for all of them). The offsets are copied
+// to LDS (soff, n_r + 1 entries) and one thread walks the groups. Returns false past
+// the last tile.
+__device__ bool decode_row_tile(const BwdArgs& a, int mode, int id, Ctx& c, int* sh, int* soff) {
+  const int nsg = a.n_s == 0 ? 0 : (mode == kGateUp ? a.n_s : 1);
+  const int ntn = (mode == kGateUp ? a.F : a.d) / kBT;
+  for (int i = threadIdx.x; i <= a.n_r; i += kThr) soff[i] = a.offset[i];
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    int base = 0, found = -1, rb = 0;
+    for (int g = 0; g < a.n_r + nsg && found < 0; ++g) {
+      const int r = g < a.n_r ? soff[g + 1] - soff[g] : static_cast<int>(a.T);
+      const int n = ((r + kBT - 1) / kBT) * ntn;
+      if (id < base + n) {
+        found = g;
+        rb = id - base;
+      }
+      base += n;
+    }
+    sh[0] = found;
+    sh[1] = rb;
+  }
+  __syncthreads();
+  const int g = sh[0], rb = sh[1];
+  if (g < 0) return false;
+  c.g = g;
+  c.shared = g >= a.n_r;
+  const int r = c.shared ? static_cast<int>(a.T) : soff[g + 1] - soff[g];
+  c.row0 = c.shared ? 0 : soff[g];
+  c.m0 = static_cast<int64_t>(rb / ntn) * kBT;
+  c.c0 = (rb % ntn) * kBT;
+  c.rows = r - static_cast<int>(c.m0) < kBT ? r - static_cast<int>(c.m0) : kBT;
+  return true;
+}
+
+// Global address of staged chunk i (0, 1) of operand op at K-step kt; nullptr = zeros.
+// K-contiguous operands: chunk q = tid + 256 i is row q / 4, 8 elements at k 8 (q % 4).
+// K-major operands: chunk q is K-row q / 16, 8 elements at column 8 (q % 16).
+template <int MODE>
+__device__ __forceinline__ const uint16_t* src(const BwdArgs& a, const Ctx& c, bool is_a, int op, int i, int kt) {
+  const int q = threadIdx.x + kThr * i;
+  const int64_t F = a.F, d = a.d;
+  if constexpr (MODE == kGateUp) {
+    if (is_a) {  // X or dY, row r of the tile, k = 32 kt + 8 (q % 4)
+      const int r = q / 4;
+      if (r >= c.rows) return nullptr;
+      const int64_t k = static_cast<int64_t>(kBK) * kt + 8 * (q % 4);
+      const int64_t row = c.m0 + r;
+      if (op == 0) {
+        const int64_t tok = c.shared ? row : a.sorted_token[c.row0 + row];
+        return a.u + tok * d + k;
+      }
+      return c.shared ? a.dout + row * d + k : a.dy_routed + (c.row0 + row) * d + k;
+    }
+    const int e = c.shared ? c.g - a.n_r : c.g;
+    if (op < 2) {  // W1 / W3 row c0 + r, k contiguous
+      const uint16_t* w = c.shared ? (op == 0 ? a.w1s : a.w3s) : (op == 0 ? a.w1r : a.w3r);
+      const int r = q / 4;
+      return w + static_cast<int64_t>(e) * F * d + (c.c0 + r) * d + static_cast<int64_t>(kBK) * kt + 8 * (q % 4);
+    }
+    // W2 [d][d_ff]: K-row 32 kt + q / 16, columns c0 + 8 (q % 16)
+    const uint16_t* w = c.shared ? a.w2s : a.w2r;
+    const int64_t k = static_cast<int64_t>(kBK) * kt + q / 16;
+    return w + static_cast<int64_t>(e) * d * F + k * F + c.c0 + 8 * (q % 16);
+  } else if constexpr (MODE == kDx) {
+    const int64_t kk = static_cast<int64_t>(kBK) * kt;  // K position (shared: across the experts)
+    if (is_a) {  // da / dv row r
+      const int r = q / 4;
+      if (r >= c.rows) return nullptr;
+      const int64_t row = c.m0 + r;
+      const int64_t k = kk + 8 * (q % 4);
+      if (c.shared) return (op == 0 ? a.da_s : a.dv_s) + row * (a.n_s * F) + k;
+      return (op == 0 ? a.da_r : a.dv_r) + (c.row0 + row) * F + k;
+    }
+    // W1 / W3 [d_ff][d]: K-row j, columns c0 + 8 (q % 16)
+    const int64_t seg = c.shared ? kk / F : c.g;
+    const int64_t j = kk - (c.shared ? seg * F : 0) + q / 16;
+    const uint16_t* w = c.shared ? (op == 0 ? a.w1s : a.w3s) : (op == 0 ? a.w1r : a.w3r);
+    return w + seg * F * d + j * d + c.c0 + 8 * (q % 16);
+  } else {
+    // weight gradients: K-row = row 32 kt + q / 16 of the group, columns 8 (q % 16)
+    const int64_t row = static_cast<int64_t>(kBK) * kt + q / 16;
+    if (row >= c.rows) return nullptr;
+    const int col = 8 * (q % 16);
+    const int s = c.shared ? c.g - a.n_r : 0;
+    if constexpr (MODE == kDw13) {
+      if (is_a) {  // da / dv columns mo.. (d_ff)
+        if (c.shared) return (op == 0 ? a.da_s : a.dv_s) + row * (a.n_s * F) + s * F + c.mo + col;
+        return (op == 0 ? a.da_r : a.dv_r) + (c.row0 + row) * F + c.mo + col;
+      }
+      const int64_t tok = c.shared ? row : a.sorted_token[c.row0 + row];  // X columns no.. (d)
+      return a.u + tok * d + c.no + col;
+    } else {
+      if (is_a) {  // dY columns mo.. (d)
+        if (c.shared) return a.dout + row * d + c.mo + col;
+        return a.dy_routed + (c.row0 + row) * d + c.mo + col;
+      }
+      if (c.shared) return a.h_s + row * (a.n_s * F) + s * F + c.no + col;  // h columns no.. (d_ff)
+      return a.h_r + (c.row0 + row) * F + c.no + col;
+    }
+  }
+}
+
+template <int MODE>
+__device__ __forceinline__ void stage_load(const BwdArgs& a, const Ctx& c, int kt, uint4 (&st)[Cfg<MODE>::NA + Cfg<MODE>::NB][2]) {
+  constexpr int NA = Cfg<MODE>::NA, NB = Cfg<MODE>::NB;
+#pragma unroll
+  for (int op = 0; op < NA + NB; ++op)
+#pragma unroll
+    for (int i = 0; i < 2; ++i) st[op][i] = ld_or_zero(src<MODE>(a, c, op < NA, op < NA ? op : op - NA, i, kt));
+}
+
+template <int MODE>
+__device__ __forceinline__ void stage_store(unsigned char* base, const uint4 (&st)[Cfg<MODE>::NA + Cfg<MODE>::NB][2]) {
+  constexpr int NA = Cfg<MODE>::NA, NB = Cfg<MODE>::NB;
+#pragma unroll
+  for (int op = 0; op < NA + NB; ++op) {
+    const bool km = op < NA ? Cfg<MODE>::a_km : Cfg<MODE>::b_km(op - NA);
+    unsigned char* t = base + op * kTileBytes;
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      const int q = threadIdx.x + kThr * i;
+      const int off = km ? km_off(q / 16, 16 * (q % 16)) : kc_off(q / 4, q % 4);
+      *reinterpret_cast<uint4*>(t + off) = st[op][i];
+    }
+  }
+}
+
+template <int MODE>
+__device__ __forceinline__ void compute(const unsigned char* base, f32x16 (&acc)[Cfg<MODE>::NACC][2][2], int wm,
+                                        int wn, int lane) {
+  constexpr int NA = Cfg<MODE>::NA, NB = Cfg<MODE>::NB;
+#pragma unroll
+  for (int s = 0; s < 2; ++s) {
+    bf16x8 fa[NA][2], fb[NB][2];
+#pragma unroll
+    for (int op = 0; op < NA; ++op)
+#pragma unroll
+      for (int mb = 0; mb < 2; ++mb) {
+        const unsigned char* t = base + op * kTileBytes;
+        fa[op][mb] = Cfg<MODE>::a_km ? frag_km(t, 64 * wm + 32 * mb, s, lane) : frag_kc(t, 64 * wm + 32 * mb, s, lane);
+      }
+#pragma unroll
+    for (int op = 0; op < NB; ++op)
+#pragma unroll
+      for (int nb = 0; nb < 2; ++nb) {
+        const unsigned char* t = base + (NA + op) * kTileBytes;
+        fb[op][nb] = Cfg<MODE>::b_km(op) ? frag_km(t, 64 * wn + 32 * nb, s, lane) : frag_kc(t, 64 * wn + 32 * nb, s, lane);
+      }
+#pragma unroll
+    for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+      for (int nb = 0; nb < 2; ++nb) {
+        if constexpr (MODE == kGateUp) {
+          acc[0][mb][nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[0][mb], fb[0][nb], acc[0][mb][nb], 0, 0, 0);
+          acc[1][mb][nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[0][mb], fb[1][nb], acc[1][mb][nb], 0, 0, 0);
+          acc[2][mb][nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[1][mb], fb[2][nb], acc[2][mb][nb], 0, 0, 0);
+        } else if constexpr (MODE == kDx) {
+          acc[0][mb][nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[0][mb], fb[0][nb], acc[0][mb][nb], 0, 0, 0);
+          acc[0][mb][nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[1][mb], fb[1][nb], acc[0][mb][nb], 0, 0, 0);
+        } else if constexpr (MODE == kDw13) {
+          acc[0][mb][nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[0][mb], fb[0][nb], acc[0][mb][nb], 0, 0, 0);
+          acc[1][mb][nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[1][mb], fb[0][nb], acc[1][mb][nb], 0, 0, 0);
+        } else {
+          acc[0][mb][nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[0][mb], fb[0][nb], acc[0][mb][nb], 0, 0, 0);
+        }
+      }
+  }
+}
+
+template <int MODE>
+__global__ __launch_bounds__(kThr) void ffn_bwd_kernel(BwdArgs a) {
+  constexpr int NA = Cfg<MODE>::NA, NB = Cfg<MODE>::NB, NACC = Cfg<MODE>::NACC;
+  constexpr int kStage = (NA + NB) * kTileBytes;
+  __shared__ __align__(16) unsigned char lds[2 * kStage];
+  __shared__ int sh[2];
+  __shared__ int soff[257];
+  const int lane = threadIdx.x % kWave, w = threadIdx.x / kWave;
+  const int wm = w / 2, wn = w % 2;
+
+  Ctx c{};
+  if constexpr (MODE == kGateUp || MODE == kDx) {
+    if (!decode_row_tile(a, MODE, blockIdx.x, c, sh, soff)) return;
+    if constexpr (MODE == kGateUp)
+      c.nk = a.d / kBK;
+    else
+      c.nk = (c.shared ? a.n_s * a.F : a.F) / kBK;
+  } else {
+    // per group: (M / 128) x (N / 128) tiles; M = d_ff, N = d (kDw13) or M = d, N = d_ff
+    const int mt = (MODE == kDw13 ? a.F : a.d) / kBT, nt = (MODE == kDw13 ? a.d : a.F) / kBT;
+    const int id = blockIdx.x;
+    c.g = id / (mt * nt);
+    const int rest = id % (mt * nt);
+    c.mo = (rest / nt) * kBT;
+    c.no = (rest % nt) * kBT;
+    c.shared = c.g >= a.n_r;
+    c.row0 = c.shared ? 0 : a.offset[c.g];
+    c.rows = c.shared ? static_cast<int>(a.T) : a.offset[c.g + 1] - a.offset[c.g];
+    c.nk = (c.rows + kBK - 1) / kBK;
+  }
+
+  f32x16 acc[NACC][2][2];
+#pragma unroll
+  for (int x = 0; x < NACC; ++x)
+#pragma unroll
+    for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+      for (int nb = 0; nb < 2; ++nb)
+#pragma unroll
+        for (int v = 0; v < 16; ++v) acc[x][mb][nb][v] = 0.0f;
+
+  uint4 st[NA + NB][2];
+  if (c.nk > 0) {
+    stage_load<MODE>(a, c, 0, st);
+    stage_store<MODE>(lds, st);
+    __syncthreads();
+  }
+  for (int kt = 0; kt < c.nk; ++kt) {
+    const bool more = kt + 1 < c.nk;
+    if (more) stage_load<MODE>(a, c, kt + 1, st);
+    compute<MODE>(lds + (kt & 1) * kStage, acc, wm, wn, lane);
+    if (more) stage_store<MODE>(lds + ((kt + 1) & 1) * kStage, st);
+    __syncthreads();
+  }
+
+  // epilogue; C layout of the 32x32 MFMA: lane holds column lane % 32 and rows
+  // 8 (v / 4) + 4 (lane / 32) + v % 4 of its block
+  const int col_in = lane % 32;
+#pragma unroll
+  for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+    for (int nb = 0; nb < 2; ++nb)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) {
+        const int r = 64 * wm + 32 * mb + 8 * (v / 4) + 4 * (lane / 32) + (v % 4);
+        const int n = 64 * wn + 32 * nb + col_in;
+        if constexpr (MODE == kGateUp) {
+          if (r >= c.rows) continue;
+          const float av = acc[0][mb][nb][v], vv = acc[1][mb][nb][v], dh = acc[2][mb][nb][v];
+          const float sg = fast_sigmoid(av);
+          const float silu_a = av * sg;
+          const int64_t row = c.m0 + r;
+          const int64_t col = c.c0 + n;
+          uint16_t *hp, *dap, *dvp;
+          if (c.shared) {
+            const int64_t o = row * (a.n_s * static_cast<int64_t>(a.F)) + static_cast<int64_t>(c.g - a.n_r) * a.F + col;
+            hp = a.h_s + o; dap = a.da_s + o; dvp = a.dv_s + o;
+          } else {
+            const int64_t o = (c.row0 + row) * a.F + col;
+            hp = a.h_r + o; dap = a.da_r + o; dvp = a.dv_r + o;
+          }
+          *hp = f32_to_bf16(silu_a * vv);
+          *dap = f32_to_bf16(dh * vv * sg * (1.0f + av * (1.0f - sg)));
+          *dvp = f32_to_bf16(dh * silu_a);
+        } else if constexpr (MODE == kDx) {
+          if (r >= c.rows) continue;
+          const int64_t row = c.m0 + r;
+          const int64_t col = c.c0 + n;
+          if (c.shared)
+            a.dx_s[row * a.d + col] = acc[0][mb][nb][v];
+          else
+            a.dx_r[(c.row0 + row) * a.d + col] = f32_to_bf16(acc[0][mb][nb][v]);
+        } else {
+          const int64_t e = c.shared ? c.g - a.n_r : c.g;
+          const int64_t M = MODE == kDw13 ? a.F : a.d, N = MODE == kDw13 ? a.d : a.F;
+          const int64_t o = e * M * N + static_cast<int64_t>(c.mo + r) * N + c.no + n;
+          if constexpr (MODE == kDw13) {
+            (c.shared ? a.dw1s : a.dw1r)[o] = f32_to_bf16(acc[0][mb][nb][v]);
+            (c.shared ? a.dw3s : a.dw3r)[o] = f32_to_bf16(acc[1][mb][nb][v]);
+          } else {
+            (c.shared ? a.dw2s : a.dw2r)[o] = f32_to_bf16(acc[0][mb][nb][v]);
+          }
+        }
+      }
+}
+
+}  // namespace
+
+int64_t bwd_row_tiles(int mode, int64_t T, int K, int n_r, int n_s, int d, int F) {
+  const int64_t P = T * K;
+  const int64_t ntn = (mode == 0 ? F : d) / kBT;
+  const int64_t nsg = n_s == 0 ? 0 : (mode == 0 ? n_s : 1);
+  return ((P + kBT - 1) / kBT + n_r + nsg * ((T + kBT - 1) / kBT)) * ntn;
+}
+
+hipError_t launch_ffn_backward(const BwdArgs& a, hipStream_t stream) {
+  const unsigned g1 = static_cast<unsigned>(bwd_row_tiles(0, a.T, a.K, a.n_r, a.n_s, a.d, a.F));
+  hipLaunchKernelGGL(ffn_bwd_kernel<kGateUp>, dim3(g1), dim3(kThr), 0, stream, a);
+  hipError_t err = hipGetLastError();
+  if (err != hipSuccess) return err;
+  const unsigned g2 = static_cast<unsigned>(bwd_row_tiles(1, a.T, a.K, a.n_r, a.n_s, a.d, a.F));
+  hipLaunchKernelGGL(ffn_bwd_kernel<kDx>, dim3(g2), dim3(kThr), 0, stream, a);
+  if ((err = hipGetLastError()) != hipSuccess) return err;
+  const unsigned groups = static_cast<unsigned>(a.n_r + a.n_s);
+  const unsigned tiles = static_cast<unsigned>((a.F / kBT) * (a.d / kBT));
+  hipLaunchKernelGGL(ffn_bwd_kernel<kDw13>, dim3(groups * tiles), dim3(kThr), 0, stream, a);
+  if ((err = hipGetLastError()) != hipSuccess) return err;
+  hipLaunchKernelGGL(ffn_bwd_kernel<kDw2>, dim3(groups * tiles), dim3(kThr), 0, stream, a);
+  return hipGetLastError();
+}
+
+}  // namespace moe

@@ -113,4 +113,36 @@ hipError_t launch_pack_weights(const void* src, void* dst, int esz, int64_t E, i
 hipError_t launch_quantize_fp8(const void* x, int xt, int64_t rows, int64_t cols, int tile_r,
                                int tile_c, uint8_t* q, float* scale, hipStream_t stream);
 
+// ---------------------------------------------------------------------------- backward
+// Grouped SwiGLU backward (bf16, row-major weights; d and d_ff multiples of 128).
+struct BwdArgs {
+  const uint16_t* u;             // [T, d]
+  const uint16_t* dout;          // [T, d]: the shared experts' output gradient
+  const uint16_t* dy_routed;     // [P, d]: the routed rows' output gradient (sorted rows)
+  const int32_t* offset;         // expert_offset [n_r + 1]
+  const int32_t* sorted_token;   // [P]
+  const uint16_t *w1r, *w3r, *w2r;  // routed weights [n_r, d_ff, d], [n_r, d, d_ff]
+  const uint16_t *w1s, *w3s, *w2s;  // shared weights (n_s experts)
+  uint16_t *h_r, *da_r, *dv_r;   // workspace [P, d_ff]: h, da, dv of the routed rows
+  uint16_t *h_s, *da_s, *dv_s;   // workspace [T, n_s * d_ff]
+  uint16_t* dx_r;                // out [P, d] bf16
+  float* dx_s;                   // out [T, d] fp32, sum over the shared experts
+  uint16_t *dw1r, *dw3r, *dw2r;  // out, routed weight gradients (bf16, weight layouts)
+  uint16_t *dw1s, *dw3s, *dw2s;  // out, shared
+  int64_t T;
+  int K, d, F, n_r, n_s;
+};
+int64_t bwd_row_tiles(int mode, int64_t T, int K, int n_r, int n_s, int d, int F);
+hipError_t launch_ffn_backward(const BwdArgs& args, hipStream_t stream);
+
+hipError_t launch_combine_backward(const void* dout, const void* y_routed, const int32_t* pair_row,
+                                   const float* gate, void* dy_routed, float* dgate, int64_t T, int d, int K,
+                                   hipStream_t stream);
+// score: 0 sigmoid, 1 softmax. dz_sorted: workspace [P] fp32.
+hipError_t launch_route_backward(int score, const void* u, const void* e, const int32_t* idx, const float* gate,
+                                 const float* dgate, const int32_t* offset, const int32_t* sorted_token,
+                                 const int32_t* pair_row, const void* dout, const void* dx_routed,
+                                 const float* dx_shared, void* du, void* de, float* dz, float* dz_sorted,
+                                 int64_t T, int d, int n_r, int K, hipStream_t stream);
+
 }  // namespace moe

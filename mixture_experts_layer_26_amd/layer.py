@@ -72,6 +72,44 @@ class MoeLayer:
     def bias_update(self, bias, gamma: float, stream=None):
         abi.moe_bias_update(self.shape, self.expert_count, gamma, bias, stream)
 
+    # -- backward ----------------------------------------------------------------
+    def alloc_backward(self):
+        """Buffers of the three backward calls (bf16 layer, row-major weights)."""
+        dev, T, d, K, F = self.device, self.T, self.d, self.top_k, self.d_ff
+        bf = torch.bfloat16
+        self.dy_routed = torch.empty((T * K, d), dtype=bf, device=dev)
+        self.dgate = torch.empty((T, K), dtype=torch.float32, device=dev)
+        self.dx_routed = torch.empty((T * K, d), dtype=bf, device=dev)
+        self.dx_shared = torch.empty((T, d), dtype=torch.float32, device=dev) if self.n_shared > 0 else None
+        self.du = torch.empty((T, d), dtype=bf, device=dev)
+        self.dcentroids = torch.empty((self.n_routed, d), dtype=bf, device=dev)
+        self.dz = torch.empty((T, K), dtype=torch.float32, device=dev)
+        mk = lambda E: (torch.empty((E, F, d), dtype=bf, device=dev), torch.empty((E, F, d), dtype=bf, device=dev),
+                        torch.empty((E, d, F), dtype=bf, device=dev))
+        self.dw_routed = mk(self.n_routed)
+        self.dw_shared = mk(self.n_shared) if self.n_shared > 0 else None
+        self.g_routed = abi.make_expert_grads(*self.dw_routed)
+        self.g_shared = abi.make_expert_grads(*self.dw_shared) if self.dw_shared is not None else None
+        self.ws_bwd_bytes = abi.moe_workspace_bytes(self.shape, abi.MOE_CALL_GROUPED_FFN_BACKWARD)
+        self.ws_rbwd_bytes = abi.moe_workspace_bytes(self.shape, abi.MOE_CALL_ROUTE_BACKWARD)
+        self.ws_bwd = torch.empty(max(1, self.ws_bwd_bytes), dtype=torch.uint8, device=dev)
+        self.ws_rbwd = torch.empty(max(1, self.ws_rbwd_bytes), dtype=torch.uint8, device=dev)
+
+    def backward(self, u, centroids, dout, stream=None):
+        """Gradients of sum(dout * out) for the step just run (routing held fixed): fills du,
+        dcentroids, dz, the weight gradients dw_routed / dw_shared and the intermediates."""
+        if not hasattr(self, "du"):
+            self.alloc_backward()
+        abi.moe_combine_backward(self.shape, dout, self.y_routed, self.pair_row, self.topk_gate, self.dy_routed,
+                                 self.dgate, stream)
+        abi.moe_grouped_ffn_backward(self.shape, u, dout, self.expert_offset, self.sorted_token, self.routed,
+                                     self.shared, self.dy_routed, self.dx_routed, self.dx_shared, self.g_routed,
+                                     self.g_shared, self.ws_bwd, self.ws_bwd_bytes, stream)
+        abi.moe_route_backward(self.shape, u, centroids, self.topk_idx, self.topk_gate, self.dgate,
+                               self.expert_offset, self.sorted_token, self.pair_row, dout, self.dx_routed,
+                               self.dx_shared, self.du, self.dcentroids, self.dz, self.ws_rbwd, self.ws_rbwd_bytes,
+                               stream)
+
     def step(self, u, centroids, bias, gamma: float = 0.001, stream=None):
         """One pass of the whole layer; returns the output buffer (overwritten next step)."""
         self.route(u, centroids, bias, stream)

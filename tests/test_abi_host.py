@@ -161,3 +161,43 @@ def test_pack_weights_args_rejected():
     assert p(_shape(), abi.MOE_W1, 1, FAKE, other) == abi.MOE_ERR_UNSUPPORTED  # fp32 is never tiled
     assert p(_shape(d=320, d_ff=128, act="bf16", ffn="bf16"), abi.MOE_W1, 1, FAKE, other) == \
         abi.MOE_ERR_UNSUPPORTED
+
+
+def test_backward_args_rejected():
+    """The backward runs bf16 layers with row-major weights and 128-multiple d, d_ff; every
+    call below is stopped on the host before any HIP call."""
+    lib = abi.load()
+    fp32 = _shape()
+    bf = _shape(act="bf16", ffn="bf16")
+    odd = _shape(act="bf16", ffn="bf16", d=192)  # d % 128 != 0
+    fp8 = _shape(act="bf16", ffn="fp8")
+    for s in (fp32, odd, fp8):
+        assert abi.moe_workspace_bytes(s, abi.MOE_CALL_GROUPED_FFN_BACKWARD) == 0
+        assert abi.moe_workspace_bytes(s, abi.MOE_CALL_ROUTE_BACKWARD) == 0
+        assert lib.moe_combine_backward(ctypes.byref(s), FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None) == \
+            abi.MOE_ERR_UNSUPPORTED
+    need = abi.moe_workspace_bytes(bf, abi.MOE_CALL_GROUPED_FFN_BACKWARD)
+    # h, da, dv for the routed rows and the shared experts' rows, bf16
+    assert need >= 3 * 2 * (64 * 2 + 64 * 1) * 128
+    assert abi.moe_workspace_bytes(bf, abi.MOE_CALL_ROUTE_BACKWARD) >= 64 * 2 * 4
+    es = abi.make_expert_set(FAKE, FAKE, FAKE)
+    tiled = abi.make_expert_set(FAKE, FAKE, FAKE, layout=abi.MOE_LAYOUT_TILED)
+    gr = abi.make_expert_grads(FAKE, FAKE, FAKE)
+    nullg = abi.make_expert_grads(FAKE, None, FAKE)
+    call = lambda s, r, sh, g, gs, dxs, ws, n: lib.moe_grouped_ffn_backward(
+        ctypes.byref(s), FAKE, FAKE, FAKE, FAKE, ctypes.byref(r), None if sh is None else ctypes.byref(sh),
+        FAKE, FAKE, dxs, ctypes.byref(g), None if gs is None else ctypes.byref(gs), ws, n, None)
+    assert call(bf, es, es, gr, gr, FAKE, FAKE, need - 1) == abi.MOE_ERR_WORKSPACE
+    assert call(bf, es, es, gr, gr, FAKE, None, need) == abi.MOE_ERR_WORKSPACE
+    assert call(bf, tiled, tiled, gr, gr, FAKE, FAKE, need) == abi.MOE_ERR_UNSUPPORTED
+    assert call(bf, es, es, nullg, gr, FAKE, FAKE, need) == abi.MOE_ERR_INVALID_ARG
+    assert call(bf, es, None, gr, gr, FAKE, FAKE, need) == abi.MOE_ERR_INVALID_ARG   # n_shared = 1
+    assert call(bf, es, es, gr, None, FAKE, FAKE, need) == abi.MOE_ERR_INVALID_ARG
+    assert call(bf, es, es, gr, gr, None, FAKE, need) == abi.MOE_ERR_INVALID_ARG     # dx_shared
+    rneed = abi.moe_workspace_bytes(bf, abi.MOE_CALL_ROUTE_BACKWARD)
+    args = [FAKE] * 14
+    assert lib.moe_route_backward(ctypes.byref(bf), *args, FAKE, rneed - 1, None) == abi.MOE_ERR_WORKSPACE
+    args[10] = None  # dx_shared with a shared expert
+    assert lib.moe_route_backward(ctypes.byref(bf), *args, FAKE, rneed, None) == abi.MOE_ERR_INVALID_ARG
+    assert lib.moe_combine_backward(ctypes.byref(bf), FAKE, FAKE, FAKE, FAKE, FAKE, None, None) == \
+        abi.MOE_ERR_INVALID_ARG
