@@ -11,6 +11,11 @@ intends. The default workload is the DeepSeek-V3-shaped prefill layer in bf16
 Prints one JSON line: whole-layer tokens/s, plus a roofline entry for the grouped
 FFN (the two expert GEMM launches, >99% of the FLOPs) timed with HIP events on the
 launch stream, and the CPU oracle timed on a bounded sample of the same workload.
+
+--backward times the layer backward instead (moe_combine_backward ->
+moe_grouped_ffn_backward -> moe_route_backward after one forward step, row-major bf16
+weights) and prints its own line, with the roofline of the grouped FFN backward (four
+MFMA launches: 16 d d_ff FLOPs per expert row).
 """
 from __future__ import annotations
 
@@ -44,6 +49,7 @@ def parse():
     p.add_argument("--cpu-tokens", type=int, default=0, help="oracle sample size (0 = auto)")
     p.add_argument("--layout", choices=["tiled", "rows"], default="tiled",
                    help="expert weight layout: tiled (packed once at setup by moe_pack_weights) or row-major")
+    p.add_argument("--backward", action="store_true", help="time the layer backward instead")
     p.add_argument("--calibrate-copy", action="store_true",
                    help="also run one plain 1 GiB device copy (the reference for FETCH_SIZE/WRITE_SIZE)")
     return p.parse_args()
@@ -203,6 +209,107 @@ def cpu_baseline(w, n_tokens: int):
                       f"{n_tokens} tokens of the {w.name} batch, double precision, {dt:.1f} s"}
 
 
+def bench_backward(args):
+    """The layer backward on the workload: one forward step, then `steps` timed backward
+    passes (each the three backward calls) after `warmup` untimed ones."""
+    import torch
+
+    from mixture_experts_layer_26_amd import abi
+    from mixture_experts_layer_26_amd import inputs as I
+
+    w, dev, L, layout = setup(args.workload, "rows")
+    assert w.act == "bf16" and w.ffn == "bf16", "the backward runs bf16 layers"
+    stream = torch.cuda.current_stream()
+    L.route(dev["u"], dev["e"], dev["b"], stream)
+    L.dispatch(stream)
+    L.grouped_ffn(dev["u"], stream)
+    L.combine(dev["u"], stream)
+    L.alloc_backward()
+    dout = torch.from_numpy(I.make_u(w, batch=99).view("int16")).view(torch.bfloat16).cuda()
+    torch.cuda.synchronize()
+    for _ in range(args.warmup):
+        L.backward(dev["u"], dev["e"], dout, stream)
+    torch.cuda.synchronize()
+    names = ["combine_backward", "grouped_ffn_backward", "route_backward"]
+    acc = dict.fromkeys(names, 0.0)
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(4)]
+        ev[0].record(stream)
+        abi.moe_combine_backward(L.shape, dout, L.y_routed, L.pair_row, L.topk_gate, L.dy_routed, L.dgate, stream)
+        ev[1].record(stream)
+        abi.moe_grouped_ffn_backward(L.shape, dev["u"], dout, L.expert_offset, L.sorted_token, L.routed, L.shared,
+                                     L.dy_routed, L.dx_routed, L.dx_shared, L.g_routed, L.g_shared, L.ws_bwd,
+                                     L.ws_bwd_bytes, stream)
+        ev[2].record(stream)
+        abi.moe_route_backward(L.shape, dev["u"], dev["e"], L.topk_idx, L.topk_gate, L.dgate, L.expert_offset,
+                               L.sorted_token, L.pair_row, dout, L.dx_routed, L.dx_shared, L.du, L.dcentroids,
+                               L.dz, L.ws_rbwd, L.ws_rbwd_bytes, stream)
+        ev[3].record(stream)
+        ev[3].synchronize()
+        for i, n in enumerate(names):
+            acc[n] += ev[i].elapsed_time(ev[i + 1])
+    elapsed = time.perf_counter() - t0
+    calls = {n: round(v / args.steps, 4) for n, v in acc.items()}
+    rows = w.pairs + w.n_shared * w.T
+    flops = 16.0 * w.d * w.d_ff * rows
+    ffn_ms = calls["grouped_ffn_backward"]
+    tf = flops / (ffn_ms * 1e-3) / 1e12
+    step_ms = sum(calls.values())
+    res = {
+        "metric": "MoE layer backward tokens/s (dX, dW, router gradients), V3 shape bf16, 1 MI355X",
+        "value": round(w.T / (step_ms * 1e-3), 1),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(step_ms, 4),
+        "wall_ms_per_step": round(1e3 * elapsed / args.steps, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic (seeded Philox/Box-Muller inputs, random-init expert weights, dout ~ N(0,1))",
+        "config": {"workload": w.name, "pass": "backward", "T": w.T, "d": w.d, "n_routed": w.n_routed,
+                   "top_k": w.top_k, "n_shared": w.n_shared, "d_ff": w.d_ff, "act": w.act, "ffn": w.ffn,
+                   "weights": layout},
+        "call_ms": calls,
+        "roofline": {"bound": "mfma", "achieved": round(tf, 2), "peak": PEAKS["bf16"], "unit": "TFLOP/s",
+                     "frac": round(tf / PEAKS["bf16"], 4), "traffic": None,
+                     "kernel": "grouped FFN backward (gate/up recompute + dh, dX, dW1/dW3, dW2)",
+                     "ms_per_launch": ffn_ms, "algorithmic_flops": flops},
+    }
+    if args.cpu:
+        res["cpu_baseline"] = cpu_baseline_backward(w, min(args.cpu_tokens or 48, w.T))
+    print(json.dumps(res), flush=True)
+
+
+def cpu_baseline_backward(w, n_tokens: int):
+    """The oracle's backward on the first n tokens: du, dgate, dz (their rows' recompute,
+    dh and dx, and the router's gradient); weight-gradient sums are not formed."""
+    import numpy as np
+
+    import oracle
+    from mixture_experts_layer_26_amd import inputs as I
+
+    rows = slice(0, n_tokens)
+    u = I.make_u(w, rows)
+    dout = I.make_u(w, batch=99)[rows]
+    e, b = I.make_e(w), I.make_b(w)
+    idx, _, _, _ = oracle.route(u, e, b, w.top_k, w.act)
+    routed = {int(i): I.make_expert(w, False, int(i)) for i in np.unique(idx)}
+    shared = [I.make_expert(w, True, j) for j in range(w.n_shared)]
+    t0 = time.perf_counter()
+    oracle.layer_backward(u, e, b, routed, shared, dout, top_k=w.top_k, d_ff=w.d_ff, act=w.act, ffn=w.ffn,
+                          want_de=False)
+    dt = time.perf_counter() - t0
+    cores = len(os.sched_getaffinity(0))
+    threads = min(int(os.environ.get("OMP_NUM_THREADS", cores)), cores)
+    return {"value": round(n_tokens / dt, 3), "unit": "tokens/s", "cores": threads, "kind": "oracle",
+            "sample": f"backward (du, dgate, dz; no weight-gradient sums) of the first {n_tokens} tokens of "
+                      f"the {w.name} batch, double precision, {dt:.1f} s"}
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -213,6 +320,9 @@ def main():
     assert torch.cuda.is_available(), "bench needs a GPU"
     from mixture_experts_layer_26_amd import inputs as I  # noqa: F401
 
+    if args.backward:
+        bench_backward(args)
+        return
     w, dev, L, layout = setup(args.workload, args.layout)
     if args.calibrate_copy:
         src = torch.empty(1 << 30, dtype=torch.uint8, device="cuda")
