@@ -39,23 +39,25 @@ enum { kGateUp = 0, kDx = 1, kDw13 = 2, kDw2 = 3 };
 
 // operands per mode: A operands (M side), B operands (N side); K-major flags
 template <int MODE> struct Cfg;
+// kOcc: waves per SIMD the register budget is held to (two workgroups per CU overlap one
+// tile's epilogue with another's K loop where the accumulators allow it)
 template <> struct Cfg<kGateUp> {  // A: X, dY (K-contiguous); B: W1, W3 (K-contig.), W2 (K-major)
-  static constexpr int NA = 2, NB = 3, NACC = 3;
+  static constexpr int NA = 2, NB = 3, NACC = 3, kOcc = 1;
   static constexpr bool a_km = false;
   static constexpr bool b_km(int j) { return j == 2; }
 };
 template <> struct Cfg<kDx> {  // A: da, dv (K-contiguous); B: W1, W3 (K-major)
-  static constexpr int NA = 2, NB = 2, NACC = 1;
+  static constexpr int NA = 2, NB = 2, NACC = 1, kOcc = 2;
   static constexpr bool a_km = false;
   static constexpr bool b_km(int) { return true; }
 };
 template <> struct Cfg<kDw13> {  // A: da, dv; B: X (all K-major)
-  static constexpr int NA = 2, NB = 1, NACC = 2;
+  static constexpr int NA = 2, NB = 1, NACC = 2, kOcc = 2;
   static constexpr bool a_km = true;
   static constexpr bool b_km(int) { return true; }
 };
 template <> struct Cfg<kDw2> {  // A: dY; B: h (K-major)
-  static constexpr int NA = 1, NB = 1, NACC = 1;
+  static constexpr int NA = 1, NB = 1, NACC = 1, kOcc = 2;
   static constexpr bool a_km = true;
   static constexpr bool b_km(int) { return true; }
 };
@@ -256,25 +258,27 @@ __device__ __forceinline__ void compute(const unsigned char* base, f32x16 (&acc)
     for (int mb = 0; mb < 2; ++mb)
 #pragma unroll
       for (int nb = 0; nb < 2; ++nb) {
+        // the n-side fragment goes first, so each lane's accumulator holds 4 consecutive
+        // output columns of one output row (see the epilogue)
         if constexpr (MODE == kGateUp) {
-          acc[0][mb][nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[0][mb], fb[0][nb], acc[0][mb][nb], 0, 0, 0);
-          acc[1][mb][nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[0][mb], fb[1][nb], acc[1][mb][nb], 0, 0, 0);
-          acc[2][mb][nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[1][mb], fb[2][nb], acc[2][mb][nb], 0, 0, 0);
+          acc[0][mb][nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fb[0][nb], fa[0][mb], acc[0][mb][nb], 0, 0, 0);
+          acc[1][mb][nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fb[1][nb], fa[0][mb], acc[1][mb][nb], 0, 0, 0);
+          acc[2][mb][nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fb[2][nb], fa[1][mb], acc[2][mb][nb], 0, 0, 0);
         } else if constexpr (MODE == kDx) {
-          acc[0][mb][nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[0][mb], fb[0][nb], acc[0][mb][nb], 0, 0, 0);
-          acc[0][mb][nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[1][mb], fb[1][nb], acc[0][mb][nb], 0, 0, 0);
+          acc[0][mb][nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fb[0][nb], fa[0][mb], acc[0][mb][nb], 0, 0, 0);
+          acc[0][mb][nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fb[1][nb], fa[1][mb], acc[0][mb][nb], 0, 0, 0);
         } else if constexpr (MODE == kDw13) {
-          acc[0][mb][nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[0][mb], fb[0][nb], acc[0][mb][nb], 0, 0, 0);
-          acc[1][mb][nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[1][mb], fb[0][nb], acc[1][mb][nb], 0, 0, 0);
+          acc[0][mb][nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fb[0][nb], fa[0][mb], acc[0][mb][nb], 0, 0, 0);
+          acc[1][mb][nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fb[0][nb], fa[1][mb], acc[1][mb][nb], 0, 0, 0);
         } else {
-          acc[0][mb][nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[0][mb], fb[0][nb], acc[0][mb][nb], 0, 0, 0);
+          acc[0][mb][nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fb[0][nb], fa[0][mb], acc[0][mb][nb], 0, 0, 0);
         }
       }
   }
 }
 
 template <int MODE>
-__global__ __launch_bounds__(kThr) void ffn_bwd_kernel(BwdArgs a) {
+__global__ __launch_bounds__(kThr, Cfg<MODE>::kOcc) void ffn_bwd_kernel(BwdArgs a) {
   constexpr int NA = Cfg<MODE>::NA, NB = Cfg<MODE>::NB, NACC = Cfg<MODE>::NACC;
   constexpr int kStage = (NA + NB) * kTileBytes;
   __shared__ __align__(16) unsigned char lds[2 * kStage];
@@ -328,52 +332,71 @@ __global__ __launch_bounds__(kThr) void ffn_bwd_kernel(BwdArgs a) {
     __syncthreads();
   }
 
-  // epilogue; C layout of the 32x32 MFMA: lane holds column lane % 32 and rows
-  // 8 (v / 4) + 4 (lane / 32) + v % 4 of its block
-  const int col_in = lane % 32;
+  // epilogue. The MFMA's first operand indexes the output rows of its 32x32 result and the
+  // second the columns: with the n-side fragment first, lane l holds output row m =
+  // l % 32 of its 32-row block and columns n = 8 (v / 4) + 4 (l / 32) + v % 4 of its
+  // 32-column block, i.e. 4 consecutive columns per group of 4 v: one 8-byte store each.
+  const int m_in = lane % 32;
 #pragma unroll
   for (int mb = 0; mb < 2; ++mb)
 #pragma unroll
     for (int nb = 0; nb < 2; ++nb)
 #pragma unroll
-      for (int v = 0; v < 16; ++v) {
-        const int r = 64 * wm + 32 * mb + 8 * (v / 4) + 4 * (lane / 32) + (v % 4);
-        const int n = 64 * wn + 32 * nb + col_in;
+      for (int p = 0; p < 4; ++p) {
+        const int r = 64 * wm + 32 * mb + m_in;
+        const int n = 64 * wn + 32 * nb + 8 * p + 4 * (lane / 32);
         if constexpr (MODE == kGateUp) {
           if (r >= c.rows) continue;
-          const float av = acc[0][mb][nb][v], vv = acc[1][mb][nb][v], dh = acc[2][mb][nb][v];
-          const float sg = fast_sigmoid(av);
-          const float silu_a = av * sg;
-          const int64_t row = c.m0 + r;
-          const int64_t col = c.c0 + n;
-          uint16_t *hp, *dap, *dvp;
-          if (c.shared) {
-            const int64_t o = row * (a.n_s * static_cast<int64_t>(a.F)) + static_cast<int64_t>(c.g - a.n_r) * a.F + col;
-            hp = a.h_s + o; dap = a.da_s + o; dvp = a.dv_s + o;
-          } else {
-            const int64_t o = (c.row0 + row) * a.F + col;
-            hp = a.h_r + o; dap = a.da_r + o; dvp = a.dv_r + o;
+          float hv[4], dav[4], dvv[4];
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            const float av = acc[0][mb][nb][4 * p + q], vv = acc[1][mb][nb][4 * p + q];
+            const float dh = acc[2][mb][nb][4 * p + q];
+            const float sg = fast_sigmoid(av);
+            const float silu_a = av * sg;
+            hv[q] = silu_a * vv;
+            dav[q] = dh * vv * sg * (1.0f + av * (1.0f - sg));
+            dvv[q] = dh * silu_a;
           }
-          *hp = f32_to_bf16(silu_a * vv);
-          *dap = f32_to_bf16(dh * vv * sg * (1.0f + av * (1.0f - sg)));
-          *dvp = f32_to_bf16(dh * silu_a);
-        } else if constexpr (MODE == kDx) {
-          if (r >= c.rows) continue;
           const int64_t row = c.m0 + r;
           const int64_t col = c.c0 + n;
-          if (c.shared)
-            a.dx_s[row * a.d + col] = acc[0][mb][nb][v];
-          else
-            a.dx_r[(c.row0 + row) * a.d + col] = f32_to_bf16(acc[0][mb][nb][v]);
-        } else {
-          const int64_t e = c.shared ? c.g - a.n_r : c.g;
-          const int64_t M = MODE == kDw13 ? a.F : a.d, N = MODE == kDw13 ? a.d : a.F;
-          const int64_t o = e * M * N + static_cast<int64_t>(c.mo + r) * N + c.no + n;
-          if constexpr (MODE == kDw13) {
-            (c.shared ? a.dw1s : a.dw1r)[o] = f32_to_bf16(acc[0][mb][nb][v]);
-            (c.shared ? a.dw3s : a.dw3r)[o] = f32_to_bf16(acc[1][mb][nb][v]);
+          int64_t o;
+          uint16_t *hb, *dab, *dvb;
+          if (c.shared) {
+            o = row * (a.n_s * static_cast<int64_t>(a.F)) + static_cast<int64_t>(c.g - a.n_r) * a.F + col;
+            hb = a.h_s; dab = a.da_s; dvb = a.dv_s;
           } else {
-            (c.shared ? a.dw2s : a.dw2r)[o] = f32_to_bf16(acc[0][mb][nb][v]);
+            o = (c.row0 + row) * a.F + col;
+            hb = a.h_r; dab = a.da_r; dvb = a.dv_r;
+          }
+          *reinterpret_cast<uint2*>(hb + o) = make_uint2(pack_bf16x2(hv[0], hv[1]), pack_bf16x2(hv[2], hv[3]));
+          *reinterpret_cast<uint2*>(dab + o) = make_uint2(pack_bf16x2(dav[0], dav[1]), pack_bf16x2(dav[2], dav[3]));
+          *reinterpret_cast<uint2*>(dvb + o) = make_uint2(pack_bf16x2(dvv[0], dvv[1]), pack_bf16x2(dvv[2], dvv[3]));
+        } else {
+          const f32x16& x0 = acc[0][mb][nb];
+          if constexpr (MODE == kDx) {
+            if (r >= c.rows) continue;
+            const int64_t row = c.m0 + r;
+            const int64_t col = c.c0 + n;
+            if (c.shared)
+              *reinterpret_cast<float4*>(a.dx_s + row * a.d + col) =
+                  make_float4(x0[4 * p], x0[4 * p + 1], x0[4 * p + 2], x0[4 * p + 3]);
+            else
+              *reinterpret_cast<uint2*>(a.dx_r + (c.row0 + row) * a.d + col) =
+                  make_uint2(pack_bf16x2(x0[4 * p], x0[4 * p + 1]), pack_bf16x2(x0[4 * p + 2], x0[4 * p + 3]));
+          } else {
+            const int64_t e = c.shared ? c.g - a.n_r : c.g;
+            const int64_t M = MODE == kDw13 ? a.F : a.d, N = MODE == kDw13 ? a.d : a.F;
+            const int64_t o = e * M * N + static_cast<int64_t>(c.mo + r) * N + c.no + n;
+            const uint2 v0 = make_uint2(pack_bf16x2(x0[4 * p], x0[4 * p + 1]), pack_bf16x2(x0[4 * p + 2], x0[4 * p + 3]));
+            if constexpr (MODE == kDw13) {
+              const f32x16& x1 = acc[1][mb][nb];
+              *reinterpret_cast<uint2*>((c.shared ? a.dw1s : a.dw1r) + o) = v0;
+              *reinterpret_cast<uint2*>((c.shared ? a.dw3s : a.dw3r) + o) =
+                  make_uint2(pack_bf16x2(x1[4 * p], x1[4 * p + 1]), pack_bf16x2(x1[4 * p + 2], x1[4 * p + 3]));
+            } else {
+              *reinterpret_cast<uint2*>((c.shared ? a.dw2s : a.dw2r) + o) = v0;
+            }
           }
         }
       }
