@@ -127,7 +127,7 @@ bool backward_shape(const moe_shape* s) {
 }
 
 struct BwdWorkspace {
-  size_t h_r, da_r, dv_r, h_s, da_s, dv_s, total;
+  size_t zero, xs, h_r, da_r, dv_r, h_s, da_s, dv_s, total;
 };
 
 BwdWorkspace bwd_workspace(const moe_shape* s) {
@@ -135,6 +135,10 @@ BwdWorkspace bwd_workspace(const moe_shape* s) {
   const size_t pr = static_cast<size_t>(s->T) * s->top_k * s->d_ff * 2;
   const size_t ps = static_cast<size_t>(s->T) * s->n_shared * s->d_ff * 2;
   size_t off = 0;
+  w.zero = off;
+  off = align_up(off + 256);
+  w.xs = off;
+  off = align_up(off + static_cast<size_t>(s->T) * s->top_k * s->d * 2);
   w.h_r = off;
   off = align_up(off + pr);
   w.da_r = off;
@@ -497,6 +501,8 @@ moe_status moe_grouped_ffn_backward(const moe_shape* s, const void* u, const voi
   a.w1s = has_s ? static_cast<const uint16_t*>(shared->w1) : nullptr;
   a.w3s = has_s ? static_cast<const uint16_t*>(shared->w3) : nullptr;
   a.w2s = has_s ? static_cast<const uint16_t*>(shared->w2) : nullptr;
+  a.zero = reinterpret_cast<uint16_t*>(wsb + w.zero);
+  a.xs = reinterpret_cast<uint16_t*>(wsb + w.xs);
   a.h_r = reinterpret_cast<uint16_t*>(wsb + w.h_r);
   a.da_r = reinterpret_cast<uint16_t*>(wsb + w.da_r);
   a.dv_r = reinterpret_cast<uint16_t*>(wsb + w.dv_r);

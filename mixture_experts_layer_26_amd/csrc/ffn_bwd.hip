@@ -7,14 +7,16 @@
 //   dh = dY W2,  da = dh v SiLU'(a),  dv = dh SiLU(a),  dX = da W1 + dv W3,
 //   dW1 = da^T X,  dW3 = dv^T X,  dW2 = dY^T h.
 // Four launches, each a grid of 128 x 128 output tiles on 4 waves (64 x 64 each, four
-// v_mfma_f32_32x32x16_bf16 tiles per product), K in steps of 32 through two LDS stages
-// filled from registers:
+// v_mfma_f32_32x32x16_bf16 tiles per product), K in steps of 32 through a ring of LDS
+// stages filled by global_load_lds_dwordx4 (no staging registers):
 //   kGateUp: rows x d_ff tiles, K = d: a, v and dh in three accumulators; the epilogue
 //            forms h (as the forward does), da and dv and stores them in bf16.
 //   kDx:     rows x d tiles, K = d_ff (the shared experts' K ranges one after another):
 //            dX = da W1 + dv W3 in one accumulator.
 //   kDw13:   d_ff x d tiles per expert, K = the expert's rows: dW1 and dW3.
 //   kDw2:    d x d_ff tiles per expert, K = the expert's rows: dW2.
+// The routed rows of X are read from a sorted copy of u (gathered once per call), so no
+// index lookups sit in the K loops.
 // Operands whose K is contiguous in memory (X, dY, da, dv in kGateUp/kDx, the rows of
 // W1/W3 in kGateUp) are staged as [rows][32 k] and read with ds_read_b128. Operands
 // whose K runs across rows (W2 in kGateUp, W1/W3 in kDx, everything in the weight
@@ -40,24 +42,25 @@ enum { kGateUp = 0, kDx = 1, kDw13 = 2, kDw2 = 3 };
 // operands per mode: A operands (M side), B operands (N side); K-major flags
 template <int MODE> struct Cfg;
 // kOcc: waves per SIMD the register budget is held to (two workgroups per CU overlap one
-// tile's epilogue with another's K loop where the accumulators allow it)
+// tile's epilogue with another's K loop where the accumulators allow it); NST: LDS stages
+// in the load ring (NST - 1 K-steps in flight), as many as the LDS of kOcc workgroups holds
 template <> struct Cfg<kGateUp> {  // A: X, dY (K-contiguous); B: W1, W3 (K-contig.), W2 (K-major)
-  static constexpr int NA = 2, NB = 3, NACC = 3, kOcc = 1;
+  static constexpr int NA = 2, NB = 3, NACC = 3, kOcc = 1, NST = 3;
   static constexpr bool a_km = false;
   static constexpr bool b_km(int j) { return j == 2; }
 };
 template <> struct Cfg<kDx> {  // A: da, dv (K-contiguous); B: W1, W3 (K-major)
-  static constexpr int NA = 2, NB = 2, NACC = 1, kOcc = 2;
+  static constexpr int NA = 2, NB = 2, NACC = 1, kOcc = 2, NST = 2;
   static constexpr bool a_km = false;
   static constexpr bool b_km(int) { return true; }
 };
 template <> struct Cfg<kDw13> {  // A: da, dv; B: X (all K-major)
-  static constexpr int NA = 2, NB = 1, NACC = 2, kOcc = 2;
+  static constexpr int NA = 2, NB = 1, NACC = 2, kOcc = 2, NST = 3;
   static constexpr bool a_km = true;
   static constexpr bool b_km(int) { return true; }
 };
 template <> struct Cfg<kDw2> {  // A: dY; B: h (K-major)
-  static constexpr int NA = 1, NB = 1, NACC = 1, kOcc = 2;
+  static constexpr int NA = 1, NB = 1, NACC = 1, kOcc = 2, NST = 3;
   static constexpr bool a_km = true;
   static constexpr bool b_km(int) { return true; }
 };
@@ -86,10 +89,6 @@ __device__ __forceinline__ bf16x8 frag_km(const unsigned char* t, int c0, int s,
   typedef short v8s __attribute__((ext_vector_type(8)));
   const v8s both = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
   return __builtin_bit_cast(bf16x8, both);
-}
-
-__device__ __forceinline__ uint4 ld_or_zero(const uint16_t* p) {
-  return p ? ld16(p) : make_uint4(0, 0, 0, 0);
 }
 
 // Where a tile's rows, weights and outputs are.
@@ -140,97 +139,114 @@ __device__ bool decode_row_tile(const BwdArgs& a, int mode, int id, Ctx& c, int*
   return true;
 }
 
-// Global address of staged chunk i (0, 1) of operand op at K-step kt; nullptr = zeros.
-// K-contiguous operands: chunk q = tid + 256 i is row q / 4, 8 elements at k 8 (q % 4).
-// K-major operands: chunk q is K-row q / 16, 8 elements at column 8 (q % 16).
+// Global address of the 16 bytes one lane copies for operand op at K-step kt.
+// K-contiguous operands: (x, y) = (tile row, 8-element chunk of the step's 32 k); rows past
+// the tile's rows repeat its last row (they feed only outputs that are not stored).
+// K-major operands: (x, y) = (K-row of the step, first of 8 columns); K-rows past the
+// group's rows (weight gradients) read the zeroed 16 bytes at a.zero.
 template <int MODE>
-__device__ __forceinline__ const uint16_t* src(const BwdArgs& a, const Ctx& c, bool is_a, int op, int i, int kt) {
-  const int q = threadIdx.x + kThr * i;
+__device__ __forceinline__ const uint16_t* src(const BwdArgs& a, const Ctx& c, bool is_a, int op, int x, int y,
+                                               int kt) {
   const int64_t F = a.F, d = a.d;
   if constexpr (MODE == kGateUp) {
-    if (is_a) {  // X or dY, row r of the tile, k = 32 kt + 8 (q % 4)
-      const int r = q / 4;
-      if (r >= c.rows) return nullptr;
-      const int64_t k = static_cast<int64_t>(kBK) * kt + 8 * (q % 4);
-      const int64_t row = c.m0 + r;
-      if (op == 0) {
-        const int64_t tok = c.shared ? row : a.sorted_token[c.row0 + row];
-        return a.u + tok * d + k;
-      }
+    if (is_a) {  // X (sorted copy) or dY, row x of the tile, k = 32 kt + 8 y
+      const int64_t row = c.m0 + (x < c.rows ? x : c.rows - 1);
+      const int64_t k = static_cast<int64_t>(kBK) * kt + 8 * y;
+      if (op == 0) return c.shared ? a.u + row * d + k : a.xs + (c.row0 + row) * d + k;
       return c.shared ? a.dout + row * d + k : a.dy_routed + (c.row0 + row) * d + k;
     }
     const int e = c.shared ? c.g - a.n_r : c.g;
-    if (op < 2) {  // W1 / W3 row c0 + r, k contiguous
+    if (op < 2) {  // W1 / W3 row c0 + x, k contiguous
       const uint16_t* w = c.shared ? (op == 0 ? a.w1s : a.w3s) : (op == 0 ? a.w1r : a.w3r);
-      const int r = q / 4;
-      return w + static_cast<int64_t>(e) * F * d + (c.c0 + r) * d + static_cast<int64_t>(kBK) * kt + 8 * (q % 4);
+      return w + static_cast<int64_t>(e) * F * d + (c.c0 + x) * d + static_cast<int64_t>(kBK) * kt + 8 * y;
     }
-    // W2 [d][d_ff]: K-row 32 kt + q / 16, columns c0 + 8 (q % 16)
+    // W2 [d][d_ff]: K-row 32 kt + x, columns c0 + y
     const uint16_t* w = c.shared ? a.w2s : a.w2r;
-    const int64_t k = static_cast<int64_t>(kBK) * kt + q / 16;
-    return w + static_cast<int64_t>(e) * d * F + k * F + c.c0 + 8 * (q % 16);
+    const int64_t k = static_cast<int64_t>(kBK) * kt + x;
+    return w + static_cast<int64_t>(e) * d * F + k * F + c.c0 + y;
   } else if constexpr (MODE == kDx) {
     const int64_t kk = static_cast<int64_t>(kBK) * kt;  // K position (shared: across the experts)
-    if (is_a) {  // da / dv row r
-      const int r = q / 4;
-      if (r >= c.rows) return nullptr;
-      const int64_t row = c.m0 + r;
-      const int64_t k = kk + 8 * (q % 4);
+    if (is_a) {  // da / dv row x
+      const int64_t row = c.m0 + (x < c.rows ? x : c.rows - 1);
+      const int64_t k = kk + 8 * y;
       if (c.shared) return (op == 0 ? a.da_s : a.dv_s) + row * (a.n_s * F) + k;
       return (op == 0 ? a.da_r : a.dv_r) + (c.row0 + row) * F + k;
     }
-    // W1 / W3 [d_ff][d]: K-row j, columns c0 + 8 (q % 16)
+    // W1 / W3 [d_ff][d]: K-row j, columns c0 + y
     const int64_t seg = c.shared ? kk / F : c.g;
-    const int64_t j = kk - (c.shared ? seg * F : 0) + q / 16;
+    const int64_t j = kk - (c.shared ? seg * F : 0) + x;
     const uint16_t* w = c.shared ? (op == 0 ? a.w1s : a.w3s) : (op == 0 ? a.w1r : a.w3r);
-    return w + seg * F * d + j * d + c.c0 + 8 * (q % 16);
+    return w + seg * F * d + j * d + c.c0 + y;
   } else {
-    // weight gradients: K-row = row 32 kt + q / 16 of the group, columns 8 (q % 16)
-    const int64_t row = static_cast<int64_t>(kBK) * kt + q / 16;
-    if (row >= c.rows) return nullptr;
-    const int col = 8 * (q % 16);
+    // weight gradients: K-row = row 32 kt + x of the group, columns y
+    const int64_t row = static_cast<int64_t>(kBK) * kt + x;
+    if (row >= c.rows) return a.zero;
     const int s = c.shared ? c.g - a.n_r : 0;
     if constexpr (MODE == kDw13) {
       if (is_a) {  // da / dv columns mo.. (d_ff)
-        if (c.shared) return (op == 0 ? a.da_s : a.dv_s) + row * (a.n_s * F) + s * F + c.mo + col;
-        return (op == 0 ? a.da_r : a.dv_r) + (c.row0 + row) * F + c.mo + col;
+        if (c.shared) return (op == 0 ? a.da_s : a.dv_s) + row * (a.n_s * F) + s * F + c.mo + y;
+        return (op == 0 ? a.da_r : a.dv_r) + (c.row0 + row) * F + c.mo + y;
       }
-      const int64_t tok = c.shared ? row : a.sorted_token[c.row0 + row];  // X columns no.. (d)
-      return a.u + tok * d + c.no + col;
+      // X columns no.. (d)
+      return c.shared ? a.u + row * d + c.no + y : a.xs + (c.row0 + row) * d + c.no + y;
     } else {
       if (is_a) {  // dY columns mo.. (d)
-        if (c.shared) return a.dout + row * d + c.mo + col;
-        return a.dy_routed + (c.row0 + row) * d + c.mo + col;
+        if (c.shared) return a.dout + row * d + c.mo + y;
+        return a.dy_routed + (c.row0 + row) * d + c.mo + y;
       }
-      if (c.shared) return a.h_s + row * (a.n_s * F) + s * F + c.no + col;  // h columns no.. (d_ff)
-      return a.h_r + (c.row0 + row) * F + c.no + col;
+      if (c.shared) return a.h_s + row * (a.n_s * F) + s * F + c.no + y;  // h columns no.. (d_ff)
+      return a.h_r + (c.row0 + row) * F + c.no + y;
     }
   }
 }
 
-template <int MODE>
-__device__ __forceinline__ void stage_load(const BwdArgs& a, const Ctx& c, int kt, uint4 (&st)[Cfg<MODE>::NA + Cfg<MODE>::NB][2]) {
-  constexpr int NA = Cfg<MODE>::NA, NB = Cfg<MODE>::NB;
-#pragma unroll
-  for (int op = 0; op < NA + NB; ++op)
-#pragma unroll
-    for (int i = 0; i < 2; ++i) st[op][i] = ld_or_zero(src<MODE>(a, c, op < NA, op < NA ? op : op - NA, i, kt));
+typedef __attribute__((address_space(3))) unsigned char* lds_ptr;
+
+// One global_load_lds_dwordx4: lane i copies the 16 bytes at gptr (its own address) to
+// LDS byte lds + 16 i. M0 holds the LDS address (one wait state after writing it). The
+// instruction is written out so that the compiler adds no wait of its own before the LDS
+// reads; the waits are the explicit ones in ring_wait.
+__device__ __forceinline__ void dma16(const void* gptr, const unsigned char* lds) {
+  const uint32_t m0 = static_cast<uint32_t>(reinterpret_cast<uintptr_t>((lds_ptr)(lds)));
+  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(gptr), "s"(m0) : "memory");
 }
 
+// Loads of K-step kt into one stage: each operand's 8 KB tile is 512 16-byte slots; wave
+// w fills slots 128 w .. 128 w + 127 with two instructions (slot 128 w + 64 i + lane).
+// The lane picks the global chunk whose swizzled LDS position is its slot.
 template <int MODE>
-__device__ __forceinline__ void stage_store(unsigned char* base, const uint4 (&st)[Cfg<MODE>::NA + Cfg<MODE>::NB][2]) {
+__device__ __forceinline__ void dma_step(const BwdArgs& a, const Ctx& c, int kt, unsigned char* stage, int w,
+                                         int lane) {
   constexpr int NA = Cfg<MODE>::NA, NB = Cfg<MODE>::NB;
 #pragma unroll
   for (int op = 0; op < NA + NB; ++op) {
     const bool km = op < NA ? Cfg<MODE>::a_km : Cfg<MODE>::b_km(op - NA);
-    unsigned char* t = base + op * kTileBytes;
 #pragma unroll
     for (int i = 0; i < 2; ++i) {
-      const int q = threadIdx.x + kThr * i;
-      const int off = km ? km_off(q / 16, 16 * (q % 16)) : kc_off(q / 4, q % 4);
-      *reinterpret_cast<uint4*>(t + off) = st[op][i];
+      const int slot = 128 * w + 64 * i + lane;
+      int x, y;
+      if (km) {  // slot = 16 k + 4 (unit ^ (k & 3)) + 16-byte piece of the unit
+        x = slot / 16;
+        const int ws = slot % 16;
+        y = ((((ws / 4) ^ x) & 3) * 32) + (ws % 4) * 8;
+      } else {  // slot = 4 r + (chunk ^ ((r >> 2) & 3))
+        x = slot / 4;
+        y = (slot % 4) ^ ((x >> 2) & 3);
+      }
+      dma16(src<MODE>(a, c, op < NA, op < NA ? op : op - NA, x, y, kt),
+            stage + op * kTileBytes + (128 * w + 64 * i) * 16);
     }
   }
+}
+
+// Wait until this wave's loads of the oldest stage in flight have landed (the N loads
+// issued after them may stay in flight), then the workgroup barrier.
+template <int N>
+__device__ __forceinline__ void ring_wait() {
+  if constexpr (N == 0)
+    asm volatile("s_waitcnt vmcnt(0)\n\ts_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+  else
+    asm volatile("s_waitcnt vmcnt(%0)\n\ts_waitcnt lgkmcnt(0)\n\ts_barrier" ::"n"(N) : "memory");
 }
 
 template <int MODE>
@@ -280,11 +296,14 @@ __device__ __forceinline__ void compute(const unsigned char* base, f32x16 (&acc)
 template <int MODE>
 __global__ __launch_bounds__(kThr, Cfg<MODE>::kOcc) void ffn_bwd_kernel(BwdArgs a) {
   constexpr int NA = Cfg<MODE>::NA, NB = Cfg<MODE>::NB, NACC = Cfg<MODE>::NACC;
+  constexpr int NST = Cfg<MODE>::NST;
   constexpr int kStage = (NA + NB) * kTileBytes;
-  __shared__ __align__(16) unsigned char lds[2 * kStage];
+  constexpr int ND = (NA + NB) * 2;  // loads per wave per K-step
+  __shared__ __align__(16) unsigned char lds[NST * kStage];
   __shared__ int sh[2];
   __shared__ int soff[257];
-  const int lane = threadIdx.x % kWave, w = threadIdx.x / kWave;
+  const int lane = threadIdx.x % kWave;
+  const int w = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
   const int wm = w / 2, wn = w % 2;
 
   Ctx c{};
@@ -318,18 +337,19 @@ __global__ __launch_bounds__(kThr, Cfg<MODE>::kOcc) void ffn_bwd_kernel(BwdArgs 
 #pragma unroll
         for (int v = 0; v < 16; ++v) acc[x][mb][nb][v] = 0.0f;
 
-  uint4 st[NA + NB][2];
-  if (c.nk > 0) {
-    stage_load<MODE>(a, c, 0, st);
-    stage_store<MODE>(lds, st);
-    __syncthreads();
-  }
+  // load ring: steps 0 .. NST - 2 first; at step kt, once step kt has landed, the load of
+  // step kt + NST - 1 goes into the stage step kt - 1 was read from (every wave is past
+  // that read: it came before the barrier)
+#pragma unroll
+  for (int s0 = 0; s0 < NST - 1; ++s0)
+    if (s0 < c.nk) dma_step<MODE>(a, c, s0, lds + s0 * kStage, w, lane);
   for (int kt = 0; kt < c.nk; ++kt) {
-    const bool more = kt + 1 < c.nk;
-    if (more) stage_load<MODE>(a, c, kt + 1, st);
-    compute<MODE>(lds + (kt & 1) * kStage, acc, wm, wn, lane);
-    if (more) stage_store<MODE>(lds + ((kt + 1) & 1) * kStage, st);
-    __syncthreads();
+    if (NST == 3 && kt + 1 < c.nk)
+      ring_wait<ND>();  // step kt + 1's loads may stay in flight
+    else
+      ring_wait<0>();
+    if (kt + NST - 1 < c.nk) dma_step<MODE>(a, c, kt + NST - 1, lds + ((kt + NST - 1) % NST) * kStage, w, lane);
+    compute<MODE>(lds + (kt % NST) * kStage, acc, wm, wn, lane);
   }
 
   // epilogue. The MFMA's first operand indexes the output rows of its 32x32 result and the
@@ -402,6 +422,23 @@ __global__ __launch_bounds__(kThr, Cfg<MODE>::kOcc) void ffn_bwd_kernel(BwdArgs 
       }
 }
 
+// xs[r] = u[sorted_token[r]] for the P sorted rows (16 bytes per thread); the first
+// block also clears the 256 zero bytes that padded K-rows read.
+__global__ __launch_bounds__(256) void gather_rows_kernel(const uint16_t* __restrict__ u,
+                                                          const int32_t* __restrict__ sorted_token,
+                                                          uint16_t* __restrict__ xs, uint16_t* __restrict__ zero,
+                                                          int64_t P, int d) {
+  if (blockIdx.x == 0 && threadIdx.x < 16) reinterpret_cast<uint4*>(zero)[threadIdx.x] = make_uint4(0, 0, 0, 0);
+  const int cpr = d / 8;  // 16-byte chunks per row
+  const int64_t n = P * cpr;
+  for (int64_t q = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x; q < n;
+       q += static_cast<int64_t>(gridDim.x) * 256) {
+    const int64_t r = q / cpr;
+    const int ch = static_cast<int>(q % cpr);
+    st16(xs + r * d + 8 * ch, ld16(u + static_cast<int64_t>(sorted_token[r]) * d + 8 * ch));
+  }
+}
+
 }  // namespace
 
 int64_t bwd_row_tiles(int mode, int64_t T, int K, int n_r, int n_s, int d, int F) {
@@ -412,6 +449,12 @@ int64_t bwd_row_tiles(int mode, int64_t T, int K, int n_r, int n_s, int d, int F
 }
 
 hipError_t launch_ffn_backward(const BwdArgs& a, hipStream_t stream) {
+  const int64_t chunks = a.T * a.K * (a.d / 8);
+  const unsigned gg = static_cast<unsigned>(chunks / 256 + 1 < 8192 ? chunks / 256 + 1 : 8192);
+  hipLaunchKernelGGL(gather_rows_kernel, dim3(gg), dim3(256), 0, stream, a.u, a.sorted_token, a.xs, a.zero,
+                     a.T * a.K, a.d);
+  hipError_t err0 = hipGetLastError();
+  if (err0 != hipSuccess) return err0;
   const unsigned g1 = static_cast<unsigned>(bwd_row_tiles(0, a.T, a.K, a.n_r, a.n_s, a.d, a.F));
   hipLaunchKernelGGL(ffn_bwd_kernel<kGateUp>, dim3(g1), dim3(kThr), 0, stream, a);
   hipError_t err = hipGetLastError();

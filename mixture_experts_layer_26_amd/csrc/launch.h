@@ -125,6 +125,8 @@ struct BwdArgs {
   const uint16_t *w1s, *w3s, *w2s;  // shared weights (n_s experts)
   uint16_t *h_r, *da_r, *dv_r;   // workspace [P, d_ff]: h, da, dv of the routed rows
   uint16_t *h_s, *da_s, *dv_s;   // workspace [T, n_s * d_ff]
+  uint16_t* xs;                  // workspace [P, d]: u of the sorted rows
+  uint16_t* zero;                // workspace, 256 bytes cleared by the call
   uint16_t* dx_r;                // out [P, d] bf16
   float* dx_s;                   // out [T, d] fp32, sum over the shared experts
   uint16_t *dw1r, *dw3r, *dw2r;  // out, routed weight gradients (bf16, weight layouts)
