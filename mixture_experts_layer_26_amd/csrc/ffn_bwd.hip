@@ -33,9 +33,7 @@ namespace moe {
 namespace {
 
 constexpr int kBT = 128;                 // tile rows and columns
-constexpr int kBK = 32;                  // K per step
 constexpr int kThr = 256;                // 4 waves
-constexpr int kTileBytes = kBT * kBK * 2;  // one staged operand: 8 KB
 
 enum { kGateUp = 0, kDx = 1, kDw13 = 2, kDw2 = 3 };
 
@@ -43,40 +41,47 @@ enum { kGateUp = 0, kDx = 1, kDw13 = 2, kDw2 = 3 };
 template <int MODE> struct Cfg;
 // kOcc: waves per SIMD the register budget is held to (two workgroups per CU overlap one
 // tile's epilogue with another's K loop where the accumulators allow it); NST: LDS stages
-// in the load ring (NST - 1 K-steps in flight), as many as the LDS of kOcc workgroups holds
+// in the load ring (NST - 1 K-steps in flight), as many as the LDS of kOcc workgroups holds;
+// BK: K per step. Operands whose K runs along their rows take whole 128-byte lines per row
+// with BK = 64; with BK = 32 each line is requested twice, a step apart.
 template <> struct Cfg<kGateUp> {  // A: X, dY (K-contiguous); B: W1, W3 (K-contig.), W2 (K-major)
-  static constexpr int NA = 2, NB = 3, NACC = 3, kOcc = 1, NST = 3;
+  static constexpr int NA = 2, NB = 3, NACC = 3, kOcc = 1, NST = 2, BK = 64;
   static constexpr bool a_km = false;
   static constexpr bool b_km(int j) { return j == 2; }
 };
 template <> struct Cfg<kDx> {  // A: da, dv (K-contiguous); B: W1, W3 (K-major)
-  static constexpr int NA = 2, NB = 2, NACC = 1, kOcc = 2, NST = 2;
+  static constexpr int NA = 2, NB = 2, NACC = 1, kOcc = 2, NST = 2, BK = 32;
   static constexpr bool a_km = false;
   static constexpr bool b_km(int) { return true; }
 };
 template <> struct Cfg<kDw13> {  // A: da, dv; B: X (all K-major)
-  static constexpr int NA = 2, NB = 1, NACC = 2, kOcc = 2, NST = 3;
+  static constexpr int NA = 2, NB = 1, NACC = 2, kOcc = 2, NST = 3, BK = 32;
   static constexpr bool a_km = true;
   static constexpr bool b_km(int) { return true; }
 };
 template <> struct Cfg<kDw2> {  // A: dY; B: h (K-major)
-  static constexpr int NA = 1, NB = 1, NACC = 1, kOcc = 2, NST = 3;
+  static constexpr int NA = 1, NB = 1, NACC = 1, kOcc = 2, NST = 3, BK = 32;
   static constexpr bool a_km = true;
   static constexpr bool b_km(int) { return true; }
 };
 
-// LDS offsets. K-contiguous tile [128 rows][32 k]: 64-byte rows, 16-byte chunk c of row r
-// at chunk c ^ ((r >> 2) & 3), so the 32 rows of a fragment read cover all banks.
-__device__ __forceinline__ int kc_off(int r, int c) { return r * 64 + ((c ^ ((r >> 2) & 3)) << 4); }
-// K-major tile [32 k][128 columns]: 256-byte rows, 64-byte unit q of row k at q ^ (k & 3),
+// LDS offsets. K-contiguous tile [128 rows][BK k]: 2 BK-byte rows; 16-byte chunk c of row r
+// at chunk c ^ ((r >> 2) & 3) (BK = 32) or c ^ ((r >> 1) & 7) (BK = 64), so the 32 rows of a
+// fragment read cover all banks.
+template <int BK>
+__device__ __forceinline__ int kc_swz(int r) { return BK == 32 ? (r >> 2) & 3 : (r >> 1) & 7; }
+template <int BK>
+__device__ __forceinline__ int kc_off(int r, int c) { return r * (2 * BK) + ((c ^ kc_swz<BK>(r)) << 4); }
+// K-major tile [BK k][128 columns]: 256-byte rows, 64-byte unit q of row k at q ^ (k & 3),
 // so the 4 rows of one transposed read fall in different banks.
 __device__ __forceinline__ int km_off(int k, int byte) { return k * 256 + ((((byte >> 6) ^ k) & 3) << 6) + (byte & 63); }
 
 typedef short v4s __attribute__((ext_vector_type(4)));
 
 // MFMA fragment (8 consecutive k of row/column `lane % 32` of a 32-block) of sub-step s.
+template <int BK>
 __device__ __forceinline__ bf16x8 frag_kc(const unsigned char* t, int r0, int s, int lane) {
-  return *reinterpret_cast<const bf16x8*>(t + kc_off(r0 + lane % 32, 2 * s + lane / 32));
+  return *reinterpret_cast<const bf16x8*>(t + kc_off<BK>(r0 + lane % 32, 2 * s + lane / 32));
 }
 __device__ __forceinline__ bf16x8 frag_km(const unsigned char* t, int c0, int s, int lane) {
   const int g = lane / 16, j = lane % 16;
@@ -140,7 +145,7 @@ __device__ bool decode_row_tile(const BwdArgs& a, int mode, int id, Ctx& c, int*
 }
 
 // Global address of the 16 bytes one lane copies for operand op at K-step kt.
-// K-contiguous operands: (x, y) = (tile row, 8-element chunk of the step's 32 k); rows past
+// K-contiguous operands: (x, y) = (tile row, 8-element chunk of the step's BK k); rows past
 // the tile's rows repeat its last row (they feed only outputs that are not stored).
 // K-major operands: (x, y) = (K-row of the step, first of 8 columns); K-rows past the
 // group's rows (weight gradients) read the zeroed 16 bytes at a.zero.
@@ -149,23 +154,23 @@ __device__ __forceinline__ const uint16_t* src(const BwdArgs& a, const Ctx& c, b
                                                int kt) {
   const int64_t F = a.F, d = a.d;
   if constexpr (MODE == kGateUp) {
-    if (is_a) {  // X (sorted copy) or dY, row x of the tile, k = 32 kt + 8 y
+    if (is_a) {  // X (sorted copy) or dY, row x of the tile, k = BK kt + 8 y
       const int64_t row = c.m0 + (x < c.rows ? x : c.rows - 1);
-      const int64_t k = static_cast<int64_t>(kBK) * kt + 8 * y;
+      const int64_t k = static_cast<int64_t>(Cfg<MODE>::BK) * kt + 8 * y;
       if (op == 0) return c.shared ? a.u + row * d + k : a.xs + (c.row0 + row) * d + k;
       return c.shared ? a.dout + row * d + k : a.dy_routed + (c.row0 + row) * d + k;
     }
     const int e = c.shared ? c.g - a.n_r : c.g;
     if (op < 2) {  // W1 / W3 row c0 + x, k contiguous
       const uint16_t* w = c.shared ? (op == 0 ? a.w1s : a.w3s) : (op == 0 ? a.w1r : a.w3r);
-      return w + static_cast<int64_t>(e) * F * d + (c.c0 + x) * d + static_cast<int64_t>(kBK) * kt + 8 * y;
+      return w + static_cast<int64_t>(e) * F * d + (c.c0 + x) * d + static_cast<int64_t>(Cfg<MODE>::BK) * kt + 8 * y;
     }
-    // W2 [d][d_ff]: K-row 32 kt + x, columns c0 + y
+    // W2 [d][d_ff]: K-row BK kt + x, columns c0 + y
     const uint16_t* w = c.shared ? a.w2s : a.w2r;
-    const int64_t k = static_cast<int64_t>(kBK) * kt + x;
+    const int64_t k = static_cast<int64_t>(Cfg<MODE>::BK) * kt + x;
     return w + static_cast<int64_t>(e) * d * F + k * F + c.c0 + y;
   } else if constexpr (MODE == kDx) {
-    const int64_t kk = static_cast<int64_t>(kBK) * kt;  // K position (shared: across the experts)
+    const int64_t kk = static_cast<int64_t>(Cfg<MODE>::BK) * kt;  // K position (shared: across the experts)
     if (is_a) {  // da / dv row x
       const int64_t row = c.m0 + (x < c.rows ? x : c.rows - 1);
       const int64_t k = kk + 8 * y;
@@ -178,8 +183,8 @@ __device__ __forceinline__ const uint16_t* src(const BwdArgs& a, const Ctx& c, b
     const uint16_t* w = c.shared ? (op == 0 ? a.w1s : a.w3s) : (op == 0 ? a.w1r : a.w3r);
     return w + seg * F * d + j * d + c.c0 + y;
   } else {
-    // weight gradients: K-row = row 32 kt + x of the group, columns y
-    const int64_t row = static_cast<int64_t>(kBK) * kt + x;
+    // weight gradients: K-row = row BK kt + x of the group, columns y
+    const int64_t row = static_cast<int64_t>(Cfg<MODE>::BK) * kt + x;
     if (row >= c.rows) return a.zero;
     const int s = c.shared ? c.g - a.n_r : 0;
     if constexpr (MODE == kDw13) {
@@ -211,30 +216,31 @@ __device__ __forceinline__ void dma16(const void* gptr, const unsigned char* lds
   asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(gptr), "s"(m0) : "memory");
 }
 
-// Loads of K-step kt into one stage: each operand's 8 KB tile is 512 16-byte slots; wave
-// w fills slots 128 w .. 128 w + 127 with two instructions (slot 128 w + 64 i + lane).
-// The lane picks the global chunk whose swizzled LDS position is its slot.
+// Loads of K-step kt into one stage: each operand's tile is 16 BK 16-byte slots; wave w
+// fills its quarter with BK / 16 instructions (slot 4 BK w + 64 i + lane). The lane picks
+// the global chunk whose swizzled LDS position is its slot.
 template <int MODE>
 __device__ __forceinline__ void dma_step(const BwdArgs& a, const Ctx& c, int kt, unsigned char* stage, int w,
                                          int lane) {
-  constexpr int NA = Cfg<MODE>::NA, NB = Cfg<MODE>::NB;
+  constexpr int NA = Cfg<MODE>::NA, NB = Cfg<MODE>::NB, BK = Cfg<MODE>::BK;
+  constexpr int kTile = kBT * BK * 2;
 #pragma unroll
   for (int op = 0; op < NA + NB; ++op) {
     const bool km = op < NA ? Cfg<MODE>::a_km : Cfg<MODE>::b_km(op - NA);
 #pragma unroll
-    for (int i = 0; i < 2; ++i) {
-      const int slot = 128 * w + 64 * i + lane;
+    for (int i = 0; i < BK / 16; ++i) {
+      const int slot = 4 * BK * w + 64 * i + lane;
       int x, y;
       if (km) {  // slot = 16 k + 4 (unit ^ (k & 3)) + 16-byte piece of the unit
         x = slot / 16;
         const int ws = slot % 16;
         y = ((((ws / 4) ^ x) & 3) * 32) + (ws % 4) * 8;
-      } else {  // slot = 4 r + (chunk ^ ((r >> 2) & 3))
-        x = slot / 4;
-        y = (slot % 4) ^ ((x >> 2) & 3);
+      } else {  // slot = (BK / 8) r + (chunk ^ swizzle(r))
+        x = slot / (BK / 8);
+        y = (slot % (BK / 8)) ^ kc_swz<BK>(x);
       }
       dma16(src<MODE>(a, c, op < NA, op < NA ? op : op - NA, x, y, kt),
-            stage + op * kTileBytes + (128 * w + 64 * i) * 16);
+            stage + op * kTile + (4 * BK * w + 64 * i) * 16);
     }
   }
 }
@@ -252,23 +258,24 @@ __device__ __forceinline__ void ring_wait() {
 template <int MODE>
 __device__ __forceinline__ void compute(const unsigned char* base, f32x16 (&acc)[Cfg<MODE>::NACC][2][2], int wm,
                                         int wn, int lane) {
-  constexpr int NA = Cfg<MODE>::NA, NB = Cfg<MODE>::NB;
+  constexpr int NA = Cfg<MODE>::NA, NB = Cfg<MODE>::NB, BK = Cfg<MODE>::BK;
+  constexpr int kTile = kBT * BK * 2;
 #pragma unroll
-  for (int s = 0; s < 2; ++s) {
+  for (int s = 0; s < BK / 16; ++s) {
     bf16x8 fa[NA][2], fb[NB][2];
 #pragma unroll
     for (int op = 0; op < NA; ++op)
 #pragma unroll
       for (int mb = 0; mb < 2; ++mb) {
-        const unsigned char* t = base + op * kTileBytes;
-        fa[op][mb] = Cfg<MODE>::a_km ? frag_km(t, 64 * wm + 32 * mb, s, lane) : frag_kc(t, 64 * wm + 32 * mb, s, lane);
+        const unsigned char* t = base + op * kTile;
+        fa[op][mb] = Cfg<MODE>::a_km ? frag_km(t, 64 * wm + 32 * mb, s, lane) : frag_kc<BK>(t, 64 * wm + 32 * mb, s, lane);
       }
 #pragma unroll
     for (int op = 0; op < NB; ++op)
 #pragma unroll
       for (int nb = 0; nb < 2; ++nb) {
-        const unsigned char* t = base + (NA + op) * kTileBytes;
-        fb[op][nb] = Cfg<MODE>::b_km(op) ? frag_km(t, 64 * wn + 32 * nb, s, lane) : frag_kc(t, 64 * wn + 32 * nb, s, lane);
+        const unsigned char* t = base + (NA + op) * kTile;
+        fb[op][nb] = Cfg<MODE>::b_km(op) ? frag_km(t, 64 * wn + 32 * nb, s, lane) : frag_kc<BK>(t, 64 * wn + 32 * nb, s, lane);
       }
 #pragma unroll
     for (int mb = 0; mb < 2; ++mb)
@@ -296,12 +303,14 @@ __device__ __forceinline__ void compute(const unsigned char* base, f32x16 (&acc)
 template <int MODE>
 __global__ __launch_bounds__(kThr, Cfg<MODE>::kOcc) void ffn_bwd_kernel(BwdArgs a) {
   constexpr int NA = Cfg<MODE>::NA, NB = Cfg<MODE>::NB, NACC = Cfg<MODE>::NACC;
-  constexpr int NST = Cfg<MODE>::NST;
-  constexpr int kStage = (NA + NB) * kTileBytes;
-  constexpr int ND = (NA + NB) * 2;  // loads per wave per K-step
+  constexpr int NST = Cfg<MODE>::NST, BK = Cfg<MODE>::BK;
+  constexpr int kStage = (NA + NB) * kBT * BK * 2;
+  constexpr int ND = (NA + NB) * BK / 16;  // loads per wave per K-step
   __shared__ __align__(16) unsigned char lds[NST * kStage];
-  __shared__ int sh[2];
-  __shared__ int soff[257];
+  // the tile decoder's scratch lives in the last stage, which no load touches before the
+  // ring's first barrier
+  int* sh = reinterpret_cast<int*>(lds + (NST - 1) * kStage);
+  int* soff = sh + 2;
   const int lane = threadIdx.x % kWave;
   const int w = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
   const int wm = w / 2, wn = w % 2;
@@ -310,9 +319,9 @@ __global__ __launch_bounds__(kThr, Cfg<MODE>::kOcc) void ffn_bwd_kernel(BwdArgs 
   if constexpr (MODE == kGateUp || MODE == kDx) {
     if (!decode_row_tile(a, MODE, blockIdx.x, c, sh, soff)) return;
     if constexpr (MODE == kGateUp)
-      c.nk = a.d / kBK;
+      c.nk = a.d / BK;
     else
-      c.nk = (c.shared ? a.n_s * a.F : a.F) / kBK;
+      c.nk = (c.shared ? a.n_s * a.F : a.F) / BK;
   } else {
     // per group: (M / 128) x (N / 128) tiles; M = d_ff, N = d (kDw13) or M = d, N = d_ff
     const int mt = (MODE == kDw13 ? a.F : a.d) / kBT, nt = (MODE == kDw13 ? a.d : a.F) / kBT;
@@ -324,7 +333,7 @@ __global__ __launch_bounds__(kThr, Cfg<MODE>::kOcc) void ffn_bwd_kernel(BwdArgs 
     c.shared = c.g >= a.n_r;
     c.row0 = c.shared ? 0 : a.offset[c.g];
     c.rows = c.shared ? static_cast<int>(a.T) : a.offset[c.g + 1] - a.offset[c.g];
-    c.nk = (c.rows + kBK - 1) / kBK;
+    c.nk = (c.rows + BK - 1) / BK;
   }
 
   f32x16 acc[NACC][2][2];
