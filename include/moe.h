@@ -197,7 +197,7 @@ moe_status moe_pack_weights(const moe_shape* shape, int32_t matrix, int64_t n_ex
  * piecewise constant, and the bias only selects, so it has no gradient). Gradients are
  * bf16 ("gradients in BF16", quantisation section of deepseekmodel.com): GEMM operands
  * bf16, fp32 accumulation, each gradient rounded once. Needs act = ffn = MOE_BF16, the
- * ROWS weight layout, d % 128 == 0 and d_ff % 128 == 0 (else MOE_ERR_UNSUPPORTED).
+ * ROWS weight layout, d % 256 == 0 and d_ff % 128 == 0 (else MOE_ERR_UNSUPPORTED).
  * The order of the three calls: moe_combine_backward, moe_grouped_ffn_backward,
  * moe_route_backward. */
 

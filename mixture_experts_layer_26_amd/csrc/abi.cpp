@@ -123,7 +123,7 @@ FfnWorkspace ffn_workspace(const moe_shape* s) {
 
 // Backward: shapes it runs (bf16, row-major weights, 128-multiples) and its workspaces.
 bool backward_shape(const moe_shape* s) {
-  return s->act == MOE_BF16 && s->ffn == MOE_BF16 && s->d % 128 == 0 && s->d_ff % 128 == 0 && s->top_k <= 16;
+  return s->act == MOE_BF16 && s->ffn == MOE_BF16 && s->d % 256 == 0 && s->d_ff % 128 == 0 && s->top_k <= 16;
 }
 
 struct BwdWorkspace {

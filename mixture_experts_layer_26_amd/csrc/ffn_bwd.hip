@@ -6,21 +6,25 @@
 // gradient dY, a = X W1^T, v = X W3^T, h = SiLU(a) v and y = h W2^T:
 //   dh = dY W2,  da = dh v SiLU'(a),  dv = dh SiLU(a),  dX = da W1 + dv W3,
 //   dW1 = da^T X,  dW3 = dv^T X,  dW2 = dY^T h.
-// Four launches, each a grid of 128 x 128 output tiles on 4 waves (64 x 64 each, four
-// v_mfma_f32_32x32x16_bf16 tiles per product), K in steps of 32 through a ring of LDS
-// stages filled by global_load_lds_dwordx4 (no staging registers):
-//   kGateUp: rows x d_ff tiles, K = d: a, v and dh in three accumulators; the epilogue
-//            forms h (as the forward does), da and dv and stores them in bf16.
-//   kDx:     rows x d tiles, K = d_ff (the shared experts' K ranges one after another):
-//            dX = da W1 + dv W3 in one accumulator.
-//   kDw13:   d_ff x d tiles per expert, K = the expert's rows: dW1 and dW3.
-//   kDw2:    d x d_ff tiles per expert, K = the expert's rows: dW2.
+// Four launches, each a grid of output tiles (v_mfma_f32_32x32x16_bf16, each wave a grid
+// of 32 x 32 blocks), K through a ring of LDS stages filled by global_load_lds_dwordx4
+// (no staging registers):
+//   kGateUp: 128 rows x 128 d_ff tiles on 4 waves, K = d in steps of 64: a, v and dh in
+//            three accumulators; the epilogue forms h (as the forward does), da and dv
+//            and stores them in bf16.
+//   kDx:     256 rows x 256 d tiles on 8 waves, K = d_ff in steps of 32 (the shared
+//            experts' K ranges one after another): dX = da W1 + dv W3.
+//   kDw13:   128 d_ff x 128 d tiles per expert on 4 waves, K = the expert's rows: dW1, dW3
+//            (two workgroups per CU hide the short K loops' ends better than one of 8 waves).
+//   kDw2:    256 d x 128 d_ff tiles per expert on 8 waves, K = the expert's rows: dW2.
+// The tiles are as large as the accumulators allow: FLOP per staged byte is what bounds
+// these loops (the L1 keeps a fixed number of line requests in flight).
 // The routed rows of X are read from a sorted copy of u (gathered once per call), so no
 // index lookups sit in the K loops.
 // Operands whose K is contiguous in memory (X, dY, da, dv in kGateUp/kDx, the rows of
-// W1/W3 in kGateUp) are staged as [rows][32 k] and read with ds_read_b128. Operands
+// W1/W3 in kGateUp) are staged as [rows][BK k] and read with ds_read_b128. Operands
 // whose K runs across rows (W2 in kGateUp, W1/W3 in kDx, everything in the weight
-// gradients) are staged as they lie, [32 k][128 columns], and read with
+// gradients) are staged as they lie, [BK k][columns], and read with
 // ds_read_b64_tr_b16, which hands each lane four consecutive k of one column: within
 // 16 lanes, lane i receives column i of the 4 x 16 block whose rows the lanes'
 // addresses name (lane j points at row j / 4, columns 4 (j % 4) .. + 3). Two such reads
@@ -32,38 +36,50 @@ namespace moe {
 
 namespace {
 
-constexpr int kBT = 128;                 // tile rows and columns
-constexpr int kThr = 256;                // 4 waves
+constexpr int kMaxThreads = 512;
 
 enum { kGateUp = 0, kDx = 1, kDw13 = 2, kDw2 = 3 };
 
-// operands per mode: A operands (M side), B operands (N side); K-major flags
+// Per mode: NA A operands (M side) and NB B operands (N side) with their K-major flags;
+// NACC accumulators; a WM x WN grid of waves, each NMB x NNB blocks of 32 x 32, so the
+// tile is TM = 32 WM NMB rows by TN = 32 WN NNB columns; kOcc: waves per SIMD the
+// register budget is held to; NST: LDS stages in the load ring (NST - 1 K-steps in
+// flight); BK: K per step. Operands whose K runs along their rows take whole 128-byte
+// lines per row with BK = 64; with BK = 32 each line is requested twice, a step apart.
 template <int MODE> struct Cfg;
-// kOcc: waves per SIMD the register budget is held to (two workgroups per CU overlap one
-// tile's epilogue with another's K loop where the accumulators allow it); NST: LDS stages
-// in the load ring (NST - 1 K-steps in flight), as many as the LDS of kOcc workgroups holds;
-// BK: K per step. Operands whose K runs along their rows take whole 128-byte lines per row
-// with BK = 64; with BK = 32 each line is requested twice, a step apart.
 template <> struct Cfg<kGateUp> {  // A: X, dY (K-contiguous); B: W1, W3 (K-contig.), W2 (K-major)
-  static constexpr int NA = 2, NB = 3, NACC = 3, kOcc = 1, NST = 2, BK = 64;
+  static constexpr int NA = 2, NB = 3, NACC = 3, WM = 2, WN = 2, NMB = 2, NNB = 2, kOcc = 1, NST = 2, BK = 64;
   static constexpr bool a_km = false;
   static constexpr bool b_km(int j) { return j == 2; }
 };
 template <> struct Cfg<kDx> {  // A: da, dv (K-contiguous); B: W1, W3 (K-major)
-  static constexpr int NA = 2, NB = 2, NACC = 1, kOcc = 2, NST = 2, BK = 32;
+  static constexpr int NA = 2, NB = 2, NACC = 1, WM = 2, WN = 4, NMB = 4, NNB = 2, kOcc = 2, NST = 2, BK = 32;
   static constexpr bool a_km = false;
   static constexpr bool b_km(int) { return true; }
 };
 template <> struct Cfg<kDw13> {  // A: da, dv; B: X (all K-major)
-  static constexpr int NA = 2, NB = 1, NACC = 2, kOcc = 2, NST = 3, BK = 32;
+  static constexpr int NA = 2, NB = 1, NACC = 2, WM = 2, WN = 2, NMB = 2, NNB = 2, kOcc = 2, NST = 3, BK = 32;
   static constexpr bool a_km = true;
   static constexpr bool b_km(int) { return true; }
 };
 template <> struct Cfg<kDw2> {  // A: dY; B: h (K-major)
-  static constexpr int NA = 1, NB = 1, NACC = 1, kOcc = 2, NST = 3, BK = 32;
+  static constexpr int NA = 1, NB = 1, NACC = 1, WM = 4, WN = 2, NMB = 2, NNB = 2, kOcc = 2, NST = 3, BK = 32;
   static constexpr bool a_km = true;
   static constexpr bool b_km(int) { return true; }
 };
+template <int MODE> constexpr int kWaves = Cfg<MODE>::WM * Cfg<MODE>::WN;
+template <int MODE> constexpr int kTM = 32 * Cfg<MODE>::WM * Cfg<MODE>::NMB;
+template <int MODE> constexpr int kTN = 32 * Cfg<MODE>::WN * Cfg<MODE>::NNB;
+// bytes of operand op's tile in one stage, and its offset in the stage
+template <int MODE> constexpr int op_bytes(int op) {
+  return (op < Cfg<MODE>::NA ? kTM<MODE> : kTN<MODE>) * Cfg<MODE>::BK * 2;
+}
+template <int MODE> constexpr int op_offset(int op) {
+  int o = 0;
+  for (int i = 0; i < op; ++i) o += op_bytes<MODE>(i);
+  return o;
+}
+template <int MODE> constexpr int kStageBytes = op_offset<MODE>(Cfg<MODE>::NA + Cfg<MODE>::NB);
 
 // LDS offsets. K-contiguous tile [128 rows][BK k]: 2 BK-byte rows; 16-byte chunk c of row r
 // at chunk c ^ ((r >> 2) & 3) (BK = 32) or c ^ ((r >> 1) & 7) (BK = 64), so the 32 rows of a
@@ -72,9 +88,10 @@ template <int BK>
 __device__ __forceinline__ int kc_swz(int r) { return BK == 32 ? (r >> 2) & 3 : (r >> 1) & 7; }
 template <int BK>
 __device__ __forceinline__ int kc_off(int r, int c) { return r * (2 * BK) + ((c ^ kc_swz<BK>(r)) << 4); }
-// K-major tile [BK k][128 columns]: 256-byte rows, 64-byte unit q of row k at q ^ (k & 3),
+// K-major tile [BK k][W columns]: RB = 2 W-byte rows, 64-byte unit q of row k at q ^ (k & 3),
 // so the 4 rows of one transposed read fall in different banks.
-__device__ __forceinline__ int km_off(int k, int byte) { return k * 256 + ((((byte >> 6) ^ k) & 3) << 6) + (byte & 63); }
+template <int RB>
+__device__ __forceinline__ int km_off(int k, int byte) { return k * RB + ((((byte >> 6) ^ (k & 3))) << 6) + (byte & 63); }
 
 typedef short v4s __attribute__((ext_vector_type(4)));
 
@@ -83,14 +100,15 @@ template <int BK>
 __device__ __forceinline__ bf16x8 frag_kc(const unsigned char* t, int r0, int s, int lane) {
   return *reinterpret_cast<const bf16x8*>(t + kc_off<BK>(r0 + lane % 32, 2 * s + lane / 32));
 }
+template <int RB>
 __device__ __forceinline__ bf16x8 frag_km(const unsigned char* t, int c0, int s, int lane) {
   const int g = lane / 16, j = lane % 16;
   const int col = c0 + 16 * (g % 2) + 4 * (j % 4);
   const int k = 16 * s + 8 * (g / 2) + j / 4;
   typedef __attribute__((address_space(3))) v4s lds_v4s;  // the tile lives in LDS
   unsigned char* p = const_cast<unsigned char*>(t);
-  const v4s lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4s*)(p + km_off(k, 2 * col)));
-  const v4s hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4s*)(p + km_off(k + 4, 2 * col)));
+  const v4s lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4s*)(p + km_off<RB>(k, 2 * col)));
+  const v4s hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4s*)(p + km_off<RB>(k + 4, 2 * col)));
   typedef short v8s __attribute__((ext_vector_type(8)));
   const v8s both = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
   return __builtin_bit_cast(bf16x8, both);
@@ -112,16 +130,18 @@ struct Ctx {
 // (kGateUp: each shared expert; kDx: one group for all of them). The offsets are copied
 // to LDS (soff, n_r + 1 entries) and one thread walks the groups. Returns false past
 // the last tile.
-__device__ bool decode_row_tile(const BwdArgs& a, int mode, int id, Ctx& c, int* sh, int* soff) {
-  const int nsg = a.n_s == 0 ? 0 : (mode == kGateUp ? a.n_s : 1);
-  const int ntn = (mode == kGateUp ? a.F : a.d) / kBT;
-  for (int i = threadIdx.x; i <= a.n_r; i += kThr) soff[i] = a.offset[i];
+template <int MODE>
+__device__ bool decode_row_tile(const BwdArgs& a, int id, Ctx& c, int* sh, int* soff) {
+  constexpr int TM = kTM<MODE>, TN = kTN<MODE>;
+  const int nsg = a.n_s == 0 ? 0 : (MODE == kGateUp ? a.n_s : 1);
+  const int ntn = (MODE == kGateUp ? a.F : a.d) / TN;
+  for (int i = threadIdx.x; i <= a.n_r; i += blockDim.x) soff[i] = a.offset[i];
   __syncthreads();
   if (threadIdx.x == 0) {
     int base = 0, found = -1, rb = 0;
     for (int g = 0; g < a.n_r + nsg && found < 0; ++g) {
       const int r = g < a.n_r ? soff[g + 1] - soff[g] : static_cast<int>(a.T);
-      const int n = ((r + kBT - 1) / kBT) * ntn;
+      const int n = ((r + TM - 1) / TM) * ntn;
       if (id < base + n) {
         found = g;
         rb = id - base;
@@ -138,9 +158,9 @@ __device__ bool decode_row_tile(const BwdArgs& a, int mode, int id, Ctx& c, int*
   c.shared = g >= a.n_r;
   const int r = c.shared ? static_cast<int>(a.T) : soff[g + 1] - soff[g];
   c.row0 = c.shared ? 0 : soff[g];
-  c.m0 = static_cast<int64_t>(rb / ntn) * kBT;
-  c.c0 = (rb % ntn) * kBT;
-  c.rows = r - static_cast<int>(c.m0) < kBT ? r - static_cast<int>(c.m0) : kBT;
+  c.m0 = static_cast<int64_t>(rb / ntn) * TM;
+  c.c0 = (rb % ntn) * TN;
+  c.rows = r - static_cast<int>(c.m0) < TM ? r - static_cast<int>(c.m0) : TM;
   return true;
 }
 
@@ -216,33 +236,42 @@ __device__ __forceinline__ void dma16(const void* gptr, const unsigned char* lds
   asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(gptr), "s"(m0) : "memory");
 }
 
-// Loads of K-step kt into one stage: each operand's tile is 16 BK 16-byte slots; wave w
-// fills its quarter with BK / 16 instructions (slot 4 BK w + 64 i + lane). The lane picks
-// the global chunk whose swizzled LDS position is its slot.
+// Loads of K-step kt into one stage: each operand's tile is split evenly over the waves,
+// 64 16-byte slots per instruction (slot = per-wave share * w + 64 i + lane). The lane
+// picks the global chunk whose swizzled LDS position is its slot.
 template <int MODE>
 __device__ __forceinline__ void dma_step(const BwdArgs& a, const Ctx& c, int kt, unsigned char* stage, int w,
                                          int lane) {
-  constexpr int NA = Cfg<MODE>::NA, NB = Cfg<MODE>::NB, BK = Cfg<MODE>::BK;
-  constexpr int kTile = kBT * BK * 2;
+  constexpr int NA = Cfg<MODE>::NA, NB = Cfg<MODE>::NB, BK = Cfg<MODE>::BK, NW = kWaves<MODE>;
 #pragma unroll
   for (int op = 0; op < NA + NB; ++op) {
     const bool km = op < NA ? Cfg<MODE>::a_km : Cfg<MODE>::b_km(op - NA);
+    const int width = op < NA ? kTM<MODE> : kTN<MODE>;  // tile rows (K-contig.) or columns (K-major)
+    const int per_wave = op_bytes<MODE>(op) / 16 / NW;   // slots
 #pragma unroll
-    for (int i = 0; i < BK / 16; ++i) {
-      const int slot = 4 * BK * w + 64 * i + lane;
+    for (int i = 0; i < per_wave / 64; ++i) {
+      const int slot = per_wave * w + 64 * i + lane;
       int x, y;
-      if (km) {  // slot = 16 k + 4 (unit ^ (k & 3)) + 16-byte piece of the unit
-        x = slot / 16;
-        const int ws = slot % 16;
-        y = ((((ws / 4) ^ x) & 3) * 32) + (ws % 4) * 8;
+      if (km) {  // slot = (width / 8) k + 4 (unit ^ (k & 3)) + 16-byte piece of the unit
+        const int spr = width / 8;
+        x = slot / spr;
+        const int ws = slot % spr;
+        y = (((ws / 4) ^ (x & 3)) * 32) + (ws % 4) * 8;
       } else {  // slot = (BK / 8) r + (chunk ^ swizzle(r))
         x = slot / (BK / 8);
         y = (slot % (BK / 8)) ^ kc_swz<BK>(x);
       }
       dma16(src<MODE>(a, c, op < NA, op < NA ? op : op - NA, x, y, kt),
-            stage + op * kTile + (4 * BK * w + 64 * i) * 16);
+            stage + op_offset<MODE>(op) + (per_wave * w + 64 * i) * 16);
     }
   }
+}
+
+template <int MODE>
+constexpr int loads_per_step() {
+  int n = 0;
+  for (int op = 0; op < Cfg<MODE>::NA + Cfg<MODE>::NB; ++op) n += op_bytes<MODE>(op) / 16 / kWaves<MODE> / 64;
+  return n;
 }
 
 // Wait until this wave's loads of the oldest stage in flight have landed (the N loads
@@ -256,31 +285,36 @@ __device__ __forceinline__ void ring_wait() {
 }
 
 template <int MODE>
-__device__ __forceinline__ void compute(const unsigned char* base, f32x16 (&acc)[Cfg<MODE>::NACC][2][2], int wm,
+__device__ __forceinline__ void compute(const unsigned char* base,
+                                        f32x16 (&acc)[Cfg<MODE>::NACC][Cfg<MODE>::NMB][Cfg<MODE>::NNB], int wm,
                                         int wn, int lane) {
   constexpr int NA = Cfg<MODE>::NA, NB = Cfg<MODE>::NB, BK = Cfg<MODE>::BK;
-  constexpr int kTile = kBT * BK * 2;
+  constexpr int NMB = Cfg<MODE>::NMB, NNB = Cfg<MODE>::NNB;
+  constexpr int TM = kTM<MODE>, TN = kTN<MODE>;
+  const int r0 = (TM / Cfg<MODE>::WM) * wm, n0 = (TN / Cfg<MODE>::WN) * wn;
 #pragma unroll
   for (int s = 0; s < BK / 16; ++s) {
-    bf16x8 fa[NA][2], fb[NB][2];
+    bf16x8 fa[NA][NMB], fb[NB][NNB];
 #pragma unroll
     for (int op = 0; op < NA; ++op)
 #pragma unroll
-      for (int mb = 0; mb < 2; ++mb) {
-        const unsigned char* t = base + op * kTile;
-        fa[op][mb] = Cfg<MODE>::a_km ? frag_km(t, 64 * wm + 32 * mb, s, lane) : frag_kc<BK>(t, 64 * wm + 32 * mb, s, lane);
+      for (int mb = 0; mb < NMB; ++mb) {
+        const unsigned char* t = base + op_offset<MODE>(op);
+        fa[op][mb] = Cfg<MODE>::a_km ? frag_km<2 * TM>(t, r0 + 32 * mb, s, lane)
+                                     : frag_kc<BK>(t, r0 + 32 * mb, s, lane);
       }
 #pragma unroll
     for (int op = 0; op < NB; ++op)
 #pragma unroll
-      for (int nb = 0; nb < 2; ++nb) {
-        const unsigned char* t = base + (NA + op) * kTile;
-        fb[op][nb] = Cfg<MODE>::b_km(op) ? frag_km(t, 64 * wn + 32 * nb, s, lane) : frag_kc<BK>(t, 64 * wn + 32 * nb, s, lane);
+      for (int nb = 0; nb < NNB; ++nb) {
+        const unsigned char* t = base + op_offset<MODE>(NA + op);
+        fb[op][nb] = Cfg<MODE>::b_km(op) ? frag_km<2 * TN>(t, n0 + 32 * nb, s, lane)
+                                         : frag_kc<BK>(t, n0 + 32 * nb, s, lane);
       }
 #pragma unroll
-    for (int mb = 0; mb < 2; ++mb)
+    for (int mb = 0; mb < NMB; ++mb)
 #pragma unroll
-      for (int nb = 0; nb < 2; ++nb) {
+      for (int nb = 0; nb < NNB; ++nb) {
         // the n-side fragment goes first, so each lane's accumulator holds 4 consecutive
         // output columns of one output row (see the epilogue)
         if constexpr (MODE == kGateUp) {
@@ -301,11 +335,12 @@ __device__ __forceinline__ void compute(const unsigned char* base, f32x16 (&acc)
 }
 
 template <int MODE>
-__global__ __launch_bounds__(kThr, Cfg<MODE>::kOcc) void ffn_bwd_kernel(BwdArgs a) {
-  constexpr int NA = Cfg<MODE>::NA, NB = Cfg<MODE>::NB, NACC = Cfg<MODE>::NACC;
+__global__ __launch_bounds__(64 * kWaves<MODE>, Cfg<MODE>::kOcc) void ffn_bwd_kernel(BwdArgs a) {
+  constexpr int NACC = Cfg<MODE>::NACC, NMB = Cfg<MODE>::NMB, NNB = Cfg<MODE>::NNB;
   constexpr int NST = Cfg<MODE>::NST, BK = Cfg<MODE>::BK;
-  constexpr int kStage = (NA + NB) * kBT * BK * 2;
-  constexpr int ND = (NA + NB) * BK / 16;  // loads per wave per K-step
+  constexpr int TM = kTM<MODE>, TN = kTN<MODE>;
+  constexpr int kStage = kStageBytes<MODE>;
+  constexpr int ND = loads_per_step<MODE>();  // loads per wave per K-step
   __shared__ __align__(16) unsigned char lds[NST * kStage];
   // the tile decoder's scratch lives in the last stage, which no load touches before the
   // ring's first barrier
@@ -313,36 +348,36 @@ __global__ __launch_bounds__(kThr, Cfg<MODE>::kOcc) void ffn_bwd_kernel(BwdArgs 
   int* soff = sh + 2;
   const int lane = threadIdx.x % kWave;
   const int w = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
-  const int wm = w / 2, wn = w % 2;
+  const int wm = w / Cfg<MODE>::WN, wn = w % Cfg<MODE>::WN;
 
   Ctx c{};
   if constexpr (MODE == kGateUp || MODE == kDx) {
-    if (!decode_row_tile(a, MODE, blockIdx.x, c, sh, soff)) return;
+    if (!decode_row_tile<MODE>(a, blockIdx.x, c, sh, soff)) return;
     if constexpr (MODE == kGateUp)
       c.nk = a.d / BK;
     else
       c.nk = (c.shared ? a.n_s * a.F : a.F) / BK;
   } else {
-    // per group: (M / 128) x (N / 128) tiles; M = d_ff, N = d (kDw13) or M = d, N = d_ff
-    const int mt = (MODE == kDw13 ? a.F : a.d) / kBT, nt = (MODE == kDw13 ? a.d : a.F) / kBT;
+    // per group: (M / TM) x (N / TN) tiles; M = d_ff, N = d (kDw13) or M = d, N = d_ff
+    const int mt = (MODE == kDw13 ? a.F : a.d) / TM, nt = (MODE == kDw13 ? a.d : a.F) / TN;
     const int id = blockIdx.x;
     c.g = id / (mt * nt);
     const int rest = id % (mt * nt);
-    c.mo = (rest / nt) * kBT;
-    c.no = (rest % nt) * kBT;
+    c.mo = (rest / nt) * TM;
+    c.no = (rest % nt) * TN;
     c.shared = c.g >= a.n_r;
     c.row0 = c.shared ? 0 : a.offset[c.g];
     c.rows = c.shared ? static_cast<int>(a.T) : a.offset[c.g + 1] - a.offset[c.g];
     c.nk = (c.rows + BK - 1) / BK;
   }
 
-  f32x16 acc[NACC][2][2];
+  f32x16 acc[NACC][NMB][NNB];
 #pragma unroll
   for (int x = 0; x < NACC; ++x)
 #pragma unroll
-    for (int mb = 0; mb < 2; ++mb)
+    for (int mb = 0; mb < NMB; ++mb)
 #pragma unroll
-      for (int nb = 0; nb < 2; ++nb)
+      for (int nb = 0; nb < NNB; ++nb)
 #pragma unroll
         for (int v = 0; v < 16; ++v) acc[x][mb][nb][v] = 0.0f;
 
@@ -367,13 +402,13 @@ __global__ __launch_bounds__(kThr, Cfg<MODE>::kOcc) void ffn_bwd_kernel(BwdArgs 
   // 32-column block, i.e. 4 consecutive columns per group of 4 v: one 8-byte store each.
   const int m_in = lane % 32;
 #pragma unroll
-  for (int mb = 0; mb < 2; ++mb)
+  for (int mb = 0; mb < NMB; ++mb)
 #pragma unroll
-    for (int nb = 0; nb < 2; ++nb)
+    for (int nb = 0; nb < NNB; ++nb)
 #pragma unroll
       for (int p = 0; p < 4; ++p) {
-        const int r = 64 * wm + 32 * mb + m_in;
-        const int n = 64 * wn + 32 * nb + 8 * p + 4 * (lane / 32);
+        const int r = (TM / Cfg<MODE>::WM) * wm + 32 * mb + m_in;
+        const int n = (TN / Cfg<MODE>::WN) * wn + 32 * nb + 8 * p + 4 * (lane / 32);
         if constexpr (MODE == kGateUp) {
           if (r >= c.rows) continue;
           float hv[4], dav[4], dvv[4];
@@ -452,9 +487,10 @@ __global__ __launch_bounds__(256) void gather_rows_kernel(const uint16_t* __rest
 
 int64_t bwd_row_tiles(int mode, int64_t T, int K, int n_r, int n_s, int d, int F) {
   const int64_t P = T * K;
-  const int64_t ntn = (mode == 0 ? F : d) / kBT;
+  const int64_t TM = mode == 0 ? kTM<kGateUp> : kTM<kDx>;
+  const int64_t ntn = mode == 0 ? F / kTN<kGateUp> : d / kTN<kDx>;
   const int64_t nsg = n_s == 0 ? 0 : (mode == 0 ? n_s : 1);
-  return ((P + kBT - 1) / kBT + n_r + nsg * ((T + kBT - 1) / kBT)) * ntn;
+  return ((P + TM - 1) / TM + n_r + nsg * ((T + TM - 1) / TM)) * ntn;
 }
 
 hipError_t launch_ffn_backward(const BwdArgs& a, hipStream_t stream) {
@@ -462,20 +498,20 @@ hipError_t launch_ffn_backward(const BwdArgs& a, hipStream_t stream) {
   const unsigned gg = static_cast<unsigned>(chunks / 256 + 1 < 8192 ? chunks / 256 + 1 : 8192);
   hipLaunchKernelGGL(gather_rows_kernel, dim3(gg), dim3(256), 0, stream, a.u, a.sorted_token, a.xs, a.zero,
                      a.T * a.K, a.d);
-  hipError_t err0 = hipGetLastError();
-  if (err0 != hipSuccess) return err0;
-  const unsigned g1 = static_cast<unsigned>(bwd_row_tiles(0, a.T, a.K, a.n_r, a.n_s, a.d, a.F));
-  hipLaunchKernelGGL(ffn_bwd_kernel<kGateUp>, dim3(g1), dim3(kThr), 0, stream, a);
   hipError_t err = hipGetLastError();
   if (err != hipSuccess) return err;
+  const unsigned g1 = static_cast<unsigned>(bwd_row_tiles(0, a.T, a.K, a.n_r, a.n_s, a.d, a.F));
+  hipLaunchKernelGGL(ffn_bwd_kernel<kGateUp>, dim3(g1), dim3(64 * kWaves<kGateUp>), 0, stream, a);
+  if ((err = hipGetLastError()) != hipSuccess) return err;
   const unsigned g2 = static_cast<unsigned>(bwd_row_tiles(1, a.T, a.K, a.n_r, a.n_s, a.d, a.F));
-  hipLaunchKernelGGL(ffn_bwd_kernel<kDx>, dim3(g2), dim3(kThr), 0, stream, a);
+  hipLaunchKernelGGL(ffn_bwd_kernel<kDx>, dim3(g2), dim3(64 * kWaves<kDx>), 0, stream, a);
   if ((err = hipGetLastError()) != hipSuccess) return err;
-  const unsigned groups = static_cast<unsigned>(a.n_r + a.n_s);
-  const unsigned tiles = static_cast<unsigned>((a.F / kBT) * (a.d / kBT));
-  hipLaunchKernelGGL(ffn_bwd_kernel<kDw13>, dim3(groups * tiles), dim3(kThr), 0, stream, a);
+  const int64_t groups = a.n_r + a.n_s;
+  const unsigned g3 = static_cast<unsigned>(groups * (a.F / kTM<kDw13>) * (a.d / kTN<kDw13>));
+  hipLaunchKernelGGL(ffn_bwd_kernel<kDw13>, dim3(g3), dim3(64 * kWaves<kDw13>), 0, stream, a);
   if ((err = hipGetLastError()) != hipSuccess) return err;
-  hipLaunchKernelGGL(ffn_bwd_kernel<kDw2>, dim3(groups * tiles), dim3(kThr), 0, stream, a);
+  const unsigned g4 = static_cast<unsigned>(groups * (a.d / kTM<kDw2>) * (a.F / kTN<kDw2>));
+  hipLaunchKernelGGL(ffn_bwd_kernel<kDw2>, dim3(g4), dim3(64 * kWaves<kDw2>), 0, stream, a);
   return hipGetLastError();
 }
 

@@ -114,7 +114,7 @@ hipError_t launch_quantize_fp8(const void* x, int xt, int64_t rows, int64_t cols
                                int tile_c, uint8_t* q, float* scale, hipStream_t stream);
 
 // ---------------------------------------------------------------------------- backward
-// Grouped SwiGLU backward (bf16, row-major weights; d and d_ff multiples of 128).
+// Grouped SwiGLU backward (bf16, row-major weights; d a multiple of 256, d_ff of 128).
 struct BwdArgs {
   const uint16_t* u;             // [T, d]
   const uint16_t* dout;          // [T, d]: the shared experts' output gradient

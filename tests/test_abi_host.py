@@ -164,12 +164,12 @@ def test_pack_weights_args_rejected():
 
 
 def test_backward_args_rejected():
-    """The backward runs bf16 layers with row-major weights and 128-multiple d, d_ff; every
+    """The backward runs bf16 layers with row-major weights, d % 256 == 0, d_ff % 128 == 0; every
     call below is stopped on the host before any HIP call."""
     lib = abi.load()
     fp32 = _shape()
     bf = _shape(act="bf16", ffn="bf16")
-    odd = _shape(act="bf16", ffn="bf16", d=192)  # d % 128 != 0
+    odd = _shape(act="bf16", ffn="bf16", d=384)  # d % 256 != 0
     fp8 = _shape(act="bf16", ffn="fp8")
     for s in (fp32, odd, fp8):
         assert abi.moe_workspace_bytes(s, abi.MOE_CALL_GROUPED_FFN_BACKWARD) == 0
