@@ -24,7 +24,12 @@
  *    device-to-host copy or synchronisation inside any call.
  *  - Arguments are validated on the host before anything is enqueued; a bad
  *    argument returns MOE_ERR_INVALID_ARG (or MOE_ERR_UNSUPPORTED / MOE_ERR_WORKSPACE)
- *    and touches no memory. Kernels trust the index arrays produced by earlier calls.
+ *    and touches no memory. Kernels trust the index arrays produced by earlier calls,
+ *    unless the environment variable MOE_DEBUG is 1: then every call that takes
+ *    topk_idx, expert_offset, sorted_token or pair_row first checks them on the device
+ *    (in range; offsets from 0 to T*K, non-decreasing), waits for the check (the one
+ *    synchronisation in the library), and returns MOE_ERR_INVALID_ARG without launching
+ *    anything else if one fails.
  *  - Results are deterministic: the same inputs give bit-identical outputs, counts,
  *    permutations and biases on every run (no atomics on any result).
  *  - Row-major layouts throughout; "[A, B]" means A rows of B contiguous elements.

@@ -5,6 +5,7 @@
 
 #include <hip/hip_runtime.h>
 
+#include <cstdlib>
 #include <mutex>
 
 #include "launch.h"
@@ -42,6 +43,25 @@ size_t act_bytes(int dt) { return dt == MOE_F32 ? 4 : 2; }
 hipStream_t as_stream(void* p) { return static_cast<hipStream_t>(p); }
 
 moe_status from_hip(hipError_t e) { return e == hipSuccess ? MOE_OK : MOE_ERR_HIP; }
+
+// MOE_DEBUG=1 (read at every call): index arrays from earlier calls are checked on the
+// device before use; a bad one gives MOE_ERR_INVALID_ARG and nothing else is launched.
+bool debug_on() {
+  const char* e = std::getenv("MOE_DEBUG");
+  return e != nullptr && e[0] == '1';
+}
+
+moe_status debug_check(std::initializer_list<moe::IndexCheck> checks, void* stream) {
+  if (!debug_on()) return MOE_OK;
+  bool bad = false;
+  const hipError_t e = moe::debug_check_indices(checks.begin(), static_cast<int>(checks.size()),
+                                                as_stream(stream), &bad);
+  if (e != hipSuccess) return MOE_ERR_HIP;
+  return bad ? MOE_ERR_INVALID_ARG : MOE_OK;
+}
+
+moe::IndexCheck range(const int32_t* p, int64_t n, int32_t lo, int32_t hi) { return {p, n, lo, hi, false}; }
+moe::IndexCheck offsets(const int32_t* p, int n, int32_t total) { return {p, n, 0, total, true}; }
 
 int grid_for_device() {
   // one persistent workgroup per CU; cached per device
@@ -294,6 +314,8 @@ moe_status moe_dispatch(const moe_shape* s, const int32_t* topk_idx, int32_t* ex
   if (!valid_shape(s) || !topk_idx || !expert_count || !expert_offset || !sorted_token || !pair_row)
     return MOE_ERR_INVALID_ARG;
   if (!ws || ws_bytes < moe_workspace_bytes(s, MOE_CALL_DISPATCH)) return MOE_ERR_WORKSPACE;
+  const int64_t P = s->T * s->top_k;
+  if (moe_status d = debug_check({range(topk_idx, P, 0, s->n_routed)}, stream)) return d;
   return from_hip(moe::launch_dispatch(topk_idx, s->T, s->top_k, s->n_routed,
                                        static_cast<int32_t*>(ws), expert_count, expert_offset,
                                        sorted_token, pair_row, as_stream(stream)));
@@ -322,6 +344,10 @@ moe_status moe_grouped_ffn(const moe_shape* s, const void* u, const int32_t* exp
   hipStream_t st = as_stream(stream);
   unsigned char* wsb = static_cast<unsigned char*>(ws);
   const int64_t P = s->T * s->top_k;
+  if (moe_status d = debug_check({offsets(expert_offset, s->n_routed, static_cast<int32_t>(P)),
+                                  range(sorted_token, P, 0, static_cast<int32_t>(s->T))},
+                                 stream))
+    return d;
 
   if (s->ffn == MOE_F32) {
     const moe_expert_set empty{};
@@ -413,6 +439,9 @@ moe_status moe_combine(const moe_shape* s, const void* u, const void* y_routed,
     return MOE_ERR_INVALID_ARG;
   if (s->n_shared > 0 && !y_shared) return MOE_ERR_INVALID_ARG;
   if (out == u) return MOE_ERR_INVALID_ARG;
+  if (moe_status d = debug_check({range(pair_row, s->T * s->top_k, 0, static_cast<int32_t>(s->T * s->top_k))},
+                                 stream))
+    return d;
   return from_hip(moe::launch_combine(s->act == MOE_BF16 ? 1 : 0, u, y_routed,
                                       s->n_shared > 0 ? y_shared : nullptr, pair_row, topk_gate,
                                       out, s->T, s->d, s->top_k, as_stream(stream)));
@@ -462,6 +491,9 @@ moe_status moe_combine_backward(const moe_shape* s, const void* dout, const void
   if (!valid_shape(s) || !dout || !y_routed || !pair_row || !topk_gate || !dy_routed || !dgate)
     return MOE_ERR_INVALID_ARG;
   if (!backward_shape(s)) return MOE_ERR_UNSUPPORTED;
+  if (moe_status d = debug_check({range(pair_row, s->T * s->top_k, 0, static_cast<int32_t>(s->T * s->top_k))},
+                                 stream))
+    return d;
   return from_hip(moe::launch_combine_backward(dout, y_routed, pair_row, topk_gate, dy_routed, dgate, s->T, s->d,
                                                s->top_k, as_stream(stream)));
 }
@@ -487,6 +519,13 @@ moe_status moe_grouped_ffn_backward(const moe_shape* s, const void* u, const voi
     return MOE_ERR_UNSUPPORTED;
   const BwdWorkspace w = bwd_workspace(s);
   if (!ws || ws_bytes < w.total) return MOE_ERR_WORKSPACE;
+  {
+    const int64_t P = s->T * s->top_k;
+    if (moe_status d = debug_check({offsets(expert_offset, s->n_routed, static_cast<int32_t>(P)),
+                                    range(sorted_token, P, 0, static_cast<int32_t>(s->T))},
+                                   stream))
+      return d;
+  }
   unsigned char* wsb = static_cast<unsigned char*>(ws);
   moe::BwdArgs a{};
   a.u = static_cast<const uint16_t*>(u);
@@ -537,6 +576,14 @@ moe_status moe_route_backward(const moe_shape* s, const void* u, const void* cen
   if (s->n_shared > 0 && !dx_shared) return MOE_ERR_INVALID_ARG;
   if (!backward_shape(s)) return MOE_ERR_UNSUPPORTED;
   if (!ws || ws_bytes < moe_workspace_bytes(s, MOE_CALL_ROUTE_BACKWARD)) return MOE_ERR_WORKSPACE;
+  {
+    const int64_t P = s->T * s->top_k;
+    if (moe_status d = debug_check({range(topk_idx, P, 0, s->n_routed), range(pair_row, P, 0, static_cast<int32_t>(P)),
+                                    offsets(expert_offset, s->n_routed, static_cast<int32_t>(P)),
+                                    range(sorted_token, P, 0, static_cast<int32_t>(s->T))},
+                                   stream))
+      return d;
+  }
   return from_hip(moe::launch_route_backward(s->score == MOE_SCORE_SOFTMAX ? 1 : 0, u, centroids, topk_idx,
                                              topk_gate, dgate, expert_offset, sorted_token, pair_row, dout,
                                              dx_routed, s->n_shared > 0 ? dx_shared : nullptr, du, dcentroids, dz,

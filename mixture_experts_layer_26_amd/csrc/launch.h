@@ -147,4 +147,16 @@ hipError_t launch_route_backward(int score, const void* u, const void* e, const 
                                  const float* dx_shared, void* du, void* de, float* dz, float* dz_sorted,
                                  int64_t T, int d, int n_r, int K, hipStream_t stream);
 
+// ---------------------------------------------------------------------------- MOE_DEBUG
+// One check: every p[i] of n entries in [lo, hi), or (offsets) p[0] == 0, p[n] == hi and
+// p non-decreasing over n + 1 entries.
+struct IndexCheck {
+  const int32_t* p;
+  int64_t n;
+  int32_t lo, hi;
+  bool offsets;
+};
+// Runs the checks on `stream`, waits for them, and sets *bad if any failed.
+hipError_t debug_check_indices(const IndexCheck* checks, int count, hipStream_t stream, bool* bad);
+
 }  // namespace moe
