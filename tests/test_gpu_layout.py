@@ -3,9 +3,10 @@
 moe_pack_weights only reorders bytes: its output is compared bit for bit with torch's
 reshape/permute of the same tensor. The grouped FFN must then give bit-identical
 outputs from either layout: bf16 and FP8 on the mid shape (two shared experts, an odd
-number of 128-wide K-steps in the FP8 down projection) and the skewed decode batch at
-the V3 shape. The row-major path itself is checked against the oracle in
-test_gpu_parity.py and test_gpu_fp8.py.
+number of 128-wide K-steps in the FP8 down projection), the skewed decode batch at the
+V3 shape, and the V3 prefill layer in bf16 and FP8 (the configurations the benchmark
+times). The row-major path itself is checked against the oracle in test_gpu_parity.py
+and test_gpu_fp8.py.
 """
 import pytest
 import torch
@@ -40,7 +41,8 @@ def test_pack_matches_permute(ffn):
 
 
 @pytest.mark.parametrize("base,T,ffn", [("mid_bf16", 512, "bf16"), ("mid_bf16", 512, "fp8"),
-                                        ("v3_decode_skewed", None, "bf16")])
+                                        ("v3_decode_skewed", None, "bf16"), ("v3_prefill_bf16", None, "bf16"),
+                                        ("v3_prefill_bf16", None, "fp8")])
 def test_tiled_layout_bit_identical(base, T, ffn):
     wb = I.WORKLOADS[base]
     w = wb.with_tokens(T) if T is not None else wb
