@@ -17,8 +17,9 @@
 //   kDw13:   128 d_ff x 128 d tiles per expert on 4 waves, K = the expert's rows: dW1, dW3
 //            (two workgroups per CU hide the short K loops' ends better than one of 8 waves).
 //   kDw2:    256 d x 128 d_ff tiles per expert on 8 waves, K = the expert's rows: dW2.
-// The tiles are as large as the accumulators allow: FLOP per staged byte is what bounds
-// these loops (the L1 keeps a fixed number of line requests in flight).
+// The tile shapes trade FLOP per staged byte, which bounds these loops (the L1 keeps a
+// fixed number of line requests in flight), against workgroups per CU, which hide the
+// ends of short K loops.
 // The routed rows of X are read from a sorted copy of u (gathered once per call), so no
 // index lookups sit in the K loops.
 // Operands whose K is contiguous in memory (X, dY, da, dv in kGateUp/kDx, the rows of
@@ -35,8 +36,6 @@
 namespace moe {
 
 namespace {
-
-constexpr int kMaxThreads = 512;
 
 enum { kGateUp = 0, kDx = 1, kDw13 = 2, kDw2 = 3 };
 

@@ -4,6 +4,7 @@ A step is: moe_route -> moe_dispatch -> moe_grouped_ffn -> moe_combine ->
 moe_bias_update, all enqueued on one stream with no host synchronisation. The
 bias is the caller's persistent state; the update feeds the next step's routing
 (DeepSeek-V3 explainer, method section 2: the bias moves at the end of each step).
+`backward` runs the three backward calls for the step just taken.
 """
 from __future__ import annotations
 
