@@ -1,5 +1,6 @@
 /*
- * moe.h - C ABI of the DeepSeekMoE layer forward pass on AMD MI355X (gfx950).
+ * moe.h - C ABI of the DeepSeekMoE layer (forward, bias update, backward) on AMD MI355X
+ * (gfx950).
  *
  * The layer (DeepSeek-V3 explainer, "DeepSeek-V3 テクニカルレポート 論文解説",
  * xyznot.com, method section 2 "DeepSeekMoE with auxiliary-loss-free balancing"):
