@@ -16,6 +16,10 @@ launch stream, and the CPU oracle timed on a bounded sample of the same workload
 moe_grouped_ffn_backward -> moe_route_backward after one forward step, row-major bf16
 weights) and prints its own line, with the roofline of the grouped FFN backward (four
 MFMA launches: 16 d d_ff FLOPs per expert row).
+
+--balance S runs S layer steps over fresh token batches with the bias carried from step
+to step (the end-of-step rule of the method) and prints the max/mean and min/mean expert
+load of every step and the bias drift.
 """
 from __future__ import annotations
 
@@ -50,6 +54,8 @@ def parse():
     p.add_argument("--layout", choices=["tiled", "rows"], default="tiled",
                    help="expert weight layout: tiled (packed once at setup by moe_pack_weights) or row-major")
     p.add_argument("--backward", action="store_true", help="time the layer backward instead")
+    p.add_argument("--balance", type=int, default=0, metavar="S",
+                   help="run S steps over fresh batches and report the expert loads instead")
     p.add_argument("--calibrate-copy", action="store_true",
                    help="also run one plain 1 GiB device copy (the reference for FETCH_SIZE/WRITE_SIZE)")
     return p.parse_args()
@@ -284,6 +290,44 @@ def bench_backward(args):
     print(json.dumps(res), flush=True)
 
 
+def bench_balance(args):
+    """S full layer steps over fresh batches (generator stream batch s), the bias carried on
+    the device; per step the max/mean and min/mean of the expert counts."""
+    import torch
+
+    from mixture_experts_layer_26_amd import inputs as I
+
+    w, dev, L, layout = setup(args.workload, args.layout)
+    bias = dev["b"].clone()
+    b0 = bias.clone()
+    mean = w.T * w.top_k / w.n_routed
+    mx, mn, ms = [], [], []
+    for s in range(1, args.balance + 1):
+        u = torch.from_numpy(I.make_u(w, batch=s).view("int16" if w.act == "bf16" else "float32"))
+        u = (u.view(torch.bfloat16) if w.act == "bf16" else u).cuda()
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        L.step(u, dev["e"], bias, w.gamma)
+        torch.cuda.synchronize()
+        ms.append(1e3 * (time.perf_counter() - t0))
+        c = L.expert_count.cpu().numpy()
+        mx.append(round(float(c.max()) / mean, 4))
+        mn.append(round(float(c.min()) / mean, 4))
+        log(f"[balance] step {s}: max/mean {mx[-1]:.3f} min/mean {mn[-1]:.3f}")
+    drift = float((bias - b0).abs().max())
+    res = {
+        "metric": "aux-loss-free balancing: expert load per step over fresh batches",
+        "workload": w.name, "steps": args.balance, "gamma": w.gamma,
+        "max_over_mean": mx, "min_over_mean": mn,
+        "bias_drift_max": round(drift, 6), "drift_bound": round(args.balance * w.gamma, 6),
+        "ms_per_step": [round(x, 3) for x in ms],
+        "data": "synthetic (seeded Philox/Box-Muller inputs, a fresh token batch per step)",
+        "config": {"workload": w.name, "T": w.T, "d": w.d, "n_routed": w.n_routed, "top_k": w.top_k,
+                   "weights": layout},
+    }
+    print(json.dumps(res), flush=True)
+
+
 def cpu_baseline_backward(w, n_tokens: int):
     """The oracle's backward on the first n tokens: du, dgate, dz (their rows' recompute,
     dh and dx, and the router's gradient); weight-gradient sums are not formed."""
@@ -322,6 +366,9 @@ def main():
 
     if args.backward:
         bench_backward(args)
+        return
+    if args.balance:
+        bench_balance(args)
         return
     w, dev, L, layout = setup(args.workload, args.layout)
     if args.calibrate_copy:
