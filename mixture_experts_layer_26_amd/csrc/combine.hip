@@ -3,7 +3,9 @@
 // combine: h'_t = u_t + (shared sum)_t + sum_k g_{k,t} * y_routed[pair_row[t,k]], the
 // DeepSeek-V3 explainer's equation for h'_t (method section 2), as a gather over the
 // token's K sorted rows (no atomics), added in fp32 in the order residual, shared,
-// routed experts ascending, and rounded once to the output dtype.
+// routed experts ascending, and rounded once to the output dtype. One workgroup per
+// token with one thread per 16-byte vector of the row (up to 1024), so every load of
+// the token is issued at once.
 //
 // bias update: the same section's end-of-step rule, b_i -= gamma when expert i's load
 // is above the mean T*K/N_r, += gamma when below, compared exactly in integers.
@@ -14,10 +16,9 @@ namespace moe {
 
 namespace {
 
-constexpr int kThreads = 256;
 
 template <int ACT>  // 0: fp32 in/out (4 per vector), 1: bf16 (8 per vector)
-__global__ __launch_bounds__(kThreads) void combine_kernel(
+__global__ __launch_bounds__(1024) void combine_kernel(
     const void* __restrict__ u, const void* __restrict__ y_routed, const float* __restrict__ y_shared,
     const int32_t* __restrict__ pair_row, const float* __restrict__ gate, void* __restrict__ out,
     int64_t T, int d, int K) {
@@ -30,7 +31,7 @@ __global__ __launch_bounds__(kThreads) void combine_kernel(
     gs[threadIdx.x] = gate[t * K + threadIdx.x];
   }
   __syncthreads();
-  for (int c0 = threadIdx.x * V; c0 < d; c0 += kThreads * V) {
+  for (int c0 = threadIdx.x * V; c0 < d; c0 += blockDim.x * V) {
     float acc[V];
     if (ACT == 1) {
       const uint4 uv = ld16(static_cast<const uint16_t*>(u) + t * d + c0);
@@ -97,11 +98,14 @@ hipError_t launch_combine(int act, const void* u, const void* y_routed, const fl
                           const int32_t* pair_row, const float* gate, void* out, int64_t T, int d,
                           int K, hipStream_t stream) {
   const dim3 grid(static_cast<unsigned>(T));
+  const int V = act == 1 ? 8 : 4;
+  int thr = (d / V + 63) / 64 * 64;
+  thr = thr > 1024 ? 1024 : (thr < 64 ? 64 : thr);
   if (act == 1)
-    hipLaunchKernelGGL(combine_kernel<1>, grid, dim3(kThreads), 0, stream, u, y_routed, y_shared,
+    hipLaunchKernelGGL(combine_kernel<1>, grid, dim3(thr), 0, stream, u, y_routed, y_shared,
                        pair_row, gate, out, T, d, K);
   else
-    hipLaunchKernelGGL(combine_kernel<0>, grid, dim3(kThreads), 0, stream, u, y_routed, y_shared,
+    hipLaunchKernelGGL(combine_kernel<0>, grid, dim3(thr), 0, stream, u, y_routed, y_shared,
                        pair_row, gate, out, T, d, K);
   return hipGetLastError();
 }
