@@ -11,7 +11,9 @@ tolerances (relative Frobenius 5e-3, max-abs 2e-2 of the largest reference magni
 - K = N_r (every expert on every token) and the largest K (16 of 256 experts);
 - every token on the same K experts (bias +10 on experts 0..K-1, which the sigmoid scores in
   (0, 1) cannot overturn): K groups of T rows, many row blocks each, every other expert empty;
-- FP8 experts with a ragged token count; fp32 with a ragged token count.
+- FP8 experts with a ragged token count; fp32 with a ragged token count;
+- the largest number of shared experts (8), in bf16 and FP8: the shared down-projection's K
+  range runs over eight weight matrices.
 """
 import numpy as np
 import pytest
@@ -43,6 +45,9 @@ CASES = {
     "max_top_k": _w("max_top_k", T=200, d=512, n_routed=256, top_k=16, n_shared=1, d_ff=256, seed=2703),
     "all_on_k_experts": _w("all_on_k_experts", T=2048, seed=2704),
     "fp8_ragged_333": _w("fp8_ragged_333", T=333, ffn="fp8"),
+    "max_shared_8": _w("max_shared_8", T=200, d=512, n_routed=32, top_k=4, n_shared=8, d_ff=256, seed=2705),
+    "fp8_max_shared_8": _w("fp8_max_shared_8", T=200, d=512, n_routed=32, top_k=4, n_shared=8, d_ff=256,
+                           seed=2705, ffn="fp8"),
     "f32_ragged_77": _w("f32_ragged_77", base=I.WORKLOADS["tiny_f32"], T=77),
 }
 
