@@ -29,9 +29,11 @@ struct Tile {
   int rows;   // valid rows in this tile
 };
 
-// Tile list, by position: first the routed experts with an even number of row blocks,
-// then those with an odd number, then the shared groups, so that with 16 column tiles
-// per block and 32-tile gang items an expert of two blocks fills exactly one item.
+// Tile list, by position: first the shared groups, then the routed experts with an even
+// number of row blocks, then those with an odd number, so that with 16 column tiles per
+// block and 32-tile gang items an expert of two blocks fills exactly one item. The shared
+// groups' tiles are all of full height and come first; the routed tiles, whose heights
+// vary, fill the tail of the launch, where short tiles even out the finish.
 // Routed groups list their tiles column-major (the row blocks of one column tile are
 // neighbours: they read the same weights); shared groups row-major (the column tiles of
 // one row block are neighbours: they read the same rows). Built per workgroup in LDS.
@@ -58,10 +60,10 @@ __device__ inline void build_tile_map(TileMap& tm, const int32_t* offset, int n_
   if (threadIdx.x == 0) {
     int acc = 0, pos = 0;
     for (int pass = 0; pass < 3; ++pass) {
-      const int lo = pass < 2 ? 0 : n_r, hi = pass < 2 ? n_r : ng;
+      const int lo = pass == 0 ? n_r : 0, hi = pass == 0 ? ng : n_r;
       for (int g = lo; g < hi; ++g) {
         const int mt = tm.mt[g];
-        if (mt == 0 || (pass < 2 && (mt & 1) != pass)) continue;
+        if (mt == 0 || (pass > 0 && (mt & 1) != pass - 1)) continue;
         tm.grp[pos] = g;
         tm.cum[pos] = acc;
         acc += mt * ntn;

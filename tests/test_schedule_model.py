@@ -1,0 +1,151 @@
+"""CPU model of the grouped GEMMs' tile list and gang scheduling (no GPU).
+
+The device code (gemm_common.h: build_tile_map, tile_at, for_each_tile) builds a tile list
+from expert_offset and hands it out to gangs of 8 workgroups through one atomic item
+counter and per-gang claim slots. This test restates those rules in Python and runs them
+under random interleavings of the workgroups, on random and skewed expert loads, checking:
+
+- every (group, row, output-column tile) is computed exactly once;
+- no tile is empty and no tile is taller than 256 rows;
+- the tile count stays within the bound the workspace is sized for (ffn_max_tiles in
+  abi.cpp) and no gang reads past its row of slots (slot stride ceil(max/G) + 2);
+- the list order: shared groups first, then routed experts with an even number of row
+  blocks, then those with an odd number.
+
+It is a model: it checks the protocol's design, and the GPU parity tests check the
+kernels that implement it.
+"""
+import random
+
+import numpy as np
+
+BM = 256
+GANGS = 8
+
+
+def tile_map(rows, n_r):
+    """Row blocks per group, rows per block, and the list order (shared, even, odd)."""
+    mt, rpb = [], []
+    for r in rows:
+        mt0 = (r + BM - 1) // BM
+        p = (r + mt0 - 1) // mt0 if mt0 else 0
+        rpb.append(p)
+        mt.append((r + p - 1) // p if p else 0)
+    order = [g for g in range(n_r, len(rows)) if mt[g]]
+    order += [g for g in range(n_r) if mt[g] and mt[g] % 2 == 0]
+    order += [g for g in range(n_r) if mt[g] and mt[g] % 2 == 1]
+    return mt, rpb, order
+
+
+def tiles_of(rows, n_r, ntn):
+    mt, rpb, order = tile_map(rows, n_r)
+    out = []
+    for g in order:
+        if g < n_r:  # column-major: the row blocks of one column tile are neighbours
+            pairs = [(m, n) for n in range(ntn) for m in range(mt[g])]
+        else:  # row-major: the column tiles of one row block are neighbours
+            pairs = [(m, n) for m in range(mt[g]) for n in range(ntn)]
+        for m, n in pairs:
+            m0 = m * rpb[g]
+            out.append((g, m0, n, min(rpb[g], rows[g] - m0)))
+    return out
+
+
+def max_tiles(T, top_k, n_r, n_shared, d, d_ff, phase):
+    P = T * top_k
+    routed_blocks = P // BM + n_r + 1
+    tb = (T + BM - 1) // BM
+    if phase == 1:
+        return (routed_blocks + n_shared * tb) * (d_ff // 128)
+    return (routed_blocks + (tb if n_shared else 0)) * (d // 256)
+
+
+def run_gangs(tiles, grid, stride, rng):
+    """Random interleaving of the claim protocol; returns the tiles each workgroup ran."""
+    total = len(tiles)
+    G = grid // GANGS
+    n_items = (total + G - 1) // G
+    counter = 0
+    slots = np.zeros((GANGS, stride), np.int64)
+    step = {b: 0 for b in range(GANGS * G)}  # workgroups past G * 8 idle at once
+    ran = []
+    active = list(step)
+    while active:
+        b = rng.choice(active)
+        gang, rank = b % GANGS, b // GANGS
+        k = step[b]
+        assert k < stride, "a gang read past its slots"
+        if slots[gang, k] == 0:  # first member at step k claims the next item
+            counter += 1
+            slots[gang, k] = counter
+        item = slots[gang, k] - 1
+        if item >= n_items:
+            active.remove(b)
+            continue
+        L = item * G + rank
+        if L < total:
+            ran.append(tiles[L])
+        step[b] = k + 1
+    return ran
+
+
+def check(T, top_k, n_r, n_shared, d, d_ff, counts, grid, rng):
+    for phase in (1, 2):
+        ns_groups = n_shared if phase == 1 else min(n_shared, 1)
+        ntn = d_ff // 128 if phase == 1 else d // 256
+        rows = list(counts) + [T] * ns_groups
+        tiles = tiles_of(rows, n_r, ntn)
+        bound = max_tiles(T, top_k, n_r, n_shared, d, d_ff, phase)
+        assert len(tiles) <= bound
+        G = grid // GANGS
+        stride = (bound + G - 1) // G + 2
+        ran = run_gangs(tiles, grid, stride, rng)
+        seen = set()
+        for g, m0, n, r in ran:
+            assert 1 <= r <= BM
+            for row in range(m0, m0 + r):
+                key = (g, row, n)
+                assert key not in seen, key
+                seen.add(key)
+        assert len(seen) == sum(rows) * ntn
+
+
+def _counts(rng, T, top_k, n_r, skew):
+    p = rng.dirichlet(np.ones(n_r) * skew)
+    return rng.multinomial(T * top_k, p)
+
+
+def test_schedule_v3_prefill_shape():
+    rng = np.random.default_rng(1)
+    r = random.Random(1)
+    counts = _counts(rng, 8192, 8, 256, 20.0)
+    check(8192, 8, 256, 1, 7168, 2048, counts, 256, r)
+
+
+def test_schedule_random_shapes():
+    rng = np.random.default_rng(2)
+    r = random.Random(2)
+    for _ in range(40):
+        n_r = int(rng.choice([1, 2, 16, 64, 256]))
+        T = int(rng.choice([1, 7, 64, 300, 2048]))
+        top_k = int(rng.integers(1, min(8, n_r) + 1))
+        counts = _counts(rng, T, top_k, n_r, float(rng.choice([0.1, 1.0, 10.0])))
+        n_shared = int(rng.choice([0, 1, 2, 8]))
+        d = int(rng.choice([256, 512, 2816]))
+        d_ff = int(rng.choice([128, 1408, 2048]))
+        grid = int(rng.choice([64, 256, 264]))
+        check(T, top_k, n_r, n_shared, d, d_ff, counts, grid, r)
+
+
+def test_schedule_all_rows_on_few_experts():
+    r = random.Random(3)
+    check(4096, 4, 4, 1, 512, 256, np.array([4096] * 4), 64, r)  # 16 blocks per expert
+    check(3000, 1, 2, 2, 256, 128, np.array([2999, 1]), 64, r)   # a one-row expert
+
+
+def test_tile_order():
+    rows = [300, 0, 600, 256, 513, 9000, 70]  # n_r = 5, two shared groups
+    mt, rpb, order = tile_map(rows, 5)
+    assert mt == [2, 0, 3, 1, 3, 36, 1]
+    assert rpb == [150, 0, 200, 256, 171, 250, 70]
+    assert order == [5, 6, 0, 2, 3, 4]
