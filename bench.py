@@ -61,19 +61,21 @@ def parse():
     return p.parse_args()
 
 
-def kernel_source_hash() -> str:
-    """Hash of the grouped-FFN kernel sources; a stored traffic measurement is used only
-    while the kernels it was taken on are unchanged."""
+def kernel_source_hash(ffn: str) -> str:
+    """Hash of the sources of the grouped-FFN kernels that run for expert dtype `ffn`; a
+    stored traffic measurement is used only while the kernels it was taken on are
+    unchanged."""
     import hashlib
     h = hashlib.sha256()
     csrc = os.path.join(ROOT, "mixture_experts_layer_26_amd", "csrc")
-    for f in ("gemm_common.h", "ffn_bf16.hip", "ffn_fp8.hip", "device.h", "pack.hip"):
+    kernel = {"bf16": "ffn_bf16.hip", "fp8": "ffn_fp8.hip"}[ffn]
+    for f in ("gemm_common.h", kernel, "device.h", "pack.hip"):
         with open(os.path.join(csrc, f), "rb") as fh:
             h.update(fh.read())
     return h.hexdigest()[:16]
 
 
-def stored_traffic(workload: str, layout: str):
+def stored_traffic(workload: str, ffn: str, layout: str):
     """HBM bytes per grouped-FFN call from the committed counter runs (profiles/), or
     None when absent or taken on other kernel sources or another weight layout."""
     path = os.path.join(ROOT, "profiles", f"traffic_{workload}.json")
@@ -81,7 +83,7 @@ def stored_traffic(workload: str, layout: str):
         return None
     with open(path) as f:
         t = json.load(f)
-    if t.get("kernel_source_hash") != kernel_source_hash() or t.get("weights", "rows") != layout:
+    if t.get("kernel_source_hash") != kernel_source_hash(ffn) or t.get("weights", "rows") != layout:
         return None
     return t
 
@@ -386,7 +388,7 @@ def main():
     ffn_tf = w.ffn_flops() / (ffn_avg * 1e-3) / 1e12
     dt = "fp8" if w.ffn == "fp8" else w.act
     abytes, active = ffn_algorithmic_bytes(w, L)
-    traffic = stored_traffic(w.name, layout)
+    traffic = stored_traffic(w.name, w.ffn, layout)
     decode = w.T * w.top_k < 32 * w.n_routed  # under one MFMA block of rows per expert: weight streaming
     if decode:
         gbs = abytes / (ffn_avg * 1e-3) / 1e9

@@ -106,7 +106,7 @@ struct SchedState {  // the two launches' regions of the scheduling state
 };
 
 struct FfnWorkspace {
-  size_t sched, h_routed, h_shared, q_u, s_u, s_h_routed, s_h_shared, total;
+  size_t sched, h_routed, h_shared, q_u, s_u, s_cols, s_h_routed, s_h_shared, total;
 };
 
 FfnWorkspace ffn_workspace(const moe_shape* s) {
@@ -122,6 +122,8 @@ FfnWorkspace ffn_workspace(const moe_shape* s) {
     off = align_up(off + static_cast<size_t>(s->T) * s->d);
     w.s_u = off;
     off = align_up(off + static_cast<size_t>(s->T) * (s->d / 128) * 4);
+    w.s_cols = off;  // the same scales K-block-major, routed rows in sorted order then the tokens
+    off = align_up(off + static_cast<size_t>(P + s->T) * (s->d / 128) * 4);
     w.h_routed = off;
     off = align_up(off + static_cast<size_t>(P) * s->d_ff);
     w.s_h_routed = off;
@@ -185,12 +187,15 @@ moe_status grouped_ffn_fp8(const moe_shape* s, const void* u, const int32_t* exp
                            int b_tiled, hipStream_t st) {
   uint8_t* q_u = wsb + w.q_u;
   float* s_u = reinterpret_cast<float*>(wsb + w.s_u);
+  float* s_cols = reinterpret_cast<float*>(wsb + w.s_cols);
   uint8_t* h_r = wsb + w.h_routed;
   uint8_t* h_s = wsb + w.h_shared;
   float* sh_r = reinterpret_cast<float*>(wsb + w.s_h_routed);
   float* sh_s = reinterpret_cast<float*>(wsb + w.s_h_shared);
   const int d = s->d, I = s->d_ff, ns = s->n_shared;
+  const int64_t P = s->T * s->top_k;
   if (moe::launch_quantize_fp8(u, MOE_BF16, s->T, d, 1, 128, q_u, s_u, st) != hipSuccess) return MOE_ERR_HIP;
+  if (moe::launch_scale_columns(s_u, d / 128, sorted_token, P, s->T, s_cols, st) != hipSuccess) return MOE_ERR_HIP;
   auto b = [](const void* p) { return static_cast<const uint16_t*>(p); };
 
   moe::Fp8Args f1{};
@@ -217,8 +222,9 @@ moe_status grouped_ffn_fp8(const moe_shape* s, const void* u, const int32_t* exp
   f1.g.sched = sc.s1;
   f1.g.b_tiled = b_tiled;
   f1.g.slot_stride = sc.stride1;
-  f1.sa_routed = f1.sa_shared = s_u;
-  f1.ldsa_routed = f1.ldsa_shared = d / 128;
+  f1.sa_routed = s_cols;
+  f1.sa_shared = s_cols + P;
+  f1.ldsa_routed = f1.ldsa_shared = P + s->T;
   f1.sb1_routed = routed->s1;
   f1.sb3_routed = routed->s3;
   f1.sb1_shared = ns > 0 ? shared->s1 : nullptr;
@@ -227,8 +233,8 @@ moe_status grouped_ffn_fp8(const moe_shape* s, const void* u, const int32_t* exp
   f1.kblocks = d / 128;
   f1.os_routed = sh_r;
   f1.os_shared = sh_s;
-  f1.ldos_routed = I / 128;
-  f1.ldos_shared = static_cast<int64_t>(ns) * (I / 128);
+  f1.ldos_routed = P;
+  f1.ldos_shared = s->T;
   if (moe::launch_grouped_gemm_fp8(f1, true, grid, st) != hipSuccess) return MOE_ERR_HIP;
 
   moe::Fp8Args f2{};
@@ -256,9 +262,9 @@ moe_status grouped_ffn_fp8(const moe_shape* s, const void* u, const int32_t* exp
   f2.g.b_tiled = b_tiled;
   f2.g.slot_stride = sc.stride2;
   f2.sa_routed = sh_r;
-  f2.ldsa_routed = I / 128;
+  f2.ldsa_routed = P;
   f2.sa_shared = sh_s;
-  f2.ldsa_shared = static_cast<int64_t>(ns) * (I / 128);
+  f2.ldsa_shared = s->T;
   f2.sb1_routed = routed->s2;
   f2.sb1_shared = ns > 0 ? shared->s2 : nullptr;
   f2.sb_expert_stride = static_cast<int64_t>(d / 128) * (I / 128);

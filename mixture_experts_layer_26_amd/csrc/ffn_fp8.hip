@@ -42,6 +42,20 @@ __device__ __forceinline__ unsigned char* stage() {
 
 typedef __attribute__((address_space(3))) unsigned char* lds_ptr;
 
+// Weight scales are wave-uniform and read-only in these kernels, so they are read
+// through the constant address space with a wave-uniform address: the loads become
+// scalar loads, whose waits count on lgkmcnt. A vector load here would be waited for
+// with a vmcnt that the compiler sizes without the DMA loads it cannot see, so the
+// wait would also cover the next step's tile loads and stall the step's MFMAs on them.
+typedef const __attribute__((address_space(4))) float* scale_ptr;
+
+__device__ __forceinline__ scale_ptr uniform_scales(const float* p) {
+  const uint64_t v = reinterpret_cast<uint64_t>(p);
+  const uint64_t lo = static_cast<uint32_t>(__builtin_amdgcn_readfirstlane(static_cast<uint32_t>(v)));
+  const uint64_t hi = static_cast<uint32_t>(__builtin_amdgcn_readfirstlane(static_cast<uint32_t>(v >> 32)));
+  return (scale_ptr)((hi << 32) | lo);
+}
+
 // One global_load_lds_dwordx4: lane i copies the 16 bytes at gptr (its own address) to
 // LDS byte base + OFF + 16 i. M0 holds the LDS address (one wait state after writing
 // it). The instruction is written out rather than taken from the builtin so that the
@@ -69,8 +83,9 @@ struct TileCtx {
   const uint8_t* b;         // this lane's first B row (chunk included); row j: + 8 j ldb,
   int64_t ldb8;             //   and + odd_chunk for odd j (8 rows on, the swizzle term
   int odd_chunk;            //   (row/2)%8 differs by 4: the chunk index flips bit 2)
-  const float* sa_row;      // threads 0..255: A-row scales of tile row tid (K-block 0)
-  const float* sb[2];       // this wave's two B-scale rows (gate/up, or the wave's block)
+  const float* sa_row;      // threads 0..255: scale of the tile row LDS slot tid holds, K block 0
+  int64_t sa_ld;            //   and the distance from one K block to the next
+  scale_ptr sb[2];          // this wave's two B-scale rows (gate/up, or the wave's block)
   int64_t seg_stride;       // phase 2 shared: W2 stride per K segment, else 0
   int bstep;                // bytes from one K-step of a B row to the next
   int64_t sb_seg_stride;    // same for the W2 scales
@@ -97,7 +112,7 @@ __device__ __forceinline__ void dma_step(const TileCtx& c, int kt) {
   dma16<ST * kStageSize + kOperand + 1 * 8 * BK>(c.b + (boff + 1 * c.ldb8 + c.odd_chunk), c.lds_wave);
   dma16<ST * kStageSize + kOperand + 2 * 8 * BK>(c.b + (boff + 2 * c.ldb8), c.lds_wave);
   dma16<ST * kStageSize + kOperand + 3 * 8 * BK>(c.b + (boff + 3 * c.ldb8 + c.odd_chunk), c.lds_wave);
-  if (c.load_scale) dma4<ST * kStageSize>(c.sa_row + kt, c.lds_scale);
+  if (c.load_scale) dma4<ST * kStageSize>(c.sa_row + kt * c.sa_ld, c.lds_scale);
 }
 
 // A 16 x 128 fp8 fragment (rows row.., this lane's 32 bytes of K) from a swizzled stage.
@@ -114,39 +129,65 @@ __device__ __forceinline__ i32x8 rd_frag(const unsigned char* base, int row, int
 __device__ __forceinline__ void fence() { __builtin_amdgcn_sched_barrier(0); }
 
 // One K-step (one scale block) from stage ST for a wave holding NM live 32-row blocks
-// (2*NM 16-row MFMA blocks). sw[p]: the weight scale of output blocks 2p, 2p+1. The
-// MFMAs of a block start from a zero that an empty asm statement produces after the
-// previous block's accumulators are final, so the compiler cannot hoist all MFMAs of
-// the step ahead of their scaling (which would hold 32 MFMA results at once).
+// (2*NM 16-row MFMA blocks, 4 column blocks each: 8*NM MFMAs). sw[p]: the weight scale
+// of column blocks 2p, 2p+1. The weight fragment is the MFMA's first operand, so a
+// lane's result holds 4 consecutive output columns of one token row (16*mb + lane%16)
+// and the fold needs one row scale per lane and block: acc += blk * (s_a[row] * s_w).
+// Each MFMA covers one scale block from zero. MFMAs and folds are software-pipelined:
+// MFMA j is issued before the fold of MFMA j-1, so the fold's VALU work runs while the
+// matrix core computes, and an empty asm statement ties MFMA j's A operand to the fold
+// of MFMA j-2, so at most two MFMA results are held at once and the compiler cannot
+// hoist the step's MFMAs ahead of their folds. The activation fragment of block mb+1 is
+// read from LDS while block mb is computed.
 template <int ST, int NM>
-__device__ __forceinline__ void compute_step(int arow0, const int (&brow)[4], const float (&sw)[2], int lane,
-                                             f32x4 (&acc)[8][4]) {
+__device__ __forceinline__ void compute_step(int arow0, const int (&brow)[4], int lsa_off, const float (&sw)[2],
+                                             int lane, f32x4 (&acc)[8][4]) {
   if constexpr (NM == 0) return;
+  constexpr int NMF = 8 * NM;
   const unsigned char* la = stage<ST>();
   const unsigned char* lb = la + kOperand;
-  const float* lsa = reinterpret_cast<const float*>(la + 2 * kOperand);
   const int q = lane / 16;
+  // this lane's row scales of blocks 0..7, contiguous in LDS (see the DMA's row order)
+  const float* lsa = reinterpret_cast<const float*>(la + 2 * kOperand) + lsa_off;
+  float sa[8];
+  {
+    const f32x4 s0 = *reinterpret_cast<const f32x4*>(lsa);
+#pragma unroll
+    for (int v = 0; v < 4; ++v) sa[v] = s0[v];
+    if constexpr (NM > 2) {
+      const f32x4 s1 = *reinterpret_cast<const f32x4*>(lsa + 4);
+#pragma unroll
+      for (int v = 0; v < 4; ++v) sa[4 + v] = s1[v];
+    }
+  }
   i32x8 bfr[4];
 #pragma unroll
   for (int nb = 0; nb < 4; ++nb) bfr[nb] = rd_frag(lb, brow[nb], q);
+  i32x8 af = rd_frag(la, arow0, q);
+  i32x8 af_next;
+  float prod[2][2];  // [block parity][column pair]: row scale x weight scale
+  f32x4 blk[2];
 #pragma unroll
-  for (int mb = 0; mb < 2 * NM; ++mb) {
-    f32x4 zero = {};
-    if (mb > 0)
-      asm volatile("" : "+v"(zero) : "v"(acc[mb - 1][0]), "v"(acc[mb - 1][1]), "v"(acc[mb - 1][2]), "v"(acc[mb - 1][3]));
-    const i32x8 af = rd_frag(la, arow0 + 16 * mb, q);
-    // scales of this lane's 4 rows (16*mb + 4*q + v), contiguous in LDS
-    const f32x4 sa = *reinterpret_cast<const f32x4*>(lsa + (arow0 - lane % 16) + 16 * mb + 4 * q);
-    f32x4 prod[2];  // row scale x weight scale, per pair of output blocks
+  for (int j = 0; j <= NMF; ++j) {
+    const int mb = j / 4, nb = j % 4;
+    if (j < NMF) {
+      if (nb == 0) {
+        if (mb > 0) af = af_next;
+        if (mb + 1 < 2 * NM) af_next = rd_frag(la, arow0 + 16 * (mb + 1), q);
+        prod[mb & 1][0] = sa[mb] * sw[0];
+        prod[mb & 1][1] = sa[mb] * sw[1];
+      }
+      if (j >= 2) {  // ties the activation fragment (in place, no copy) to the fold of MFMA j-2
+        const int mp = (j - 2) / 4, np = (j - 2) % 4;
+        asm volatile("" : "+v"(af) : "v"(acc[mp][np]));
+      }
+      blk[j & 1] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(bfr[nb], af, f32x4{}, 0, 0, 0, 127, 0, 127);
+    }
+    if (j >= 1) {  // fold MFMA j-1
+      const int mp = (j - 1) / 4, np = (j - 1) % 4;
 #pragma unroll
-    for (int p = 0; p < 2; ++p)
-#pragma unroll
-      for (int v = 0; v < 4; ++v) prod[p][v] = sa[v] * sw[p];
-#pragma unroll
-    for (int nb = 0; nb < 4; ++nb) {
-      const f32x4 blk = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(af, bfr[nb], zero, 0, 0, 0, 127, 0, 127);
-#pragma unroll
-      for (int v = 0; v < 4; ++v) acc[mb][nb][v] = fmaf(blk[v], prod[nb / 2][v], acc[mb][nb][v]);
+      for (int v = 0; v < 4; ++v)
+        acc[mp][np][v] = fmaf(blk[(j - 1) & 1][v], prod[mp & 1][np / 2], acc[mp][np][v]);
     }
   }
 }
@@ -170,20 +211,17 @@ __device__ __forceinline__ void wscales(const TileCtx& c, int kt, float (&sw)[2]
 // DMA, the weight scales into sw for the next step) is loaded into the other stage
 // while this one is computed.
 template <int ST, int NM, bool MORE>
-__device__ __forceinline__ void k_step(const TileCtx& c, int s, int arow0, const int (&brow)[4], int lane,
-                                       float (&sw)[2], f32x4 (&acc)[8][4]) {
-  float swn[2];
-  if constexpr (MORE) {
-    dma_step<(ST + 1) % 2>(c, s + 1);
-    wscales(c, s + 1, swn);
-  }
+__device__ __forceinline__ void k_step(const TileCtx& c, int s, int arow0, const int (&brow)[4], int lsa_off,
+                                       int lane, float (&sw)[2], f32x4 (&acc)[8][4]) {
+  if constexpr (MORE) dma_step<(ST + 1) % 2>(c, s + 1);
   fence();
-  compute_step<ST, NM>(arow0, brow, sw, lane, acc);
+  compute_step<ST, NM>(arow0, brow, lsa_off, sw, lane, acc);
   fence();
-  if constexpr (MORE) {
-    sw[0] = swn[0];
-    sw[1] = swn[1];
-  }
+  // the next step's weight scales: scalar loads issued after this step's last use of sw,
+  // so that no wait for them falls among this step's LDS reads; the barrier's lgkmcnt(0)
+  // covers them
+  if constexpr (MORE) wscales(c, s + 1, sw);
+  fence();
   step_barrier();
 }
 
@@ -197,6 +235,7 @@ __device__ __forceinline__ void mainloop(const TileCtx& c, f32x4 (&acc)[8][4]) {
   const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);
   const int g = wave / 4, wn = wave % 4;
   const int arow0 = 128 * g + lane % 16;
+  const int lsa_off = 128 * g + 8 * (lane % 16);  // row scales of rows arow0 + 16 mb, mb = 0..7
   int brow[4];
 #pragma unroll
   for (int nb = 0; nb < 4; ++nb) {
@@ -211,18 +250,18 @@ __device__ __forceinline__ void mainloop(const TileCtx& c, f32x4 (&acc)[8][4]) {
   if (c.nk & 1) {  // odd: step 0 from stage 1, the rest in pairs as below
     dma_step<1>(c, 0);
     step_barrier();
-    k_step<1, NM, true>(c, 0, arow0, brow, lane, sw, acc);
+    k_step<1, NM, true>(c, 0, arow0, brow, lsa_off, lane, sw, acc);
     s = 1;
   } else {
     dma_step<0>(c, 0);
     step_barrier();
   }
   for (; s + 2 < c.nk; s += 2) {
-    k_step<0, NM, true>(c, s, arow0, brow, lane, sw, acc);
-    k_step<1, NM, true>(c, s + 1, arow0, brow, lane, sw, acc);
+    k_step<0, NM, true>(c, s, arow0, brow, lsa_off, lane, sw, acc);
+    k_step<1, NM, true>(c, s + 1, arow0, brow, lsa_off, lane, sw, acc);
   }
-  k_step<0, NM, true>(c, s, arow0, brow, lane, sw, acc);
-  k_step<1, NM, false>(c, s + 1, arow0, brow, lane, sw, acc);
+  k_step<0, NM, true>(c, s, arow0, brow, lsa_off, lane, sw, acc);
+  k_step<1, NM, false>(c, s + 1, arow0, brow, lsa_off, lane, sw, acc);
 }
 
 __device__ __forceinline__ uint32_t e4m3(float x) {
@@ -304,19 +343,25 @@ __global__ __launch_bounds__(kThreads) void grouped_gemm_fp8(Fp8Args fa) {
       }
       c.odd_chunk = ((chunk ^ 4) - chunk) * 16;
     }
-    {
-      const int64_t src = src_row(tid & (BM - 1));
-      c.sa_row = routed ? fa.sa_routed + src * fa.ldsa_routed : fa.sa_shared + src * fa.ldsa_shared;
+    {  // scales are indexed by sorted row (routed) or token (shared), not by the gathered A row.
+      // LDS slot 128 g + 8 c + mb holds row 128 g + 16 mb + c, so that a lane's scales of its
+      // 8 row blocks (rows arow0 + 16 mb) are contiguous
+      const int slot = tid & (BM - 1);
+      int r = 128 * (slot / 128) + 16 * (slot % 8) + (slot % 128) / 8;
+      if (r >= t.rows) r = t.rows - 1;
+      const int64_t m = t.m0 + r;
+      c.sa_row = routed ? fa.sa_routed + row_base + m : fa.sa_shared + m;
+      c.sa_ld = routed ? fa.ldsa_routed : fa.ldsa_shared;
     }
     // weight-scale rows: [expert][N/128][K/128]
     const int64_t sbe = (routed || GATED) ? eidx * fa.sb_expert_stride : 0;
     if (GATED) {
       const int64_t nblk = t.n0 / 128;
-      c.sb[0] = (routed ? fa.sb1_routed : fa.sb1_shared) + sbe + nblk * fa.kblocks;
-      c.sb[1] = (routed ? fa.sb3_routed : fa.sb3_shared) + sbe + nblk * fa.kblocks;
+      c.sb[0] = uniform_scales((routed ? fa.sb1_routed : fa.sb1_shared) + sbe + nblk * fa.kblocks);
+      c.sb[1] = uniform_scales((routed ? fa.sb3_routed : fa.sb3_shared) + sbe + nblk * fa.kblocks);
     } else {
       const int64_t nblk = t.n0 / 128 + wn / 2;  // the wave's 64 columns lie in one block
-      c.sb[0] = c.sb[1] = (routed ? fa.sb1_routed : fa.sb1_shared) + sbe + nblk * fa.kblocks;
+      c.sb[0] = c.sb[1] = uniform_scales((routed ? fa.sb1_routed : fa.sb1_shared) + sbe + nblk * fa.kblocks);
     }
     c.seg_stride = (!routed && !GATED) ? args.b_expert_stride : 0;
     c.bstep = args.b_tiled ? (GATED ? 128 : 256) * BK : BK;
@@ -342,74 +387,76 @@ __global__ __launch_bounds__(kThreads) void grouped_gemm_fp8(Fp8Args fa) {
       default: mainloop<GATED, 0>(c, acc); break;
     }
 
-    // epilogue: C layout of the 16x16 MFMA -- lane holds column lane%16 and rows
-    // 4*(lane/16) + v of its 16x16 block
-    const int col_in = lane % 16, q = lane / 16;
+    // epilogue: the MFMA took the weight fragment first, so a lane holds token row
+    // 128 g + 16 mb + lane%16 and, in each 16-column block nb, the 4 consecutive columns
+    // 4 (lane/16) + v
+    const int rc = lane % 16, q = lane / 16;
     if (GATED) {
       // H = SiLU(gate) * up, then per-row 1x128 quantisation over the tile's 128 gate
       // columns (spread over the 4 waves of the group): amax per row via LDS
       float* amaxbuf = reinterpret_cast<float*>(stage<0>());  // [4 waves][256 rows]
       float h[8][2][4];
 #pragma unroll
-      for (int mb = 0; mb < 8; ++mb)
+      for (int mb = 0; mb < 8; ++mb) {
+        float m = 0.0f;
 #pragma unroll
-        for (int v = 0; v < 4; ++v) {
-          float m = 0.0f;
+        for (int nb = 0; nb < 2; ++nb)
 #pragma unroll
-          for (int nb = 0; nb < 2; ++nb) {
+          for (int v = 0; v < 4; ++v) {
             h[mb][nb][v] = silu(acc[mb][nb][v]) * acc[mb][nb + 2][v];
             m = fmaxf(m, fabsf(h[mb][nb][v]));
           }
-#pragma unroll
-          for (int off = 1; off < 16; off <<= 1) m = fmaxf(m, __shfl_xor(m, off, kWave));
-          if (col_in == 0) amaxbuf[wn * 256 + 128 * g + 16 * mb + 4 * q + v] = m;
-        }
+        m = fmaxf(m, __shfl_xor(m, 16, kWave));
+        m = fmaxf(m, __shfl_xor(m, 32, kWave));
+        if (q == 0) amaxbuf[wn * 256 + 128 * g + 16 * mb + rc] = m;
+      }
       __syncthreads();
 #pragma unroll
       for (int mb = 0; mb < 8; ++mb) {
-#pragma unroll
-        for (int v = 0; v < 4; ++v) {
-          const int i = 128 * g + 16 * mb + 4 * q + v;
-          const float amax = fmaxf(fmaxf(amaxbuf[i], amaxbuf[256 + i]), fmaxf(amaxbuf[512 + i], amaxbuf[768 + i]));
-          if (i >= t.rows) continue;
-          const float s = amax / 448.0f;
-          const int64_t m = t.m0 + i;
-          uint8_t* orow;
-          float* srow;
-          if (routed) {
-            orow = reinterpret_cast<uint8_t*>(args.out_routed) + (row_base + m) * args.ldo_routed;
-            srow = fa.os_routed + (row_base + m) * fa.ldos_routed;
-          } else {
-            orow = reinterpret_cast<uint8_t*>(args.out_shared) + m * args.ldo_shared +
-                   static_cast<int64_t>(sg) * args.N;
-            srow = fa.os_shared + m * fa.ldos_shared + static_cast<int64_t>(sg) * (args.N / 128);
-          }
-#pragma unroll
-          for (int nb = 0; nb < 2; ++nb) {
-            const int n = t.n0 + 32 * wn + 16 * nb + col_in;
-            orow[n] = static_cast<uint8_t>(s == 0.0f ? 0u : e4m3(h[mb][nb][v] / s));
-          }
-          if (wn == 0 && col_in == 0) srow[t.n0 / 128] = s;
+        const int i = 128 * g + 16 * mb + rc;
+        const float amax = fmaxf(fmaxf(amaxbuf[i], amaxbuf[256 + i]), fmaxf(amaxbuf[512 + i], amaxbuf[768 + i]));
+        if (i >= t.rows) continue;
+        const float s = amax / 448.0f;
+        const int64_t m = t.m0 + i;
+        uint8_t* orow;
+        float* srow;
+        if (routed) {
+          orow = reinterpret_cast<uint8_t*>(args.out_routed) + (row_base + m) * args.ldo_routed;
+          srow = fa.os_routed + (t.n0 / 128) * fa.ldos_routed + row_base + m;
+        } else {
+          orow = reinterpret_cast<uint8_t*>(args.out_shared) + m * args.ldo_shared +
+                 static_cast<int64_t>(sg) * args.N;
+          srow = fa.os_shared + (static_cast<int64_t>(sg) * (args.N / 128) + t.n0 / 128) * fa.ldos_shared + m;
         }
+#pragma unroll
+        for (int nb = 0; nb < 2; ++nb) {
+          uint32_t codes = 0;
+#pragma unroll
+          for (int v = 0; v < 4; ++v)
+            codes |= (s == 0.0f ? 0u : e4m3(h[mb][nb][v] / s)) << (8 * v);
+          *reinterpret_cast<uint32_t*>(orow + t.n0 + 32 * wn + 16 * nb + 4 * q) = codes;
+        }
+        if (wn == 0 && q == 0) *srow = s;
       }
       __syncthreads();  // amaxbuf (LDS stage 0) is reused by the next tile
     } else {
 #pragma unroll
       for (int mb = 0; mb < 8; ++mb) {
         if (mb >= 2 * vblk) continue;
+        const int i = 128 * g + 16 * mb + rc;
+        if (i >= t.rows) continue;
+        const int64_t m = t.m0 + i;
 #pragma unroll
-        for (int v = 0; v < 4; ++v) {
-          const int i = 128 * g + 16 * mb + 4 * q + v;
-          if (i >= t.rows) continue;
-          const int64_t m = t.m0 + i;
-#pragma unroll
-          for (int nb = 0; nb < 4; ++nb) {
-            const int n = t.n0 + 64 * wn + 16 * nb + col_in;
-            const float y = acc[mb][nb][v];
-            if (routed)
-              static_cast<uint16_t*>(args.out_routed)[(row_base + m) * args.ldo_routed + n] = f32_to_bf16(y);
-            else
-              static_cast<float*>(args.out_shared)[m * args.ldo_shared + n] = y;
+        for (int nb = 0; nb < 4; ++nb) {
+          const int n = t.n0 + 64 * wn + 16 * nb + 4 * q;
+          if (routed) {
+            uint2 o;
+            o.x = pack_bf16x2(acc[mb][nb][0], acc[mb][nb][1]);
+            o.y = pack_bf16x2(acc[mb][nb][2], acc[mb][nb][3]);
+            *reinterpret_cast<uint2*>(static_cast<uint16_t*>(args.out_routed) + (row_base + m) * args.ldo_routed + n) = o;
+          } else {
+            *reinterpret_cast<float4*>(static_cast<float*>(args.out_shared) + m * args.ldo_shared + n) =
+                make_float4(acc[mb][nb][0], acc[mb][nb][1], acc[mb][nb][2], acc[mb][nb][3]);
           }
         }
       }

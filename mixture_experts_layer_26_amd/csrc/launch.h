@@ -51,12 +51,14 @@ inline int64_t sched_ints(int64_t max_tiles, int grid) { return 1 + kGangs * sch
 hipError_t launch_zero_i32(int* p, int n, hipStream_t stream);
 
 // FP8 grouped GEMM: the codes travel in the GemmArgs pointers (as bytes), the fp32
-// scales here. A-row scales: one per row per 128-wide K block; B scales: one per
-// 128 x 128 block of a weight matrix [E, N/128, K/128].
+// scales here. A-row scales: one per row per 128-wide K block, stored K-block-major
+// (the scale of row r in K block kb at [kb * ld + r]) so that one K-step's scales of a
+// tile's rows are contiguous; routed rows are indexed by sorted row, shared rows by
+// token. B scales: one per 128 x 128 block of a weight matrix [E, N/128, K/128].
 struct Fp8Args {
   GemmArgs g;
-  const float* sa_routed;   // [rows, K/128] (routed A rows, same row index as A)
-  const float* sa_shared;
+  const float* sa_routed;   // [K/128][ldsa_routed] by sorted row
+  const float* sa_shared;   // [K/128][ldsa_shared] by token
   int64_t ldsa_routed, ldsa_shared;
   const float* sb1_routed;  // phase 1: s1; phase 2: s2
   const float* sb3_routed;  // phase 1: s3
@@ -64,8 +66,8 @@ struct Fp8Args {
   const float* sb3_shared;
   int64_t sb_expert_stride; // scales per expert: (N/128) * (K/128)
   int kblocks;              // K/128 of one expert (scale row length)
-  float* os_routed;         // phase 1: H scales [P, d_ff/128]
-  float* os_shared;         // phase 1: H scales [T, n_s * d_ff/128]
+  float* os_routed;         // phase 1: H scales, K-block-major [d_ff/128][ldos_routed] by sorted row
+  float* os_shared;         // phase 1: H scales, K-block-major [n_s * d_ff/128][ldos_shared] by token
   int64_t ldos_routed, ldos_shared;
 };
 
@@ -110,6 +112,11 @@ hipError_t launch_bias_update(const int32_t* count, int64_t T, int n_r, int K, f
 hipError_t launch_pack_weights(const void* src, void* dst, int esz, int64_t E, int64_t N, int64_t K, int R,
                                hipStream_t stream);
 
+// K-block-major A-row scales of the FP8 phase 1 from the 1x128 tile scales s [T][nkb] of
+// u: out[kb * (P + T) + j] is the scale of sorted row j (token sorted_token[j]) for
+// j < P and of token j - P for P <= j < P + T.
+hipError_t launch_scale_columns(const float* s, int nkb, const int32_t* sorted_token, int64_t P, int64_t T,
+                                float* out, hipStream_t stream);
 hipError_t launch_quantize_fp8(const void* x, int xt, int64_t rows, int64_t cols, int tile_r,
                                int tile_c, uint8_t* q, float* scale, hipStream_t stream);
 

@@ -123,7 +123,25 @@ __global__ __launch_bounds__(256) void quant_block_tiles(const void* __restrict_
   if (tid == 0) scale[blockIdx.x] = s;
 }
 
+// grid (ceil((P + T) / 256), nkb): one thread per output, coalesced writes
+__global__ __launch_bounds__(256) void scale_columns_kernel(const float* __restrict__ s, int nkb,
+                                                            const int32_t* __restrict__ sorted_token, int64_t P,
+                                                            int64_t T, float* __restrict__ out) {
+  const int64_t j = blockIdx.x * 256LL + threadIdx.x;
+  const int kb = blockIdx.y;
+  if (j >= P + T) return;
+  const int64_t tok = j < P ? sorted_token[j] : j - P;
+  out[kb * (P + T) + j] = s[tok * nkb + kb];
+}
+
 }  // namespace
+
+hipError_t launch_scale_columns(const float* s, int nkb, const int32_t* sorted_token, int64_t P, int64_t T,
+                                float* out, hipStream_t stream) {
+  const dim3 grid(static_cast<unsigned>((P + T + 255) / 256), static_cast<unsigned>(nkb));
+  hipLaunchKernelGGL(scale_columns_kernel, grid, dim3(256), 0, stream, s, nkb, sorted_token, P, T, out);
+  return hipGetLastError();
+}
 
 hipError_t launch_quantize_fp8(const void* x, int xt, int64_t rows, int64_t cols, int tile_r,
                                int tile_c, uint8_t* q, float* scale, hipStream_t stream) {
