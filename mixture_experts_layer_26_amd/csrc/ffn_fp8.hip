@@ -166,22 +166,27 @@ __device__ __forceinline__ void compute_step(int arow0, const int (&brow)[4], in
   i32x8 af = rd_frag(la, arow0, q);
   i32x8 af_next;
   float prod[2][2];  // [block parity][column pair]: row scale x weight scale
+  prod[0][0] = sa[0] * sw[0];
+  prod[0][1] = sa[0] * sw[1];
   f32x4 blk[2];
+  // Issue order, pinned by fences: MFMA j, then the fold of MFMA j-1 (its result is
+  // ready by the time MFMA j has been accepted), so the fold's VALU work overlaps MFMA j.
 #pragma unroll
   for (int j = 0; j <= NMF; ++j) {
     const int mb = j / 4, nb = j % 4;
     if (j < NMF) {
-      if (nb == 0) {
-        if (mb > 0) af = af_next;
-        if (mb + 1 < 2 * NM) af_next = rd_frag(la, arow0 + 16 * (mb + 1), q);
-        prod[mb & 1][0] = sa[mb] * sw[0];
-        prod[mb & 1][1] = sa[mb] * sw[1];
-      }
+      if (nb == 0 && mb > 0) af = af_next;
       if (j >= 2) {  // ties the activation fragment (in place, no copy) to the fold of MFMA j-2
         const int mp = (j - 2) / 4, np = (j - 2) % 4;
         asm volatile("" : "+v"(af) : "v"(acc[mp][np]));
       }
       blk[j & 1] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(bfr[nb], af, f32x4{}, 0, 0, 0, 127, 0, 127);
+      fence();
+      if (nb == 0 && mb + 1 < 2 * NM) af_next = rd_frag(la, arow0 + 16 * (mb + 1), q);
+      if (nb == 3 && mb + 1 < 2 * NM) {
+        prod[(mb + 1) & 1][0] = sa[mb + 1] * sw[0];
+        prod[(mb + 1) & 1][1] = sa[mb + 1] * sw[1];
+      }
     }
     if (j >= 1) {  // fold MFMA j-1
       const int mp = (j - 1) / 4, np = (j - 1) % 4;
@@ -189,6 +194,7 @@ __device__ __forceinline__ void compute_step(int arow0, const int (&brow)[4], in
       for (int v = 0; v < 4; ++v)
         acc[mp][np][v] = fmaf(blk[(j - 1) & 1][v], prod[mp & 1][np / 2], acc[mp][np][v]);
     }
+    fence();
   }
 }
 
