@@ -160,9 +160,11 @@ __device__ __forceinline__ void compute_step(int arow0, const int (&brow)[4], in
       for (int v = 0; v < 4; ++v) sa[4 + v] = s1[v];
     }
   }
+  // weight fragments of column blocks 0, 1 first; those of blocks 2, 3 are read while
+  // the first MFMA runs, which shortens the LDS burst at the start of the step
   i32x8 bfr[4];
-#pragma unroll
-  for (int nb = 0; nb < 4; ++nb) bfr[nb] = rd_frag(lb, brow[nb], q);
+  bfr[0] = rd_frag(lb, brow[0], q);
+  bfr[1] = rd_frag(lb, brow[1], q);
   i32x8 af = rd_frag(la, arow0, q);
   i32x8 af_next;
   float prod[2][2];  // [block parity][column pair]: row scale x weight scale
@@ -182,6 +184,10 @@ __device__ __forceinline__ void compute_step(int arow0, const int (&brow)[4], in
       }
       blk[j & 1] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(bfr[nb], af, f32x4{}, 0, 0, 0, 127, 0, 127);
       fence();
+      if (j == 0) {
+        bfr[2] = rd_frag(lb, brow[2], q);
+        bfr[3] = rd_frag(lb, brow[3], q);
+      }
       if (nb == 0 && mb + 1 < 2 * NM) af_next = rd_frag(la, arow0 + 16 * (mb + 1), q);
       if (nb == 3 && mb + 1 < 2 * NM) {
         prod[(mb + 1) & 1][0] = sa[mb + 1] * sw[0];
