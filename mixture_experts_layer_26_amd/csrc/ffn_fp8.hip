@@ -238,9 +238,9 @@ __device__ __forceinline__ void k_step(const TileCtx& c, int s, int arow0, const
 }
 
 // The K loop of one tile: stage s % 2 is computed while step s+1 is loaded into the
-// other stage. With an odd number of steps the first runs from stage 1, so the rest
-// pair up (stage 0, stage 1). On exit no load is in flight and every wave is past the
-// last read of the stages.
+// other stage. With an odd number of steps (more than one) the first runs from stage 1,
+// so the rest pair up (stage 0, stage 1). On exit no load is in flight and every wave
+// is past the last read of the stages.
 template <bool GATED, int NM>
 __device__ __forceinline__ void mainloop(const TileCtx& c, f32x4 (&acc)[8][4]) {
   const int tid = threadIdx.x, lane = tid % kWave;
@@ -258,6 +258,12 @@ __device__ __forceinline__ void mainloop(const TileCtx& c, f32x4 (&acc)[8][4]) {
   }
   float sw[2];
   wscales(c, 0, sw);
+  if (c.nk == 1) {  // a single step (K = 128): nothing to load ahead
+    dma_step<0>(c, 0);
+    step_barrier();
+    k_step<0, NM, false>(c, 0, arow0, brow, lsa_off, lane, sw, acc);
+    return;
+  }
   int s = 0;
   if (c.nk & 1) {  // odd: step 0 from stage 1, the rest in pairs as below
     dma_step<1>(c, 0);

@@ -159,10 +159,11 @@ __device__ __forceinline__ int swz(int r, int c) { return r * kRowBytes + ((c ^ 
 // Element offset of K-step kt within a B row. For the shared down-projection the K
 // range runs over the shared experts' segments (seg selects the expert, seg_stride is
 // its distance); elsewhere kseg_steps == nk, so seg is 0. The quotient uses a
-// precomputed reciprocal kseg_inv = ceil(2^32 / kseg_steps), exact below 2^16.
+// precomputed reciprocal kseg_inv = ceil(2^32 / kseg_steps), exact below 2^16 for
+// kseg_steps > 1; a segment of one step (2^32 does not fit) is taken directly.
 __device__ __forceinline__ int64_t b_offset(int kt, int kseg_steps, uint32_t kseg_inv, int64_t seg_stride,
                                             int step_elems) {
-  const int seg = static_cast<int>(__umulhi(static_cast<uint32_t>(kt), kseg_inv));
+  const int seg = kseg_steps == 1 ? kt : static_cast<int>(__umulhi(static_cast<uint32_t>(kt), kseg_inv));
   return static_cast<int64_t>(seg) * seg_stride + static_cast<int64_t>(kt - seg * kseg_steps) * step_elems;
 }
 

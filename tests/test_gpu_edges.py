@@ -13,7 +13,9 @@ tolerances (relative Frobenius 5e-3, max-abs 2e-2 of the largest reference magni
   (0, 1) cannot overturn): K groups of T rows, many row blocks each, every other expert empty;
 - FP8 experts with a ragged token count; fp32 with a ragged token count;
 - the largest number of shared experts (8), in bf16 and FP8: the shared down-projection's K
-  range runs over eight weight matrices.
+  range runs over eight weight matrices;
+- FP8 with d_ff = 128: the routed down-projection has a single 128-wide K-step, and the
+  shared one (two experts) two K segments of one step each.
 """
 import numpy as np
 import pytest
@@ -49,6 +51,8 @@ CASES = {
     "fp8_max_shared_8": _w("fp8_max_shared_8", T=200, d=512, n_routed=32, top_k=4, n_shared=8, d_ff=256,
                            seed=2705, ffn="fp8"),
     "f32_ragged_77": _w("f32_ragged_77", base=I.WORKLOADS["tiny_f32"], T=77),
+    "fp8_dff_128": _w("fp8_dff_128", T=300, d=256, n_routed=16, top_k=4, n_shared=2, d_ff=128, seed=2706,
+                      ffn="fp8"),
 }
 
 
