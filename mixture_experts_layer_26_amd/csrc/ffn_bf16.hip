@@ -261,7 +261,7 @@ __global__ __launch_bounds__(kThreads) void grouped_gemm_bf16(GemmArgs args) {
     c.seg_stride = (!routed && !GATED) ? args.b_expert_stride : 0;
     c.bstep = args.b_tiled ? (GATED ? 128 : 256) * BK : BK;
     c.kseg_steps = args.K / BK;
-    c.kseg_inv = static_cast<uint32_t>((0x100000000ull + c.kseg_steps - 1) / c.kseg_steps);
+    c.kseg_inv = kseg_recip(c.kseg_steps);
     c.nk = (routed ? args.K : args.K * (GATED ? 1 : args.k_segments)) / BK;
 
     f32x16 acc[4][2];

@@ -100,6 +100,7 @@ struct TileCtx {
 // the tile's rows loads no A.
 template <int ST>
 __device__ __forceinline__ void dma_step(const TileCtx& c, int kt) {
+  if (kt >= c.nk) return;  // past the last step (a K loop of one step)
   const int64_t aoff = static_cast<int64_t>(kt) * BK;
   const int64_t boff = b_offset(kt, c.kseg_steps, c.kseg_inv, c.seg_stride, c.bstep);
   if (c.load_a) {
@@ -214,6 +215,7 @@ __device__ __forceinline__ void step_barrier() {
 
 // Weight scales of K-step kt for this wave's two pairs of output blocks.
 __device__ __forceinline__ void wscales(const TileCtx& c, int kt, float (&sw)[2]) {
+  if (kt >= c.nk) kt = c.nk - 1;  // past the last step: any valid scale (not used)
   const int64_t o = b_offset(kt, c.kseg_steps, c.kseg_inv, c.sb_seg_stride, 1);
   sw[0] = c.sb[0][o];
   sw[1] = c.sb[1][o];
@@ -258,17 +260,11 @@ __device__ __forceinline__ void mainloop(const TileCtx& c, f32x4 (&acc)[8][4]) {
   }
   float sw[2];
   wscales(c, 0, sw);
-  if (c.nk == 1) {  // a single step (K = 128): nothing to load ahead
-    dma_step<0>(c, 0);
-    step_barrier();
-    k_step<0, NM, false>(c, 0, arow0, brow, lsa_off, lane, sw, acc);
-    return;
-  }
   int s = 0;
   if (c.nk & 1) {  // odd: step 0 from stage 1, the rest in pairs as below
     dma_step<1>(c, 0);
     step_barrier();
-    k_step<1, NM, true>(c, 0, arow0, brow, lsa_off, lane, sw, acc);
+    k_step<1, NM, true>(c, 0, arow0, brow, lsa_off, lane, sw, acc);  // nk = 1: loads nothing more
     s = 1;
   } else {
     dma_step<0>(c, 0);
@@ -278,8 +274,10 @@ __device__ __forceinline__ void mainloop(const TileCtx& c, f32x4 (&acc)[8][4]) {
     k_step<0, NM, true>(c, s, arow0, brow, lsa_off, lane, sw, acc);
     k_step<1, NM, true>(c, s + 1, arow0, brow, lsa_off, lane, sw, acc);
   }
-  k_step<0, NM, true>(c, s, arow0, brow, lsa_off, lane, sw, acc);
-  k_step<1, NM, false>(c, s + 1, arow0, brow, lsa_off, lane, sw, acc);
+  if (s < c.nk) {  // not for a single step
+    k_step<0, NM, true>(c, s, arow0, brow, lsa_off, lane, sw, acc);
+    k_step<1, NM, false>(c, s + 1, arow0, brow, lsa_off, lane, sw, acc);
+  }
 }
 
 __device__ __forceinline__ uint32_t e4m3(float x) {
@@ -385,7 +383,7 @@ __global__ __launch_bounds__(kThreads) void grouped_gemm_fp8(Fp8Args fa) {
     c.bstep = args.b_tiled ? (GATED ? 128 : 256) * BK : BK;
     c.sb_seg_stride = (!routed && !GATED) ? fa.sb_expert_stride : 0;
     c.kseg_steps = args.K / BK;
-    c.kseg_inv = static_cast<uint32_t>((0x100000000ull + c.kseg_steps - 1) / c.kseg_steps);
+    c.kseg_inv = kseg_recip(c.kseg_steps);
     c.nk = (routed ? args.K : args.K * (GATED ? 1 : args.k_segments)) / BK;
 
     f32x4 acc[8][4];

@@ -106,6 +106,11 @@ __device__ __forceinline__ Tile tile_at(const TileMap& tm, int L, int n_r, int b
   return t;
 }
 
+// The reciprocal b_offset takes for segments of kseg_steps K-steps.
+__host__ __device__ inline uint32_t kseg_recip(int kseg_steps) {
+  return static_cast<uint32_t>(((1ull << 31) + kseg_steps - 1) / kseg_steps);
+}
+
 // Tile claiming by gangs. Workgroup b is member b / 8 of gang b % 8; workgroups are
 // dispatched round-robin over the 8 XCDs, so a gang's members share one XCD and its L2.
 // A gang takes items of G = gridDim.x / 8 consecutive tiles and member i computes tile i
@@ -158,12 +163,12 @@ __device__ __forceinline__ int swz(int r, int c) { return r * kRowBytes + ((c ^ 
 
 // Element offset of K-step kt within a B row. For the shared down-projection the K
 // range runs over the shared experts' segments (seg selects the expert, seg_stride is
-// its distance); elsewhere kseg_steps == nk, so seg is 0. The quotient uses a
-// precomputed reciprocal kseg_inv = ceil(2^32 / kseg_steps), exact below 2^16 for
-// kseg_steps > 1; a segment of one step (2^32 does not fit) is taken directly.
+// its distance); elsewhere kseg_steps == nk, so seg is 0. The quotient is
+// floor(2 kt * kseg_inv / 2^32) with the precomputed kseg_inv = ceil(2^31 / kseg_steps)
+// (kseg_recip), exact while kt * kseg_steps < 2^31, and defined for kseg_steps = 1.
 __device__ __forceinline__ int64_t b_offset(int kt, int kseg_steps, uint32_t kseg_inv, int64_t seg_stride,
                                             int step_elems) {
-  const int seg = kseg_steps == 1 ? kt : static_cast<int>(__umulhi(static_cast<uint32_t>(kt), kseg_inv));
+  const int seg = static_cast<int>(__umulhi(2u * static_cast<uint32_t>(kt), kseg_inv));
   return static_cast<int64_t>(seg) * seg_stride + static_cast<int64_t>(kt - seg * kseg_steps) * step_elems;
 }
 

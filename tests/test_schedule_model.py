@@ -149,3 +149,14 @@ def test_tile_order():
     assert mt == [2, 0, 3, 1, 3, 36, 1]
     assert rpb == [150, 0, 200, 256, 171, 250, 70]
     assert order == [5, 6, 0, 2, 3, 4]
+
+
+def test_k_segment_reciprocal():
+    """b_offset's segment index: floor(2 kt * ceil(2^31 / d) / 2^32) equals kt // d for
+    every segment length d the kernels use (one step included) and every step index up
+    to the longest K loop (8 shared experts of d_ff 2048 in 64-wide bf16 steps: 256)."""
+    kt = np.arange(0, 4096, dtype=np.uint64)
+    for d in range(1, 2049):
+        inv = np.uint64(((1 << 31) + d - 1) // d)
+        seg = ((np.uint64(2) * kt) * inv) >> np.uint64(32)
+        assert np.array_equal(seg, kt // np.uint64(d)), d
