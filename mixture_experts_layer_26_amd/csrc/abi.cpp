@@ -149,7 +149,7 @@ bool backward_shape(const moe_shape* s) {
 }
 
 struct BwdWorkspace {
-  size_t zero, xs, h_r, da_r, dv_r, h_s, da_s, dv_s, total;
+  size_t zero, xs, h_r, da_r, dv_r, h_s, da_s, dv_s, a_r, v_r, a_s, v_s, total;
 };
 
 BwdWorkspace bwd_workspace(const moe_shape* s) {
@@ -173,6 +173,15 @@ BwdWorkspace bwd_workspace(const moe_shape* s) {
   off = align_up(off + ps);
   w.dv_s = off;
   off = align_up(off + ps);
+  // a and v in fp32 (twice the bf16 sizes), from the gate/up launch to the dh launch
+  w.a_r = off;
+  off = align_up(off + 2 * pr);
+  w.v_r = off;
+  off = align_up(off + 2 * pr);
+  w.a_s = off;
+  off = align_up(off + 2 * ps);
+  w.v_s = off;
+  off = align_up(off + 2 * ps);
   w.total = off;
   return w;
 }
@@ -554,6 +563,10 @@ moe_status moe_grouped_ffn_backward(const moe_shape* s, const void* u, const voi
   a.h_s = reinterpret_cast<uint16_t*>(wsb + w.h_s);
   a.da_s = reinterpret_cast<uint16_t*>(wsb + w.da_s);
   a.dv_s = reinterpret_cast<uint16_t*>(wsb + w.dv_s);
+  a.a_r = reinterpret_cast<float*>(wsb + w.a_r);
+  a.v_r = reinterpret_cast<float*>(wsb + w.v_r);
+  a.a_s = reinterpret_cast<float*>(wsb + w.a_s);
+  a.v_s = reinterpret_cast<float*>(wsb + w.v_s);
   a.dx_r = static_cast<uint16_t*>(dx_routed);
   a.dx_s = has_s ? dx_shared : nullptr;
   a.dw1r = static_cast<uint16_t*>(d_routed->dw1);

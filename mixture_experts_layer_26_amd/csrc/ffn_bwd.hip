@@ -6,12 +6,14 @@
 // gradient dY, a = X W1^T, v = X W3^T, h = SiLU(a) v and y = h W2^T:
 //   dh = dY W2,  da = dh v SiLU'(a),  dv = dh SiLU(a),  dX = da W1 + dv W3,
 //   dW1 = da^T X,  dW3 = dv^T X,  dW2 = dY^T h.
-// Four launches, each a grid of output tiles (v_mfma_f32_32x32x16_bf16, each wave a grid
+// Five launches, each a grid of output tiles (v_mfma_f32_32x32x16_bf16, each wave a grid
 // of 32 x 32 blocks), K through a ring of LDS stages filled by global_load_lds_dwordx4
 // (no staging registers):
-//   kGateUp: 128 rows x 128 d_ff tiles on 4 waves, K = d in steps of 64: a, v and dh in
-//            three accumulators; the epilogue forms h (as the forward does), da and dv
-//            and stores them in bf16.
+//   kAV:     256 rows x 128 d_ff tiles on 8 waves, K = d in steps of 64: a and v in two
+//            accumulators; the epilogue stores h (bf16, as the forward forms it) and a, v
+//            (fp32, for the next launch).
+//   kDh:     256 rows x 256 d_ff tiles on 8 waves (128 d_ff when d_ff % 256 != 0), K = d in
+//            steps of 64: dh; the epilogue reads a and v and stores da and dv in bf16.
 //   kDx:     256 rows x 256 d tiles on 8 waves, K = d_ff in steps of 32 (the shared
 //            experts' K ranges one after another): dX = da W1 + dv W3.
 //   kDw13:   128 d_ff x 128 d tiles per expert on 4 waves, K = the expert's rows: dW1, dW3
@@ -22,9 +24,9 @@
 // ends of short K loops.
 // The routed rows of X are read from a sorted copy of u (gathered once per call), so no
 // index lookups sit in the K loops.
-// Operands whose K is contiguous in memory (X, dY, da, dv in kGateUp/kDx, the rows of
-// W1/W3 in kGateUp) are staged as [rows][BK k] and read with ds_read_b128. Operands
-// whose K runs across rows (W2 in kGateUp, W1/W3 in kDx, everything in the weight
+// Operands whose K is contiguous in memory (X in kAV, dY in kDh, da, dv in kDx, the rows
+// of W1/W3 in kAV) are staged as [rows][BK k] and read with ds_read_b128. Operands
+// whose K runs across rows (W2 in kDh, W1/W3 in kDx, everything in the weight
 // gradients) are staged as they lie, [BK k][columns], and read with
 // ds_read_b64_tr_b16, which hands each lane four consecutive k of one column: within
 // 16 lanes, lane i receives column i of the 4 x 16 block whose rows the lanes'
@@ -37,7 +39,9 @@ namespace moe {
 
 namespace {
 
-enum { kGateUp = 0, kDx = 1, kDw13 = 2, kDw2 = 3 };
+enum { kDx = 1, kDw13 = 2, kDw2 = 3, kAV = 4, kDh = 5, kDh128 = 6 };
+// modes whose row tiles span d_ff columns, one group per shared expert
+template <int MODE> constexpr bool kRowsByFf = MODE == kAV || MODE == kDh || MODE == kDh128;
 
 // Per mode: NA A operands (M side) and NB B operands (N side) with their K-major flags;
 // NACC accumulators; a WM x WN grid of waves, each NMB x NNB blocks of 32 x 32, so the
@@ -46,10 +50,20 @@ enum { kGateUp = 0, kDx = 1, kDw13 = 2, kDw2 = 3 };
 // flight); BK: K per step. Operands whose K runs along their rows take whole 128-byte
 // lines per row with BK = 64; with BK = 32 each line is requested twice, a step apart.
 template <int MODE> struct Cfg;
-template <> struct Cfg<kGateUp> {  // A: X, dY (K-contiguous); B: W1, W3 (K-contig.), W2 (K-major)
-  static constexpr int NA = 2, NB = 3, NACC = 3, WM = 2, WN = 2, NMB = 2, NNB = 2, kOcc = 1, NST = 2, BK = 64;
+template <> struct Cfg<kAV> {  // A: X (K-contiguous); B: W1, W3 (K-contiguous)
+  static constexpr int NA = 1, NB = 2, NACC = 2, WM = 4, WN = 2, NMB = 2, NNB = 2, kOcc = 2, NST = 2, BK = 64;
   static constexpr bool a_km = false;
-  static constexpr bool b_km(int j) { return j == 2; }
+  static constexpr bool b_km(int) { return false; }
+};
+template <> struct Cfg<kDh> {  // A: dY (K-contiguous); B: W2 (K-major)
+  static constexpr int NA = 1, NB = 1, NACC = 1, WM = 2, WN = 4, NMB = 4, NNB = 2, kOcc = 2, NST = 2, BK = 64;
+  static constexpr bool a_km = false;
+  static constexpr bool b_km(int) { return true; }
+};
+template <> struct Cfg<kDh128> {  // as kDh, 128 d_ff columns per tile
+  static constexpr int NA = 1, NB = 1, NACC = 1, WM = 4, WN = 2, NMB = 2, NNB = 2, kOcc = 2, NST = 2, BK = 64;
+  static constexpr bool a_km = false;
+  static constexpr bool b_km(int) { return true; }
 };
 template <> struct Cfg<kDx> {  // A: da, dv (K-contiguous); B: W1, W3 (K-major)
   static constexpr int NA = 2, NB = 2, NACC = 1, WM = 2, WN = 4, NMB = 4, NNB = 2, kOcc = 2, NST = 2, BK = 32;
@@ -118,22 +132,22 @@ struct Ctx {
   int g;          // group: routed expert (< n_r) or shared expert / shared group
   bool shared;
   int64_t row0;   // first row of the group in the routed row space (routed) or 0 (shared)
-  int rows;       // rows of the group (kDw*: the K extent) or valid rows of the tile (kGateUp/kDx)
-  int64_t m0;     // tile's first row within the group (kGateUp/kDx), else 0
-  int c0;         // tile's first output column (kGateUp: d_ff; kDx: d)
+  int rows;       // rows of the group (kDw*: the K extent) or valid rows of the tile (row-tile modes)
+  int64_t m0;     // tile's first row within the group (row-tile modes), else 0
+  int c0;         // tile's first output column (kAV, kDh: d_ff; kDx: d)
   int mo, no;     // kDw*: tile's first output row / column
   int nk;         // K-steps
 };
 
-// Row tiles of kGateUp / kDx: groups are the routed experts, then the shared groups
-// (kGateUp: each shared expert; kDx: one group for all of them). The offsets are copied
+// Row tiles of kAV / kDh / kDx: groups are the routed experts, then the shared groups
+// (kAV, kDh: each shared expert; kDx: one group for all of them). The offsets are copied
 // to LDS (soff, n_r + 1 entries) and one thread walks the groups. Returns false past
 // the last tile.
 template <int MODE>
 __device__ bool decode_row_tile(const BwdArgs& a, int id, Ctx& c, int* sh, int* soff) {
   constexpr int TM = kTM<MODE>, TN = kTN<MODE>;
-  const int nsg = a.n_s == 0 ? 0 : (MODE == kGateUp ? a.n_s : 1);
-  const int ntn = (MODE == kGateUp ? a.F : a.d) / TN;
+  const int nsg = a.n_s == 0 ? 0 : (kRowsByFf<MODE> ? a.n_s : 1);
+  const int ntn = (kRowsByFf<MODE> ? a.F : a.d) / TN;
   for (int i = threadIdx.x; i <= a.n_r; i += blockDim.x) soff[i] = a.offset[i];
   __syncthreads();
   if (threadIdx.x == 0) {
@@ -172,19 +186,24 @@ template <int MODE>
 __device__ __forceinline__ const uint16_t* src(const BwdArgs& a, const Ctx& c, bool is_a, int op, int x, int y,
                                                int kt) {
   const int64_t F = a.F, d = a.d;
-  if constexpr (MODE == kGateUp) {
-    if (is_a) {  // X (sorted copy) or dY, row x of the tile, k = BK kt + 8 y
+  if constexpr (MODE == kAV) {
+    if (is_a) {  // X (sorted copy), row x of the tile, k = BK kt + 8 y
       const int64_t row = c.m0 + (x < c.rows ? x : c.rows - 1);
       const int64_t k = static_cast<int64_t>(Cfg<MODE>::BK) * kt + 8 * y;
-      if (op == 0) return c.shared ? a.u + row * d + k : a.xs + (c.row0 + row) * d + k;
+      return c.shared ? a.u + row * d + k : a.xs + (c.row0 + row) * d + k;
+    }
+    // W1 / W3 row c0 + x, k contiguous
+    const int e = c.shared ? c.g - a.n_r : c.g;
+    const uint16_t* w = c.shared ? (op == 0 ? a.w1s : a.w3s) : (op == 0 ? a.w1r : a.w3r);
+    return w + static_cast<int64_t>(e) * F * d + (c.c0 + x) * d + static_cast<int64_t>(Cfg<MODE>::BK) * kt + 8 * y;
+  } else if constexpr (MODE == kDh || MODE == kDh128) {
+    if (is_a) {  // dY, row x of the tile, k = BK kt + 8 y
+      const int64_t row = c.m0 + (x < c.rows ? x : c.rows - 1);
+      const int64_t k = static_cast<int64_t>(Cfg<MODE>::BK) * kt + 8 * y;
       return c.shared ? a.dout + row * d + k : a.dy_routed + (c.row0 + row) * d + k;
     }
-    const int e = c.shared ? c.g - a.n_r : c.g;
-    if (op < 2) {  // W1 / W3 row c0 + x, k contiguous
-      const uint16_t* w = c.shared ? (op == 0 ? a.w1s : a.w3s) : (op == 0 ? a.w1r : a.w3r);
-      return w + static_cast<int64_t>(e) * F * d + (c.c0 + x) * d + static_cast<int64_t>(Cfg<MODE>::BK) * kt + 8 * y;
-    }
     // W2 [d][d_ff]: K-row BK kt + x, columns c0 + y
+    const int e = c.shared ? c.g - a.n_r : c.g;
     const uint16_t* w = c.shared ? a.w2s : a.w2r;
     const int64_t k = static_cast<int64_t>(Cfg<MODE>::BK) * kt + x;
     return w + static_cast<int64_t>(e) * d * F + k * F + c.c0 + y;
@@ -316,10 +335,9 @@ __device__ __forceinline__ void compute(const unsigned char* base,
       for (int nb = 0; nb < NNB; ++nb) {
         // the n-side fragment goes first, so each lane's accumulator holds 4 consecutive
         // output columns of one output row (see the epilogue)
-        if constexpr (MODE == kGateUp) {
+        if constexpr (MODE == kAV) {
           acc[0][mb][nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fb[0][nb], fa[0][mb], acc[0][mb][nb], 0, 0, 0);
           acc[1][mb][nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fb[1][nb], fa[0][mb], acc[1][mb][nb], 0, 0, 0);
-          acc[2][mb][nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fb[2][nb], fa[1][mb], acc[2][mb][nb], 0, 0, 0);
         } else if constexpr (MODE == kDx) {
           acc[0][mb][nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fb[0][nb], fa[0][mb], acc[0][mb][nb], 0, 0, 0);
           acc[0][mb][nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fb[1][nb], fa[1][mb], acc[0][mb][nb], 0, 0, 0);
@@ -350,9 +368,9 @@ __global__ __launch_bounds__(64 * kWaves<MODE>, Cfg<MODE>::kOcc) void ffn_bwd_ke
   const int wm = w / Cfg<MODE>::WN, wn = w % Cfg<MODE>::WN;
 
   Ctx c{};
-  if constexpr (MODE == kGateUp || MODE == kDx) {
+  if constexpr (kRowsByFf<MODE> || MODE == kDx) {
     if (!decode_row_tile<MODE>(a, blockIdx.x, c, sh, soff)) return;
-    if constexpr (MODE == kGateUp)
+    if constexpr (kRowsByFf<MODE>)
       c.nk = a.d / BK;
     else
       c.nk = (c.shared ? a.n_s * a.F : a.F) / BK;
@@ -408,33 +426,49 @@ __global__ __launch_bounds__(64 * kWaves<MODE>, Cfg<MODE>::kOcc) void ffn_bwd_ke
       for (int p = 0; p < 4; ++p) {
         const int r = (TM / Cfg<MODE>::WM) * wm + 32 * mb + m_in;
         const int n = (TN / Cfg<MODE>::WN) * wn + 32 * nb + 8 * p + 4 * (lane / 32);
-        if constexpr (MODE == kGateUp) {
+        if constexpr (kRowsByFf<MODE>) {
           if (r >= c.rows) continue;
-          float hv[4], dav[4], dvv[4];
-#pragma unroll
-          for (int q = 0; q < 4; ++q) {
-            const float av = acc[0][mb][nb][4 * p + q], vv = acc[1][mb][nb][4 * p + q];
-            const float dh = acc[2][mb][nb][4 * p + q];
-            const float sg = fast_sigmoid(av);
-            const float silu_a = av * sg;
-            hv[q] = silu_a * vv;
-            dav[q] = dh * vv * sg * (1.0f + av * (1.0f - sg));
-            dvv[q] = dh * silu_a;
-          }
           const int64_t row = c.m0 + r;
           const int64_t col = c.c0 + n;
           int64_t o;
-          uint16_t *hb, *dab, *dvb;
-          if (c.shared) {
+          if (c.shared)
             o = row * (a.n_s * static_cast<int64_t>(a.F)) + static_cast<int64_t>(c.g - a.n_r) * a.F + col;
-            hb = a.h_s; dab = a.da_s; dvb = a.dv_s;
-          } else {
+          else
             o = (c.row0 + row) * a.F + col;
-            hb = a.h_r; dab = a.da_r; dvb = a.dv_r;
+          if constexpr (MODE == kAV) {  // h = SiLU(a) v as the forward forms it; a, v kept in fp32
+            float hv[4];
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+              const float av = acc[0][mb][nb][4 * p + q], vv = acc[1][mb][nb][4 * p + q];
+              hv[q] = av * fast_sigmoid(av) * vv;
+            }
+            *reinterpret_cast<uint2*>((c.shared ? a.h_s : a.h_r) + o) =
+                make_uint2(pack_bf16x2(hv[0], hv[1]), pack_bf16x2(hv[2], hv[3]));
+            const f32x16& x0 = acc[0][mb][nb];
+            const f32x16& x1 = acc[1][mb][nb];
+            *reinterpret_cast<float4*>((c.shared ? a.a_s : a.a_r) + o) =
+                make_float4(x0[4 * p], x0[4 * p + 1], x0[4 * p + 2], x0[4 * p + 3]);
+            *reinterpret_cast<float4*>((c.shared ? a.v_s : a.v_r) + o) =
+                make_float4(x1[4 * p], x1[4 * p + 1], x1[4 * p + 2], x1[4 * p + 3]);
+          } else {  // da = dh v SiLU'(a), dv = dh SiLU(a)
+            const float4 a4 = *reinterpret_cast<const float4*>((c.shared ? a.a_s : a.a_r) + o);
+            const float4 v4 = *reinterpret_cast<const float4*>((c.shared ? a.v_s : a.v_r) + o);
+            const float aa[4] = {a4.x, a4.y, a4.z, a4.w}, vv4[4] = {v4.x, v4.y, v4.z, v4.w};
+            float dav[4], dvv[4];
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+              const float av = aa[q], vv = vv4[q];
+              const float dh = acc[0][mb][nb][4 * p + q];
+              const float sg = fast_sigmoid(av);
+              const float silu_a = av * sg;
+              dav[q] = dh * vv * sg * (1.0f + av * (1.0f - sg));
+              dvv[q] = dh * silu_a;
+            }
+            *reinterpret_cast<uint2*>((c.shared ? a.da_s : a.da_r) + o) =
+                make_uint2(pack_bf16x2(dav[0], dav[1]), pack_bf16x2(dav[2], dav[3]));
+            *reinterpret_cast<uint2*>((c.shared ? a.dv_s : a.dv_r) + o) =
+                make_uint2(pack_bf16x2(dvv[0], dvv[1]), pack_bf16x2(dvv[2], dvv[3]));
           }
-          *reinterpret_cast<uint2*>(hb + o) = make_uint2(pack_bf16x2(hv[0], hv[1]), pack_bf16x2(hv[2], hv[3]));
-          *reinterpret_cast<uint2*>(dab + o) = make_uint2(pack_bf16x2(dav[0], dav[1]), pack_bf16x2(dav[2], dav[3]));
-          *reinterpret_cast<uint2*>(dvb + o) = make_uint2(pack_bf16x2(dvv[0], dvv[1]), pack_bf16x2(dvv[2], dvv[3]));
         } else {
           const f32x16& x0 = acc[0][mb][nb];
           if constexpr (MODE == kDx) {
@@ -482,15 +516,24 @@ __global__ __launch_bounds__(256) void gather_rows_kernel(const uint16_t* __rest
   }
 }
 
-}  // namespace
-
-int64_t bwd_row_tiles(int mode, int64_t T, int K, int n_r, int n_s, int d, int F) {
-  const int64_t P = T * K;
-  const int64_t TM = mode == 0 ? kTM<kGateUp> : kTM<kDx>;
-  const int64_t ntn = mode == 0 ? F / kTN<kGateUp> : d / kTN<kDx>;
-  const int64_t nsg = n_s == 0 ? 0 : (mode == 0 ? n_s : 1);
+// Row tiles of a row-tile launch: routed rows in blocks of TM per expert (at most
+// P / TM + n_r blocks), shared rows in blocks of TM per shared group, times the column tiles.
+template <int MODE>
+int64_t row_tiles(int64_t T, int K, int n_r, int n_s, int d, int F) {
+  const int64_t P = T * K, TM = kTM<MODE>;
+  const int64_t ntn = (kRowsByFf<MODE> ? F : d) / kTN<MODE>;
+  const int64_t nsg = n_s == 0 ? 0 : (kRowsByFf<MODE> ? n_s : 1);
   return ((P + TM - 1) / TM + n_r + nsg * ((T + TM - 1) / TM)) * ntn;
 }
+
+template <int MODE>
+hipError_t launch_rows(const BwdArgs& a, hipStream_t stream) {
+  const unsigned g = static_cast<unsigned>(row_tiles<MODE>(a.T, a.K, a.n_r, a.n_s, a.d, a.F));
+  hipLaunchKernelGGL(ffn_bwd_kernel<MODE>, dim3(g), dim3(64 * kWaves<MODE>), 0, stream, a);
+  return hipGetLastError();
+}
+
+}  // namespace
 
 hipError_t launch_ffn_backward(const BwdArgs& a, hipStream_t stream) {
   const int64_t chunks = a.T * a.K * (a.d / 8);
@@ -499,12 +542,10 @@ hipError_t launch_ffn_backward(const BwdArgs& a, hipStream_t stream) {
                      a.T * a.K, a.d);
   hipError_t err = hipGetLastError();
   if (err != hipSuccess) return err;
-  const unsigned g1 = static_cast<unsigned>(bwd_row_tiles(0, a.T, a.K, a.n_r, a.n_s, a.d, a.F));
-  hipLaunchKernelGGL(ffn_bwd_kernel<kGateUp>, dim3(g1), dim3(64 * kWaves<kGateUp>), 0, stream, a);
-  if ((err = hipGetLastError()) != hipSuccess) return err;
-  const unsigned g2 = static_cast<unsigned>(bwd_row_tiles(1, a.T, a.K, a.n_r, a.n_s, a.d, a.F));
-  hipLaunchKernelGGL(ffn_bwd_kernel<kDx>, dim3(g2), dim3(64 * kWaves<kDx>), 0, stream, a);
-  if ((err = hipGetLastError()) != hipSuccess) return err;
+  if ((err = launch_rows<kAV>(a, stream)) != hipSuccess) return err;
+  if ((err = (a.F % kTN<kDh> == 0 ? launch_rows<kDh>(a, stream) : launch_rows<kDh128>(a, stream))) != hipSuccess)
+    return err;
+  if ((err = launch_rows<kDx>(a, stream)) != hipSuccess) return err;
   const int64_t groups = a.n_r + a.n_s;
   const unsigned g3 = static_cast<unsigned>(groups * (a.F / kTM<kDw13>) * (a.d / kTN<kDw13>));
   hipLaunchKernelGGL(ffn_bwd_kernel<kDw13>, dim3(g3), dim3(64 * kWaves<kDw13>), 0, stream, a);

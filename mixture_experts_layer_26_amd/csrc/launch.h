@@ -132,6 +132,8 @@ struct BwdArgs {
   const uint16_t *w1s, *w3s, *w2s;  // shared weights (n_s experts)
   uint16_t *h_r, *da_r, *dv_r;   // workspace [P, d_ff]: h, da, dv of the routed rows
   uint16_t *h_s, *da_s, *dv_s;   // workspace [T, n_s * d_ff]
+  float *a_r, *v_r;              // workspace [P, d_ff]: a = X W1^T, v = X W3^T (fp32)
+  float *a_s, *v_s;              // workspace [T, n_s * d_ff]
   uint16_t* xs;                  // workspace [P, d]: u of the sorted rows
   uint16_t* zero;                // workspace, 256 bytes cleared by the call
   uint16_t* dx_r;                // out [P, d] bf16
@@ -141,7 +143,6 @@ struct BwdArgs {
   int64_t T;
   int K, d, F, n_r, n_s;
 };
-int64_t bwd_row_tiles(int mode, int64_t T, int K, int n_r, int n_s, int d, int F);
 hipError_t launch_ffn_backward(const BwdArgs& args, hipStream_t stream);
 
 hipError_t launch_combine_backward(const void* dout, const void* y_routed, const int32_t* pair_row,
