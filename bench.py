@@ -14,7 +14,7 @@ launch stream, and the CPU oracle timed on a bounded sample of the same workload
 
 --backward times the layer backward instead (moe_combine_backward ->
 moe_grouped_ffn_backward -> moe_route_backward after one forward step, row-major bf16
-weights) and prints its own line, with the roofline of the grouped FFN backward (four
+weights) and prints its own line, with the roofline of the grouped FFN backward (five
 MFMA launches: 16 d d_ff FLOPs per expert row).
 
 --balance S runs S layer steps over fresh token batches with the bias carried from step
@@ -284,7 +284,7 @@ def bench_backward(args):
         "call_ms": calls,
         "roofline": {"bound": "mfma", "achieved": round(tf, 2), "peak": PEAKS["bf16"], "unit": "TFLOP/s",
                      "frac": round(tf / PEAKS["bf16"], 4), "traffic": None,
-                     "kernel": "grouped FFN backward (gate/up recompute + dh, dX, dW1/dW3, dW2)",
+                     "kernel": "grouped FFN backward (gate/up recompute, dh, dX, dW1/dW3, dW2)",
                      "ms_per_launch": ffn_ms, "algorithmic_flops": flops},
     }
     if args.cpu:
