@@ -46,12 +46,4 @@ __device__ __forceinline__ void lds_barrier() {
   asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
 }
 
-// XCD-aware ordering: workgroups are dispatched round-robin over the 8 XCDs, so
-// workgroup b runs on XCD b % 8. Returns the index b would have if the grid were
-// split into 8 contiguous chunks, one per XCD (grid must be a multiple of 8).
-__device__ __forceinline__ int xcd_major(int b, int grid) {
-  const int per = grid / 8;
-  return (b % 8) * per + (b / 8);
-}
-
 }  // namespace moe
