@@ -10,13 +10,16 @@
 // Phase 1 writes H = SiLU(gate) * up quantised per 1 x 128 (codes + fp32 scales);
 // phase 2 writes y (bf16 routed rows, fp32 shared sum).
 //
-// The tile walk, tile claiming, LDS layout and ping-pong schedule are those of the bf16
-// kernel (256 x 256 tiles, 128-byte rows per K-step, so one K-step is exactly one
-// 128-wide scale block). The MFMA is v_mfma_scale_f32_16x16x128_f8f6f4 with unit
-// (E8M0 = 127) scales: one instruction covers one scale block of a 16 x 16 output
-// block, starting from zero, and its result is folded into the accumulator with one
-// fp32 FMA per element: acc += blk * (s_a[row] * s_w). The fp32 scales are arbitrary
-// (not powers of two), so they cannot ride in the MFMA's E8M0 scale operands.
+// The tile walk, tile claiming and LDS layout are those of the bf16 kernel (256 x 256
+// tiles, 128-byte rows per K-step, so one K-step is exactly one 128-wide scale block),
+// with two stages: step s+1 is loaded while step s is computed. The MFMA is
+// v_mfma_scale_f32_16x16x128_f8f6f4 with unit (E8M0 = 127) scales: one instruction
+// covers one scale block of a 16 x 16 output block, starting from zero, and its result
+// is folded into the accumulator with one fp32 FMA per element:
+// acc += blk * (s_a[row] * s_w). The fp32 scales are arbitrary (not powers of two), so
+// they cannot ride in the MFMA's E8M0 scale operands. The A-row scales arrive in LDS
+// with the tiles (K-block-major in memory, so a step's scales of a tile are contiguous);
+// the weight scales are read by scalar loads.
 #include "gemm_common.h"
 #include "launch.h"
 
