@@ -359,7 +359,7 @@ def cpu_baseline_backward(w, n_tokens: int):
 def main():
     args = parse()
     if args.gpus != 1:
-        print(json.dumps({"error": "this build runs on one GPU only; --gpus must be 1"}))
+        print(json.dumps({"error": "the benchmark runs on one GPU (the layer on one GPU's share); --gpus must be 1"}))
         sys.exit(2)
     import torch
 
