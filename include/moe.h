@@ -45,7 +45,7 @@
 extern "C" {
 #endif
 
-#define MOE_ABI_VERSION 3
+#define MOE_ABI_VERSION 4
 
 typedef enum {
   MOE_OK = 0,
@@ -65,12 +65,20 @@ typedef enum { MOE_F32 = 0, MOE_BF16 = 1, MOE_FP8_E4M3 = 2 } moe_dtype;
 typedef enum { MOE_SCORE_SIGMOID = 0, MOE_SCORE_SOFTMAX = 1 } moe_score;
 
 /* Layer shape.
- *   T        tokens in the batch (>= 1)
- *   d        hidden size (multiple of 8; multiple of 128 when ffn == MOE_FP8_E4M3)
+ *   T        tokens in the batch (>= 0). An empty batch (T = 0) is valid: arrays whose
+ *            size scales with T may then be NULL, and each call only defines its outputs
+ *            that do not: moe_dispatch zeroes expert_count and expert_offset,
+ *            moe_bias_update leaves the bias unchanged (every count equals the mean, 0),
+ *            moe_grouped_ffn_backward zeroes the weight gradients and moe_route_backward
+ *            the centroid gradient; the other calls return MOE_OK and do nothing.
+ *   d        hidden size (multiple of 64, at least 64)
  *   n_routed routed experts N_r (1..256)
  *   top_k    experts per token K (1..min(N_r, 16))
  *   n_shared shared experts N_s (0..8)
- *   d_ff     SwiGLU intermediate size per expert (multiple of 64; of 128 for FP8)
+ *   d_ff     SwiGLU intermediate size per expert (multiple of 64, at least 64)
+ *            The bf16 and FP8 expert GEMMs need d % 256 == 0 and d_ff % 128 == 0
+ *            (moe_grouped_ffn returns MOE_ERR_UNSUPPORTED otherwise); fp32 takes any valid
+ *            shape.
  *   act      dtype of u, the centroids and the output: MOE_F32 or MOE_BF16
  *   ffn      dtype of the expert GEMM operands: MOE_F32 (with act F32), MOE_BF16 or
  *            MOE_FP8_E4M3 (both with act BF16)
@@ -263,8 +271,8 @@ moe_status moe_route_backward(const moe_shape* shape, const void* u, const void*
                               size_t ws_bytes, void* stream);
 
 /* workspace sizing: call = MOE_CALL_ROUTE, MOE_CALL_DISPATCH, MOE_CALL_GROUPED_FFN,
- * MOE_CALL_GROUPED_FFN_BACKWARD or MOE_CALL_ROUTE_BACKWARD; 0 for others and for invalid
- * shapes */
+ * MOE_CALL_GROUPED_FFN_BACKWARD or MOE_CALL_ROUTE_BACKWARD; 0 for others, for invalid
+ * shapes and for an empty batch (T = 0: no call needs a workspace, ws may be NULL) */
 enum { MOE_CALL_ROUTE = 0, MOE_CALL_DISPATCH = 1, MOE_CALL_GROUPED_FFN = 2,
        MOE_CALL_COMBINE = 3, MOE_CALL_BIAS_UPDATE = 4, MOE_CALL_GROUPED_FFN_BACKWARD = 5,
        MOE_CALL_ROUTE_BACKWARD = 6 };

@@ -20,7 +20,7 @@ MOE_CALL_GROUPED_FFN_BACKWARD, MOE_CALL_ROUTE_BACKWARD = 5, 6
 MOE_LAYOUT_ROWS, MOE_LAYOUT_TILED = 0, 1
 MOE_W1, MOE_W3, MOE_W2 = 0, 1, 2
 MOE_SCORE_SIGMOID, MOE_SCORE_SOFTMAX = 0, 1
-ABI_VERSION = 3
+ABI_VERSION = 4
 DTYPES = {"f32": MOE_F32, "bf16": MOE_BF16, "fp8": MOE_FP8_E4M3}
 SCORES = {"sigmoid": MOE_SCORE_SIGMOID, "softmax": MOE_SCORE_SOFTMAX}
 

@@ -18,7 +18,7 @@ size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
 
 bool valid_shape(const moe_shape* s) {
   if (!s) return false;
-  if (s->T < 1 || s->T > (1LL << 26)) return false;
+  if (s->T < 0 || s->T > (1LL << 26)) return false;
   if (s->n_routed < 1 || s->n_routed > 256) return false;
   if (s->top_k < 1 || s->top_k > 16 || s->top_k > s->n_routed) return false;
   if (s->n_shared < 0 || s->n_shared > 8) return false;
@@ -29,6 +29,23 @@ bool valid_shape(const moe_shape* s) {
   const bool fp8 = s->act == MOE_BF16 && s->ffn == MOE_FP8_E4M3;
   if (s->score != MOE_SCORE_SIGMOID && s->score != MOE_SCORE_SOFTMAX) return false;
   return f32 || bf16 || fp8;
+}
+
+// Arrays whose size scales with T may be NULL for an empty batch (T = 0).
+bool ok_t(const moe_shape* s, const void* p) { return p != nullptr || s->T == 0; }
+
+// Clears `bytes` (a multiple of 4) with a fill kernel, in pieces of at most 2^30 words.
+hipError_t zero_bytes(void* p, size_t bytes, hipStream_t stream) {
+  int32_t* q = static_cast<int32_t*>(p);
+  size_t words = bytes / 4;
+  while (words > 0) {
+    const size_t n = words < (size_t(1) << 30) ? words : (size_t(1) << 30);
+    const hipError_t e = moe::launch_zero_i32(q, static_cast<int>(n), stream);
+    if (e != hipSuccess) return e;
+    q += n;
+    words -= n;
+  }
+  return hipSuccess;
 }
 
 // shapes the MFMA kernels tile exactly: output columns of the gated phase in 128s, of
@@ -299,7 +316,7 @@ const char* moe_status_string(moe_status st) {
 }
 
 size_t moe_workspace_bytes(const moe_shape* s, int32_t call) {
-  if (!valid_shape(s)) return 0;
+  if (!valid_shape(s) || s->T == 0) return 0;  // an empty batch needs no workspace
   if (call == MOE_CALL_DISPATCH)
     return align_up(static_cast<size_t>(moe::dispatch_blocks(s->T)) * s->n_routed * sizeof(int32_t));
   if (call == MOE_CALL_GROUPED_FFN) return ffn_workspace(s).total;
@@ -313,9 +330,11 @@ size_t moe_workspace_bytes(const moe_shape* s, int32_t call) {
 
 moe_status moe_route(const moe_shape* s, const void* u, const void* centroids, const float* bias,
                      int32_t* topk_idx, float* topk_gate, void* ws, size_t ws_bytes, void* stream) {
-  if (!valid_shape(s) || !u || !centroids || !topk_idx || !topk_gate) return MOE_ERR_INVALID_ARG;
+  if (!valid_shape(s) || !ok_t(s, u) || !centroids || !ok_t(s, topk_idx) || !ok_t(s, topk_gate))
+    return MOE_ERR_INVALID_ARG;
   const bool softmax = s->score == MOE_SCORE_SOFTMAX;
   if (!bias && !softmax) return MOE_ERR_INVALID_ARG;
+  if (s->T == 0) return MOE_OK;
   const size_t need = moe_workspace_bytes(s, MOE_CALL_ROUTE);
   if (need > 0 && (!ws || ws_bytes < need)) return MOE_ERR_WORKSPACE;
   return from_hip(moe::launch_route(s->act == MOE_BF16 ? 1 : 0, softmax ? 1 : 0, u, centroids,
@@ -326,8 +345,14 @@ moe_status moe_route(const moe_shape* s, const void* u, const void* centroids, c
 moe_status moe_dispatch(const moe_shape* s, const int32_t* topk_idx, int32_t* expert_count,
                         int32_t* expert_offset, int32_t* sorted_token, int32_t* pair_row, void* ws,
                         size_t ws_bytes, void* stream) {
-  if (!valid_shape(s) || !topk_idx || !expert_count || !expert_offset || !sorted_token || !pair_row)
+  if (!valid_shape(s) || !ok_t(s, topk_idx) || !expert_count || !expert_offset || !ok_t(s, sorted_token) ||
+      !ok_t(s, pair_row))
     return MOE_ERR_INVALID_ARG;
+  if (s->T == 0) {  // no pairs: every count and offset is zero
+    hipError_t e = zero_bytes(expert_count, sizeof(int32_t) * s->n_routed, as_stream(stream));
+    if (e == hipSuccess) e = zero_bytes(expert_offset, sizeof(int32_t) * (s->n_routed + 1), as_stream(stream));
+    return from_hip(e);
+  }
   if (!ws || ws_bytes < moe_workspace_bytes(s, MOE_CALL_DISPATCH)) return MOE_ERR_WORKSPACE;
   const int64_t P = s->T * s->top_k;
   if (moe_status d = debug_check({range(topk_idx, P, 0, s->n_routed)}, stream)) return d;
@@ -340,10 +365,10 @@ moe_status moe_grouped_ffn(const moe_shape* s, const void* u, const int32_t* exp
                            const int32_t* sorted_token, const moe_expert_set* routed,
                            const moe_expert_set* shared, void* y_routed, float* y_shared, void* ws,
                            size_t ws_bytes, void* stream) {
-  if (!valid_shape(s) || !u || !expert_offset || !sorted_token || !routed || !y_routed)
+  if (!valid_shape(s) || !ok_t(s, u) || !expert_offset || !ok_t(s, sorted_token) || !routed || !ok_t(s, y_routed))
     return MOE_ERR_INVALID_ARG;
   if (!routed->w1 || !routed->w3 || !routed->w2) return MOE_ERR_INVALID_ARG;
-  if (s->n_shared > 0 && (!shared || !shared->w1 || !shared->w3 || !shared->w2 || !y_shared))
+  if (s->n_shared > 0 && (!shared || !shared->w1 || !shared->w3 || !shared->w2 || !ok_t(s, y_shared)))
     return MOE_ERR_INVALID_ARG;
   const bool fp8 = s->ffn == MOE_FP8_E4M3;
   if (fp8 && (!routed->s1 || !routed->s3 || !routed->s2 ||
@@ -354,6 +379,7 @@ moe_status moe_grouped_ffn(const moe_shape* s, const void* u, const int32_t* exp
   const int b_tiled = routed->layout == MOE_LAYOUT_TILED ? 1 : 0;
   if (b_tiled && s->ffn == MOE_F32) return MOE_ERR_UNSUPPORTED;
   if (!tiled_shape(s)) return MOE_ERR_UNSUPPORTED;
+  if (s->T == 0) return MOE_OK;
   const FfnWorkspace w = ffn_workspace(s);
   if (!ws || ws_bytes < w.total) return MOE_ERR_WORKSPACE;
   hipStream_t st = as_stream(stream);
@@ -450,9 +476,11 @@ moe_status moe_grouped_ffn(const moe_shape* s, const void* u, const int32_t* exp
 moe_status moe_combine(const moe_shape* s, const void* u, const void* y_routed,
                        const float* y_shared, const int32_t* pair_row, const float* topk_gate,
                        void* out, void* stream) {
-  if (!valid_shape(s) || !u || !y_routed || !pair_row || !topk_gate || !out)
+  if (!valid_shape(s) || !ok_t(s, u) || !ok_t(s, y_routed) || !ok_t(s, pair_row) || !ok_t(s, topk_gate) ||
+      !ok_t(s, out))
     return MOE_ERR_INVALID_ARG;
-  if (s->n_shared > 0 && !y_shared) return MOE_ERR_INVALID_ARG;
+  if (s->n_shared > 0 && !ok_t(s, y_shared)) return MOE_ERR_INVALID_ARG;
+  if (s->T == 0) return MOE_OK;
   if (out == u) return MOE_ERR_INVALID_ARG;
   if (moe_status d = debug_check({range(pair_row, s->T * s->top_k, 0, static_cast<int32_t>(s->T * s->top_k))},
                                  stream))
@@ -503,9 +531,11 @@ moe_status moe_quantize_fp8(const void* x, int32_t xt, int64_t rows, int64_t col
 moe_status moe_combine_backward(const moe_shape* s, const void* dout, const void* y_routed,
                                 const int32_t* pair_row, const float* topk_gate, void* dy_routed, float* dgate,
                                 void* stream) {
-  if (!valid_shape(s) || !dout || !y_routed || !pair_row || !topk_gate || !dy_routed || !dgate)
+  if (!valid_shape(s) || !ok_t(s, dout) || !ok_t(s, y_routed) || !ok_t(s, pair_row) || !ok_t(s, topk_gate) ||
+      !ok_t(s, dy_routed) || !ok_t(s, dgate))
     return MOE_ERR_INVALID_ARG;
   if (!backward_shape(s)) return MOE_ERR_UNSUPPORTED;
+  if (s->T == 0) return MOE_OK;
   if (moe_status d = debug_check({range(pair_row, s->T * s->top_k, 0, static_cast<int32_t>(s->T * s->top_k))},
                                  stream))
     return d;
@@ -519,19 +549,30 @@ moe_status moe_grouped_ffn_backward(const moe_shape* s, const void* u, const voi
                                     const void* dy_routed, void* dx_routed, float* dx_shared,
                                     const moe_expert_grads* d_routed, const moe_expert_grads* d_shared, void* ws,
                                     size_t ws_bytes, void* stream) {
-  if (!valid_shape(s) || !u || !dout || !expert_offset || !sorted_token || !routed || !dy_routed || !dx_routed ||
-      !d_routed)
+  if (!valid_shape(s) || !ok_t(s, u) || !ok_t(s, dout) || !expert_offset || !ok_t(s, sorted_token) || !routed ||
+      !ok_t(s, dy_routed) || !ok_t(s, dx_routed) || !d_routed)
     return MOE_ERR_INVALID_ARG;
   if (!routed->w1 || !routed->w3 || !routed->w2 || !d_routed->dw1 || !d_routed->dw3 || !d_routed->dw2)
     return MOE_ERR_INVALID_ARG;
   if (s->n_shared > 0) {
-    if (!shared || !shared->w1 || !shared->w3 || !shared->w2 || !dx_shared || !d_shared || !d_shared->dw1 ||
-        !d_shared->dw3 || !d_shared->dw2)
+    if (!shared || !shared->w1 || !shared->w3 || !shared->w2 || !ok_t(s, dx_shared) || !d_shared ||
+        !d_shared->dw1 || !d_shared->dw3 || !d_shared->dw2)
       return MOE_ERR_INVALID_ARG;
   }
   if (!backward_shape(s)) return MOE_ERR_UNSUPPORTED;
   if (routed->layout != MOE_LAYOUT_ROWS || (s->n_shared > 0 && shared->layout != MOE_LAYOUT_ROWS))
     return MOE_ERR_UNSUPPORTED;
+  if (s->T == 0) {  // no rows: every weight gradient is zero
+    const size_t m = sizeof(uint16_t) * s->d * s->d_ff;  // one weight matrix
+    hipStream_t st = as_stream(stream);
+    hipError_t e = hipSuccess;
+    for (void* p : {d_routed->dw1, d_routed->dw3, d_routed->dw2})
+      if (e == hipSuccess) e = zero_bytes(p, m * s->n_routed, st);
+    if (s->n_shared > 0)
+      for (void* p : {d_shared->dw1, d_shared->dw3, d_shared->dw2})
+        if (e == hipSuccess) e = zero_bytes(p, m * s->n_shared, st);
+    return from_hip(e);
+  }
   const BwdWorkspace w = bwd_workspace(s);
   if (!ws || ws_bytes < w.total) return MOE_ERR_WORKSPACE;
   {
@@ -589,11 +630,14 @@ moe_status moe_route_backward(const moe_shape* s, const void* u, const void* cen
                               const int32_t* sorted_token, const int32_t* pair_row, const void* dout,
                               const void* dx_routed, const float* dx_shared, void* du, void* dcentroids, float* dz,
                               void* ws, size_t ws_bytes, void* stream) {
-  if (!valid_shape(s) || !u || !centroids || !topk_idx || !topk_gate || !dgate || !expert_offset ||
-      !sorted_token || !pair_row || !dout || !dx_routed || !du || !dcentroids || !dz)
+  if (!valid_shape(s) || !ok_t(s, u) || !centroids || !ok_t(s, topk_idx) || !ok_t(s, topk_gate) ||
+      !ok_t(s, dgate) || !expert_offset || !ok_t(s, sorted_token) || !ok_t(s, pair_row) || !ok_t(s, dout) ||
+      !ok_t(s, dx_routed) || !ok_t(s, du) || !dcentroids || !ok_t(s, dz))
     return MOE_ERR_INVALID_ARG;
-  if (s->n_shared > 0 && !dx_shared) return MOE_ERR_INVALID_ARG;
+  if (s->n_shared > 0 && !ok_t(s, dx_shared)) return MOE_ERR_INVALID_ARG;
   if (!backward_shape(s)) return MOE_ERR_UNSUPPORTED;
+  if (s->T == 0)  // no tokens: the centroid gradient is zero
+    return from_hip(zero_bytes(dcentroids, sizeof(uint16_t) * s->n_routed * s->d, as_stream(stream)));
   if (!ws || ws_bytes < moe_workspace_bytes(s, MOE_CALL_ROUTE_BACKWARD)) return MOE_ERR_WORKSPACE;
   {
     const int64_t P = s->T * s->top_k;

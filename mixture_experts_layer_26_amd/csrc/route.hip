@@ -260,7 +260,7 @@ __global__ __launch_bounds__(kThreads) void route_kernel(const float* __restrict
 RouteChunks route_chunks(int64_t T, int d) {
   // enough (token block, K chunk) workgroups to fill the chip: about 512, at most 32
   // chunks, each a whole number of 64-wide K-steps
-  const int64_t blocks = (T + kTB - 1) / kTB;
+  const int64_t blocks = T > 0 ? (T + kTB - 1) / kTB : 1;
   const int nsteps = d / kLK;
   int64_t want = (512 + blocks - 1) / blocks;
   const int cap = nsteps < 32 ? nsteps : 32;

@@ -23,7 +23,7 @@ def test_exports_every_declared_symbol():
     assert {"moe_route", "moe_dispatch", "moe_grouped_ffn", "moe_combine", "moe_bias_update"} <= set(names)
     for n in names:
         assert hasattr(lib, n), n
-    assert lib.moe_abi_version() == abi.ABI_VERSION == 3
+    assert lib.moe_abi_version() == abi.ABI_VERSION == 4
     assert lib.moe_status_string(0) == b"ok"
 
 
@@ -36,7 +36,7 @@ def _shape(**kw):
 FAKE = 0x1000  # never dereferenced: every call below is rejected on the host
 
 
-@pytest.mark.parametrize("kw", [dict(T=0), dict(top_k=0), dict(top_k=17, n_routed=32), dict(top_k=20),
+@pytest.mark.parametrize("kw", [dict(T=-1), dict(top_k=0), dict(top_k=17, n_routed=32), dict(top_k=20),
                                 dict(n_routed=0), dict(n_routed=257), dict(d=100), dict(d_ff=100),
                                 dict(n_shared=9), dict(act="f32", ffn="bf16"), dict(act="bf16", ffn="f32"),
                                 dict(act="f32", ffn="fp8")])
@@ -64,6 +64,25 @@ def test_null_pointers_rejected():
         abi.MOE_ERR_INVALID_ARG
     assert lib.moe_bias_update(ctypes.byref(s), FAKE, ctypes.c_float(-1.0), FAKE, None) == \
         abi.MOE_ERR_INVALID_ARG
+
+
+def test_empty_batch_host_calls():
+    """T = 0: the arrays that scale with T may be NULL; the calls that own no T-free output
+    return MOE_OK without touching the device (the ones that zero outputs are GPU tests)."""
+    lib = abi.load()
+    s = _shape(T=0)
+    assert lib.moe_route(ctypes.byref(s), None, FAKE, FAKE, None, None, None, 0, None) == abi.MOE_OK
+    assert lib.moe_route(ctypes.byref(s), None, None, FAKE, None, None, None, 0, None) == abi.MOE_ERR_INVALID_ARG
+    assert lib.moe_combine(ctypes.byref(s), None, None, None, None, None, None, None) == abi.MOE_OK
+    ex = abi.moe_expert_set()
+    ex.w1 = ex.w3 = ex.w2 = FAKE
+    ex.layout = abi.MOE_LAYOUT_ROWS
+    assert lib.moe_grouped_ffn(ctypes.byref(s), None, FAKE, None, ctypes.byref(ex), ctypes.byref(ex), None, None,
+                               None, 0, None) == abi.MOE_OK
+    assert lib.moe_grouped_ffn(ctypes.byref(s), None, None, None, ctypes.byref(ex), ctypes.byref(ex), None, None,
+                               None, 0, None) == abi.MOE_ERR_INVALID_ARG  # expert_offset does not scale with T
+    sb = _shape(T=0, act="bf16", ffn="bf16")
+    assert lib.moe_combine_backward(ctypes.byref(sb), None, None, None, None, None, None, None) == abi.MOE_OK
 
 
 def test_workspace_checks():

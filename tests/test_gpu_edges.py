@@ -106,3 +106,31 @@ def test_layer_edge_case(case):
     log(f"[edge] {case}: tokens {tok.size} exempt {n_exempt} differing {len(diff)} frob {frob:.2e} "
         f"maxabs {mx:.2e}")
     assert frob <= FROB_TOL and mx <= MAXABS_TOL
+
+
+def test_empty_batch():
+    """T = 0 through the forward and backward calls: counts and offsets zero, the bias
+    unchanged (every count equals the mean, 0), zero weight and centroid gradients, MOE_OK
+    everywhere, with NULL pointers for the empty token arrays."""
+    w = _w("empty", T=0, d=512, n_routed=16, top_k=4, n_shared=2, d_ff=256, seed=2707)
+    ws = _w("empty_weights", base=w, T=4)  # the same tensors' generator needs a token count
+    dev = D.upload(ws, "cuda")
+    log(f"[edge] empty batch: d={w.d} N_r={w.n_routed} K={w.top_k} N_s={w.n_shared} d_ff={w.d_ff}")
+    L = MoeLayer(0, w.d, w.n_routed, w.top_k, w.n_shared, w.d_ff, w.act, w.ffn)
+    L.set_experts(dev["routed"], dev["shared"])
+    L.expert_count.fill_(7)
+    L.expert_offset.fill_(7)
+    u = torch.empty((0, w.d), dtype=torch.bfloat16, device="cuda")
+    bias = to_dev(I.make_b(w).copy())
+    b0 = bias.clone()
+    L.step(u, dev["e"], bias, w.gamma)
+    torch.cuda.synchronize()
+    assert not torch.any(L.expert_count != 0) and not torch.any(L.expert_offset != 0)
+    assert torch.equal(bias, b0)
+    L.alloc_backward()
+    for t in (*L.dw_routed, *L.dw_shared, L.dcentroids):
+        t.fill_(3.0)
+    L.backward(u, dev["e"], torch.empty((0, w.d), dtype=torch.bfloat16, device="cuda"))
+    torch.cuda.synchronize()
+    for t in (*L.dw_routed, *L.dw_shared, L.dcentroids):
+        assert not torch.any(t.float() != 0)
