@@ -151,7 +151,8 @@ moe_status moe_dispatch(const moe_shape* shape, const int32_t* topk_idx, int32_t
  *   sorted_token  [T*K]        from moe_dispatch
  *   routed        N_r experts; shared: N_s experts (may be NULL when N_s == 0)
  *   y_routed      [T*K, d]     out, act dtype: FFN_i(u_t) for sorted row r of (t, i)
- *   y_shared      [T, d]       out, fp32: sum over the shared experts (zeros if N_s = 0)
+ *   y_shared      [T, d]       out, fp32: sum over the shared experts (not used, and may
+ *                              be NULL, when N_s = 0)
  *   ws            workspace of moe_workspace_bytes(shape, MOE_CALL_GROUPED_FFN) bytes;
  *                 holds H (and, for FP8, the 1x128-quantised u and H with their scales)
  *                 and the GEMMs' tile-scheduling state

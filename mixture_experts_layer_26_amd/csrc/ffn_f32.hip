@@ -64,7 +64,7 @@ __global__ __launch_bounds__(kThreads) void down_f32(
     const float* __restrict__ w2s, int64_t T, int d, int d_ff, int n_r, int K, int n_s,
     float* __restrict__ y_routed, float* __restrict__ y_shared) {
   const int64_t P = T * K;
-  const int64_t total = (P + T) * d;
+  const int64_t total = (P + (n_s > 0 ? T : 0)) * d;  // no shared rows (and no y_shared) when n_s = 0
   for (int64_t o = blockIdx.x * static_cast<int64_t>(kThreads) + threadIdx.x; o < total;
        o += static_cast<int64_t>(gridDim.x) * kThreads) {
     const int64_t r = o / d;
@@ -107,7 +107,7 @@ hipError_t launch_ffn_f32(const float* u, const int32_t* offset, const int32_t* 
                      offset, sorted_token, w1r, w3r, w1s, w3s, T, d, d_ff, n_r, K, n_s, h);
   hipError_t err = hipGetLastError();
   if (err != hipSuccess) return err;
-  hipLaunchKernelGGL(down_f32, dim3(grid_for((P + T) * d)), dim3(kThreads), 0, stream, h, offset,
+  hipLaunchKernelGGL(down_f32, dim3(grid_for((P + (n_s > 0 ? T : 0)) * d)), dim3(kThreads), 0, stream, h, offset,
                      w2r, w2s, T, d, d_ff, n_r, K, n_s, y_routed, y_shared);
   return hipGetLastError();
 }

@@ -15,7 +15,8 @@ tolerances (relative Frobenius 5e-3, max-abs 2e-2 of the largest reference magni
 - the largest number of shared experts (8), in bf16 and FP8: the shared down-projection's K
   range runs over eight weight matrices;
 - FP8 with d_ff = 128: the routed down-projection has a single 128-wide K-step, and the
-  shared one (two experts) two K segments of one step each.
+  shared one (two experts) two K segments of one step each;
+- fp32 without shared experts (no y_shared buffer).
 """
 import numpy as np
 import pytest
@@ -51,6 +52,8 @@ CASES = {
     "fp8_max_shared_8": _w("fp8_max_shared_8", T=200, d=512, n_routed=32, top_k=4, n_shared=8, d_ff=256,
                            seed=2705, ffn="fp8"),
     "f32_ragged_77": _w("f32_ragged_77", base=I.WORKLOADS["tiny_f32"], T=77),
+    "f32_no_shared": _w("f32_no_shared", base=I.WORKLOADS["tiny_f32"], T=100, d=128, n_routed=8, top_k=2,
+                        n_shared=0, d_ff=64, seed=2708),
     "fp8_dff_128": _w("fp8_dff_128", T=300, d=256, n_routed=16, top_k=4, n_shared=2, d_ff=128, seed=2706,
                       ffn="fp8"),
 }
@@ -64,12 +67,22 @@ def _q_host(tup):
 @pytest.mark.parametrize("case", list(CASES))
 def test_layer_edge_case(case):
     w = CASES[case]
-    log(f"[edge] {case}: T={w.T} d={w.d} N_r={w.n_routed} K={w.top_k} N_s={w.n_shared} d_ff={w.d_ff} "
-        f"ffn={w.ffn}")
     b = I.make_b(w)
     if case == "all_on_k_experts":
         b = b.copy()
         b[:w.top_k] += 10.0
+    run_layer_case(w, b, case)
+    if case == "all_on_k_experts":
+        counts = np.bincount(oracle.route(I.make_u(w), I.make_e(w), b, w.top_k, w.act)[0].ravel(),
+                             minlength=w.n_routed)
+        assert np.all(counts[:w.top_k] == w.T) and not np.any(counts[w.top_k:])
+
+
+def run_layer_case(w, b, case):
+    """One layer step on the GPU against the oracle: routing, dispatch and bias bit for bit
+    (outside the tie band), the output on sampled tokens within the output tolerances."""
+    log(f"[edge] {case}: T={w.T} d={w.d} N_r={w.n_routed} K={w.top_k} N_s={w.n_shared} d_ff={w.d_ff} "
+        f"ffn={w.ffn}")
     bw = w if w.ffn != "fp8" else _w(w.name, base=w, ffn="bf16")  # FP8 codes come from the bf16 tensors
     dev = D.upload(bw, "cuda")
     routed, shared = dev["routed"], dev["shared"]
@@ -91,8 +104,6 @@ def test_layer_edge_case(case):
     for g, r, what in zip(got, want, ("count", "offset", "sorted_token", "pair_row")):
         assert np.array_equal(g.reshape(r.shape), r), what
     assert np.array_equal(to_np(bias), oracle.bias_update(want[0], w.T, w.top_k, w.gamma, b))
-    if case == "all_on_k_experts":
-        assert np.all(want[0][:w.top_k] == w.T) and not np.any(want[0][w.top_k:])
 
     tok = np.setdiff1d(sample_tokens(w.T, 48), diff)
     need = sorted(set(idx[tok].ravel().tolist()))
