@@ -98,7 +98,8 @@ int grid_for_device() {
 
 // Upper bound on the tiles of a grouped GEMM launch (phase 1: gate/up, 128 output
 // columns per tile; phase 2: down, 256): an expert of r rows has ceil(r / 256) row
-// blocks, at most r / 256 + 1, and each shared group ceil(T / 256).
+// blocks, at most r / 256 + 1, and each shared group ceil(T / 256). Kernels with taller
+// tiles (the bf16 gate/up GEMM's 320 rows) have no more blocks than that.
 int64_t ffn_max_tiles(const moe_shape* s, int phase) {
   const int64_t bm = moe::kTileRows;
   const int64_t P = s->T * s->top_k;

@@ -2,9 +2,9 @@
 //
 // A launch covers a list of groups: routed expert g < n_r owns the sorted rows
 // [offset[g], offset[g+1]); groups n_r.. are the shared experts (all T tokens). Each
-// group is cut into row blocks of at most BM rows -- a group of r rows into ceil(r/BM)
-// blocks of equal size, so the two blocks of an expert with 257..512 rows take the same
-// time -- and each block into output-column tiles. The tile list is built on the device
+// group is cut into row blocks of at most RB rows (the kernel's tile height) -- a group
+// of r rows into ceil(r/RB) blocks of equal size, so the blocks of one expert take the
+// same time -- and each block into output-column tiles. The tile list is built on the device
 // from expert_offset, so no host synchronisation is needed, and it is walked by gangs of
 // workgroups that run neighbouring tiles at the same time (see for_each_tile).
 #pragma once
@@ -16,10 +16,9 @@ namespace moe {
 namespace gemm {
 
 constexpr int kThreads = 512;  // 8 waves: two groups of 4, one wave of each group per SIMD
-constexpr int BM = kTileRows;  // rows per tile (at most)
+constexpr int BM = kTileRows;  // rows per tile (at most) of the FP8 kernel and the bf16 down-projection
 constexpr int BNB = 256;       // B rows (weight rows) per tile
 constexpr int kRowBytes = 128; // bytes per tile row per K-step (64 bf16 or 128 fp8)
-constexpr int kStageBytes = BM * kRowBytes;  // one operand's LDS stage (32 KB)
 constexpr int kMaxGroups = 256 + 8;
 
 struct Tile {
@@ -46,13 +45,14 @@ struct TileMap {
   int total;
 };
 
+template <int RB = BM>  // rows per block at most
 __device__ inline void build_tile_map(TileMap& tm, const int32_t* offset, int n_r, int n_groups_shared,
                                       int64_t T, int ntn) {
   const int ng = n_r + n_groups_shared;
   for (int g = threadIdx.x; g < ng; g += kThreads) {
     const int64_t rows = g < n_r ? (offset[g + 1] - offset[g]) : T;
-    const int64_t mt0 = (rows + BM - 1) / BM;
-    const int64_t rpb = mt0 > 0 ? (rows + mt0 - 1) / mt0 : 0;  // <= BM
+    const int64_t mt0 = (rows + RB - 1) / RB;
+    const int64_t rpb = mt0 > 0 ? (rows + mt0 - 1) / mt0 : 0;  // <= RB
     tm.rpb[g] = static_cast<int>(rpb);
     tm.mt[g] = rpb > 0 ? static_cast<int>((rows + rpb - 1) / rpb) : 0;  // no empty last block
   }

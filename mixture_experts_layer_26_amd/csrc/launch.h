@@ -41,7 +41,7 @@ struct GemmArgs {
 // gang per XCD). Ints of scheduling state one launch of at most max_tiles tiles needs on
 // a grid of `grid` workgroups, and the slot stride that goes with it.
 constexpr int kGangs = 8;
-constexpr int kTileRows = 256;  // rows per tile at most
+constexpr int kTileRows = 256;  // row-block size of the tile-count bound (no kernel has more blocks)
 inline int64_t sched_slot_stride(int64_t max_tiles, int grid) {
   const int64_t G = grid / kGangs > 0 ? grid / kGangs : 1;
   return (max_tiles + G - 1) / G + 2;

@@ -6,9 +6,11 @@ counter and per-gang claim slots. This test restates those rules in Python and r
 under random interleavings of the workgroups, on random and skewed expert loads, checking:
 
 - every (group, row, output-column tile) is computed exactly once;
-- no tile is empty and no tile is taller than 256 rows;
+- no tile is empty and no tile is taller than the kernel's tile height (the bf16 kernel's
+  320 rows in phase 1, 256 in phase 2; the FP8 kernel's 256 in both);
 - the tile count stays within the bound the workspace is sized for (ffn_max_tiles in
-  abi.cpp) and no gang reads past its row of slots (slot stride ceil(max/G) + 2);
+  abi.cpp, counted in 256-row blocks, so it also bounds the taller tiles) and no gang
+  reads past its row of slots (slot stride ceil(max/G) + 2);
 - the list order: shared groups first, then routed experts with an even number of row
   blocks, then those with an odd number.
 
@@ -19,15 +21,16 @@ import random
 
 import numpy as np
 
-BM = 256
+BM = 256   # the row-block size the workspace bound counts in
 GANGS = 8
 
 
-def tile_map(rows, n_r):
-    """Row blocks per group, rows per block, and the list order (shared, even, odd)."""
+def tile_map(rows, n_r, rb=BM):
+    """Row blocks of at most rb rows per group, rows per block, and the list order (shared,
+    even, odd)."""
     mt, rpb = [], []
     for r in rows:
-        mt0 = (r + BM - 1) // BM
+        mt0 = (r + rb - 1) // rb
         p = (r + mt0 - 1) // mt0 if mt0 else 0
         rpb.append(p)
         mt.append((r + p - 1) // p if p else 0)
@@ -37,8 +40,8 @@ def tile_map(rows, n_r):
     return mt, rpb, order
 
 
-def tiles_of(rows, n_r, ntn):
-    mt, rpb, order = tile_map(rows, n_r)
+def tiles_of(rows, n_r, ntn, rb=BM):
+    mt, rpb, order = tile_map(rows, n_r, rb)
     out = []
     for g in order:
         if g < n_r:  # column-major: the row blocks of one column tile are neighbours
@@ -90,11 +93,11 @@ def run_gangs(tiles, grid, stride, rng):
 
 
 def check(T, top_k, n_r, n_shared, d, d_ff, counts, grid, rng):
-    for phase in (1, 2):
+    for phase, rb in ((1, 256), (2, 256), (1, 320)):
         ns_groups = n_shared if phase == 1 else min(n_shared, 1)
         ntn = d_ff // 128 if phase == 1 else d // 256
         rows = list(counts) + [T] * ns_groups
-        tiles = tiles_of(rows, n_r, ntn)
+        tiles = tiles_of(rows, n_r, ntn, rb)
         bound = max_tiles(T, top_k, n_r, n_shared, d, d_ff, phase)
         assert len(tiles) <= bound
         G = grid // GANGS
@@ -102,7 +105,7 @@ def check(T, top_k, n_r, n_shared, d, d_ff, counts, grid, rng):
         ran = run_gangs(tiles, grid, stride, rng)
         seen = set()
         for g, m0, n, r in ran:
-            assert 1 <= r <= BM
+            assert 1 <= r <= rb
             for row in range(m0, m0 + r):
                 key = (g, row, n)
                 assert key not in seen, key
@@ -149,6 +152,20 @@ def test_tile_order():
     assert mt == [2, 0, 3, 1, 3, 36, 1]
     assert rpb == [150, 0, 200, 256, 171, 250, 70]
     assert order == [5, 6, 0, 2, 3, 4]
+    mt, rpb, order = tile_map(rows, 5, 320)  # the bf16 kernel's phase-1 tiles
+    assert mt == [1, 0, 2, 1, 2, 29, 1]
+    assert rpb == [300, 0, 300, 256, 257, 311, 70]
+    assert order == [5, 6, 2, 4, 0, 3]
+
+
+def test_taller_tiles_split_fewer_v3_experts():
+    """At V3 prefill (65536 pairs over 256 experts, 256 on average) 320-row blocks leave
+    less than half as many experts in two blocks as 256-row blocks do, so fewer experts'
+    weights are read twice."""
+    rng = np.random.default_rng(4)
+    counts = _counts(rng, 8192, 8, 256, 20.0)
+    split = lambda rb: sum(1 for m in tile_map(list(counts), 256, rb)[0] if m > 1)
+    assert split(320) * 2 < split(256)
 
 
 def test_k_segment_reciprocal():
