@@ -1,0 +1,234 @@
+"""Expert row counts on the grouped GEMMs' tile boundaries (needs an MI355X).
+
+Routing is forced so that routed expert i receives exactly COUNTS[i] rows: centroid e_i is 8
+times the unit vector of channel i, and token t holds 8 in the channel of its assigned expert
+and 0 in the other routed channels (the remaining channels keep their N(0,1) values). Its
+logits are then 64 for that expert and 0 for every other one, and with K = 1 the sigmoid
+scores 1 and 0.5 decide the choice with a gap near 0.5. The assignment is shuffled over the
+tokens, so every expert's rows are gathered from scattered tokens.
+
+The counts sit on both sides of each row boundary of the tiles: the 32-row MFMA blocks (31,
+32, 33); the bf16 gate/up kernel's 160-row wave groups and 320-row tiles (159..161, 319..321,
+and 640, 641 as two blocks of 320 and of 320 + 321); the 256-row tiles of the bf16
+down-projection and of the FP8 kernel (255..257); an empty and a one-row expert. The shared
+expert runs over all 3586 tokens.
+
+Forward, in bf16 and FP8. Checked against the oracle: routing, counts, permutation and bias
+bit for bit, and the whole output within the layer's tolerances. Then every GEMM row on its
+own. With K = 1 each gate is exactly 1, so row r of y_routed is the routed sum of the token at
+that row, and y_shared row t its shared sum.
+- bf16: each row within a relative Frobenius error of 5e-3 of the oracle's (H and y rounded to
+  bf16 on both sides; only the accumulation order differs).
+- FP8: a single H code that rounds to the other side of a midpoint moves its row by up to a few
+  percent, so the rows are checked in two parts. First H: the GPU's H codes and scales, read
+  from the grouped FFN's workspace, must be a correct E4M3 rounding of the oracle's H to within
+  MFMA_DEV of each 128-block's largest value, and the scales within MFMA_DEV of the oracle's.
+  Then the down-projection: each row must match the exact product of the GPU's own H codes and
+  scales with W2, within 5e-3 for the bf16 y_routed and 1e-3 for the fp32 y_shared.
+  MFMA_DEV covers the FP8 MFMA's own accumulation. Given identical codes and scales, its
+  128-term block sums put the fp32 shared output up to 1.2e-4 of a row's largest value away
+  from the exact product, where fp32 rounding alone would give about 1e-7.
+
+Backward, in bf16: the same routing, with du, the gate gradient and the weight gradients of
+every expert that has rows (their sums over an expert's rows run across the same row
+boundaries) and of the shared expert within the output tolerances. dz and the centroid
+gradient vanish exactly with K = 1 (the gate is 1 whatever the logits) and must come out
+exactly zero.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from mixture_experts_layer_26_amd import inputs as I
+from mixture_experts_layer_26_amd.inputs import device as D
+from mixture_experts_layer_26_amd.layer import MoeLayer, quantize_experts
+from tests.gpu_util import FROB_TOL, MAXABS_TOL, check_routing, log, rel_errors, to_dev, to_np
+from tests.test_gpu_random_backward import _check
+from tests.test_gpu_backward import _f
+
+pytestmark = pytest.mark.gpu
+
+COUNTS = [1, 31, 32, 33, 159, 160, 161, 255, 256, 257, 319, 320, 321, 640, 641, 0]
+BF16_EIGHT = 0x4100  # bit pattern of 8.0 in bf16
+ROW_TOL = 5e-3      # bf16 rows, and FP8 routed rows against the product of the GPU's own H
+SHARED_FP8_TOL = 1e-3  # fp32 shared rows against the product of the GPU's own H
+MFMA_DEV = 5e-4     # FP8 H against the oracle's, in units of each 128-block's largest value
+
+
+def _forced_inputs(w, counts, seed):
+    n_r = len(counts)
+    assign = np.random.default_rng(seed).permutation(np.repeat(np.arange(n_r), counts))
+    u = I.make_u(w).copy()
+    u[:, :n_r] = 0
+    u[np.arange(w.T), assign] = BF16_EIGHT
+    e = np.zeros((n_r, w.d), np.uint16)
+    e[np.arange(n_r), np.arange(n_r)] = BF16_EIGHT
+    return u, e, assign
+
+
+def _row_errors(got, ref):
+    return np.linalg.norm(got - ref, axis=1) / np.linalg.norm(ref, axis=1)
+
+
+def _q_host(tup):
+    out = [oracle.quantize(a, "bf16", 128, 128) for a in tup]
+    return (out[0][0], out[1][0], out[2][0], out[0][1], out[1][1], out[2][1])
+
+
+def _fp8_h(L, w):
+    """The GPU's FP8 H codes and scales (K-block-major), read from the grouped FFN's workspace.
+    White box: they are the last regions of its FP8 layout, each 256-byte aligned, in the order
+    q_u, s_u, the row scales K-block-major, H codes and scales of the routed rows, H codes and
+    scales of the shared experts."""
+    T, d, F, P, ns = w.T, w.d, w.d_ff, w.T * w.top_k, w.n_shared
+    sizes = [T * d, T * d // 128 * 4, (P + T) * d // 128 * 4, P * F, P * F // 128 * 4, T * ns * F,
+             T * ns * F // 128 * 4]
+    al = lambda n: -(-n // 256) * 256
+    ws = to_np(L.ws_ffn)
+    off = ws.size - sum(al(n) for n in sizes)
+    assert off >= 0 and off % 256 == 0
+    regs = []
+    for n in sizes:
+        regs.append(ws[off:off + n])
+        off += al(n)
+    return (regs[3].reshape(P, F), regs[4].view(np.float32).reshape(F // 128, P).T,
+            regs[5].reshape(T, ns * F), regs[6].view(np.float32).reshape(ns * F // 128, T).T)
+
+
+def _check_h_codes(h, codes, scales, tab, what):
+    """codes and 1x128 scales of the GPU against the oracle's H (double, rounded to fp32 as the
+    oracle quantises it): the scales within MFMA_DEV, each code a correct E4M3 rounding of
+    h / scale to within MFMA_DEV of the block's largest value (448 after scaling)."""
+    h32 = h.astype(np.float32).astype(np.float64)
+    blocks = h32.reshape(h.shape[0], -1, 128)
+    s_o = (np.abs(blocks).max(axis=2).astype(np.float32) / np.float32(448)).astype(np.float64)
+    sg = scales.astype(np.float64)
+    assert np.all(np.abs(sg - s_o) <= MFMA_DEV * s_o), f"{what}: H scales"
+    x = np.clip(blocks / sg[:, :, None], -448, 448).reshape(h.shape)
+    spacing = 2.0 ** (np.maximum(np.floor(np.log2(np.maximum(np.abs(x), 2.0 ** -9))), -6) - 3)
+    excess = np.abs(tab[codes] - x) - spacing / 2
+    log(f"[tile edges] {what}: H codes differing from a rounding of the oracle's H "
+        f"{int(np.sum(excess > 0))} of {codes.size}, worst by {max(0.0, excess.max()) / 448:.1e} of the block max")
+    assert excess.max() <= MFMA_DEV * 448, f"{what}: H codes"
+
+
+def _down(codes, scales, w2q, tab):
+    """Exact (double) product of FP8 H codes and scales with the FP8 W2 (codes, 128x128 scales)."""
+    hv = tab[codes] * np.repeat(scales.astype(np.float64), 128, axis=1)
+    w2 = tab[w2q[2]] * np.repeat(np.repeat(w2q[5].astype(np.float64), 128, axis=0), 128, axis=1)
+    return hv @ w2.T
+
+
+def _check_fp8_rows(L, w, u, sorted_token, y_r):
+    tab = oracle.e4m3_table()
+    h_r, s_r, h_s, s_s = _fp8_h(L, w)
+    off = np.concatenate([[0], np.cumsum(COUNTS)])
+    worst = {}
+    for i, c in enumerate(COUNTS):
+        if not c:
+            continue
+        q = _q_host(I.make_expert(w, False, i))
+        rows = slice(off[i], off[i + 1])
+        h_o, _ = oracle.expert_rows(u[sorted_token[rows]], *q[:3], "fp8", *q[3:])
+        _check_h_codes(h_o, h_r[rows], s_r[rows], tab, f"expert {i} ({c} rows)")
+        worst[c] = float(_row_errors(y_r[rows], _down(h_r[rows], s_r[rows], q, tab)).max())
+    log(f"[tile edges] fp8: worst routed row against the product of the GPU's H, per count {worst}")
+    assert max(worst.values()) <= ROW_TOL
+    q = _q_host(I.make_expert(w, True, 0))
+    h_o, _ = oracle.expert_rows(u, *q[:3], "fp8", *q[3:])
+    _check_h_codes(h_o, h_s, s_s, tab, "shared expert")
+    err_s = _row_errors(to_np(L.y_shared).astype(np.float64), _down(h_s, s_s, q, tab))
+    log(f"[tile edges] fp8: worst shared row {err_s.max():.2e}")
+    assert err_s.max() <= SHARED_FP8_TOL
+
+
+def _workload(name):
+    return I.Workload(name, T=sum(COUNTS), d=512, n_routed=len(COUNTS), top_k=1, n_shared=1, d_ff=256,
+                      act="bf16", ffn="bf16", seed=2709, bias_range=0.01)
+
+
+@pytest.mark.parametrize("ffn", ["bf16", "fp8"])
+def test_counts_on_tile_boundaries(ffn):
+    T = sum(COUNTS)
+    w = _workload(f"tile_edges_{ffn}")
+    log(f"[tile edges] ffn={ffn} T={T} d={w.d} N_r={w.n_routed} d_ff={w.d_ff} counts={COUNTS}")
+    u, e, assign = _forced_inputs(w, COUNTS, 2709)
+    b = I.make_b(w)
+    dev = D.upload(w, "cuda")
+    routed, shared = dev["routed"], dev["shared"]
+    if ffn == "fp8":
+        routed, shared = quantize_experts(routed), quantize_experts(shared)
+    L = MoeLayer(T, w.d, w.n_routed, 1, w.n_shared, w.d_ff, w.act, ffn)
+    L.set_experts(routed, shared)
+    bias = to_dev(b.copy())
+    L.step(to_dev(u, bf16=True), to_dev(e, bf16=True), bias, w.gamma)
+    torch.cuda.synchronize()
+
+    idx, gate, gap, v = oracle.route(u, e, b, 1, "bf16", want_v=True)
+    assert np.array_equal(idx[:, 0], assign) and np.all(gap > 0.4)  # the construction routes as intended
+    idx_g = to_np(L.topk_idx)
+    diff, _ = check_routing(idx_g, to_np(L.topk_gate), idx, gate, gap, v, 1)
+    assert len(diff) == 0
+    want = oracle.dispatch(idx_g, w.n_routed)
+    got = [to_np(t) for t in (L.expert_count, L.expert_offset, L.sorted_token, L.pair_row)]
+    for g_, r_, what in zip(got, want, ("count", "offset", "sorted_token", "pair_row")):
+        assert np.array_equal(g_.reshape(r_.shape), r_), what
+    assert np.array_equal(got[0], np.array(COUNTS, np.int32))
+    assert np.array_equal(to_np(bias), oracle.bias_update(want[0], T, 1, w.gamma, b))
+
+    mk = _q_host if ffn == "fp8" else (lambda t: t)
+    r_host = {i: mk(I.make_expert(w, False, i)) for i in range(w.n_routed) if COUNTS[i]}
+    s_host = [mk(I.make_expert(w, True, 0))]
+    res = oracle.layer(u, e, b, r_host, s_host, top_k=1, d_ff=w.d_ff, act="bf16", ffn=ffn,
+                       want_components=True)
+
+    out = I.bf16_bits_to_f32(to_np(L.out))
+    frob, mx = rel_errors(out, res["out"])
+    log(f"[tile edges] ffn={ffn}: output frob {frob:.2e} maxabs {mx:.2e}")
+    assert frob <= FROB_TOL and mx <= MAXABS_TOL
+    y_r = to_np(L.y_routed)
+    y_r = (I.bf16_bits_to_f32(y_r) if y_r.dtype == np.uint16 else y_r).astype(np.float64)
+    sorted_token = got[2].ravel()
+    if ffn == "fp8":
+        _check_fp8_rows(L, w, u, sorted_token, y_r)
+        return
+    err_r = _row_errors(y_r, res["routed_sum"][sorted_token])
+    err_s = _row_errors(to_np(L.y_shared).astype(np.float64), res["shared_sum"])
+    off = np.concatenate([[0], np.cumsum(COUNTS)])
+    worst = {c: float(err_r[off[i]:off[i + 1]].max()) for i, c in enumerate(COUNTS) if c}
+    log(f"[tile edges] bf16: worst routed row per count {worst}; worst shared row {err_s.max():.2e}")
+    assert err_r.max() <= ROW_TOL and err_s.max() <= ROW_TOL
+
+
+def test_backward_counts_on_tile_boundaries():
+    w = _workload("tile_edges_backward")
+    log(f"[tile edges] backward T={w.T} d={w.d} N_r={w.n_routed} d_ff={w.d_ff} counts={COUNTS}")
+    u, e, assign = _forced_inputs(w, COUNTS, 2709)
+    b = I.make_b(w)
+    dev = D.upload(w, "cuda")
+    L = MoeLayer(w.T, w.d, w.n_routed, 1, w.n_shared, w.d_ff, w.act, w.ffn)
+    L.set_experts(dev["routed"], dev["shared"])
+    u_dev, e_dev = to_dev(u, bf16=True), to_dev(e, bf16=True)
+    L.route(u_dev, e_dev, to_dev(b.copy()))
+    L.dispatch()
+    L.grouped_ffn(u_dev)
+    L.combine(u_dev)
+    dout = I.make_u(w, batch=99)
+    L.backward(u_dev, e_dev, to_dev(dout, bf16=True))
+    torch.cuda.synchronize()
+    assert np.array_equal(to_np(L.topk_idx)[:, 0], assign)
+    live = [i for i in range(w.n_routed) if COUNTS[i]]
+    routed = {i: I.make_expert(w, False, i) for i in live}
+    shared = [I.make_expert(w, True, 0)]
+    g = oracle.layer_backward(u, e, b, routed, shared, dout, top_k=1, d_ff=w.d_ff, act=w.act, ffn=w.ffn,
+                              grad_routed=live, grad_shared=True)
+    _check("du", _f(L.du), g["du"])
+    _check("dgate", _f(L.dgate), g["dgate"])
+    for name, got, ref in (("dcentroids", L.dcentroids, g["de"]), ("dz", L.dz, g["dz"])):
+        assert not np.any(ref) and not np.any(_f(got)), name
+    for i in live:
+        for m, mname in enumerate(("dW1", "dW3", "dW2")):
+            _check(f"{mname}[{i}] ({COUNTS[i]} rows)", _f(L.dw_routed[m][i]), g["dw_routed"][i][m])
+    for m, mname in enumerate(("dW1", "dW3", "dW2")):
+        _check(f"shared {mname}", _f(L.dw_shared[m][0]), g["dw_shared"][0][m])
