@@ -62,16 +62,20 @@ def parse():
 
 
 def kernel_source_hash(ffn: str) -> str:
-    """Hash of the sources of the grouped-FFN kernels that run for expert dtype `ffn`; a
-    stored traffic measurement is used only while the kernels it was taken on are
-    unchanged."""
+    """Hash of the code of the grouped-FFN kernels that run for expert dtype `ffn` (the
+    sources with comments removed and white space collapsed, so that editing a comment
+    keeps a measurement); a stored traffic measurement is used only while the code it was
+    taken on is unchanged."""
     import hashlib
+    import re
     h = hashlib.sha256()
     csrc = os.path.join(ROOT, "mixture_experts_layer_26_amd", "csrc")
     kernel = {"bf16": "ffn_bf16.hip", "fp8": "ffn_fp8.hip"}[ffn]
     for f in ("gemm_common.h", kernel, "device.h", "pack.hip"):
-        with open(os.path.join(csrc, f), "rb") as fh:
-            h.update(fh.read())
+        with open(os.path.join(csrc, f), encoding="utf-8") as fh:
+            code = re.sub(r"/\*.*?\*/", " ", fh.read(), flags=re.S)
+        code = re.sub(r"//[^\n]*", " ", code)
+        h.update(" ".join(code.split()).encode())
     return h.hexdigest()[:16]
 
 

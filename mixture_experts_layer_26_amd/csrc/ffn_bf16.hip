@@ -8,19 +8,19 @@
 // through sorted_token) and the shared experts (rows = all tokens).
 //
 // Kernel shape: a persistent grid of one 8-wave workgroup per CU walks the device-built
-// tile list in gangs (gemm_common.h). A tile is up to 320 rows x 256 weight rows (phase
-// 1: 128 gate + 128 up columns): at V3 prefill most routed experts hold 185..345 rows, so
-// with 320-row tiles nearly every expert is one row block and its weights pass through
-// the L1 once, where 256-row tiles split 120 of the 256 experts in two. K advances in steps of 64 (128-byte rows) through two
-// LDS stages filled by direct global-to-LDS loads (global_load_lds_dwordx4): no staging
+// tile list in gangs (gemm_common.h). A phase-1 tile is up to 320 rows x 256 weight rows
+// (128 gate + 128 up columns): at V3 prefill the routed experts hold about 185..345 rows,
+// so with 320-row tiles most experts are one row block and their weights pass through the
+// L1 once, where 256-row tiles split about 120 of the 256 experts in two. K advances in
+// steps of 64 (128-byte rows) through two LDS stages filled by direct global-to-LDS loads (global_load_lds_dwordx4): no staging
 // registers and no LDS store instructions; a stage is loaded one step before it is
 // computed. One barrier per step, before its last 16-wide sub-step, so each wave reads
 // the next step's first fragments while the MFMAs of the current one run. In phase 1
 // every wave computes a 160 x 64 block with v_mfma_f32_32x32x16_bf16 (10 MFMA tiles):
 // wave (g, wn) owns rows 160g.. of the tile and gate rows 32wn.. with the matching up
 // rows (so SiLU(gate) * up is formed in registers). Phase 2 keeps 256-row tiles (waves
-// of 128 x 64, 8 MFMA tiles): its two 32-column blocks per wave need more fragment
-// registers than 160-row waves leave free. The K loop is specialised on the
+// of 128 x 64, 8 MFMA tiles): at 320 rows its kernel, which also carries the shared
+// experts' segmented K range and fp32 epilogue, spilled registers inside the K loop. The K loop is specialised on the
 // number of 32-row blocks of a wave that hold rows, so row blocks past an expert's
 // count cost no MFMA work. Weights are read row-major or in the tiled layout of
 // pack.hip.
@@ -41,8 +41,8 @@ constexpr int kSubs = BK / 16;          // MFMA sub-steps per K-step
 constexpr int kDmaB = BNB / 64;         // B loads (global_load_lds of 8 rows) per wave per step
 
 // Tile geometry for TRW tile rows: two wave groups of TRW / 2 rows, each wave a
-// TRW / 2 x 64 block of 32 x 32 MFMA tiles. Phase 1 uses 320 rows, phase 2 256: the
-// down-projection's 160-row waves would not fit the register file with its operands.
+// TRW / 2 x 64 block of 32 x 32 MFMA tiles. Phase 1 uses 320 rows, phase 2 256 (at 320 the
+// down-projection spilled registers inside its K loop).
 template <int TRW>
 struct Geo {
   static constexpr int GR = TRW / 2;      // rows per wave group

@@ -88,3 +88,16 @@ def test_committed_traffic_matches_its_workload(name):
         t = json.load(f)
     assert t["workload"] == name and t["weights"] == "tiled"
     assert abs(t["hbm_bytes_per_call"] - (t["phase1_bytes"] + t["phase2_bytes"])) <= 1  # each rounded down
+
+
+def test_source_hash_ignores_comments(tmp_path, monkeypatch):
+    csrc = tmp_path / "mixture_experts_layer_26_amd" / "csrc"
+    csrc.mkdir(parents=True)
+    for f in ("gemm_common.h", "ffn_bf16.hip", "device.h", "pack.hip"):
+        (csrc / f).write_text("int a = 1;  // one\n/* block\n comment */ int b = 2;\n")
+    monkeypatch.setattr(bench, "ROOT", str(tmp_path))
+    h = bench.kernel_source_hash("bf16")
+    (csrc / "ffn_bf16.hip").write_text("int a = 1;  // another comment\n\nint b = 2;\n")
+    assert bench.kernel_source_hash("bf16") == h
+    (csrc / "ffn_bf16.hip").write_text("int a = 1;\nint b = 3;\n")
+    assert bench.kernel_source_hash("bf16") != h
