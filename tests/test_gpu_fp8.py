@@ -3,7 +3,9 @@
 Quantisation of inputs (weights in 128x128 blocks, activations in 1x128 tiles) is
 deterministic, so the GPU's codes and scales must equal the oracle's bit for bit.
 The FP8 layer output is compared with the oracle applying the identical
-quantisation, within the layer tolerance.
+quantisation, within the layer tolerance. On the sampled rows the GPU's H codes and scales
+are also checked against the oracle's H, and the fp32 shared rows against the exact product
+of the GPU's own shared H (the checks and their bounds are those of test_gpu_tile_edges.py).
 """
 import numpy as np
 import pytest
@@ -15,6 +17,7 @@ from mixture_experts_layer_26_amd import inputs as I
 from mixture_experts_layer_26_amd.layer import MoeLayer, quantize_experts
 from tests.gpu_util import (FROB_TOL, MAXABS_TOL, check_routing, log, rel_errors, sample_tokens, to_dev,
                             to_np, workload_on_device)
+from tests.test_gpu_tile_edges import SHARED_FP8_TOL, _check_h_codes, _down, _fp8_h, _row_errors
 
 pytestmark = pytest.mark.gpu
 
@@ -150,9 +153,27 @@ def test_fp8_layer_end_to_end(base, T):
     pr = to_np(L.pair_row)[tok]
     y_gpu = I.bf16_bits_to_f32(to_np(L.y_routed[torch.from_numpy(pr.ravel()).cuda()]))
     y_ref = np.empty_like(y_gpu, dtype=np.float64)
+    h_ref = np.empty((y_gpu.shape[0], w.d_ff))
     sel = to_np(L.topk_idx)[tok]
     for j, (t, row) in enumerate(zip(np.repeat(tok, w.top_k), sel.ravel())):
-        y_ref[j] = oracle.expert_rows(u[t:t + 1], *r_host[int(row)][:3], "fp8", *r_host[int(row)][3:])[1][0]
+        h1, y1 = oracle.expert_rows(u[t:t + 1], *r_host[int(row)][:3], "fp8", *r_host[int(row)][3:])
+        h_ref[j], y_ref[j] = h1[0], y1[0]
     f3, m3 = rel_errors(y_gpu, y_ref)
     log(f"[fp8 ffn] {w.name}: routed rows {y_gpu.shape[0]} frob {f3:.2e} maxabs {m3:.2e}")
     assert f3 <= FROB_TOL and m3 <= MAXABS_TOL
+    # H of those rows and of the sampled tokens' shared rows, against the oracle's H
+    tab = oracle.e4m3_table()
+    h_r, s_r, h_s, s_s = _fp8_h(L, w)
+    rows_dev = torch.from_numpy(pr.ravel().astype(np.int64)).cuda()
+    _check_h_codes(h_ref, to_np(h_r[rows_dev]), to_np(s_r[rows_dev]), tab, f"{w.name} routed rows")
+    tok_dev = torch.from_numpy(tok.astype(np.int64)).cuda()
+    hs, ss = to_np(h_s[tok_dev]), to_np(s_s[tok_dev])
+    F, nb = w.d_ff, w.d_ff // 128
+    y_adopt = np.zeros((tok.size, w.d))
+    for j in range(w.n_shared):
+        h_o, _ = oracle.expert_rows(u[tok], *s_host[j][:3], "fp8", *s_host[j][3:])
+        _check_h_codes(h_o, hs[:, j * F:(j + 1) * F], ss[:, j * nb:(j + 1) * nb], tab, f"{w.name} shared {j}")
+        y_adopt += _down(hs[:, j * F:(j + 1) * F], ss[:, j * nb:(j + 1) * nb], s_host[j], tab)
+    err = _row_errors(ysh.astype(np.float64), y_adopt)
+    log(f"[fp8 ffn] {w.name}: shared rows against the product of the GPU's H: worst {err.max():.2e}")
+    assert err.max() <= SHARED_FP8_TOL

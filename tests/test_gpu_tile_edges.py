@@ -77,23 +77,23 @@ def _q_host(tup):
 
 
 def _fp8_h(L, w):
-    """The GPU's FP8 H codes and scales (K-block-major), read from the grouped FFN's workspace.
-    White box: they are the last regions of its FP8 layout, each 256-byte aligned, in the order
-    q_u, s_u, the row scales K-block-major, H codes and scales of the routed rows, H codes and
-    scales of the shared experts."""
+    """The GPU's FP8 H codes and scales (scales K-block-major, returned row-major), read from
+    the grouped FFN's workspace as device views. White box: they are the last regions of its
+    FP8 layout, each 256-byte aligned, in the order q_u, s_u, the row scales K-block-major, H
+    codes and scales of the routed rows, H codes and scales of the shared experts."""
     T, d, F, P, ns = w.T, w.d, w.d_ff, w.T * w.top_k, w.n_shared
     sizes = [T * d, T * d // 128 * 4, (P + T) * d // 128 * 4, P * F, P * F // 128 * 4, T * ns * F,
              T * ns * F // 128 * 4]
     al = lambda n: -(-n // 256) * 256
-    ws = to_np(L.ws_ffn)
-    off = ws.size - sum(al(n) for n in sizes)
+    ws = L.ws_ffn
+    off = ws.numel() - sum(al(n) for n in sizes)
     assert off >= 0 and off % 256 == 0
     regs = []
     for n in sizes:
         regs.append(ws[off:off + n])
         off += al(n)
-    return (regs[3].reshape(P, F), regs[4].view(np.float32).reshape(F // 128, P).T,
-            regs[5].reshape(T, ns * F), regs[6].view(np.float32).reshape(ns * F // 128, T).T)
+    return (regs[3].view(P, F), regs[4].view(torch.float32).view(F // 128, P).t(),
+            regs[5].view(T, ns * F), regs[6].view(torch.float32).view(ns * F // 128, T).t())
 
 
 def _check_h_codes(h, codes, scales, tab, what):
@@ -108,7 +108,7 @@ def _check_h_codes(h, codes, scales, tab, what):
     x = np.clip(blocks / sg[:, :, None], -448, 448).reshape(h.shape)
     spacing = 2.0 ** (np.maximum(np.floor(np.log2(np.maximum(np.abs(x), 2.0 ** -9))), -6) - 3)
     excess = np.abs(tab[codes] - x) - spacing / 2
-    log(f"[tile edges] {what}: H codes differing from a rounding of the oracle's H "
+    log(f"[fp8 H] {what}: H codes differing from a rounding of the oracle's H "
         f"{int(np.sum(excess > 0))} of {codes.size}, worst by {max(0.0, excess.max()) / 448:.1e} of the block max")
     assert excess.max() <= MFMA_DEV * 448, f"{what}: H codes"
 
@@ -122,7 +122,7 @@ def _down(codes, scales, w2q, tab):
 
 def _check_fp8_rows(L, w, u, sorted_token, y_r):
     tab = oracle.e4m3_table()
-    h_r, s_r, h_s, s_s = _fp8_h(L, w)
+    h_r, s_r, h_s, s_s = (to_np(x) for x in _fp8_h(L, w))
     off = np.concatenate([[0], np.cumsum(COUNTS)])
     worst = {}
     for i, c in enumerate(COUNTS):
