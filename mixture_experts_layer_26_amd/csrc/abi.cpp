@@ -55,6 +55,15 @@ bool tiled_shape(const moe_shape* s) {
   return s->d % 256 == 0 && s->d_ff % 128 == 0;
 }
 
+// The bf16 grouped GEMMs hold each lane's row offsets within an operand as 32-bit element
+// offsets: u [T, d], H [T*K, d_ff] and [T, N_s*d_ff], and one expert's weights [d_ff, d]
+// must each have fewer than 2^32 elements.
+bool bf16_offsets_fit(const moe_shape* s) {
+  const int64_t lim = 1LL << 32;
+  return s->T * s->d < lim && s->T * s->top_k * s->d_ff < lim && s->T * s->n_shared * s->d_ff < lim &&
+         static_cast<int64_t>(s->d) * s->d_ff < lim;
+}
+
 size_t act_bytes(int dt) { return dt == MOE_F32 ? 4 : 2; }
 
 hipStream_t as_stream(void* p) { return static_cast<hipStream_t>(p); }
@@ -380,6 +389,7 @@ moe_status moe_grouped_ffn(const moe_shape* s, const void* u, const int32_t* exp
   const int b_tiled = routed->layout == MOE_LAYOUT_TILED ? 1 : 0;
   if (b_tiled && s->ffn == MOE_F32) return MOE_ERR_UNSUPPORTED;
   if (!tiled_shape(s)) return MOE_ERR_UNSUPPORTED;
+  if (s->ffn == MOE_BF16 && !bf16_offsets_fit(s)) return MOE_ERR_UNSUPPORTED;
   if (s->T == 0) return MOE_OK;
   const FfnWorkspace w = ffn_workspace(s);
   if (!ws || ws_bytes < w.total) return MOE_ERR_WORKSPACE;

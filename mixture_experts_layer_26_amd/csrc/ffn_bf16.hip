@@ -250,7 +250,7 @@ __global__ __launch_bounds__(kThreads) void grouped_gemm_bf16(GemmArgs args) {
     // swizzle of swz)
     const int64_t eoff = static_cast<int64_t>(routed ? t.group : sg) * args.b_expert_stride;
     c.load_a = __builtin_amdgcn_readfirstlane(8 * kDmaA * wave < t.rows ? 1 : 0) != 0;
-    // element offsets fit 32 bits: the host checks the operand sizes
+    // element offsets fit 32 bits: moe_grouped_ffn rejects bf16 operands of 2^32 elements or more
     c.abase = routed ? args.a_routed : args.a_shared;
 #pragma unroll
     for (int j = 0; j < kDmaA; ++j) {

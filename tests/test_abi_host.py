@@ -220,3 +220,25 @@ def test_backward_args_rejected():
     assert lib.moe_route_backward(ctypes.byref(bf), *args, FAKE, rneed, None) == abi.MOE_ERR_INVALID_ARG
     assert lib.moe_combine_backward(ctypes.byref(bf), FAKE, FAKE, FAKE, FAKE, FAKE, None, None) == \
         abi.MOE_ERR_INVALID_ARG
+
+
+@pytest.mark.parametrize("kw,fits", [
+    (dict(T=600_000, d=7168, d_ff=256), dict(T=599_000)),                        # u: T*d
+    (dict(T=300_000, top_k=8, d=256, d_ff=2048), dict(T=262_000)),               # routed H: T*K*d_ff
+    (dict(T=1_100_000, n_shared=2, top_k=1, d=256, d_ff=2048), dict(n_shared=1)),  # shared H: T*N_s*d_ff
+    (dict(T=4, d=65536, d_ff=65536), dict(d_ff=65408))])                         # one expert: d_ff*d
+def test_bf16_ffn_rejects_operands_past_32_bit_offsets(kw, fits):
+    """The bf16 grouped GEMMs keep row offsets within an operand in 32 bits: u [T, d], H
+    [T*K, d_ff] and [T, N_s*d_ff] and one expert's weights [d_ff, d] must each have fewer
+    than 2^32 elements. Larger shapes are refused on the host, before any launch; the same
+    shape just below the limit passes the check (and stops at the workspace check)."""
+    base = dict(n_routed=16, top_k=2, n_shared=1, act="bf16", ffn="bf16")
+    base.update(kw)
+    lib = abi.load()
+    es = abi.make_expert_set(FAKE, FAKE, FAKE)
+    s = _shape(**base)
+    assert lib.moe_grouped_ffn(ctypes.byref(s), FAKE, FAKE, FAKE, ctypes.byref(es), ctypes.byref(es), FAKE, FAKE,
+                               FAKE, 1 << 62, None) == abi.MOE_ERR_UNSUPPORTED
+    ok = _shape(**dict(base, **fits))
+    assert lib.moe_grouped_ffn(ctypes.byref(ok), FAKE, FAKE, FAKE, ctypes.byref(es), ctypes.byref(es), FAKE, FAKE,
+                               FAKE, 0, None) == abi.MOE_ERR_WORKSPACE
