@@ -10,9 +10,10 @@
 // Phase 1 writes H = SiLU(gate) * up quantised per 1 x 128 (codes + fp32 scales);
 // phase 2 writes y (bf16 routed rows, fp32 shared sum).
 //
-// The tile walk, tile claiming and LDS layout are those of the bf16 kernel (256 x 256
-// tiles, 128-byte rows per K-step, so one K-step is exactly one 128-wide scale block),
-// with two stages: step s+1 is loaded while step s is computed. The MFMA is
+// The tile walk, tile claiming and LDS layout are those of the bf16 kernel, with 256 x 256
+// tiles in both phases (the bf16 down-projection's shape; its gate/up tiles are 320 rows)
+// and 128-byte rows per K-step, so one K-step is exactly one 128-wide scale block. There
+// are two stages: step s+1 is loaded while step s is computed. The MFMA is
 // v_mfma_scale_f32_16x16x128_f8f6f4 with unit (E8M0 = 127) scales: one instruction
 // covers one scale block of a 16 x 16 output block, starting from zero, and its result
 // is folded into the accumulator with one fp32 FMA per element:
