@@ -17,7 +17,8 @@ from mixture_experts_layer_26_amd import inputs as I
 from mixture_experts_layer_26_amd.layer import MoeLayer, quantize_experts
 from tests.gpu_util import (FROB_TOL, MAXABS_TOL, check_routing, log, rel_errors, sample_tokens, to_dev,
                             to_np, workload_on_device)
-from tests.test_gpu_tile_edges import SHARED_FP8_TOL, _check_h_codes, _down, _fp8_h, _row_errors
+from tests.test_gpu_tile_edges import (SHARED_FP8_TOL, _check_h_codes, _check_layout_reading, _down, _fp8_h,
+                                      _row_errors)
 
 pytestmark = pytest.mark.gpu
 
@@ -163,10 +164,11 @@ def test_fp8_layer_end_to_end(base, T):
     assert f3 <= FROB_TOL and m3 <= MAXABS_TOL
     # H of those rows and of the sampled tokens' shared rows, against the oracle's H
     tab = oracle.e4m3_table()
-    h_r, s_r, h_s, s_s = _fp8_h(L, w)
+    h_r, s_r, h_s, s_s, q_u = _fp8_h(L, w)
+    tok_dev = torch.from_numpy(tok.astype(np.int64)).cuda()
+    _check_layout_reading(to_np(q_u[tok_dev]), u[tok], w.name)
     rows_dev = torch.from_numpy(pr.ravel().astype(np.int64)).cuda()
     _check_h_codes(h_ref, to_np(h_r[rows_dev]), to_np(s_r[rows_dev]), tab, f"{w.name} routed rows")
-    tok_dev = torch.from_numpy(tok.astype(np.int64)).cuda()
     hs, ss = to_np(h_s[tok_dev]), to_np(s_s[tok_dev])
     F, nb = w.d_ff, w.d_ff // 128
     y_adopt = np.zeros((tok.size, w.d))

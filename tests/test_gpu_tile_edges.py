@@ -93,7 +93,13 @@ def _fp8_h(L, w):
         regs.append(ws[off:off + n])
         off += al(n)
     return (regs[3].view(P, F), regs[4].view(torch.float32).view(F // 128, P).t(),
-            regs[5].view(T, ns * F), regs[6].view(torch.float32).view(ns * F // 128, T).t())
+            regs[5].view(T, ns * F), regs[6].view(torch.float32).view(ns * F // 128, T).t(), regs[0].view(T, d))
+
+
+def _check_layout_reading(q_u, u_rows, what):
+    """The workspace reading is right if the region it takes for the quantised u holds the
+    oracle's 1x128 codes of u, bit for bit."""
+    assert np.array_equal(q_u, oracle.quantize(u_rows, "bf16", 1, 128)[0]), f"{what}: workspace layout"
 
 
 def _check_h_codes(h, codes, scales, tab, what):
@@ -122,7 +128,8 @@ def _down(codes, scales, w2q, tab):
 
 def _check_fp8_rows(L, w, u, sorted_token, y_r):
     tab = oracle.e4m3_table()
-    h_r, s_r, h_s, s_s = (to_np(x) for x in _fp8_h(L, w))
+    h_r, s_r, h_s, s_s, q_u = (to_np(x) for x in _fp8_h(L, w))
+    _check_layout_reading(q_u, u, "tile edges")
     off = np.concatenate([[0], np.cumsum(COUNTS)])
     worst = {}
     for i, c in enumerate(COUNTS):
