@@ -70,11 +70,17 @@ typedef __attribute__((address_space(3))) unsigned char* lds_ptr;
 // instruction is written out rather than taken from the builtin so that the compiler,
 // which cannot follow which stage a load lands in across loop iterations, adds no wait
 // of its own before the LDS reads; the waits are the explicit ones in step_barrier.
-// Nothing else in these kernels uses M0.
+// M0 is declared clobbered, so the compiler keeps no value of its own in M0 across the
+// statement (clang warns that M0 is a reserved register; the clobber is what tells its
+// M0-initialisation passes that the statement writes it).
+#pragma clang diagnostic push
+#pragma clang diagnostic ignored "-Winline-asm"
 __device__ __forceinline__ void dma16(const void* gptr, const unsigned char* lds) {
   const uint32_t m0 = static_cast<uint32_t>(reinterpret_cast<uintptr_t>((lds_ptr)(lds)));
-  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(gptr), "s"(m0) : "memory");
+  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(gptr), "s"(m0)
+               : "memory", "m0");
 }
+#pragma clang diagnostic pop
 
 template <int TRW>
 struct TileCtx {

@@ -267,11 +267,18 @@ typedef __attribute__((address_space(3))) unsigned char* lds_ptr;
 // One global_load_lds_dwordx4: lane i copies the 16 bytes at gptr (its own address) to
 // LDS byte lds + 16 i. M0 holds the LDS address (one wait state after writing it). The
 // instruction is written out so that the compiler adds no wait of its own before the LDS
-// reads; the waits are the explicit ones in ring_wait.
+// reads; the waits are the explicit ones in ring_wait. M0 is declared clobbered, so the
+// compiler keeps no value of its own in M0 across the statement (clang warns that M0 is a
+// reserved register; the clobber is what tells its M0-initialisation passes that the
+// statement writes it).
+#pragma clang diagnostic push
+#pragma clang diagnostic ignored "-Winline-asm"
 __device__ __forceinline__ void dma16(const void* gptr, const unsigned char* lds) {
   const uint32_t m0 = static_cast<uint32_t>(reinterpret_cast<uintptr_t>((lds_ptr)(lds)));
-  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(gptr), "s"(m0) : "memory");
+  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(gptr), "s"(m0)
+               : "memory", "m0");
 }
+#pragma clang diagnostic pop
 
 // Loads of K-step kt into one stage: each operand's tile is split evenly over the waves,
 // 64 16-byte slots per instruction (slot = per-wave share * w + 64 i + lane). The lane

@@ -64,19 +64,25 @@ __device__ __forceinline__ scale_ptr uniform_scales(const float* p) {
 // LDS byte base + OFF + 16 i. M0 holds the LDS address (one wait state after writing
 // it). The instruction is written out rather than taken from the builtin so that the
 // compiler adds no wait of its own before the LDS reads; the waits are the explicit
-// ones in step_barrier. Nothing else in these kernels uses M0.
+// ones in step_barrier. The statement writes M0 and SCC (the add), and declares both
+// clobbered, so the compiler keeps no value of its own in either across it (clang warns
+// that M0 is a reserved register; the clobber is what tells its M0-initialisation passes
+// that the statement writes it).
+#pragma clang diagnostic push
+#pragma clang diagnostic ignored "-Winline-asm"
 template <int OFF>
 __device__ __forceinline__ void dma16(const void* gptr, uint32_t base) {
   asm volatile("s_add_u32 m0, %1, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(gptr), "s"(base), "n"(OFF)
-               : "memory");
+               : "memory", "m0", "scc");
 }
 
 // The same with 4 bytes per lane (lane i writes LDS byte base + OFF + 4 i).
 template <int OFF>
 __device__ __forceinline__ void dma4(const void* gptr, uint32_t base) {
   asm volatile("s_add_u32 m0, %1, %2\n\ts_nop 0\n\tglobal_load_lds_dword %0, off" ::"v"(gptr), "s"(base), "n"(OFF)
-               : "memory");
+               : "memory", "m0", "scc");
 }
+#pragma clang diagnostic pop
 
 struct TileCtx {
   uint32_t lds_wave;        // LDS address of this wave's rows (32 wave) in stage 0
