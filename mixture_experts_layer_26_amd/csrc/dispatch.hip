@@ -2,14 +2,20 @@
 // expert's load, the exclusive offsets, the source token of every sorted row and the
 // row of every pair. This is the per-expert grouping of the sums in the DeepSeek-V3
 // explainer's equation for h'_t (method section 2); the deepseekmodel.com forward
-// listing forms the same groups with one token mask per expert.
+// listing forms the same groups with one token mask per expert. The loads feed the
+// end-of-step bias rule of the same section.
 //
-// Two kernels, no global atomics (the result is deterministic):
-//   count:   block b histograms the pairs of its token range in LDS -> hist[b][e]
-//   scatter: every block scans hist over blocks and experts (for its own bases),
-//            re-reads its tokens in chunks of 256 and ranks each pair within the
-//            chunk by a popcount over a per-expert LDS bitmap of the chunk's tokens,
-//            so rows inside an expert keep ascending token order.
+// Two kernels, and no atomic operation anywhere (global or LDS): the counts and the
+// permutation come from wave ballots, so the result is deterministic by construction.
+//   count:   block b counts the pairs of its token range per expert -> hist[b][e]
+//   scatter: every block scans hist over blocks and experts (for its own bases), then
+//            re-reads its pairs in passes of 256 and gives each pair its row: the rows of
+//            earlier passes, of earlier waves in this pass and of lower lanes of its own
+//            wave that hold the same expert. Pairs are read in index order t * K + k, so
+//            rows inside an expert keep ascending token order.
+// Inside a wave, the lanes that hold the same expert id are found by one ballot per bit
+// of the id (a match over 8 bits); the lowest such lane writes the group's size to the
+// wave's own LDS slot of that expert, which no other lane writes in that pass.
 #include "device.h"
 #include "launch.h"
 
@@ -18,22 +24,52 @@ namespace moe {
 namespace {
 
 constexpr int kThreads = 256;
-constexpr int kChunk = 256;          // tokens per bitmap chunk
-constexpr int kWords = kChunk / 32;  // bitmap words per expert
+constexpr int kWaves = kThreads / kWave;
+constexpr int kChunk = 256;          // tokens per block are a multiple of this
 constexpr int kMaxExperts = 256;
+constexpr int kIdBits = 8;           // expert ids are below 256
+
+// Active lanes of this wave that hold expert id e (bit j for lane j). Every lane of the
+// wave must call it (the ballots are wave-wide).
+__device__ __forceinline__ uint64_t same_expert_lanes(int e, bool active) {
+  uint64_t m = __ballot(active);
+#pragma unroll
+  for (int bit = 0; bit < kIdBits; ++bit) {
+    const uint64_t ones = __ballot((e >> bit) & 1);
+    m &= ((e >> bit) & 1) ? ones : ~ones;
+  }
+  return m;
+}
+
+__device__ __forceinline__ int lane_id() { return static_cast<int>(threadIdx.x % kWave); }
+
+// the lowest lane of a non-empty lane set
+__device__ __forceinline__ int first_lane(uint64_t m) { return __ffsll(static_cast<unsigned long long>(m)) - 1; }
 
 __global__ __launch_bounds__(kThreads) void count_kernel(const int32_t* __restrict__ idx, int64_t T,
                                                          int K, int n_r, int64_t tok_per_block,
                                                          int32_t* __restrict__ hist) {
-  __shared__ int32_t h[kMaxExperts];
-  for (int e = threadIdx.x; e < n_r; e += kThreads) h[e] = 0;
+  __shared__ int32_t wh[kWaves][kMaxExperts];  // pairs per wave and expert
+  for (int i = threadIdx.x; i < kWaves * kMaxExperts; i += kThreads) (&wh[0][0])[i] = 0;
   __syncthreads();
+  const int wave = threadIdx.x / kWave, lane = lane_id();
   const int64_t t0 = static_cast<int64_t>(blockIdx.x) * tok_per_block;
   int64_t t1 = t0 + tok_per_block;
   if (t1 > T) t1 = T;
-  for (int64_t p = t0 * K + threadIdx.x; p < t1 * K; p += kThreads) atomicAdd(&h[idx[p]], 1);
+  const int64_t p1 = t1 * K;
+  for (int64_t q0 = t0 * K; q0 < p1; q0 += kThreads) {  // uniform over the block
+    const int64_t p = q0 + threadIdx.x;
+    const bool act = p < p1;
+    const int e = act ? idx[p] : 0;
+    const uint64_t peers = same_expert_lanes(e, act);
+    if (act && first_lane(peers) == lane) wh[wave][e] += __popcll(peers);
+  }
   __syncthreads();
-  for (int e = threadIdx.x; e < n_r; e += kThreads) hist[static_cast<int64_t>(blockIdx.x) * n_r + e] = h[e];
+  for (int e = threadIdx.x; e < n_r; e += kThreads) {
+    int32_t n = 0;
+    for (int w = 0; w < kWaves; ++w) n += wh[w][e];
+    hist[static_cast<int64_t>(blockIdx.x) * n_r + e] = n;
+  }
 }
 
 __global__ __launch_bounds__(kThreads) void scatter_kernel(
@@ -41,9 +77,9 @@ __global__ __launch_bounds__(kThreads) void scatter_kernel(
     const int32_t* __restrict__ hist, int32_t* __restrict__ count, int32_t* __restrict__ offset,
     int32_t* __restrict__ sorted_token, int32_t* __restrict__ pair_row) {
   __shared__ int32_t base[kMaxExperts];  // first row of this block's pairs, per expert
-  __shared__ int32_t run[kMaxExperts];   // pairs of earlier chunks of this block, per expert
+  __shared__ int32_t run[kMaxExperts];   // pairs of earlier passes of this block, per expert
   __shared__ int32_t tot[kMaxExperts];
-  __shared__ uint32_t bits[kMaxExperts * kWords];
+  __shared__ int32_t wc[2][kWaves][kMaxExperts];  // pairs per wave and expert of a pass (two buffers)
   const int b = blockIdx.x;
   for (int e = threadIdx.x; e < n_r; e += kThreads) {
     int32_t before = 0, all = 0;
@@ -56,6 +92,7 @@ __global__ __launch_bounds__(kThreads) void scatter_kernel(
     tot[e] = all;
     run[e] = 0;
   }
+  for (int i = threadIdx.x; i < 2 * kWaves * kMaxExperts; i += kThreads) (&wc[0][0][0])[i] = 0;
   __syncthreads();
   // exclusive scan of tot over experts (n_r <= 256, serial in thread 0)
   if (threadIdx.x == 0) {
@@ -78,36 +115,40 @@ __global__ __launch_bounds__(kThreads) void scatter_kernel(
     base[e] += tot[e];
   }
   __syncthreads();
+  const int wave = threadIdx.x / kWave, lane = lane_id();
+  const uint64_t below = (uint64_t(1) << lane) - 1;  // lanes under this one
   const int64_t t0 = static_cast<int64_t>(b) * tok_per_block;
   int64_t t1 = t0 + tok_per_block;
   if (t1 > T) t1 = T;
-  for (int64_t c0 = t0; c0 < t1; c0 += kChunk) {
-    const int64_t c1 = (c0 + kChunk < t1) ? c0 + kChunk : t1;
-    for (int w = threadIdx.x; w < n_r * kWords; w += kThreads) bits[w] = 0;
+  const int64_t p1 = t1 * K;
+  int cur = 0;
+  for (int64_t q0 = t0 * K; q0 < p1; q0 += kThreads, cur ^= 1) {  // uniform over the block
+    // phase 1: each wave's group sizes of this pass (buffer cur was cleared two passes ago)
+    const int64_t p = q0 + threadIdx.x;
+    const bool act = p < p1;
+    const int e = act ? idx[p] : 0;
+    const uint64_t peers = same_expert_lanes(e, act);
+    if (act && first_lane(peers) == lane) wc[cur][wave][e] = __popcll(peers);
     __syncthreads();
-    for (int64_t p = c0 * K + threadIdx.x; p < c1 * K; p += kThreads) {
-      const int tl = static_cast<int>(p / K - c0);
-      atomicOr(&bits[idx[p] * kWords + tl / 32], 1u << (tl % 32));
-    }
-    __syncthreads();
-    for (int64_t p = c0 * K + threadIdx.x; p < c1 * K; p += kThreads) {
-      const int64_t t = p / K;
-      const int tl = static_cast<int>(t - c0);
-      const int e = idx[p];
-      const uint32_t* bw = bits + e * kWords;
-      int rank = __popc(bw[tl / 32] & ((1u << (tl % 32)) - 1u));
-      for (int q = 0; q < tl / 32; ++q) rank += __popc(bw[q]);
-      const int32_t row = base[e] + run[e] + rank;
-      sorted_token[row] = static_cast<int32_t>(t);
+    // phase 2: rows of this pass's pairs
+    if (act) {
+      int32_t row = base[e] + run[e] + __popcll(peers & below);
+      for (int w = 0; w < wave; ++w) row += wc[cur][w][e];
+      sorted_token[row] = static_cast<int32_t>(p / K);
       pair_row[p] = row;
     }
     __syncthreads();
-    for (int e = threadIdx.x; e < n_r; e += kThreads) {
+    // phase 3: carry the pass's counts into run and clear buffer cur for the pass after
+    // next (the next pass writes the other buffer, and its phase 2 reads run only after
+    // its own barrier)
+    for (int e2 = threadIdx.x; e2 < n_r; e2 += kThreads) {
       int32_t n = 0;
-      for (int q = 0; q < kWords; ++q) n += __popc(bits[e * kWords + q]);
-      run[e] += n;
+      for (int w = 0; w < kWaves; ++w) {
+        n += wc[cur][w][e2];
+        wc[cur][w][e2] = 0;
+      }
+      run[e2] += n;
     }
-    __syncthreads();
   }
 }
 
