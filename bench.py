@@ -4,13 +4,18 @@
 A step is one pass of the whole layer over one batch of synthetic tokens:
 moe_route -> moe_dispatch -> moe_grouped_ffn -> moe_combine -> moe_bias_update, all
 on one HIP stream through the C ABI, with inputs and weights resident in HBM before
-the timed region. The bias carries over from step to step, as the end-of-step rule
-intends. The default workload is the DeepSeek-V3-shaped prefill layer in bf16
-(T=8192, d=7168, 256 routed experts, top-8, 1 shared, d_ff=2048).
+the timed region. Before every step the bias is restored from the workload's b, so
+each step runs the configuration as named (b ~ U(-0.01, 0.01)) instead of the flatter
+loads the update would reach after a few steps on one fixed batch. The headline
+workload is the DeepSeek-V3-shaped prefill layer in bf16 (T=8192, d=7168, 256 routed
+experts, top-8, 1 shared, d_ff=2048).
 
-Prints one JSON line: whole-layer tokens/s, plus a roofline entry for the grouped
-FFN (the two expert GEMM launches, >99% of the FLOPs) timed with HIP events on the
-launch stream, and the CPU oracle timed on a bounded sample of the same workload.
+Prints one JSON line: whole-layer tokens/s of the headline workload, a roofline entry
+for its grouped FFN (the two expert GEMM launches, >99% of the FLOPs) timed with HIP
+events on the launch stream, and the CPU oracle timed on a bounded sample of the same
+workload. The other workloads (FP8 prefill, skewed decode, mid and tiny) are timed
+after it in the same run and appear under "workloads", each with its own roofline
+and oracle baseline.
 
 --backward times the layer backward instead (moe_combine_backward ->
 moe_grouped_ffn_backward -> moe_route_backward after one forward step, row-major bf16
@@ -28,6 +33,8 @@ import json
 import os
 import sys
 import time
+
+import numpy as np
 
 ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
@@ -47,7 +54,10 @@ def parse():
     p.add_argument("--gpus", type=int, default=1)
     p.add_argument("--steps", type=int, default=20)
     p.add_argument("--warmup", type=int, default=3)
-    p.add_argument("--workload", default="v3_prefill_bf16")
+    p.add_argument("--workload", default="v3_prefill_bf16", help="the headline workload")
+    p.add_argument("--also", default=",".join(SUB_WORKLOADS),
+                   help="workloads timed after the headline one, each a sub-entry of the same line "
+                        "('none' for the headline only)")
     p.add_argument("--cpu-baseline", dest="cpu", action="store_true", default=True)
     p.add_argument("--no-cpu-baseline", dest="cpu", action="store_false")
     p.add_argument("--cpu-tokens", type=int, default=0, help="oracle sample size (0 = auto)")
@@ -92,7 +102,12 @@ def stored_traffic(workload: str, ffn: str, layout: str):
     return t
 
 
-def setup(wname: str, layout: str):
+def setup(wname: str, layout: str, cache: dict | None = None, keep_rows: bool = False):
+    """Generate the workload on the device and prepare its expert weights (FP8 codes, tiled
+    layout) outside any timed region. `cache` maps a seed to the uploaded tensors of an
+    earlier workload with the same seed and shape (the FP8 prefill workload reuses the bf16
+    one's tensors, from which its codes are quantised); `keep_rows` leaves the row-major
+    weights in the cache for that."""
     import torch
 
     from mixture_experts_layer_26_amd import abi
@@ -102,7 +117,15 @@ def setup(wname: str, layout: str):
 
     w = I.WORKLOADS[wname]
     t0 = time.time()
-    dev = D.upload(w, "cuda")
+    key = (w.seed, w.T, w.d, w.n_routed, w.d_ff, w.n_shared, w.act)
+    if cache is not None and key in cache:
+        dev = dict(cache.pop(key))
+        reused = True
+    else:
+        dev = D.upload(w, "cuda")
+        reused = False
+    if keep_rows and cache is not None:
+        cache[key] = dict(dev)
     L = MoeLayer(w.T, w.d, w.n_routed, w.top_k, w.n_shared, w.d_ff, w.act, w.ffn)
     routed, shared = dev["routed"], dev["shared"]
     if w.ffn == "fp8":  # one-time preparation of the weights, outside the timed region
@@ -119,44 +142,62 @@ def setup(wname: str, layout: str):
     L.set_experts(routed, shared, lay)
     dev["weights"] = (routed, shared)
     torch.cuda.synchronize()
-    log(f"[bench] {wname}: inputs generated and resident in {time.time() - t0:.1f} s "
+    log(f"[bench] {wname}: inputs {'reused' if reused else 'generated'} and resident in {time.time() - t0:.1f} s "
         f"({'tiled' if lay == abi.MOE_LAYOUT_TILED else 'row-major'} weights)")
     return w, dev, L, ("tiled" if lay == abi.MOE_LAYOUT_TILED else "rows")
 
 
 def time_steps(w, dev, L, steps: int, warmup: int):
+    """W untimed and K timed layer steps on one batch. Before every step the bias is
+    restored from the workload's b (a 1 KB device copy ahead of the step's events), so
+    every step routes the same tokens with the same b: the workload stays the one the
+    configuration names, instead of drifting towards balance as the update would carry
+    it. HIP events on the launch stream bracket each step's five calls and, separately,
+    its grouped FFN; each step's expert counts are copied to a log read once at the end.
+    Returns (wall seconds of the K steps, per-step ms, per-step FFN ms, count log)."""
     import torch
 
     stream = torch.cuda.current_stream()
-    bias = dev["b"].clone()
+    b0 = dev["b"]
+    bias = b0.clone()
     for _ in range(warmup):
+        bias.copy_(b0)
         L.step(dev["u"], dev["e"], bias, w.gamma, stream)
+    counts = torch.empty((steps, w.n_routed), dtype=torch.int32, device="cuda")
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(steps)]
     torch.cuda.synchronize()
-    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
     t0 = time.perf_counter()
     for i in range(steps):
+        bias.copy_(b0)
+        ev[i][0].record(stream)
         L.route(dev["u"], dev["e"], bias, stream)
         L.dispatch(stream)
-        ev[i][0].record(stream)
-        L.grouped_ffn(dev["u"], stream)
         ev[i][1].record(stream)
+        L.grouped_ffn(dev["u"], stream)
+        ev[i][2].record(stream)
         L.combine(dev["u"], stream)
         L.bias_update(bias, w.gamma, stream)
+        ev[i][3].record(stream)
+        counts[i].copy_(L.expert_count)
     torch.cuda.synchronize()
     elapsed = time.perf_counter() - t0
-    ffn_ms = [a.elapsed_time(b) for a, b in ev]
-    return elapsed, ffn_ms
+    step_ms = [e[0].elapsed_time(e[3]) for e in ev]
+    ffn_ms = [e[1].elapsed_time(e[2]) for e in ev]
+    return elapsed, step_ms, ffn_ms, counts.cpu().numpy()
 
 
 def call_breakdown(w, dev, L, steps: int = 3):
-    """Average milliseconds of each ABI call (HIP events on the launch stream)."""
+    """Average milliseconds of each ABI call (HIP events on the launch stream), the bias
+    restored before every step as in the timed loop."""
     import torch
 
     stream = torch.cuda.current_stream()
-    bias = dev["b"].clone()
+    b0 = dev["b"]
+    bias = b0.clone()
     names = ["route", "dispatch", "grouped_ffn", "combine", "bias_update"]
     acc = dict.fromkeys(names, 0.0)
     for _ in range(steps):
+        bias.copy_(b0)
         ev = [torch.cuda.Event(enable_timing=True) for _ in range(len(names) + 1)]
         ev[0].record(stream)
         L.route(dev["u"], dev["e"], bias, stream)
@@ -175,26 +216,49 @@ def call_breakdown(w, dev, L, steps: int = 3):
     return {n: round(v / steps, 4) for n, v in acc.items()}
 
 
-def ffn_algorithmic_bytes(w, L) -> float:
-    """Bytes the grouped FFN must move at least once: the weights of every expert that
-    received a row (plus the shared experts) and scales for FP8, the activations read
-    (u) and the outputs written (y_routed, y_shared). H is an intermediate and is not
-    counted."""
-    counts = L.expert_count.cpu().numpy()
+def ffn_algorithmic_bytes(w, counts) -> tuple:
+    """Bytes the grouped FFN must move at least once: the weights of every routed expert
+    that received a row plus the shared experts (with their 128x128 block scales for FP8),
+    and the activations u it reads. Intermediates and outputs (H, y_routed, y_shared) are
+    not counted. counts: the expert loads of the step."""
+    counts = np.asarray(counts)
     active = int((counts > 0).sum())
     wbytes = 1 if w.ffn == "fp8" else (4 if w.ffn == "f32" else 2)
     per_expert = 3 * w.d * w.d_ff * wbytes
     if w.ffn == "fp8":
         per_expert += 3 * (w.d // 128) * (w.d_ff // 128) * 4
     abytes = 4 if w.act == "f32" else 2
-    io = w.T * w.d * abytes + w.pairs * w.d * abytes + (w.T * w.d * 4 if w.n_shared else 0)
-    return (active + w.n_shared) * per_expert + io, active
+    return (active + w.n_shared) * per_expert + w.T * w.d * abytes, active
+
+
+def roofline_kind(w) -> str:
+    """What bounds the grouped FFN of a workload: "latency" for the tiny fp32 layer, "hbm"
+    when the experts average fewer rows than one 32-row MFMA block (weight streaming), else
+    "mfma"."""
+    if w.ffn == "f32":
+        return "latency"
+    return "hbm" if w.T * w.top_k < 32 * w.n_routed else "mfma"
+
+
+def cpu_model() -> str:
+    """The host CPU's model name (first 'model name' line of /proc/cpuinfo)."""
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def cpu_threads() -> int:
+    cores = len(os.sched_getaffinity(0))
+    return min(cores, int(os.environ.get("OMP_NUM_THREADS", cores)))
 
 
 def cpu_baseline(w, n_tokens: int):
     """The oracle, untuned, on the first n tokens of the same batch (whole layer per token)."""
-    import numpy as np
-
     import oracle
     from mixture_experts_layer_26_amd import inputs as I
 
@@ -213,12 +277,85 @@ def cpu_baseline(w, n_tokens: int):
     t0 = time.perf_counter()
     oracle.layer(u, e, b, routed, shared, top_k=w.top_k, d_ff=w.d_ff, act=w.act, ffn=w.ffn)
     dt = time.perf_counter() - t0
-    cores = len(os.sched_getaffinity(0))
-    threads = int(os.environ.get("OMP_NUM_THREADS", cores))
-    del np
-    return {"value": n_tokens / dt, "unit": "tokens/s", "cores": min(cores, threads), "kind": "oracle",
+    return {"value": round(n_tokens / dt, 3), "unit": "tokens/s", "cores": cpu_threads(), "cpu": cpu_model(),
+            "kind": "oracle",
             "sample": f"whole layer (route, {w.top_k}+{w.n_shared} SwiGLU experts, combine) for the first "
                       f"{n_tokens} tokens of the {w.name} batch, double precision, {dt:.1f} s"}
+
+
+# Oracle sample per workload: about 5-15 s of host time each on 16 cores.
+CPU_TOKENS = {"v3_prefill_bf16": 384, "v3_prefill_fp8": 256, "v3_decode_skewed": 128, "mid_bf16": 512,
+              "tiny_f32": 64}
+# Timed steps of the workloads timed beside the headline one (the headline takes --steps).
+SUB_STEPS = {"v3_prefill_fp8": 20, "v3_decode_skewed": 50, "mid_bf16": 100, "tiny_f32": 200}
+SUB_WORKLOADS = ("v3_prefill_fp8", "v3_decode_skewed", "mid_bf16", "tiny_f32")
+
+
+def bench_forward(wname: str, layout: str, steps: int, warmup: int, cpu: bool, cpu_tokens: int,
+                  cache: dict | None = None, keep_rows: bool = False, calibrate: bool = False) -> dict:
+    """Time one workload's layer step and return its JSON entry (the fields of the headline
+    line: value, ms_per_step, roofline, cpu_baseline, ...)."""
+    import torch
+
+    w, dev, L, layout = setup(wname, layout, cache, keep_rows)
+    if calibrate:
+        src = torch.empty(1 << 30, dtype=torch.uint8, device="cuda")
+        dst = torch.empty_like(src)
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
+    elapsed, step_ms, ffn_ms, counts = time_steps(w, dev, L, steps, warmup)
+    calls = call_breakdown(w, dev, L)
+    mean = w.T * w.top_k / w.n_routed
+    loads = sorted({round(float(c.max()) / mean, 4) for c in counts})
+    same = bool((counts == counts[0]).all())
+    ms_wall = 1e3 * elapsed / steps
+    ms_ev = sum(step_ms) / len(step_ms)
+    ffn_avg = sum(ffn_ms) / len(ffn_ms)
+    ffn_tf = w.ffn_flops() / (ffn_avg * 1e-3) / 1e12
+    dt = "fp8" if w.ffn == "fp8" else w.act
+    abytes, active = ffn_algorithmic_bytes(w, counts[0])
+    gbs = abytes / (ffn_avg * 1e-3) / 1e9
+    kind = roofline_kind(w)
+    if kind == "hbm":
+        roof = {"bound": "hbm", "achieved": round(gbs, 1), "peak": PEAKS["hbm"], "unit": "GB/s",
+                "frac": round(gbs / PEAKS["hbm"], 4)}
+    else:  # the tiny fp32 layer is latency-bound: its fp32 FLOP rate is reported, not claimed
+        pk = PEAKS["f32" if w.ffn == "f32" else dt]
+        roof = {"bound": "mfma" if kind == "mfma" else "latency", "achieved": round(ffn_tf, 3), "peak": pk,
+                "unit": "TFLOP/s", "frac": round(ffn_tf / pk, 4)}
+    traffic = stored_traffic(w.name, w.ffn, layout) if w.ffn != "f32" else None
+    roof.update({"traffic": traffic["hbm_bytes_per_call"] if traffic else None,
+                 "kernel": "grouped FFN (gate/up GEMM + SwiGLU, down GEMM)",
+                 "ms_per_launch": round(ffn_avg, 4),
+                 "algorithmic_bytes": abytes, "algorithmic_flops": w.ffn_flops(),
+                 "ffn_tflops": round(ffn_tf, 2), "ffn_hbm_gbs": round(gbs, 1),
+                 "active_experts": active})
+    res = {
+        "value": round(w.T * steps / elapsed, 1),
+        "unit": "tokens/s",
+        "steps": steps,
+        "warmup": warmup,
+        "ms_per_step": round(ms_wall, 4),
+        "gpu_ms_per_step": round(ms_ev, 4),
+        "dtype": dt,
+        "config": {"workload": w.name, "T": w.T, "d": w.d, "n_routed": w.n_routed, "top_k": w.top_k,
+                   "n_shared": w.n_shared, "d_ff": w.d_ff, "act": w.act, "ffn": w.ffn, "weights": layout},
+        "layer_tflops": round(w.flops() / (ms_ev * 1e-3) / 1e12, 3),
+        "call_ms": calls,
+        "load_max_over_mean": loads[0] if same else loads,
+        "loads_identical_every_step": same,
+        "roofline": roof,
+    }
+    if kind == "latency":
+        res["us_per_step"] = round(1e3 * ms_ev, 2)
+        res["call_us"] = {k: round(1e3 * v, 2) for k, v in calls.items()}
+    del L, dev
+    torch.cuda.synchronize()
+    torch.cuda.empty_cache()
+    if cpu:
+        res["cpu_baseline"] = cpu_baseline(w, min(cpu_tokens or CPU_TOKENS.get(w.name, 256), w.T))
+    return res
 
 
 def bench_backward(args):
@@ -376,61 +513,35 @@ def main():
     if args.balance:
         bench_balance(args)
         return
-    w, dev, L, layout = setup(args.workload, args.layout)
-    if args.calibrate_copy:
-        src = torch.empty(1 << 30, dtype=torch.uint8, device="cuda")
-        dst = torch.empty_like(src)
-        dst.copy_(src)
-        torch.cuda.synchronize()
-        del src, dst
-    elapsed, ffn_ms = time_steps(w, dev, L, args.steps, args.warmup)
-    calls = call_breakdown(w, dev, L)
-    ms_step = 1e3 * elapsed / args.steps
-    tok_s = w.T * args.steps / elapsed
-    tflops = w.flops() * args.steps / elapsed / 1e12
-    ffn_avg = sum(ffn_ms) / len(ffn_ms)
-    ffn_tf = w.ffn_flops() / (ffn_avg * 1e-3) / 1e12
-    dt = "fp8" if w.ffn == "fp8" else w.act
-    abytes, active = ffn_algorithmic_bytes(w, L)
-    traffic = stored_traffic(w.name, w.ffn, layout)
-    decode = w.T * w.top_k < 32 * w.n_routed  # under one MFMA block of rows per expert: weight streaming
-    if decode:
-        gbs = abytes / (ffn_avg * 1e-3) / 1e9
-        roof = {"bound": "hbm", "achieved": round(gbs, 1), "peak": PEAKS["hbm"], "unit": "GB/s",
-                "frac": round(gbs / PEAKS["hbm"], 4)}
-    else:
-        roof = {"bound": "mfma", "achieved": round(ffn_tf, 2), "peak": PEAKS[dt], "unit": "TFLOP/s",
-                "frac": round(ffn_tf / PEAKS[dt], 4)}
-    roof.update({"traffic": traffic["hbm_bytes_per_call"] if traffic else None,
-                 "kernel": "grouped FFN (gate/up GEMM + SwiGLU, down GEMM)",
-                 "ms_per_launch": round(ffn_avg, 4),
-                 "algorithmic_bytes": abytes, "algorithmic_flops": w.ffn_flops(),
-                 "ffn_tflops": round(ffn_tf, 2),
-                 "ffn_hbm_gbs": round(abytes / (ffn_avg * 1e-3) / 1e9, 1),
-                 "active_experts": active})
+    also = [] if args.also in ("", "none") else [x for x in args.also.split(",") if x and x != args.workload]
+    cache = {}
+    head = bench_forward(args.workload, args.layout, args.steps, args.warmup, args.cpu, args.cpu_tokens, cache,
+                         keep_rows=any(x == "v3_prefill_fp8" for x in also), calibrate=args.calibrate_copy)
     res = {
         "metric": "MoE layer tokens/s + TFLOP/s (% MFMA peak), V3 shape bf16/fp8, 1 MI355X",
-        "value": round(tok_s, 1),
-        "unit": "tokens/s",
+        "value": head.pop("value"),
+        "unit": head.pop("unit"),
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
-        "ms_per_step": round(ms_step, 4),
+        "ms_per_step": head.pop("ms_per_step"),
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": dt,
+        "dtype": head.pop("dtype"),
         "data": "synthetic (seeded Philox/Box-Muller inputs, random-init expert weights)",
-        "config": {"workload": w.name, "T": w.T, "d": w.d, "n_routed": w.n_routed, "top_k": w.top_k,
-                   "n_shared": w.n_shared, "d_ff": w.d_ff, "act": w.act, "ffn": w.ffn, "weights": layout},
-        "layer_tflops": round(tflops, 2),
-        "layer_frac_of_peak": round(tflops / PEAKS[dt], 4),
-        "call_ms": calls,
-        "roofline": roof,
     }
-    if args.cpu:
-        n = args.cpu_tokens or (1024 if w.d <= 2048 else 384)
-        res["cpu_baseline"] = cpu_baseline(w, min(n, w.T))
+    head.pop("steps")
+    head.pop("warmup")
+    res.update(head)
+    if also:
+        res["workloads"] = {}
+    for name in also:
+        sub = bench_forward(name, args.layout, SUB_STEPS.get(name, args.steps), args.warmup, args.cpu, 0, cache)
+        res["workloads"][name] = sub
+        log(f"[bench] {name}: {sub['value']:.1f} tokens/s, grouped FFN {sub['roofline']['ms_per_launch']} ms, "
+            f"frac {sub['roofline']['frac']}")
+    cache.clear()
     print(json.dumps(res), flush=True)
 
 

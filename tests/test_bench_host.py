@@ -14,12 +14,6 @@ from mixture_experts_layer_26_amd import inputs as I
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 
 
-class _Layer:  # the one attribute ffn_algorithmic_bytes reads
-    def __init__(self, counts):
-        import torch
-        self.expert_count = torch.from_numpy(np.asarray(counts, dtype=np.int32))
-
-
 def test_v3_prefill_flops():
     # 3 matrices, 2 FLOP per multiply-add: 6 d d_ff per routed row and per shared row
     w = I.WORKLOADS["v3_prefill_bf16"]
@@ -27,12 +21,13 @@ def test_v3_prefill_flops():
 
 
 def test_v3_prefill_algorithmic_bytes():
+    # weights of every active routed expert and the shared one, plus u read once; H and the
+    # outputs y_routed, y_shared are not algorithmic bytes
     w = I.WORKLOADS["v3_prefill_bf16"]
     counts = np.full(256, 8192 * 8 // 256)
-    got, active = bench.ffn_algorithmic_bytes(w, _Layer(counts))
-    weights = (256 + 1) * 3 * 7168 * 2048 * 2          # every routed expert and the shared one, bf16
-    io = 8192 * 7168 * 2 + 8192 * 8 * 7168 * 2 + 8192 * 7168 * 4  # u, y_routed, y_shared (fp32)
-    assert active == 256 and got == weights + io
+    got, active = bench.ffn_algorithmic_bytes(w, counts)
+    weights = (256 + 1) * 3 * 7168 * 2048 * 2
+    assert active == 256 and got == weights + 8192 * 7168 * 2
 
 
 def test_algorithmic_bytes_count_active_experts_only():
@@ -40,17 +35,27 @@ def test_algorithmic_bytes_count_active_experts_only():
     counts = np.zeros(256, dtype=np.int64)
     counts[:10] = 128 * 8 // 10
     counts[10] = 128 * 8 - counts[:10].sum()
-    got, active = bench.ffn_algorithmic_bytes(w, _Layer(counts))
+    got, active = bench.ffn_algorithmic_bytes(w, counts)
     assert active == 11
-    assert got == (11 + 1) * 3 * 7168 * 2048 * 2 + 128 * 7168 * 2 + 128 * 8 * 7168 * 2 + 128 * 7168 * 4
+    assert got == (11 + 1) * 3 * 7168 * 2048 * 2 + 128 * 7168 * 2
 
 
 def test_fp8_bytes_include_block_scales():
     w = I.WORKLOADS["v3_prefill_fp8"]
-    got, _ = bench.ffn_algorithmic_bytes(w, _Layer(np.full(256, 256)))
+    got, _ = bench.ffn_algorithmic_bytes(w, np.full(256, 256))
     per_expert = 3 * 7168 * 2048 + 3 * 56 * 16 * 4
-    io = 8192 * 7168 * 2 + 65536 * 7168 * 2 + 8192 * 7168 * 4
-    assert got == 257 * per_expert + io
+    assert got == 257 * per_expert + 8192 * 7168 * 2
+
+
+def test_roofline_kind_per_workload():
+    kinds = {n: bench.roofline_kind(w) for n, w in I.WORKLOADS.items()}
+    assert kinds == {"tiny_f32": "latency", "mid_bf16": "mfma", "v3_prefill_bf16": "mfma",
+                     "v3_prefill_fp8": "mfma", "v3_decode_skewed": "hbm"}
+
+
+def test_sub_workloads_cover_every_other_workload():
+    assert set(bench.SUB_WORKLOADS) | {"v3_prefill_bf16"} == set(I.WORKLOADS)
+    assert set(bench.CPU_TOKENS) == set(I.WORKLOADS)
 
 
 def test_stored_traffic_needs_matching_sources(tmp_path, monkeypatch):
