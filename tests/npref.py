@@ -2,8 +2,8 @@
 
 These are written independently of ``oracle/moe_oracle.c``: NumPy float64 with
 BLAS matrix products (a different summation order), bit-level roundings, full
-sorts instead of arg-max passes, and the per-expert masked loop of the
-"DeepSeek モデルアーキテクチャ徹底解説" forward listing instead of per-token
+sorts instead of arg-max passes, and an evaluation over the (token, expert) pairs
+ordered by expert with a scatter-add back to the tokens instead of per-token
 evaluation. They agree with the oracle to rounding order, not bit for bit.
 """
 import numpy as np
@@ -80,18 +80,26 @@ def dense_layer(u, e, b, routed, shared, K, hround, score="sigmoid"):
     return out, sel, G
 
 
-def masked_loop_layer(u, sel, gates, routed, shared, hround):
-    """The per-expert masked loop: for each expert, the tokens that chose it, their FFN
-    rows, and a gate-weighted accumulation; plus the shared experts and the residual."""
+def pair_scatter_layer(u, sel, gates, routed, shared, hround):
+    """h'_t of the method's equation built from the (token, expert, gate) pairs: the T*K
+    pairs are ordered by expert with a stable argsort, each expert's run of pairs is
+    evaluated as one batch of FFN rows, and every row is scattered into its token's
+    output with its gate (np.add.at adds the rows of one token in pair order). The shared
+    experts and the residual complete the sum."""
+    n, K = sel.shape
+    tok = np.repeat(np.arange(n), K)
+    ex = np.asarray(sel).reshape(-1)
+    g = np.asarray(gates, np.float64).reshape(-1)
+    order = np.argsort(ex, kind="stable")
+    ex_sorted = ex[order]
+    starts = np.flatnonzero(np.r_[True, ex_sorted[1:] != ex_sorted[:-1]])
+    ends = np.r_[starts[1:], ex_sorted.size]
+    rows = np.empty((ex.size, u.shape[1]))
+    for a, z in zip(starts, ends):
+        p = order[a:z]
+        rows[p] = swiglu_ffn(u[tok[p]], *routed[int(ex_sorted[a])], hround)
     routed_out = np.zeros_like(u)
-    for i in sorted(routed):
-        mask = (sel == i)
-        tok = np.nonzero(mask.any(axis=1))[0]
-        if tok.size == 0:
-            continue
-        y = swiglu_ffn(u[tok], *routed[i], hround)
-        w = gates[mask]
-        routed_out[tok] += y * w[:, None]
+    np.add.at(routed_out, tok, rows * g[:, None])
     shared_out = np.zeros_like(u)
     for (w1, w3, w2) in shared:
         shared_out += swiglu_ffn(u, w1, w3, w2, hround)

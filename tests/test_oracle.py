@@ -516,10 +516,10 @@ def test_layer_dense_all_experts(name, T, score):
     assert np.array_equal(res["idx"], sel)
     scale = np.max(np.abs(ref))
     assert np.max(np.abs(res["out"] - ref)) <= 1e-12 * scale
-    # the masked per-expert loop gives the same output
-    ref2 = npref.masked_loop_layer(npref.widen(u, w.act), res["idx"], res["gate"],
-                                   {i: _widen_tuple(w, t) for i, t in routed.items()},
-                                   [_widen_tuple(w, t) for t in shared], _hround(w))
+    # the pairs ordered by expert, evaluated per expert and scattered back, give the same output
+    ref2 = npref.pair_scatter_layer(npref.widen(u, w.act), res["idx"], res["gate"],
+                                    {i: _widen_tuple(w, t) for i, t in routed.items()},
+                                    [_widen_tuple(w, t) for t in shared], _hround(w))
     assert np.max(np.abs(res["out"] - ref2)) <= 1e-12 * scale
     # components add up to the output
     recon = npref.widen(u, w.act) + res["shared_sum"] + res["routed_sum"]
