@@ -19,7 +19,9 @@
  *
  * Conventions for every call:
  *  - All array pointers are DEVICE pointers, allocated and owned by the caller.
- *    The library allocates no device memory and keeps no per-call state.
+ *    The library allocates no device memory and keeps no per-call state; the one
+ *    exception, moe_grouped_ffn_noalloc, uses a fixed array that is part of the
+ *    library's device code (each GPU's copy keeps the last call's scratch contents).
  *  - `stream` is a hipStream_t passed as void* (NULL = the null stream). Every call
  *    only enqueues work and returns; calls on one stream run in order. There is no
  *    device-to-host copy or synchronisation inside any call.
@@ -45,14 +47,16 @@
 extern "C" {
 #endif
 
-#define MOE_ABI_VERSION 4
+#define MOE_ABI_VERSION 5
 
 typedef enum {
   MOE_OK = 0,
   MOE_ERR_INVALID_ARG = 1, /* null pointer, bad shape or bad dtype combination   */
   MOE_ERR_UNSUPPORTED = 2, /* valid request outside what the kernels implement    */
   MOE_ERR_WORKSPACE = 3,   /* workspace pointer null or smaller than required     */
-  MOE_ERR_HIP = 4          /* a HIP runtime call or kernel launch failed          */
+  MOE_ERR_HIP = 4,         /* a HIP runtime call or kernel launch failed          */
+  MOE_ERR_SCRATCH_LIMIT = 5 /* moe_grouped_ffn_noalloc: the shape needs more scratch
+                               than its fixed buffer (MOE_NOALLOC_SCRATCH_BYTES) holds */
 } moe_status;
 
 typedef enum { MOE_F32 = 0, MOE_BF16 = 1, MOE_FP8_E4M3 = 2 } moe_dtype;
@@ -165,6 +169,28 @@ moe_status moe_grouped_ffn(const moe_shape* shape, const void* u, const int32_t*
                            const int32_t* sorted_token, const moe_expert_set* routed,
                            const moe_expert_set* shared, void* y_routed, float* y_shared,
                            void* ws, size_t ws_bytes, void* stream);
+
+/* ---------------------------------------------------------------------------
+ * moe_grouped_ffn_noalloc: moe_grouped_ffn without a workspace argument, for callers that
+ * cannot allocate device memory (code under HIP graph capture, serving loops, harnesses
+ * that forbid hipMalloc). It calls no allocating routine: the scratch the kernels need
+ * (tile-scheduling state and H, the bytes moe_workspace_bytes(shape, MOE_CALL_GROUPED_FFN)
+ * gives) lives in a fixed device array inside the library, MOE_NOALLOC_SCRATCH_BYTES long,
+ * of which each GPU holds its own copy until the process ends (its address is looked up
+ * once per device, on that device's first call). Arguments, outputs and results are those
+ * of moe_grouped_ffn, bit for bit.
+ *  - A shape whose workspace exceeds MOE_NOALLOC_SCRATCH_BYTES returns
+ *    MOE_ERR_SCRATCH_LIMIT and enqueues nothing (at the V3 shape, d = 7168 and d_ff = 2048
+ *    with 8 + 1 experts per token, bf16 fits up to 1,818 tokens).
+ *  - Every call on one GPU shares that GPU's array, and the array keeps the last call's
+ *    contents (the call clears the state it needs zeroed itself, with a fill kernel). So
+ *    calls that overlap on one GPU (on different streams, or from several threads without
+ *    ordering) race and give wrong results: order them on one stream. */
+#define MOE_NOALLOC_SCRATCH_BYTES ((size_t)64 << 20)
+moe_status moe_grouped_ffn_noalloc(const moe_shape* shape, const void* u, const int32_t* expert_offset,
+                                   const int32_t* sorted_token, const moe_expert_set* routed,
+                                   const moe_expert_set* shared, void* y_routed, float* y_shared,
+                                   void* stream);
 
 /* ---------------------------------------------------------------------------
  * moe_combine: h'_t = u_t + shared sum + sum_k g_{k,t} * y_routed[pair_row[t,k]], in

@@ -13,14 +13,15 @@ import os
 HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(HERE, "libmoe.so")
 
-MOE_OK, MOE_ERR_INVALID_ARG, MOE_ERR_UNSUPPORTED, MOE_ERR_WORKSPACE, MOE_ERR_HIP = range(5)
+MOE_OK, MOE_ERR_INVALID_ARG, MOE_ERR_UNSUPPORTED, MOE_ERR_WORKSPACE, MOE_ERR_HIP, MOE_ERR_SCRATCH_LIMIT = range(6)
+MOE_NOALLOC_SCRATCH_BYTES = 64 << 20
 MOE_F32, MOE_BF16, MOE_FP8_E4M3 = 0, 1, 2
 MOE_CALL_ROUTE, MOE_CALL_DISPATCH, MOE_CALL_GROUPED_FFN, MOE_CALL_COMBINE, MOE_CALL_BIAS_UPDATE = range(5)
 MOE_CALL_GROUPED_FFN_BACKWARD, MOE_CALL_ROUTE_BACKWARD = 5, 6
 MOE_LAYOUT_ROWS, MOE_LAYOUT_TILED = 0, 1
 MOE_W1, MOE_W3, MOE_W2 = 0, 1, 2
 MOE_SCORE_SIGMOID, MOE_SCORE_SOFTMAX = 0, 1
-ABI_VERSION = 4
+ABI_VERSION = 5
 DTYPES = {"f32": MOE_F32, "bf16": MOE_BF16, "fp8": MOE_FP8_E4M3}
 SCORES = {"sigmoid": MOE_SCORE_SIGMOID, "softmax": MOE_SCORE_SOFTMAX}
 
@@ -67,6 +68,7 @@ def load():
         "moe_route": [sp, vp, vp, vp, vp, vp, vp, sz, vp],
         "moe_dispatch": [sp, vp, vp, vp, vp, vp, vp, sz, vp],
         "moe_grouped_ffn": [sp, vp, vp, vp, ep, ep, vp, vp, vp, sz, vp],
+        "moe_grouped_ffn_noalloc": [sp, vp, vp, vp, ep, ep, vp, vp, vp],
         "moe_combine": [sp, vp, vp, vp, vp, vp, vp, vp],
         "moe_bias_update": [sp, vp, f32, vp, vp],
         "moe_quantize_fp8": [vp, i32, i64, i64, i32, i32, vp, vp, vp],
@@ -142,6 +144,14 @@ def moe_grouped_ffn(shape, u, expert_offset, sorted_token, routed: moe_expert_se
                                                      _ptr(sorted_token), ctypes.byref(routed), sh,
                                                      _ptr(y_routed), _ptr(y_shared), _ptr(ws), ws_bytes,
                                                      _stream(stream)))
+
+
+def moe_grouped_ffn_noalloc(shape, u, expert_offset, sorted_token, routed: moe_expert_set, shared, y_routed,
+                            y_shared, stream=None):
+    sh = ctypes.byref(shared) if shared is not None else None
+    _check("moe_grouped_ffn_noalloc", load().moe_grouped_ffn_noalloc(
+        ctypes.byref(shape), _ptr(u), _ptr(expert_offset), _ptr(sorted_token), ctypes.byref(routed), sh,
+        _ptr(y_routed), _ptr(y_shared), _stream(stream)))
 
 
 def moe_combine(shape, u, y_routed, y_shared, pair_row, topk_gate, out, stream=None):

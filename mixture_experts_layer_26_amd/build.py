@@ -13,7 +13,7 @@ LIB = os.path.join(HERE, "libmoe.so")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
 SOURCES = ["abi.cpp", "route.hip", "dispatch.hip", "ffn_bf16.hip", "ffn_fp8.hip", "ffn_f32.hip", "combine.hip",
-           "quant.hip", "pack.hip", "ffn_bwd.hip", "bwd_misc.hip", "debug.hip"]
+           "quant.hip", "pack.hip", "ffn_bwd.hip", "bwd_misc.hip", "debug.hip", "scratch.hip"]
 
 # Packed fp32 VALU ops are disabled for all device code.
 FLAGS = ["--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-Wall",

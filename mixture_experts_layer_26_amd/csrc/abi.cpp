@@ -321,6 +321,9 @@ const char* moe_status_string(moe_status st) {
     case MOE_ERR_UNSUPPORTED: return "unsupported shape or dtype";
     case MOE_ERR_WORKSPACE: return "workspace missing or too small";
     case MOE_ERR_HIP: return "HIP runtime error";
+    case MOE_ERR_SCRATCH_LIMIT:
+      return "shape needs more scratch than moe_grouped_ffn_noalloc's fixed buffer holds "
+             "(MOE_NOALLOC_SCRATCH_BYTES; use moe_grouped_ffn with a workspace)";
   }
   return "unknown status";
 }
@@ -371,10 +374,14 @@ moe_status moe_dispatch(const moe_shape* s, const int32_t* topk_idx, int32_t* ex
                                        sorted_token, pair_row, as_stream(stream)));
 }
 
-moe_status moe_grouped_ffn(const moe_shape* s, const void* u, const int32_t* expert_offset,
-                           const int32_t* sorted_token, const moe_expert_set* routed,
-                           const moe_expert_set* shared, void* y_routed, float* y_shared, void* ws,
-                           size_t ws_bytes, void* stream) {
+}  // extern "C"
+
+namespace {
+
+// Host-side checks of moe_grouped_ffn's arguments other than the workspace.
+moe_status grouped_ffn_check(const moe_shape* s, const void* u, const int32_t* expert_offset,
+                             const int32_t* sorted_token, const moe_expert_set* routed,
+                             const moe_expert_set* shared, const void* y_routed, const float* y_shared) {
   if (!valid_shape(s) || !ok_t(s, u) || !expert_offset || !ok_t(s, sorted_token) || !routed || !ok_t(s, y_routed))
     return MOE_ERR_INVALID_ARG;
   if (!routed->w1 || !routed->w3 || !routed->w2) return MOE_ERR_INVALID_ARG;
@@ -390,9 +397,18 @@ moe_status moe_grouped_ffn(const moe_shape* s, const void* u, const int32_t* exp
   if (b_tiled && s->ffn == MOE_F32) return MOE_ERR_UNSUPPORTED;
   if (!tiled_shape(s)) return MOE_ERR_UNSUPPORTED;
   if (s->ffn == MOE_BF16 && !bf16_offsets_fit(s)) return MOE_ERR_UNSUPPORTED;
-  if (s->T == 0) return MOE_OK;
+  return MOE_OK;
+}
+
+// The grouped FFN on a checked shape with T > 0 and a workspace of at least
+// ffn_workspace(s).total bytes.
+moe_status grouped_ffn_run(const moe_shape* s, const void* u, const int32_t* expert_offset,
+                           const int32_t* sorted_token, const moe_expert_set* routed,
+                           const moe_expert_set* shared, void* y_routed, float* y_shared, void* ws,
+                           void* stream) {
   const FfnWorkspace w = ffn_workspace(s);
-  if (!ws || ws_bytes < w.total) return MOE_ERR_WORKSPACE;
+  const bool fp8 = s->ffn == MOE_FP8_E4M3;
+  const int b_tiled = routed->layout == MOE_LAYOUT_TILED ? 1 : 0;
   hipStream_t st = as_stream(stream);
   unsigned char* wsb = static_cast<unsigned char*>(ws);
   const int64_t P = s->T * s->top_k;
@@ -482,6 +498,33 @@ moe_status moe_grouped_ffn(const moe_shape* s, const void* u, const int32_t* exp
   g2.slot_stride = sc.stride2;
   (void)P;
   return from_hip(moe::launch_grouped_gemm_bf16(g2, false, grid, st));
+}
+
+}  // namespace
+
+extern "C" {
+
+moe_status moe_grouped_ffn(const moe_shape* s, const void* u, const int32_t* expert_offset,
+                           const int32_t* sorted_token, const moe_expert_set* routed,
+                           const moe_expert_set* shared, void* y_routed, float* y_shared, void* ws,
+                           size_t ws_bytes, void* stream) {
+  if (moe_status c = grouped_ffn_check(s, u, expert_offset, sorted_token, routed, shared, y_routed, y_shared))
+    return c;
+  if (s->T == 0) return MOE_OK;
+  if (!ws || ws_bytes < ffn_workspace(s).total) return MOE_ERR_WORKSPACE;
+  return grouped_ffn_run(s, u, expert_offset, sorted_token, routed, shared, y_routed, y_shared, ws, stream);
+}
+
+moe_status moe_grouped_ffn_noalloc(const moe_shape* s, const void* u, const int32_t* expert_offset,
+                                   const int32_t* sorted_token, const moe_expert_set* routed,
+                                   const moe_expert_set* shared, void* y_routed, float* y_shared, void* stream) {
+  if (moe_status c = grouped_ffn_check(s, u, expert_offset, sorted_token, routed, shared, y_routed, y_shared))
+    return c;
+  if (s->T == 0) return MOE_OK;
+  if (ffn_workspace(s).total > moe::kNoAllocScratchBytes) return MOE_ERR_SCRATCH_LIMIT;
+  void* scratch = nullptr;  // this device's copy of the library's fixed scratch array
+  if (moe::noalloc_scratch(&scratch) != hipSuccess) return MOE_ERR_HIP;
+  return grouped_ffn_run(s, u, expert_offset, sorted_token, routed, shared, y_routed, y_shared, scratch, stream);
 }
 
 moe_status moe_combine(const moe_shape* s, const void* u, const void* y_routed,

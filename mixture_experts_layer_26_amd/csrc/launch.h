@@ -50,6 +50,11 @@ inline int64_t sched_ints(int64_t max_tiles, int grid) { return 1 + kGangs * sch
 
 hipError_t launch_zero_i32(int* p, int n, hipStream_t stream);
 
+// The fixed scratch of moe_grouped_ffn_noalloc (scratch.hip): its size, and its device
+// address on the current device (looked up once per device, then cached).
+constexpr size_t kNoAllocScratchBytes = size_t(64) << 20;
+hipError_t noalloc_scratch(void** ptr);
+
 // FP8 grouped GEMM: the codes travel in the GemmArgs pointers (as bytes), the fp32
 // scales here. A-row scales: one per row per 128-wide K block, stored K-block-major
 // (the scale of row r in K block kb at [kb * ld + r]) so that one K-step's scales of a

@@ -23,7 +23,7 @@ def test_exports_every_declared_symbol():
     assert {"moe_route", "moe_dispatch", "moe_grouped_ffn", "moe_combine", "moe_bias_update"} <= set(names)
     for n in names:
         assert hasattr(lib, n), n
-    assert lib.moe_abi_version() == abi.ABI_VERSION == 4
+    assert lib.moe_abi_version() == abi.ABI_VERSION == 5
     assert lib.moe_status_string(0) == b"ok"
 
 
@@ -242,3 +242,29 @@ def test_bf16_ffn_rejects_operands_past_32_bit_offsets(kw, fits):
     ok = _shape(**dict(base, **fits))
     assert lib.moe_grouped_ffn(ctypes.byref(ok), FAKE, FAKE, FAKE, ctypes.byref(es), ctypes.byref(es), FAKE, FAKE,
                                FAKE, 0, None) == abi.MOE_ERR_WORKSPACE
+
+
+def test_noalloc_ffn_checks_on_the_host():
+    """moe_grouped_ffn_noalloc takes moe_grouped_ffn's arguments without a workspace: the same
+    argument checks, an empty batch does nothing, and a shape whose workspace exceeds the fixed
+    scratch is refused with MOE_ERR_SCRATCH_LIMIT before any HIP call."""
+    lib = abi.load()
+    es = abi.make_expert_set(FAKE, FAKE, FAKE, layout=abi.MOE_LAYOUT_TILED)
+    call = lambda s: lib.moe_grouped_ffn_noalloc(ctypes.byref(s), FAKE, FAKE, FAKE, ctypes.byref(es),
+                                                 ctypes.byref(es), FAKE, FAKE, None)
+    v3 = dict(d=7168, n_routed=256, top_k=8, n_shared=1, d_ff=2048, act="bf16", ffn="bf16")
+    big = _shape(T=8192, **v3)
+    assert abi.moe_workspace_bytes(big, abi.MOE_CALL_GROUPED_FFN) > abi.MOE_NOALLOC_SCRATCH_BYTES
+    assert call(big) == abi.MOE_ERR_SCRATCH_LIMIT
+    assert b"scratch" in lib.moe_status_string(abi.MOE_ERR_SCRATCH_LIMIT)
+    # the largest V3 batch that fits, and the next one
+    fit = max(T for T in range(1, 4096) if abi.moe_workspace_bytes(_shape(T=T, **v3), abi.MOE_CALL_GROUPED_FFN)
+              <= abi.MOE_NOALLOC_SCRATCH_BYTES)
+    assert 1700 <= fit < 1900
+    assert call(_shape(T=fit + 1, **v3)) == abi.MOE_ERR_SCRATCH_LIMIT
+    assert call(_shape(T=0, **v3)) == abi.MOE_OK
+    assert call(_shape(T=16, d=100, **{k: v for k, v in v3.items() if k != "d"})) == abi.MOE_ERR_INVALID_ARG
+    assert lib.moe_grouped_ffn_noalloc(ctypes.byref(_shape(T=16, **v3)), FAKE, FAKE, FAKE, None, None, FAKE,
+                                       FAKE, None) == abi.MOE_ERR_INVALID_ARG
+    fp8 = dict(v3, ffn="fp8")  # FP8 needs its block scales
+    assert call(_shape(T=16, **fp8)) == abi.MOE_ERR_INVALID_ARG
