@@ -162,9 +162,10 @@ moe_status moe_dispatch(const moe_shape* shape, const int32_t* topk_idx, int32_t
  *                 and the GEMMs' tile-scheduling state
  * H is rounded to the GEMM operand type (fp32, bf16; FP8: fp32 then 1x128 E4M3).
  * routed and shared must have the same layout; TILED needs ffn BF16 or FP8 (else
- * MOE_ERR_UNSUPPORTED). Both layouts give bit-identical results. With ffn BF16, u
- * (T*d), H (T*K*d_ff routed, T*N_s*d_ff shared) and one expert's weights (d_ff*d) must
- * each hold fewer than 2^32 elements, else MOE_ERR_UNSUPPORTED. */
+ * MOE_ERR_UNSUPPORTED). Both layouts give bit-identical results. With ffn BF16 or FP8, u
+ * must take fewer than 2^32 bytes in the GEMM operand type (bf16: T*d below 2^31, at
+ * d = 7168 up to 299,593 tokens; FP8: T*d below 2^32) and d, d_ff and N_s*d_ff must each
+ * be below 2^22, else MOE_ERR_UNSUPPORTED. */
 moe_status moe_grouped_ffn(const moe_shape* shape, const void* u, const int32_t* expert_offset,
                            const int32_t* sorted_token, const moe_expert_set* routed,
                            const moe_expert_set* shared, void* y_routed, float* y_shared,

@@ -55,13 +55,17 @@ bool tiled_shape(const moe_shape* s) {
   return s->d % 256 == 0 && s->d_ff % 128 == 0;
 }
 
-// The bf16 grouped GEMMs hold each lane's row offsets within an operand as 32-bit element
-// offsets: u [T, d], H [T*K, d_ff] and [T, N_s*d_ff], and one expert's weights [d_ff, d]
-// must each have fewer than 2^32 elements.
-bool bf16_offsets_fit(const moe_shape* s) {
-  const int64_t lim = 1LL << 32;
-  return s->T * s->d < lim && s->T * s->top_k * s->d_ff < lim && s->T * s->n_shared * s->d_ff < lim &&
-         static_cast<int64_t>(s->d) * s->d_ff < lim;
+// The bf16 and FP8 grouped GEMMs address each loaded row with a wave-uniform 64-bit base
+// and a 32-bit byte offset. The gathered rows of u (bf16: u itself; FP8: its 1x128 codes)
+// are offsets from the operand's start, so it must hold fewer than 2^32 bytes (bf16: T*d
+// below 2^31; FP8: below 2^32); every other offset stays within one tile's rows (at most
+// 320 rows of d, d_ff or N_s * d_ff elements, or 256 weight rows), which row lengths below
+// 2^22 elements keep under 2^32 bytes.
+bool gemm_offsets_fit(const moe_shape* s) {
+  const int64_t row_lim = 1LL << 22;
+  const int64_t elem = s->ffn == MOE_FP8_E4M3 ? 1 : 2;
+  return s->T * s->d * elem < (1LL << 32) && s->d < row_lim && s->d_ff < row_lim &&
+         static_cast<int64_t>(s->n_shared) * s->d_ff < row_lim;
 }
 
 size_t act_bytes(int dt) { return dt == MOE_F32 ? 4 : 2; }
@@ -396,7 +400,7 @@ moe_status grouped_ffn_check(const moe_shape* s, const void* u, const int32_t* e
   const int b_tiled = routed->layout == MOE_LAYOUT_TILED ? 1 : 0;
   if (b_tiled && s->ffn == MOE_F32) return MOE_ERR_UNSUPPORTED;
   if (!tiled_shape(s)) return MOE_ERR_UNSUPPORTED;
-  if (s->ffn == MOE_BF16 && !bf16_offsets_fit(s)) return MOE_ERR_UNSUPPORTED;
+  if (s->ffn != MOE_F32 && !gemm_offsets_fit(s)) return MOE_ERR_UNSUPPORTED;
   return MOE_OK;
 }
 

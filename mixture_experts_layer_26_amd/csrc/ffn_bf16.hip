@@ -8,22 +8,22 @@
 // through sorted_token) and the shared experts (rows = all tokens).
 //
 // Kernel shape: a persistent grid of one 8-wave workgroup per CU walks the device-built
-// tile list in gangs (gemm_common.h). A phase-1 tile is up to 320 rows x 256 weight rows
-// (128 gate + 128 up columns): at V3 prefill the routed experts hold about 185..345 rows,
-// so with 320-row tiles most experts are one row block and their weights pass through the
-// L1 once, where 256-row tiles split about 120 of the 256 experts in two. K advances in
-// steps of 64 (128-byte rows) through two LDS stages filled by direct global-to-LDS loads (global_load_lds_dwordx4): no staging
-// registers and no LDS store instructions; a stage is loaded one step before it is
-// computed. One barrier per step, before its last 16-wide sub-step, so each wave reads
-// the next step's first fragments while the MFMAs of the current one run. In phase 1
-// every wave computes a 160 x 64 block with v_mfma_f32_32x32x16_bf16 (10 MFMA tiles):
-// wave (g, wn) owns rows 160g.. of the tile and gate rows 32wn.. with the matching up
-// rows (so SiLU(gate) * up is formed in registers). Phase 2 keeps 256-row tiles (waves
-// of 128 x 64, 8 MFMA tiles): at 320 rows its kernel, which also carries the shared
-// experts' segmented K range and fp32 epilogue, spilled registers inside the K loop. The K loop is specialised on the
-// number of 32-row blocks of a wave that hold rows, so row blocks past an expert's
-// count cost no MFMA work. Weights are read row-major or in the tiled layout of
-// pack.hip.
+// tile list in gangs (gemm_common.h). A tile is up to 320 rows x 256 weight rows (phase 1:
+// 128 gate + 128 up columns; phase 2: 256 output columns): at V3 prefill the routed
+// experts hold about 185..345 rows, so with 320-row tiles most experts are one row block
+// and their weights pass through the L1 once, where 256-row tiles split about 120 of the
+// 256 experts in two. K advances in steps of 64 (128-byte rows) through two LDS stages
+// filled by direct global-to-LDS loads (global_load_lds_dwordx4): no staging registers
+// and no LDS store instructions; a stage is loaded one step before it is computed. One
+// barrier per step, before its last 16-wide sub-step, so each wave reads the next step's
+// first fragments while the MFMAs of the current one run. Every wave computes a 160 x 64
+// block with v_mfma_f32_32x32x16_bf16 (10 MFMA tiles): wave (g, wn) owns rows 160g.. of
+// the tile; in phase 1 gate rows 32wn.. with the matching up rows (so SiLU(gate) * up is
+// formed in registers), in phase 2 output columns 64wn... The load addresses keep their
+// wave-uniform part in SGPRs (one VGPR per loaded row), which leaves the K loops free of
+// register spills at 320 rows in both phases. The K loop is specialised on the number of
+// 32-row blocks of a wave that hold rows, so row blocks past an expert's count cost no
+// MFMA work. Weights are read row-major or in the tiled layout of pack.hip.
 #include "gemm_common.h"
 #include "launch.h"
 
@@ -41,8 +41,7 @@ constexpr int kSubs = BK / 16;          // MFMA sub-steps per K-step
 constexpr int kDmaB = BNB / 64;         // B loads (global_load_lds of 8 rows) per wave per step
 
 // Tile geometry for TRW tile rows: two wave groups of TRW / 2 rows, each wave a
-// TRW / 2 x 64 block of 32 x 32 MFMA tiles. Phase 1 uses 320 rows, phase 2 256 (at 320 the
-// down-projection spilled registers inside its K loop).
+// TRW / 2 x 64 block of 32 x 32 MFMA tiles. Both phases use 320 rows.
 template <int TRW>
 struct Geo {
   static constexpr int GR = TRW / 2;      // rows per wave group
@@ -50,7 +49,7 @@ struct Geo {
   static constexpr int kOpA = TRW * kRow; // the A rows of one stage
   static constexpr int kDmaA = TRW / 64;  // A loads per wave per step
 };
-constexpr int kTR1 = 320, kTR2 = 256;     // tile rows of phase 1 and phase 2
+constexpr int kTR1 = 320, kTR2 = 320;     // tile rows of phase 1 and phase 2
 constexpr int kStageSz = Geo<kTR1>::kOpA + kOpB;  // 72 KB
 
 // The two stages.
@@ -65,31 +64,44 @@ __device__ __forceinline__ unsigned char* stage() {
 
 typedef __attribute__((address_space(3))) unsigned char* lds_ptr;
 
-// One global_load_lds_dwordx4: lane i copies the 16 bytes at gptr (its own address) to
-// LDS byte lds + 16 i. M0 holds the LDS address (one wait state after writing it). The
+// One global_load_lds_dwordx4 in its SGPR-base form: lane i copies the 16 bytes at
+// sbase + voff (sbase wave-uniform in SGPRs, voff the lane's 32-bit byte offset) to LDS
+// byte lds + 16 i. M0 holds the LDS address (one wait state after writing it). The
 // instruction is written out rather than taken from the builtin so that the compiler,
 // which cannot follow which stage a load lands in across loop iterations, adds no wait
 // of its own before the LDS reads; the waits are the explicit ones in step_barrier.
-// M0 is declared clobbered, so the compiler keeps no value of its own in M0 across the
-// statement (clang warns that M0 is a reserved register; the clobber is what tells its
-// M0-initialisation passes that the statement writes it).
+// Keeping the wave-uniform part of every address in SGPRs leaves one VGPR per loaded row
+// (a 64-bit per-lane address would take two, plus the temporaries of its add), and a
+// K-step moves the base with scalar adds. M0 is declared clobbered, so the compiler keeps
+// no value of its own in M0 across the statement (clang warns that M0 is a reserved
+// register; the clobber is what tells its M0-initialisation passes that the statement
+// writes it).
 #pragma clang diagnostic push
 #pragma clang diagnostic ignored "-Winline-asm"
-__device__ __forceinline__ void dma16(const void* gptr, const unsigned char* lds) {
+__device__ __forceinline__ void dma16(uint32_t voff, const unsigned char* sbase, const unsigned char* lds) {
   const uint32_t m0 = static_cast<uint32_t>(reinterpret_cast<uintptr_t>((lds_ptr)(lds)));
-  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(gptr), "s"(m0)
+  asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1" ::"v"(voff), "s"(sbase), "s"(m0)
                : "memory", "m0");
 }
 #pragma clang diagnostic pop
 
+// A wave-uniform pointer made explicit (both halves read from the first lane), so that it
+// can sit in SGPRs as the base of dma16.
+__device__ __forceinline__ const unsigned char* uniform_ptr(const void* p) {
+  const uint64_t v = reinterpret_cast<uint64_t>(p);
+  const uint64_t lo = static_cast<uint32_t>(__builtin_amdgcn_readfirstlane(static_cast<uint32_t>(v)));
+  const uint64_t hi = static_cast<uint32_t>(__builtin_amdgcn_readfirstlane(static_cast<uint32_t>(v >> 32)));
+  return reinterpret_cast<const unsigned char*>((hi << 32) | lo);
+}
+
 template <int TRW>
 struct TileCtx {
-  bool load_a;                // this wave's A rows hold at least one of the tile's rows
-  const uint16_t* abase;      // wave-uniform base of the A operand
-  uint32_t a[Geo<TRW>::kDmaA];  // this lane's A rows: element offsets from abase (chunk included)
-  const uint16_t* bbase;      // wave-uniform base of this wave's B rows
-  uint32_t b[kDmaB];          // this lane's four B rows: element offsets from bbase (chunk included)
-  int64_t seg_stride;    // phase 2 shared: W2 stride per K segment, else 0
+  bool load_a;                  // this wave's A rows hold at least one of the tile's rows
+  const unsigned char* abase;   // wave-uniform: K-step 0 of the A rows
+  uint32_t a[Geo<TRW>::kDmaA];  // this lane's A rows: byte offsets from abase (chunk included)
+  const unsigned char* bbase;   // wave-uniform: K-step 0 of this wave's B rows
+  uint32_t b[kDmaB];            // this lane's four B rows: byte offsets from bbase (chunk included)
+  int64_t seg_stride;    // phase 2 shared: W2 stride per K segment (elements), else 0
   int bstep;             // elements from one K-step of a B row to the next
   int kseg_steps;
   uint32_t kseg_inv;
@@ -98,22 +110,21 @@ struct TileCtx {
 
 // Direct loads of K-step kt into stage ST: wave w fills A rows 8 kDmaA w.. (kDmaA 8-row
 // instructions: 40 rows in phase 1, 32 in phase 2) and B rows 32w..32w+31 (four); lane i
-// writes row 8j + i/8 of its
-// instruction's block, 16-byte slot i%8, whose global chunk was chosen when the pointers
-// were made. A wave whose A rows all lie past the tile's rows loads no A (those LDS rows
-// feed only outputs that are not stored).
+// writes row 8j + i/8 of its instruction's block, 16-byte slot i%8, whose global chunk
+// was chosen when the offsets were made. A wave whose A rows all lie past the tile's rows
+// loads no A (those LDS rows feed only outputs that are not stored).
 template <int ST, int TRW>
 __device__ __forceinline__ void dma_step(const TileCtx<TRW>& c, int kt, int wave) {
   constexpr int kDmaA = Geo<TRW>::kDmaA, kOpA = Geo<TRW>::kOpA;
   unsigned char* st = stage<ST>();
-  const int64_t aoff = static_cast<int64_t>(kt) * BK;
-  const int64_t boff = b_offset(kt, c.kseg_steps, c.kseg_inv, c.seg_stride, c.bstep);
+  const unsigned char* ak = c.abase + static_cast<int64_t>(kt) * (BK * 2);
+  const unsigned char* bk = c.bbase + 2 * b_offset(kt, c.kseg_steps, c.kseg_inv, c.seg_stride, c.bstep);
   if (c.load_a) {
 #pragma unroll
-    for (int j = 0; j < kDmaA; ++j) dma16(c.abase + (aoff + c.a[j]), st + (8 * kDmaA * wave + 8 * j) * kRow);
+    for (int j = 0; j < kDmaA; ++j) dma16(c.a[j], ak, st + (8 * kDmaA * wave + 8 * j) * kRow);
   }
 #pragma unroll
-  for (int j = 0; j < kDmaB; ++j) dma16(c.bbase + (boff + c.b[j]), st + kOpA + (8 * kDmaB * wave + 8 * j) * kRow);
+  for (int j = 0; j < kDmaB; ++j) dma16(c.b[j], bk, st + kOpA + (8 * kDmaB * wave + 8 * j) * kRow);
 }
 
 // Fragments of one 16-wide sub-step of stage ST for a wave holding NMB live 32-row
@@ -253,20 +264,26 @@ __global__ __launch_bounds__(kThreads) void grouped_gemm_bf16(GemmArgs args) {
     TileCtx<TR> c;
     // this lane's load rows: 8*kDmaA*wave + 8j + lane/8 of the tile's A rows and 32*wave + 8j +
     // lane/8 of its B rows, slot lane%8, holding global chunk slot ^ ((row/2)%8) (the
-    // swizzle of swz)
+    // swizzle of swz). Offsets are in bytes from a wave-uniform base: the gathered rows of
+    // phase 1 from u itself (moe_grouped_ffn refuses u of 2^31 elements or more, so they fit
+    // 32 bits), every other A operand from the tile's first row, B from the tile's weights.
     const int64_t eoff = static_cast<int64_t>(routed ? t.group : sg) * args.b_expert_stride;
     c.load_a = __builtin_amdgcn_readfirstlane(8 * kDmaA * wave < t.rows ? 1 : 0) != 0;
-    // element offsets fit 32 bits: moe_grouped_ffn rejects bf16 operands of 2^32 elements or more
-    c.abase = routed ? args.a_routed : args.a_shared;
+    const bool gathered = routed && args.gather != nullptr;
+    const int64_t lda = routed ? args.lda_routed : args.lda_shared;
+    {
+      const uint16_t* a0 = routed ? args.a_routed : args.a_shared;
+      const int64_t first = gathered ? 0 : (routed ? row_base : 0) + t.m0;  // row of A at offset 0
+      c.abase = uniform_ptr(a0 + first * lda);
+    }
 #pragma unroll
     for (int j = 0; j < kDmaA; ++j) {
       const int r = 8 * kDmaA * wave + 8 * j + lane / 8;
       const int chunk = (lane % 8) ^ ((r >> 1) & 7);
       // rows past the tile's valid rows repeat its last one
       const int ra = r < t.rows ? r : t.rows - 1;
-      const int64_t m = t.m0 + ra;
-      const int64_t src = routed ? (args.gather ? args.gather[row_base + m] : (row_base + m)) : m;
-      c.a[j] = static_cast<uint32_t>(src * (routed ? args.lda_routed : args.lda_shared) + chunk * 8);
+      const int64_t row = gathered ? args.gather[row_base + t.m0 + ra] : ra;
+      c.a[j] = static_cast<uint32_t>(2 * (row * lda + chunk * 8));
     }
     {
       // B rows 32*wave..: in phase 1 waves 0..3 hold gate rows and 4..7 up rows, so the
@@ -276,13 +293,13 @@ __global__ __launch_bounds__(kThreads) void grouped_gemm_bf16(GemmArgs args) {
                                          : (routed ? args.b1_routed : args.b1_shared)) + eoff
                                    : (routed ? args.b1_routed + eoff : args.b1_shared);
       constexpr int R = GATED ? 128 : 256;  // tiled layout: [E][N/R][K/64][R][64]
-      c.bbase = args.b_tiled ? base + (t.n0 / R) * (args.ldb / BK) * (R * BK) : base;
+      c.bbase = uniform_ptr(args.b_tiled ? base + (t.n0 / R) * (args.ldb / BK) * (R * BK) : base + t.n0 * args.ldb);
 #pragma unroll
       for (int j = 0; j < kDmaB; ++j) {
         const int r = 8 * kDmaB * wave + 8 * j + lane / 8;
         const int chunk = (lane % 8) ^ ((r >> 1) & 7);
-        const int64_t nrow = t.n0 + (GATED ? (r & 127) : r);
-        c.b[j] = static_cast<uint32_t>(args.b_tiled ? (nrow - t.n0) * BK + chunk * 8 : nrow * args.ldb + chunk * 8);
+        const int64_t nrow = GATED ? (r & 127) : r;  // weight row within the tile
+        c.b[j] = static_cast<uint32_t>(2 * (args.b_tiled ? nrow * BK + chunk * 8 : nrow * args.ldb + chunk * 8));
       }
     }
     c.seg_stride = (!routed && !GATED) ? args.b_expert_stride : 0;
@@ -327,7 +344,7 @@ __global__ __launch_bounds__(kThreads) void grouped_gemm_bf16(GemmArgs args) {
       // bf16 outputs go through LDS (the stages are free once the K loop is done): group
       // g writes its rows as a [rows][W] bf16 tile into stage g, then its 256 threads
       // store whole rows with 16-byte stores, in passes of as many row blocks as a stage
-      // holds (one pass in both phases: 160 rows of 256 B, 128 rows of 512 B). Rows whose
+      // holds (phase 1: one pass of 160 rows of 256 B; phase 2: 128 + 32 rows of 512 B). Rows whose
       // bit 2 is set have their 64-byte halves swapped, so
       // the two half-waves' 2-byte writes (rows r and r+4) fall in different banks.
       constexpr int W = GATED ? BNB / 2 : BNB;  // output columns of the tile

@@ -60,45 +60,59 @@ __device__ __forceinline__ scale_ptr uniform_scales(const float* p) {
   return (scale_ptr)((hi << 32) | lo);
 }
 
-// One global_load_lds_dwordx4: lane i copies the 16 bytes at gptr (its own address) to
-// LDS byte base + OFF + 16 i. M0 holds the LDS address (one wait state after writing
-// it). The instruction is written out rather than taken from the builtin so that the
-// compiler adds no wait of its own before the LDS reads; the waits are the explicit
-// ones in step_barrier. The statement writes M0 and SCC (the add), and declares both
-// clobbered, so the compiler keeps no value of its own in either across it (clang warns
-// that M0 is a reserved register; the clobber is what tells its M0-initialisation passes
-// that the statement writes it).
+// One global_load_lds_dwordx4 in its SGPR-base form: lane i copies the 16 bytes at
+// sbase + voff (sbase wave-uniform in SGPRs, voff the lane's 32-bit byte offset) to LDS
+// byte lbase + OFF + 16 i. M0 holds the LDS address (one wait state after writing it).
+// The instruction is written out rather than taken from the builtin so that the compiler
+// adds no wait of its own before the LDS reads; the waits are the explicit ones in
+// step_barrier. Keeping the wave-uniform part of every address in SGPRs leaves one VGPR
+// per loaded row, and a K-step moves the bases with scalar adds. The statement writes M0
+// and SCC (the add), and declares both clobbered, so the compiler keeps no value of its
+// own in either across it (clang warns that M0 is a reserved register; the clobber is
+// what tells its M0-initialisation passes that the statement writes it).
 #pragma clang diagnostic push
 #pragma clang diagnostic ignored "-Winline-asm"
 template <int OFF>
-__device__ __forceinline__ void dma16(const void* gptr, uint32_t base) {
-  asm volatile("s_add_u32 m0, %1, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(gptr), "s"(base), "n"(OFF)
+__device__ __forceinline__ void dma16(uint32_t voff, const unsigned char* sbase, uint32_t lbase) {
+  asm volatile("s_add_u32 m0, %2, %3\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1" ::"v"(voff), "s"(sbase),
+               "s"(lbase), "n"(OFF)
                : "memory", "m0", "scc");
 }
 
-// The same with 4 bytes per lane (lane i writes LDS byte base + OFF + 4 i).
+// The same with 4 bytes per lane (lane i writes LDS byte lbase + OFF + 4 i).
 template <int OFF>
-__device__ __forceinline__ void dma4(const void* gptr, uint32_t base) {
-  asm volatile("s_add_u32 m0, %1, %2\n\ts_nop 0\n\tglobal_load_lds_dword %0, off" ::"v"(gptr), "s"(base), "n"(OFF)
+__device__ __forceinline__ void dma4(uint32_t voff, const unsigned char* sbase, uint32_t lbase) {
+  asm volatile("s_add_u32 m0, %2, %3\n\ts_nop 0\n\tglobal_load_lds_dword %0, %1" ::"v"(voff), "s"(sbase),
+               "s"(lbase), "n"(OFF)
                : "memory", "m0", "scc");
 }
 #pragma clang diagnostic pop
 
+// A wave-uniform pointer made explicit (both halves read from the first lane), so that it
+// can sit in SGPRs as the base of dma16 and dma4.
+__device__ __forceinline__ const unsigned char* uniform_ptr(const void* p) {
+  const uint64_t v = reinterpret_cast<uint64_t>(p);
+  const uint64_t lo = static_cast<uint32_t>(__builtin_amdgcn_readfirstlane(static_cast<uint32_t>(v)));
+  const uint64_t hi = static_cast<uint32_t>(__builtin_amdgcn_readfirstlane(static_cast<uint32_t>(v >> 32)));
+  return reinterpret_cast<const unsigned char*>((hi << 32) | lo);
+}
+
 struct TileCtx {
-  uint32_t lds_wave;        // LDS address of this wave's rows (32 wave) in stage 0
-  uint32_t lds_scale;       // waves 0..3: LDS address of row scales 64 wave.. in stage 0
-  bool load_a;              // this wave's 32 A rows hold at least one of the tile's rows
-  bool load_scale;          // waves 0..3 load the A-row scales (one row per lane)
-  const uint8_t* a[4];      // this lane's four A rows (chunk included)
-  const uint8_t* b;         // this lane's first B row (chunk included); row j: + 8 j ldb,
-  int64_t ldb8;             //   and + odd_chunk for odd j (8 rows on, the swizzle term
-  int odd_chunk;            //   (row/2)%8 differs by 4: the chunk index flips bit 2)
-  const float* sa_row;      // threads 0..255: scale of the tile row LDS slot tid holds, K block 0
-  int64_t sa_ld;            //   and the distance from one K block to the next
-  scale_ptr sb[2];          // this wave's two B-scale rows (gate/up, or the wave's block)
-  int64_t seg_stride;       // phase 2 shared: W2 stride per K segment, else 0
-  int bstep;                // bytes from one K-step of a B row to the next
-  int64_t sb_seg_stride;    // same for the W2 scales
+  uint32_t lds_wave;          // LDS address of this wave's rows (32 wave) in stage 0
+  uint32_t lds_scale;         // waves 0..3: LDS address of row scales 64 wave.. in stage 0
+  bool load_a;                // this wave's 32 A rows hold at least one of the tile's rows
+  bool load_scale;            // waves 0..3 load the A-row scales (one row per lane)
+  const unsigned char* abase; // wave-uniform: K-step 0 of the A rows
+  uint32_t a[4];              // this lane's four A rows: byte offsets from abase (chunk included)
+  const unsigned char* bbase; // wave-uniform: K-step 0 of this wave's B rows
+  uint32_t b[4];              // this lane's four B rows: byte offsets from bbase (chunk included)
+  const unsigned char* sbase; // wave-uniform: K block 0 of the A-row scales
+  uint32_t s;                 // threads 0..255: byte offset of the scale of the row LDS slot tid holds
+  int64_t sa_step;            // bytes from one K block of the row scales to the next
+  scale_ptr sb[2];            // this wave's two B-scale rows (gate/up, or the wave's block)
+  int64_t seg_stride;         // phase 2 shared: W2 stride per K segment, else 0
+  int bstep;                  // bytes from one K-step of a B row to the next
+  int64_t sb_seg_stride;      // same for the W2 scales
   int kseg_steps;
   uint32_t kseg_inv;
   int nk;
@@ -106,24 +120,24 @@ struct TileCtx {
 
 // Direct loads of K-step kt into stage ST: wave w fills A rows and B rows 32w..32w+31,
 // four 8-row instructions each; lane i writes row 8j + i/8, 16-byte slot i%8, whose
-// global chunk was chosen when the pointers were made. A wave whose A rows all lie past
+// global chunk was chosen when the offsets were made. A wave whose A rows all lie past
 // the tile's rows loads no A.
 template <int ST>
 __device__ __forceinline__ void dma_step(const TileCtx& c, int kt) {
   if (kt >= c.nk) return;  // past the last step (a K loop of one step)
-  const int64_t aoff = static_cast<int64_t>(kt) * BK;
-  const int64_t boff = b_offset(kt, c.kseg_steps, c.kseg_inv, c.seg_stride, c.bstep);
+  const unsigned char* ak = c.abase + static_cast<int64_t>(kt) * BK;
+  const unsigned char* bk = c.bbase + b_offset(kt, c.kseg_steps, c.kseg_inv, c.seg_stride, c.bstep);
   if (c.load_a) {
-    dma16<ST * kStageSize + 0 * 8 * BK>(c.a[0] + aoff, c.lds_wave);
-    dma16<ST * kStageSize + 1 * 8 * BK>(c.a[1] + aoff, c.lds_wave);
-    dma16<ST * kStageSize + 2 * 8 * BK>(c.a[2] + aoff, c.lds_wave);
-    dma16<ST * kStageSize + 3 * 8 * BK>(c.a[3] + aoff, c.lds_wave);
+    dma16<ST * kStageSize + 0 * 8 * BK>(c.a[0], ak, c.lds_wave);
+    dma16<ST * kStageSize + 1 * 8 * BK>(c.a[1], ak, c.lds_wave);
+    dma16<ST * kStageSize + 2 * 8 * BK>(c.a[2], ak, c.lds_wave);
+    dma16<ST * kStageSize + 3 * 8 * BK>(c.a[3], ak, c.lds_wave);
   }
-  dma16<ST * kStageSize + kOperand + 0 * 8 * BK>(c.b + (boff + 0 * c.ldb8), c.lds_wave);
-  dma16<ST * kStageSize + kOperand + 1 * 8 * BK>(c.b + (boff + 1 * c.ldb8 + c.odd_chunk), c.lds_wave);
-  dma16<ST * kStageSize + kOperand + 2 * 8 * BK>(c.b + (boff + 2 * c.ldb8), c.lds_wave);
-  dma16<ST * kStageSize + kOperand + 3 * 8 * BK>(c.b + (boff + 3 * c.ldb8 + c.odd_chunk), c.lds_wave);
-  if (c.load_scale) dma4<ST * kStageSize>(c.sa_row + kt * c.sa_ld, c.lds_scale);
+  dma16<ST * kStageSize + kOperand + 0 * 8 * BK>(c.b[0], bk, c.lds_wave);
+  dma16<ST * kStageSize + kOperand + 1 * 8 * BK>(c.b[1], bk, c.lds_wave);
+  dma16<ST * kStageSize + kOperand + 2 * 8 * BK>(c.b[2], bk, c.lds_wave);
+  dma16<ST * kStageSize + kOperand + 3 * 8 * BK>(c.b[3], bk, c.lds_wave);
+  if (c.load_scale) dma4<ST * kStageSize>(c.s, c.sbase + kt * c.sa_step, c.lds_scale);
 }
 
 // A 16 x 128 fp8 fragment (rows row.., this lane's 32 bytes of K) from a swizzled stage.
@@ -318,12 +332,20 @@ __global__ __launch_bounds__(kThreads) void grouped_gemm_fp8(Fp8Args fa) {
     const int64_t row_base = routed ? args.offset[t.group] : 0;
 
     TileCtx c;
-    auto src_row = [&](int r) -> int64_t {  // A/scale row index of tile row r (clamped)
+    // Load offsets are bytes from wave-uniform bases: the gathered rows of phase 1 from the
+    // quantised u itself (T * d bytes; moe_grouped_ffn refuses FP8 shapes where that reaches
+    // 2^32), every other A operand from the tile's first row, B from the tile's weights.
+    const bool gathered = routed && args.gather != nullptr;
+    const int64_t lda = routed ? args.lda_routed : args.lda_shared;
+    auto a_row = [&](int r) -> int64_t {  // A row of tile row r (clamped), relative to abase
       if (r >= t.rows) r = t.rows - 1;
-      const int64_t m = t.m0 + r;
-      if (routed) return args.gather ? args.gather[row_base + m] : (row_base + m);
-      return m;
+      return gathered ? args.gather[row_base + t.m0 + r] : r;
     };
+    {
+      const uint8_t* a0 = routed ? a_routed : a_shared;
+      const int64_t first = gathered ? 0 : (routed ? row_base : 0) + t.m0;  // row of A at offset 0
+      c.abase = uniform_ptr(a0 + first * lda);
+    }
     const int64_t eidx = routed ? t.group : sg;
     const int64_t eoff = eidx * args.b_expert_stride;
     const uint8_t* b1r = reinterpret_cast<const uint8_t*>(args.b1_routed);
@@ -344,30 +366,23 @@ __global__ __launch_bounds__(kThreads) void grouped_gemm_fp8(Fp8Args fa) {
     for (int j = 0; j < 4; ++j) {
       const int r = 32 * wave + 8 * j + lane / 8;
       const int chunk = (lane % 8) ^ ((r >> 1) & 7);
-      const int64_t src = src_row(r);
-      c.a[j] = (routed ? a_routed + src * args.lda_routed : a_shared + src * args.lda_shared) + chunk * 16;
+      c.a[j] = static_cast<uint32_t>(a_row(r) * lda + chunk * 16);
     }
     {
-      const int r = 32 * wave + lane / 8;
-      const int chunk = (lane % 8) ^ ((r >> 1) & 7);
       const uint8_t* base;
-      int64_t nrow;
-      if (GATED) {  // tile rows 0..127 gate, 128..255 up (a wave's 32 rows lie in one)
-        base = (r < 128 ? (routed ? b1r : b1s) : (routed ? b3r : b3s)) + eoff;
-        nrow = t.n0 + (r & 127);
-      } else {
+      if (GATED)  // tile rows 0..127 gate, 128..255 up (a wave's 32 rows lie in one)
+        base = (wave < 4 ? (routed ? b1r : b1s) : (routed ? b3r : b3s)) + eoff;
+      else
         base = routed ? b1r + eoff : b1s;
-        nrow = t.n0 + r;
+      constexpr int R = GATED ? 128 : 256;  // [E][N/R][K/128][R][128]: one K-step of the tile is R contiguous rows
+      c.bbase = uniform_ptr(args.b_tiled ? base + (t.n0 / R) * (args.ldb / BK) * (R * BK) : base + t.n0 * args.ldb);
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int r = 32 * wave + 8 * j + lane / 8;
+        const int chunk = (lane % 8) ^ ((r >> 1) & 7);
+        const int64_t nrow = GATED ? (r & 127) : r;  // weight row within the tile
+        c.b[j] = static_cast<uint32_t>((args.b_tiled ? nrow * BK : nrow * args.ldb) + chunk * 16);
       }
-      if (args.b_tiled) {  // [E][N/R][K/128][R][128]: one K-step of the tile is R contiguous rows
-        constexpr int R = GATED ? 128 : 256;
-        c.b = base + (t.n0 / R) * (args.ldb / BK) * (R * BK) + static_cast<int64_t>(nrow - t.n0) * BK + chunk * 16;
-        c.ldb8 = 8 * BK;
-      } else {
-        c.b = base + nrow * args.ldb + chunk * 16;
-        c.ldb8 = 8 * args.ldb;
-      }
-      c.odd_chunk = ((chunk ^ 4) - chunk) * 16;
     }
     {  // scales are indexed by sorted row (routed) or token (shared), not by the gathered A row.
       // LDS slot 128 g + 8 c + mb holds row 128 g + 16 mb + c, so that a lane's scales of its
@@ -375,9 +390,9 @@ __global__ __launch_bounds__(kThreads) void grouped_gemm_fp8(Fp8Args fa) {
       const int slot = tid & (BM - 1);
       int r = 128 * (slot / 128) + 16 * (slot % 8) + (slot % 128) / 8;
       if (r >= t.rows) r = t.rows - 1;
-      const int64_t m = t.m0 + r;
-      c.sa_row = routed ? fa.sa_routed + row_base + m : fa.sa_shared + m;
-      c.sa_ld = routed ? fa.ldsa_routed : fa.ldsa_shared;
+      c.sbase = uniform_ptr(routed ? fa.sa_routed + row_base + t.m0 : fa.sa_shared + t.m0);
+      c.s = static_cast<uint32_t>(4 * r);
+      c.sa_step = 4 * (routed ? fa.ldsa_routed : fa.ldsa_shared);
     }
     // weight-scale rows: [expert][N/128][K/128]
     const int64_t sbe = (routed || GATED) ? eidx * fa.sb_expert_stride : 0;

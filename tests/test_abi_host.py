@@ -223,19 +223,21 @@ def test_backward_args_rejected():
 
 
 @pytest.mark.parametrize("kw,fits", [
-    (dict(T=600_000, d=7168, d_ff=256), dict(T=599_000)),                        # u: T*d
-    (dict(T=300_000, top_k=8, d=256, d_ff=2048), dict(T=262_000)),               # routed H: T*K*d_ff
-    (dict(T=1_100_000, n_shared=2, top_k=1, d=256, d_ff=2048), dict(n_shared=1)),  # shared H: T*N_s*d_ff
-    (dict(T=4, d=65536, d_ff=65536), dict(d_ff=65408))])                         # one expert: d_ff*d
+    (dict(T=299_594, d=7168, d_ff=256), dict(T=299_593)),                 # u: T*d < 2^31
+    (dict(T=4, d=1 << 22, d_ff=128), dict(d=(1 << 22) - 256)),             # row length d
+    (dict(T=4, d=256, d_ff=1 << 22), dict(d_ff=(1 << 22) - 128)),          # row length d_ff
+    (dict(T=4, n_shared=2, d=256, d_ff=1 << 21), dict(n_shared=1)),       # shared H row N_s*d_ff
+    (dict(T=599_187, d=7168, d_ff=256, ffn="fp8"), dict(T=599_186))])      # FP8 codes of u: T*d < 2^32
 def test_bf16_ffn_rejects_operands_past_32_bit_offsets(kw, fits):
-    """The bf16 grouped GEMMs keep row offsets within an operand in 32 bits: u [T, d], H
-    [T*K, d_ff] and [T, N_s*d_ff] and one expert's weights [d_ff, d] must each have fewer
-    than 2^32 elements. Larger shapes are refused on the host, before any launch; the same
-    shape just below the limit passes the check (and stops at the workspace check)."""
+    """The bf16 grouped GEMMs address loaded rows with a wave-uniform base and a 32-bit byte
+    offset: the gathered rows of u are offsets from u itself (u must have fewer than 2^31
+    elements), every other offset stays within one tile's rows (row lengths below 2^22
+    elements). Larger shapes are refused on the host, before any launch; the same shape just
+    inside the limit passes the check (and stops at the workspace check)."""
     base = dict(n_routed=16, top_k=2, n_shared=1, act="bf16", ffn="bf16")
     base.update(kw)
     lib = abi.load()
-    es = abi.make_expert_set(FAKE, FAKE, FAKE)
+    es = abi.make_expert_set(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE)  # scales are read for FP8 only
     s = _shape(**base)
     assert lib.moe_grouped_ffn(ctypes.byref(s), FAKE, FAKE, FAKE, ctypes.byref(es), ctypes.byref(es), FAKE, FAKE,
                                FAKE, 1 << 62, None) == abi.MOE_ERR_UNSUPPORTED

@@ -7,7 +7,7 @@ under random interleavings of the workgroups, on random and skewed expert loads,
 
 - every (group, row, output-column tile) is computed exactly once;
 - no tile is empty and no tile is taller than the kernel's tile height (the bf16 kernel's
-  320 rows in phase 1, 256 in phase 2; the FP8 kernel's 256 in both);
+  320 rows in both phases; the FP8 kernel's 256 in both);
 - the tile count stays within the bound the workspace is sized for (ffn_max_tiles in
   abi.cpp, counted in 256-row blocks, so it also bounds the taller tiles) and no gang
   reads past its row of slots (slot stride ceil(max/G) + 2);
@@ -93,7 +93,7 @@ def run_gangs(tiles, grid, stride, rng):
 
 
 def check(T, top_k, n_r, n_shared, d, d_ff, counts, grid, rng):
-    for phase, rb in ((1, 256), (2, 256), (1, 320)):
+    for phase, rb in ((1, 256), (2, 256), (1, 320), (2, 320)):
         ns_groups = n_shared if phase == 1 else min(n_shared, 1)
         ntn = d_ff // 128 if phase == 1 else d // 256
         rows = list(counts) + [T] * ns_groups
