@@ -10,10 +10,11 @@
 // Phase 1 writes H = SiLU(gate) * up quantised per 1 x 128 (codes + fp32 scales);
 // phase 2 writes y (bf16 routed rows, fp32 shared sum).
 //
-// The tile walk, tile claiming and LDS layout are those of the bf16 kernel, with 256 x 256
-// tiles in both phases (the bf16 down-projection's shape; its gate/up tiles are 320 rows)
-// and 128-byte rows per K-step, so one K-step is exactly one 128-wide scale block. There
-// are two stages: step s+1 is loaded while step s is computed. The MFMA is
+// The tile walk, tile claiming and LDS layout are those of the bf16 kernel, with tiles of
+// up to 320 rows x 256 weight rows in both phases (at V3 prefill most experts, 185..345
+// rows, are then one row block and their weights pass through the L1 once) and 128-byte
+// rows per K-step, so one K-step is exactly one 128-wide scale block. There are two
+// stages: step s+1 is loaded while step s is computed. The MFMA is
 // v_mfma_scale_f32_16x16x128_f8f6f4 with unit (E8M0 = 127) scales: one instruction
 // covers one scale block of a 16 x 16 output block, starting from zero, and its result
 // is folded into the accumulator with one fp32 FMA per element:
@@ -31,9 +32,24 @@ namespace {
 using namespace gemm;
 
 constexpr int BK = 128;                 // fp8 elements (bytes) per K-step = one scale block
-constexpr int kOperand = BM * BK;       // 32 KB: one operand of one stage
-constexpr int kScaleBytes = BM * 4;     // A-row scales of one stage
-constexpr int kStageSize = 2 * kOperand + kScaleBytes;
+constexpr int TR = 320;                 // tile rows (A rows per tile)
+constexpr int GR = TR / 2;              // rows per wave group
+constexpr int kRB = GR / 16;            // 16-row MFMA blocks per wave
+constexpr int kNM = GR / 32;            // 32-row blocks per wave
+constexpr int kDmaA = TR / 64;          // A loads (8 rows each) per wave per step
+constexpr int kOpA = TR * BK;           // 40 KB: the A rows of one stage
+constexpr int kOpB = BNB * BK;          // 32 KB: the B rows of one stage
+// A-row scales of one stage: slot GS g + 12 c + mb holds the scale of row GR g + 16 mb + c
+// (c = 0..15, mb = 0..kRB-1; slots 10 and 11 of each 12 are padding), so that a lane's
+// scales of its row blocks are contiguous and 16-byte aligned, and the 16 lanes that read
+// one 16-byte piece each (at a 48-byte stride) fall in 16 different 4-bank groups.
+constexpr int kScalePitch = 12;
+constexpr int GS = 16 * kScalePitch;    // scale slots per wave group
+constexpr int kScaleSlots = 2 * GS;     // 384: six 64-lane loads
+constexpr int kScaleBytes = kScaleSlots * 4;
+constexpr int kStageSize = kOpA + kOpB + kScaleBytes;
+static_assert(kRB <= kScalePitch, "a lane's row scales fit its slot run");
+static_assert(kStageSize % 16 == 0, "16-byte aligned stages");
 
 // The two stages (A rows, B rows, A-row scales), one LDS array so that every load
 // destination is a wave base plus a constant.
@@ -98,12 +114,13 @@ __device__ __forceinline__ const unsigned char* uniform_ptr(const void* p) {
 }
 
 struct TileCtx {
-  uint32_t lds_wave;          // LDS address of this wave's rows (32 wave) in stage 0
-  uint32_t lds_scale;         // waves 0..3: LDS address of row scales 64 wave.. in stage 0
-  bool load_a;                // this wave's 32 A rows hold at least one of the tile's rows
-  bool load_scale;            // waves 0..3 load the A-row scales (one row per lane)
+  uint32_t lds_a;             // LDS address of this wave's A rows (8 kDmaA wave..) in stage 0
+  uint32_t lds_b;             // LDS address of this wave's B rows (32 wave..) in stage 0
+  uint32_t lds_scale;         // waves 0..5: LDS address of scale slots 64 wave.. in stage 0
+  bool load_a;                // this wave's A rows hold at least one of the tile's rows
+  bool load_scale;            // waves 0..5 load the A-row scales (one slot per lane)
   const unsigned char* abase; // wave-uniform: K-step 0 of the A rows
-  uint32_t a[4];              // this lane's four A rows: byte offsets from abase (chunk included)
+  uint32_t a[kDmaA];          // this lane's A rows: byte offsets from abase (chunk included)
   const unsigned char* bbase; // wave-uniform: K-step 0 of this wave's B rows
   uint32_t b[4];              // this lane's four B rows: byte offsets from bbase (chunk included)
   const unsigned char* sbase; // wave-uniform: K block 0 of the A-row scales
@@ -118,25 +135,28 @@ struct TileCtx {
   int nk;
 };
 
-// Direct loads of K-step kt into stage ST: wave w fills A rows and B rows 32w..32w+31,
-// four 8-row instructions each; lane i writes row 8j + i/8, 16-byte slot i%8, whose
-// global chunk was chosen when the offsets were made. A wave whose A rows all lie past
-// the tile's rows loads no A.
+// Direct loads of K-step kt into stage ST: wave w fills A rows 8 kDmaA w.. (kDmaA 8-row
+// instructions) and B rows 32w..32w+31 (four); lane i writes row 8j + i/8 of its
+// instruction's block, 16-byte slot i%8, whose global chunk was chosen when the offsets
+// were made. A wave whose A rows all lie past the tile's rows loads no A.
+template <int ST, int J = 0>
+__device__ __forceinline__ void dma_a(const TileCtx& c, const unsigned char* ak) {
+  if constexpr (J < kDmaA) {
+    dma16<ST * kStageSize + J * 8 * BK>(c.a[J], ak, c.lds_a);
+    dma_a<ST, J + 1>(c, ak);
+  }
+}
+
 template <int ST>
 __device__ __forceinline__ void dma_step(const TileCtx& c, int kt) {
   if (kt >= c.nk) return;  // past the last step (a K loop of one step)
   const unsigned char* ak = c.abase + static_cast<int64_t>(kt) * BK;
   const unsigned char* bk = c.bbase + b_offset(kt, c.kseg_steps, c.kseg_inv, c.seg_stride, c.bstep);
-  if (c.load_a) {
-    dma16<ST * kStageSize + 0 * 8 * BK>(c.a[0], ak, c.lds_wave);
-    dma16<ST * kStageSize + 1 * 8 * BK>(c.a[1], ak, c.lds_wave);
-    dma16<ST * kStageSize + 2 * 8 * BK>(c.a[2], ak, c.lds_wave);
-    dma16<ST * kStageSize + 3 * 8 * BK>(c.a[3], ak, c.lds_wave);
-  }
-  dma16<ST * kStageSize + kOperand + 0 * 8 * BK>(c.b[0], bk, c.lds_wave);
-  dma16<ST * kStageSize + kOperand + 1 * 8 * BK>(c.b[1], bk, c.lds_wave);
-  dma16<ST * kStageSize + kOperand + 2 * 8 * BK>(c.b[2], bk, c.lds_wave);
-  dma16<ST * kStageSize + kOperand + 3 * 8 * BK>(c.b[3], bk, c.lds_wave);
+  if (c.load_a) dma_a<ST>(c, ak);
+  dma16<ST * kStageSize + 0 * 8 * BK>(c.b[0], bk, c.lds_b);  // lds_b includes the A region
+  dma16<ST * kStageSize + 1 * 8 * BK>(c.b[1], bk, c.lds_b);
+  dma16<ST * kStageSize + 2 * 8 * BK>(c.b[2], bk, c.lds_b);
+  dma16<ST * kStageSize + 3 * 8 * BK>(c.b[3], bk, c.lds_b);
   if (c.load_scale) dma4<ST * kStageSize>(c.s, c.sbase + kt * c.sa_step, c.lds_scale);
 }
 
@@ -166,24 +186,20 @@ __device__ __forceinline__ void fence() { __builtin_amdgcn_sched_barrier(0); }
 // read from LDS while block mb is computed.
 template <int ST, int NM>
 __device__ __forceinline__ void compute_step(int arow0, const int (&brow)[4], int lsa_off, const float (&sw)[2],
-                                             int lane, f32x4 (&acc)[8][4]) {
+                                             int lane, f32x4 (&acc)[kRB][4]) {
   if constexpr (NM == 0) return;
   constexpr int NMF = 8 * NM;
   const unsigned char* la = stage<ST>();
-  const unsigned char* lb = la + kOperand;
+  const unsigned char* lb = la + kOpA;
   const int q = lane / 16;
-  // this lane's row scales of blocks 0..7, contiguous in LDS (see the DMA's row order)
-  const float* lsa = reinterpret_cast<const float*>(la + 2 * kOperand) + lsa_off;
-  float sa[8];
-  {
-    const f32x4 s0 = *reinterpret_cast<const f32x4*>(lsa);
+  // this lane's row scales of blocks 0..2NM-1, contiguous in LDS (see the DMA's slot order)
+  const float* lsa = reinterpret_cast<const float*>(lb + kOpB) + lsa_off;
+  float sa[NM > 0 ? 4 * ((2 * NM + 3) / 4) : 4];
 #pragma unroll
-    for (int v = 0; v < 4; ++v) sa[v] = s0[v];
-    if constexpr (NM > 2) {
-      const f32x4 s1 = *reinterpret_cast<const f32x4*>(lsa + 4);
+  for (int p = 0; p < (2 * NM + 3) / 4; ++p) {
+    const f32x4 s4 = *reinterpret_cast<const f32x4*>(lsa + 4 * p);
 #pragma unroll
-      for (int v = 0; v < 4; ++v) sa[4 + v] = s1[v];
-    }
+    for (int v = 0; v < 4; ++v) sa[4 * p + v] = s4[v];
   }
   // weight fragments of column blocks 0, 1 first; those of blocks 2, 3 are read while
   // the first MFMA runs, which shortens the LDS burst at the start of the step
@@ -250,7 +266,7 @@ __device__ __forceinline__ void wscales(const TileCtx& c, int kt, float (&sw)[2]
 // while this one is computed.
 template <int ST, int NM, bool MORE>
 __device__ __forceinline__ void k_step(const TileCtx& c, int s, int arow0, const int (&brow)[4], int lsa_off,
-                                       int lane, float (&sw)[2], f32x4 (&acc)[8][4]) {
+                                       int lane, float (&sw)[2], f32x4 (&acc)[kRB][4]) {
   if constexpr (MORE) dma_step<(ST + 1) % 2>(c, s + 1);
   fence();
   compute_step<ST, NM>(arow0, brow, lsa_off, sw, lane, acc);
@@ -268,12 +284,12 @@ __device__ __forceinline__ void k_step(const TileCtx& c, int s, int arow0, const
 // so the rest pair up (stage 0, stage 1). On exit no load is in flight and every wave
 // is past the last read of the stages.
 template <bool GATED, int NM>
-__device__ __forceinline__ void mainloop(const TileCtx& c, f32x4 (&acc)[8][4]) {
+__device__ __forceinline__ void mainloop(const TileCtx& c, f32x4 (&acc)[kRB][4]) {
   const int tid = threadIdx.x, lane = tid % kWave;
   const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);
   const int g = wave / 4, wn = wave % 4;
-  const int arow0 = 128 * g + lane % 16;
-  const int lsa_off = 128 * g + 8 * (lane % 16);  // row scales of rows arow0 + 16 mb, mb = 0..7
+  const int arow0 = GR * g + lane % 16;
+  const int lsa_off = GS * g + kScalePitch * (lane % 16);  // row scales of rows arow0 + 16 mb
   int brow[4];
 #pragma unroll
   for (int nb = 0; nb < 4; ++nb) {
@@ -317,7 +333,7 @@ __global__ __launch_bounds__(kThreads) void grouped_gemm_fp8(Fp8Args fa) {
   const int n_r = args.n_r;
   const int bn_out = GATED ? BNB / 2 : BNB;
   const int ntn = args.N / bn_out;
-  build_tile_map(tm, args.offset, n_r, args.n_shared_groups, args.T, ntn);
+  build_tile_map<TR>(tm, args.offset, n_r, args.n_shared_groups, args.T, ntn);
   auto rows_of = [&](int grp) -> int64_t { return grp < n_r ? args.offset[grp + 1] - args.offset[grp] : args.T; };
 
   const int tid = threadIdx.x, lane = tid % kWave, wave = tid / kWave;
@@ -352,19 +368,21 @@ __global__ __launch_bounds__(kThreads) void grouped_gemm_fp8(Fp8Args fa) {
     const uint8_t* b3r = reinterpret_cast<const uint8_t*>(args.b3_routed);
     const uint8_t* b1s = reinterpret_cast<const uint8_t*>(args.b1_shared);
     const uint8_t* b3s = reinterpret_cast<const uint8_t*>(args.b3_shared);
-    c.load_a = __builtin_amdgcn_readfirstlane(32 * wave < t.rows ? 1 : 0) != 0;
+    c.load_a = __builtin_amdgcn_readfirstlane(8 * kDmaA * wave < t.rows ? 1 : 0) != 0;
     {
       const uint32_t lds0 = static_cast<uint32_t>(reinterpret_cast<uintptr_t>((lds_ptr)(stages)));
       const int wv = __builtin_amdgcn_readfirstlane(wave);
-      c.lds_wave = lds0 + static_cast<uint32_t>(32 * wv * BK);
-      c.lds_scale = lds0 + static_cast<uint32_t>(2 * kOperand + 4 * kWave * wv);
-      c.load_scale = wv < BM / kWave;
+      c.lds_a = lds0 + static_cast<uint32_t>(8 * kDmaA * wv * BK);
+      c.lds_b = lds0 + static_cast<uint32_t>(kOpA + 32 * wv * BK);
+      c.lds_scale = lds0 + static_cast<uint32_t>(kOpA + kOpB + 4 * kWave * wv);
+      c.load_scale = wv < kScaleSlots / kWave;
     }
-    // this lane's load rows: 32*wave + 8j + lane/8 of the tile, slot lane%8, holding
-    // global chunk slot ^ ((row/2)%8) (the swizzle of swz)
+    // this lane's load rows: 8 kDmaA wave + 8j + lane/8 of the tile's A rows (and 32 wave +
+    // 8j + lane/8 of its B rows), slot lane%8, holding global chunk slot ^ ((row/2)%8) (the
+    // swizzle of swz)
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int r = 32 * wave + 8 * j + lane / 8;
+    for (int j = 0; j < kDmaA; ++j) {
+      const int r = 8 * kDmaA * wave + 8 * j + lane / 8;
       const int chunk = (lane % 8) ^ ((r >> 1) & 7);
       c.a[j] = static_cast<uint32_t>(a_row(r) * lda + chunk * 16);
     }
@@ -385,10 +403,10 @@ __global__ __launch_bounds__(kThreads) void grouped_gemm_fp8(Fp8Args fa) {
       }
     }
     {  // scales are indexed by sorted row (routed) or token (shared), not by the gathered A row.
-      // LDS slot 128 g + 8 c + mb holds row 128 g + 16 mb + c, so that a lane's scales of its
-      // 8 row blocks (rows arow0 + 16 mb) are contiguous
-      const int slot = tid & (BM - 1);
-      int r = 128 * (slot / 128) + 16 * (slot % 8) + (slot % 128) / 8;
+      // LDS slot GS g + 12 c + mb holds row GR g + 16 mb + c (padding slots: row GR g + c)
+      const int slot = tid % kScaleSlots;
+      const int sg2 = slot / GS, c12 = (slot % GS) / kScalePitch, mb = slot % kScalePitch;
+      int r = GR * sg2 + 16 * (mb < kRB ? mb : 0) + c12;
       if (r >= t.rows) r = t.rows - 1;
       c.sbase = uniform_ptr(routed ? fa.sa_routed + row_base + t.m0 : fa.sa_shared + t.m0);
       c.s = static_cast<uint32_t>(4 * r);
@@ -411,16 +429,18 @@ __global__ __launch_bounds__(kThreads) void grouped_gemm_fp8(Fp8Args fa) {
     c.kseg_inv = kseg_recip(c.kseg_steps);
     c.nk = (routed ? args.K : args.K * (GATED ? 1 : args.k_segments)) / BK;
 
-    f32x4 acc[8][4];
+    f32x4 acc[kRB][4];
 #pragma unroll
-    for (int a = 0; a < 8; ++a)
+    for (int a = 0; a < kRB; ++a)
 #pragma unroll
       for (int b = 0; b < 4; ++b) acc[a][b] = f32x4{};
 
-    int vblk = (t.rows - 128 * g + 31) / 32;
-    vblk = vblk < 0 ? 0 : (vblk > 4 ? 4 : vblk);
+    int vblk = (t.rows - GR * g + 31) / 32;
+    vblk = vblk < 0 ? 0 : (vblk > kNM ? kNM : vblk);
     vblk = __builtin_amdgcn_readfirstlane(vblk);
+    static_assert(kNM == 5, "the K loop is specialised for 0..5 live 32-row blocks");
     switch (vblk) {  // every wave runs the same loads and barriers; only the MFMA count differs
+      case 5: mainloop<GATED, 5>(c, acc); break;
       case 4: mainloop<GATED, 4>(c, acc); break;
       case 3: mainloop<GATED, 3>(c, acc); break;
       case 2: mainloop<GATED, 2>(c, acc); break;
@@ -429,16 +449,16 @@ __global__ __launch_bounds__(kThreads) void grouped_gemm_fp8(Fp8Args fa) {
     }
 
     // epilogue: the MFMA took the weight fragment first, so a lane holds token row
-    // 128 g + 16 mb + lane%16 and, in each 16-column block nb, the 4 consecutive columns
+    // GR g + 16 mb + lane%16 and, in each 16-column block nb, the 4 consecutive columns
     // 4 (lane/16) + v
     const int rc = lane % 16, q = lane / 16;
     if (GATED) {
       // H = SiLU(gate) * up, then per-row 1x128 quantisation over the tile's 128 gate
       // columns (spread over the 4 waves of the group): amax per row via LDS
-      float* amaxbuf = reinterpret_cast<float*>(stage<0>());  // [4 waves][256 rows]
-      float h[8][2][4];
+      float* amaxbuf = reinterpret_cast<float*>(stage<0>());  // [4 waves][TR rows]
+      float h[kRB][2][4];
 #pragma unroll
-      for (int mb = 0; mb < 8; ++mb) {
+      for (int mb = 0; mb < kRB; ++mb) {
         float m = 0.0f;
 #pragma unroll
         for (int nb = 0; nb < 2; ++nb)
@@ -449,13 +469,14 @@ __global__ __launch_bounds__(kThreads) void grouped_gemm_fp8(Fp8Args fa) {
           }
         m = fmaxf(m, __shfl_xor(m, 16, kWave));
         m = fmaxf(m, __shfl_xor(m, 32, kWave));
-        if (q == 0) amaxbuf[wn * 256 + 128 * g + 16 * mb + rc] = m;
+        if (q == 0) amaxbuf[wn * TR + GR * g + 16 * mb + rc] = m;
       }
       __syncthreads();
 #pragma unroll
-      for (int mb = 0; mb < 8; ++mb) {
-        const int i = 128 * g + 16 * mb + rc;
-        const float amax = fmaxf(fmaxf(amaxbuf[i], amaxbuf[256 + i]), fmaxf(amaxbuf[512 + i], amaxbuf[768 + i]));
+      for (int mb = 0; mb < kRB; ++mb) {
+        const int i = GR * g + 16 * mb + rc;
+        const float amax =
+            fmaxf(fmaxf(amaxbuf[i], amaxbuf[TR + i]), fmaxf(amaxbuf[2 * TR + i], amaxbuf[3 * TR + i]));
         if (i >= t.rows) continue;
         const float s = amax / 448.0f;
         const int64_t m = t.m0 + i;
@@ -482,9 +503,9 @@ __global__ __launch_bounds__(kThreads) void grouped_gemm_fp8(Fp8Args fa) {
       __syncthreads();  // amaxbuf (LDS stage 0) is reused by the next tile
     } else {
 #pragma unroll
-      for (int mb = 0; mb < 8; ++mb) {
+      for (int mb = 0; mb < kRB; ++mb) {
         if (mb >= 2 * vblk) continue;
-        const int i = 128 * g + 16 * mb + rc;
+        const int i = GR * g + 16 * mb + rc;
         if (i >= t.rows) continue;
         const int64_t m = t.m0 + i;
 #pragma unroll

@@ -8,9 +8,10 @@ scores 1 and 0.5 decide the choice with a gap near 0.5. The assignment is shuffl
 tokens, so every expert's rows are gathered from scattered tokens.
 
 The counts sit on both sides of each row boundary of the tiles: the 32-row MFMA blocks (31,
-32, 33); the bf16 gate/up kernel's 160-row wave groups and 320-row tiles (159..161, 319..321,
-and 640, 641 as two blocks of 320 and of 320 + 321); the 256-row tiles of the bf16
-down-projection and of the FP8 kernel (255..257); an empty and a one-row expert. The shared
+32, 33) and the FP8 kernel's 16-row blocks inside them; the 160-row wave groups and 320-row
+tiles of both kernels, bf16 and FP8, in both phases (159..161, 319..321, and 640, 641 as two
+blocks of 320 and of 320 + 321); 255..257, the 256-row tiles the kernels used before; an
+empty and a one-row expert. The shared
 expert runs over all 3586 tokens.
 
 Forward, in bf16 and FP8. Checked against the oracle: routing, counts, permutation and bias

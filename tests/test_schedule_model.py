@@ -6,8 +6,8 @@ counter and per-gang claim slots. This test restates those rules in Python and r
 under random interleavings of the workgroups, on random and skewed expert loads, checking:
 
 - every (group, row, output-column tile) is computed exactly once;
-- no tile is empty and no tile is taller than the kernel's tile height (the bf16 kernel's
-  320 rows in both phases; the FP8 kernel's 256 in both);
+- no tile is empty and no tile is taller than the kernel's tile height (320 rows in both
+  phases of the bf16 and the FP8 kernels; 256-row blocks are checked as well);
 - the tile count stays within the bound the workspace is sized for (ffn_max_tiles in
   abi.cpp, counted in 256-row blocks, so it also bounds the taller tiles) and no gang
   reads past its row of slots (slot stride ceil(max/G) + 2);
