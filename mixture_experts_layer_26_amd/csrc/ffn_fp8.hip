@@ -479,6 +479,7 @@ __global__ __launch_bounds__(kThreads) void grouped_gemm_fp8(Fp8Args fa) {
             fmaxf(fmaxf(amaxbuf[i], amaxbuf[TR + i]), fmaxf(amaxbuf[2 * TR + i], amaxbuf[3 * TR + i]));
         if (i >= t.rows) continue;
         const float s = amax / 448.0f;
+        const float rs = s == 0.0f ? 0.0f : 1.0f / s;  // H's codes: h * (1/s), one division per row
         const int64_t m = t.m0 + i;
         uint8_t* orow;
         float* srow;
@@ -495,7 +496,7 @@ __global__ __launch_bounds__(kThreads) void grouped_gemm_fp8(Fp8Args fa) {
           uint32_t codes = 0;
 #pragma unroll
           for (int v = 0; v < 4; ++v)
-            codes |= (s == 0.0f ? 0u : e4m3(h[mb][nb][v] / s)) << (8 * v);
+            codes |= e4m3(h[mb][nb][v] * rs) << (8 * v);
           *reinterpret_cast<uint32_t*>(orow + t.n0 + 32 * wn + 16 * nb + 4 * q) = codes;
         }
         if (wn == 0 && q == 0) *srow = s;

@@ -34,8 +34,13 @@ struct Tile {
 // groups' tiles are all of full height and come first; the routed tiles, whose heights
 // vary, fill the tail of the launch, where short tiles even out the finish.
 // Routed groups list their tiles column-major (the row blocks of one column tile are
-// neighbours: they read the same weights); shared groups row-major (the column tiles of
-// one row block are neighbours: they read the same rows). Built per workgroup in LDS.
+// neighbours: they read the same weights). A shared group is a dense GEMM over all tokens
+// (many row blocks), so its tiles go in blocks of kSharedBR row blocks x kSharedBC column
+// tiles (one 32-tile gang item): within a gang's item each weight tile is read by 4 CUs and
+// each row block by 8, through the XCD's L2, where a row-major order re-read the shared
+// expert's weights once per row block. Built per workgroup in LDS.
+constexpr int kSharedBR = 4, kSharedBC = 8;  // shared groups: tiles in blocks of 4 row blocks x 8 columns
+
 struct TileMap {
   int cum[kMaxGroups + 1];  // first tile index of the group at each position
   int grp[kMaxGroups];      // group at each position
@@ -95,8 +100,17 @@ __device__ __forceinline__ Tile tile_at(const TileMap& tm, int L, int n_r, int b
     n = local / mt;
     m = local - n * mt;
   } else {
-    m = local / ntn;
-    n = local - m * ntn;
+    // row groups of kSharedBR row blocks (the last may be shorter); within one, column
+    // groups of kSharedBC tiles (the last may be narrower); row-major inside a block
+    const int mt = tm.mt[t.group];
+    const int rg = local / (kSharedBR * ntn);
+    const int rem = local - rg * kSharedBR * ntn;
+    const int br = mt - rg * kSharedBR < kSharedBR ? mt - rg * kSharedBR : kSharedBR;
+    const int cg = rem / (br * kSharedBC);
+    const int rem2 = rem - cg * br * kSharedBC;
+    const int bc = ntn - cg * kSharedBC < kSharedBC ? ntn - cg * kSharedBC : kSharedBC;
+    m = rg * kSharedBR + rem2 / bc;
+    n = cg * kSharedBC + rem2 % bc;
   }
   const int rpb = tm.rpb[t.group];
   t.n0 = n * bn_out;

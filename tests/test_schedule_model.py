@@ -46,8 +46,9 @@ def tiles_of(rows, n_r, ntn, rb=BM):
     for g in order:
         if g < n_r:  # column-major: the row blocks of one column tile are neighbours
             pairs = [(m, n) for n in range(ntn) for m in range(mt[g])]
-        else:  # row-major: the column tiles of one row block are neighbours
-            pairs = [(m, n) for m in range(mt[g]) for n in range(ntn)]
+        else:  # blocks of 4 row blocks x 8 column tiles, row-major inside a block
+            pairs = [(m, n) for r0 in range(0, mt[g], 4) for c0 in range(0, ntn, 8)
+                     for m in range(r0, min(r0 + 4, mt[g])) for n in range(c0, min(c0 + 8, ntn))]
         for m, n in pairs:
             m0 = m * rpb[g]
             out.append((g, m0, n, min(rpb[g], rows[g] - m0)))
@@ -177,3 +178,28 @@ def test_k_segment_reciprocal():
         inv = np.uint64(((1 << 31) + d - 1) // d)
         seg = ((np.uint64(2) * kt) * inv) >> np.uint64(32)
         assert np.array_equal(seg, kt // np.uint64(d)), d
+
+
+def _shared_tile_at(local, mt, ntn, br_full=4, bc_full=8):
+    """tile_at's closed form for a shared group (gemm_common.h), restated: row groups of 4 row
+    blocks (the last may be shorter), inside one column groups of 8 tiles (the last may be
+    narrower), row-major inside a block."""
+    rg = local // (br_full * ntn)
+    rem = local - rg * br_full * ntn
+    br = min(br_full, mt - rg * br_full)
+    cg = rem // (br * bc_full)
+    rem2 = rem - cg * br * bc_full
+    bc = min(bc_full, ntn - cg * bc_full)
+    return rg * br_full + rem2 // bc, cg * bc_full + rem2 % bc
+
+
+def test_shared_block_order_closed_form():
+    """The device's index arithmetic for shared groups gives, position by position, the
+    blocked order the list model enumerates, and so covers every (row block, column tile)
+    exactly once, including short last row groups and narrow last column groups."""
+    for mt in (1, 2, 3, 4, 5, 7, 8, 13, 26, 33):
+        for ntn in (1, 3, 8, 11, 16, 28):
+            want = [(m, n) for _, m0, n, _ in tiles_of([mt * 100], 0, ntn, 100) for m in [m0 // 100]]
+            got = [_shared_tile_at(L, mt, ntn) for L in range(mt * ntn)]
+            assert got == want, (mt, ntn)
+            assert len(set(got)) == mt * ntn
