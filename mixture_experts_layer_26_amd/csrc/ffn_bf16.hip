@@ -8,22 +8,27 @@
 // through sorted_token) and the shared experts (rows = all tokens).
 //
 // Kernel shape: a persistent grid of one 8-wave workgroup per CU walks the device-built
-// tile list in gangs (gemm_common.h). A tile is up to 320 rows x 256 weight rows (phase 1:
-// 128 gate + 128 up columns; phase 2: 256 output columns): at V3 prefill the routed
-// experts hold about 185..345 rows, so with 320-row tiles most experts are one row block
-// and their weights pass through the L1 once, where 256-row tiles split about 120 of the
-// 256 experts in two. K advances in steps of 64 (128-byte rows) through two LDS stages
-// filled by direct global-to-LDS loads (global_load_lds_dwordx4): no staging registers
-// and no LDS store instructions; a stage is loaded one step before it is computed. One
-// barrier per step, before its last 16-wide sub-step, so each wave reads the next step's
-// first fragments while the MFMAs of the current one run. Every wave computes a 160 x 64
-// block with v_mfma_f32_32x32x16_bf16 (10 MFMA tiles): wave (g, wn) owns rows 160g.. of
-// the tile; in phase 1 gate rows 32wn.. with the matching up rows (so SiLU(gate) * up is
-// formed in registers), in phase 2 output columns 64wn... The load addresses keep their
-// wave-uniform part in SGPRs (one VGPR per loaded row), which leaves the K loops free of
-// register spills at 320 rows in both phases. The K loop is specialised on the number of
-// 32-row blocks of a wave that hold rows, so row blocks past an expert's count cost no
-// MFMA work. Weights are read row-major or in the tiled layout of pack.hip.
+// tile list in gangs (gemm_common.h). A tile is up to TRW rows x 256 weight rows (phase 1:
+// 128 gate + 128 up columns; phase 2: 256 output columns). Two tile shapes:
+// - large batches: 320-row tiles, two LDS stages. At V3 prefill the routed experts hold
+//   about 185..345 rows, so most experts are one row block and their weights pass through
+//   the L1 once, where 256-row tiles split about 120 of the 256 experts in two.
+// - batches of at most 128 tokens (decode): 128-row tiles, so every group is one row
+//   block, and three LDS stages. These launches stream the weights once and do little MFMA
+//   work; the third stage keeps two K-steps of weights in flight per CU across each
+//   barrier instead of one.
+// K advances in steps of 64 (128-byte rows) through a ring of LDS stages filled by direct
+// global-to-LDS loads (global_load_lds_dwordx4): no staging registers and no LDS store
+// instructions. One barrier per step, before its last 16-wide sub-step, so each wave reads
+// the next step's first fragments while the MFMAs of the current one run. Every wave
+// computes a TRW/2 x 64 block with v_mfma_f32_32x32x16_bf16: wave (g, wn) owns rows
+// g*TRW/2.. of the tile; in phase 1 gate rows 32wn.. with the matching up rows (so
+// SiLU(gate) * up is formed in registers), in phase 2 output columns 64wn... The load
+// addresses keep their wave-uniform part in SGPRs (one VGPR per loaded row), which leaves
+// the K loops free of register spills at 320 rows in both phases. The K loop is
+// specialised on the number of 32-row blocks of a wave that hold rows, so row blocks past
+// an expert's count cost no MFMA work. Weights are read row-major or in the tiled layout
+// of pack.hip.
 #include "gemm_common.h"
 #include "launch.h"
 
@@ -36,30 +41,35 @@ using namespace gemm;
 constexpr int BK = 64;                  // bf16 per K-step: 128-byte rows (whole cache lines)
 constexpr int kRow = 128;               // bytes per tile row per stage
 constexpr int kOpB = BNB * kRow;        // 32 KB: the B rows of one stage
-constexpr int kStages = 2;
 constexpr int kSubs = BK / 16;          // MFMA sub-steps per K-step
 constexpr int kDmaB = BNB / 64;         // B loads (global_load_lds of 8 rows) per wave per step
 
-// Tile geometry for TRW tile rows: two wave groups of TRW / 2 rows, each wave a
-// TRW / 2 x 64 block of 32 x 32 MFMA tiles. Both phases use 320 rows.
-template <int TRW>
+// Tile geometry for TRW tile rows and S stages: two wave groups of TRW / 2 rows, each wave
+// a TRW / 2 x 64 block of 32 x 32 MFMA tiles.
+template <int TRW, int S>
 struct Geo {
   static constexpr int GR = TRW / 2;      // rows per wave group
   static constexpr int kMB = GR / 32;     // 32-row blocks per wave
   static constexpr int kOpA = TRW * kRow; // the A rows of one stage
   static constexpr int kDmaA = TRW / 64;  // A loads per wave per step
+  static constexpr int kStage = kOpA + kOpB;
+  static constexpr int kS = S;
 };
-constexpr int kTR1 = 320, kTR2 = 320;     // tile rows of phase 1 and phase 2
-constexpr int kStageSz = Geo<kTR1>::kOpA + kOpB;  // 72 KB
+using GeoLarge = Geo<320, 2>;  // 2 x 72 KB
+using GeoSmall = Geo<128, 3>;  // 3 x 48 KB; every group of a batch of <= 128 tokens is one block
+static_assert(GeoSmall::GR * 2 == kSmallBatchRows, "the small tiles hold a whole small batch");
 
-// The two stages.
-__shared__ __attribute__((aligned(16))) unsigned char stage0[kStageSz];
-__shared__ __attribute__((aligned(16))) unsigned char stage1[kStageSz];
+// The ring of S stages of one geometry (one LDS array per geometry: a kernel allocates
+// only the ring it uses).
+template <class G>
+__device__ __forceinline__ unsigned char* ring() {
+  __shared__ __attribute__((aligned(16))) unsigned char r[G::kS * G::kStage];
+  return r;
+}
 
-template <int ST>
+template <class G, int ST>
 __device__ __forceinline__ unsigned char* stage() {
-  if constexpr (ST == 0) return stage0;
-  else return stage1;
+  return ring<G>() + ST * G::kStage;
 }
 
 typedef __attribute__((address_space(3))) unsigned char* lds_ptr;
@@ -76,12 +86,23 @@ typedef __attribute__((address_space(3))) unsigned char* lds_ptr;
 // no value of its own in M0 across the statement (clang warns that M0 is a reserved
 // register; the clobber is what tells its M0-initialisation passes that the statement
 // writes it).
+// NT sets the non-temporal cache policy, used for the weights: each weight byte is read
+// by one workgroup, or by the few of a gang close together in time, and streaming it
+// with that policy measured faster in every phase (V3 decode 3.86 -> 3.67 ms, V3 prefill
+// 7.08 -> 6.86 ms). The rows of A are re-read by many workgroups through the L2 and keep
+// the default policy (with it set on A, V3 prefill took 8.5 ms).
 #pragma clang diagnostic push
 #pragma clang diagnostic ignored "-Winline-asm"
+template <bool NT>
 __device__ __forceinline__ void dma16(uint32_t voff, const unsigned char* sbase, const unsigned char* lds) {
   const uint32_t m0 = static_cast<uint32_t>(reinterpret_cast<uintptr_t>((lds_ptr)(lds)));
-  asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1" ::"v"(voff), "s"(sbase), "s"(m0)
-               : "memory", "m0");
+  if constexpr (NT)
+    asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1 nt" ::"v"(voff), "s"(sbase),
+                 "s"(m0)
+                 : "memory", "m0");
+  else
+    asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1" ::"v"(voff), "s"(sbase), "s"(m0)
+                 : "memory", "m0");
 }
 #pragma clang diagnostic pop
 
@@ -94,11 +115,11 @@ __device__ __forceinline__ const unsigned char* uniform_ptr(const void* p) {
   return reinterpret_cast<const unsigned char*>((hi << 32) | lo);
 }
 
-template <int TRW>
+template <class G>
 struct TileCtx {
   bool load_a;                  // this wave's A rows hold at least one of the tile's rows
   const unsigned char* abase;   // wave-uniform: K-step 0 of the A rows
-  uint32_t a[Geo<TRW>::kDmaA];  // this lane's A rows: byte offsets from abase (chunk included)
+  uint32_t a[G::kDmaA];         // this lane's A rows: byte offsets from abase (chunk included)
   const unsigned char* bbase;   // wave-uniform: K-step 0 of this wave's B rows
   uint32_t b[kDmaB];            // this lane's four B rows: byte offsets from bbase (chunk included)
   int64_t seg_stride;    // phase 2 shared: W2 stride per K segment (elements), else 0
@@ -109,22 +130,22 @@ struct TileCtx {
 };
 
 // Direct loads of K-step kt into stage ST: wave w fills A rows 8 kDmaA w.. (kDmaA 8-row
-// instructions: 40 rows in phase 1, 32 in phase 2) and B rows 32w..32w+31 (four); lane i
-// writes row 8j + i/8 of its instruction's block, 16-byte slot i%8, whose global chunk
-// was chosen when the offsets were made. A wave whose A rows all lie past the tile's rows
-// loads no A (those LDS rows feed only outputs that are not stored).
-template <int ST, int TRW>
-__device__ __forceinline__ void dma_step(const TileCtx<TRW>& c, int kt, int wave) {
-  constexpr int kDmaA = Geo<TRW>::kDmaA, kOpA = Geo<TRW>::kOpA;
-  unsigned char* st = stage<ST>();
+// instructions: 40 rows with 320-row tiles, 16 with 128-row tiles) and B rows 32w..32w+31
+// (four); lane i writes row 8j + i/8 of its instruction's block, 16-byte slot i%8, whose
+// global chunk was chosen when the offsets were made. A wave whose A rows all lie past the
+// tile's rows loads no A (those LDS rows feed only outputs that are not stored).
+template <int ST, class G>
+__device__ __forceinline__ void dma_step(const TileCtx<G>& c, int kt, int wave) {
+  constexpr int kDmaA = G::kDmaA, kOpA = G::kOpA;
+  unsigned char* st = stage<G, ST>();
   const unsigned char* ak = c.abase + static_cast<int64_t>(kt) * (BK * 2);
   const unsigned char* bk = c.bbase + 2 * b_offset(kt, c.kseg_steps, c.kseg_inv, c.seg_stride, c.bstep);
   if (c.load_a) {
 #pragma unroll
-    for (int j = 0; j < kDmaA; ++j) dma16(c.a[j], ak, st + (8 * kDmaA * wave + 8 * j) * kRow);
+    for (int j = 0; j < kDmaA; ++j) dma16<false>(c.a[j], ak, st + (8 * kDmaA * wave + 8 * j) * kRow);
   }
 #pragma unroll
-  for (int j = 0; j < kDmaB; ++j) dma16(c.b[j], bk, st + kOpA + (8 * kDmaB * wave + 8 * j) * kRow);
+  for (int j = 0; j < kDmaB; ++j) dma16<true>(c.b[j], bk, st + kOpA + (8 * kDmaB * wave + 8 * j) * kRow);
 }
 
 // Fragments of one 16-wide sub-step of stage ST for a wave holding NMB live 32-row
@@ -135,10 +156,10 @@ struct Frags {
   bf16x8 b[2];
 };
 
-template <int ST, int TRW, int NMB>
+template <int ST, class G, int NMB>
 __device__ __forceinline__ void read_frags(Frags<NMB>& f, int sub, int arow0, const int (&brow)[2], int lane) {
-  const unsigned char* la = stage<ST>();
-  const unsigned char* lb = la + Geo<TRW>::kOpA;
+  const unsigned char* la = stage<G, ST>();
+  const unsigned char* lb = la + G::kOpA;
   const int ch = 2 * sub + lane / 32;
 #pragma unroll
   for (int mb = 0; mb < NMB; ++mb) f.a[mb] = *reinterpret_cast<const bf16x8*>(la + swz(arow0 + 32 * mb, ch));
@@ -163,87 +184,134 @@ __device__ __forceinline__ void mfma_sub(const Frags<NMB>& f, f32x16 (&acc)[KMB]
 // below (MFMAs, barrier, loads, reads) is the order issued.
 __device__ __forceinline__ void fence() { __builtin_amdgcn_sched_barrier(0); }
 
-// Wait until this wave's LDS reads have returned and its loads of the next step have
-// landed (NEWER loads issued after them may stay in flight), then the workgroup
-// barrier: after it every wave's part of the next step is in LDS and no wave reads the
-// current step's stage any more. Loads complete in order, so any extra memory
+// Wait until at most N of this wave's loads are in flight. Loads complete in order, so
+// with N = the loads issued after those of a step, that step has landed; any extra memory
 // operation only makes the wait stricter.
-template <int NEWER>
-__device__ __forceinline__ void step_barrier() {
-  static_assert(NEWER >= 0 && NEWER < 64, "vmcnt range");
-  asm volatile("s_waitcnt vmcnt(%0)\n\ts_waitcnt lgkmcnt(0)\n\ts_barrier" ::"n"(NEWER) : "memory");
+template <int N>
+__device__ __forceinline__ void wait_vm() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
 }
 
-// One K-step s from stage ST = s % 2, four 16-wide sub-steps. Fragment sets f0 and f1
+// Wait until this wave's LDS reads have returned and its loads of the next step have
+// landed, with `steps` later K-steps of its loads left in flight (0 .. S - 1; a wave issues
+// kDmaB loads per step, plus kDmaA when it loads A), then the workgroup barrier: after it
+// every wave's part of the next step is in LDS and no wave reads the current step's stage
+// any more. The branches choose only the count of the load wait (their conditions are
+// wave-uniform); the barrier itself is issued once, unconditionally.
+template <class G>
+__device__ __forceinline__ void step_barrier(int steps, bool load_a) {
+  constexpr int LB = kDmaB, LAB = G::kDmaA + kDmaB;
+  static_assert(G::kS <= 3, "wait counts written out for up to two later steps");
+  if (steps <= 0)
+    wait_vm<0>();
+  else if (steps == 1)
+    load_a ? wait_vm<LAB>() : wait_vm<LB>();
+  else
+    load_a ? wait_vm<2 * LAB>() : wait_vm<2 * LB>();
+  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
+
+// One K-step s from stage ST = s % S, four 16-wide sub-steps. Fragment sets f0 and f1
 // alternate: each sub-step's MFMAs run while the sub-step after next is read. On entry
-// sub-steps 0 and 1 have been requested. The barrier sits before the last sub-step: the
-// wave has then issued every read of stage ST, so after it stage ST takes the load of
-// step s+2 (when DMA) and the next step's first two sub-steps are read from the other
-// stage (loaded one step ago, landed; when READ) while the last sub-step runs.
-template <int ST, int TRW, int NMB, bool DMA, bool READ>
-__device__ __forceinline__ void k_step(const TileCtx<TRW>& c, int s, int wave, int arow0, const int (&brow)[2],
-                                       int lane, Frags<NMB>& f0, Frags<NMB>& f1,
-                                       f32x16 (&acc)[Geo<TRW>::kMB][2]) {
-  constexpr int NMF = 2 * NMB;
+// sub-steps 0 and 1 have been requested, steps up to s + S - 1 have been loaded or are in
+// flight, and `newer` of them lie beyond s + 1. The barrier sits before the last sub-step:
+// the wave has then issued every read of stage ST, and step s + 1 has landed; after it
+// stage ST takes the load of step s + S (when dma) and the next step's first two
+// sub-steps are read (when read) while the last sub-step runs.
+template <int ST, class G, int NMB>
+__device__ __forceinline__ void k_step(const TileCtx<G>& c, int s, int wave, int arow0, const int (&brow)[2],
+                                       int lane, Frags<NMB>& f0, Frags<NMB>& f1, f32x16 (&acc)[G::kMB][2],
+                                       bool dma, bool read, int newer) {
+  constexpr int NMF = 2 * NMB, S = G::kS, NX = (ST + 1) % S;
   mfma_sub(f0, acc);
   fence();
-  read_frags<ST, TRW, NMB>(f0, 2, arow0, brow, lane);
+  read_frags<ST, G, NMB>(f0, 2, arow0, brow, lane);
   fence();
   mfma_sub(f1, acc);
   fence();
-  read_frags<ST, TRW, NMB>(f1, 3, arow0, brow, lane);
+  read_frags<ST, G, NMB>(f1, 3, arow0, brow, lane);
   fence();
   mfma_sub(f0, acc);
   fence();
-  step_barrier<0>();
+  step_barrier<G>(newer, c.load_a);
   fence();
   if constexpr (NMF > 0) mfma_one(f1, acc, 0);
   fence();
-  if constexpr (DMA) dma_step<ST, TRW>(c, s + kStages, wave);
+  if (dma) dma_step<ST, G>(c, s + S, wave);
   fence();
   if constexpr (NMF > 1) mfma_one(f1, acc, 1);
   fence();
-  if constexpr (READ) read_frags<(ST + 1) % kStages, TRW, NMB>(f0, 0, arow0, brow, lane);
+  if (read) read_frags<NX, G, NMB>(f0, 0, arow0, brow, lane);
   fence();
 #pragma unroll
   for (int i = 2; i < NMF; ++i) mfma_one(f1, acc, i);
   fence();
-  if constexpr (READ) read_frags<(ST + 1) % kStages, TRW, NMB>(f1, 1, arow0, brow, lane);
+  if (read) read_frags<NX, G, NMB>(f1, 1, arow0, brow, lane);
   fence();
 }
 
-// The K loop of one tile. nk is even (K is a multiple of 128): the loop runs all but
-// the last two steps, which load nothing. On exit no load is in flight and every wave
-// is past the last read of the stages.
-template <int TRW, int NMB>
-__device__ __forceinline__ void mainloop(const TileCtx<TRW>& c, f32x16 (&acc)[Geo<TRW>::kMB][2], int arow0,
-                                         const int (&brow)[2]) {
-  const int lane = threadIdx.x % kWave;
-  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
-  dma_step<0, TRW>(c, 0, wave);
-  dma_step<1, TRW>(c, 1, wave);
-  // step 0 landed; step 1 (kDmaA + 4 loads, or 4 without A) in flight
-  if (c.load_a)
-    step_barrier<Geo<TRW>::kDmaA + kDmaB>();
-  else
-    step_barrier<kDmaB>();
-  Frags<NMB> f0, f1;
-  read_frags<0, TRW, NMB>(f0, 0, arow0, brow, lane);
-  read_frags<0, TRW, NMB>(f1, 1, arow0, brow, lane);
-  int s = 0;
-  for (; s < c.nk - kStages; s += kStages) {
-    k_step<0, TRW, NMB, true, true>(c, s, wave, arow0, brow, lane, f0, f1, acc);
-    k_step<1, TRW, NMB, true, true>(c, s + 1, wave, arow0, brow, lane, f0, f1, acc);
+// Steps base + I, base + I + 1, ... below base + R (base a multiple of S, R <= 2S - 1): the
+// tail of the K loop, whose loads and waits depend on how many steps remain.
+template <int I, class G, int NMB>
+__device__ __forceinline__ void tail_steps(const TileCtx<G>& c, int base, int R, int wave, int arow0,
+                                           const int (&brow)[2], int lane, Frags<NMB>& f0, Frags<NMB>& f1,
+                                           f32x16 (&acc)[G::kMB][2]) {
+  constexpr int S = G::kS;
+  if constexpr (I < 2 * S - 1) {
+    if (I < R) {
+      const int left = R - I;  // steps from this one to the end
+      const int newer = left - 2 < S - 2 ? left - 2 : S - 2;
+      k_step<I % S, G, NMB>(c, base + I, wave, arow0, brow, lane, f0, f1, acc, left > S, left > 1, newer);
+      tail_steps<I + 1, G, NMB>(c, base, R, wave, arow0, brow, lane, f0, f1, acc);
+    }
   }
-  k_step<0, TRW, NMB, false, true>(c, s, wave, arow0, brow, lane, f0, f1, acc);
-  k_step<1, TRW, NMB, false, false>(c, s + 1, wave, arow0, brow, lane, f0, f1, acc);
 }
 
-template <bool GATED>
+template <int J, class G>
+__device__ __forceinline__ void prologue_dma(const TileCtx<G>& c, int wave) {
+  if constexpr (J < G::kS) {
+    if (J < c.nk) {
+      dma_step<J, G>(c, J, wave);
+      prologue_dma<J + 1, G>(c, wave);
+    }
+  }
+}
+
+template <int I, class G, int NMB>
+__device__ __forceinline__ void body_steps(const TileCtx<G>& c, int s, int wave, int arow0, const int (&brow)[2],
+                                           int lane, Frags<NMB>& f0, Frags<NMB>& f1, f32x16 (&acc)[G::kMB][2]) {
+  if constexpr (I < G::kS) {
+    k_step<I, G, NMB>(c, s + I, wave, arow0, brow, lane, f0, f1, acc, true, true, G::kS - 2);
+    body_steps<I + 1, G, NMB>(c, s, wave, arow0, brow, lane, f0, f1, acc);
+  }
+}
+
+// The K loop of one tile: steps 0 .. S-1 are loaded up front, and step s loads step s + S
+// into the stage it has just finished. The loop runs S steps at a time while every one of
+// them loads; the last S .. 2S - 1 steps (or all, for a short K) go through tail_steps. On
+// exit no load is in flight and every wave is past the last read of the stages.
+template <class G, int NMB>
+__device__ __forceinline__ void mainloop(const TileCtx<G>& c, f32x16 (&acc)[G::kMB][2], int arow0,
+                                         const int (&brow)[2]) {
+  constexpr int S = G::kS;
+  const int lane = threadIdx.x % kWave;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
+  prologue_dma<0, G>(c, wave);
+  // step 0 landed; steps 1 .. min(S, nk) - 1 in flight
+  step_barrier<G>((c.nk < S ? c.nk : S) - 1, c.load_a);
+  Frags<NMB> f0, f1;
+  read_frags<0, G, NMB>(f0, 0, arow0, brow, lane);
+  read_frags<0, G, NMB>(f1, 1, arow0, brow, lane);
+  int s = 0;
+  for (; s + 2 * S <= c.nk; s += S) body_steps<0, G, NMB>(c, s, wave, arow0, brow, lane, f0, f1, acc);
+  tail_steps<0, G, NMB>(c, s, c.nk - s, wave, arow0, brow, lane, f0, f1, acc);
+}
+
+template <bool GATED, class G>
 __global__ __launch_bounds__(kThreads) void grouped_gemm_bf16(GemmArgs args) {
   __shared__ TileMap tm;
-  constexpr int TR = GATED ? kTR1 : kTR2;
-  using G = Geo<TR>;
+  constexpr int TR = 2 * G::GR;
   constexpr int GR = G::GR, kMB = G::kMB, kDmaA = G::kDmaA;
 
   const int n_r = args.n_r;
@@ -261,7 +329,7 @@ __global__ __launch_bounds__(kThreads) void grouped_gemm_bf16(GemmArgs args) {
     const int sg = t.group - n_r;  // shared group index
     const int64_t row_base = routed ? args.offset[t.group] : 0;
 
-    TileCtx<TR> c;
+    TileCtx<G> c;
     // this lane's load rows: 8*kDmaA*wave + 8j + lane/8 of the tile's A rows and 32*wave + 8j +
     // lane/8 of its B rows, slot lane%8, holding global chunk slot ^ ((row/2)%8) (the
     // swizzle of swz). Offsets are in bytes from a wave-uniform base: the gathered rows of
@@ -306,7 +374,8 @@ __global__ __launch_bounds__(kThreads) void grouped_gemm_bf16(GemmArgs args) {
     c.bstep = args.b_tiled ? (GATED ? 128 : 256) * BK : BK;
     c.kseg_steps = args.K / BK;
     c.kseg_inv = kseg_recip(c.kseg_steps);
-    c.nk = (routed ? args.K : args.K * (GATED ? 1 : args.k_segments)) / BK;
+    // wave-uniform (it sets the K loop's loads and waits)
+    c.nk = __builtin_amdgcn_readfirstlane((routed ? args.K : args.K * (GATED ? 1 : args.k_segments)) / BK);
 
     f32x16 acc[kMB][2];
 #pragma unroll
@@ -325,16 +394,20 @@ __global__ __launch_bounds__(kThreads) void grouped_gemm_bf16(GemmArgs args) {
     int vblk = (t.rows - GR * g + 31) / 32;
     vblk = vblk < 0 ? 0 : (vblk > kMB ? kMB : vblk);
     vblk = __builtin_amdgcn_readfirstlane(vblk);
-    static_assert(kMB == 4 || kMB == 5, "the K loop is specialised for 0..kMB live row blocks");
+    static_assert(kMB >= 2 && kMB <= 5, "the K loop is specialised for 0..kMB live row blocks");
     switch (vblk) {  // every wave runs the same loads and barriers; only the MFMA count differs
       case 5:
-        if constexpr (kMB >= 5) mainloop<TR, (kMB >= 5 ? 5 : 4)>(c, acc, arow0, brow);
+        if constexpr (kMB >= 5) mainloop<G, (kMB >= 5 ? 5 : 1)>(c, acc, arow0, brow);
         break;
-      case 4: mainloop<TR, 4>(c, acc, arow0, brow); break;
-      case 3: mainloop<TR, 3>(c, acc, arow0, brow); break;
-      case 2: mainloop<TR, 2>(c, acc, arow0, brow); break;
-      case 1: mainloop<TR, 1>(c, acc, arow0, brow); break;
-      default: mainloop<TR, 0>(c, acc, arow0, brow); break;
+      case 4:
+        if constexpr (kMB >= 4) mainloop<G, (kMB >= 4 ? 4 : 1)>(c, acc, arow0, brow);
+        break;
+      case 3:
+        if constexpr (kMB >= 3) mainloop<G, (kMB >= 3 ? 3 : 1)>(c, acc, arow0, brow);
+        break;
+      case 2: mainloop<G, 2>(c, acc, arow0, brow); break;
+      case 1: mainloop<G, 1>(c, acc, arow0, brow); break;
+      default: mainloop<G, 0>(c, acc, arow0, brow); break;
     }
 
     // epilogue. C layout of the 32x32 MFMA: lane holds column lane%32 and rows
@@ -344,16 +417,16 @@ __global__ __launch_bounds__(kThreads) void grouped_gemm_bf16(GemmArgs args) {
       // bf16 outputs go through LDS (the stages are free once the K loop is done): group
       // g writes its rows as a [rows][W] bf16 tile into stage g, then its 256 threads
       // store whole rows with 16-byte stores, in passes of as many row blocks as a stage
-      // holds (phase 1: one pass of 160 rows of 256 B; phase 2: 128 + 32 rows of 512 B). Rows whose
-      // bit 2 is set have their 64-byte halves swapped, so
-      // the two half-waves' 2-byte writes (rows r and r+4) fall in different banks.
+      // holds (320-row tiles, phase 1: one pass of 160 rows of 256 B; phase 2: 128 + 32 rows
+      // of 512 B; 128-row tiles: one pass). Rows whose bit 2 is set have their 64-byte halves
+      // swapped, so the two half-waves' 2-byte writes (rows r and r+4) fall in different banks.
       constexpr int W = GATED ? BNB / 2 : BNB;  // output columns of the tile
       constexpr int pitch = 2 * W;               // bytes per row
-      constexpr int kFit = kStageSz / (32 * pitch);
+      constexpr int kFit = G::kStage / (32 * pitch);
       constexpr int kPassMB = kMB < kFit ? kMB : kFit;  // row blocks per pass
       constexpr int kPasses = (kMB + kPassMB - 1) / kPassMB;
-      static_assert(kPassMB * 32 * pitch <= kStageSz, "a pass fits in a stage");
-      unsigned char* ep = g == 0 ? stage<0>() : stage<1>();
+      static_assert(kPassMB * 32 * pitch <= G::kStage, "a pass fits in a stage");
+      unsigned char* ep = g == 0 ? stage<G, 0>() : stage<G, 1>();
       auto eoff = [](int r, int byte) { return r * pitch + (byte ^ (((r >> 2) & 1) << 6)); };
       const int gt = tid % 256;
       constexpr int cpr = pitch / 16;  // 16-byte chunks per row
@@ -416,14 +489,23 @@ __global__ __launch_bounds__(kThreads) void grouped_gemm_bf16(GemmArgs args) {
 
 }  // namespace
 
-size_t ffn_bf16_lds_bytes() { return kStages * kStageSz; }
+size_t ffn_bf16_lds_bytes() {
+  const size_t a = GeoLarge::kS * GeoLarge::kStage, b = GeoSmall::kS * GeoSmall::kStage;
+  return a > b ? a : b;
+}
 
 hipError_t launch_grouped_gemm_bf16(const GemmArgs& args, bool gated, int grid, hipStream_t stream) {
-  if (args.K % (kStages * BK) != 0) return hipErrorInvalidValue;
-  if (gated)
-    hipLaunchKernelGGL(grouped_gemm_bf16<true>, dim3(grid), dim3(kThreads), 0, stream, args);
+  if (args.K % (2 * BK) != 0) return hipErrorInvalidValue;
+  const bool small = args.T <= kSmallBatchRows;  // every group fits one 128-row tile
+  const dim3 g(grid), b(kThreads);
+  if (gated && small)
+    hipLaunchKernelGGL((grouped_gemm_bf16<true, GeoSmall>), g, b, 0, stream, args);
+  else if (gated)
+    hipLaunchKernelGGL((grouped_gemm_bf16<true, GeoLarge>), g, b, 0, stream, args);
+  else if (small)
+    hipLaunchKernelGGL((grouped_gemm_bf16<false, GeoSmall>), g, b, 0, stream, args);
   else
-    hipLaunchKernelGGL(grouped_gemm_bf16<false>, dim3(grid), dim3(kThreads), 0, stream, args);
+    hipLaunchKernelGGL((grouped_gemm_bf16<false, GeoLarge>), g, b, 0, stream, args);
   return hipGetLastError();
 }
 

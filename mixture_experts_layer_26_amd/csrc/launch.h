@@ -96,6 +96,10 @@ hipError_t launch_dispatch(const int32_t* idx, int64_t T, int K, int n_r, int32_
                            int32_t* count, int32_t* offset, int32_t* sorted_token,
                            int32_t* pair_row, hipStream_t stream);
 
+// bf16 grouped GEMM. Batches of at most kSmallBatchRows tokens (every group then fits one
+// row block of that height) run on 128-row tiles with a three-stage ring, larger ones on
+// 320-row tiles with two stages.
+constexpr int kSmallBatchRows = 128;
 size_t ffn_bf16_lds_bytes();
 hipError_t launch_grouped_gemm_bf16(const GemmArgs& args, bool gated, int grid, hipStream_t stream);
 

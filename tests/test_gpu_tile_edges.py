@@ -12,7 +12,9 @@ The counts sit on both sides of each row boundary of the tiles: the 32-row MFMA 
 tiles of both kernels, bf16 and FP8, in both phases (159..161, 319..321, and 640, 641 as two
 blocks of 320 and of 320 + 321); 255..257, the 256-row tiles the kernels used before; an
 empty and a one-row expert. The shared
-expert runs over all 3586 tokens.
+expert runs over all 3586 tokens. Batches of at most 128 tokens run the bf16 GEMMs on 128-row
+tiles (64-row wave groups): three more bf16 cases of 128 and 127 tokens put expert counts on
+31..33, 63..65 and 128 rows, and the shared expert on a full and a one-short tile.
 
 Forward, in bf16 and FP8. Checked against the oracle: routing, counts, permutation and bias
 bit for bit, and the whole output within the layer's tolerances. Then every GEMM row on its
@@ -54,6 +56,11 @@ from tests.test_gpu_backward import _f
 pytestmark = pytest.mark.gpu
 
 COUNTS = [1, 31, 32, 33, 159, 160, 161, 255, 256, 257, 319, 320, 321, 640, 641, 0]
+SMALL = {  # batches of <= 128 tokens (the bf16 GEMMs' 128-row tiles)
+    "small_a": [1, 31, 32, 33, 0, 31],  # T = 128: the 32-row MFMA blocks
+    "small_b": [63, 64, 1, 0],          # T = 128: the 64-row wave groups
+    "small_c": [65, 61, 1],             # T = 127: a shared tile one row short
+}
 BF16_EIGHT = 0x4100  # bit pattern of 8.0 in bf16
 ROW_TOL = 5e-3      # bf16 rows, and FP8 routed rows against the product of the GPU's own H
 SHARED_FP8_TOL = 1e-3  # fp32 shared rows against the product of the GPU's own H
@@ -156,13 +163,13 @@ def _down(codes, scales, w2q, tab):
     return hv @ w2.T
 
 
-def _check_fp8_rows(L, w, u, sorted_token, y_r):
+def _check_fp8_rows(L, w, u, sorted_token, y_r, counts):
     tab = oracle.e4m3_table()
     h_r, s_r, h_s, s_s, q_u = (to_np(x) for x in _fp8_h(L, w))
     _check_layout_reading(q_u, u, "tile edges")
-    off = np.concatenate([[0], np.cumsum(COUNTS)])
+    off = np.concatenate([[0], np.cumsum(counts)])
     worst = {}
-    for i, c in enumerate(COUNTS):
+    for i, c in enumerate(counts):
         if not c:
             continue
         q = _q_host(I.make_expert(w, False, i))
@@ -180,17 +187,19 @@ def _check_fp8_rows(L, w, u, sorted_token, y_r):
     assert err_s.max() <= SHARED_FP8_TOL
 
 
-def _workload(name):
-    return I.Workload(name, T=sum(COUNTS), d=512, n_routed=len(COUNTS), top_k=1, n_shared=1, d_ff=256,
+def _workload(name, counts=COUNTS):
+    return I.Workload(name, T=sum(counts), d=512, n_routed=len(counts), top_k=1, n_shared=1, d_ff=256,
                       act="bf16", ffn="bf16", seed=2709, bias_range=0.01)
 
 
-@pytest.mark.parametrize("ffn", ["bf16", "fp8"])
-def test_counts_on_tile_boundaries(ffn):
-    T = sum(COUNTS)
-    w = _workload(f"tile_edges_{ffn}")
-    log(f"[tile edges] ffn={ffn} T={T} d={w.d} N_r={w.n_routed} d_ff={w.d_ff} counts={COUNTS}")
-    u, e, assign = _forced_inputs(w, COUNTS, 2709)
+@pytest.mark.parametrize("ffn,case", [("bf16", "large"), ("fp8", "large"), ("bf16", "small_a"),
+                                      ("bf16", "small_b"), ("bf16", "small_c")])
+def test_counts_on_tile_boundaries(ffn, case):
+    counts = COUNTS if case == "large" else SMALL[case]
+    T = sum(counts)
+    w = _workload(f"tile_edges_{ffn}", counts)
+    log(f"[tile edges] ffn={ffn} T={T} d={w.d} N_r={w.n_routed} d_ff={w.d_ff} counts={counts}")
+    u, e, assign = _forced_inputs(w, counts, 2709)
     b = I.make_b(w)
     dev = D.upload(w, "cuda")
     routed, shared = dev["routed"], dev["shared"]
@@ -211,11 +220,11 @@ def test_counts_on_tile_boundaries(ffn):
     got = [to_np(t) for t in (L.expert_count, L.expert_offset, L.sorted_token, L.pair_row)]
     for g_, r_, what in zip(got, want, ("count", "offset", "sorted_token", "pair_row")):
         assert np.array_equal(g_.reshape(r_.shape), r_), what
-    assert np.array_equal(got[0], np.array(COUNTS, np.int32))
+    assert np.array_equal(got[0], np.array(counts, np.int32))
     assert np.array_equal(to_np(bias), oracle.bias_update(want[0], T, 1, w.gamma, b))
 
     mk = _q_host if ffn == "fp8" else (lambda t: t)
-    r_host = {i: mk(I.make_expert(w, False, i)) for i in range(w.n_routed) if COUNTS[i]}
+    r_host = {i: mk(I.make_expert(w, False, i)) for i in range(w.n_routed) if counts[i]}
     s_host = [mk(I.make_expert(w, True, 0))]
     res = oracle.layer(u, e, b, r_host, s_host, top_k=1, d_ff=w.d_ff, act="bf16", ffn=ffn,
                        want_components=True)
@@ -228,18 +237,18 @@ def test_counts_on_tile_boundaries(ffn):
     y_r = (I.bf16_bits_to_f32(y_r) if y_r.dtype == np.uint16 else y_r).astype(np.float64)
     sorted_token = got[2].ravel()
     if ffn == "fp8":
-        _check_fp8_rows(L, w, u, sorted_token, y_r)
+        _check_fp8_rows(L, w, u, sorted_token, y_r, counts)
         return
     h_r, h_s = (to_np(x) for x in _bf16_h(L, w))
-    off = np.concatenate([[0], np.cumsum(COUNTS)])
-    for i, c in enumerate(COUNTS):
+    off = np.concatenate([[0], np.cumsum(counts)])
+    for i, c in enumerate(counts):
         if c:
             h_o, _ = oracle.expert_rows(u[sorted_token[off[i]:off[i + 1]]], *I.make_expert(w, False, i), "bf16")
             _check_bf16_h(h_o, h_r[off[i]:off[i + 1]], f"expert {i} ({c} rows)")
     _check_bf16_h(oracle.expert_rows(u, *I.make_expert(w, True, 0), "bf16")[0], h_s, "shared expert")
     err_r = _row_errors(y_r, res["routed_sum"][sorted_token])
     err_s = _row_errors(to_np(L.y_shared).astype(np.float64), res["shared_sum"])
-    worst = {c: float(err_r[off[i]:off[i + 1]].max()) for i, c in enumerate(COUNTS) if c}
+    worst = {c: float(err_r[off[i]:off[i + 1]].max()) for i, c in enumerate(counts) if c}
     log(f"[tile edges] bf16: worst routed row per count {worst}; worst shared row {err_s.max():.2e}")
     assert err_r.max() <= ROW_TOL and err_s.max() <= ROW_TOL
 

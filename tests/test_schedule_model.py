@@ -7,7 +7,8 @@ under random interleavings of the workgroups, on random and skewed expert loads,
 
 - every (group, row, output-column tile) is computed exactly once;
 - no tile is empty and no tile is taller than the kernel's tile height (320 rows in both
-  phases of the bf16 and the FP8 kernels; 256-row blocks are checked as well);
+  phases of the bf16 and the FP8 kernels, 128 rows in the bf16 kernels for batches of at most
+  128 tokens; 256-row blocks are checked as well);
 - the tile count stays within the bound the workspace is sized for (ffn_max_tiles in
   abi.cpp, counted in 256-row blocks, so it also bounds the taller tiles) and no gang
   reads past its row of slots (slot stride ceil(max/G) + 2);
@@ -23,6 +24,7 @@ import numpy as np
 
 BM = 256   # the row-block size the workspace bound counts in
 GANGS = 8
+SMALL_BATCH = 128  # batches of at most this many tokens: bf16 tiles of 128 rows
 
 
 def tile_map(rows, n_r, rb=BM):
@@ -94,7 +96,10 @@ def run_gangs(tiles, grid, stride, rng):
 
 
 def check(T, top_k, n_r, n_shared, d, d_ff, counts, grid, rng):
-    for phase, rb in ((1, 256), (2, 256), (1, 320), (2, 320)):
+    heights = [(1, 256), (2, 256), (1, 320), (2, 320)]
+    if T <= SMALL_BATCH:
+        heights += [(1, SMALL_BATCH), (2, SMALL_BATCH)]
+    for phase, rb in heights:
         ns_groups = n_shared if phase == 1 else min(n_shared, 1)
         ntn = d_ff // 128 if phase == 1 else d // 256
         rows = list(counts) + [T] * ns_groups
@@ -139,6 +144,19 @@ def test_schedule_random_shapes():
         d_ff = int(rng.choice([128, 1408, 2048]))
         grid = int(rng.choice([64, 256, 264]))
         check(T, top_k, n_r, n_shared, d, d_ff, counts, grid, r)
+
+
+def test_schedule_v3_decode_shape():
+    """128 tokens (the small-batch tiles), 8 hot experts: every group is one 128-row block."""
+    rng = np.random.default_rng(5)
+    r = random.Random(5)
+    p = rng.dirichlet(np.ones(256) * 0.3)  # skewed, but each token picks 8 distinct experts
+    picks = np.concatenate([rng.choice(256, 8, replace=False, p=p) for _ in range(128)])
+    counts = np.bincount(picks, minlength=256)
+    assert counts.max() > 32
+    check(128, 8, 256, 1, 7168, 2048, counts, 256, r)
+    mt, _, _ = tile_map(list(counts) + [128], 256, SMALL_BATCH)
+    assert max(mt) == 1
 
 
 def test_schedule_all_rows_on_few_experts():
