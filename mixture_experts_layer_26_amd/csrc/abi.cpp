@@ -182,7 +182,7 @@ bool backward_shape(const moe_shape* s) {
 }
 
 struct BwdWorkspace {
-  size_t zero, xs, h_r, da_r, dv_r, h_s, da_s, dv_s, a_r, v_r, a_s, v_s, total;
+  size_t sched, zero, xs, h_r, da_r, dv_r, h_s, da_s, dv_s, a_r, v_r, a_s, v_s, total;
 };
 
 BwdWorkspace bwd_workspace(const moe_shape* s) {
@@ -190,6 +190,8 @@ BwdWorkspace bwd_workspace(const moe_shape* s) {
   const size_t pr = static_cast<size_t>(s->T) * s->top_k * s->d_ff * 2;
   const size_t ps = static_cast<size_t>(s->T) * s->n_shared * s->d_ff * 2;
   size_t off = 0;
+  w.sched = off;  // gang-scheduling state of the gate/up launch, sized for the smallest grid
+  off = align_up(off + moe::sched_ints(ffn_max_tiles(s, 1), kMinGemmGrid) * sizeof(int32_t));
   w.zero = off;
   off = align_up(off + 256);
   w.xs = off;
@@ -406,6 +408,41 @@ moe_status grouped_ffn_check(const moe_shape* s, const void* u, const int32_t* e
   return MOE_OK;
 }
 
+// Arguments of the bf16 gate/up GEMM (phase 1): x gathered from u through sorted_token,
+// H into h_r (routed rows, sorted order) and h_s (tokens, N_s * d_ff columns).
+moe::GemmArgs gate_up_args(const moe_shape* s, const void* u, const int32_t* expert_offset,
+                           const int32_t* sorted_token, const moe_expert_set* routed,
+                           const moe_expert_set* shared, uint16_t* h_r, uint16_t* h_s, int b_tiled,
+                           int32_t* sched, int slot_stride) {
+  moe::GemmArgs g{};
+  const uint16_t* ub = static_cast<const uint16_t*>(u);
+  g.a_routed = ub;
+  g.a_shared = ub;
+  g.lda_routed = g.lda_shared = s->d;
+  g.gather = sorted_token;
+  g.b1_routed = static_cast<const uint16_t*>(routed->w1);
+  g.b3_routed = static_cast<const uint16_t*>(routed->w3);
+  g.b1_shared = s->n_shared > 0 ? static_cast<const uint16_t*>(shared->w1) : nullptr;
+  g.b3_shared = s->n_shared > 0 ? static_cast<const uint16_t*>(shared->w3) : nullptr;
+  g.b_expert_stride = static_cast<int64_t>(s->d_ff) * s->d;
+  g.ldb = s->d;
+  g.out_routed = h_r;
+  g.out_shared = h_s;
+  g.ldo_routed = s->d_ff;
+  g.ldo_shared = static_cast<int64_t>(s->n_shared) * s->d_ff;
+  g.offset = expert_offset;
+  g.n_r = s->n_routed;
+  g.n_shared_groups = s->n_shared;
+  g.T = s->T;
+  g.N = s->d_ff;
+  g.K = s->d;
+  g.k_segments = 1;
+  g.sched = sched;
+  g.b_tiled = b_tiled;
+  g.slot_stride = slot_stride;
+  return g;
+}
+
 // The grouped FFN on a checked shape with T > 0 and a workspace of at least
 // ffn_workspace(s).total bytes.
 moe_status grouped_ffn_run(const moe_shape* s, const void* u, const int32_t* expert_offset,
@@ -448,33 +485,8 @@ moe_status grouped_ffn_run(const moe_shape* s, const void* u, const int32_t* exp
                                   wsb, w, sc, grid, b_tiled, st);
   uint16_t* h_r = reinterpret_cast<uint16_t*>(wsb + w.h_routed);
   uint16_t* h_s = reinterpret_cast<uint16_t*>(wsb + w.h_shared);
-  const uint16_t* ub = static_cast<const uint16_t*>(u);
-
-  moe::GemmArgs g1{};
-  g1.a_routed = ub;
-  g1.a_shared = ub;
-  g1.lda_routed = g1.lda_shared = s->d;
-  g1.gather = sorted_token;
-  g1.b1_routed = static_cast<const uint16_t*>(routed->w1);
-  g1.b3_routed = static_cast<const uint16_t*>(routed->w3);
-  g1.b1_shared = s->n_shared > 0 ? static_cast<const uint16_t*>(shared->w1) : nullptr;
-  g1.b3_shared = s->n_shared > 0 ? static_cast<const uint16_t*>(shared->w3) : nullptr;
-  g1.b_expert_stride = static_cast<int64_t>(s->d_ff) * s->d;
-  g1.ldb = s->d;
-  g1.out_routed = h_r;
-  g1.out_shared = h_s;
-  g1.ldo_routed = s->d_ff;
-  g1.ldo_shared = static_cast<int64_t>(s->n_shared) * s->d_ff;
-  g1.offset = expert_offset;
-  g1.n_r = s->n_routed;
-  g1.n_shared_groups = s->n_shared;
-  g1.T = s->T;
-  g1.N = s->d_ff;
-  g1.K = s->d;
-  g1.k_segments = 1;
-  g1.sched = sc.s1;
-  g1.b_tiled = b_tiled;
-  g1.slot_stride = sc.stride1;
+  const moe::GemmArgs g1 =
+      gate_up_args(s, u, expert_offset, sorted_token, routed, shared, h_r, h_s, b_tiled, sc.s1, sc.stride1);
   hipError_t err = moe::launch_grouped_gemm_bf16(g1, true, grid, st);
   if (err != hipSuccess) return MOE_ERR_HIP;
 
@@ -619,7 +631,7 @@ moe_status moe_grouped_ffn_backward(const moe_shape* s, const void* u, const voi
         !d_shared->dw1 || !d_shared->dw3 || !d_shared->dw2)
       return MOE_ERR_INVALID_ARG;
   }
-  if (!backward_shape(s)) return MOE_ERR_UNSUPPORTED;
+  if (!backward_shape(s) || !gemm_offsets_fit(s)) return MOE_ERR_UNSUPPORTED;
   if (routed->layout != MOE_LAYOUT_ROWS || (s->n_shared > 0 && shared->layout != MOE_LAYOUT_ROWS))
     return MOE_ERR_UNSUPPORTED;
   if (s->T == 0) {  // no rows: every weight gradient is zero
@@ -682,7 +694,21 @@ moe_status moe_grouped_ffn_backward(const moe_shape* s, const void* u, const voi
   a.F = s->d_ff;
   a.n_r = s->n_routed;
   a.n_s = s->n_shared;
-  return from_hip(moe::launch_ffn_backward(a, as_stream(stream)));
+  // a, v (fp32) and h (bf16) from the forward's gate/up GEMM, then the rest of the backward
+  hipStream_t st = as_stream(stream);
+  const int grid = gemm_grid();
+  const int64_t t1 = ffn_max_tiles(s, 1);
+  if (t1 > INT32_MAX / 2) return MOE_ERR_UNSUPPORTED;
+  int32_t* sched = reinterpret_cast<int32_t*>(wsb + w.sched);
+  if (moe::launch_zero_i32(sched, static_cast<int>(moe::sched_ints(t1, grid)), st) != hipSuccess) return MOE_ERR_HIP;
+  moe::GemmArgs g1 = gate_up_args(s, u, expert_offset, sorted_token, routed, shared, a.h_r, a.h_s, 0, sched,
+                                  static_cast<int>(moe::sched_slot_stride(t1, grid)));
+  g1.pre_gate_routed = a.a_r;
+  g1.pre_up_routed = a.v_r;
+  g1.pre_gate_shared = a.a_s;
+  g1.pre_up_shared = a.v_s;
+  if (moe::launch_grouped_gemm_bf16(g1, true, grid, st) != hipSuccess) return MOE_ERR_HIP;
+  return from_hip(moe::launch_ffn_backward(a, st));
 }
 
 moe_status moe_route_backward(const moe_shape* s, const void* u, const void* centroids, const int32_t* topk_idx,

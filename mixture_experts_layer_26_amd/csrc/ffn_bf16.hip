@@ -466,6 +466,28 @@ __global__ __launch_bounds__(kThreads) void grouped_gemm_bf16(GemmArgs args) {
           st16(dst + t.n0 + 8 * ch, val);
         }
       }
+      if constexpr (GATED) {
+        // the pre-activations a and v in fp32 when asked for (the backward), straight from
+        // the accumulators: lane column 32 wn + col_in, 128 contiguous bytes per row
+        float* pa = routed ? args.pre_gate_routed : args.pre_gate_shared;
+        float* pv = routed ? args.pre_up_routed : args.pre_up_shared;
+        if (pa != nullptr) {
+          const int64_t ld = routed ? args.ldo_routed : args.ldo_shared;
+          const int64_t col = t.n0 + 32 * wn + col_in + (routed ? 0 : static_cast<int64_t>(sg) * args.N);
+#pragma unroll
+          for (int mb = 0; mb < kMB; ++mb) {
+            if (mb >= vblk) continue;
+#pragma unroll
+            for (int v = 0; v < 16; ++v) {
+              const int i = GR * g + 32 * mb + 8 * (v / 4) + 4 * (lane / 32) + (v % 4);
+              if (i >= t.rows) continue;
+              const int64_t o = ((routed ? row_base : 0) + t.m0 + i) * ld + col;
+              pa[o] = acc[mb][0][v];
+              pv[o] = acc[mb][1][v];
+            }
+          }
+        }
+      }
     } else {
       // fp32 shared-expert sum: direct stores
 #pragma unroll

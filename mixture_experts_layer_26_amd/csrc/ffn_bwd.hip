@@ -6,12 +6,11 @@
 // gradient dY, a = X W1^T, v = X W3^T, h = SiLU(a) v and y = h W2^T:
 //   dh = dY W2,  da = dh v SiLU'(a),  dv = dh SiLU(a),  dX = da W1 + dv W3,
 //   dW1 = da^T X,  dW3 = dv^T X,  dW2 = dY^T h.
-// Five launches, each a grid of output tiles (v_mfma_f32_32x32x16_bf16, each wave a grid
-// of 32 x 32 blocks), K through a ring of LDS stages filled by global_load_lds_dwordx4
-// (no staging registers):
-//   kAV:     256 rows x 128 d_ff tiles on 8 waves, K = d in steps of 64: a and v in two
-//            accumulators; the epilogue stores h (bf16, as the forward forms it) and a, v
-//            (fp32, for the next launch).
+// a, v and h come from the forward's gate/up GEMM (ffn_bf16.hip), which also stores a and
+// v in fp32 when asked to; h is then bit for bit the forward's. Then four launches here,
+// each a grid of output tiles (v_mfma_f32_32x32x16_bf16, each wave a grid of 32 x 32
+// blocks), K through a ring of LDS stages filled by global_load_lds_dwordx4 (no staging
+// registers):
 //   kDh:     256 rows x 256 d_ff tiles on 8 waves (128 d_ff when d_ff % 256 != 0), K = d in
 //            steps of 64: dh; the epilogue reads a and v and stores da and dv in bf16.
 //   kDx:     256 rows x 256 d tiles on 8 waves, K = d_ff in steps of 32 (the shared
@@ -24,8 +23,8 @@
 // ends of short K loops.
 // The routed rows of X are read from a sorted copy of u (gathered once per call), so no
 // index lookups sit in the K loops.
-// Operands whose K is contiguous in memory (X in kAV, dY in kDh, da, dv in kDx, the rows
-// of W1/W3 in kAV) are staged as [rows][BK k] and read with ds_read_b128. Operands
+// Operands whose K is contiguous in memory (dY in kDh, da, dv in kDx) are staged as
+// [rows][BK k] and read with ds_read_b128. Operands
 // whose K runs across rows (W2 in kDh, W1/W3 in kDx, everything in the weight
 // gradients) are staged as they lie, [BK k][columns], and read with
 // ds_read_b64_tr_b16, which hands each lane four consecutive k of one column: within
@@ -39,9 +38,9 @@ namespace moe {
 
 namespace {
 
-enum { kDx = 1, kDw13 = 2, kDw2 = 3, kAV = 4, kDh = 5, kDh128 = 6 };
+enum { kDx = 1, kDw13 = 2, kDw2 = 3, kDh = 5, kDh128 = 6 };
 // modes whose row tiles span d_ff columns, one group per shared expert
-template <int MODE> constexpr bool kRowsByFf = MODE == kAV || MODE == kDh || MODE == kDh128;
+template <int MODE> constexpr bool kRowsByFf = MODE == kDh || MODE == kDh128;
 
 // Per mode: NA A operands (M side) and NB B operands (N side) with their K-major flags;
 // NACC accumulators; a WM x WN grid of waves, each NMB x NNB blocks of 32 x 32, so the
@@ -50,11 +49,6 @@ template <int MODE> constexpr bool kRowsByFf = MODE == kAV || MODE == kDh || MOD
 // flight); BK: K per step. Operands whose K runs along their rows take whole 128-byte
 // lines per row with BK = 64; with BK = 32 each line is requested twice, a step apart.
 template <int MODE> struct Cfg;
-template <> struct Cfg<kAV> {  // A: X (K-contiguous); B: W1, W3 (K-contiguous)
-  static constexpr int NA = 1, NB = 2, NACC = 2, WM = 4, WN = 2, NMB = 2, NNB = 2, kOcc = 2, NST = 2, BK = 64;
-  static constexpr bool a_km = false;
-  static constexpr bool b_km(int) { return false; }
-};
 template <> struct Cfg<kDh> {  // A: dY (K-contiguous); B: W2 (K-major)
   static constexpr int NA = 1, NB = 1, NACC = 1, WM = 2, WN = 4, NMB = 4, NNB = 2, kOcc = 2, NST = 2, BK = 64;
   static constexpr bool a_km = false;
@@ -133,11 +127,11 @@ __device__ __forceinline__ bf16x8 frag_km(const unsigned char* t, int c0, int s,
 // blocks of one expert) run on one XCD and share its L2, while the tiles -- real ones and
 // the empty ones at the end of an upper-bound grid alike -- spread evenly over the XCDs.
 // The grid is a multiple of 256, so this is a permutation of the tile indices.
-// Measured per launch at V3 prefill, it helps the a/v (6.89 -> 6.78 ms), dh (3.70 -> 3.57)
-// and dW2 (4.71 -> 4.48) launches and hurts dW1/dW3 (9.06 -> 9.49); dX is unchanged. The
-// launches that gain use it.
+// Measured per launch at V3 prefill, it helped the dh (3.70 -> 3.57 ms) and dW2 (4.71 ->
+// 4.48) launches (and the a/v launch these kernels had then) and hurt dW1/dW3 (9.06 ->
+// 9.49); dX was unchanged. The launches that gain use it.
 constexpr int kChunk = 32;
-template <int MODE> constexpr bool kChunked = MODE == kAV || MODE == kDh || MODE == kDh128 || MODE == kDw2;
+template <int MODE> constexpr bool kChunked = MODE == kDh || MODE == kDh128 || MODE == kDw2;
 template <int MODE>
 __device__ __forceinline__ int chunked_tile(int b) {
   if constexpr (!kChunked<MODE>) return b;
@@ -153,13 +147,13 @@ struct Ctx {
   int64_t row0;   // first row of the group in the routed row space (routed) or 0 (shared)
   int rows;       // rows of the group (kDw*: the K extent) or valid rows of the tile (row-tile modes)
   int64_t m0;     // tile's first row within the group (row-tile modes), else 0
-  int c0;         // tile's first output column (kAV, kDh: d_ff; kDx: d)
+  int c0;         // tile's first output column (kDh: d_ff; kDx: d)
   int mo, no;     // kDw*: tile's first output row / column
   int nk;         // K-steps
 };
 
-// Row tiles of kAV / kDh / kDx: groups are the routed experts, then the shared groups
-// (kAV, kDh: each shared expert; kDx: one group for all of them). The offsets are copied
+// Row tiles of kDh / kDx: groups are the routed experts, then the shared groups (kDh:
+// each shared expert; kDx: one group for all of them). The offsets are copied
 // to LDS (soff, n_r + 1 entries) and one thread walks the groups. Returns false past
 // the last tile.
 template <int MODE>
@@ -205,17 +199,7 @@ template <int MODE>
 __device__ __forceinline__ const uint16_t* src(const BwdArgs& a, const Ctx& c, bool is_a, int op, int x, int y,
                                                int kt) {
   const int64_t F = a.F, d = a.d;
-  if constexpr (MODE == kAV) {
-    if (is_a) {  // X (sorted copy), row x of the tile, k = BK kt + 8 y
-      const int64_t row = c.m0 + (x < c.rows ? x : c.rows - 1);
-      const int64_t k = static_cast<int64_t>(Cfg<MODE>::BK) * kt + 8 * y;
-      return c.shared ? a.u + row * d + k : a.xs + (c.row0 + row) * d + k;
-    }
-    // W1 / W3 row c0 + x, k contiguous
-    const int e = c.shared ? c.g - a.n_r : c.g;
-    const uint16_t* w = c.shared ? (op == 0 ? a.w1s : a.w3s) : (op == 0 ? a.w1r : a.w3r);
-    return w + static_cast<int64_t>(e) * F * d + (c.c0 + x) * d + static_cast<int64_t>(Cfg<MODE>::BK) * kt + 8 * y;
-  } else if constexpr (MODE == kDh || MODE == kDh128) {
+  if constexpr (MODE == kDh || MODE == kDh128) {
     if (is_a) {  // dY, row x of the tile, k = BK kt + 8 y
       const int64_t row = c.m0 + (x < c.rows ? x : c.rows - 1);
       const int64_t k = static_cast<int64_t>(Cfg<MODE>::BK) * kt + 8 * y;
@@ -361,10 +345,7 @@ __device__ __forceinline__ void compute(const unsigned char* base,
       for (int nb = 0; nb < NNB; ++nb) {
         // the n-side fragment goes first, so each lane's accumulator holds 4 consecutive
         // output columns of one output row (see the epilogue)
-        if constexpr (MODE == kAV) {
-          acc[0][mb][nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fb[0][nb], fa[0][mb], acc[0][mb][nb], 0, 0, 0);
-          acc[1][mb][nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fb[1][nb], fa[0][mb], acc[1][mb][nb], 0, 0, 0);
-        } else if constexpr (MODE == kDx) {
+        if constexpr (MODE == kDx) {
           acc[0][mb][nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fb[0][nb], fa[0][mb], acc[0][mb][nb], 0, 0, 0);
           acc[0][mb][nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fb[1][nb], fa[1][mb], acc[0][mb][nb], 0, 0, 0);
         } else if constexpr (MODE == kDw13) {
@@ -462,22 +443,7 @@ __global__ __launch_bounds__(64 * kWaves<MODE>, Cfg<MODE>::kOcc) void ffn_bwd_ke
             o = row * (a.n_s * static_cast<int64_t>(a.F)) + static_cast<int64_t>(c.g - a.n_r) * a.F + col;
           else
             o = (c.row0 + row) * a.F + col;
-          if constexpr (MODE == kAV) {  // h = SiLU(a) v as the forward forms it; a, v kept in fp32
-            float hv[4];
-#pragma unroll
-            for (int q = 0; q < 4; ++q) {
-              const float av = acc[0][mb][nb][4 * p + q], vv = acc[1][mb][nb][4 * p + q];
-              hv[q] = av * fast_sigmoid(av) * vv;
-            }
-            *reinterpret_cast<uint2*>((c.shared ? a.h_s : a.h_r) + o) =
-                make_uint2(pack_bf16x2(hv[0], hv[1]), pack_bf16x2(hv[2], hv[3]));
-            const f32x16& x0 = acc[0][mb][nb];
-            const f32x16& x1 = acc[1][mb][nb];
-            *reinterpret_cast<float4*>((c.shared ? a.a_s : a.a_r) + o) =
-                make_float4(x0[4 * p], x0[4 * p + 1], x0[4 * p + 2], x0[4 * p + 3]);
-            *reinterpret_cast<float4*>((c.shared ? a.v_s : a.v_r) + o) =
-                make_float4(x1[4 * p], x1[4 * p + 1], x1[4 * p + 2], x1[4 * p + 3]);
-          } else {  // da = dh v SiLU'(a), dv = dh SiLU(a)
+          {  // da = dh v SiLU'(a), dv = dh SiLU(a)
             const float4 a4 = *reinterpret_cast<const float4*>((c.shared ? a.a_s : a.a_r) + o);
             const float4 v4 = *reinterpret_cast<const float4*>((c.shared ? a.v_s : a.v_r) + o);
             const float aa[4] = {a4.x, a4.y, a4.z, a4.w}, vv4[4] = {v4.x, v4.y, v4.z, v4.w};
@@ -569,7 +535,6 @@ hipError_t launch_ffn_backward(const BwdArgs& a, hipStream_t stream) {
                      a.T * a.K, a.d);
   hipError_t err = hipGetLastError();
   if (err != hipSuccess) return err;
-  if ((err = launch_rows<kAV>(a, stream)) != hipSuccess) return err;
   if ((err = (a.F % kTN<kDh> == 0 ? launch_rows<kDh>(a, stream) : launch_rows<kDh128>(a, stream))) != hipSuccess)
     return err;
   if ((err = launch_rows<kDx>(a, stream)) != hipSuccess) return err;

@@ -35,6 +35,13 @@ struct GemmArgs {
   int k_segments;            // phase 2 shared: n_s
   int* sched;                // zeroed gang-scheduling state: 1 + kGangs * slot_stride ints
   int slot_stride;           // slots per gang (> tiles / (grid / kGangs))
+  // bf16 phase 1 only, optional (nullptr: not stored): the pre-activations a = x W1^T and
+  // v = x W3^T in fp32, laid out as H (routed [P][ldo_routed], shared [T][ldo_shared] at
+  // column s * N); the backward reads them
+  float* pre_gate_routed;
+  float* pre_up_routed;
+  float* pre_gate_shared;
+  float* pre_up_shared;
 };
 
 // Tile scheduling of the grouped GEMMs: workgroup b belongs to gang b % kGangs (one
