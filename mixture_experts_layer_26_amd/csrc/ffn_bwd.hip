@@ -262,7 +262,23 @@ __device__ __forceinline__ void dma16(const void* gptr, const unsigned char* lds
   asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(gptr), "s"(m0)
                : "memory", "m0");
 }
+
+// The same in the SGPR-base form: lane i copies the 16 bytes at sbase + voff (sbase
+// wave-uniform, voff the lane's 32-bit byte offset).
+__device__ __forceinline__ void dma16s(uint32_t voff, const unsigned char* sbase, const unsigned char* lds) {
+  const uint32_t m0 = static_cast<uint32_t>(reinterpret_cast<uintptr_t>((lds_ptr)(lds)));
+  asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1" ::"v"(voff), "s"(sbase), "s"(m0)
+               : "memory", "m0");
+}
 #pragma clang diagnostic pop
+
+// A wave-uniform pointer made explicit (both halves from the first lane), for dma16s.
+__device__ __forceinline__ const unsigned char* uniform_ptr(const void* p) {
+  const uint64_t v = reinterpret_cast<uint64_t>(p);
+  const uint64_t lo = static_cast<uint32_t>(__builtin_amdgcn_readfirstlane(static_cast<uint32_t>(v)));
+  const uint64_t hi = static_cast<uint32_t>(__builtin_amdgcn_readfirstlane(static_cast<uint32_t>(v >> 32)));
+  return reinterpret_cast<const unsigned char*>((hi << 32) | lo);
+}
 
 // Loads of K-step kt into one stage: each operand's tile is split evenly over the waves,
 // 64 16-byte slots per instruction (slot = per-wave share * w + 64 i + lane). The lane
@@ -291,6 +307,97 @@ __device__ __forceinline__ void dma_step(const BwdArgs& a, const Ctx& c, int kt,
       }
       dma16(src<MODE>(a, c, op < NA, op < NA ? op : op - NA, x, y, kt),
             stage + op_offset<MODE>(op) + (per_wave * w + 64 * i) * 16);
+    }
+  }
+}
+
+// Loads of the weight-gradient launches (every operand K-major, K = the group's rows).
+// Per operand: a wave-uniform pointer to K-row 0 of the tile's columns and the bytes from
+// one K-row to the next; per lane and instruction: the 32-bit byte offset of its 16 bytes
+// (K-row x, column y of the step, chosen as in dma_step). A step moves the pointers by BK
+// K-rows with scalar arithmetic, so the K loop spends no VALU work on addresses. Only a
+// step that runs past the group's rows (its last) checks rows, lane by lane, and sends
+// the lanes past them to the zeroed 16 bytes at a.zero.
+template <int MODE>
+constexpr int dw_instrs(int op) {
+  return op_bytes<MODE>(op) / 16 / kWaves<MODE> / 64;
+}
+template <int MODE>
+struct DwLoads {
+  static constexpr int NOP = Cfg<MODE>::NA + Cfg<MODE>::NB;
+  const unsigned char* base[NOP];  // wave-uniform
+  int64_t row_bytes[NOP];
+  uint32_t off[NOP][4];
+};
+
+// (x, y) of slot `slot` of a K-major operand `width` columns wide.
+__device__ __forceinline__ void km_slot(int slot, int width, int& x, int& y) {
+  const int spr = width / 8;
+  x = slot / spr;
+  const int ws = slot % spr;
+  y = (((ws / 4) ^ (x & 3)) * 32) + (ws % 4) * 8;
+}
+
+template <int MODE>
+__device__ __forceinline__ void dw_setup(const BwdArgs& a, const Ctx& c, int w, int lane, DwLoads<MODE>& L) {
+  constexpr int NA = Cfg<MODE>::NA, NOP = DwLoads<MODE>::NOP, NW = kWaves<MODE>;
+  const int64_t F = a.F, d = a.d, sF = static_cast<int64_t>(a.n_s) * a.F;
+  const int64_t s = c.shared ? c.g - a.n_r : 0;
+#pragma unroll
+  for (int op = 0; op < NOP; ++op) {
+    const uint16_t* p;
+    int64_t ld;
+    if constexpr (MODE == kDw13) {
+      if (op < NA) {  // da / dv, columns mo.. (d_ff)
+        ld = c.shared ? sF : F;
+        p = c.shared ? (op == 0 ? a.da_s : a.dv_s) + s * F + c.mo : (op == 0 ? a.da_r : a.dv_r) + c.row0 * F + c.mo;
+      } else {  // X, columns no.. (d)
+        ld = d;
+        p = c.shared ? a.u + c.no : a.xs + c.row0 * d + c.no;
+      }
+    } else {
+      if (op < NA) {  // dY, columns mo.. (d)
+        ld = d;
+        p = c.shared ? a.dout + c.mo : a.dy_routed + c.row0 * d + c.mo;
+      } else {  // h, columns no.. (d_ff)
+        ld = c.shared ? sF : F;
+        p = c.shared ? a.h_s + s * F + c.no : a.h_r + c.row0 * F + c.no;
+      }
+    }
+    L.base[op] = uniform_ptr(p);
+    L.row_bytes[op] = 2 * ld;
+    const int width = op < NA ? kTM<MODE> : kTN<MODE>;
+    const int per_wave = op_bytes<MODE>(op) / 16 / NW;
+#pragma unroll
+    for (int i = 0; i < dw_instrs<MODE>(op); ++i) {
+      int x, y;
+      km_slot(per_wave * w + 64 * i + lane, width, x, y);
+      L.off[op][i] = static_cast<uint32_t>(x * 2 * ld + 2 * y);
+    }
+  }
+}
+
+template <int MODE>
+__device__ __forceinline__ void dw_step(const BwdArgs& a, const Ctx& c, const DwLoads<MODE>& L, int kt,
+                                        unsigned char* stage, int w, int lane) {
+  constexpr int NA = Cfg<MODE>::NA, NOP = DwLoads<MODE>::NOP, BK = Cfg<MODE>::BK, NW = kWaves<MODE>;
+  const bool full = (kt + 1) * BK <= c.rows;  // wave-uniform
+#pragma unroll
+  for (int op = 0; op < NOP; ++op) {
+    const unsigned char* sb = L.base[op] + static_cast<int64_t>(kt) * BK * L.row_bytes[op];
+    const int width = op < NA ? kTM<MODE> : kTN<MODE>;
+    const int per_wave = op_bytes<MODE>(op) / 16 / NW;
+#pragma unroll
+    for (int i = 0; i < dw_instrs<MODE>(op); ++i) {
+      unsigned char* dst = stage + op_offset<MODE>(op) + (per_wave * w + 64 * i) * 16;
+      if (full) {
+        dma16s(L.off[op][i], sb, dst);
+      } else {
+        int x, y;
+        km_slot(per_wave * w + 64 * i + lane, width, x, y);
+        dma16(kt * BK + x < c.rows ? static_cast<const void*>(sb + L.off[op][i]) : static_cast<const void*>(a.zero),
+              dst);
+      }
     }
   }
 }
@@ -406,18 +513,28 @@ __global__ __launch_bounds__(64 * kWaves<MODE>, Cfg<MODE>::kOcc) void ffn_bwd_ke
 #pragma unroll
         for (int v = 0; v < 16; ++v) acc[x][mb][nb][v] = 0.0f;
 
+  constexpr bool kDw = MODE == kDw13 || MODE == kDw2;
+  DwLoads<MODE> dl;
+  if constexpr (kDw) dw_setup<MODE>(a, c, w, lane, dl);
+  auto issue = [&](int kt, unsigned char* st) {
+    if constexpr (kDw)
+      dw_step<MODE>(a, c, dl, kt, st, w, lane);
+    else
+      dma_step<MODE>(a, c, kt, st, w, lane);
+  };
+
   // load ring: steps 0 .. NST - 2 first; at step kt, once step kt has landed, the load of
   // step kt + NST - 1 goes into the stage step kt - 1 was read from (every wave is past
   // that read: it came before the barrier)
 #pragma unroll
   for (int s0 = 0; s0 < NST - 1; ++s0)
-    if (s0 < c.nk) dma_step<MODE>(a, c, s0, lds + s0 * kStage, w, lane);
+    if (s0 < c.nk) issue(s0, lds + s0 * kStage);
   for (int kt = 0; kt < c.nk; ++kt) {
     if (NST == 3 && kt + 1 < c.nk)
       ring_wait<ND>();  // step kt + 1's loads may stay in flight
     else
       ring_wait<0>();
-    if (kt + NST - 1 < c.nk) dma_step<MODE>(a, c, kt + NST - 1, lds + ((kt + NST - 1) % NST) * kStage, w, lane);
+    if (kt + NST - 1 < c.nk) issue(kt + NST - 1, lds + ((kt + NST - 1) % NST) * kStage);
     compute<MODE>(lds + (kt % NST) * kStage, acc, wm, wn, lane);
   }
 
