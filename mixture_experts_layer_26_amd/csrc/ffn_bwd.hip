@@ -550,7 +550,8 @@ __global__ __launch_bounds__(64 * kWaves<MODE>, Cfg<MODE>::kOcc) void ffn_bwd_ke
     // from 9.1 to 5.4 ms and dW2 from 4.5 to 2.5 ms at V3 prefill). The bf16 tiles of the
     // NACC outputs go into the free ring, rows padded by 16 bytes (row m's banks shift by
     // 4 per row, so a write's 32 rows meet at most in pairs), then whole rows go out with
-    // 16-byte stores, TN / 8 lanes per row.
+    // 16-byte stores, TN / 8 lanes per row. The stores are non-temporal: nothing in this
+    // launch reads the gradients back (6.8 and 3.4 ms instead of 7.0 and 3.5).
     constexpr int kPitch = 2 * TN + 16;
     static_assert(NACC * TM * kPitch <= NST * kStage, "the output tiles fit in the ring");
     __syncthreads();  // every wave is past its last read of the ring
@@ -581,7 +582,8 @@ __global__ __launch_bounds__(64 * kWaves<MODE>, Cfg<MODE>::kOcc) void ffn_bwd_ke
       out += e * M * N + static_cast<int64_t>(c.mo) * N + c.no;
       for (int idx = threadIdx.x; idx < TM * (TN / 8); idx += 64 * kWaves<MODE>) {
         const int r = idx / (TN / 8), ch = idx % (TN / 8);
-        st16(out + r * N + 8 * ch, *reinterpret_cast<const uint4*>(lds + (x * TM + r) * kPitch + 16 * ch));
+        __builtin_nontemporal_store(*reinterpret_cast<const i32x4*>(lds + (x * TM + r) * kPitch + 16 * ch),
+                                    reinterpret_cast<i32x4*>(out + r * N + 8 * ch));
       }
     }
     return;
