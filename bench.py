@@ -18,9 +18,11 @@ after it in the same run and appear under "workloads", each with its own rooflin
 and oracle baseline.
 
 --backward times the layer backward instead (moe_combine_backward ->
-moe_grouped_ffn_backward -> moe_route_backward after one forward step, row-major bf16
-weights) and prints its own line, with the roofline of the grouped FFN backward (five
-MFMA launches: 16 d d_ff FLOPs per expert row).
+moe_grouped_ffn_backward -> moe_route_backward after one forward step, bf16 weights in
+the --backward-layout given, row-major by default: its dX launch reads the weights along
+their columns, which row-major rows serve better, and the tiled layout was 0.5 ms slower
+at V3 prefill) and prints its own line, with the roofline of the grouped FFN backward
+(five MFMA launches: 16 d d_ff FLOPs per expert row).
 
 --balance S runs S layer steps over fresh token batches with the bias carried from step
 to step (the end-of-step rule of the method) and prints the max/mean and min/mean expert
@@ -63,6 +65,8 @@ def parse():
     p.add_argument("--cpu-tokens", type=int, default=0, help="oracle sample size (0 = auto)")
     p.add_argument("--layout", choices=["tiled", "rows"], default="tiled",
                    help="expert weight layout: tiled (packed once at setup by moe_pack_weights) or row-major")
+    p.add_argument("--backward-layout", choices=["tiled", "rows"], default="rows",
+                   help="expert weight layout of --backward (the gradients come out in the same layout)")
     p.add_argument("--backward", action="store_true", help="time the layer backward instead")
     p.add_argument("--balance", type=int, default=0, metavar="S",
                    help="run S steps over fresh batches and report the expert loads instead")
@@ -366,7 +370,7 @@ def bench_backward(args):
     from mixture_experts_layer_26_amd import abi
     from mixture_experts_layer_26_amd import inputs as I
 
-    w, dev, L, layout = setup(args.workload, "rows")
+    w, dev, L, layout = setup(args.workload, args.backward_layout)
     assert w.act == "bf16" and w.ffn == "bf16", "the backward runs bf16 layers"
     stream = torch.cuda.current_stream()
     L.route(dev["u"], dev["e"], dev["b"], stream)

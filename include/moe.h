@@ -240,14 +240,17 @@ moe_status moe_pack_weights(const moe_shape* shape, int32_t matrix, int64_t n_ex
  * Backward (gradients of L = sum dout . h' with the routing held fixed; the selection is
  * piecewise constant, and the bias only selects, so it has no gradient). Gradients are
  * bf16 ("gradients in BF16", quantisation section of deepseekmodel.com): GEMM operands
- * bf16, fp32 accumulation, each gradient rounded once. Needs act = ffn = MOE_BF16, the
- * ROWS weight layout, d % 256 == 0 and d_ff % 128 == 0, and the size limits of the bf16
- * moe_grouped_ffn (its gate/up GEMM recomputes a, v and h here), else MOE_ERR_UNSUPPORTED.
+ * bf16, fp32 accumulation, each gradient rounded once. Needs act = ffn = MOE_BF16,
+ * d % 256 == 0 and d_ff % 128 == 0, and the size limits of the bf16 moe_grouped_ffn (its
+ * gate/up GEMM recomputes a, v and h here), else MOE_ERR_UNSUPPORTED. The weights may be in
+ * either layout (the same for routed and shared, else MOE_ERR_INVALID_ARG); the weight
+ * gradients are written in the weights' layout, so an elementwise optimiser step applies to
+ * TILED weights as it is. Both layouts give bit-identical results.
  * The order of the three calls: moe_combine_backward, moe_grouped_ffn_backward,
  * moe_route_backward. */
 
-/* Weight gradients of one expert kind, bf16, in the weight layouts:
- *   dw1, dw3 [E, d_ff, d]; dw2 [E, d, d_ff] */
+/* Weight gradients of one expert kind, bf16, in the layout of the weights they belong to
+ * (ROWS: dw1, dw3 [E, d_ff, d], dw2 [E, d, d_ff]; TILED: as moe_pack_weights makes them). */
 typedef struct {
   void *dw1, *dw3, *dw2;
 } moe_expert_grads;

@@ -176,7 +176,8 @@ FfnWorkspace ffn_workspace(const moe_shape* s) {
   return w;
 }
 
-// Backward: shapes it runs (bf16, row-major weights, 128-multiples) and its workspaces.
+// Backward: shapes it runs (bf16, either weight layout, d % 256 == 0, d_ff % 128 == 0) and its
+// workspaces.
 bool backward_shape(const moe_shape* s) {
   return s->act == MOE_BF16 && s->ffn == MOE_BF16 && s->d % 256 == 0 && s->d_ff % 128 == 0 && s->top_k <= 16;
 }
@@ -632,9 +633,10 @@ moe_status moe_grouped_ffn_backward(const moe_shape* s, const void* u, const voi
       return MOE_ERR_INVALID_ARG;
   }
   if (!backward_shape(s) || !gemm_offsets_fit(s)) return MOE_ERR_UNSUPPORTED;
-  if (routed->layout != MOE_LAYOUT_ROWS || (s->n_shared > 0 && shared->layout != MOE_LAYOUT_ROWS))
-    return MOE_ERR_UNSUPPORTED;
-  if (s->T == 0) {  // no rows: every weight gradient is zero
+  if (routed->layout != MOE_LAYOUT_ROWS && routed->layout != MOE_LAYOUT_TILED) return MOE_ERR_INVALID_ARG;
+  if (s->n_shared > 0 && shared->layout != routed->layout) return MOE_ERR_INVALID_ARG;
+  const int tiled = routed->layout == MOE_LAYOUT_TILED ? 1 : 0;
+  if (s->T == 0) {  // no rows: every weight gradient is zero (in either layout)
     const size_t m = sizeof(uint16_t) * s->d * s->d_ff;  // one weight matrix
     hipStream_t st = as_stream(stream);
     hipError_t e = hipSuccess;
@@ -694,6 +696,7 @@ moe_status moe_grouped_ffn_backward(const moe_shape* s, const void* u, const voi
   a.F = s->d_ff;
   a.n_r = s->n_routed;
   a.n_s = s->n_shared;
+  a.tiled = tiled;
   // a, v (fp32) and h (bf16) from the forward's gate/up GEMM, then the rest of the backward
   hipStream_t st = as_stream(stream);
   const int grid = gemm_grid();
@@ -701,7 +704,7 @@ moe_status moe_grouped_ffn_backward(const moe_shape* s, const void* u, const voi
   if (t1 > INT32_MAX / 2) return MOE_ERR_UNSUPPORTED;
   int32_t* sched = reinterpret_cast<int32_t*>(wsb + w.sched);
   if (moe::launch_zero_i32(sched, static_cast<int>(moe::sched_ints(t1, grid)), st) != hipSuccess) return MOE_ERR_HIP;
-  moe::GemmArgs g1 = gate_up_args(s, u, expert_offset, sorted_token, routed, shared, a.h_r, a.h_s, 0, sched,
+  moe::GemmArgs g1 = gate_up_args(s, u, expert_offset, sorted_token, routed, shared, a.h_r, a.h_s, tiled, sched,
                                   static_cast<int>(moe::sched_slot_stride(t1, grid)));
   g1.pre_gate_routed = a.a_r;
   g1.pre_up_routed = a.v_r;

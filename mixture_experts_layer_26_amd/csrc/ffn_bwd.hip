@@ -190,6 +190,14 @@ __device__ bool decode_row_tile(const BwdArgs& a, int id, Ctx& c, int* sh, int* 
   return true;
 }
 
+// Element offset of (n, k) in one expert's matrix of row length K in the tiled layout of
+// pack.hip, [N/R][K/64][R][64]: R = 128 for W1 and W3 (rows n over d_ff), 256 for W2 (rows
+// over d). Eight consecutive k from a multiple of 8 stay within one 64-wide block.
+template <int R>
+__device__ __forceinline__ int64_t tiled_off(int64_t n, int64_t k, int64_t K) {
+  return ((n / R) * (K / 64) + k / 64) * (R * 64) + (n % R) * 64 + k % 64;
+}
+
 // Global address of the 16 bytes one lane copies for operand op at K-step kt.
 // K-contiguous operands: (x, y) = (tile row, 8-element chunk of the step's BK k); rows past
 // the tile's rows repeat its last row (they feed only outputs that are not stored).
@@ -207,9 +215,9 @@ __device__ __forceinline__ const uint16_t* src(const BwdArgs& a, const Ctx& c, b
     }
     // W2 [d][d_ff]: K-row BK kt + x, columns c0 + y
     const int e = c.shared ? c.g - a.n_r : c.g;
-    const uint16_t* w = c.shared ? a.w2s : a.w2r;
+    const uint16_t* w = (c.shared ? a.w2s : a.w2r) + static_cast<int64_t>(e) * d * F;
     const int64_t k = static_cast<int64_t>(Cfg<MODE>::BK) * kt + x;
-    return w + static_cast<int64_t>(e) * d * F + k * F + c.c0 + y;
+    return w + (a.tiled ? tiled_off<256>(k, c.c0 + y, F) : k * F + c.c0 + y);
   } else if constexpr (MODE == kDx) {
     const int64_t kk = static_cast<int64_t>(Cfg<MODE>::BK) * kt;  // K position (shared: across the experts)
     if (is_a) {  // da / dv row x
@@ -221,8 +229,8 @@ __device__ __forceinline__ const uint16_t* src(const BwdArgs& a, const Ctx& c, b
     // W1 / W3 [d_ff][d]: K-row j, columns c0 + y
     const int64_t seg = c.shared ? kk / F : c.g;
     const int64_t j = kk - (c.shared ? seg * F : 0) + x;
-    const uint16_t* w = c.shared ? (op == 0 ? a.w1s : a.w3s) : (op == 0 ? a.w1r : a.w3r);
-    return w + seg * F * d + j * d + c.c0 + y;
+    const uint16_t* w = (c.shared ? (op == 0 ? a.w1s : a.w3s) : (op == 0 ? a.w1r : a.w3r)) + seg * F * d;
+    return w + (a.tiled ? tiled_off<128>(j, c.c0 + y, d) : j * d + c.c0 + y);
   } else {
     // weight gradients: K-row = row BK kt + x of the group, columns y
     const int64_t row = static_cast<int64_t>(Cfg<MODE>::BK) * kt + x;
@@ -579,11 +587,14 @@ __global__ __launch_bounds__(64 * kWaves<MODE>, Cfg<MODE>::kOcc) void ffn_bwd_ke
         out = x == 0 ? (c.shared ? a.dw1s : a.dw1r) : (c.shared ? a.dw3s : a.dw3r);
       else
         out = c.shared ? a.dw2s : a.dw2r;
-      out += e * M * N + static_cast<int64_t>(c.mo) * N + c.no;
+      out += e * M * N;
       for (int idx = threadIdx.x; idx < TM * (TN / 8); idx += 64 * kWaves<MODE>) {
         const int r = idx / (TN / 8), ch = idx % (TN / 8);
+        // the gradient in the weights' layout: row mo + r, columns no + 8 ch ..
+        const int64_t m = c.mo + r, n = c.no + 8 * ch;
+        const int64_t o = a.tiled ? (MODE == kDw13 ? tiled_off<128>(m, n, N) : tiled_off<256>(m, n, N)) : m * N + n;
         __builtin_nontemporal_store(*reinterpret_cast<const i32x4*>(lds + (x * TM + r) * kPitch + 16 * ch),
-                                    reinterpret_cast<i32x4*>(out + r * N + 8 * ch));
+                                    reinterpret_cast<i32x4*>(out + o));
       }
     }
     return;

@@ -137,7 +137,7 @@ hipError_t launch_quantize_fp8(const void* x, int xt, int64_t rows, int64_t cols
                                int tile_c, uint8_t* q, float* scale, hipStream_t stream);
 
 // ---------------------------------------------------------------------------- backward
-// Grouped SwiGLU backward (bf16, row-major weights; d a multiple of 256, d_ff of 128).
+// Grouped SwiGLU backward (bf16, row-major or tiled weights; d a multiple of 256, d_ff of 128).
 struct BwdArgs {
   const uint16_t* u;             // [T, d]
   const uint16_t* dout;          // [T, d]: the shared experts' output gradient
@@ -158,6 +158,7 @@ struct BwdArgs {
   uint16_t *dw1s, *dw3s, *dw2s;  // out, shared
   int64_t T;
   int K, d, F, n_r, n_s;
+  int tiled;                     // weights and weight gradients in the tiled layout (else row-major)
 };
 hipError_t launch_ffn_backward(const BwdArgs& args, hipStream_t stream);
 

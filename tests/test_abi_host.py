@@ -183,8 +183,8 @@ def test_pack_weights_args_rejected():
 
 
 def test_backward_args_rejected():
-    """The backward runs bf16 layers with row-major weights, d % 256 == 0, d_ff % 128 == 0; every
-    call below is stopped on the host before any HIP call."""
+    """The backward runs bf16 layers with either weight layout (the same for both expert kinds),
+    d % 256 == 0, d_ff % 128 == 0; every call below is stopped on the host before any HIP call."""
     lib = abi.load()
     fp32 = _shape()
     bf = _shape(act="bf16", ffn="bf16")
@@ -201,6 +201,7 @@ def test_backward_args_rejected():
     assert abi.moe_workspace_bytes(bf, abi.MOE_CALL_ROUTE_BACKWARD) >= 64 * 2 * 4
     es = abi.make_expert_set(FAKE, FAKE, FAKE)
     tiled = abi.make_expert_set(FAKE, FAKE, FAKE, layout=abi.MOE_LAYOUT_TILED)
+    bad = abi.make_expert_set(FAKE, FAKE, FAKE, layout=7)
     gr = abi.make_expert_grads(FAKE, FAKE, FAKE)
     nullg = abi.make_expert_grads(FAKE, None, FAKE)
     call = lambda s, r, sh, g, gs, dxs, ws, n: lib.moe_grouped_ffn_backward(
@@ -208,7 +209,8 @@ def test_backward_args_rejected():
         FAKE, FAKE, dxs, ctypes.byref(g), None if gs is None else ctypes.byref(gs), ws, n, None)
     assert call(bf, es, es, gr, gr, FAKE, FAKE, need - 1) == abi.MOE_ERR_WORKSPACE
     assert call(bf, es, es, gr, gr, FAKE, None, need) == abi.MOE_ERR_WORKSPACE
-    assert call(bf, tiled, tiled, gr, gr, FAKE, FAKE, need) == abi.MOE_ERR_UNSUPPORTED
+    assert call(bf, tiled, es, gr, gr, FAKE, FAKE, need) == abi.MOE_ERR_INVALID_ARG  # mixed layouts
+    assert call(bf, bad, bad, gr, gr, FAKE, FAKE, need) == abi.MOE_ERR_INVALID_ARG
     assert call(bf, es, es, nullg, gr, FAKE, FAKE, need) == abi.MOE_ERR_INVALID_ARG
     assert call(bf, es, None, gr, gr, FAKE, FAKE, need) == abi.MOE_ERR_INVALID_ARG   # n_shared = 1
     assert call(bf, es, es, gr, None, FAKE, FAKE, need) == abi.MOE_ERR_INVALID_ARG
