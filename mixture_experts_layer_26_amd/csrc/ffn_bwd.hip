@@ -11,10 +11,17 @@
 // each a grid of output tiles (v_mfma_f32_32x32x16_bf16, each wave a grid of 32 x 32
 // blocks), K through a ring of LDS stages filled by global_load_lds_dwordx4 (no staging
 // registers):
-//   kDh:     256 rows x 256 d_ff tiles on 8 waves (128 d_ff when d_ff % 256 != 0), K = d in
+//   kDh:     320 rows x 256 d_ff tiles on 8 waves (128 d_ff when d_ff % 256 != 0), K = d in
 //            steps of 64: dh; the epilogue reads a and v and stores da and dv in bf16.
-//   kDx:     256 rows x 256 d tiles on 8 waves, K = d_ff in steps of 32 (the shared
-//            experts' K ranges one after another): dX = da W1 + dv W3.
+//   kDx:     320 rows x 256 d tiles on 8 waves: dX = [da dv] [W1; W3] as one GEMM whose K
+//            runs over da's columns with W1, then dv's with W3 (for the shared group, over
+//            all shared experts' columns in each half), in steps of 64.
+// In both, a group of r rows is cut into ceil(r / 320) row blocks of equal size, as in the
+// forward's GEMMs: a V3 prefill expert of 185..345 rows is then mostly one block, where
+// 256-row blocks with a short last one cost two full tiles for most experts (about 40%
+// of these launches' MFMA work fell on padding rows, and those experts' weights were read
+// twice). The K loop is specialised on the number of 32-row blocks of a wave that hold
+// rows, and a wave whose A rows all lie past the tile's rows loads no A.
 //   kDw13:   128 d_ff x 128 d tiles per expert on 4 waves, K = the expert's rows: dW1, dW3
 //            (two workgroups per CU hide the short K loops' ends better than one of 8 waves).
 //   kDw2:    256 d x 128 d_ff tiles per expert on 8 waves, K = the expert's rows: dW2.
@@ -50,17 +57,17 @@ template <int MODE> constexpr bool kRowsByFf = MODE == kDh || MODE == kDh128;
 // lines per row with BK = 64; with BK = 32 each line is requested twice, a step apart.
 template <int MODE> struct Cfg;
 template <> struct Cfg<kDh> {  // A: dY (K-contiguous); B: W2 (K-major)
-  static constexpr int NA = 1, NB = 1, NACC = 1, WM = 2, WN = 4, NMB = 4, NNB = 2, kOcc = 2, NST = 2, BK = 64;
+  static constexpr int NA = 1, NB = 1, NACC = 1, WM = 2, WN = 4, NMB = 5, NNB = 2, kOcc = 2, NST = 2, BK = 64;
   static constexpr bool a_km = false;
   static constexpr bool b_km(int) { return true; }
 };
 template <> struct Cfg<kDh128> {  // as kDh, 128 d_ff columns per tile
-  static constexpr int NA = 1, NB = 1, NACC = 1, WM = 4, WN = 2, NMB = 2, NNB = 2, kOcc = 2, NST = 2, BK = 64;
+  static constexpr int NA = 1, NB = 1, NACC = 1, WM = 2, WN = 4, NMB = 5, NNB = 1, kOcc = 2, NST = 2, BK = 64;
   static constexpr bool a_km = false;
   static constexpr bool b_km(int) { return true; }
 };
-template <> struct Cfg<kDx> {  // A: da, dv (K-contiguous); B: W1, W3 (K-major)
-  static constexpr int NA = 2, NB = 2, NACC = 1, WM = 2, WN = 4, NMB = 4, NNB = 2, kOcc = 2, NST = 2, BK = 32;
+template <> struct Cfg<kDx> {  // A: da, then dv (K-contiguous); B: W1, then W3 (K-major)
+  static constexpr int NA = 1, NB = 1, NACC = 1, WM = 2, WN = 4, NMB = 5, NNB = 2, kOcc = 2, NST = 2, BK = 64;
   static constexpr bool a_km = false;
   static constexpr bool b_km(int) { return true; }
 };
@@ -153,9 +160,19 @@ struct Ctx {
 };
 
 // Row tiles of kDh / kDx: groups are the routed experts, then the shared groups (kDh:
-// each shared expert; kDx: one group for all of them). The offsets are copied
-// to LDS (soff, n_r + 1 entries) and one thread walks the groups. Returns false past
-// the last tile.
+// each shared expert; kDx: one group for all of them). A group of r rows has
+// ceil(r / TM) row blocks of equal size (row_blocks). The offsets are copied to LDS
+// (soff, n_r + 1 entries) and one thread walks the groups. Returns false past the last
+// tile.
+__device__ __forceinline__ int block_rows(int r, int TM) {  // rows per block (0 for r = 0)
+  const int mt = (r + TM - 1) / TM;
+  return mt > 0 ? (r + mt - 1) / mt : 0;
+}
+__device__ __forceinline__ int row_blocks(int r, int TM) {
+  const int rpb = block_rows(r, TM);
+  return rpb > 0 ? (r + rpb - 1) / rpb : 0;
+}
+
 template <int MODE>
 __device__ bool decode_row_tile(const BwdArgs& a, int id, Ctx& c, int* sh, int* soff) {
   constexpr int TM = kTM<MODE>, TN = kTN<MODE>;
@@ -167,7 +184,7 @@ __device__ bool decode_row_tile(const BwdArgs& a, int id, Ctx& c, int* sh, int* 
     int base = 0, found = -1, rb = 0;
     for (int g = 0; g < a.n_r + nsg && found < 0; ++g) {
       const int r = g < a.n_r ? soff[g + 1] - soff[g] : static_cast<int>(a.T);
-      const int n = ((r + TM - 1) / TM) * ntn;
+      const int n = row_blocks(r, TM) * ntn;
       if (id < base + n) {
         found = g;
         rb = id - base;
@@ -184,9 +201,10 @@ __device__ bool decode_row_tile(const BwdArgs& a, int id, Ctx& c, int* sh, int* 
   c.shared = g >= a.n_r;
   const int r = c.shared ? static_cast<int>(a.T) : soff[g + 1] - soff[g];
   c.row0 = c.shared ? 0 : soff[g];
-  c.m0 = static_cast<int64_t>(rb / ntn) * TM;
+  const int rpb = block_rows(r, TM);
+  c.m0 = static_cast<int64_t>(rb / ntn) * rpb;
   c.c0 = (rb % ntn) * TN;
-  c.rows = r - static_cast<int>(c.m0) < TM ? r - static_cast<int>(c.m0) : TM;
+  c.rows = r - static_cast<int>(c.m0) < rpb ? r - static_cast<int>(c.m0) : rpb;
   return true;
 }
 
@@ -196,62 +214,6 @@ __device__ bool decode_row_tile(const BwdArgs& a, int id, Ctx& c, int* sh, int* 
 template <int R>
 __device__ __forceinline__ int64_t tiled_off(int64_t n, int64_t k, int64_t K) {
   return ((n / R) * (K / 64) + k / 64) * (R * 64) + (n % R) * 64 + k % 64;
-}
-
-// Global address of the 16 bytes one lane copies for operand op at K-step kt.
-// K-contiguous operands: (x, y) = (tile row, 8-element chunk of the step's BK k); rows past
-// the tile's rows repeat its last row (they feed only outputs that are not stored).
-// K-major operands: (x, y) = (K-row of the step, first of 8 columns); K-rows past the
-// group's rows (weight gradients) read the zeroed 16 bytes at a.zero.
-template <int MODE>
-__device__ __forceinline__ const uint16_t* src(const BwdArgs& a, const Ctx& c, bool is_a, int op, int x, int y,
-                                               int kt) {
-  const int64_t F = a.F, d = a.d;
-  if constexpr (MODE == kDh || MODE == kDh128) {
-    if (is_a) {  // dY, row x of the tile, k = BK kt + 8 y
-      const int64_t row = c.m0 + (x < c.rows ? x : c.rows - 1);
-      const int64_t k = static_cast<int64_t>(Cfg<MODE>::BK) * kt + 8 * y;
-      return c.shared ? a.dout + row * d + k : a.dy_routed + (c.row0 + row) * d + k;
-    }
-    // W2 [d][d_ff]: K-row BK kt + x, columns c0 + y
-    const int e = c.shared ? c.g - a.n_r : c.g;
-    const uint16_t* w = (c.shared ? a.w2s : a.w2r) + static_cast<int64_t>(e) * d * F;
-    const int64_t k = static_cast<int64_t>(Cfg<MODE>::BK) * kt + x;
-    return w + (a.tiled ? tiled_off<256>(k, c.c0 + y, F) : k * F + c.c0 + y);
-  } else if constexpr (MODE == kDx) {
-    const int64_t kk = static_cast<int64_t>(Cfg<MODE>::BK) * kt;  // K position (shared: across the experts)
-    if (is_a) {  // da / dv row x
-      const int64_t row = c.m0 + (x < c.rows ? x : c.rows - 1);
-      const int64_t k = kk + 8 * y;
-      if (c.shared) return (op == 0 ? a.da_s : a.dv_s) + row * (a.n_s * F) + k;
-      return (op == 0 ? a.da_r : a.dv_r) + (c.row0 + row) * F + k;
-    }
-    // W1 / W3 [d_ff][d]: K-row j, columns c0 + y
-    const int64_t seg = c.shared ? kk / F : c.g;
-    const int64_t j = kk - (c.shared ? seg * F : 0) + x;
-    const uint16_t* w = (c.shared ? (op == 0 ? a.w1s : a.w3s) : (op == 0 ? a.w1r : a.w3r)) + seg * F * d;
-    return w + (a.tiled ? tiled_off<128>(j, c.c0 + y, d) : j * d + c.c0 + y);
-  } else {
-    // weight gradients: K-row = row BK kt + x of the group, columns y
-    const int64_t row = static_cast<int64_t>(Cfg<MODE>::BK) * kt + x;
-    if (row >= c.rows) return a.zero;
-    const int s = c.shared ? c.g - a.n_r : 0;
-    if constexpr (MODE == kDw13) {
-      if (is_a) {  // da / dv columns mo.. (d_ff)
-        if (c.shared) return (op == 0 ? a.da_s : a.dv_s) + row * (a.n_s * F) + s * F + c.mo + y;
-        return (op == 0 ? a.da_r : a.dv_r) + (c.row0 + row) * F + c.mo + y;
-      }
-      // X columns no.. (d)
-      return c.shared ? a.u + row * d + c.no + y : a.xs + (c.row0 + row) * d + c.no + y;
-    } else {
-      if (is_a) {  // dY columns mo.. (d)
-        if (c.shared) return a.dout + row * d + c.mo + y;
-        return a.dy_routed + (c.row0 + row) * d + c.mo + y;
-      }
-      if (c.shared) return a.h_s + row * (a.n_s * F) + s * F + c.no + y;  // h columns no.. (d_ff)
-      return a.h_r + (c.row0 + row) * F + c.no + y;
-    }
-  }
 }
 
 typedef __attribute__((address_space(3))) unsigned char* lds_ptr;
@@ -288,41 +250,110 @@ __device__ __forceinline__ const unsigned char* uniform_ptr(const void* p) {
   return reinterpret_cast<const unsigned char*>((hi << 32) | lo);
 }
 
-// Loads of K-step kt into one stage: each operand's tile is split evenly over the waves,
-// 64 16-byte slots per instruction (slot = per-wave share * w + 64 i + lane). The lane
-// picks the global chunk whose swizzled LDS position is its slot.
+// Loads of the row-tile launches (kDh, kDx): operand A (dY; kDx: da, then dv) is
+// K-contiguous, B (W2; kDx: W1, then W3) is K-major. Each operand's tile is split evenly
+// over the waves, 64 16-byte slots per instruction (slot = per-wave share * w + 64 i +
+// lane), and each lane picks the global chunk whose swizzled LDS position is its slot:
+// K-contiguous, slot = (BK / 8) r + (chunk ^ swizzle(r)); K-major, slot = (width / 8) k +
+// 4 (unit ^ (k & 3)) + 16-byte piece of the unit (km_slot). Per operand a wave-uniform
+// pointer (A at the tile's first row, B at K-row 0 of the expert's matrix) moves with the
+// K-step by scalar arithmetic; per lane and instruction a 32-bit byte offset from it is
+// made once per tile (A rows past the tile's rows repeat its last row). A wave whose A
+// rows all lie past the tile's rows loads no A.
 template <int MODE>
-__device__ __forceinline__ void dma_step(const BwdArgs& a, const Ctx& c, int kt, unsigned char* stage, int w,
-                                         int lane) {
-  constexpr int NA = Cfg<MODE>::NA, NB = Cfg<MODE>::NB, BK = Cfg<MODE>::BK, NW = kWaves<MODE>;
-#pragma unroll
-  for (int op = 0; op < NA + NB; ++op) {
-    const bool km = op < NA ? Cfg<MODE>::a_km : Cfg<MODE>::b_km(op - NA);
-    const int width = op < NA ? kTM<MODE> : kTN<MODE>;  // tile rows (K-contig.) or columns (K-major)
-    const int per_wave = op_bytes<MODE>(op) / 16 / NW;   // slots
-#pragma unroll
-    for (int i = 0; i < per_wave / 64; ++i) {
-      const int slot = per_wave * w + 64 * i + lane;
-      int x, y;
-      if (km) {  // slot = (width / 8) k + 4 (unit ^ (k & 3)) + 16-byte piece of the unit
-        const int spr = width / 8;
-        x = slot / spr;
-        const int ws = slot % spr;
-        y = (((ws / 4) ^ (x & 3)) * 32) + (ws % 4) * 8;
-      } else {  // slot = (BK / 8) r + (chunk ^ swizzle(r))
-        x = slot / (BK / 8);
-        y = (slot % (BK / 8)) ^ kc_swz<BK>(x);
-      }
-      dma16(src<MODE>(a, c, op < NA, op < NA ? op : op - NA, x, y, kt),
-            stage + op_offset<MODE>(op) + (per_wave * w + 64 * i) * 16);
-    }
+struct RowLoads {
+  const unsigned char* a[2];  // A at the tile's first row (kDx: da, dv), wave-uniform
+  const unsigned char* b[2];  // B of the group at K-row 0 (kDx: W1, W3), wave-uniform
+  uint32_t off_a[5], off_b[4];
+  bool load_a;
+};
+template <int MODE> constexpr int row_instrs_a() { return op_bytes<MODE>(0) / 16 / kWaves<MODE> / 64; }
+template <int MODE> constexpr int row_instrs_b() { return op_bytes<MODE>(1) / 16 / kWaves<MODE> / 64; }
+
+__device__ __forceinline__ void km_slot(int slot, int width, int& x, int& y);
+
+template <int MODE>
+__device__ __forceinline__ void row_setup(const BwdArgs& a, const Ctx& c, int w, int lane, RowLoads<MODE>& L) {
+  constexpr int BK = Cfg<MODE>::BK, NW = kWaves<MODE>, TN = kTN<MODE>;
+  static_assert(Cfg<MODE>::NA == 1 && Cfg<MODE>::NB == 1 && BK == 64, "row tiles: one A and one B operand");
+  static_assert(row_instrs_a<MODE>() <= 5 && row_instrs_b<MODE>() <= 4, "offset arrays");
+  const int64_t F = a.F, d = a.d;
+  const int e = c.shared ? c.g - a.n_r : c.g;
+  int64_t lda, ldk;  // A's row length; B's row length (the K-major stride)
+  if constexpr (MODE == kDx) {
+    lda = c.shared ? a.n_s * F : F;
+    const int64_t first = (c.shared ? 0 : c.row0) + c.m0;
+    L.a[0] = uniform_ptr((c.shared ? a.da_s : a.da_r) + first * lda);
+    L.a[1] = uniform_ptr((c.shared ? a.dv_s : a.dv_r) + first * lda);
+    L.b[0] = uniform_ptr((c.shared ? a.w1s : a.w1r) + static_cast<int64_t>(c.shared ? 0 : e) * F * d);
+    L.b[1] = uniform_ptr((c.shared ? a.w3s : a.w3r) + static_cast<int64_t>(c.shared ? 0 : e) * F * d);
+    ldk = d;
+  } else {
+    lda = d;
+    L.a[0] = L.a[1] = uniform_ptr((c.shared ? a.dout : a.dy_routed + c.row0 * d) + c.m0 * d);
+    L.b[0] = L.b[1] = uniform_ptr((c.shared ? a.w2s : a.w2r) + static_cast<int64_t>(e) * d * F);
+    ldk = F;
   }
+  constexpr int pa = op_bytes<MODE>(0) / 16 / NW, pb = op_bytes<MODE>(1) / 16 / NW;  // slots per wave
+  L.load_a = __builtin_amdgcn_readfirstlane(pa * w / (BK / 8) < c.rows ? 1 : 0) != 0;
+#pragma unroll
+  for (int i = 0; i < row_instrs_a<MODE>(); ++i) {
+    const int slot = pa * w + 64 * i + lane;
+    const int x = slot / (BK / 8), y = (slot % (BK / 8)) ^ kc_swz<BK>(x);
+    const int xr = x < c.rows ? x : c.rows - 1;
+    L.off_a[i] = static_cast<uint32_t>(2 * (xr * lda + 8 * y));
+  }
+  constexpr int R = MODE == kDx ? 128 : 256;  // the tiled layout's row block of W1/W3, W2
+#pragma unroll
+  for (int i = 0; i < row_instrs_b<MODE>(); ++i) {
+    int x, y;
+    km_slot(pb * w + 64 * i + lane, TN, x, y);
+    const int64_t col = c.c0 + y;
+    const int64_t o = a.tiled ? (col / 64) * (R * 64) + x * 64 + col % 64 : x * ldk + col;
+    L.off_b[i] = static_cast<uint32_t>(2 * o);
+  }
+}
+
+template <int MODE>
+__device__ __forceinline__ void row_step(const BwdArgs& a, const Ctx& c, const RowLoads<MODE>& L, int kt,
+                                         unsigned char* stage, int w) {
+  constexpr int BK = Cfg<MODE>::BK, NW = kWaves<MODE>;
+  const int64_t F = a.F, d = a.d;
+  const unsigned char *sa, *sb;
+  if constexpr (MODE == kDx) {
+    // K position: the first half of the steps runs over da (with W1), the second over dv
+    // (with W3); each half spans F columns (routed) or n_s F (shared, one expert after
+    // another). A step never straddles the halves or the experts (F is a multiple of 128).
+    const int64_t half = c.shared ? a.n_s * F : F;
+    int64_t kk = static_cast<int64_t>(BK) * kt;
+    const int second = kk >= half ? 1 : 0;
+    kk -= second ? half : 0;
+    sa = L.a[second] + 2 * kk;
+    const int64_t seg = c.shared ? kk / F : 0;  // shared: the expert of this K range
+    const int64_t j0 = kk - seg * F;            // first W row (d_ff index) of the step
+    const int64_t ob = a.tiled ? (j0 / 128) * (d / 64) * (128 * 64) + (j0 % 128) * 64 : j0 * d;
+    sb = L.b[second] + 2 * (seg * F * d + ob);
+  } else {
+    sa = L.a[0] + 2 * static_cast<int64_t>(BK) * kt;
+    // W2 [d][d_ff], K-rows BK kt.. (d index); tiled: 256-row blocks of 64-wide K-steps
+    const int64_t k0 = static_cast<int64_t>(BK) * kt;
+    const int64_t ob = a.tiled ? (k0 / 256) * (F / 64) * (256 * 64) + (k0 % 256) * 64 : k0 * F;
+    sb = L.b[0] + 2 * ob;
+  }
+  constexpr int pa = op_bytes<MODE>(0) / 16 / NW, pb = op_bytes<MODE>(1) / 16 / NW;
+  if (L.load_a) {
+#pragma unroll
+    for (int i = 0; i < row_instrs_a<MODE>(); ++i) dma16s(L.off_a[i], sa, stage + (pa * w + 64 * i) * 16);
+  }
+#pragma unroll
+  for (int i = 0; i < row_instrs_b<MODE>(); ++i)
+    dma16s(L.off_b[i], sb, stage + op_offset<MODE>(1) + (pb * w + 64 * i) * 16);
 }
 
 // Loads of the weight-gradient launches (every operand K-major, K = the group's rows).
 // Per operand: a wave-uniform pointer to K-row 0 of the tile's columns and the bytes from
 // one K-row to the next; per lane and instruction: the 32-bit byte offset of its 16 bytes
-// (K-row x, column y of the step, chosen as in dma_step). A step moves the pointers by BK
+// (K-row x, column y of the step, chosen as in row_setup). A step moves the pointers by BK
 // K-rows with scalar arithmetic, so the K loop spends no VALU work on addresses. Only a
 // step that runs past the group's rows (its last) checks rows, lane by lane, and sends
 // the lanes past them to the zeroed 16 bytes at a.zero.
@@ -427,17 +458,19 @@ __device__ __forceinline__ void ring_wait() {
     asm volatile("s_waitcnt vmcnt(%0)\n\ts_waitcnt lgkmcnt(0)\n\ts_barrier" ::"n"(N) : "memory");
 }
 
-template <int MODE>
+// One K-step's MFMAs for the first NL of the wave's NMB 32-row blocks (the others hold no
+// rows of the tile).
+template <int MODE, int NL>
 __device__ __forceinline__ void compute(const unsigned char* base,
                                         f32x16 (&acc)[Cfg<MODE>::NACC][Cfg<MODE>::NMB][Cfg<MODE>::NNB], int wm,
                                         int wn, int lane) {
   constexpr int NA = Cfg<MODE>::NA, NB = Cfg<MODE>::NB, BK = Cfg<MODE>::BK;
-  constexpr int NMB = Cfg<MODE>::NMB, NNB = Cfg<MODE>::NNB;
+  constexpr int NMB = NL, NNB = Cfg<MODE>::NNB;
   constexpr int TM = kTM<MODE>, TN = kTN<MODE>;
   const int r0 = (TM / Cfg<MODE>::WM) * wm, n0 = (TN / Cfg<MODE>::WN) * wn;
 #pragma unroll
   for (int s = 0; s < BK / 16; ++s) {
-    bf16x8 fa[NA][NMB], fb[NB][NNB];
+    bf16x8 fa[NA][NMB > 0 ? NMB : 1], fb[NB][NNB];
 #pragma unroll
     for (int op = 0; op < NA; ++op)
 #pragma unroll
@@ -460,10 +493,7 @@ __device__ __forceinline__ void compute(const unsigned char* base,
       for (int nb = 0; nb < NNB; ++nb) {
         // the n-side fragment goes first, so each lane's accumulator holds 4 consecutive
         // output columns of one output row (see the epilogue)
-        if constexpr (MODE == kDx) {
-          acc[0][mb][nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fb[0][nb], fa[0][mb], acc[0][mb][nb], 0, 0, 0);
-          acc[0][mb][nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fb[1][nb], fa[1][mb], acc[0][mb][nb], 0, 0, 0);
-        } else if constexpr (MODE == kDw13) {
+        if constexpr (MODE == kDw13) {
           acc[0][mb][nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fb[0][nb], fa[0][mb], acc[0][mb][nb], 0, 0, 0);
           acc[1][mb][nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fb[0][nb], fa[1][mb], acc[1][mb][nb], 0, 0, 0);
         } else {
@@ -473,13 +503,45 @@ __device__ __forceinline__ void compute(const unsigned char* base,
   }
 }
 
+// The load ring and MFMAs of one tile, for NL live row blocks per wave: steps 0 .. NST - 2
+// first; at step kt, once step kt has landed, the load of step kt + NST - 1 goes into the
+// stage step kt - 1 was read from (every wave is past that read: it came before the
+// barrier). On exit every wave is past its last read of the ring.
+template <int MODE, int NL>
+__device__ __forceinline__ void k_loop(const BwdArgs& a, const Ctx& c, const DwLoads<MODE>& dl,
+                                       const RowLoads<MODE>& rl, unsigned char* lds,
+                                       f32x16 (&acc)[Cfg<MODE>::NACC][Cfg<MODE>::NMB][Cfg<MODE>::NNB], int w,
+                                       int wm, int wn, int lane) {
+  constexpr int NST = Cfg<MODE>::NST;
+  constexpr int kStage = kStageBytes<MODE>;
+  constexpr int ND = loads_per_step<MODE>();  // loads per wave per K-step
+  constexpr bool kDw = MODE == kDw13 || MODE == kDw2;
+  auto issue = [&](int kt, unsigned char* st) {
+    if constexpr (kDw)
+      dw_step<MODE>(a, c, dl, kt, st, w, lane);
+    else
+      row_step<MODE>(a, c, rl, kt, st, w);
+  };
+#pragma unroll
+  for (int s0 = 0; s0 < NST - 1; ++s0)
+    if (s0 < c.nk) issue(s0, lds + s0 * kStage);
+  for (int kt = 0; kt < c.nk; ++kt) {
+    if (NST == 3 && kt + 1 < c.nk)
+      ring_wait<ND>();  // step kt + 1's loads may stay in flight (the weight-gradient modes,
+                        // whose waves all issue ND loads per step)
+    else
+      ring_wait<0>();
+    if (kt + NST - 1 < c.nk) issue(kt + NST - 1, lds + ((kt + NST - 1) % NST) * kStage);
+    compute<MODE, NL>(lds + (kt % NST) * kStage, acc, wm, wn, lane);
+  }
+}
+
 template <int MODE>
 __global__ __launch_bounds__(64 * kWaves<MODE>, Cfg<MODE>::kOcc) void ffn_bwd_kernel(BwdArgs a) {
   constexpr int NACC = Cfg<MODE>::NACC, NMB = Cfg<MODE>::NMB, NNB = Cfg<MODE>::NNB;
   constexpr int NST = Cfg<MODE>::NST, BK = Cfg<MODE>::BK;
   constexpr int TM = kTM<MODE>, TN = kTN<MODE>;
   constexpr int kStage = kStageBytes<MODE>;
-  constexpr int ND = loads_per_step<MODE>();  // loads per wave per K-step
   __shared__ __align__(16) unsigned char lds[NST * kStage];
   // the tile decoder's scratch lives in the last stage, which no load touches before the
   // ring's first barrier
@@ -495,7 +557,7 @@ __global__ __launch_bounds__(64 * kWaves<MODE>, Cfg<MODE>::kOcc) void ffn_bwd_ke
     if constexpr (kRowsByFf<MODE>)
       c.nk = a.d / BK;
     else
-      c.nk = (c.shared ? a.n_s * a.F : a.F) / BK;
+      c.nk = 2 * (c.shared ? a.n_s * a.F : a.F) / BK;
   } else {
     // per group: (M / TM) x (N / TN) tiles; M = d_ff, N = d (kDw13) or M = d, N = d_ff
     const int mt = (MODE == kDw13 ? a.F : a.d) / TM, nt = (MODE == kDw13 ? a.d : a.F) / TN;
@@ -523,27 +585,34 @@ __global__ __launch_bounds__(64 * kWaves<MODE>, Cfg<MODE>::kOcc) void ffn_bwd_ke
 
   constexpr bool kDw = MODE == kDw13 || MODE == kDw2;
   DwLoads<MODE> dl;
-  if constexpr (kDw) dw_setup<MODE>(a, c, w, lane, dl);
-  auto issue = [&](int kt, unsigned char* st) {
-    if constexpr (kDw)
-      dw_step<MODE>(a, c, dl, kt, st, w, lane);
-    else
-      dma_step<MODE>(a, c, kt, st, w, lane);
-  };
-
-  // load ring: steps 0 .. NST - 2 first; at step kt, once step kt has landed, the load of
-  // step kt + NST - 1 goes into the stage step kt - 1 was read from (every wave is past
-  // that read: it came before the barrier)
-#pragma unroll
-  for (int s0 = 0; s0 < NST - 1; ++s0)
-    if (s0 < c.nk) issue(s0, lds + s0 * kStage);
-  for (int kt = 0; kt < c.nk; ++kt) {
-    if (NST == 3 && kt + 1 < c.nk)
-      ring_wait<ND>();  // step kt + 1's loads may stay in flight
-    else
-      ring_wait<0>();
-    if (kt + NST - 1 < c.nk) issue(kt + NST - 1, lds + ((kt + NST - 1) % NST) * kStage);
-    compute<MODE>(lds + (kt % NST) * kStage, acc, wm, wn, lane);
+  RowLoads<MODE> rl;
+  if constexpr (kDw)
+    dw_setup<MODE>(a, c, w, lane, dl);
+  else
+    row_setup<MODE>(a, c, w, lane, rl);
+  // live 32-row blocks of this wave (wave-uniform; all of them in the weight-gradient modes)
+  int live = NMB;
+  if constexpr (!kDw) {
+    live = (c.rows - (TM / Cfg<MODE>::WM) * wm + 31) / 32;
+    live = live < 0 ? 0 : (live > NMB ? NMB : live);
+    live = __builtin_amdgcn_readfirstlane(live);
+  }
+  static_assert(NMB <= 5, "the K loop is specialised for 0..5 live row blocks");
+  switch (live) {  // every wave runs the same loads and barriers; only the MFMA count differs
+    case 5:
+      if constexpr (NMB >= 5) k_loop<MODE, (NMB >= 5 ? 5 : 0)>(a, c, dl, rl, lds, acc, w, wm, wn, lane);
+      break;
+    case 4:
+      if constexpr (NMB >= 4) k_loop<MODE, (NMB >= 4 ? 4 : 0)>(a, c, dl, rl, lds, acc, w, wm, wn, lane);
+      break;
+    case 3:
+      if constexpr (NMB >= 3) k_loop<MODE, (NMB >= 3 ? 3 : 0)>(a, c, dl, rl, lds, acc, w, wm, wn, lane);
+      break;
+    case 2:
+      if constexpr (NMB >= 2) k_loop<MODE, (NMB >= 2 ? 2 : 0)>(a, c, dl, rl, lds, acc, w, wm, wn, lane);
+      break;
+    case 1: k_loop<MODE, 1>(a, c, dl, rl, lds, acc, w, wm, wn, lane); break;
+    default: k_loop<MODE, 0>(a, c, dl, rl, lds, acc, w, wm, wn, lane); break;
   }
 
   // epilogue. The MFMA's first operand indexes the output rows of its 32x32 result and the
@@ -601,10 +670,10 @@ __global__ __launch_bounds__(64 * kWaves<MODE>, Cfg<MODE>::kOcc) void ffn_bwd_ke
   }
   if constexpr (kRowsByFf<MODE>) {
     // da = dh v SiLU'(a), dv = dh SiLU(a), with a and v (fp32) from the gate/up launch. Per
-    // 32-row block, all of its loads of a and v are issued before any result is stored, so
-    // a tile waits NMB load latencies instead of one per 4 columns (the loads used to wait
-    // behind the previous columns' stores: 0.5 of this launch's 3.7 ms at V3 prefill). Rows
-    // past the tile's read its last row and store nothing.
+    // 32 x 32 block, all of its loads of a and v are issued before any result is stored, so
+    // a tile waits one load latency per block instead of one per 4 columns (the loads used
+    // to wait behind the previous columns' stores: 0.5 of this launch's 3.7 ms at V3
+    // prefill). Rows past the tile's read its last row and store nothing.
     const int64_t ldr = c.shared ? a.n_s * static_cast<int64_t>(a.F) : a.F;
     const int64_t col0 = (c.shared ? static_cast<int64_t>(c.g - a.n_r) * a.F : 0) + c.c0;
     const int64_t row0 = c.shared ? 0 : c.row0;
@@ -614,25 +683,24 @@ __global__ __launch_bounds__(64 * kWaves<MODE>, Cfg<MODE>::kOcc) void ffn_bwd_ke
     uint16_t* pdv = c.shared ? a.dv_s : a.dv_r;
 #pragma unroll
     for (int mb = 0; mb < NMB; ++mb) {
+      if ((TM / Cfg<MODE>::WM) * wm + 32 * mb >= c.rows) continue;  // no row of this block (wave-uniform)
       const int r = (TM / Cfg<MODE>::WM) * wm + 32 * mb + m_in;
       const bool live = r < c.rows;
       const int64_t o = (row0 + c.m0 + (live ? r : c.rows - 1)) * ldr + col0;
-      float4 a4[NNB][4], v4[NNB][4];
 #pragma unroll
-      for (int nb = 0; nb < NNB; ++nb)
+      for (int nb = 0; nb < NNB; ++nb) {
+        float4 a4[4], v4[4];
 #pragma unroll
         for (int p = 0; p < 4; ++p) {
           const int n = (TN / Cfg<MODE>::WN) * wn + 32 * nb + 8 * p + 4 * (lane / 32);
-          a4[nb][p] = *reinterpret_cast<const float4*>(pa + o + n);
-          v4[nb][p] = *reinterpret_cast<const float4*>(pv + o + n);
+          a4[p] = *reinterpret_cast<const float4*>(pa + o + n);
+          v4[p] = *reinterpret_cast<const float4*>(pv + o + n);
         }
 #pragma unroll
-      for (int nb = 0; nb < NNB; ++nb)
-#pragma unroll
         for (int p = 0; p < 4; ++p) {
           const int n = (TN / Cfg<MODE>::WN) * wn + 32 * nb + 8 * p + 4 * (lane / 32);
-          const float aa[4] = {a4[nb][p].x, a4[nb][p].y, a4[nb][p].z, a4[nb][p].w};
-          const float vv[4] = {v4[nb][p].x, v4[nb][p].y, v4[nb][p].z, v4[nb][p].w};
+          const float aa[4] = {a4[p].x, a4[p].y, a4[p].z, a4[p].w};
+          const float vv[4] = {v4[p].x, v4[p].y, v4[p].z, v4[p].w};
           float dav[4], dvv[4];
 #pragma unroll
           for (int q = 0; q < 4; ++q) {
@@ -646,6 +714,7 @@ __global__ __launch_bounds__(64 * kWaves<MODE>, Cfg<MODE>::kOcc) void ffn_bwd_ke
             *reinterpret_cast<uint2*>(pdv + o + n) = make_uint2(pack_bf16x2(dvv[0], dvv[1]), pack_bf16x2(dvv[2], dvv[3]));
           }
         }
+      }
     }
   } else if constexpr (MODE == kDx) {
     // dX: bf16 for the routed rows, the fp32 sum over the shared experts for the shared group
