@@ -86,23 +86,41 @@ typedef __attribute__((address_space(3))) unsigned char* lds_ptr;
 // no value of its own in M0 across the statement (clang warns that M0 is a reserved
 // register; the clobber is what tells its M0-initialisation passes that the statement
 // writes it).
-// NT sets the non-temporal cache policy, used for the weights: each weight byte is read
-// by one workgroup, or by the few of a gang close together in time, and streaming it
-// with that policy measured faster in every phase (V3 decode 3.86 -> 3.67 ms, V3 prefill
-// 7.08 -> 6.86 ms). The rows of A are re-read by many workgroups through the L2 and keep
-// the default policy (with it set on A, V3 prefill took 8.5 ms).
+// The A rows are re-read by many workgroups through the L2 and take the default cache
+// policy (the non-temporal policy on them took V3 prefill to 8.5 ms).
 #pragma clang diagnostic push
 #pragma clang diagnostic ignored "-Winline-asm"
-template <bool NT>
 __device__ __forceinline__ void dma16(uint32_t voff, const unsigned char* sbase, const unsigned char* lds) {
   const uint32_t m0 = static_cast<uint32_t>(reinterpret_cast<uintptr_t>((lds_ptr)(lds)));
-  if constexpr (NT)
-    asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1 nt" ::"v"(voff), "s"(sbase),
-                 "s"(m0)
-                 : "memory", "m0");
-  else
-    asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1" ::"v"(voff), "s"(sbase), "s"(m0)
-                 : "memory", "m0");
+  asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1" ::"v"(voff), "s"(sbase), "s"(m0)
+               : "memory", "m0");
+}
+
+// The same for a weight row, whose cache policy depends on the tile's group: non-temporal
+// (stream != 0) for groups of one row block, whose weight bytes one workgroup reads once;
+// streaming them with that policy measured faster in every phase (V3 decode 3.86 -> 3.67
+// ms, V3 prefill 7.08 -> 6.86 ms). Weights that several row blocks read (the shared
+// experts', a large expert's) keep the default policy, so that the blocks after the first
+// find them in the L2 (with the policy on them too, the shared expert's gate/up weights
+// came from HBM once per row block). The choice is a scalar branch inside the statement,
+// between two copies of the load, so the compiler sees one instruction and its register
+// allocation of the K loop is the same as with a fixed policy (two copies of the K loop
+// spilled). SCC is clobbered by the compare.
+__device__ __forceinline__ void dma16_w(uint32_t voff, const unsigned char* sbase, const unsigned char* lds,
+                                        uint32_t stream) {
+  const uint32_t m0 = static_cast<uint32_t>(reinterpret_cast<uintptr_t>((lds_ptr)(lds)));
+  const uint32_t st = __builtin_amdgcn_readfirstlane(stream);
+  asm volatile(
+      "s_mov_b32 m0, %2\n\t"
+      "s_cmp_eq_u32 %3, 0\n\t"
+      "s_cbranch_scc1 1f\n\t"
+      "global_load_lds_dwordx4 %0, %1 nt\n\t"
+      "s_branch 2f\n"
+      "1:\n\t"
+      "global_load_lds_dwordx4 %0, %1\n"
+      "2:" ::"v"(voff),
+      "s"(sbase), "s"(m0), "s"(st)
+      : "memory", "m0", "scc");
 }
 #pragma clang diagnostic pop
 
@@ -118,6 +136,7 @@ __device__ __forceinline__ const unsigned char* uniform_ptr(const void* p) {
 template <class G>
 struct TileCtx {
   bool load_a;                  // this wave's A rows hold at least one of the tile's rows
+  uint32_t b_stream;            // 1: the group has one row block, its weights are read once
   const unsigned char* abase;   // wave-uniform: K-step 0 of the A rows
   uint32_t a[G::kDmaA];         // this lane's A rows: byte offsets from abase (chunk included)
   const unsigned char* bbase;   // wave-uniform: K-step 0 of this wave's B rows
@@ -142,10 +161,10 @@ __device__ __forceinline__ void dma_step(const TileCtx<G>& c, int kt, int wave) 
   const unsigned char* bk = c.bbase + 2 * b_offset(kt, c.kseg_steps, c.kseg_inv, c.seg_stride, c.bstep);
   if (c.load_a) {
 #pragma unroll
-    for (int j = 0; j < kDmaA; ++j) dma16<false>(c.a[j], ak, st + (8 * kDmaA * wave + 8 * j) * kRow);
+    for (int j = 0; j < kDmaA; ++j) dma16(c.a[j], ak, st + (8 * kDmaA * wave + 8 * j) * kRow);
   }
 #pragma unroll
-  for (int j = 0; j < kDmaB; ++j) dma16<true>(c.b[j], bk, st + kOpA + (8 * kDmaB * wave + 8 * j) * kRow);
+  for (int j = 0; j < kDmaB; ++j) dma16_w(c.b[j], bk, st + kOpA + (8 * kDmaB * wave + 8 * j) * kRow, c.b_stream);
 }
 
 // Fragments of one 16-wide sub-step of stage ST for a wave holding NMB live 32-row
@@ -308,7 +327,9 @@ __device__ __forceinline__ void mainloop(const TileCtx<G>& c, f32x16 (&acc)[G::k
   tail_steps<0, G, NMB>(c, s, c.nk - s, wave, arow0, brow, lane, f0, f1, acc);
 }
 
-template <bool GATED, class G>
+// PRE (phase 1 only): also store the pre-activations a and v in fp32 (the backward's
+// recompute). A separate instance, so that the forward's keeps its register allocation.
+template <bool GATED, class G, bool PRE>
 __global__ __launch_bounds__(kThreads) void grouped_gemm_bf16(GemmArgs args) {
   __shared__ TileMap tm;
   constexpr int TR = 2 * G::GR;
@@ -337,6 +358,7 @@ __global__ __launch_bounds__(kThreads) void grouped_gemm_bf16(GemmArgs args) {
     // 32 bits), every other A operand from the tile's first row, B from the tile's weights.
     const int64_t eoff = static_cast<int64_t>(routed ? t.group : sg) * args.b_expert_stride;
     c.load_a = __builtin_amdgcn_readfirstlane(8 * kDmaA * wave < t.rows ? 1 : 0) != 0;
+    c.b_stream = __builtin_amdgcn_readfirstlane(tm.mt[t.group] == 1 ? 1 : 0);
     const bool gathered = routed && args.gather != nullptr;
     const int64_t lda = routed ? args.lda_routed : args.lda_shared;
     {
@@ -466,12 +488,12 @@ __global__ __launch_bounds__(kThreads) void grouped_gemm_bf16(GemmArgs args) {
           st16(dst + t.n0 + 8 * ch, val);
         }
       }
-      if constexpr (GATED) {
-        // the pre-activations a and v in fp32 when asked for (the backward), straight from
-        // the accumulators: lane column 32 wn + col_in, 128 contiguous bytes per row
+      if constexpr (GATED && PRE) {
+        // the pre-activations a and v in fp32, straight from the accumulators: lane column
+        // 32 wn + col_in, 128 contiguous bytes per row
         float* pa = routed ? args.pre_gate_routed : args.pre_gate_shared;
         float* pv = routed ? args.pre_up_routed : args.pre_up_shared;
-        if (pa != nullptr) {
+        {
           const int64_t ld = routed ? args.ldo_routed : args.ldo_shared;
           const int64_t col = t.n0 + 32 * wn + col_in + (routed ? 0 : static_cast<int64_t>(sg) * args.N);
 #pragma unroll
@@ -519,15 +541,21 @@ size_t ffn_bf16_lds_bytes() {
 hipError_t launch_grouped_gemm_bf16(const GemmArgs& args, bool gated, int grid, hipStream_t stream) {
   if (args.K % (2 * BK) != 0) return hipErrorInvalidValue;
   const bool small = args.T <= kSmallBatchRows;  // every group fits one 128-row tile
+  const bool pre = gated && args.pre_gate_routed != nullptr;
+  if (pre && (!args.pre_up_routed || !args.pre_gate_shared || !args.pre_up_shared)) return hipErrorInvalidValue;
   const dim3 g(grid), b(kThreads);
-  if (gated && small)
-    hipLaunchKernelGGL((grouped_gemm_bf16<true, GeoSmall>), g, b, 0, stream, args);
+  if (pre && small)
+    hipLaunchKernelGGL((grouped_gemm_bf16<true, GeoSmall, true>), g, b, 0, stream, args);
+  else if (pre)
+    hipLaunchKernelGGL((grouped_gemm_bf16<true, GeoLarge, true>), g, b, 0, stream, args);
+  else if (gated && small)
+    hipLaunchKernelGGL((grouped_gemm_bf16<true, GeoSmall, false>), g, b, 0, stream, args);
   else if (gated)
-    hipLaunchKernelGGL((grouped_gemm_bf16<true, GeoLarge>), g, b, 0, stream, args);
+    hipLaunchKernelGGL((grouped_gemm_bf16<true, GeoLarge, false>), g, b, 0, stream, args);
   else if (small)
-    hipLaunchKernelGGL((grouped_gemm_bf16<false, GeoSmall>), g, b, 0, stream, args);
+    hipLaunchKernelGGL((grouped_gemm_bf16<false, GeoSmall, false>), g, b, 0, stream, args);
   else
-    hipLaunchKernelGGL((grouped_gemm_bf16<false, GeoLarge>), g, b, 0, stream, args);
+    hipLaunchKernelGGL((grouped_gemm_bf16<false, GeoLarge, false>), g, b, 0, stream, args);
   return hipGetLastError();
 }
 
