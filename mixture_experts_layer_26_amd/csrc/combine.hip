@@ -4,8 +4,9 @@
 // DeepSeek-V3 explainer's equation for h'_t (method section 2), as a gather over the
 // token's K sorted rows (no atomics), added in fp32 in the order residual, shared,
 // routed experts ascending, and rounded once to the output dtype. One workgroup per
-// token with one thread per 16-byte vector of the row (up to 1024), so every load of
-// the token is issued at once.
+// token with one thread per 16-byte vector of the row (up to 1024). A thread issues the
+// loads of all K routed rows before it adds the first (K <= 16, unrolled), so they are in
+// flight together instead of one latency per row.
 //
 // bias update: the same section's end-of-step rule, b_i -= gamma when expert i's load
 // is above the mean T*K/N_r, += gamma when below, compared exactly in integers.
@@ -32,35 +33,46 @@ __global__ __launch_bounds__(1024) void combine_kernel(
   }
   __syncthreads();
   for (int c0 = threadIdx.x * V; c0 < d; c0 += blockDim.x * V) {
-    float acc[V];
-    if (ACT == 1) {
-      const uint4 uv = ld16(static_cast<const uint16_t*>(u) + t * d + c0);
-      const uint16_t* up = reinterpret_cast<const uint16_t*>(&uv);
-#pragma unroll
-      for (int q = 0; q < V; ++q) acc[q] = bf16_to_f32(up[q]);
-    } else {
-      const float4 uv = *reinterpret_cast<const float4*>(static_cast<const float*>(u) + t * d + c0);
-      acc[0] = uv.x; acc[1] = uv.y; acc[2] = uv.z; acc[3] = uv.w;
-    }
+    // every load of this vector first: the residual, the shared sum, the K routed rows
+    const uint4 uv = ACT == 1 ? ld16(static_cast<const uint16_t*>(u) + t * d + c0)
+                              : ld16(static_cast<const float*>(u) + t * d + c0);
+    float4 sv[V / 4];
     if (y_shared) {
 #pragma unroll
-      for (int q = 0; q < V; q += 4) {
-        const float4 s = *reinterpret_cast<const float4*>(y_shared + t * d + c0 + q);
-        acc[q] += s.x; acc[q + 1] += s.y; acc[q + 2] += s.z; acc[q + 3] += s.w;
+      for (int q = 0; q < V / 4; ++q) sv[q] = *reinterpret_cast<const float4*>(y_shared + t * d + c0 + 4 * q);
+    }
+    uint4 yv[16];  // the K routed rows' vectors (bf16: 8 values; fp32: 4)
+#pragma unroll
+    for (int k = 0; k < 16; ++k) {
+      if (k < K) {
+        const int64_t r = rows[k];
+        yv[k] = ACT == 1 ? ld16(static_cast<const uint16_t*>(y_routed) + r * d + c0)
+                         : ld16(static_cast<const float*>(y_routed) + r * d + c0);
       }
     }
-    for (int k = 0; k < K; ++k) {
-      const int64_t r = rows[k];
-      const float g = gs[k];
-      if (ACT == 1) {
-        const uint4 yv = ld16(static_cast<const uint16_t*>(y_routed) + r * d + c0);
-        const uint16_t* yp = reinterpret_cast<const uint16_t*>(&yv);
+    float acc[V];
 #pragma unroll
-        for (int q = 0; q < V; ++q) acc[q] = fmaf(g, bf16_to_f32(yp[q]), acc[q]);
-      } else {
-        const float4 yv = *reinterpret_cast<const float4*>(static_cast<const float*>(y_routed) + r * d + c0);
-        acc[0] = fmaf(g, yv.x, acc[0]); acc[1] = fmaf(g, yv.y, acc[1]);
-        acc[2] = fmaf(g, yv.z, acc[2]); acc[3] = fmaf(g, yv.w, acc[3]);
+    for (int q = 0; q < V; ++q)
+      acc[q] = ACT == 1 ? bf16_to_f32(reinterpret_cast<const uint16_t*>(&uv)[q]) : reinterpret_cast<const float*>(&uv)[q];
+    if (y_shared) {
+#pragma unroll
+      for (int q = 0; q < V / 4; ++q) {
+        acc[4 * q] += sv[q].x; acc[4 * q + 1] += sv[q].y; acc[4 * q + 2] += sv[q].z; acc[4 * q + 3] += sv[q].w;
+      }
+    }
+#pragma unroll
+    for (int k = 0; k < 16; ++k) {
+      if (k < K) {
+        const float g = gs[k];
+        if (ACT == 1) {
+          const uint16_t* yp = reinterpret_cast<const uint16_t*>(&yv[k]);
+#pragma unroll
+          for (int q = 0; q < V; ++q) acc[q] = fmaf(g, bf16_to_f32(yp[q]), acc[q]);
+        } else {
+          const float* yp = reinterpret_cast<const float*>(&yv[k]);
+#pragma unroll
+          for (int q = 0; q < V; ++q) acc[q] = fmaf(g, yp[q], acc[q]);
+        }
       }
     }
     if (ACT == 1) {
