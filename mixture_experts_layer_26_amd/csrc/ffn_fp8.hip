@@ -170,9 +170,15 @@ __device__ __forceinline__ void dma_step(const TileCtx& c, int kt) {
 }
 
 // A 16 x 128 fp8 fragment (rows row.., this lane's 32 bytes of K) from a swizzled stage.
+// Lane group q (lanes 16q..16q+15) takes the 16-byte chunks q and q + 4 of its row, i.e.
+// K elements 16q.. and 64 + 16q.., for the weight and the activation fragments alike: the
+// MFMA pairs the same K elements of both operands, so the 128-wide block's sum is the same
+// set of products in another order. Chunks 2q and 2q + 1 (K elements 32q..32q+31) cost 4
+// bank-conflict cycles per ds_read_b128 under the (row/2)%8 swizzle, chunks q and q + 4
+// none (SQ_LDS_BANK_CONFLICT, measured with an in-bounds probe of both patterns).
 __device__ __forceinline__ i32x8 rd_frag(const unsigned char* base, int row, int q) {
-  const uint4 lo = *reinterpret_cast<const uint4*>(base + swz(row, 2 * q));
-  const uint4 hi = *reinterpret_cast<const uint4*>(base + swz(row, 2 * q + 1));
+  const uint4 lo = *reinterpret_cast<const uint4*>(base + swz(row, q));
+  const uint4 hi = *reinterpret_cast<const uint4*>(base + swz(row, q + 4));
   i32x8 f;
   f[0] = lo.x; f[1] = lo.y; f[2] = lo.z; f[3] = lo.w;
   f[4] = hi.x; f[5] = hi.y; f[6] = hi.z; f[7] = hi.w;
