@@ -49,8 +49,9 @@ enum { kDx = 1, kDw13 = 2, kDw2 = 3, kDh = 5, kDh128 = 6 };
 // modes whose row tiles span d_ff columns, one group per shared expert
 template <int MODE> constexpr bool kRowsByFf = MODE == kDh || MODE == kDh128;
 
-// Per mode: NA A operands (M side) and NB B operands (N side) with their K-major flags;
-// NACC accumulators; a WM x WN grid of waves, each NMB x NNB blocks of 32 x 32, so the
+// Per mode: NA A operands (M side) and NB B operands (N side) -- in the row-tile modes A is
+// K-contiguous and B K-major, in the weight-gradient modes every operand is K-major; NACC
+// accumulators; a WM x WN grid of waves, each NMB x NNB blocks of 32 x 32, so the
 // tile is TM = 32 WM NMB rows by TN = 32 WN NNB columns; kOcc: waves per SIMD the
 // register budget is held to; NST: LDS stages in the load ring (NST - 1 K-steps in
 // flight); BK: K per step. Operands whose K runs along their rows take whole 128-byte
@@ -58,28 +59,18 @@ template <int MODE> constexpr bool kRowsByFf = MODE == kDh || MODE == kDh128;
 template <int MODE> struct Cfg;
 template <> struct Cfg<kDh> {  // A: dY (K-contiguous); B: W2 (K-major)
   static constexpr int NA = 1, NB = 1, NACC = 1, WM = 2, WN = 4, NMB = 5, NNB = 2, kOcc = 2, NST = 2, BK = 64;
-  static constexpr bool a_km = false;
-  static constexpr bool b_km(int) { return true; }
 };
 template <> struct Cfg<kDh128> {  // as kDh, 128 d_ff columns per tile
   static constexpr int NA = 1, NB = 1, NACC = 1, WM = 2, WN = 4, NMB = 5, NNB = 1, kOcc = 2, NST = 2, BK = 64;
-  static constexpr bool a_km = false;
-  static constexpr bool b_km(int) { return true; }
 };
 template <> struct Cfg<kDx> {  // A: da, then dv (K-contiguous); B: W1, then W3 (K-major)
   static constexpr int NA = 1, NB = 1, NACC = 1, WM = 2, WN = 4, NMB = 5, NNB = 2, kOcc = 2, NST = 2, BK = 64;
-  static constexpr bool a_km = false;
-  static constexpr bool b_km(int) { return true; }
 };
 template <> struct Cfg<kDw13> {  // A: da, dv; B: X (all K-major)
   static constexpr int NA = 2, NB = 1, NACC = 2, WM = 2, WN = 2, NMB = 2, NNB = 2, kOcc = 2, NST = 3, BK = 32;
-  static constexpr bool a_km = true;
-  static constexpr bool b_km(int) { return true; }
 };
 template <> struct Cfg<kDw2> {  // A: dY; B: h (K-major)
   static constexpr int NA = 1, NB = 1, NACC = 1, WM = 4, WN = 2, NMB = 2, NNB = 2, kOcc = 2, NST = 3, BK = 32;
-  static constexpr bool a_km = true;
-  static constexpr bool b_km(int) { return true; }
 };
 template <int MODE> constexpr int kWaves = Cfg<MODE>::WM * Cfg<MODE>::WN;
 template <int MODE> constexpr int kTM = 32 * Cfg<MODE>::WM * Cfg<MODE>::NMB;
@@ -324,15 +315,16 @@ __device__ __forceinline__ void row_step(const BwdArgs& a, const Ctx& c, const R
     // K position: the first half of the steps runs over da (with W1), the second over dv
     // (with W3); each half spans F columns (routed) or n_s F (shared, one expert after
     // another). A step never straddles the halves or the experts (F is a multiple of 128).
+    // The shared experts' matrices lie one after another, F rows each, so K-row kk of the
+    // half is W row kk of the stacked matrices in either layout (in the tiled one, whose
+    // 128-row blocks never straddle two experts, block kk / 128 and row kk % 128 of it).
     const int64_t half = c.shared ? a.n_s * F : F;
     int64_t kk = static_cast<int64_t>(BK) * kt;
     const int second = kk >= half ? 1 : 0;
     kk -= second ? half : 0;
     sa = L.a[second] + 2 * kk;
-    const int64_t seg = c.shared ? kk / F : 0;  // shared: the expert of this K range
-    const int64_t j0 = kk - seg * F;            // first W row (d_ff index) of the step
-    const int64_t ob = a.tiled ? (j0 / 128) * (d / 64) * (128 * 64) + (j0 % 128) * 64 : j0 * d;
-    sb = L.b[second] + 2 * (seg * F * d + ob);
+    const int64_t ob = a.tiled ? (kk >> 7) * (d / 64) * (128 * 64) + (kk & 127) * 64 : kk * d;
+    sb = L.b[second] + 2 * ob;
   } else {
     sa = L.a[0] + 2 * static_cast<int64_t>(BK) * kt;
     // W2 [d][d_ff], K-rows BK kt.. (d index); tiled: 256-row blocks of 64-wide K-steps
@@ -416,26 +408,34 @@ __device__ __forceinline__ void dw_setup(const BwdArgs& a, const Ctx& c, int w, 
   }
 }
 
+// K-step kt's loads of the weight-gradient modes into a stage of the ring. sb[op]: the
+// operands' wave-uniform pointers at K-row BK kt. A step wholly within the group's rows
+// takes the SGPR-base form; the one that runs past them sends those lanes to the zeroed
+// 16 bytes at a.zero. The choice is made once per step (it is wave-uniform).
 template <int MODE>
-__device__ __forceinline__ void dw_step(const BwdArgs& a, const Ctx& c, const DwLoads<MODE>& L, int kt,
-                                        unsigned char* stage, int w, int lane) {
+__device__ __forceinline__ void dw_issue(const BwdArgs& a, const Ctx& c, const DwLoads<MODE>& L,
+                                         const unsigned char* const (&sb)[DwLoads<MODE>::NOP], int kt,
+                                         unsigned char* stage, int w, int lane) {
   constexpr int NA = Cfg<MODE>::NA, NOP = DwLoads<MODE>::NOP, BK = Cfg<MODE>::BK, NW = kWaves<MODE>;
-  const bool full = (kt + 1) * BK <= c.rows;  // wave-uniform
+  if ((kt + 1) * BK <= c.rows) {
 #pragma unroll
-  for (int op = 0; op < NOP; ++op) {
-    const unsigned char* sb = L.base[op] + static_cast<int64_t>(kt) * BK * L.row_bytes[op];
-    const int width = op < NA ? kTM<MODE> : kTN<MODE>;
-    const int per_wave = op_bytes<MODE>(op) / 16 / NW;
+    for (int op = 0; op < NOP; ++op) {
+      const int per_wave = op_bytes<MODE>(op) / 16 / NW;
 #pragma unroll
-    for (int i = 0; i < dw_instrs<MODE>(op); ++i) {
-      unsigned char* dst = stage + op_offset<MODE>(op) + (per_wave * w + 64 * i) * 16;
-      if (full) {
-        dma16s(L.off[op][i], sb, dst);
-      } else {
+      for (int i = 0; i < dw_instrs<MODE>(op); ++i)
+        dma16s(L.off[op][i], sb[op], stage + op_offset<MODE>(op) + (per_wave * w + 64 * i) * 16);
+    }
+  } else {
+#pragma unroll
+    for (int op = 0; op < NOP; ++op) {
+      const int width = op < NA ? kTM<MODE> : kTN<MODE>;
+      const int per_wave = op_bytes<MODE>(op) / 16 / NW;
+#pragma unroll
+      for (int i = 0; i < dw_instrs<MODE>(op); ++i) {
         int x, y;
         km_slot(per_wave * w + 64 * i + lane, width, x, y);
-        dma16(kt * BK + x < c.rows ? static_cast<const void*>(sb + L.off[op][i]) : static_cast<const void*>(a.zero),
-              dst);
+        dma16(kt * BK + x < c.rows ? static_cast<const void*>(sb[op] + L.off[op][i]) : static_cast<const void*>(a.zero),
+              stage + op_offset<MODE>(op) + (per_wave * w + 64 * i) * 16);
       }
     }
   }
@@ -458,55 +458,155 @@ __device__ __forceinline__ void ring_wait() {
     asm volatile("s_waitcnt vmcnt(%0)\n\ts_waitcnt lgkmcnt(0)\n\ts_barrier" ::"n"(N) : "memory");
 }
 
-// One K-step's MFMAs for the first NL of the wave's NMB 32-row blocks (the others hold no
-// rows of the tile).
+// One K-step's MFMAs of the row-tile modes for the first NL of the wave's NMB 32-row blocks
+// (the others hold no rows of the tile).
 template <int MODE, int NL>
 __device__ __forceinline__ void compute(const unsigned char* base,
                                         f32x16 (&acc)[Cfg<MODE>::NACC][Cfg<MODE>::NMB][Cfg<MODE>::NNB], int wm,
                                         int wn, int lane) {
-  constexpr int NA = Cfg<MODE>::NA, NB = Cfg<MODE>::NB, BK = Cfg<MODE>::BK;
+  static_assert(Cfg<MODE>::NA == 1 && Cfg<MODE>::NB == 1 && Cfg<MODE>::NACC == 1, "the row-tile modes");
+  constexpr int BK = Cfg<MODE>::BK;
   constexpr int NMB = NL, NNB = Cfg<MODE>::NNB;
   constexpr int TM = kTM<MODE>, TN = kTN<MODE>;
   const int r0 = (TM / Cfg<MODE>::WM) * wm, n0 = (TN / Cfg<MODE>::WN) * wn;
 #pragma unroll
   for (int s = 0; s < BK / 16; ++s) {
-    bf16x8 fa[NA][NMB > 0 ? NMB : 1], fb[NB][NNB];
+    bf16x8 fa[NMB > 0 ? NMB : 1], fb[NNB];
+#pragma unroll
+    for (int mb = 0; mb < NMB; ++mb) fa[mb] = frag_kc<BK>(base + op_offset<MODE>(0), r0 + 32 * mb, s, lane);
+#pragma unroll
+    for (int nb = 0; nb < NNB; ++nb) fb[nb] = frag_km<2 * TN>(base + op_offset<MODE>(1), n0 + 32 * nb, s, lane);
+#pragma unroll
+    for (int mb = 0; mb < NMB; ++mb)
+#pragma unroll
+      for (int nb = 0; nb < NNB; ++nb)
+        // the n-side fragment goes first, so each lane's accumulator holds 4 consecutive
+        // output columns of one output row (see the epilogue)
+        acc[0][mb][nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fb[nb], fa[mb], acc[0][mb][nb], 0, 0, 0);
+  }
+}
+
+// This lane's fragment addresses (LDS bytes, stage 0) in the weight-gradient modes, one
+// per operand and 32-block: with k = 16 s + k0 and k0 = 8 (lane/16 / 2) + lane%16 / 4, the
+// swizzle term k & 3 does not depend on s, so a fragment of sub-step s lies at the base
+// plus the stage's offset, plus 16 s RB (and its upper half 4 RB further), which are
+// immediate offsets of the transposing read.
+template <int MODE>
+struct DwFrag {
+  uint32_t a[Cfg<MODE>::NA][Cfg<MODE>::NMB];
+  uint32_t b[Cfg<MODE>::NNB];
+};
+
+template <int MODE>
+__device__ __forceinline__ void dw_frag_setup(const unsigned char* lds, int wm, int wn, int lane, DwFrag<MODE>& f) {
+  constexpr int TM = kTM<MODE>, TN = kTN<MODE>, NA = Cfg<MODE>::NA;
+  const uint32_t l0 = static_cast<uint32_t>(reinterpret_cast<uintptr_t>((lds_ptr)(lds)));
+  const int g = lane / 16, j = lane % 16;
+  const int k0 = 8 * (g / 2) + j / 4, cl = 16 * (g % 2) + 4 * (j % 4);
+  const int r0 = (TM / Cfg<MODE>::WM) * wm, n0 = (TN / Cfg<MODE>::WN) * wn;
+#pragma unroll
+  for (int op = 0; op < NA; ++op)
+#pragma unroll
+    for (int mb = 0; mb < Cfg<MODE>::NMB; ++mb)
+      f.a[op][mb] = l0 + op_offset<MODE>(op) + km_off<2 * TM>(k0, 2 * (r0 + 32 * mb + cl));
+#pragma unroll
+  for (int nb = 0; nb < Cfg<MODE>::NNB; ++nb)
+    f.b[nb] = l0 + op_offset<MODE>(NA) + km_off<2 * TN>(k0, 2 * (n0 + 32 * nb + cl));
+}
+
+// The 8 consecutive k of a fragment: two transposing reads 4 K-rows apart.
+template <int RB>
+__device__ __forceinline__ bf16x8 frag_at(uint32_t base, int off) {
+  typedef __attribute__((address_space(3))) v4s lds_v4s;
+  const v4s lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4s*)(base + off));
+  const v4s hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4s*)(base + off + 4 * RB));
+  return __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+}
+
+// One K-step's MFMAs of the weight-gradient modes from stage ST.
+template <int MODE>
+__device__ __forceinline__ void compute_dw(const DwFrag<MODE>& f, uint32_t stage_off,
+                                           f32x16 (&acc)[Cfg<MODE>::NACC][Cfg<MODE>::NMB][Cfg<MODE>::NNB]) {
+  constexpr int NA = Cfg<MODE>::NA, NMB = Cfg<MODE>::NMB, NNB = Cfg<MODE>::NNB, BK = Cfg<MODE>::BK;
+  constexpr int TM = kTM<MODE>, TN = kTN<MODE>;
+  static_assert(16 * (BK / 16 - 1) * 2 * (TM > TN ? TM : TN) + 4 * 2 * (TM > TN ? TM : TN) < 65536,
+                "the fragment offsets fit the read's 16-bit immediate");
+  uint32_t ba[NA][NMB], bb[NNB];  // this step's fragment bases
+#pragma unroll
+  for (int op = 0; op < NA; ++op)
+#pragma unroll
+    for (int mb = 0; mb < NMB; ++mb) ba[op][mb] = f.a[op][mb] + stage_off;
+#pragma unroll
+  for (int nb = 0; nb < NNB; ++nb) bb[nb] = f.b[nb] + stage_off;
+#pragma unroll
+  for (int s = 0; s < BK / 16; ++s) {
+    bf16x8 fa[NA][NMB], fb[NNB];
 #pragma unroll
     for (int op = 0; op < NA; ++op)
 #pragma unroll
-      for (int mb = 0; mb < NMB; ++mb) {
-        const unsigned char* t = base + op_offset<MODE>(op);
-        fa[op][mb] = Cfg<MODE>::a_km ? frag_km<2 * TM>(t, r0 + 32 * mb, s, lane)
-                                     : frag_kc<BK>(t, r0 + 32 * mb, s, lane);
-      }
+      for (int mb = 0; mb < NMB; ++mb) fa[op][mb] = frag_at<2 * TM>(ba[op][mb], 16 * s * 2 * TM);
 #pragma unroll
-    for (int op = 0; op < NB; ++op)
-#pragma unroll
-      for (int nb = 0; nb < NNB; ++nb) {
-        const unsigned char* t = base + op_offset<MODE>(NA + op);
-        fb[op][nb] = Cfg<MODE>::b_km(op) ? frag_km<2 * TN>(t, n0 + 32 * nb, s, lane)
-                                         : frag_kc<BK>(t, n0 + 32 * nb, s, lane);
-      }
+    for (int nb = 0; nb < NNB; ++nb) fb[nb] = frag_at<2 * TN>(bb[nb], 16 * s * 2 * TN);
 #pragma unroll
     for (int mb = 0; mb < NMB; ++mb)
 #pragma unroll
       for (int nb = 0; nb < NNB; ++nb) {
-        // the n-side fragment goes first, so each lane's accumulator holds 4 consecutive
-        // output columns of one output row (see the epilogue)
-        if constexpr (MODE == kDw13) {
-          acc[0][mb][nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fb[0][nb], fa[0][mb], acc[0][mb][nb], 0, 0, 0);
-          acc[1][mb][nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fb[0][nb], fa[1][mb], acc[1][mb][nb], 0, 0, 0);
-        } else {
-          acc[0][mb][nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fb[0][nb], fa[0][mb], acc[0][mb][nb], 0, 0, 0);
-        }
+        // the n-side fragment first, as in compute
+        acc[0][mb][nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fb[nb], fa[0][mb], acc[0][mb][nb], 0, 0, 0);
+        if constexpr (MODE == kDw13)
+          acc[1][mb][nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fb[nb], fa[1][mb], acc[1][mb][nb], 0, 0, 0);
       }
   }
 }
 
-// The load ring and MFMAs of one tile, for NL live row blocks per wave: steps 0 .. NST - 2
-// first; at step kt, once step kt has landed, the load of step kt + NST - 1 goes into the
-// stage step kt - 1 was read from (every wave is past that read: it came before the
-// barrier). On exit every wave is past its last read of the ring.
+// The weight-gradient K loop, a ring of three stages: steps 0 and 1 first; at step kt, once
+// it has landed (step kt + 1's loads may stay in flight), step kt + 2 goes into the stage
+// step kt - 1 was read from (every wave is past that read: it came before the barrier),
+// then the MFMAs. The stages' offsets rotate in scalar registers and each operand's
+// pointer moves by one scalar add per step, so the loop spends its vector instructions on
+// the transposing reads and the MFMAs. On exit every wave is past its last read of the ring.
+template <int MODE>
+__device__ __forceinline__ void k_loop_dw(const BwdArgs& a, const Ctx& c, const DwLoads<MODE>& dl,
+                                          unsigned char* lds,
+                                          f32x16 (&acc)[Cfg<MODE>::NACC][Cfg<MODE>::NMB][Cfg<MODE>::NNB], int w,
+                                          int wm, int wn, int lane) {
+  static_assert(Cfg<MODE>::NST == 3, "a ring of three stages");
+  constexpr int NOP = DwLoads<MODE>::NOP, BK = Cfg<MODE>::BK, kStage = kStageBytes<MODE>;
+  constexpr int ND = loads_per_step<MODE>();  // loads per wave per K-step
+  const unsigned char* sb[NOP];
+  int64_t adv[NOP];
+#pragma unroll
+  for (int op = 0; op < NOP; ++op) {
+    sb[op] = dl.base[op];
+    adv[op] = BK * dl.row_bytes[op];
+  }
+  DwFrag<MODE> f;
+  dw_frag_setup<MODE>(lds, wm, wn, lane, f);
+  auto issue = [&](int kt, uint32_t off) {
+    dw_issue<MODE>(a, c, dl, sb, kt, lds + off, w, lane);
+#pragma unroll
+    for (int op = 0; op < NOP; ++op) sb[op] += adv[op];
+  };
+  issue(0, 0);
+  if (1 < c.nk) issue(1, kStage);
+  uint32_t rd = 0, wr = 2 * kStage;  // the stage read at step kt, the stage step kt + 2 goes into
+  for (int kt = 0; kt < c.nk; ++kt) {
+    if (kt + 1 < c.nk)
+      ring_wait<ND>();
+    else
+      ring_wait<0>();
+    if (kt + 2 < c.nk) issue(kt + 2, wr);
+    compute_dw<MODE>(f, rd, acc);
+    rd = rd == 2 * kStage ? 0 : rd + kStage;
+    wr = wr == 2 * kStage ? 0 : wr + kStage;
+  }
+}
+
+// The load ring and MFMAs of one tile, for NL live row blocks per wave. The row-tile modes
+// run a ring of two stages: step 0 first; at step kt, once step kt has landed, step kt + 1
+// goes into the stage step kt - 1 was read from (every wave is past that read: it came
+// before the barrier). The weight-gradient modes run k_loop_dw. On exit every wave is past
+// its last read of the ring.
 template <int MODE, int NL>
 __device__ __forceinline__ void k_loop(const BwdArgs& a, const Ctx& c, const DwLoads<MODE>& dl,
                                        const RowLoads<MODE>& rl, unsigned char* lds,
@@ -514,25 +614,16 @@ __device__ __forceinline__ void k_loop(const BwdArgs& a, const Ctx& c, const DwL
                                        int wm, int wn, int lane) {
   constexpr int NST = Cfg<MODE>::NST;
   constexpr int kStage = kStageBytes<MODE>;
-  constexpr int ND = loads_per_step<MODE>();  // loads per wave per K-step
-  constexpr bool kDw = MODE == kDw13 || MODE == kDw2;
-  auto issue = [&](int kt, unsigned char* st) {
-    if constexpr (kDw)
-      dw_step<MODE>(a, c, dl, kt, st, w, lane);
-    else
-      row_step<MODE>(a, c, rl, kt, st, w);
-  };
-#pragma unroll
-  for (int s0 = 0; s0 < NST - 1; ++s0)
-    if (s0 < c.nk) issue(s0, lds + s0 * kStage);
-  for (int kt = 0; kt < c.nk; ++kt) {
-    if (NST == 3 && kt + 1 < c.nk)
-      ring_wait<ND>();  // step kt + 1's loads may stay in flight (the weight-gradient modes,
-                        // whose waves all issue ND loads per step)
-    else
+  if constexpr (MODE == kDw13 || MODE == kDw2) {
+    k_loop_dw<MODE>(a, c, dl, lds, acc, w, wm, wn, lane);
+  } else {
+    static_assert(NST == 2, "the row-tile modes run a ring of two stages");
+    row_step<MODE>(a, c, rl, 0, lds, w);
+    for (int kt = 0; kt < c.nk; ++kt) {
       ring_wait<0>();
-    if (kt + NST - 1 < c.nk) issue(kt + NST - 1, lds + ((kt + NST - 1) % NST) * kStage);
-    compute<MODE, NL>(lds + (kt % NST) * kStage, acc, wm, wn, lane);
+      if (kt + 1 < c.nk) row_step<MODE>(a, c, rl, kt + 1, lds + ((kt + 1) % 2) * kStage, w);
+      compute<MODE, NL>(lds + (kt % 2) * kStage, acc, wm, wn, lane);
+    }
   }
 }
 
