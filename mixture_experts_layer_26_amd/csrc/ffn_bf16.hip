@@ -243,6 +243,7 @@ __device__ __forceinline__ void k_step(const TileCtx<G>& c, int s, int wave, int
                                        int lane, Frags<NMB>& f0, Frags<NMB>& f1, f32x16 (&acc)[G::kMB][2],
                                        bool dma, bool read, int newer) {
   constexpr int NMF = 2 * NMB, S = G::kS, NX = (ST + 1) % S;
+  static_assert(kSubs == 4, "a K-step is four 16-wide sub-steps, read in alternating fragment sets");
   mfma_sub(f0, acc);
   fence();
   read_frags<ST, G, NMB>(f0, 2, arow0, brow, lane);
