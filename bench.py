@@ -15,7 +15,8 @@ for its grouped FFN (the two expert GEMM launches, >99% of the FLOPs) timed with
 events on the launch stream, and the CPU oracle timed on a bounded sample of the same
 workload. The other workloads (FP8 prefill, skewed decode, mid and tiny) are timed
 after it in the same run and appear under "workloads", each with its own roofline
-and oracle baseline.
+and oracle baseline, followed by one GPU's share of the V3 layer under 8-way expert
+parallelism (32 local experts of about 2048 rows each, bf16 and FP8).
 
 --backward times the layer backward instead (moe_combine_backward ->
 moe_grouped_ffn_backward -> moe_route_backward after one forward step, bf16 weights in
@@ -289,10 +290,17 @@ def cpu_baseline(w, n_tokens: int):
 
 # Oracle sample per workload: about 5-15 s of host time each on 16 cores.
 CPU_TOKENS = {"v3_prefill_bf16": 384, "v3_prefill_fp8": 256, "v3_decode_skewed": 128, "mid_bf16": 512,
-              "tiny_f32": 64}
+              "tiny_f32": 64, "v3_ep8_share_bf16": 384, "v3_ep8_share_fp8": 256}
 # Timed steps of the workloads timed beside the headline one (the headline takes --steps).
-SUB_STEPS = {"v3_prefill_fp8": 20, "v3_decode_skewed": 50, "mid_bf16": 100, "tiny_f32": 200}
-SUB_WORKLOADS = ("v3_prefill_fp8", "v3_decode_skewed", "mid_bf16", "tiny_f32")
+SUB_STEPS = {"v3_prefill_fp8": 20, "v3_decode_skewed": 50, "mid_bf16": 100, "tiny_f32": 200,
+             "v3_ep8_share_bf16": 20, "v3_ep8_share_fp8": 20}
+SUB_WORKLOADS = ("v3_prefill_fp8", "v3_decode_skewed", "mid_bf16", "tiny_f32", "v3_ep8_share_bf16",
+                 "v3_ep8_share_fp8")
+
+
+def fp8_twin(name: str) -> str:
+    """The FP8 workload drawn from the same tensors as a bf16 one."""
+    return name.replace("_bf16", "_fp8")
 
 
 def bench_forward(wname: str, layout: str, steps: int, warmup: int, cpu: bool, cpu_tokens: int,
@@ -520,7 +528,7 @@ def main():
     also = [] if args.also in ("", "none") else [x for x in args.also.split(",") if x and x != args.workload]
     cache = {}
     head = bench_forward(args.workload, args.layout, args.steps, args.warmup, args.cpu, args.cpu_tokens, cache,
-                         keep_rows=any(x == "v3_prefill_fp8" for x in also), calibrate=args.calibrate_copy)
+                         keep_rows=fp8_twin(args.workload) in also, calibrate=args.calibrate_copy)
     res = {
         "metric": "MoE layer tokens/s + TFLOP/s (% MFMA peak), V3 shape bf16/fp8, 1 MI355X",
         "value": head.pop("value"),
@@ -541,7 +549,8 @@ def main():
     if also:
         res["workloads"] = {}
     for name in also:
-        sub = bench_forward(name, args.layout, SUB_STEPS.get(name, args.steps), args.warmup, args.cpu, 0, cache)
+        sub = bench_forward(name, args.layout, SUB_STEPS.get(name, args.steps), args.warmup, args.cpu, 0, cache,
+                            keep_rows=name != fp8_twin(name) and fp8_twin(name) in also)
         res["workloads"][name] = sub
         log(f"[bench] {name}: {sub['value']:.1f} tokens/s, grouped FFN {sub['roofline']['ms_per_launch']} ms, "
             f"frac {sub['roofline']['frac']}")

@@ -6,10 +6,10 @@ oracle's tests have in common.  Values come from ``gen.c`` (Philox4x32-10 bits,
 Box-Muller normals), so element ``i`` of a tensor depends only on
 ``(seed, tensor id, i)`` and any slice can be regenerated alone.
 
-The five workloads follow the layer shapes of the DeepSeek-V3 explainer
+The workloads follow the layer shapes of the DeepSeek-V3 explainer
 ("DeepSeek-V3 テクニカルレポート 論文解説", key ideas: 1 shared + 256 routed
-experts with 8 active; method section 2 for the layer) plus two smaller
-shapes.  Shapes, distributions and seeds are fixed here; the design doc lists
+experts with 8 active; method section 2 for the layer), one GPU's share of that
+layer under 8-way expert parallelism, and two smaller shapes.  Shapes, distributions and seeds are fixed here; the design doc lists
 the recipe.
 """
 from __future__ import annotations
@@ -83,6 +83,14 @@ WORKLOADS = {
     "v3_decode_skewed": Workload("v3_decode_skewed", T=128, d=7168, n_routed=256, top_k=8, n_shared=1,
                                  d_ff=2048, act=BF16, ffn=BF16, seed=2605, bias_range=0.01,
                                  hot_experts=tuple(range(0, 256, 32)), hot_scale=3.0),
+    # One GPU's share of the V3 layer under expert parallelism over 8 GPUs: 32 local routed
+    # experts receiving about 2048 rows each (T*K/N_r of the 8 GPUs' tokens) and the local
+    # shared expert over this GPU's 8192 tokens, drawn as a layer of 32 routed experts with
+    # top-8 over 8192 tokens, which gives the grouped FFN that shape.
+    "v3_ep8_share_bf16": Workload("v3_ep8_share_bf16", T=8192, d=7168, n_routed=32, top_k=8, n_shared=1,
+                                  d_ff=2048, act=BF16, ffn=BF16, seed=2607, bias_range=0.01),
+    "v3_ep8_share_fp8": Workload("v3_ep8_share_fp8", T=8192, d=7168, n_routed=32, top_k=8, n_shared=1,
+                                 d_ff=2048, act=BF16, ffn=FP8, seed=2607, bias_range=0.01),
 }
 
 _lib = None

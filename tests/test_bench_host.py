@@ -50,7 +50,8 @@ def test_fp8_bytes_include_block_scales():
 def test_roofline_kind_per_workload():
     kinds = {n: bench.roofline_kind(w) for n, w in I.WORKLOADS.items()}
     assert kinds == {"tiny_f32": "latency", "mid_bf16": "mfma", "v3_prefill_bf16": "mfma",
-                     "v3_prefill_fp8": "mfma", "v3_decode_skewed": "hbm"}
+                     "v3_prefill_fp8": "mfma", "v3_decode_skewed": "hbm", "v3_ep8_share_bf16": "mfma",
+                     "v3_ep8_share_fp8": "mfma"}
 
 
 def test_sub_workloads_cover_every_other_workload():

@@ -129,7 +129,7 @@ def _layer(w):
 
 
 @pytest.mark.timeout(900)
-@pytest.mark.parametrize("base,T", [("mid_bf16", 512), ("v3_prefill_bf16", None)])
+@pytest.mark.parametrize("base,T", [("mid_bf16", 512), ("v3_prefill_bf16", None), ("v3_ep8_share_bf16", None)])
 def test_fp8_layer_end_to_end(base, T):
     """The V3 prefill workload in FP8, and the mid shape in FP8 (d = 2048, d_ff = 1408,
     two shared experts, ragged 11-block d_ff), on the tensors of the bf16 workloads. 64

@@ -18,7 +18,7 @@ from tests.gpu_util import (FROB_TOL, MAXABS_TOL, ROW_TOL, check_routing, host_e
 
 pytestmark = pytest.mark.gpu
 
-BF16_CONFIGS = ["mid_bf16", "v3_prefill_bf16", "v3_decode_skewed"]
+BF16_CONFIGS = ["mid_bf16", "v3_prefill_bf16", "v3_decode_skewed", "v3_ep8_share_bf16"]
 ALL_CONFIGS = ["tiny_f32"] + BF16_CONFIGS
 
 
@@ -206,7 +206,7 @@ def _oracle_layer_for(w, u_rows, e, b):
                         want_components=True)
 
 
-SAMPLES = {"tiny_f32": 64, "mid_bf16": 96, "v3_prefill_bf16": 64, "v3_decode_skewed": 64}
+SAMPLES = {"tiny_f32": 64, "mid_bf16": 96, "v3_prefill_bf16": 64, "v3_decode_skewed": 64, "v3_ep8_share_bf16": 64}
 
 
 @pytest.mark.timeout(600)
