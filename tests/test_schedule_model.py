@@ -13,7 +13,8 @@ under random interleavings of the workgroups, on random and skewed expert loads,
   abi.cpp, counted in 256-row blocks, so it also bounds the taller tiles) and no gang
   reads past its row of slots (slot stride ceil(max/G) + 2);
 - the list order: shared groups first, then routed experts with an even number of row
-  blocks, then those with an odd number.
+  blocks, then those with an odd number, each pass by row count (most first, ties to the
+  lower id).
 
 It is a model: it checks the protocol's design, and the GPU parity tests check the
 kernels that implement it.
@@ -29,16 +30,18 @@ SMALL_BATCH = 128  # batches of at most this many tokens: bf16 tiles of 128 rows
 
 def tile_map(rows, n_r, rb=BM):
     """Row blocks of at most rb rows per group, rows per block, and the list order (shared,
-    even, odd)."""
+    even, odd; the routed experts of each pass by row count, most first)."""
     mt, rpb = [], []
     for r in rows:
         mt0 = (r + rb - 1) // rb
         p = (r + mt0 - 1) // mt0 if mt0 else 0
         rpb.append(p)
         mt.append((r + p - 1) // p if p else 0)
+    # routed experts by row count, most first, ties to the lower id
+    by_rows = sorted(range(n_r), key=lambda g: (-rows[g], g))
     order = [g for g in range(n_r, len(rows)) if mt[g]]
-    order += [g for g in range(n_r) if mt[g] and mt[g] % 2 == 0]
-    order += [g for g in range(n_r) if mt[g] and mt[g] % 2 == 1]
+    order += [g for g in by_rows if mt[g] and mt[g] % 2 == 0]
+    order += [g for g in by_rows if mt[g] and mt[g] % 2 == 1]
     return mt, rpb, order
 
 
@@ -170,7 +173,7 @@ def test_tile_order():
     mt, rpb, order = tile_map(rows, 5)
     assert mt == [2, 0, 3, 1, 3, 36, 1]
     assert rpb == [150, 0, 200, 256, 171, 250, 70]
-    assert order == [5, 6, 0, 2, 3, 4]
+    assert order == [5, 6, 0, 2, 4, 3]  # odd pass: 600, 513, 256 rows
     mt, rpb, order = tile_map(rows, 5, 320)  # the bf16 kernel's phase-1 tiles
     assert mt == [1, 0, 2, 1, 2, 29, 1]
     assert rpb == [300, 0, 300, 256, 257, 311, 70]
@@ -221,3 +224,20 @@ def test_shared_block_order_closed_form():
             got = [_shared_tile_at(L, mt, ntn) for L in range(mt * ntn)]
             assert got == want, (mt, ntn)
             assert len(set(got)) == mt * ntn
+
+
+def test_tile_order_by_rows():
+    """Each routed pass runs from the expert with the most rows to the one with the fewest;
+    equal counts keep ascending ids, and the shared groups stay first in id order."""
+    rows = [100, 250, 100, 600, 0, 250, 700, 640, 8192]  # n_r = 8, one shared group
+    mt, _, order = tile_map(rows, 8, 320)
+    assert mt[:8] == [1, 1, 1, 2, 0, 1, 3, 2]
+    assert order == [8, 7, 3, 6, 1, 5, 0, 2]
+    rng = np.random.default_rng(6)
+    counts = list(_counts(rng, 8192, 8, 256, 20.0))
+    mt, _, order = tile_map(counts + [8192], 256, 320)
+    routed = [g for g in order if g < 256]
+    for par in (0, 1):
+        seq = [g for g in routed if mt[g] % 2 == par]
+        assert all((counts[a], -a) > (counts[b], -b) for a, b in zip(seq, seq[1:]))
+    assert sorted(routed) == [g for g in range(256) if mt[g]]
