@@ -191,6 +191,35 @@ def time_steps(w, dev, L, steps: int, warmup: int):
     return elapsed, step_ms, ffn_ms, counts.cpu().numpy()
 
 
+def time_graph(w, dev, L, steps: int, warmup: int):
+    """The layer step of a launch-bound batch replayed from a HIP graph: the five calls
+    are captured once (after the eager steps, so every kernel is loaded) and each replay
+    runs them with one host launch. b is restored before every replay, outside the graph
+    and outside the replay's events, as in time_steps. Returns (wall seconds of the K
+    replays, per-replay ms from HIP events on the launch stream)."""
+    import torch
+
+    stream = torch.cuda.current_stream()
+    b0 = dev["b"]
+    bias = b0.clone()
+    g = L.capture_step(dev["u"], dev["e"], bias, w.gamma)
+    for _ in range(warmup):
+        bias.copy_(b0)
+        g.replay()
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(steps):
+        bias.copy_(b0)
+        ev[i][0].record(stream)
+        g.replay()
+        ev[i][1].record(stream)
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    del g
+    return elapsed, [e[0].elapsed_time(e[1]) for e in ev]
+
+
 def call_breakdown(w, dev, L, steps: int = 3):
     """Average milliseconds of each ABI call (HIP events on the launch stream), the bias
     restored before every step as in the timed loop."""
@@ -362,6 +391,12 @@ def bench_forward(wname: str, layout: str, steps: int, warmup: int, cpu: bool, c
     if kind == "latency":
         res["us_per_step"] = round(1e3 * ms_ev, 2)
         res["call_us"] = {k: round(1e3 * v, 2) for k, v in calls.items()}
+        # a launch-bound step run as HIP-graph replays: the same five calls, one host launch
+        g_elapsed, g_ms = time_graph(w, dev, L, steps, warmup)
+        res["graph"] = {"us_per_step": round(1e3 * sum(g_ms) / len(g_ms), 2),
+                        "tokens_per_s": round(w.T * steps / g_elapsed, 1), "replays": steps,
+                        "how": "route, dispatch, grouped FFN, combine and bias update captured once into a "
+                               "HIP graph and replayed; b restored before each replay, outside the graph"}
     del L, dev
     torch.cuda.synchronize()
     torch.cuda.empty_cache()

@@ -11,7 +11,8 @@
 // bf16 MFMA 32x32x16 in fp32; it writes the chunk's partial logits. route_topk: one
 // wave per token adds the chunks' partials in chunk order, takes the sigmoid and
 // selects the top-K with 64-bit (score, ~index) keys reduced across the wave. fp32
-// activations take one kernel of plain fp32 dot products (route_kernel).
+// activations take one kernel (route_kernel): fp32 dot products from LDS-staged chunks of u
+// and e, then the same selection.
 #include "gemm_common.h"
 #include "launch.h"
 
@@ -19,7 +20,7 @@ namespace moe {
 
 namespace {
 
-constexpr int kTok = 32;
+constexpr int kTokF32 = 8;  // tokens per workgroup of the fp32 router: one per wave
 constexpr int kThreads = 512;
 constexpr int kMaxExperts = 256;
 
@@ -213,33 +214,91 @@ __global__ __launch_bounds__(256) void route_topk(const float* __restrict__ part
   topk_select<SCORE == 1>(key, sv, lane, K, topk_idx + t * K, topk_gate + t * K);
 }
 
+// fp32 logits of the workgroup's kTokF32 tokens against every expert, accumulated in zs
+// ([kTokF32][n_r]). u and e go to LDS in K chunks (256 wide when N_r <= 64, else 64, so
+// that both fit beside zs) with 16-byte coalesced loads, at a pitch of one float more
+// than the chunk so that the experts (and tokens) a wave reads at one k fall in
+// different banks; each (token, expert) logit is one fp32 FMA chain in ascending k,
+// carried in zs from chunk to chunk. Tokens past T repeat the last token (their logits
+// are not used).
+constexpr int kStageFloats = (kTokF32 + 64) * 257;  // the larger of the two chunk layouts
+static_assert(kStageFloats >= (kTokF32 + kMaxExperts) * 65, "the 64-wide chunks fit");
+constexpr int kPerF32 = 8;  // float4 loads a thread keeps in flight while staging
+
 __device__ void logits_f32(const float* __restrict__ u, const float* __restrict__ e, int64_t T,
-                           int d, int n_r, int64_t t0, float* zs) {
-  for (int p = threadIdx.x; p < kTok * n_r; p += kThreads) {
-    const int i = p / n_r, j = p % n_r;
-    int64_t t = t0 + i;
-    if (t >= T) t = T - 1;
-    const float* a = u + t * d;
-    const float* b = e + static_cast<int64_t>(j) * d;
-    float z = 0.0f;
-    for (int c = 0; c < d; ++c) z = fmaf(a[c], b[c], z);
-    zs[i * n_r + j] = z;
+                           int d, int n_r, int64_t t0, float* zs, float* stage) {
+  const int kcmax = n_r <= 64 ? 256 : 64;
+  const int pitch = kcmax + 1;
+  float* us = stage;
+  float* es = stage + kTokF32 * pitch;
+  for (int k0 = 0; k0 < d; k0 += kcmax) {
+    const int kc = d - k0 < kcmax ? d - k0 : kcmax;  // d is a multiple of 64
+    const int q4 = kc / 4;
+    if (k0 > 0) __syncthreads();  // the previous chunk has been read
+    // rows 0..kTokF32-1 of the chunk are u's, the rest e's; each thread issues all its loads
+    // of a pass before its LDS stores, so they are in flight together
+    const int n = (kTokF32 + n_r) * q4;
+    for (int q0 = 0; q0 < n; q0 += kThreads * kPerF32) {
+      float4 v[kPerF32];
+#pragma unroll
+      for (int i = 0; i < kPerF32; ++i) {
+        const int q = q0 + threadIdx.x + i * kThreads;
+        if (q < n) {
+          const int row = q / q4, k = 4 * (q % q4);
+          int64_t t = t0 + row;
+          if (t >= T) t = T - 1;
+          const float* src = row < kTokF32 ? u + t * d + k0 + k : e + static_cast<int64_t>(row - kTokF32) * d + k0 + k;
+          v[i] = *reinterpret_cast<const float4*>(src);
+        }
+      }
+#pragma unroll
+      for (int i = 0; i < kPerF32; ++i) {
+        const int q = q0 + threadIdx.x + i * kThreads;
+        if (q < n) {
+          const int row = q / q4, k = 4 * (q % q4);
+          float* dst = row < kTokF32 ? us + row * pitch + k : es + (row - kTokF32) * pitch + k;
+          dst[0] = v[i].x;
+          dst[1] = v[i].y;
+          dst[2] = v[i].z;
+          dst[3] = v[i].w;
+        }
+      }
+    }
+    __syncthreads();
+    for (int p = threadIdx.x; p < kTokF32 * n_r; p += kThreads) {
+      const int i = p / n_r, j = p % n_r;
+      const float* a = us + i * pitch;
+      const float* b = es + j * pitch;
+      float z = k0 == 0 ? 0.0f : zs[p];
+      for (int c = 0; c < kc; c += 16) {  // 16 values read ahead of their FMAs (kc % 64 == 0)
+        float av[16], bv[16];
+#pragma unroll
+        for (int q = 0; q < 16; ++q) {
+          av[q] = a[c + q];
+          bv[q] = b[c + q];
+        }
+#pragma unroll
+        for (int q = 0; q < 16; ++q) z = fmaf(av[q], bv[q], z);
+      }
+      zs[p] = z;
+    }
   }
 }
 
-// fp32 activations: one workgroup of 8 waves owns 32 tokens; logits are plain fp32
-// dot products parked in LDS, then one wave per token scores and selects.
+// fp32 activations: one workgroup of 8 waves owns 8 tokens; their logits are formed in
+// LDS (logits_f32), then one wave per token scores and selects.
 template <int SCORE>
 __global__ __launch_bounds__(kThreads) void route_kernel(const float* __restrict__ u, const float* __restrict__ e,
                                                          const float* __restrict__ bias, int64_t T, int d, int n_r,
                                                          int K, int32_t* __restrict__ topk_idx,
                                                          float* __restrict__ topk_gate) {
-  __shared__ float zs[kTok * kMaxExperts];
-  const int64_t t0 = static_cast<int64_t>(blockIdx.x) * kTok;
-  logits_f32(u, e, T, d, n_r, t0, zs);
+  __shared__ float zs[kTokF32 * kMaxExperts];
+  __shared__ float stage[kStageFloats];
+  const int64_t t0 = static_cast<int64_t>(blockIdx.x) * kTokF32;
+  logits_f32(u, e, T, d, n_r, t0, zs, stage);
   __syncthreads();
   const int lane = threadIdx.x % kWave, wave = threadIdx.x / kWave;
-  for (int i = wave; i < kTok; i += kThreads / kWave) {
+  for (int i = wave; i < kTokF32; i += kThreads / kWave) {
     const int64_t t = t0 + i;
     if (t >= T) break;
     uint64_t key[4];
@@ -293,7 +352,7 @@ hipError_t launch_route(int act, int score, const void* u, const void* e, const 
       hipLaunchKernelGGL(route_topk<0>, tgrid, dim3(256), 0, stream, part, rc.chunks, bias, T, n_r, K, idx, gate);
     return hipGetLastError();
   }
-  const dim3 grid(static_cast<unsigned>((T + kTok - 1) / kTok));
+  const dim3 grid(static_cast<unsigned>((T + kTokF32 - 1) / kTokF32));
   if (score == 1)
     hipLaunchKernelGGL(route_kernel<1>, grid, dim3(kThreads), 0, stream, static_cast<const float*>(u),
                        static_cast<const float*>(e), bias, T, d, n_r, K, idx, gate);

@@ -120,6 +120,22 @@ class MoeLayer:
         self.bias_update(bias, gamma, stream)
         return self.out
 
+    def capture_step(self, u, centroids, bias, gamma: float = 0.001):
+        """The five calls of `step` recorded once into a HIP graph (torch.cuda.CUDAGraph) on
+        these tensors; `replay()` then runs a whole step with one launch from the host,
+        which is what a batch small enough to be bound by launch latency needs. The calls
+        allocate nothing, record no memset and never synchronise, so they can be captured;
+        every replay reads u, centroids and bias and writes the layer's buffers and bias as
+        an eager step would (bias moves by the update each replay)."""
+        g = torch.cuda.CUDAGraph()
+        side = torch.cuda.Stream()  # default priority
+        side.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(side):
+            with torch.cuda.graph(g, stream=side):
+                self.step(u, centroids, bias, gamma)
+        torch.cuda.current_stream().wait_stream(side)
+        return g
+
 
 def quantize_experts(ws: tuple, stream=None) -> tuple:
     """E4M3 codes and 128x128 block scales of stacked expert weights (w1, w3, w2) ->
