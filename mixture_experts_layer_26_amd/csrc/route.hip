@@ -189,6 +189,8 @@ __device__ __forceinline__ void score_key(float z, const float* __restrict__ bia
   key = (static_cast<uint64_t>(orderable(v)) << 32) | (0xFFFFFFFFu - static_cast<uint32_t>(j));
 }
 
+constexpr int kSumBatch = 8;  // partial logits a lane loads before adding them
+
 // Top-K of one token per wave from the partial logits of n_chunks chunks.
 template <int SCORE>
 __global__ __launch_bounds__(256) void route_topk(const float* __restrict__ part, int n_chunks,
@@ -197,7 +199,24 @@ __global__ __launch_bounds__(256) void route_topk(const float* __restrict__ part
   const int lane = threadIdx.x % kWave;
   const int64_t t = static_cast<int64_t>(blockIdx.x) * (256 / kWave) + threadIdx.x / kWave;
   if (t >= T) return;
-  // this lane's candidates: experts lane, lane+64, lane+128, lane+192
+  // this lane's candidates: experts lane, lane+64, lane+128, lane+192. Their logits are the
+  // chunks' partials added in chunk order; each batch of kSumBatch chunks is loaded for all
+  // four candidates before the first of its additions, so those loads are in flight together.
+  float z[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+  for (int q0 = 0; q0 < n_chunks; q0 += kSumBatch) {
+    float pv[4][kSumBatch];
+#pragma unroll
+    for (int c = 0; c < 4; ++c)
+#pragma unroll
+      for (int i = 0; i < kSumBatch; ++i)
+        if (lane + 64 * c < n_r && q0 + i < n_chunks)
+          pv[c][i] = part[(static_cast<int64_t>(q0 + i) * T + t) * n_r + lane + 64 * c];
+#pragma unroll
+    for (int c = 0; c < 4; ++c)
+#pragma unroll
+      for (int i = 0; i < kSumBatch; ++i)
+        if (lane + 64 * c < n_r && q0 + i < n_chunks) z[c] += pv[c][i];
+  }
   float sv[4];
   uint64_t key[4];
 #pragma unroll
@@ -205,11 +224,7 @@ __global__ __launch_bounds__(256) void route_topk(const float* __restrict__ part
     const int j = lane + 64 * c;
     sv[c] = 0.0f;
     key[c] = 0;  // below every real key
-    if (j < n_r) {
-      float z = 0.0f;
-      for (int q = 0; q < n_chunks; ++q) z += part[(static_cast<int64_t>(q) * T + t) * n_r + j];
-      score_key<SCORE>(z, bias, j, sv[c], key[c]);
-    }
+    if (j < n_r) score_key<SCORE>(z[c], bias, j, sv[c], key[c]);
   }
   topk_select<SCORE == 1>(key, sv, lane, K, topk_idx + t * K, topk_gate + t * K);
 }
