@@ -348,7 +348,7 @@ __global__ __launch_bounds__(kThreads) void grouped_gemm_fp8(Fp8Args fa) {
   const int n_r = args.n_r;
   const int bn_out = GATED ? BNB / 2 : BNB;
   const int ntn = args.N / bn_out;
-  build_tile_map<TR>(tm, args.offset, n_r, args.n_shared_groups, args.T, ntn);
+  build_tile_map<TR, GATED>(tm, args.offset, n_r, args.n_shared_groups, args.T, ntn);
   auto rows_of = [&](int grp) -> int64_t { return grp < n_r ? args.offset[grp + 1] - args.offset[grp] : args.T; };
 
   const int tid = threadIdx.x, lane = tid % kWave, wave = tid / kWave;

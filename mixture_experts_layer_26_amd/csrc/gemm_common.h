@@ -32,14 +32,16 @@ struct Tile {
 // number of row blocks, then those with an odd number, so that with 16 column tiles per
 // block and 32-tile gang items an expert of two blocks fills exactly one item. The shared
 // groups' tiles are all of full height and come first; the routed tiles, whose heights
-// vary, fill the tail of the launch, where short tiles even out the finish. Within each
-// of the two routed passes the experts go by row count, most rows first (ties: lower
-// expert id first). A gang item then holds experts of about the same height, so its
+// vary, fill the tail of the launch, where short tiles even out the finish. In the gate/up
+// launch (SORT) the experts of each routed pass go by row count, most rows first (ties:
+// lower expert id first). A gang item then holds experts of about the same height, so its
 // members' tiles take about the same time and no member of the gang lags behind the
 // others, and the shortest tiles come last. A CPU model of the launch (tile times from
 // the measured per-step cost, the gang protocol run as written, the V3-prefill expert
-// loads) gave 94% of the ideal finish for the gate/up launch with the experts in id
-// order and 97% in this order.
+// loads) gave 94% of the ideal finish with the experts in id order and 97% in this
+// order. The down-projection keeps id order: its items straddle experts (28 column tiles
+// per block at d = 7168), and in id order the experts that run side by side are
+// neighbours in H and in y_routed; sorted, its launch measured 2% slower.
 // Routed groups list their tiles column-major (the row blocks of one column tile are
 // neighbours: they read the same weights). A shared group is a dense GEMM over all tokens
 // (many row blocks), so its tiles go in blocks of kSharedBR row blocks x kSharedBC column
@@ -54,12 +56,12 @@ struct TileMap {
   int mt[kMaxGroups];       // row blocks of each group
   int rpb[kMaxGroups];      // rows per block of each group
   int rows[kMaxGroups];     // rows of each routed expert (the sort key)
-  int ord[kMaxGroups];      // routed experts, most rows first (ties: lower id first)
+  int ord[kMaxGroups];      // routed experts in list order (SORT: most rows first, ties: lower id first)
   int ng;                   // positions (groups with rows)
   int total;
 };
 
-template <int RB = BM>  // rows per block at most
+template <int RB = BM, bool SORT = true>  // rows per block at most; routed experts by row count
 __device__ inline void build_tile_map(TileMap& tm, const int32_t* offset, int n_r, int n_groups_shared,
                                       int64_t T, int ntn) {
   const int ng = n_r + n_groups_shared;
@@ -73,13 +75,17 @@ __device__ inline void build_tile_map(TileMap& tm, const int32_t* offset, int n_
   }
   __syncthreads();
   // position of each routed expert in the order: the experts before it have more rows, or
-  // as many and a lower id (a total order, so the positions are a permutation)
+  // as many and a lower id (a total order, so the positions are a permutation); without
+  // SORT, id order
   for (int g = threadIdx.x; g < n_r; g += kThreads) {
-    const int rg = tm.rows[g];
-    int pos = 0;
-    for (int h = 0; h < n_r; ++h) {
-      const int rh = tm.rows[h];
-      pos += (rh > rg || (rh == rg && h < g)) ? 1 : 0;
+    int pos = g;
+    if constexpr (SORT) {
+      const int rg = tm.rows[g];
+      pos = 0;
+      for (int h = 0; h < n_r; ++h) {
+        const int rh = tm.rows[h];
+        pos += (rh > rg || (rh == rg && h < g)) ? 1 : 0;
+      }
     }
     tm.ord[pos] = g;
   }

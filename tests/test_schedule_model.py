@@ -14,7 +14,7 @@ under random interleavings of the workgroups, on random and skewed expert loads,
   reads past its row of slots (slot stride ceil(max/G) + 2);
 - the list order: shared groups first, then routed experts with an even number of row
   blocks, then those with an odd number, each pass by row count (most first, ties to the
-  lower id).
+  lower id) in the gate/up launch and in id order in the down-projection.
 
 It is a model: it checks the protocol's design, and the GPU parity tests check the
 kernels that implement it.
@@ -28,9 +28,10 @@ GANGS = 8
 SMALL_BATCH = 128  # batches of at most this many tokens: bf16 tiles of 128 rows
 
 
-def tile_map(rows, n_r, rb=BM):
+def tile_map(rows, n_r, rb=BM, sort=True):
     """Row blocks of at most rb rows per group, rows per block, and the list order (shared,
-    even, odd; the routed experts of each pass by row count, most first)."""
+    even, odd; the routed experts of each pass by row count, most first, when sort -- the
+    gate/up launch -- else in id order -- the down-projection)."""
     mt, rpb = [], []
     for r in rows:
         mt0 = (r + rb - 1) // rb
@@ -38,15 +39,15 @@ def tile_map(rows, n_r, rb=BM):
         rpb.append(p)
         mt.append((r + p - 1) // p if p else 0)
     # routed experts by row count, most first, ties to the lower id
-    by_rows = sorted(range(n_r), key=lambda g: (-rows[g], g))
+    by_rows = sorted(range(n_r), key=lambda g: (-rows[g], g)) if sort else list(range(n_r))
     order = [g for g in range(n_r, len(rows)) if mt[g]]
     order += [g for g in by_rows if mt[g] and mt[g] % 2 == 0]
     order += [g for g in by_rows if mt[g] and mt[g] % 2 == 1]
     return mt, rpb, order
 
 
-def tiles_of(rows, n_r, ntn, rb=BM):
-    mt, rpb, order = tile_map(rows, n_r, rb)
+def tiles_of(rows, n_r, ntn, rb=BM, sort=True):
+    mt, rpb, order = tile_map(rows, n_r, rb, sort)
     out = []
     for g in order:
         if g < n_r:  # column-major: the row blocks of one column tile are neighbours
@@ -106,7 +107,7 @@ def check(T, top_k, n_r, n_shared, d, d_ff, counts, grid, rng):
         ns_groups = n_shared if phase == 1 else min(n_shared, 1)
         ntn = d_ff // 128 if phase == 1 else d // 256
         rows = list(counts) + [T] * ns_groups
-        tiles = tiles_of(rows, n_r, ntn, rb)
+        tiles = tiles_of(rows, n_r, ntn, rb, sort=phase == 1)
         bound = max_tiles(T, top_k, n_r, n_shared, d, d_ff, phase)
         assert len(tiles) <= bound
         G = grid // GANGS
@@ -174,6 +175,7 @@ def test_tile_order():
     assert mt == [2, 0, 3, 1, 3, 36, 1]
     assert rpb == [150, 0, 200, 256, 171, 250, 70]
     assert order == [5, 6, 0, 2, 4, 3]  # odd pass: 600, 513, 256 rows
+    assert tile_map(rows, 5, sort=False)[2] == [5, 6, 0, 2, 3, 4]  # the down-projection: id order
     mt, rpb, order = tile_map(rows, 5, 320)  # the bf16 kernel's phase-1 tiles
     assert mt == [1, 0, 2, 1, 2, 29, 1]
     assert rpb == [300, 0, 300, 256, 257, 311, 70]
