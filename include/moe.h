@@ -24,7 +24,9 @@
  *    library's device code (each GPU's copy keeps the last call's scratch contents).
  *  - `stream` is a hipStream_t passed as void* (NULL = the null stream). Every call
  *    only enqueues work and returns; calls on one stream run in order. There is no
- *    device-to-host copy or synchronisation inside any call.
+ *    device-to-host copy or synchronisation inside any call (MOE_DEBUG aside, below),
+ *    no allocation and no memset: the forward calls can be recorded into a HIP graph by
+ *    stream capture and replayed (after one uncaptured call has loaded the kernels).
  *  - Arguments are validated on the host before anything is enqueued; a bad
  *    argument returns MOE_ERR_INVALID_ARG (or MOE_ERR_UNSUPPORTED / MOE_ERR_WORKSPACE)
  *    and touches no memory. Kernels trust the index arrays produced by earlier calls,
