@@ -10,8 +10,9 @@
 // columns in turn). The tile's operand rows go to LDS in K chunks of 256 with 16-byte
 // coalesced loads, at a pitch of 257 floats so that the 16 columns (and 4 rows) a wave
 // reads at one k fall in different banks; each thread then runs its dot products from
-// LDS, 16 K values read ahead of their FMAs. Every output is one fp32 FMA chain in ascending K (phase 2, shared: ascending
-// expert, then ascending K), so a chunk boundary changes nothing in the result.
+// LDS, 16 K values read ahead of their FMAs. Every output is one fp32 FMA chain in
+// ascending K (phase 2, shared: ascending expert, then ascending K), so a chunk boundary
+// changes nothing in the result.
 #include "device.h"
 #include "launch.h"
 
